@@ -1,0 +1,421 @@
+/*
+ * moe_oracle.c -- CPU oracle for the fused MoE expert layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the slow, plain reference that the
+ * GPU path is checked against. Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load it. The product library never
+ * links, loads or calls it, and it shares no code with the HIP kernels.
+ *
+ * What it computes (one MoE expert layer, no token dropping):
+ *   route   : per token, the k largest router logits (ties -> lower expert
+ *             index), in descending order, and a softmax over those k logits.
+ *   permute : a stable counting sort of the T*k (token, slot) assignments by
+ *             expert id into per-expert contiguous row blocks.
+ *   gate/up : per expert, G = X W_gate, U = X W_up, h = silu(G) * U.
+ *   down    : y = h W_down.
+ *   combine : out[t] = sum_j w[t,j] * y[row of (t,j)]  (+ s_t * shared(x[t])).
+ *
+ * Sources (restated, not quoted):
+ *   - "Triton-MoE-Dispatch-Kernel erreicht 131 % von Megablocks" (lumeric.app),
+ *     summary paragraph: the gate and up projections are computed together and
+ *     feed SwiGLU; the layer is dispatch -> fused gate/up -> down -> combine.
+ *   - "DeepGEMM ..." article (itsolotime.com), section 1.1: the MoE layer runs
+ *     dispatch -> linear1 -> SwiGLU -> linear2 -> combine; section 3.1: the
+ *     activations of an m-grouped GEMM are stored contiguously per expert.
+ *   - HPC-Ops article (ntfzh.com), FusedMoE paragraph: data re-arrangement
+ *     before the grouped GEMM, then a weighted-average reduce afterwards.
+ *   - Triton MoE page (setupai.cc), key points: block-scheduled grouped GEMM
+ *     over variable expert batch sizes.
+ *   The pages fix neither routing details nor precision. Readings taken here:
+ *   softmax over the k selected logits; ties to the lower expert index with
+ *   -0 == +0; rows inside an expert block in ascending token order; all
+ *   floating-point arithmetic in IEEE double (fp64) with sums taken in
+ *   ascending index order; SwiGLU h = silu(x W_gate) * (x W_up) with
+ *   silu(z) = z / (1 + exp(-z)) (Shazeer, "GLU Variants Improve Transformer").
+ *
+ * Data: bf16 tensors are passed as uint16 bit patterns; floats as fp32; all
+ * results of arithmetic are fp64. Row-major, contiguous. Weights are
+ * W_gate/W_up [E,H,F] and W_down [E,F,H].
+ *
+ * Pins (in tests/): a numpy fp64 dense brute force (every expert run on every
+ * token, masked and weighted), the E=1,k=1 reduction to a textbook SwiGLU FFN,
+ * closed-form routing weights, brute-force routing and permutation by full
+ * sort, hand-worked fixtures, exact scaling and zero invariants.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_OK 0
+#define ORC_ERR_ARG (-1)
+#define ORC_ERR_NONFINITE (-2)
+#define ORC_ERR_ID (-3)
+#define ORC_ERR_NOMEM (-4)
+
+static inline double bf16_to_f64(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------ route */
+
+/* One token: the k largest of E logits, larger first, equal logits taken in
+ * ascending expert order; then softmax over the chosen logits. `taken` is
+ * scratch of E bytes. Returns ORC_ERR_NONFINITE on a NaN/Inf logit. */
+static int route_one(const float* l, int E, int k, int32_t* ids, double* w,
+                     unsigned char* taken) {
+  for (int e = 0; e < E; ++e) {
+    if (!isfinite(l[e])) return ORC_ERR_NONFINITE;
+    taken[e] = 0;
+  }
+  for (int j = 0; j < k; ++j) {
+    int best = -1;
+    for (int e = 0; e < E; ++e) {
+      if (taken[e]) continue;
+      /* strict '>' keeps the earlier (lower) index on a tie; IEEE compare
+       * treats -0.0 and +0.0 as equal, so they tie as well */
+      if (best < 0 || l[e] > l[best]) best = e;
+    }
+    taken[best] = 1;
+    ids[j] = best;
+  }
+  /* softmax over the k selected logits; slot 0 holds the largest, which is
+   * subtracted before exponentiation */
+  double m = (double)l[ids[0]];
+  double s = 0.0;
+  for (int j = 0; j < k; ++j) {
+    w[j] = exp((double)l[ids[j]] - m);
+    s += w[j];
+  }
+  for (int j = 0; j < k; ++j) w[j] = w[j] / s;
+  return ORC_OK;
+}
+
+int oracle_route(const float* logits, int64_t T, int E, int k, int32_t* ids,
+                 double* w) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return ORC_ERR_ARG;
+  unsigned char* taken = (unsigned char*)malloc((size_t)E);
+  if (!taken) return ORC_ERR_NOMEM;
+  int rc = ORC_OK;
+  for (int64_t t = 0; t < T && rc == ORC_OK; ++t)
+    rc = route_one(logits + t * E, E, k, ids + t * k, w + t * k, taken);
+  free(taken);
+  return rc;
+}
+
+/* ---------------------------------------------------------------- permute */
+
+/* Stable counting sort of the flat assignments i = t*k + j by expert id.
+ * offsets[E+1] = exclusive prefix of the per-expert counts; row p of the
+ * permuted layout holds token row_token[p]; row_dest[t*k+j] = p. */
+int oracle_permute(const int32_t* ids, int64_t T, int E, int k,
+                   int32_t* offsets, int32_t* row_token, int32_t* row_dest) {
+  if (T < 0 || E < 1 || k < 1) return ORC_ERR_ARG;
+  int64_t A = T * k;
+  int64_t* next = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+  if (!next) return ORC_ERR_NOMEM;
+  for (int64_t i = 0; i < A; ++i) {
+    if (ids[i] < 0 || ids[i] >= E) {
+      free(next);
+      return ORC_ERR_ID;
+    }
+    next[ids[i]] += 1; /* count */
+  }
+  int64_t run = 0;
+  for (int e = 0; e < E; ++e) {
+    offsets[e] = (int32_t)run;
+    int64_t c = next[e];
+    next[e] = run; /* first free row of expert e */
+    run += c;
+  }
+  offsets[E] = (int32_t)run;
+  for (int64_t t = 0; t < T; ++t)
+    for (int j = 0; j < k; ++j) {
+      int64_t p = next[ids[t * k + j]]++;
+      row_token[p] = (int32_t)t;
+      row_dest[t * k + j] = (int32_t)p;
+    }
+  free(next);
+  return ORC_OK;
+}
+
+/* x_perm[p,:] = x[row_token[p],:] (a bit copy). */
+void oracle_gather(const uint16_t* x, const int32_t* row_token, int64_t A,
+                   int H, uint16_t* x_perm) {
+  for (int64_t p = 0; p < A; ++p)
+    memcpy(x_perm + p * H, x + (int64_t)row_token[p] * H,
+           (size_t)H * sizeof(uint16_t));
+}
+
+/* ------------------------------------------------------------ expert FFN */
+
+static inline double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* One row through gate/up + SwiGLU: G[f] = sum_h x[h] Wg[h,f] (h ascending),
+ * likewise U; h[f] = silu(G[f]) * U[f]. G and U are scratch of F doubles. */
+static void gateup_row(const uint16_t* x, int H, int F, const uint16_t* wg,
+                       const uint16_t* wu, double* hrow, double* G, double* U) {
+  for (int f = 0; f < F; ++f) G[f] = 0.0, U[f] = 0.0;
+  for (int h = 0; h < H; ++h) {
+    double xv = bf16_to_f64(x[h]);
+    const uint16_t* rg = wg + (int64_t)h * F;
+    const uint16_t* ru = wu + (int64_t)h * F;
+    for (int f = 0; f < F; ++f) {
+      G[f] += xv * bf16_to_f64(rg[f]);
+      U[f] += xv * bf16_to_f64(ru[f]);
+    }
+  }
+  for (int f = 0; f < F; ++f) hrow[f] = silu(G[f]) * U[f];
+}
+
+/* One row through the down projection: y[c] = sum_f h[f] Wd[f,c] (f asc). */
+static void down_row(const double* hrow, int F, int H, const uint16_t* wd,
+                     double* y) {
+  for (int c = 0; c < H; ++c) y[c] = 0.0;
+  for (int f = 0; f < F; ++f) {
+    double hv = hrow[f];
+    const uint16_t* rd = wd + (int64_t)f * H;
+    for (int c = 0; c < H; ++c) y[c] += hv * bf16_to_f64(rd[c]);
+  }
+}
+
+/* M rows of x [M,H] through one expert's gate/up + SwiGLU -> h [M,F]. */
+int oracle_gateup_rows(const uint16_t* x, int64_t M, int H, int F,
+                       const uint16_t* wg, const uint16_t* wu, double* h) {
+  int rc = ORC_OK;
+#pragma omp parallel
+  {
+    double* G = (double*)malloc(sizeof(double) * (size_t)F * 2);
+    if (!G) {
+#pragma omp atomic write
+      rc = ORC_ERR_NOMEM;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < M; ++r)
+        gateup_row(x + r * H, H, F, wg, wu, h + r * F, G, G + F);
+      free(G);
+    }
+  }
+  return rc;
+}
+
+/* M rows of h [M,F] through one expert's down projection -> y [M,H]. */
+int oracle_down_rows(const double* h, int64_t M, int F, int H,
+                     const uint16_t* wd, double* y) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < M; ++r) down_row(h + r * F, F, H, wd, y + r * H);
+  return ORC_OK;
+}
+
+/* Expert owning permuted row p: the e with offsets[e] <= p < offsets[e+1]. */
+static int expert_of_row(const int32_t* offsets, int E, int64_t p) {
+  int e = 0;
+  while (e < E && !(p >= offsets[e] && p < offsets[e + 1])) ++e;
+  return e;
+}
+
+/* Grouped gate/up + SwiGLU over the permuted rows: rows of expert e use
+ * W_gate[e], W_up[e]. x_perm [A,H], h [A,F], A = offsets[E]. */
+int oracle_grouped_gateup(const uint16_t* x_perm, const int32_t* offsets,
+                          int E, int H, int F, const uint16_t* wg,
+                          const uint16_t* wu, double* h) {
+  int64_t A = offsets[E];
+  int rc = ORC_OK;
+#pragma omp parallel
+  {
+    double* G = (double*)malloc(sizeof(double) * (size_t)F * 2);
+    if (!G) {
+#pragma omp atomic write
+      rc = ORC_ERR_NOMEM;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t p = 0; p < A; ++p) {
+        int e = expert_of_row(offsets, E, p);
+        int64_t wo = (int64_t)e * H * F;
+        gateup_row(x_perm + p * H, H, F, wg + wo, wu + wo, h + p * F, G,
+                   G + F);
+      }
+      free(G);
+    }
+  }
+  return rc;
+}
+
+/* Grouped down projection: rows of expert e use W_down[e]. y [A,H]. */
+int oracle_grouped_down(const double* h, const int32_t* offsets, int E, int F,
+                        int H, const uint16_t* wd, double* y) {
+  int64_t A = offsets[E];
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t p = 0; p < A; ++p) {
+    int e = expert_of_row(offsets, E, p);
+    down_row(h + p * F, F, H, wd + (int64_t)e * F * H, y + p * H);
+  }
+  return ORC_OK;
+}
+
+/* ---------------------------------------------------------------- combine */
+
+/* out[t,c] = sum_j w[t,j] * y[row_dest[t,j], c]  (j ascending), then
+ * + s[t] * y_sh[t,c] when a shared expert is present (y_sh, s non-NULL). */
+void oracle_combine(const double* y, const int32_t* row_dest, const double* w,
+                    int64_t T, int H, int k, const double* y_sh,
+                    const double* s, double* out) {
+#pragma omp parallel for
+  for (int64_t t = 0; t < T; ++t)
+    for (int c = 0; c < H; ++c) {
+      double acc = 0.0;
+      for (int j = 0; j < k; ++j)
+        acc += w[t * k + j] * y[(int64_t)row_dest[t * k + j] * H + c];
+      if (y_sh) acc += s[t] * y_sh[t * H + c];
+      out[t * H + c] = acc;
+    }
+}
+
+/* Shared-expert gate: s_t = 1 when no gate logits are given, else the
+ * logistic sigmoid 1 / (1 + exp(-g_t)). */
+void oracle_shared_gate(const float* gate_logits, int64_t T, double* s) {
+  for (int64_t t = 0; t < T; ++t)
+    s[t] = gate_logits ? 1.0 / (1.0 + exp(-(double)gate_logits[t])) : 1.0;
+}
+
+/* -------------------------------------------------------- whole forward */
+
+/* Full layer: route -> permute -> gather -> grouped gate/up -> grouped down
+ * -> (shared expert) -> combine. Shared expert is present when Fs > 0.
+ * Outputs: out [T,H] fp64, and (each may be NULL) ids [T,k], w [T,k],
+ * offsets [E+1], row_token [T*k], row_dest [T*k], h [T*k,F], y [T*k,H]. */
+int oracle_forward(const uint16_t* x, const float* logits, int64_t T, int H,
+                   int F, int E, int k, const uint16_t* wg, const uint16_t* wu,
+                   const uint16_t* wd, int Fs, const uint16_t* wsg,
+                   const uint16_t* wsu, const uint16_t* wsd,
+                   const float* gate_logits, double* out, int32_t* ids_out,
+                   double* w_out, int32_t* offsets_out,
+                   int32_t* row_token_out, int32_t* row_dest_out,
+                   double* h_out, double* y_out) {
+  if (T < 0 || H < 1 || F < 1 || E < 1 || k < 1 || k > E || Fs < 0)
+    return ORC_ERR_ARG;
+  int64_t A = T * k;
+  int rc = ORC_ERR_NOMEM;
+  int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)(A + 1));
+  double* w = (double*)malloc(sizeof(double) * (size_t)(A + 1));
+  int32_t* offsets = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
+  int32_t* row_token = (int32_t*)malloc(sizeof(int32_t) * (size_t)(A + 1));
+  int32_t* row_dest = (int32_t*)malloc(sizeof(int32_t) * (size_t)(A + 1));
+  uint16_t* x_perm = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(A * H + 1));
+  double* h = (double*)malloc(sizeof(double) * (size_t)(A * F + 1));
+  double* y = (double*)malloc(sizeof(double) * (size_t)(A * H + 1));
+  double* h_sh = Fs > 0 ? (double*)malloc(sizeof(double) * (size_t)(T * Fs + 1)) : NULL;
+  double* y_sh = Fs > 0 ? (double*)malloc(sizeof(double) * (size_t)(T * H + 1)) : NULL;
+  double* s = Fs > 0 ? (double*)malloc(sizeof(double) * (size_t)(T + 1)) : NULL;
+  if (!ids || !w || !offsets || !row_token || !row_dest || !x_perm || !h ||
+      !y || (Fs > 0 && (!h_sh || !y_sh || !s)))
+    goto done;
+
+  rc = oracle_route(logits, T, E, k, ids, w);
+  if (rc) goto done;
+  rc = oracle_permute(ids, T, E, k, offsets, row_token, row_dest);
+  if (rc) goto done;
+  oracle_gather(x, row_token, A, H, x_perm);
+  rc = oracle_grouped_gateup(x_perm, offsets, E, H, F, wg, wu, h);
+  if (rc) goto done;
+  oracle_grouped_down(h, offsets, E, F, H, wd, y);
+  if (Fs > 0) {
+    rc = oracle_gateup_rows(x, T, H, Fs, wsg, wsu, h_sh);
+    if (rc) goto done;
+    oracle_down_rows(h_sh, T, Fs, H, wsd, y_sh);
+    oracle_shared_gate(gate_logits, T, s);
+  }
+  oracle_combine(y, row_dest, w, T, H, k, y_sh, s, out);
+
+  if (ids_out) memcpy(ids_out, ids, sizeof(int32_t) * (size_t)A);
+  if (w_out) memcpy(w_out, w, sizeof(double) * (size_t)A);
+  if (offsets_out) memcpy(offsets_out, offsets, sizeof(int32_t) * (size_t)(E + 1));
+  if (row_token_out) memcpy(row_token_out, row_token, sizeof(int32_t) * (size_t)A);
+  if (row_dest_out) memcpy(row_dest_out, row_dest, sizeof(int32_t) * (size_t)A);
+  if (h_out) memcpy(h_out, h, sizeof(double) * (size_t)(A * F));
+  if (y_out) memcpy(y_out, y, sizeof(double) * (size_t)(A * H));
+  rc = ORC_OK;
+done:
+  free(ids); free(w); free(offsets); free(row_token); free(row_dest);
+  free(x_perm); free(h); free(y); free(h_sh); free(y_sh); free(s);
+  return rc;
+}
+
+/* Output rows of selected tokens only. Every token's output depends on that
+ * token alone, so out[i] for token tokens[i] equals row tokens[i] of
+ * oracle_forward; it is computed here with the same per-row functions, one
+ * token at a time (route that token, run its k experts, combine). */
+int oracle_forward_tokens(const uint16_t* x, const float* logits, int64_t T,
+                          int H, int F, int E, int k, const uint16_t* wg,
+                          const uint16_t* wu, const uint16_t* wd, int Fs,
+                          const uint16_t* wsg, const uint16_t* wsu,
+                          const uint16_t* wsd, const float* gate_logits,
+                          const int64_t* tokens, int64_t n, double* out,
+                          int32_t* ids_out, double* w_out) {
+  if (T < 0 || H < 1 || F < 1 || E < 1 || k < 1 || k > E || Fs < 0)
+    return ORC_ERR_ARG;
+  for (int64_t i = 0; i < n; ++i)
+    if (tokens[i] < 0 || tokens[i] >= T) return ORC_ERR_ARG;
+  int rc = ORC_OK;
+#pragma omp parallel
+  {
+    int Fmax = F > Fs ? F : Fs;
+    unsigned char* taken = (unsigned char*)malloc((size_t)E);
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    int32_t* dest = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+    double* w = (double*)malloc(sizeof(double) * (size_t)k);
+    double* GU = (double*)malloc(sizeof(double) * (size_t)Fmax * 2);
+    double* hrow = (double*)malloc(sizeof(double) * (size_t)Fmax);
+    double* y = (double*)malloc(sizeof(double) * (size_t)k * H);
+    double* ysh = (double*)malloc(sizeof(double) * (size_t)H);
+    if (!taken || !ids || !dest || !w || !GU || !hrow || !y || !ysh) {
+#pragma omp atomic write
+      rc = ORC_ERR_NOMEM;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t i = 0; i < n; ++i) {
+        int64_t t = tokens[i];
+        const uint16_t* xt = x + t * H;
+        int r = route_one(logits + t * E, E, k, ids, w, taken);
+        if (r) {
+#pragma omp atomic write
+          rc = r;
+          continue;
+        }
+        for (int j = 0; j < k; ++j) {
+          int64_t wo = (int64_t)ids[j] * H * F;
+          gateup_row(xt, H, F, wg + wo, wu + wo, hrow, GU, GU + F);
+          down_row(hrow, F, H, wd + (int64_t)ids[j] * F * H, y + (int64_t)j * H);
+          dest[j] = j;
+        }
+        double s = 0.0;
+        if (Fs > 0) {
+          gateup_row(xt, H, Fs, wsg, wsu, hrow, GU, GU + Fs);
+          down_row(hrow, Fs, H, wsd, ysh);
+          oracle_shared_gate(gate_logits ? gate_logits + t : NULL, 1, &s);
+        }
+        oracle_combine(y, dest, w, 1, H, k, Fs > 0 ? ysh : NULL, &s,
+                       out + i * H);
+        if (ids_out) memcpy(ids_out + i * k, ids, sizeof(int32_t) * (size_t)k);
+        if (w_out) memcpy(w_out + i * k, w, sizeof(double) * (size_t)k);
+      }
+    }
+    free(taken); free(ids); free(dest); free(w); free(GU); free(hrow);
+    free(y); free(ysh);
+  }
+  return rc;
+}
