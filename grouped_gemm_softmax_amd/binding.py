@@ -1,0 +1,236 @@
+"""Python binding of libmoe.so (ctypes). Argument marshalling only: every step
+of the layer runs in the library's HIP kernels. torch supplies device memory
+and the current HIP stream.
+
+The function names match the C ABI in include/moe.h. Outputs that are not
+passed in are allocated with torch on the inputs' device. A non-zero status
+raises MoeError with the library's status text.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, text: str, call: str):
+        super().__init__(f"{call}: {text} (status {status})")
+        self.status = status
+
+
+class SharedExpert(ctypes.Structure):
+    _fields_ = [("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p), ("Fs", ctypes.c_int32),
+                ("gate_logits", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "moe_status_string": (ctypes.c_char_p, [_I]),
+    "moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "moe_permute": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_gateup_swiglu": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "moe_down": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_grouped_ffn": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
+    "moe_forward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "moe_forward": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P,
+                         ctypes.POINTER(SharedExpert), _P, _P, _P, _P, _SZ, _P]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so. Raises if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m grouped_gemm_softmax_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_symbols(path: str = HEADER):
+    """Function names declared in include/moe.h."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, call: str):
+    if status != 0:
+        raise MoeError(status, lib().moe_status_string(status).decode(), call)
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if t.dtype != dtype or not t.is_contiguous():
+        raise TypeError(f"{name}: expected contiguous {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name}: expected a device tensor")
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def moe_route(logits: torch.Tensor, k: int, topk_ids=None, topk_w=None, stream=None):
+    _need(logits, torch.float32, "logits")
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(lib().moe_route(_ptr(logits), T, E, k, _ptr(topk_ids), _ptr(topk_w),
+                           _stream(stream)), "moe_route")
+    return topk_ids, topk_w
+
+
+def moe_permute_workspace_bytes(T: int, E: int, k: int) -> int:
+    return int(lib().moe_permute_workspace_bytes(T, E, k))
+
+
+def moe_permute(x: torch.Tensor, topk_ids: torch.Tensor, E: int, ws=None, out=None,
+                stream=None):
+    """Returns (expert_offsets [E+1], row_token [T*k], row_dest [T,k], x_perm [T*k,H])."""
+    _need(x, torch.bfloat16, "x")
+    _need(topk_ids, torch.int32, "topk_ids")
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    dev = x.device
+    if out is None:
+        out = (torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev),
+               torch.empty((T, k), dtype=torch.int32, device=dev),
+               torch.empty((T * k, H), dtype=torch.bfloat16, device=dev))
+    offsets, row_token, row_dest, x_perm = out
+    if ws is None:
+        ws = torch.empty(max(moe_permute_workspace_bytes(T, E, k), 16),
+                         dtype=torch.uint8, device=dev)
+    _check(lib().moe_permute(_ptr(x), _ptr(topk_ids), T, H, E, k, _ptr(offsets),
+                             _ptr(row_token), _ptr(row_dest), _ptr(x_perm), _ptr(ws),
+                             ws.numel(), _stream(stream)), "moe_permute")
+    return offsets, row_token, row_dest, x_perm
+
+
+def moe_gateup_swiglu(x_perm, expert_offsets, w_gate, w_up, h=None, stream=None):
+    _need(x_perm, torch.bfloat16, "x_perm")
+    _need(expert_offsets, torch.int32, "expert_offsets")
+    _need(w_gate, torch.bfloat16, "w_gate")
+    _need(w_up, torch.bfloat16, "w_up")
+    M, H = x_perm.shape
+    E, _, F = w_gate.shape
+    if h is None:
+        h = torch.empty((M, F), dtype=torch.bfloat16, device=x_perm.device)
+    _check(lib().moe_gateup_swiglu(_ptr(x_perm), _ptr(expert_offsets), M, H, F, E,
+                                   _ptr(w_gate), _ptr(w_up), _ptr(h), _stream(stream)),
+           "moe_gateup_swiglu")
+    return h
+
+
+def moe_down(h, expert_offsets, w_down, y_perm=None, stream=None):
+    _need(h, torch.bfloat16, "h")
+    _need(expert_offsets, torch.int32, "expert_offsets")
+    _need(w_down, torch.bfloat16, "w_down")
+    M, F = h.shape
+    E, _, H = w_down.shape
+    if y_perm is None:
+        y_perm = torch.empty((M, H), dtype=torch.bfloat16, device=h.device)
+    _check(lib().moe_down(_ptr(h), _ptr(expert_offsets), M, F, H, E, _ptr(w_down),
+                          _ptr(y_perm), _stream(stream)), "moe_down")
+    return y_perm
+
+
+def moe_grouped_ffn(x_perm, expert_offsets, w_gate, w_up, w_down, h=None, y_perm=None,
+                    stream=None):
+    _need(x_perm, torch.bfloat16, "x_perm")
+    _need(expert_offsets, torch.int32, "expert_offsets")
+    for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(t, torch.bfloat16, n)
+    M, H = x_perm.shape
+    E, _, F = w_gate.shape
+    if h is None:
+        h = torch.empty((M, F), dtype=torch.bfloat16, device=x_perm.device)
+    if y_perm is None:
+        y_perm = torch.empty((M, H), dtype=torch.bfloat16, device=x_perm.device)
+    _check(lib().moe_grouped_ffn(_ptr(x_perm), _ptr(expert_offsets), M, H, F, E,
+                                 _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h),
+                                 _ptr(y_perm), _stream(stream)), "moe_grouped_ffn")
+    return h, y_perm
+
+
+def moe_combine(y_perm, row_dest, topk_w, out=None, stream=None):
+    _need(y_perm, torch.bfloat16, "y_perm")
+    _need(row_dest, torch.int32, "row_dest")
+    _need(topk_w, torch.float32, "topk_w")
+    T, k = row_dest.shape
+    H = y_perm.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y_perm.device)
+    _check(lib().moe_combine(_ptr(y_perm), _ptr(row_dest), _ptr(topk_w), T, H, k,
+                             _ptr(out), _stream(stream)), "moe_combine")
+    return out
+
+
+def moe_forward_workspace_bytes(T, H, F, E, k, Fs=0) -> int:
+    return int(lib().moe_forward_workspace_bytes(T, H, F, E, k, Fs))
+
+
+def moe_forward(x, logits, k, w_gate, w_up, w_down, shared: Optional[dict] = None,
+                out=None, topk_ids=None, topk_w=None, ws=None, stream=None):
+    """Whole layer. shared: None or dict(w_gate [H,Fs], w_up [H,Fs],
+    w_down [Fs,H], gate_logits [T] fp32 or None). Returns out [T,H] bf16."""
+    _need(x, torch.bfloat16, "x")
+    _need(logits, torch.float32, "logits")
+    for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _need(t, torch.bfloat16, n)
+    T, H = x.shape
+    E, _, F = w_gate.shape
+    sh = None
+    Fs = 0
+    if shared is not None:
+        Fs = shared["w_gate"].shape[1]
+        g = shared.get("gate_logits")
+        sh = SharedExpert(shared["w_gate"].data_ptr(), shared["w_up"].data_ptr(),
+                          shared["w_down"].data_ptr(), Fs,
+                          None if g is None else g.data_ptr())
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(moe_forward_workspace_bytes(T, H, F, E, k, Fs), 16),
+                         dtype=torch.uint8, device=x.device)
+    _check(lib().moe_forward(_ptr(x), _ptr(logits), T, H, F, E, k, _ptr(w_gate),
+                             _ptr(w_up), _ptr(w_down),
+                             ctypes.byref(sh) if sh is not None else None, _ptr(out),
+                             _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(),
+                             _stream(stream)), "moe_forward")
+    return out

@@ -1,0 +1,311 @@
+// C ABI of the MoE expert layer: argument validation, workspace carving and
+// kernel launches. Every argument is checked on the host before anything is
+// enqueued; on an error nothing is launched and no output is touched.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+using moe::bf16_t;
+
+constexpr int64_t kIndexLimit = int64_t(1) << 31;
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int check_dims(int T, int E, int k) {
+  if (T < 0 || E < 1 || k < 1) return MOE_ERR_INVALID_ARG;
+  if (E > moe::kMaxExperts || k > moe::kMaxTopK || k > E) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (static_cast<int64_t>(T) * k >= kIndexLimit) return MOE_ERR_UNSUPPORTED_SHAPE;
+  return MOE_OK;
+}
+
+int check_width(int n) {
+  if (n < 1) return MOE_ERR_INVALID_ARG;
+  if (n % 8 != 0) return MOE_ERR_UNSUPPORTED_SHAPE;
+  return MOE_OK;
+}
+
+int check_elems(int64_t rows, int64_t cols) {
+  return rows * cols >= kIndexLimit ? MOE_ERR_UNSUPPORTED_SHAPE : MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)            \
+  do {                           \
+    const int rc_ = (expr);      \
+    if (rc_ != MOE_OK) return rc_; \
+  } while (0)
+
+// bf16 tensors are read and written in 16-byte vectors; fp32/int32 arrays
+// element-wise.
+int need_bf16(const void* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  return aligned(p, 16) ? MOE_OK : MOE_ERR_MISALIGNED;
+}
+int need_word(const void* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  return aligned(p, 4) ? MOE_OK : MOE_ERR_MISALIGNED;
+}
+
+size_t permute_ws_bytes(int T, int E, int k) {
+  return align_up(static_cast<size_t>(moe::route_num_chunks(T, k)) * E * sizeof(int32_t), 256);
+}
+
+// Workspace layout of moe_forward (each piece 256-byte aligned from ws):
+// [hist | topk_ids | topk_w | offsets | row_token | row_dest | x_perm | h |
+//  h_shared | y_perm | y_shared]
+struct ForwardLayout {
+  size_t hist, ids, w, offsets, row_token, row_dest, x_perm, h, h_sh, y, y_sh, total;
+};
+
+ForwardLayout forward_layout(int T, int H, int F, int E, int k, int Fs) {
+  ForwardLayout L;
+  const size_t A = static_cast<size_t>(T) * k;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+  L.hist = take(static_cast<size_t>(moe::route_num_chunks(T, k)) * E * 4);
+  L.ids = take(A * 4);
+  L.w = take(A * 4);
+  L.offsets = take((static_cast<size_t>(E) + 1) * 4);
+  L.row_token = take(A * 4);
+  L.row_dest = take(A * 4);
+  L.x_perm = take(A * H * 2);
+  L.h = take(A * F * 2);
+  L.h_sh = take(static_cast<size_t>(T) * (Fs > 0 ? Fs : 0) * 2);
+  L.y = take(A * H * 2);
+  L.y_sh = take(static_cast<size_t>(T) * (Fs > 0 ? H : 0) * 2);
+  L.total = o;
+  return L;
+}
+
+moe::GemmProblem gateup_problem(const bf16_t* x_perm, const int32_t* offsets, int M,
+                                int H, int F, int E, const bf16_t* wg,
+                                const bf16_t* wu, bf16_t* h) {
+  moe::GemmProblem p{};
+  p.seg[0] = moe::GemmSegment{x_perm, offsets, wg, wu, h,
+                              static_cast<int64_t>(H) * F, M, E, H, F};
+  p.nseg = 1;
+  p.gated = true;
+  p.rows_hint = M / E;
+  return p;
+}
+
+moe::GemmProblem down_problem(const bf16_t* h, const int32_t* offsets, int M, int F,
+                              int H, int E, const bf16_t* wd, bf16_t* y) {
+  moe::GemmProblem p{};
+  p.seg[0] = moe::GemmSegment{h, offsets, wd, nullptr, y,
+                              static_cast<int64_t>(F) * H, M, E, F, H};
+  p.nseg = 1;
+  p.gated = false;
+  p.rows_hint = M / E;
+  return p;
+}
+
+int check_ffn_args(const void* act, const int32_t* offsets, int M, int K, int N, int E,
+                   const void* w0, const void* w1, bool need_w1, const void* out) {
+  if (M < 0 || E < 1) return MOE_ERR_INVALID_ARG;
+  if (E > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED_SHAPE;
+  MOE_TRY(check_width(K));
+  MOE_TRY(check_width(N));
+  MOE_TRY(check_elems(M, K > N ? K : N));
+  if (M == 0) return MOE_OK;
+  MOE_TRY(need_bf16(act));
+  MOE_TRY(need_word(offsets));
+  MOE_TRY(need_bf16(w0));
+  if (need_w1) MOE_TRY(need_bf16(w1));
+  MOE_TRY(need_bf16(out));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: null pointer or non-positive size";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "MOE_ERR_UNSUPPORTED_SHAPE: size outside the supported limits";
+    case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED: pointer not aligned (bf16 tensors need 16 bytes)";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL: workspace below the required size";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP runtime call or kernel launch failed";
+    default: return "unknown moe status";
+  }
+}
+
+int moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids,
+              float* topk_w, void* stream) {
+  MOE_TRY(check_dims(T, E, k));
+  MOE_TRY(check_elems(T, E));
+  if (T == 0) return MOE_OK;
+  MOE_TRY(need_word(logits));
+  MOE_TRY(need_word(topk_ids));
+  MOE_TRY(need_word(topk_w));
+  return hip_status(moe::launch_route(logits, T, E, k, topk_ids, topk_w, nullptr,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_permute_workspace_bytes(int T, int E, int k) {
+  if (check_dims(T, E, k) != MOE_OK) return 0;
+  return permute_ws_bytes(T, E, k);
+}
+
+int moe_permute(const moe_bf16* x, const int32_t* topk_ids, int T, int H, int E,
+                int k, int32_t* expert_offsets, int32_t* row_token,
+                int32_t* row_dest, moe_bf16* x_perm, void* ws, size_t ws_bytes,
+                void* stream) {
+  MOE_TRY(check_dims(T, E, k));
+  MOE_TRY(check_width(H));
+  MOE_TRY(check_elems(static_cast<int64_t>(T) * k, H));
+  if (T == 0) return MOE_OK;
+  MOE_TRY(need_bf16(x));
+  MOE_TRY(need_word(topk_ids));
+  MOE_TRY(need_word(expert_offsets));
+  MOE_TRY(need_word(row_token));
+  MOE_TRY(need_word(row_dest));
+  MOE_TRY(need_bf16(x_perm));
+  MOE_TRY(need_bf16(ws));
+  if (ws_bytes < permute_ws_bytes(T, E, k)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* hist = static_cast<int32_t*>(ws);
+  MOE_TRY(hip_status(moe::launch_hist(topk_ids, T, E, k, hist, s)));
+  return hip_status(moe::launch_permute(x, topk_ids, T, H, E, k, hist, expert_offsets,
+                                        row_token, row_dest, x_perm, s));
+}
+
+int moe_gateup_swiglu(const moe_bf16* x_perm, const int32_t* expert_offsets, int M,
+                      int H, int F, int E, const moe_bf16* w_gate,
+                      const moe_bf16* w_up, moe_bf16* h, void* stream) {
+  MOE_TRY(check_ffn_args(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, true, h));
+  if (M == 0) return MOE_OK;
+  return hip_status(moe::launch_grouped_gemm(
+      gateup_problem(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, h),
+      static_cast<hipStream_t>(stream)));
+}
+
+int moe_down(const moe_bf16* h, const int32_t* expert_offsets, int M, int F, int H,
+             int E, const moe_bf16* w_down, moe_bf16* y_perm, void* stream) {
+  MOE_TRY(check_ffn_args(h, expert_offsets, M, F, H, E, w_down, nullptr, false, y_perm));
+  if (M == 0) return MOE_OK;
+  return hip_status(moe::launch_grouped_gemm(
+      down_problem(h, expert_offsets, M, F, H, E, w_down, y_perm),
+      static_cast<hipStream_t>(stream)));
+}
+
+int moe_grouped_ffn(const moe_bf16* x_perm, const int32_t* expert_offsets, int M,
+                    int H, int F, int E, const moe_bf16* w_gate,
+                    const moe_bf16* w_up, const moe_bf16* w_down, moe_bf16* h,
+                    moe_bf16* y_perm, void* stream) {
+  MOE_TRY(check_ffn_args(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, true, h));
+  MOE_TRY(check_ffn_args(h, expert_offsets, M, F, H, E, w_down, nullptr, false, y_perm));
+  if (M == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MOE_TRY(hip_status(moe::launch_grouped_gemm(
+      gateup_problem(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, h), s)));
+  return hip_status(moe::launch_grouped_gemm(
+      down_problem(h, expert_offsets, M, F, H, E, w_down, y_perm), s));
+}
+
+int moe_combine(const moe_bf16* y_perm, const int32_t* row_dest, const float* topk_w,
+                int T, int H, int k, moe_bf16* out, void* stream) {
+  if (T < 0 || k < 1) return MOE_ERR_INVALID_ARG;
+  if (k > moe::kMaxTopK) return MOE_ERR_UNSUPPORTED_SHAPE;
+  MOE_TRY(check_width(H));
+  MOE_TRY(check_elems(static_cast<int64_t>(T) * k, H));
+  if (T == 0) return MOE_OK;
+  MOE_TRY(need_bf16(y_perm));
+  MOE_TRY(need_word(row_dest));
+  MOE_TRY(need_word(topk_w));
+  MOE_TRY(need_bf16(out));
+  return hip_status(moe::launch_combine(y_perm, row_dest, topk_w, T, H, k, nullptr,
+                                        nullptr, out, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_forward_workspace_bytes(int T, int H, int F, int E, int k, int Fs) {
+  if (check_dims(T, E, k) != MOE_OK || check_width(H) != MOE_OK ||
+      check_width(F) != MOE_OK || Fs < 0 || (Fs > 0 && check_width(Fs) != MOE_OK))
+    return 0;
+  return forward_layout(T, H, F, E, k, Fs).total;
+}
+
+int moe_forward(const moe_bf16* x, const float* logits, int T, int H, int F, int E,
+                int k, const moe_bf16* w_gate, const moe_bf16* w_up,
+                const moe_bf16* w_down, const moe_shared_expert* shared,
+                moe_bf16* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(T, E, k));
+  MOE_TRY(check_width(H));
+  MOE_TRY(check_width(F));
+  const int Fs = shared ? shared->Fs : 0;
+  if (shared) MOE_TRY(check_width(Fs));
+  const int64_t A = static_cast<int64_t>(T) * k;
+  const int64_t widest = (H > F ? H : F) > Fs ? (H > F ? H : F) : Fs;
+  MOE_TRY(check_elems(A, widest));
+  MOE_TRY(check_elems(T, E));
+  if (T == 0) return MOE_OK;
+  MOE_TRY(need_bf16(x));
+  MOE_TRY(need_word(logits));
+  MOE_TRY(need_bf16(w_gate));
+  MOE_TRY(need_bf16(w_up));
+  MOE_TRY(need_bf16(w_down));
+  MOE_TRY(need_bf16(out));
+  if (topk_ids_out) MOE_TRY(need_word(topk_ids_out));
+  if (topk_w_out) MOE_TRY(need_word(topk_w_out));
+  if (shared) {
+    MOE_TRY(need_bf16(shared->w_gate));
+    MOE_TRY(need_bf16(shared->w_up));
+    MOE_TRY(need_bf16(shared->w_down));
+    if (shared->gate_logits) MOE_TRY(need_word(shared->gate_logits));
+  }
+  MOE_TRY(need_bf16(ws));
+  const ForwardLayout L = forward_layout(T, H, F, E, k, Fs);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+  char* base = static_cast<char*>(ws);
+  int32_t* hist = reinterpret_cast<int32_t*>(base + L.hist);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(base + L.ids);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(base + L.w);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  int32_t* row_token = reinterpret_cast<int32_t*>(base + L.row_token);
+  int32_t* row_dest = reinterpret_cast<int32_t*>(base + L.row_dest);
+  bf16_t* x_perm = reinterpret_cast<bf16_t*>(base + L.x_perm);
+  bf16_t* h = reinterpret_cast<bf16_t*>(base + L.h);
+  bf16_t* h_sh = reinterpret_cast<bf16_t*>(base + L.h_sh);
+  bf16_t* y = reinterpret_cast<bf16_t*>(base + L.y);
+  bf16_t* y_sh = reinterpret_cast<bf16_t*>(base + L.y_sh);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int M = static_cast<int>(A);
+
+  // 1. route + per-chunk histogram
+  MOE_TRY(hip_status(moe::launch_route(logits, T, E, k, ids, w, hist, s)));
+  // 2. permute: scan, stable rank, row maps, x_perm gather
+  MOE_TRY(hip_status(moe::launch_permute(x, ids, T, H, E, k, hist, offsets, row_token,
+                                         row_dest, x_perm, s)));
+  // 3. grouped gate/up + SwiGLU (shared expert as one more group over x)
+  moe::GemmProblem g1 = gateup_problem(x_perm, offsets, M, H, F, E, w_gate, w_up, h);
+  if (shared) {
+    g1.seg[1] = moe::GemmSegment{x, nullptr, shared->w_gate, shared->w_up, h_sh, 0, T, 1, H, Fs};
+    g1.nseg = 2;
+  }
+  MOE_TRY(hip_status(moe::launch_grouped_gemm(g1, s)));
+  // 4. grouped down (shared expert likewise)
+  moe::GemmProblem g2 = down_problem(h, offsets, M, F, H, E, w_down, y);
+  if (shared) {
+    g2.seg[1] = moe::GemmSegment{h_sh, nullptr, shared->w_down, nullptr, y_sh, 0, T, 1, Fs, H};
+    g2.nseg = 2;
+  }
+  MOE_TRY(hip_status(moe::launch_grouped_gemm(g2, s)));
+  // 5. combine (+ gated shared term)
+  return hip_status(moe::launch_combine(y, row_dest, w, T, H, k, shared ? y_sh : nullptr,
+                                        shared ? shared->gate_logits : nullptr, out, s));
+}
+
+}  // extern "C"

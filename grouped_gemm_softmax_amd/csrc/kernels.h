@@ -1,0 +1,64 @@
+// Internal launch interface of the MoE kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;
+
+constexpr int kMaxExperts = 1024;     // E limit of the ABI
+constexpr int kMaxTopK = 16;          // k limit of the ABI
+constexpr int kMaxChunkAssign = 256;  // assignments per routing/permute chunk
+constexpr int kPermuteSliceCols = 1024;  // x columns copied per permute block
+
+// --- routing and permutation (route_permute.hip) ---
+int route_chunk_tokens(int k);
+int route_num_chunks(int T, int k);
+hipError_t launch_route(const float* logits, int T, int E, int k,
+                        int32_t* topk_ids, float* topk_w,
+                        int32_t* hist /* nullable */, hipStream_t stream);
+hipError_t launch_hist(const int32_t* topk_ids, int T, int E, int k,
+                       int32_t* hist, hipStream_t stream);
+hipError_t launch_permute(const bf16_t* x, const int32_t* topk_ids, int T,
+                          int H, int E, int k, const int32_t* hist,
+                          int32_t* expert_offsets, int32_t* row_token,
+                          int32_t* row_dest, bf16_t* x_perm,
+                          hipStream_t stream);
+
+// --- grouped GEMM (grouped_gemm.hip) ---
+// A segment is a list of groups that share K, N and the weight layout.
+// Group g owns activation rows [offsets[g], offsets[g+1]) of `act`
+// (offsets == nullptr: one group, rows [0, rows)); its weights are
+// w0 + g*w_stride ([K][N], N contiguous), and w1 likewise when gated.
+struct GemmSegment {
+  const bf16_t* act;       // [rows, K]
+  const int32_t* offsets;  // device [ngroups+1] or nullptr
+  const bf16_t* w0;
+  const bf16_t* w1;        // gated only
+  bf16_t* out;             // [rows, N]
+  int64_t w_stride;        // elements between consecutive groups' weights
+  int rows;
+  int ngroups;
+  int K;
+  int N;
+};
+
+struct GemmProblem {
+  GemmSegment seg[2];
+  int nseg;
+  bool gated;      // out = silu(act w0) * (act w1), else act w0
+  int rows_hint;   // typical rows per group, picks the tile shape
+};
+
+hipError_t launch_grouped_gemm(const GemmProblem& prob, hipStream_t stream);
+
+// --- combine (combine.hip) ---
+hipError_t launch_combine(const bf16_t* y_perm, const int32_t* row_dest,
+                          const float* topk_w, int T, int H, int k,
+                          const bf16_t* y_shared /* [T,H] or null */,
+                          const float* shared_gate /* [T] or null */,
+                          bf16_t* out, hipStream_t stream);
+
+}  // namespace moe

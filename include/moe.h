@@ -1,0 +1,181 @@
+/*
+ * moe.h -- C ABI of the fused Mixture-of-Experts expert layer for AMD MI355X
+ * (gfx950). Library: grouped_gemm_softmax_amd/libmoe.so.
+ *
+ * The layer, per token t of x[T,H]:
+ *   1. route    : the k experts with the largest router logits (equal logits
+ *                 taken in ascending expert order) and routing weights
+ *                 w[t,j] = softmax over those k logits;
+ *   2. permute  : the T*k (token, slot) assignments sorted stably by expert
+ *                 into per-expert contiguous row blocks of x_perm;
+ *   3. gate/up  : per expert e, h = silu(x_perm_e W_gate[e]) * (x_perm_e W_up[e]),
+ *                 one grouped GEMM with the SwiGLU in its epilogue, so the gate
+ *                 and up products never reach memory;
+ *   4. down     : y_perm_e = h_e W_down[e], a second grouped GEMM;
+ *   5. combine  : out[t] = sum_j w[t,j] * y_perm[row of (t,j)]
+ *                 (+ s_t * shared_expert(x[t]) when a shared expert is given).
+ * Sources: the dispatch-kernel post "Triton-MoE-Dispatch-Kernel erreicht
+ * 131 % von Megablocks" (lumeric.app), summary paragraph (fused gate+up with
+ * SwiGLU, 5 launches per layer); "Triton MoE 核心擊敗 Megablocks" (setupai.cc),
+ * key points (block-scheduled grouped GEMM over variable expert batch sizes)
+ * and technical deep-dive (top-k routing inside the kernel); the DeepGEMM
+ * article (itsolotime.com), section 1.1 (dispatch -> linear1 -> SwiGLU ->
+ * linear2 -> combine) and section 3.1 (per-expert contiguous activations);
+ * the HPC-Ops article (ntfzh.com), FusedMoE paragraph (re-arrangement, grouped
+ * GEMM, weighted reduce).
+ *
+ * Conventions for every call:
+ *   - Tensors are row-major and contiguous. bf16 values are passed as their
+ *     16-bit patterns (moe_bf16). Weights: W_gate, W_up [E,H,F]; W_down [E,F,H].
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise. The
+ *     caller owns all memory; the library allocates no device memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *     enqueues work on it and returns without synchronising. Per-expert
+ *     counts never travel to the host.
+ *   - Arguments are validated on the host before anything is enqueued. On an
+ *     error nothing is enqueued and no output is touched; the call returns a
+ *     negative moe_status. MOE_ERR_HIP reports a failed kernel launch.
+ *   - Size limits: 0 <= T; 1 <= k <= min(E, 16); 1 <= E <= 1024;
+ *     H, F (and Fs) multiples of 8; T*k*max(H, F, Fs) < 2^31. T = 0 is a
+ *     successful no-op (then pointers are not inspected).
+ *   - Alignment: bf16 tensors and workspaces 16 bytes; fp32 and int32
+ *     arrays 4 bytes (MOE_ERR_MISALIGNED otherwise).
+ *   - Calls are re-entrant; the only cached state is per-device properties.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t moe_bf16; /* bf16 bit pattern (torch.bfloat16 storage) */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,         /* null pointer, negative or zero size */
+  MOE_ERR_UNSUPPORTED_SHAPE = -2,   /* outside the size limits above */
+  MOE_ERR_MISALIGNED = -3,          /* a pointer below its required alignment */
+  MOE_ERR_WORKSPACE_TOO_SMALL = -4, /* ws_bytes below the required size */
+  MOE_ERR_HIP = -5                  /* a HIP runtime call or launch failed */
+} moe_status;
+
+/* Optional always-on shared expert, added to every token's output. The
+ * struct itself is a HOST object; its pointers are device pointers.
+ * w_gate, w_up [H,Fs]; w_down [Fs,H]; gate_logits [T] fp32 or NULL.
+ * The shared term is s_t * y_sh[t] with s_t = 1 when gate_logits is NULL,
+ * else the logistic sigmoid 1/(1+exp(-gate_logits[t])). */
+typedef struct {
+  const moe_bf16* w_gate;
+  const moe_bf16* w_up;
+  const moe_bf16* w_down;
+  int32_t Fs;
+  const float* gate_logits;
+} moe_shared_expert;
+
+/* Text for a status code (a static host string; never NULL). */
+const char* moe_status_string(int status);
+
+/* Step 1, route. logits fp32 [T,E] (finite values) -> topk_ids int32 [T,k]
+ * (expert ids, largest logit first, equal logits in ascending expert order;
+ * -0.0 and +0.0 are equal) and topk_w fp32 [T,k] (softmax over the k chosen
+ * logits, fp32 arithmetic, max subtracted; sums to 1 up to rounding).
+ * Routing inside the kernel, with no host synchronisation, follows the
+ * Triton MoE page (setupai.cc), technical deep-dive. */
+int moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids,
+              float* topk_w, void* stream);
+
+/* Workspace needed by moe_permute (device bytes); 0 for invalid sizes. */
+size_t moe_permute_workspace_bytes(int T, int E, int k);
+
+/* Step 2, permute. topk_ids int32 [T,k] (each in [0,E), e.g. from moe_route)
+ * and x bf16 [T,H] ->
+ *   expert_offsets int32 [E+1]: offsets[e] = first row of expert e,
+ *                  offsets[E] = T*k (exclusive prefix of per-expert counts);
+ *   row_token int32 [T*k]: row p of x_perm holds token row_token[p];
+ *   row_dest  int32 [T*k]: (t,j) went to row row_dest[t*k+j];
+ *   x_perm    bf16 [T*k,H]: x_perm[p] = x[row_token[p]] (a bit copy).
+ * Within an expert's block rows are in ascending token order (a stable sort
+ * of the assignments in t-major, j-minor order); the layout is unpadded.
+ * ws: at least moe_permute_workspace_bytes(T,E,k) device bytes of scratch.
+ * Ids outside [0,E) are not checked on the device; they give unspecified
+ * (but in-bounds) results. Per-expert contiguous activations as in the
+ * DeepGEMM article (itsolotime.com), section 3.1; re-arrangement before the
+ * grouped GEMM as in the HPC-Ops article (ntfzh.com), FusedMoE paragraph. */
+int moe_permute(const moe_bf16* x, const int32_t* topk_ids, int T, int H,
+                int E, int k, int32_t* expert_offsets, int32_t* row_token,
+                int32_t* row_dest, moe_bf16* x_perm, void* ws,
+                size_t ws_bytes, void* stream);
+
+/* Step 3, grouped gate/up GEMM with SwiGLU epilogue. For every expert e and
+ * row p in [offsets[e], offsets[e+1]):
+ *   h[p,f] = bf16( silu(G) * U ),  G = sum_c x_perm[p,c] W_gate[e,c,f],
+ *   U = sum_c x_perm[p,c] W_up[e,c,f], fp32 accumulation,
+ *   silu(z) = z/(1+exp(-z)) in fp32, rounded to bf16 to nearest-even.
+ * x_perm bf16 [M,H]; expert_offsets int32 [E+1] on the device, non-decreasing
+ * from 0 to M (rows outside [0,M) are never read or written whatever the
+ * offsets hold); h bf16 [M,F] (caller-owned). G and U stay in registers.
+ * Fused gate+up so the SwiGLU input never reaches global memory: the
+ * dispatch-kernel post (lumeric.app), summary paragraph. */
+int moe_gateup_swiglu(const moe_bf16* x_perm, const int32_t* expert_offsets,
+                      int M, int H, int F, int E, const moe_bf16* w_gate,
+                      const moe_bf16* w_up, moe_bf16* h, void* stream);
+
+/* Step 4, grouped down GEMM. y_perm[p,c] = bf16( sum_f h[p,f] W_down[e,f,c] )
+ * for rows p of expert e; fp32 accumulation. h bf16 [M,F], y_perm bf16 [M,H],
+ * expert_offsets as in moe_gateup_swiglu. The down projection (linear2) is
+ * its own grouped GEMM as in the DeepGEMM article (itsolotime.com),
+ * section 1.1. */
+int moe_down(const moe_bf16* h, const int32_t* expert_offsets, int M, int F,
+             int H, int E, const moe_bf16* w_down, moe_bf16* y_perm,
+             void* stream);
+
+/* Steps 3+4: moe_gateup_swiglu into h (caller-owned [M,F]), then moe_down
+ * into y_perm [M,H]. Block-scheduled grouped GEMM over variable expert batch
+ * sizes: the Triton MoE page (setupai.cc), key points. */
+int moe_grouped_ffn(const moe_bf16* x_perm, const int32_t* expert_offsets,
+                    int M, int H, int F, int E, const moe_bf16* w_gate,
+                    const moe_bf16* w_up, const moe_bf16* w_down, moe_bf16* h,
+                    moe_bf16* y_perm, void* stream);
+
+/* Step 5, combine. out[t,c] = bf16( sum_{j<k} topk_w[t,j] * y_perm[row_dest[t,j], c] ),
+ * fp32 accumulation in ascending j. y_perm bf16 [T*k,H]; row_dest int32 [T,k]
+ * with values in [0,T*k) (as from moe_permute); topk_w fp32 [T,k];
+ * out bf16 [T,H]. The weighted reduce after the grouped GEMM: the HPC-Ops
+ * article (ntfzh.com), FusedMoE paragraph. */
+int moe_combine(const moe_bf16* y_perm, const int32_t* row_dest,
+                const float* topk_w, int T, int H, int k, moe_bf16* out,
+                void* stream);
+
+/* Workspace needed by moe_forward (device bytes); Fs = 0 without a shared
+ * expert; 0 for invalid sizes. */
+size_t moe_forward_workspace_bytes(int T, int H, int F, int E, int k, int Fs);
+
+/* The whole layer, steps 1-5, as five kernel launches on `stream` (the
+ * launch count of the dispatch-kernel post (lumeric.app), summary paragraph):
+ * route (+ per-chunk expert histogram), permute (scan + stable rank + row
+ * gather), grouped gate/up+SwiGLU, grouped down, combine. The shared expert,
+ * when given, is one more group of the two grouped GEMMs over all T tokens,
+ * and its gated output is added in the combine after the routed sum.
+ *   x bf16 [T,H]; logits fp32 [T,E]; out bf16 [T,H];
+ *   shared: HOST pointer to a moe_shared_expert, or NULL;
+ *   topk_ids_out int32 [T,k], topk_w_out fp32 [T,k]: optional device copies
+ *   of the routing result (NULL: kept in the workspace);
+ *   ws: at least moe_forward_workspace_bytes(...) device bytes of scratch.
+ * Results equal route -> permute -> grouped_ffn -> combine through the split
+ * calls, plus the shared term. */
+int moe_forward(const moe_bf16* x, const float* logits, int T, int H, int F,
+                int E, int k, const moe_bf16* w_gate, const moe_bf16* w_up,
+                const moe_bf16* w_down, const moe_shared_expert* shared,
+                moe_bf16* out, int32_t* topk_ids_out, float* topk_w_out,
+                void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

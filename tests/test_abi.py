@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/moe.h declares, reports workspace sizes, and rejects
+bad arguments with the documented status before enqueuing anything.
+
+Every call here fails validation (or has T == 0), so no kernel is launched;
+the fake pointer values are never dereferenced."""
+import ctypes
+
+import pytest
+
+from grouped_gemm_softmax_amd import binding as B
+
+OK, INVALID, SHAPE, MISALIGNED, WS_SMALL, HIP = 0, -1, -2, -3, -4, -5
+P = ctypes.c_void_p(0x10000)        # 16-byte aligned fake address (never read)
+Q = ctypes.c_void_p(0x10008)        # 8 mod 16: misaligned for bf16 tensors
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def test_library_exports_every_header_symbol(L):
+    names = B.header_symbols()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(B._SIGNATURES)
+
+
+def test_status_strings(L):
+    for s in (OK, INVALID, SHAPE, MISALIGNED, WS_SMALL, HIP):
+        txt = B.moe_status_string(s)
+        assert txt and txt != "unknown moe status"
+    assert B.moe_status_string(7) == "unknown moe status"
+
+
+def test_route_validation(L):
+    assert L.moe_route(P, 4, 8, 0, P, P, NULL) == INVALID          # k < 1
+    assert L.moe_route(P, 4, 8, 9, P, P, NULL) == SHAPE            # k > E
+    assert L.moe_route(P, 4, 2000, 2, P, P, NULL) == SHAPE         # E > 1024
+    assert L.moe_route(P, 4, 32, 17, P, P, NULL) == SHAPE          # k > 16
+    assert L.moe_route(P, -1, 8, 2, P, P, NULL) == INVALID         # T < 0
+    assert L.moe_route(NULL, 4, 8, 2, P, P, NULL) == INVALID       # null logits
+    assert L.moe_route(P, 4, 8, 2, ctypes.c_void_p(0x10002), P, NULL) == MISALIGNED
+    assert L.moe_route(NULL, 0, 8, 2, NULL, NULL, NULL) == OK      # T = 0: no-op
+
+
+def test_permute_validation(L):
+    ws = B.moe_permute_workspace_bytes(100, 8, 2)
+    assert ws > 0 and ws % 256 == 0
+    assert B.moe_permute_workspace_bytes(100, 8, 9) == 0
+    args = lambda x=P, xp=P, ws_bytes=ws, H=64: (x, P, 100, H, 8, 2, P, P, P, xp, P, ws_bytes, NULL)
+    assert L.moe_permute(*args(x=NULL)) == INVALID
+    assert L.moe_permute(*args(x=Q)) == MISALIGNED
+    assert L.moe_permute(*args(xp=Q)) == MISALIGNED
+    assert L.moe_permute(*args(H=60)) == SHAPE                     # H % 8 != 0
+    assert L.moe_permute(*args(ws_bytes=ws - 1)) == WS_SMALL
+    assert L.moe_permute(NULL, NULL, 0, 64, 8, 2, NULL, NULL, NULL, NULL, NULL, 0, NULL) == OK
+
+
+def test_ffn_validation(L):
+    assert L.moe_gateup_swiglu(P, P, 128, 64, 100, 8, P, P, P, NULL) == SHAPE    # F % 8
+    assert L.moe_gateup_swiglu(P, P, 128, 64, 96, 0, P, P, P, NULL) == INVALID   # E = 0
+    assert L.moe_gateup_swiglu(P, P, 128, 64, 96, 8, P, NULL, P, NULL) == INVALID
+    assert L.moe_gateup_swiglu(P, P, 128, 64, 96, 8, Q, P, P, NULL) == MISALIGNED
+    assert L.moe_down(P, P, 128, 96, 64, 8, P, Q, NULL) == MISALIGNED
+    assert L.moe_down(P, NULL, 128, 96, 64, 8, P, P, NULL) == INVALID
+    assert L.moe_down(P, P, 1 << 20, 4096, 4096, 8, P, P, NULL) == SHAPE        # > 2^31 elements
+    assert L.moe_grouped_ffn(P, P, 128, 64, 96, 8, P, P, NULL, P, P, NULL) == INVALID
+    assert L.moe_grouped_ffn(NULL, NULL, 0, 64, 96, 8, NULL, NULL, NULL, NULL, NULL, NULL) == OK
+
+
+def test_combine_validation(L):
+    assert L.moe_combine(P, P, P, 10, 64, 0, P, NULL) == INVALID
+    assert L.moe_combine(P, P, P, 10, 64, 17, P, NULL) == SHAPE
+    assert L.moe_combine(P, P, P, 10, 63, 2, P, NULL) == SHAPE
+    assert L.moe_combine(P, P, P, 10, 64, 2, Q, NULL) == MISALIGNED
+    assert L.moe_combine(NULL, NULL, NULL, 0, 64, 2, NULL, NULL) == OK
+
+
+def _fwd(L, T=32, H=64, F=96, E=8, k=2, x=P, ws=P, ws_bytes=None, shared=None, out=P):
+    if ws_bytes is None:
+        ws_bytes = B.moe_forward_workspace_bytes(T, H, F, E, k, shared.Fs if shared else 0)
+    return L.moe_forward(x, P, T, H, F, E, k, P, P, P,
+                         ctypes.byref(shared) if shared else None, out, NULL, NULL,
+                         ws, ws_bytes, NULL)
+
+
+def test_forward_validation(L):
+    assert _fwd(L, x=NULL) == INVALID
+    assert _fwd(L, out=Q) == MISALIGNED
+    assert _fwd(L, k=9) == SHAPE
+    assert _fwd(L, ws_bytes=16) == WS_SMALL
+    bad_shared = B.SharedExpert(0x10000, 0x10000, 0x10000, 20, None)   # Fs % 8 != 0
+    assert _fwd(L, shared=bad_shared, ws_bytes=1 << 40) == SHAPE
+    null_shared = B.SharedExpert(0x10000, None, 0x10000, 32, None)
+    assert _fwd(L, shared=null_shared, ws_bytes=1 << 40) == INVALID
+    assert L.moe_forward(NULL, NULL, 0, 64, 96, 8, 2, NULL, NULL, NULL, None, NULL,
+                         NULL, NULL, NULL, 0, NULL) == OK
+
+
+def _layout_model(T, H, F, E, k, Fs):
+    """Independent re-statement of the documented forward workspace layout."""
+    al = lambda v: (v + 255) // 256 * 256
+    A = T * k
+    chunk = 256 // k
+    nch = (T + chunk - 1) // chunk
+    parts = [nch * E * 4, A * 4, A * 4, (E + 1) * 4, A * 4, A * 4, A * H * 2,
+             A * F * 2, T * Fs * 2, A * H * 2, T * (H if Fs else 0) * 2]
+    return sum(al(p) for p in parts)
+
+
+@pytest.mark.parametrize("T,H,F,E,k,Fs", [(64, 256, 512, 8, 2, 0), (4096, 7168, 2048, 256, 8, 2048),
+                                          (16384, 2048, 1408, 60, 4, 5632), (1, 4096, 14336, 8, 2, 0)])
+def test_forward_workspace_bytes(T, H, F, E, k, Fs):
+    got = B.moe_forward_workspace_bytes(T, H, F, E, k, Fs)
+    assert got == _layout_model(T, H, F, E, k, Fs)
+    assert B.moe_forward_workspace_bytes(T, H, F, E, k, 3) == 0      # Fs % 8

@@ -1,0 +1,110 @@
+"""GPU parity of the whole layer (moe_forward) with shared experts, its exact
+invariants (determinism, power-of-two scaling, zero input, T = 0) and the
+empty/degenerate cases."""
+import numpy as np
+import pytest
+import torch
+
+from grouped_gemm_softmax_amd import binding as B
+from grouped_gemm_softmax_amd import synth
+from helpers import assert_close, gpu_bf16_f64, host_layer, say
+
+pytestmark = pytest.mark.gpu
+
+SHARED_CASES = {
+    "dsv3_like": (synth.small_config("d3", H=192, F=96, E=32, k=8, Fs=160, logits="zipf"), 70),
+    "qwen2_like_gated": (synth.small_config("q2", H=128, F=88, E=60, k=4, Fs=352,
+                                            shared_gated=True), 37),
+    "qwen2_like_large_batch": (synth.small_config("q2l", H=128, F=88, E=12, k=4, Fs=176,
+                                                  shared_gated=True), 400),
+}
+
+
+def _fwd(layer):
+    return B.moe_forward(layer.x, layer.logits, layer.cfg.k, layer.w_gate, layer.w_up,
+                         layer.w_down, shared=layer.shared)
+
+
+@pytest.mark.parametrize("name", sorted(SHARED_CASES))
+def test_forward_shared_expert(name, orc):
+    cfg, T = SHARED_CASES[name]
+    layer = synth.make_layer(cfg.name, T, seed=2, device="cuda", cfg=cfg)
+    d, sh = host_layer(layer)
+    ref = orc.forward(d["x"], d["logits"], cfg.k, d["wg"], d["wu"], d["wd"], shared=sh,
+                      keep_intermediates=False)
+    say("moe_forward+shared", name, T)
+    out = _fwd(layer)
+    torch.cuda.synchronize()
+    assert_close(gpu_bf16_f64(out), ref["out"], f"out[{name}]")
+
+
+def _layer(T=96, shared=True):
+    cfg = synth.small_config("inv", H=136, F=120, E=7, k=3, Fs=64 if shared else 0,
+                             shared_gated=shared)
+    return synth.make_layer("inv", T, seed=3, device="cuda", cfg=cfg)
+
+
+def _double(t):
+    return (t.float() * 2).to(torch.bfloat16)     # exact for normal bf16 values
+
+
+def test_deterministic_bitwise():
+    layer = _layer()
+    say("determinism")
+    a = _fwd(layer).clone()
+    b = _fwd(layer)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_power_of_two_scaling_is_exact():
+    """out(2 W_down) = 2 out and out(2 W_up) = 2 out bit for bit: scaling by
+    two is exact at every fp32 and bf16 rounding of the path."""
+    layer = _layer(shared=False)
+    say("scaling")
+    base = _fwd(layer).float()
+    layer.w_down = _double(layer.w_down)
+    out_d = _fwd(layer).float()
+    layer.w_down = (layer.w_down.float() / 2).to(torch.bfloat16)
+    layer.w_up = _double(layer.w_up)
+    out_u = _fwd(layer).float()
+    torch.cuda.synchronize()
+    assert torch.equal(out_d, 2 * base)
+    assert torch.equal(out_u, 2 * base)
+
+
+def test_zero_input_gives_zero():
+    layer = _layer()
+    layer.x.zero_()
+    say("zero input")
+    out = _fwd(layer)
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all()
+
+
+def test_empty_batch_is_noop():
+    cfg = synth.small_config("e0", H=64, F=64, E=4, k=2)
+    layer = synth.make_layer("e0", 0, seed=0, device="cuda", cfg=cfg)
+    say("T=0")
+    out = _fwd(layer)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
+
+
+def test_shared_gate_zero_logit_is_half(orc):
+    """g_t = 0 gives s_t = 1/2 exactly; with routed W_down zeroed the output is
+    half the shared expert's FFN."""
+    layer = _layer(T=40)
+    layer.shared["gate_logits"].zero_()
+    layer.w_down.zero_()
+    d, sh = host_layer(layer)
+    ref = orc.forward(d["x"], d["logits"], layer.cfg.k, d["wg"], d["wu"], d["wd"], shared=sh,
+                      keep_intermediates=False)
+    sh_one = dict(sh, gate_logits=None)
+    ref_one = orc.forward(d["x"], d["logits"], layer.cfg.k, d["wg"], d["wu"], d["wd"],
+                          shared=sh_one, keep_intermediates=False)
+    assert np.array_equal(ref["out"], 0.5 * ref_one["out"])
+    say("shared gate 0")
+    out = _fwd(layer)
+    torch.cuda.synchronize()
+    assert_close(gpu_bf16_f64(out), ref["out"], "out[gate=0]")
