@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Throughput of the fused MoE expert layer on one MI355X.
+
+Workload: the Mixtral-8x7B-shaped MoE layer (H=4096, F=14336, E=8 experts,
+top-2, SwiGLU experts, bf16) at a batch of T=32 tokens, router logits
+~ N(0,1), inputs already resident in HBM. A step is one moe_forward call
+(route -> permute -> gate/up+SwiGLU -> down -> combine, 5 launches).
+
+Metric: MoE-layer HBM GB/s (algorithmic bytes / time), with TFLOP/s and the
+roofline fractions beside it. `roofline` describes the dominant kernel (the
+gate/up+SwiGLU grouped GEMM), timed with HIP events on its launch stream.
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the same
+workload. `sweep` repeats the measurement at the other batch sizes of the
+same layer shape (T = 1, 128, 512).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer TFLOP/s and HBM GB/s (roofline %) vs tokens T, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="mixtral")
+    ap.add_argument("--T", type=int, default=32)
+    ap.add_argument("--sweep", default="1,128,512",
+                    help="other batch sizes to measure ('' to skip)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=32,
+                    help="tokens in the oracle's timed sample")
+    return ap.parse_args()
+
+
+def work_model(cfg, T, counts):
+    """Algorithmic FLOPs and HBM bytes of one forward, per kernel.
+    counts: rows per routed expert (E_touched = experts with rows)."""
+    H, F, E, k, Fs = cfg.H, cfg.F, cfg.E, cfg.k, cfg.Fs
+    A = T * k
+    Et = int((counts > 0).sum())
+    m = {}
+    m["route"] = dict(bytes=4 * T * E + 8 * A, flops=0)
+    m["permute"] = dict(bytes=4 * A + 2 * T * H + 2 * A * H + 8 * A, flops=0)
+    g1 = 4 * H * F * Et + 2 * A * H + 2 * A * F
+    g1f = 4 * A * H * F
+    g2 = 2 * F * H * Et + 2 * A * F + 2 * A * H
+    g2f = 2 * A * F * H
+    cb = 2 * A * H + 8 * A + 2 * T * H
+    if Fs:
+        g1 += 4 * H * Fs + 2 * T * H + 2 * T * Fs
+        g1f += 4 * T * H * Fs
+        g2 += 2 * Fs * H + 2 * T * Fs + 2 * T * H
+        g2f += 2 * T * Fs * H
+        cb += 2 * T * H + (4 * T if cfg.shared_gated else 0)
+    m["gateup_swiglu"] = dict(bytes=g1, flops=g1f)
+    m["down"] = dict(bytes=g2, flops=g2f)
+    m["combine"] = dict(bytes=cb, flops=0)
+    total_b = sum(v["bytes"] for v in m.values())
+    total_f = sum(v["flops"] for v in m.values())
+    return total_b, total_f, m, Et
+
+
+def roof(bytes_, flops, ms):
+    s = ms * 1e-3
+    gbs = bytes_ / s / 1e9
+    tfl = flops / s / 1e12
+    t_hbm = bytes_ / (PEAK_HBM_GBS * 1e9)
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    return dict(gbs=gbs, tflops=tfl, hbm_frac=gbs / PEAK_HBM_GBS,
+                mfma_frac=tfl / PEAK_BF16_TFLOPS, bound=bound,
+                roofline_frac=max(t_hbm, t_mfma) / s)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from grouped_gemm_softmax_amd import binding as B
+    from grouped_gemm_softmax_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.CONFIGS[args.config]
+    stream = torch.cuda.current_stream()
+
+    def layer_for(T, weights_from=None):
+        if weights_from is None:
+            return synth.make_layer(cfg.name, T, seed=args.seed, device=dev)
+        lay = synth.make_layer(cfg.name, T, seed=args.seed, device=dev, with_weights=False)
+        lay.w_gate, lay.w_up, lay.w_down = (weights_from.w_gate, weights_from.w_up,
+                                            weights_from.w_down)
+        if lay.shared is not None:
+            lay.shared = dict(weights_from.shared, gate_logits=lay.shared["gate_logits"])
+        return lay
+
+    def measure(layer, steps, warmup):
+        T, H, F, E, k = layer.T, cfg.H, cfg.F, cfg.E, cfg.k
+        Fs = cfg.Fs
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        ws = torch.empty(B.moe_forward_workspace_bytes(T, H, F, E, k, Fs),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            B.moe_forward(layer.x, layer.logits, k, layer.w_gate, layer.w_up,
+                          layer.w_down, shared=layer.shared, out=out,
+                          topk_ids=ids, topk_w=w, ws=ws, stream=stream)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        counts = torch.bincount(ids.flatten().long(), minlength=E).cpu().numpy()
+        return ms, counts
+
+    def time_gateup(layer, steps):
+        """Average duration of the gate/up+SwiGLU grouped GEMM alone, with the
+        same inputs and launch configuration as inside moe_forward."""
+        k = cfg.k
+        ids, w = B.moe_route(layer.logits, k, stream=stream)
+        off, rt, rd, xp = B.moe_permute(layer.x, ids, cfg.E, stream=stream)
+        h = torch.empty((xp.shape[0], cfg.F), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            B.moe_gateup_swiglu(xp, off, layer.w_gate, layer.w_up, h=h, stream=stream)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            B.moe_gateup_swiglu(xp, off, layer.w_gate, layer.w_up, h=h, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    # ---- headline workload ----
+    layer = layer_for(args.T)
+    torch.cuda.synchronize()
+    ms, counts = measure(layer, args.steps, args.warmup)
+    total_b, total_f, per_kernel, Et = work_model(cfg, args.T, counts)
+    r = roof(total_b, total_f, ms)
+
+    g1_ms = time_gateup(layer, max(args.steps, 20))
+    g1 = per_kernel["gateup_swiglu"]
+    g1r = roof(g1["bytes"], g1["flops"], g1_ms)
+    if g1r["bound"] == "hbm":
+        roofline = dict(bound="hbm", achieved=round(g1r["gbs"], 1), peak=PEAK_HBM_GBS,
+                        unit="GB/s", frac=round(g1r["gbs"] / PEAK_HBM_GBS, 4), traffic=None)
+    else:
+        roofline = dict(bound="mfma", achieved=round(g1r["tflops"], 1), peak=PEAK_BF16_TFLOPS,
+                        unit="TFLOP/s", frac=round(g1r["tflops"] / PEAK_BF16_TFLOPS, 4),
+                        traffic=None)
+    roofline.update(kernel="grouped_gemm_kernel (gate/up + SwiGLU)",
+                    kernel_ms=round(g1_ms, 5),
+                    alg_bytes=g1["bytes"], alg_flops=g1["flops"])
+
+    # ---- the other batch sizes of the same layer shape ----
+    sweep = []
+    for tok in [int(s) for s in args.sweep.split(",") if s.strip()]:
+        if tok == args.T:
+            continue
+        lay = layer_for(tok, weights_from=layer)
+        ms_t, counts_t = measure(lay, max(10, args.steps // 2), 5)
+        b_t, f_t, _, et_t = work_model(cfg, tok, counts_t)
+        rr = roof(b_t, f_t, ms_t)
+        sweep.append(dict(T=tok, ms_per_step=round(ms_t, 5), GBs=round(rr["gbs"], 1),
+                          TFLOPs=round(rr["tflops"], 2), hbm_frac=round(rr["hbm_frac"], 4),
+                          mfma_frac=round(rr["mfma_frac"], 4), bound=rr["bound"],
+                          roofline_frac=round(rr["roofline_frac"], 4),
+                          experts_touched=et_t))
+        del lay
+
+    # ---- CPU oracle on a bounded sample of the headline workload ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        n = min(args.cpu_tokens, args.T)
+        x = synth.u16(layer.x[:n])
+        lg = synth.f32(layer.logits[:n])
+        wg, wu, wd = synth.u16(layer.w_gate), synth.u16(layer.w_up), synth.u16(layer.w_down)
+        t0 = time.perf_counter()
+        oracle.forward(x, lg, cfg.k, wg, wu, wd, keep_intermediates=False)
+        t_cpu = time.perf_counter() - t0
+        t_full = t_cpu * args.T / n        # the oracle's cost is linear in tokens
+        cpu = dict(value=round(total_b / t_full / 1e9, 3), unit="GB/s",
+                   cores=oracle.num_threads(), kind="oracle",
+                   sample=f"first {n} of {args.T} tokens, whole layer (oracle.forward, fp64), "
+                          f"{t_cpu:.2f} s; scaled linearly to the {args.T}-token step",
+                   seconds_sample=round(t_cpu, 3))
+
+    line = {
+        "metric": METRIC,
+        "value": round(r["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; x~N(0,1), weights~N(0,0.02), logits~N(0,1))",
+        "config": {"workload": f"{cfg.desc}: T={args.T}, H={cfg.H}, F={cfg.F}, E={cfg.E}, "
+                               f"top-{cfg.k}, bf16",
+                   "T": args.T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "k": cfg.k,
+                   "Fs": cfg.Fs, "experts_touched": Et, "parallelism": "none (1 GPU)"},
+        "TFLOPs": round(r["tflops"], 3),
+        "hbm_frac": round(r["hbm_frac"], 4),
+        "mfma_frac": round(r["mfma_frac"], 4),
+        "layer_bound": r["bound"],
+        "layer_roofline_frac": round(r["roofline_frac"], 4),
+        "alg_bytes": total_b,
+        "alg_flops": total_f,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -61,7 +61,10 @@ size_t permute_ws_bytes(int T, int E, int k) {
 
 // Workspace layout of moe_forward (each piece 256-byte aligned from ws):
 // [hist | topk_ids | topk_w | offsets | row_token | row_dest | x_perm | h |
-//  h_shared | y_perm | y_shared]
+//  h_shared | y_perm | y_shared]. y_perm and y_shared are fp32 here: the down
+// projection's output goes to the combine without a bf16 rounding, whose
+// error (half an ulp of |y|, up to ~0.03 at |y| ~ 10) would otherwise reach
+// outputs where the k expert terms cancel.
 struct ForwardLayout {
   size_t hist, ids, w, offsets, row_token, row_dest, x_perm, h, h_sh, y, y_sh, total;
 };
@@ -80,8 +83,8 @@ ForwardLayout forward_layout(int T, int H, int F, int E, int k, int Fs) {
   L.x_perm = take(A * H * 2);
   L.h = take(A * F * 2);
   L.h_sh = take(static_cast<size_t>(T) * (Fs > 0 ? Fs : 0) * 2);
-  L.y = take(A * H * 2);
-  L.y_sh = take(static_cast<size_t>(T) * (Fs > 0 ? H : 0) * 2);
+  L.y = take(A * H * 4);                                       // fp32
+  L.y_sh = take(static_cast<size_t>(T) * (Fs > 0 ? H : 0) * 4);  // fp32
   L.total = o;
   return L;
 }
@@ -99,7 +102,7 @@ moe::GemmProblem gateup_problem(const bf16_t* x_perm, const int32_t* offsets, in
 }
 
 moe::GemmProblem down_problem(const bf16_t* h, const int32_t* offsets, int M, int F,
-                              int H, int E, const bf16_t* wd, bf16_t* y) {
+                              int H, int E, const bf16_t* wd, void* y) {
   moe::GemmProblem p{};
   p.seg[0] = moe::GemmSegment{h, offsets, wd, nullptr, y,
                               static_cast<int64_t>(F) * H, M, E, F, H};
@@ -225,7 +228,7 @@ int moe_combine(const moe_bf16* y_perm, const int32_t* row_dest, const float* to
   MOE_TRY(need_word(row_dest));
   MOE_TRY(need_word(topk_w));
   MOE_TRY(need_bf16(out));
-  return hip_status(moe::launch_combine(y_perm, row_dest, topk_w, T, H, k, nullptr,
+  return hip_status(moe::launch_combine(y_perm, false, row_dest, topk_w, T, H, k, nullptr,
                                         nullptr, out, static_cast<hipStream_t>(stream)));
 }
 
@@ -279,8 +282,8 @@ int moe_forward(const moe_bf16* x, const float* logits, int T, int H, int F, int
   bf16_t* x_perm = reinterpret_cast<bf16_t*>(base + L.x_perm);
   bf16_t* h = reinterpret_cast<bf16_t*>(base + L.h);
   bf16_t* h_sh = reinterpret_cast<bf16_t*>(base + L.h_sh);
-  bf16_t* y = reinterpret_cast<bf16_t*>(base + L.y);
-  bf16_t* y_sh = reinterpret_cast<bf16_t*>(base + L.y_sh);
+  float* y = reinterpret_cast<float*>(base + L.y);
+  float* y_sh = reinterpret_cast<float*>(base + L.y_sh);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int M = static_cast<int>(A);
 
@@ -298,13 +301,15 @@ int moe_forward(const moe_bf16* x, const float* logits, int T, int H, int F, int
   MOE_TRY(hip_status(moe::launch_grouped_gemm(g1, s)));
   // 4. grouped down (shared expert likewise)
   moe::GemmProblem g2 = down_problem(h, offsets, M, F, H, E, w_down, y);
+  g2.out_f32 = true;
   if (shared) {
     g2.seg[1] = moe::GemmSegment{h_sh, nullptr, shared->w_down, nullptr, y_sh, 0, T, 1, Fs, H};
     g2.nseg = 2;
   }
   MOE_TRY(hip_status(moe::launch_grouped_gemm(g2, s)));
   // 5. combine (+ gated shared term)
-  return hip_status(moe::launch_combine(y, row_dest, w, T, H, k, shared ? y_sh : nullptr,
+  return hip_status(moe::launch_combine(y, true, row_dest, w, T, H, k,
+                                        shared ? y_sh : nullptr,
                                         shared ? shared->gate_logits : nullptr, out, s));
 }
 

@@ -2,6 +2,8 @@
 //   out[t,c] = bf16( sum_{j<k} w[t,j] * y_perm[row_dest[t,j], c]
 //                    + s_t * y_shared[t,c] )
 // with fp32 accumulation in ascending j and the shared term added last.
+// y_perm and y_shared are bf16 (the split ABI) or fp32 (inside the fused
+// layer, where the down projection's output skips the bf16 rounding).
 // Semantically a scatter-add of the weighted expert rows back to their
 // tokens; it is computed as a gather through the inverse map row_dest, so no
 // floating-point atomics are used and the result is deterministic. The
@@ -18,10 +20,28 @@ namespace {
 
 constexpr int kCombineThreads = 256;
 
+// 8 consecutive values of a row as fp32.
+__device__ __forceinline__ void load8(const bf16_t* p, float v[8]) {
+  const uint4 q = *reinterpret_cast<const uint4*>(p);
+  const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(static_cast<bf16_t>(u[i] & 0xffffu));
+    v[2 * i + 1] = bf16_to_f32(static_cast<bf16_t>(u[i] >> 16));
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <typename YT>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
-    const bf16_t* __restrict__ y_perm, const int32_t* __restrict__ row_dest,
+    const YT* __restrict__ y_perm, const int32_t* __restrict__ row_dest,
     const float* __restrict__ topk_w, int T, int H, int k,
-    const bf16_t* __restrict__ y_shared, const float* __restrict__ shared_gate,
+    const YT* __restrict__ y_shared, const float* __restrict__ shared_gate,
     bf16_t* __restrict__ out) {
   const int t = blockIdx.x;
   __shared__ int s_row[kMaxTopK];
@@ -38,26 +58,17 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   if (y_shared && shared_gate) s = 1.0f / (1.0f + expf(-shared_gate[t]));
   for (int c = threadIdx.x * 8; c < H; c += kCombineThreads * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float v[8];
     for (int j = 0; j < k; ++j) {
-      const uint4 v = *reinterpret_cast<const uint4*>(
-          y_perm + static_cast<int64_t>(s_row[j]) * H + c);
+      load8(y_perm + static_cast<int64_t>(s_row[j]) * H + c, v);
       const float w = s_w[j];
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += w * bf16_to_f32(static_cast<bf16_t>(u[q] & 0xffffu));
-        acc[2 * q + 1] += w * bf16_to_f32(static_cast<bf16_t>(u[q] >> 16));
-      }
+      for (int q = 0; q < 8; ++q) acc[q] += w * v[q];
     }
     if (y_shared) {
-      const uint4 v = *reinterpret_cast<const uint4*>(
-          y_shared + static_cast<int64_t>(t) * H + c);
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      load8(y_shared + static_cast<int64_t>(t) * H + c, v);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += s * bf16_to_f32(static_cast<bf16_t>(u[q] & 0xffffu));
-        acc[2 * q + 1] += s * bf16_to_f32(static_cast<bf16_t>(u[q] >> 16));
-      }
+      for (int q = 0; q < 8; ++q) acc[q] += s * v[q];
     }
     uint4 o;
     o.x = pack_bf16x2(acc[0], acc[1]);
@@ -70,14 +81,19 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 
 }  // namespace
 
-hipError_t launch_combine(const bf16_t* y_perm, const int32_t* row_dest,
+hipError_t launch_combine(const void* y_perm, bool y_f32, const int32_t* row_dest,
                           const float* topk_w, int T, int H, int k,
-                          const bf16_t* y_shared, const float* shared_gate,
+                          const void* y_shared, const float* shared_gate,
                           bf16_t* out, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(kCombineThreads), 0, stream,
-                     y_perm, row_dest, topk_w, T, H, k, y_shared, shared_gate,
-                     out);
+  if (y_f32)
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(kCombineThreads), 0, stream,
+                       static_cast<const float*>(y_perm), row_dest, topk_w, T, H, k,
+                       static_cast<const float*>(y_shared), shared_gate, out);
+  else
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(kCombineThreads), 0, stream,
+                       static_cast<const bf16_t*>(y_perm), row_dest, topk_w, T, H, k,
+                       static_cast<const bf16_t*>(y_shared), shared_gate, out);
   return hipGetLastError();
 }
 

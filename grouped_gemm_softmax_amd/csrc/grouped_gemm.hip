@@ -3,7 +3,9 @@
 // One launch computes, for every group g (an expert, or the shared expert),
 //   out[rows of g] = epilogue( act[rows of g] * W[g] ),
 // where W[g] is [K][N] with N contiguous and the epilogue is either a plain
-// bf16 store (down projection) or, in the gated form, SwiGLU over two weight
+// store (bf16, or fp32 for the fused layer's down projection, whose output
+// feeds the combine without a bf16 rounding) or, in the gated form, SwiGLU
+// over two weight
 // matrices: out = silu(act*W_gate) * (act*W_up). In the gated form the gate
 // and up products only ever live in accumulator registers, so the SwiGLU
 // input never reaches memory (the dispatch-kernel post (lumeric.app),
@@ -108,7 +110,14 @@ __device__ __forceinline__ GroupView group_view(const GemmProblem& p, int g) {
   return v;
 }
 
-template <class C>
+__device__ __forceinline__ void store4(bf16_t* p, const float v[4]) {
+  *reinterpret_cast<uint2*>(p) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+__device__ __forceinline__ void store4(float* p, const float v[4]) {
+  *reinterpret_cast<float4*>(p) = float4{v[0], v[1], v[2], v[3]};
+}
+
+template <class C, typename OutT>
 __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem prob) {
   __shared__ __attribute__((aligned(16))) bf16_t sW[C::LDS_W];
   __shared__ __attribute__((aligned(16))) bf16_t sX[C::LDS_X];
@@ -282,7 +291,8 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
     }
 
     // ---- epilogue: lane holds columns 4*g16..+3 of one token per block ----
-    bf16_t* __restrict__ out = S.out;
+    // (bf16 stores round to nearest even; fp32 stores keep the accumulator)
+    OutT* __restrict__ out = static_cast<OutT*>(S.out);
 #pragma unroll
     for (int fi = 0; fi < C::FF; ++fi)
 #pragma unroll
@@ -301,8 +311,7 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
               v[r] = acc[0][fi][ti][r];
             }
           }
-          const uint2 packed = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          *reinterpret_cast<uint2*>(out + static_cast<int64_t>(row_base + tok) * N + f) = packed;
+          store4(out + static_cast<int64_t>(row_base + tok) * N + f, v);
         }
       }
   }
@@ -329,7 +338,7 @@ int device_cu_count() {
   return cus[dev];
 }
 
-template <class C>
+template <class C, typename OutT>
 int blocks_per_cu() {
   static int cached[64] = {0};
   int dev = 0;
@@ -337,14 +346,14 @@ int blocks_per_cu() {
   if (cached[dev] == 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(grouped_gemm_kernel<C>), C::kThreads, 0) != hipSuccess || n <= 0)
+            &n, reinterpret_cast<const void*>(grouped_gemm_kernel<C, OutT>), C::kThreads, 0) != hipSuccess || n <= 0)
       n = 1;
     cached[dev] = n;
   }
   return cached[dev];
 }
 
-template <class C>
+template <class C, typename OutT>
 hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   // upper bound on items: every group may leave one partial M-tile
   int64_t bound = 0;
@@ -354,10 +363,10 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
     bound += mt * ((S.N + C::BF - 1) / C::BF);
   }
   if (bound <= 0) return hipSuccess;
-  int64_t grid = static_cast<int64_t>(device_cu_count()) * blocks_per_cu<C>();
+  int64_t grid = static_cast<int64_t>(device_cu_count()) * blocks_per_cu<C, OutT>();
   if (bound < grid) grid = bound;
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL(grouped_gemm_kernel<C>, dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((grouped_gemm_kernel<C, OutT>), dim3(static_cast<unsigned>(grid)),
                      dim3(C::kThreads), 0, stream, p);
   return hipGetLastError();
 }
@@ -367,8 +376,13 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
   const bool large = p.rows_hint >= 64;
   if (p.gated)
-    return large ? launch_cfg<GateUpLarge>(p, stream) : launch_cfg<GateUpSmall>(p, stream);
-  return large ? launch_cfg<DownLarge>(p, stream) : launch_cfg<DownSmall>(p, stream);
+    return large ? launch_cfg<GateUpLarge, bf16_t>(p, stream)
+                 : launch_cfg<GateUpSmall, bf16_t>(p, stream);
+  if (p.out_f32)
+    return large ? launch_cfg<DownLarge, float>(p, stream)
+                 : launch_cfg<DownSmall, float>(p, stream);
+  return large ? launch_cfg<DownLarge, bf16_t>(p, stream)
+               : launch_cfg<DownSmall, bf16_t>(p, stream);
 }
 
 }  // namespace moe

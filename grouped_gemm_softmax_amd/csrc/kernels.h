@@ -37,7 +37,7 @@ struct GemmSegment {
   const int32_t* offsets;  // device [ngroups+1] or nullptr
   const bf16_t* w0;
   const bf16_t* w1;        // gated only
-  bf16_t* out;             // [rows, N]
+  void* out;               // [rows, N], bf16 or fp32 (GemmProblem::out_f32)
   int64_t w_stride;        // elements between consecutive groups' weights
   int rows;
   int ngroups;
@@ -49,15 +49,17 @@ struct GemmProblem {
   GemmSegment seg[2];
   int nseg;
   bool gated;      // out = silu(act w0) * (act w1), else act w0
+  bool out_f32;    // store fp32 instead of bf16 (down projection only)
   int rows_hint;   // typical rows per group, picks the tile shape
 };
 
 hipError_t launch_grouped_gemm(const GemmProblem& prob, hipStream_t stream);
 
 // --- combine (combine.hip) ---
-hipError_t launch_combine(const bf16_t* y_perm, const int32_t* row_dest,
+// y_perm/y_shared hold bf16 values (y_f32 == false) or fp32 values.
+hipError_t launch_combine(const void* y_perm, bool y_f32, const int32_t* row_dest,
                           const float* topk_w, int T, int H, int k,
-                          const bf16_t* y_shared /* [T,H] or null */,
+                          const void* y_shared /* [T,H] or null */,
                           const float* shared_gate /* [T] or null */,
                           bf16_t* out, hipStream_t stream);
 

@@ -163,12 +163,21 @@ class Layer:
 
 def make_layer(name: str, T: int, seed: int = 0, device="cpu",
                logits_kind: Optional[str] = None, with_shared: bool = True,
-               cfg: Optional[LayerConfig] = None) -> Layer:
-    """Draw one layer's inputs. `cfg` overrides the named config's shapes."""
+               cfg: Optional[LayerConfig] = None, with_weights: bool = True) -> Layer:
+    """Draw one layer's inputs. `cfg` overrides the named config's shapes.
+    with_weights=False draws only the per-batch tensors (x, logits, gate
+    logits) and leaves the weight fields None, for reuse of drawn weights
+    (they do not depend on T)."""
     cfg = cfg or CONFIGS[name]
     H, F, E = cfg.H, cfg.F, cfg.E
     x = randn_bf16((T, H), 1.0, device, cfg.name, T, seed, "x")
     logits = router_logits(cfg, T, seed, device, logits_kind)
+    if not with_weights:
+        shared = None
+        if with_shared and cfg.Fs > 0:
+            shared = dict(w_gate=None, w_up=None, w_down=None,
+                          gate_logits=shared_gate_logits(cfg, T, seed, device))
+        return Layer(cfg, T, seed, x, logits, None, None, None, shared)
     wg = expert_weights((H, F), E, WEIGHT_STD, device, cfg.name, seed, "w_gate")
     wu = expert_weights((H, F), E, WEIGHT_STD, device, cfg.name, seed, "w_up")
     wd = expert_weights((F, H), E, WEIGHT_STD, device, cfg.name, seed, "w_down")
@@ -179,10 +188,16 @@ def make_layer(name: str, T: int, seed: int = 0, device="cpu",
             w_gate=randn_bf16((H, Fs), WEIGHT_STD, device, cfg.name, seed, "ws_gate"),
             w_up=randn_bf16((H, Fs), WEIGHT_STD, device, cfg.name, seed, "ws_up"),
             w_down=randn_bf16((Fs, H), WEIGHT_STD, device, cfg.name, seed, "ws_down"),
-            gate_logits=(torch.randn((T,), generator=_gen(device, cfg.name, T, seed, "gate"),
-                                     device=device) if cfg.shared_gated else None),
+            gate_logits=shared_gate_logits(cfg, T, seed, device),
         )
     return Layer(cfg, T, seed, x, logits, wg, wu, wd, shared)
+
+
+def shared_gate_logits(cfg: LayerConfig, T: int, seed: int, device) -> Optional[torch.Tensor]:
+    """fp32 [T] gate logits of a sigmoid-gated shared expert, else None."""
+    if not (cfg.Fs > 0 and cfg.shared_gated):
+        return None
+    return torch.randn((T,), generator=_gen(device, cfg.name, T, seed, "gate"), device=device)
 
 
 def small_config(name: str = "small", H=128, F=192, E=6, k=2, Fs=0,

@@ -108,7 +108,7 @@ def _layout_model(T, H, F, E, k, Fs):
     chunk = 256 // k
     nch = (T + chunk - 1) // chunk
     parts = [nch * E * 4, A * 4, A * 4, (E + 1) * 4, A * 4, A * 4, A * H * 2,
-             A * F * 2, T * Fs * 2, A * H * 2, T * (H if Fs else 0) * 2]
+             A * F * 2, T * Fs * 2, A * H * 4, T * (H if Fs else 0) * 4]
     return sum(al(p) for p in parts)
 
 
