@@ -67,11 +67,29 @@ size_t permute_ws_bytes(int T, int E, int k) {
 // outputs where the k expert terms cancel.
 struct ForwardLayout {
   size_t hist, ids, w, offsets, row_token, row_dest, x_perm, h, h_sh, y, y_sh, total;
+  int ksplit;  // K-slices of the down projection (y and y_shared hold that many)
 };
 
-ForwardLayout forward_layout(int T, int H, int F, int E, int k, int Fs) {
+moe::GemmProblem down_problem(const bf16_t* h, const int32_t* offsets, int M, int F,
+                              int H, int E, const bf16_t* wd, void* y);
+
+// The fused layer's down projection (routed + optional shared segment) with
+// fp32 output; pointers may be null when only the shape matters.
+moe::GemmProblem forward_down_problem(int T, int H, int F, int E, int k, int Fs) {
+  moe::GemmProblem g2 = down_problem(nullptr, nullptr, T * k, F, H, E, nullptr, nullptr);
+  g2.out_f32 = true;
+  if (Fs > 0) {
+    g2.seg[1] = moe::GemmSegment{nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, T, 1, Fs, H};
+    g2.nseg = 2;
+  }
+  return g2;
+}
+
+ForwardLayout forward_layout(int T, int H, int F, int E, int k, int Fs, int cus) {
   ForwardLayout L;
+  L.ksplit = moe::grouped_gemm_ksplit_hint(forward_down_problem(T, H, F, E, k, Fs), cus);
   const size_t A = static_cast<size_t>(T) * k;
+  const size_t S = static_cast<size_t>(L.ksplit);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
   L.hist = take(static_cast<size_t>(moe::route_num_chunks(T, k)) * E * 4);
@@ -83,8 +101,8 @@ ForwardLayout forward_layout(int T, int H, int F, int E, int k, int Fs) {
   L.x_perm = take(A * H * 2);
   L.h = take(A * F * 2);
   L.h_sh = take(static_cast<size_t>(T) * (Fs > 0 ? Fs : 0) * 2);
-  L.y = take(A * H * 4);                                       // fp32
-  L.y_sh = take(static_cast<size_t>(T) * (Fs > 0 ? H : 0) * 4);  // fp32
+  L.y = take(S * A * H * 4);                                       // fp32
+  L.y_sh = take(S * static_cast<size_t>(T) * (Fs > 0 ? H : 0) * 4);  // fp32
   L.total = o;
   return L;
 }
@@ -94,10 +112,11 @@ moe::GemmProblem gateup_problem(const bf16_t* x_perm, const int32_t* offsets, in
                                 const bf16_t* wu, bf16_t* h) {
   moe::GemmProblem p{};
   p.seg[0] = moe::GemmSegment{x_perm, offsets, wg, wu, h,
-                              static_cast<int64_t>(H) * F, M, E, H, F};
+                              static_cast<int64_t>(H) * F, 0, M, E, H, F};
   p.nseg = 1;
   p.gated = true;
   p.rows_hint = M / E;
+  p.ksplit = 1;
   return p;
 }
 
@@ -105,10 +124,11 @@ moe::GemmProblem down_problem(const bf16_t* h, const int32_t* offsets, int M, in
                               int H, int E, const bf16_t* wd, void* y) {
   moe::GemmProblem p{};
   p.seg[0] = moe::GemmSegment{h, offsets, wd, nullptr, y,
-                              static_cast<int64_t>(F) * H, M, E, F, H};
+                              static_cast<int64_t>(F) * H, 0, M, E, F, H};
   p.nseg = 1;
   p.gated = false;
   p.rows_hint = M / E;
+  p.ksplit = 1;
   return p;
 }
 
@@ -228,15 +248,16 @@ int moe_combine(const moe_bf16* y_perm, const int32_t* row_dest, const float* to
   MOE_TRY(need_word(row_dest));
   MOE_TRY(need_word(topk_w));
   MOE_TRY(need_bf16(out));
-  return hip_status(moe::launch_combine(y_perm, false, row_dest, topk_w, T, H, k, nullptr,
-                                        nullptr, out, static_cast<hipStream_t>(stream)));
+  return hip_status(moe::launch_combine(y_perm, false, 1, 0, row_dest, topk_w, T, H, k,
+                                        nullptr, 0, nullptr, out,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 size_t moe_forward_workspace_bytes(int T, int H, int F, int E, int k, int Fs) {
   if (check_dims(T, E, k) != MOE_OK || check_width(H) != MOE_OK ||
       check_width(F) != MOE_OK || Fs < 0 || (Fs > 0 && check_width(Fs) != MOE_OK))
     return 0;
-  return forward_layout(T, H, F, E, k, Fs).total;
+  return forward_layout(T, H, F, E, k, Fs, moe::grouped_gemm_device_cus()).total;
 }
 
 int moe_forward(const moe_bf16* x, const float* logits, int T, int H, int F, int E,
@@ -269,7 +290,7 @@ int moe_forward(const moe_bf16* x, const float* logits, int T, int H, int F, int
     if (shared->gate_logits) MOE_TRY(need_word(shared->gate_logits));
   }
   MOE_TRY(need_bf16(ws));
-  const ForwardLayout L = forward_layout(T, H, F, E, k, Fs);
+  const ForwardLayout L = forward_layout(T, H, F, E, k, Fs, moe::grouped_gemm_device_cus());
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
 
   char* base = static_cast<char*>(ws);
@@ -295,21 +316,25 @@ int moe_forward(const moe_bf16* x, const float* logits, int T, int H, int F, int
   // 3. grouped gate/up + SwiGLU (shared expert as one more group over x)
   moe::GemmProblem g1 = gateup_problem(x_perm, offsets, M, H, F, E, w_gate, w_up, h);
   if (shared) {
-    g1.seg[1] = moe::GemmSegment{x, nullptr, shared->w_gate, shared->w_up, h_sh, 0, T, 1, H, Fs};
+    g1.seg[1] = moe::GemmSegment{x, nullptr, shared->w_gate, shared->w_up, h_sh, 0, 0, T, 1, H, Fs};
     g1.nseg = 2;
   }
   MOE_TRY(hip_status(moe::launch_grouped_gemm(g1, s)));
   // 4. grouped down (shared expert likewise)
   moe::GemmProblem g2 = down_problem(h, offsets, M, F, H, E, w_down, y);
   g2.out_f32 = true;
+  g2.ksplit = L.ksplit;
+  g2.seg[0].slice_stride = static_cast<int64_t>(M) * H;
   if (shared) {
-    g2.seg[1] = moe::GemmSegment{h_sh, nullptr, shared->w_down, nullptr, y_sh, 0, T, 1, Fs, H};
+    g2.seg[1] = moe::GemmSegment{h_sh, nullptr, shared->w_down, nullptr, y_sh, 0,
+                                 static_cast<int64_t>(T) * H, T, 1, Fs, H};
     g2.nseg = 2;
   }
   MOE_TRY(hip_status(moe::launch_grouped_gemm(g2, s)));
   // 5. combine (+ gated shared term)
-  return hip_status(moe::launch_combine(y, true, row_dest, w, T, H, k,
-                                        shared ? y_sh : nullptr,
+  return hip_status(moe::launch_combine(y, true, L.ksplit, static_cast<int64_t>(M) * H,
+                                        row_dest, w, T, H, k, shared ? y_sh : nullptr,
+                                        static_cast<int64_t>(T) * H,
                                         shared ? shared->gate_logits : nullptr, out, s));
 }
 

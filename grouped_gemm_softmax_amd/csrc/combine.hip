@@ -3,7 +3,9 @@
 //                    + s_t * y_shared[t,c] )
 // with fp32 accumulation in ascending j and the shared term added last.
 // y_perm and y_shared are bf16 (the split ABI) or fp32 (inside the fused
-// layer, where the down projection's output skips the bf16 rounding).
+// layer, where the down projection's output skips the bf16 rounding; there a
+// decode-size down projection may come as K-slice partial sums, which are
+// added here in slice order before the routing weight is applied).
 // Semantically a scatter-add of the weighted expert rows back to their
 // tokens; it is computed as a gather through the inverse map row_dest, so no
 // floating-point atomics are used and the result is deterministic. The
@@ -37,12 +39,25 @@ __device__ __forceinline__ void load8(const float* p, float v[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// One row as the sum of its K-slices (slice order fixed).
+template <typename YT>
+__device__ __forceinline__ void load8_sum(const YT* p, int nslices, int64_t stride, float v[8]) {
+  load8(p, v);
+  for (int s = 1; s < nslices; ++s) {
+    float u[8];
+    load8(p + s * stride, u);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] += u[q];
+  }
+}
+
 template <typename YT>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
-    const YT* __restrict__ y_perm, const int32_t* __restrict__ row_dest,
+    const YT* __restrict__ y_perm, int nslices, int64_t y_slice_stride,
+    const int32_t* __restrict__ row_dest,
     const float* __restrict__ topk_w, int T, int H, int k,
-    const YT* __restrict__ y_shared, const float* __restrict__ shared_gate,
-    bf16_t* __restrict__ out) {
+    const YT* __restrict__ y_shared, int64_t ysh_slice_stride,
+    const float* __restrict__ shared_gate, bf16_t* __restrict__ out) {
   const int t = blockIdx.x;
   __shared__ int s_row[kMaxTopK];
   __shared__ float s_w[kMaxTopK];
@@ -60,13 +75,13 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float v[8];
     for (int j = 0; j < k; ++j) {
-      load8(y_perm + static_cast<int64_t>(s_row[j]) * H + c, v);
+      load8_sum(y_perm + static_cast<int64_t>(s_row[j]) * H + c, nslices, y_slice_stride, v);
       const float w = s_w[j];
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] += w * v[q];
     }
     if (y_shared) {
-      load8(y_shared + static_cast<int64_t>(t) * H + c, v);
+      load8_sum(y_shared + static_cast<int64_t>(t) * H + c, nslices, ysh_slice_stride, v);
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] += s * v[q];
     }
@@ -81,19 +96,21 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 
 }  // namespace
 
-hipError_t launch_combine(const void* y_perm, bool y_f32, const int32_t* row_dest,
+hipError_t launch_combine(const void* y_perm, bool y_f32, int nslices,
+                          int64_t y_slice_stride, const int32_t* row_dest,
                           const float* topk_w, int T, int H, int k,
-                          const void* y_shared, const float* shared_gate,
-                          bf16_t* out, hipStream_t stream) {
+                          const void* y_shared, int64_t ysh_slice_stride,
+                          const float* shared_gate, bf16_t* out, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   if (y_f32)
     hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(kCombineThreads), 0, stream,
-                       static_cast<const float*>(y_perm), row_dest, topk_w, T, H, k,
-                       static_cast<const float*>(y_shared), shared_gate, out);
+                       static_cast<const float*>(y_perm), nslices, y_slice_stride, row_dest,
+                       topk_w, T, H, k, static_cast<const float*>(y_shared),
+                       ysh_slice_stride, shared_gate, out);
   else
     hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(kCombineThreads), 0, stream,
-                       static_cast<const bf16_t*>(y_perm), row_dest, topk_w, T, H, k,
-                       static_cast<const bf16_t*>(y_shared), shared_gate, out);
+                       static_cast<const bf16_t*>(y_perm), 1, 0, row_dest, topk_w, T, H, k,
+                       static_cast<const bf16_t*>(y_shared), 0, shared_gate, out);
   return hipGetLastError();
 }
 

@@ -5,25 +5,26 @@
 // where W[g] is [K][N] with N contiguous and the epilogue is either a plain
 // store (bf16, or fp32 for the fused layer's down projection, whose output
 // feeds the combine without a bf16 rounding) or, in the gated form, SwiGLU
-// over two weight
-// matrices: out = silu(act*W_gate) * (act*W_up). In the gated form the gate
-// and up products only ever live in accumulator registers, so the SwiGLU
-// input never reaches memory (the dispatch-kernel post (lumeric.app),
-// summary paragraph). Grouping many independent GEMMs into one persistent
-// launch follows the grouped-GEMM news page (meineki.news); block scheduling
-// over variable expert batch sizes follows the Triton MoE page (setupai.cc),
-// key points.
+// over two weight matrices: out = silu(act*W_gate) * (act*W_up). In the gated
+// form the gate and up products only ever live in accumulator registers, so
+// the SwiGLU input never reaches memory (the dispatch-kernel post
+// (lumeric.app), summary paragraph). Grouping many independent GEMMs into one
+// persistent launch follows the grouped-GEMM news page (meineki.news); block
+// scheduling over variable expert batch sizes follows the Triton MoE page
+// (setupai.cc), key points.
 //
-// Work items and scheduling. An item is one (group, M-tile, N-tile): BT
-// activation rows by BF output columns over the whole K. Every item has the
-// same cost within a segment, so a static round-robin over a persistent grid
-// stays balanced however skewed the expert counts are. Each workgroup
-// rebuilds the per-group item prefix from the device-side expert offsets in
-// its prologue: there is no host synchronisation. Items are numbered group by
-// group, N-tile by N-tile, with the M-tile fastest, and the workgroup ->
-// item-slot map gives every XCD a contiguous run of items (workgroups are
-// dispatched round-robin over the 8 XCDs), so the M-tiles sharing one weight
-// tile run together under one L2.
+// Work items and scheduling. An item is one (group, M-tile, N-tile, K-slice):
+// BT activation rows by BF output columns over a K range. Items of a segment
+// have equal cost, so a static round-robin over a persistent grid stays
+// balanced however skewed the expert counts are. Each workgroup rebuilds the
+// per-group item prefix from the device-side expert offsets in its prologue:
+// there is no host synchronisation. Items are numbered group by group,
+// N-tile by N-tile, M-tile next and K-slice fastest; the workgroup -> slot map
+// gives every XCD a contiguous run of items (workgroups are dispatched
+// round-robin over the 8 XCDs), so the M-tiles sharing a weight tile run
+// together under one L2. K-slices (split-K) are used only for plain fp32
+// outputs: slice s writes its partial sums to out + s*slice_stride and the
+// consumer adds the slices in order, so results stay deterministic.
 //
 // Operand roles ("swap A/B"). The MFMA A operand is the weight tile and the
 // B operand the activations, i.e. the kernel computes (W^T X^T)^T: output
@@ -34,13 +35,22 @@
 // article (itsolotime.com), section 3.2, and in the HPC-Ops article
 // (ntfzh.com), FusedMoE paragraph.
 //
-// Data path per K-step: global -> VGPR (16-byte loads, prefetched one step
-// ahead) -> LDS in the tensors' own layouts (weights [BK][BF] N-contiguous,
-// activations [BT][BK] K-contiguous, rows padded against bank conflicts) ->
-// MFMA operands. The weight operand needs K-consecutive values per lane,
-// which the N-contiguous layout does not give; gfx950's transposing LDS read
-// (ds_read_b64_tr_b16) delivers them directly. MFMA: v_mfma_f32_16x16x32_bf16,
-// fp32 accumulation.
+// Data path. Tiles move global -> LDS with gfx950's direct-to-LDS loads
+// (global_load_lds_dwordx4: no VGPR staging) into a ring of STAGES buffers,
+// so STAGES-1 K-steps are in flight while one is computed. Each ring buffer
+// is its own __shared__ array, so the compiler's LDS-DMA alias tracking does
+// not make a read of one stage wait for loads into another; the wait for a
+// stage is an explicit vmcnt followed by a bare s_barrier (a __syncthreads
+// fence would drain every outstanding load). Each wave-wide DMA instruction
+// fills 1 KB of LDS in lane order, so tiles are stored in their global
+// layouts (weights [BK][BF] N-contiguous, activations [BT][BK] K-contiguous)
+// with an XOR swizzle of 16-byte chunks chosen on the global side. The
+// weight operand needs K-consecutive values per lane, which the N-contiguous
+// layout does not give; the transposing LDS read ds_read_b64_tr_b16 delivers
+// them. MFMA: v_mfma_f32_16x16x32_bf16, fp32 accumulation.
+#include <stdlib.h>
+#include <string.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -51,38 +61,63 @@ namespace {
 constexpr int kMaxGroups = kMaxExperts + 1;  // routed experts + one shared
 
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Transposing LDS read: within each 16-lane group, lane i receives element
 // i%4 of the 8-byte chunks read by lanes 4r + i/4, r = 0..3.
-__device__ __forceinline__ short4_t lds_read_tr16(const bf16_t* p) {
+__device__ __forceinline__ short4_t lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p));
 }
 
-template <int BT_, int BF_, int BK_, int WT_, int WF_, bool GATED_>
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maximum, i.e. not waited for).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BT_, int BF_, int BK_, int WT_, int WF_, int STAGES_, bool GATED_>
 struct TileCfg {
   static constexpr int BT = BT_;  // activation rows (tokens) per tile
   static constexpr int BF = BF_;  // output columns per tile
-  static constexpr int BK = BK_;  // K per pipeline step
+  static constexpr int BK = BK_;  // K per pipeline stage
   static constexpr int WT = WT_;  // waves along tokens
   static constexpr int WF = WF_;  // waves along output columns
+  static constexpr int STAGES = STAGES_;
   static constexpr bool GATED = GATED_;
-  static constexpr int kThreads = WT * WF * kWave;
+  static constexpr int NW = WT * WF;
+  static constexpr int kThreads = NW * kWave;
   static constexpr int NMAT = GATED ? 2 : 1;
   static constexpr int TF = BF / WF;  // columns per wave
   static constexpr int TT = BT / WT;  // tokens per wave
   static constexpr int FF = TF / 16;  // MFMA blocks per wave (columns)
   static constexpr int FT = TT / 16;  // MFMA blocks per wave (tokens)
-  static constexpr int WP = BF + 16;  // LDS pitch of a weight row (elements)
-  static constexpr int XP = BK + 8;   // LDS pitch of an activation row
-  static constexpr int W_CHUNKS = NMAT * BK * BF / 8;  // 16-byte chunks
-  static constexpr int X_CHUNKS = BT * BK / 8;
-  static constexpr int WCPT = (W_CHUNKS + kThreads - 1) / kThreads;
-  static constexpr int XCPT = (X_CHUNKS + kThreads - 1) / kThreads;
-  static constexpr int LDS_W = NMAT * BK * WP;
-  static constexpr int LDS_X = BT * XP;
+  static constexpr int W_BYTES = BK * BF * 2;  // one weight matrix per stage
+  static constexpr int X_BYTES = BT * BK * 2;
+  static constexpr int STAGE_BYTES = NMAT * W_BYTES + X_BYTES;
+  static constexpr int INSTR = STAGE_BYTES / 1024;  // 1 KB DMA instructions
+  static constexpr int IPW = INSTR / NW;            // per wave per stage
+  static constexpr int W_INSTR = NMAT * W_BYTES / 1024;
   static_assert(BF % (16 * WF) == 0 && BT % (16 * WT) == 0, "wave tiling");
-  static_assert(BK % 32 == 0, "BK must be a multiple of the MFMA K");
+  static_assert((BK == 32 || BK % 64 == 0) && BF % 64 == 0, "swizzle geometry");
+  static_assert(W_BYTES % 1024 == 0 && X_BYTES % 1024 == 0, "1 KB DMA granules");
+  static_assert(INSTR % NW == 0, "equal DMA share per wave");
+  static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
 };
+
+// 16-byte chunk swizzles (chunk index within a row).
+// Weights: the 4 rows a 16-lane transpose read touches land in 4 distinct
+// chunk pairs. Activations: 8 consecutive token rows at the same K chunk land
+// in 8 distinct 16-byte bank groups: with rows of >= 128 bytes the chunk is
+// XORed with row % 8; with 64-byte rows (BK = 32) two rows share a 128-byte
+// bank window, so row % 2 picks the half and (row / 2) % 4 is XORed in.
+__device__ __forceinline__ int swz_w(int row, int chunk) { return chunk ^ ((row & 3) << 1); }
+template <int BK>
+__device__ __forceinline__ int swz_x(int row, int chunk) {
+  return BK == 32 ? chunk ^ ((row >> 1) & 3) : chunk ^ (row & 7);
+}
 
 struct GroupView {
   int seg;      // segment index
@@ -117,20 +152,23 @@ __device__ __forceinline__ void store4(float* p, const float v[4]) {
   *reinterpret_cast<float4*>(p) = float4{v[0], v[1], v[2], v[3]};
 }
 
-template <class C, typename OutT>
+template <class C, typename OutT, bool KTAIL>
 __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem prob) {
-  __shared__ __attribute__((aligned(16))) bf16_t sW[C::LDS_W];
-  __shared__ __attribute__((aligned(16))) bf16_t sX[C::LDS_X];
-  __shared__ int s_pref[kMaxGroups + 1];
-  __shared__ int s_wave_total[C::kThreads / kWave];
+  __shared__ __attribute__((aligned(1024))) char st0[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char st1[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char st2[C::STAGES > 2 ? C::STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char st3[C::STAGES > 3 ? C::STAGE_BYTES : 16];
+  extern __shared__ int s_pref[];  // [groups + 1], sized at launch
+  __shared__ int s_wave_total[C::NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wf = wave % C::WF;
   const int wt = wave / C::WF;
   const int g16 = lane >> 4;   // k-group of the lane in an MFMA operand
   const int i16 = lane & 15;   // row/column of the lane in an MFMA operand
+  const int ksplit = prob.ksplit;
 
   // ---- prologue: item prefix over all groups of both segments ----
   const int NG = prob.seg[0].ngroups + (prob.nseg > 1 ? prob.seg[1].ngroups : 0);
@@ -144,7 +182,7 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
     if (g < NG) {
       const GroupView v = group_view(prob, g);
       const GemmSegment& s = v.seg ? prob.seg[1] : prob.seg[0];
-      cnt[i] = ((v.M + C::BT - 1) / C::BT) * ((s.N + C::BF - 1) / C::BF);
+      cnt[i] = ((v.M + C::BT - 1) / C::BT) * ((s.N + C::BF - 1) / C::BF) * ksplit;
     }
     my_sum += cnt[i];
   }
@@ -165,6 +203,7 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
   const int G = gridDim.x;
   const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8
                                 : blockIdx.x;
+  char* const ring[4] = {st0, st1, st2, st3};
 
   for (int item = slot; item < total; item += G) {
     // group owning the item: the largest g with s_pref[g] <= item
@@ -177,15 +216,51 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
     const GemmSegment& S = v.seg ? prob.seg[1] : prob.seg[0];
     const int K = S.K, N = S.N;
     const int mtiles = (v.M + C::BT - 1) / C::BT;
-    const int local = item - s_pref[lo];
+    int local = item - s_pref[lo];
+    const int ks = local % ksplit;
+    local /= ksplit;
     const int mt = local % mtiles;
     const int n0 = (local / mtiles) * C::BF;
     const int row_base = v.r0 + mt * C::BT;
     const int rows_valid = min(C::BT, v.M - mt * C::BT);
-    const bf16_t* __restrict__ act = S.act;
-    const bf16_t* wmat[C::NMAT];
-    wmat[0] = S.w0 + static_cast<int64_t>(v.local) * S.w_stride;
-    if (C::GATED) wmat[C::NMAT - 1] = S.w1 + static_cast<int64_t>(v.local) * S.w_stride;
+    // K range of this slice: whole stages (the last stage of K may be short)
+    const int nk_all = (K + C::BK - 1) / C::BK;
+    const int per = (nk_all + ksplit - 1) / ksplit;
+    const int kt_begin = ks * per;
+    const int nk = min(nk_all, kt_begin + per) - kt_begin;
+
+    // ---- DMA of one K-step into one ring buffer ----
+    // Instruction i of this wave fills 16-byte slots 64*j .. 64*j+63 of the
+    // stage, j = wave*IPW + i (wave-uniform). The lane's slot is a tile
+    // (row, physical chunk); the swizzle gives the logical chunk, hence the
+    // global source. Rows and columns are clamped to the valid range: clamped
+    // lanes fetch finite in-bounds data whose products only reach masked
+    // outputs or the zeroed K-tail rows.
+    const bf16_t* const wsrc0 = S.w0 + static_cast<int64_t>(v.local) * S.w_stride;
+    const bf16_t* const wsrc1 = C::GATED ? S.w1 + static_cast<int64_t>(v.local) * S.w_stride : wsrc0;
+    const bf16_t* const xsrc = S.act;
+    constexpr int W_PER_MAT = C::W_BYTES / 1024;   // instructions per weight matrix
+    constexpr int RPI_W = 1024 / (C::BF * 2);      // weight rows per instruction
+    constexpr int RPI_X = 1024 / (C::BK * 2);      // activation rows per instruction
+    auto issue = [&](int kt, char* buf) {
+      const int k0 = kt * C::BK;
+#pragma unroll
+      for (int i = 0; i < C::IPW; ++i) {
+        const int j = wave * C::IPW + i;
+        const bf16_t* src;
+        if (j < C::W_INSTR) {
+          const int mat = j / W_PER_MAT;
+          const int r = (j - mat * W_PER_MAT) * RPI_W + lane / (C::BF / 8);
+          const int col = min(n0 + swz_w(r, lane % (C::BF / 8)) * 8, N - 8);
+          src = (mat ? wsrc1 : wsrc0) + static_cast<int64_t>(min(k0 + r, K - 1)) * N + col;
+        } else {
+          const int r = (j - C::W_INSTR) * RPI_X + lane / (C::BK / 8);
+          const int kc = min(k0 + swz_x<C::BK>(r, lane % (C::BK / 8)) * 8, K - 8);
+          src = xsrc + static_cast<int64_t>(row_base + min(r, rows_valid - 1)) * K + kc;
+        }
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(buf + j * 1024), 16, 0, 0);
+      }
+    };
 
     floatx4 acc[C::NMAT][C::FF][C::FT];
 #pragma unroll
@@ -195,104 +270,107 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
 #pragma unroll
         for (int b = 0; b < C::FT; ++b) acc[m][a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    uint4 wreg[C::WCPT];
-    uint4 xreg[C::XCPT];
-    auto gload = [&](int k0) {
+    // one K-step on a landed ring buffer: per 32-deep substep, the token
+    // fragments once, then column block by column block the weight fragments
+    // and their MFMAs (keeps few fragments live beside the accumulators)
+    auto compute = [&](const char* buf) {
 #pragma unroll
-      for (int i = 0; i < C::WCPT; ++i) {
-        const int c = tid + i * C::kThreads;
-        wreg[i] = uint4{0u, 0u, 0u, 0u};
-        if (c < C::W_CHUNKS) {
-          const int mat = c / (C::BK * C::BF / 8);
-          const int rem = c - mat * (C::BK * C::BF / 8);
-          const int kr = rem / (C::BF / 8);
-          const int cc = rem - kr * (C::BF / 8);
-          const int kg = k0 + kr, ng = n0 + cc * 8;
-          if (kg < K && ng < N)
-            wreg[i] = *reinterpret_cast<const uint4*>(
-                wmat[mat] + static_cast<int64_t>(kg) * N + ng);
+      for (int s = 0; s < C::BK / 32; ++s) {
+        bf16x8 b[C::FT];
+#pragma unroll
+        for (int ti = 0; ti < C::FT; ++ti) {
+          const int tok = wt * C::TT + ti * 16 + i16;
+          const int chunk = swz_x<C::BK>(tok, s * 4 + g16);
+          b[ti] = *reinterpret_cast<const bf16x8*>(buf + C::NMAT * C::W_BYTES +
+                                                    tok * (C::BK * 2) + chunk * 16);
         }
-      }
 #pragma unroll
-      for (int i = 0; i < C::XCPT; ++i) {
-        const int c = tid + i * C::kThreads;
-        xreg[i] = uint4{0u, 0u, 0u, 0u};
-        if (c < C::X_CHUNKS) {
-          const int r = c / (C::BK / 8);
-          const int cc = c - r * (C::BK / 8);
-          const int kg = k0 + cc * 8;
-          if (r < rows_valid && kg < K)
-            xreg[i] = *reinterpret_cast<const uint4*>(
-                act + static_cast<int64_t>(row_base + r) * K + kg);
-        }
-      }
-    };
-    auto sstore = [&]() {
+        for (int fi = 0; fi < C::FF; ++fi) {
+          bf16x8 a[C::NMAT];
 #pragma unroll
-      for (int i = 0; i < C::WCPT; ++i) {
-        const int c = tid + i * C::kThreads;
-        if (c < C::W_CHUNKS) {
-          const int mat = c / (C::BK * C::BF / 8);
-          const int rem = c - mat * (C::BK * C::BF / 8);
-          const int kr = rem / (C::BF / 8);
-          const int cc = rem - kr * (C::BF / 8);
-          *reinterpret_cast<uint4*>(&sW[(mat * C::BK + kr) * C::WP + cc * 8]) = wreg[i];
-        }
-      }
+          for (int m = 0; m < C::NMAT; ++m) {
+            const int row = s * 32 + 8 * g16 + (i16 >> 2);          // k within the stage
+            const int col = wf * C::TF + fi * 16 + 4 * (i16 & 3);   // column within the tile
+            const int chunk = swz_w(row, col >> 3);                  // rows row, row+4 share it
+            const char* p = buf + m * C::W_BYTES + row * (C::BF * 2) + chunk * 16 + (col & 7) * 2;
+            const short4_t lo4 = lds_read_tr16(p);
+            const short4_t hi4 = lds_read_tr16(p + 4 * C::BF * 2);
+            typedef short short8_t __attribute__((ext_vector_type(8)));
+            const short8_t s8 = {lo4[0], lo4[1], lo4[2], lo4[3],
+                                 hi4[0], hi4[1], hi4[2], hi4[3]};
+            a[m] = __builtin_bit_cast(bf16x8, s8);
+          }
 #pragma unroll
-      for (int i = 0; i < C::XCPT; ++i) {
-        const int c = tid + i * C::kThreads;
-        if (c < C::X_CHUNKS) {
-          const int r = c / (C::BK / 8);
-          const int cc = c - r * (C::BK / 8);
-          *reinterpret_cast<uint4*>(&sX[r * C::XP + cc * 8]) = xreg[i];
+          for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+            for (int ti = 0; ti < C::FT; ++ti)
+              acc[m][fi][ti] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  a[m], b[ti], acc[m][fi][ti], 0, 0, 0);
         }
       }
     };
 
-    const int nk = (K + C::BK - 1) / C::BK;
-    gload(0);
-    for (int kt = 0; kt < nk; ++kt) {
-      __syncthreads();  // every wave has finished reading the previous step
-      sstore();
-      __syncthreads();
-      if (kt + 1 < nk) gload((kt + 1) * C::BK);  // in flight during the MFMAs
-#pragma unroll
-      for (int s = 0; s < C::BK / 32; ++s) {
-        bf16x8 a[C::NMAT][C::FF];
-        bf16x8 b[C::FT];
-#pragma unroll
-        for (int m = 0; m < C::NMAT; ++m)
-#pragma unroll
-          for (int fi = 0; fi < C::FF; ++fi) {
-            const int col = wf * C::TF + fi * 16 + 4 * (i16 & 3);
-            const int row = m * C::BK + s * 32 + 8 * g16 + (i16 >> 2);
-            const short4_t lo4 = lds_read_tr16(&sW[row * C::WP + col]);
-            const short4_t hi4 = lds_read_tr16(&sW[(row + 4) * C::WP + col]);
-            typedef short short8_t __attribute__((ext_vector_type(8)));
-            const short8_t s8 = {lo4[0], lo4[1], lo4[2], lo4[3],
-                                 hi4[0], hi4[1], hi4[2], hi4[3]};
-            a[m][fi] = __builtin_bit_cast(bf16x8, s8);
-          }
-#pragma unroll
-        for (int ti = 0; ti < C::FT; ++ti) {
-          const int tok = wt * C::TT + ti * 16 + i16;
-          b[ti] = *reinterpret_cast<const bf16x8*>(&sX[tok * C::XP + s * 32 + 8 * g16]);
-        }
-#pragma unroll
-        for (int m = 0; m < C::NMAT; ++m)
-#pragma unroll
-          for (int fi = 0; fi < C::FF; ++fi)
-#pragma unroll
-            for (int ti = 0; ti < C::FT; ++ti)
-              acc[m][fi][ti] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  a[m][fi], b[ti], acc[m][fi][ti], 0, 0, 0);
+    // Weight rows past K (only in the last stage of K when K % BK != 0; the
+    // KTAIL instantiation) are zeroed once they have landed, so the clamped
+    // activation columns there contribute exactly 0. The __syncthreads also
+    // waits for the refill DMA issued in this step; only the tail step pays.
+    auto zero_k_tail = [&](int kt, char* buf) {
+      const int kvalid = K - kt * C::BK;
+      if (kvalid >= C::BK) return;
+      const int nrow = C::BK - kvalid;
+      constexpr int per_row = C::BF * 2 / 16;
+      for (int i = tid; i < C::NMAT * nrow * per_row; i += C::kThreads) {
+        const int m = i / (nrow * per_row);
+        const int rem = i - m * nrow * per_row;
+        const int r = kvalid + rem / per_row;
+        const int c = rem - (rem / per_row) * per_row;
+        *reinterpret_cast<uint4*>(buf + m * C::W_BYTES + r * (C::BF * 2) + c * 16) =
+            uint4{0u, 0u, 0u, 0u};
       }
+      __syncthreads();
+    };
+
+    // One pipeline step: wait for stage t, refill the buffer freed by stage
+    // t-1 with stage t+STAGES-1, compute stage t. The refill is issued even
+    // past the end of the item's K range (the clamps keep it in bounds, and
+    // the rows it fetches are cached), so exactly STAGES-2 stages are always
+    // in flight behind stage t and the wait count is one constant.
+    auto step = [&](int t, char* cur, char* refill) {
+      wait_vmcnt<(C::STAGES - 2) * C::IPW>();
+      __builtin_amdgcn_s_barrier();
+      issue(kt_begin + t + C::STAGES - 1, refill);
+      if (KTAIL && kt_begin + t == nk_all - 1) zero_k_tail(kt_begin + t, cur);
+      compute(cur);
+    };
+
+    // every wave is done reading the previous item's stages and every DMA
+    // into them has landed
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int p = 0; p < C::STAGES - 1; ++p) issue(kt_begin + p, ring[p]);
+    // whole turns of the ring, then the remaining steps (no early exits
+    // inside the loop: they would keep the accumulators from being updated
+    // in place and double their registers)
+    {
+      const int full = nk / C::STAGES;
+      int t = 0;
+      for (int it = 0; it < full; ++it, t += C::STAGES) {
+        step(t, ring[0], ring[C::STAGES - 1]);
+        step(t + 1, ring[1], ring[0]);
+        if (C::STAGES > 2) step(t + 2, ring[2], ring[1]);
+        if (C::STAGES > 3) step(t + 3, ring[3], ring[2]);
+      }
+      const int rem = nk - t;
+      if (rem > 0) step(t, ring[0], ring[C::STAGES - 1]);
+      if (C::STAGES > 2 && rem > 1) step(t + 1, ring[1], ring[0]);
+      if (C::STAGES > 3 && rem > 2) step(t + 2, ring[2], ring[1]);
     }
 
     // ---- epilogue: lane holds columns 4*g16..+3 of one token per block ----
     // (bf16 stores round to nearest even; fp32 stores keep the accumulator)
-    OutT* __restrict__ out = static_cast<OutT*>(S.out);
+    OutT* __restrict__ out =
+        static_cast<OutT*>(S.out) + static_cast<int64_t>(ks) * S.slice_stride;
 #pragma unroll
     for (int fi = 0; fi < C::FF; ++fi)
 #pragma unroll
@@ -300,30 +378,38 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
         const int tok = wt * C::TT + ti * 16 + i16;
         const int f = n0 + wf * C::TF + fi * 16 + 4 * g16;
         if (tok < rows_valid && f < N) {
-          float v[4];
+          float vals[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             if (C::GATED) {
               const float gt = acc[0][fi][ti][r];
               const float up = acc[C::NMAT - 1][fi][ti][r];
-              v[r] = gt / (1.0f + __expf(-gt)) * up;
+              vals[r] = gt / (1.0f + __expf(-gt)) * up;
             } else {
-              v[r] = acc[0][fi][ti][r];
+              vals[r] = acc[0][fi][ti][r];
             }
           }
-          store4(out + static_cast<int64_t>(row_base + tok) * N + f, v);
+          store4(out + static_cast<int64_t>(row_base + tok) * N + f, vals);
         }
       }
   }
+  // no LDS DMA may land after the workgroup ends (its LDS may be reassigned)
+  wait_vmcnt<0>();
 }
 
-// Tile shapes. Large: 128 tokens x 128 columns, 2x2 waves of 64x64.
-// Small (decode): 16 tokens x 64 columns, 4 waves of 16 columns each, long
-// K steps so each workgroup keeps many weight bytes in flight.
-using GateUpLarge = TileCfg<128, 128, 64, 2, 2, true>;
-using GateUpSmall = TileCfg<16, 64, 128, 1, 4, true>;
-using DownLarge = TileCfg<128, 128, 64, 2, 2, false>;
-using DownSmall = TileCfg<16, 64, 256, 1, 4, false>;
+// Tile shapes (BT tokens x BF columns, BK per stage, waves, ring depth).
+// Large batch: 256 tokens x 128 columns (gated: 128 columns each of gate and
+// up; down: 256 columns), 8 waves (2 per SIMD) as 4 along tokens x 2 along
+// columns, 128 accumulators per lane, a 4-deep ring of 32-deep, 32 KB stages
+// (three stages of look-ahead).
+// Small batch (decode): gate/up 16 tokens x 64 columns on 2 waves with a
+// 4-deep ring of 18 KB stages (2 workgroups and ~108 KB of weights in flight
+// per CU); down 32 tokens x 64 columns on 4 waves, 4-deep ring of 12 KB
+// stages (3 workgroups per CU).
+using GateUpLarge = TileCfg<256, 128, 32, 4, 2, 4, true>;
+using GateUpSmall = TileCfg<16, 64, 64, 1, 2, 4, true>;
+using DownLarge = TileCfg<256, 256, 32, 4, 2, 4, false>;
+using DownSmall = TileCfg<32, 64, 64, 1, 4, 4, false>;
 
 int device_cu_count() {
   static int cus[64] = {0};
@@ -338,43 +424,105 @@ int device_cu_count() {
   return cus[dev];
 }
 
-template <class C, typename OutT>
-int blocks_per_cu() {
-  static int cached[64] = {0};
+// Resident workgroups per CU for a launch with `dyn` bytes of dynamic LDS.
+template <class C, typename OutT, bool KTAIL>
+int blocks_per_cu(size_t dyn) {
+  static int cached_n[64] = {0};
+  static size_t cached_dyn[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
+  if (cached_n[dev] == 0 || cached_dyn[dev] != dyn) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(grouped_gemm_kernel<C, OutT>), C::kThreads, 0) != hipSuccess || n <= 0)
+            &n, reinterpret_cast<const void*>(grouped_gemm_kernel<C, OutT, KTAIL>), C::kThreads,
+            dyn) != hipSuccess || n <= 0)
       n = 1;
-    cached[dev] = n;
+    cached_n[dev] = n;
+    cached_dyn[dev] = dyn;
   }
-  return cached[dev];
+  return cached_n[dev];
 }
 
-template <class C, typename OutT>
-hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
+template <class C>
+int64_t item_bound(const GemmProblem& p) {
   // upper bound on items: every group may leave one partial M-tile
   int64_t bound = 0;
   for (int s = 0; s < p.nseg; ++s) {
     const GemmSegment& S = p.seg[s];
     const int64_t mt = (S.rows + C::BT - 1) / C::BT + (S.offsets ? S.ngroups : 0);
-    bound += mt * ((S.N + C::BF - 1) / C::BF);
+    bound += mt * ((S.N + C::BF - 1) / C::BF) * p.ksplit;
   }
-  if (bound <= 0) return hipSuccess;
-  int64_t grid = static_cast<int64_t>(device_cu_count()) * blocks_per_cu<C, OutT>();
+  return bound;
+}
+
+template <class C, typename OutT, bool KTAIL>
+hipError_t launch_tail(const GemmProblem& p, int64_t bound, hipStream_t stream) {
+  int groups = 0;
+  for (int s = 0; s < p.nseg; ++s) groups += p.seg[s].ngroups;
+  const size_t dyn = static_cast<size_t>(groups + 1) * sizeof(int);
+  int64_t grid = static_cast<int64_t>(device_cu_count()) * blocks_per_cu<C, OutT, KTAIL>(dyn);
   if (bound < grid) grid = bound;
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL((grouped_gemm_kernel<C, OutT>), dim3(static_cast<unsigned>(grid)),
-                     dim3(C::kThreads), 0, stream, p);
+  hipLaunchKernelGGL((grouped_gemm_kernel<C, OutT, KTAIL>), dim3(static_cast<unsigned>(grid)),
+                     dim3(C::kThreads), dyn, stream, p);
   return hipGetLastError();
+}
+
+template <class C, typename OutT>
+hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
+  const int64_t bound = item_bound<C>(p);
+  if (bound <= 0) return hipSuccess;
+  bool ktail = false;
+  for (int s = 0; s < p.nseg; ++s) ktail = ktail || (p.seg[s].K % C::BK != 0);
+  return ktail ? launch_tail<C, OutT, true>(p, bound, stream)
+               : launch_tail<C, OutT, false>(p, bound, stream);
 }
 
 }  // namespace
 
+// Tile shape by typical rows per group: fewer than 64 -> small, else large.
+// MOE_TILE=small|large overrides the choice (for tile sweeps).
+bool grouped_gemm_uses_large_tiles(const GemmProblem& p) {
+  static int forced = -2;
+  if (forced == -2) {
+    const char* e = getenv("MOE_TILE");
+    forced = !e ? -1 : (!strcmp(e, "small") ? 0 : !strcmp(e, "large") ? 1 : -1);
+  }
+  if (forced >= 0) return forced == 1;
+  return p.rows_hint >= 64;
+}
+
+int grouped_gemm_ksplit_hint(const GemmProblem& p, int cus) {
+  // Split K only where the unsplit item count cannot fill the chip: down
+  // projections (fp32 partial outputs) with few touched experts or few
+  // row tiles.
+  if (p.gated || !p.out_f32) return 1;
+  const bool large = grouped_gemm_uses_large_tiles(p);
+  const int BT = large ? DownLarge::BT : DownSmall::BT;
+  const int BF = large ? DownLarge::BF : DownSmall::BF;
+  const int BK = large ? DownLarge::BK : DownSmall::BK;
+  int64_t items = 0;
+  int min_k = 1 << 30;
+  for (int s = 0; s < p.nseg; ++s) {
+    const GemmSegment& S = p.seg[s];
+    // expected row tiles: one partial tile per touched group plus full ones
+    const int64_t touched = S.ngroups > 1 ? (S.rows < S.ngroups ? S.rows : S.ngroups) : 1;
+    const int64_t mt = touched + S.rows / BT;
+    items += mt * ((S.N + BF - 1) / BF);
+    min_k = S.K < min_k ? S.K : min_k;
+  }
+  const int64_t want = 2 * static_cast<int64_t>(cus);
+  int split = 1;
+  while (split < kMaxKSplit && items * split * 2 <= want && min_k / (split * 2) >= 256 &&
+         min_k / (split * 2) >= 4 * BK)
+    split *= 2;
+  return split;
+}
+
+int grouped_gemm_device_cus() { return device_cu_count(); }
+
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
-  const bool large = p.rows_hint >= 64;
+  const bool large = grouped_gemm_uses_large_tiles(p);
   if (p.gated)
     return large ? launch_cfg<GateUpLarge, bf16_t>(p, stream)
                  : launch_cfg<GateUpSmall, bf16_t>(p, stream);

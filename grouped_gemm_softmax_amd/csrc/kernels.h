@@ -11,7 +11,9 @@ typedef uint16_t bf16_t;
 constexpr int kMaxExperts = 1024;     // E limit of the ABI
 constexpr int kMaxTopK = 16;          // k limit of the ABI
 constexpr int kMaxChunkAssign = 256;  // assignments per routing/permute chunk
-constexpr int kPermuteSliceCols = 1024;  // x columns copied per permute block
+constexpr int kPermuteSliceCols = 256;   // x columns copied per permute block
+constexpr int kPermChunks = 8;           // routing chunks per permute block
+constexpr int kMaxKSplit = 8;         // K-slices of a split down projection
 
 // --- routing and permutation (route_permute.hip) ---
 int route_chunk_tokens(int k);
@@ -39,6 +41,7 @@ struct GemmSegment {
   const bf16_t* w1;        // gated only
   void* out;               // [rows, N], bf16 or fp32 (GemmProblem::out_f32)
   int64_t w_stride;        // elements between consecutive groups' weights
+  int64_t slice_stride;    // elements between K-slice outputs (ksplit > 1)
   int rows;
   int ngroups;
   int K;
@@ -51,15 +54,23 @@ struct GemmProblem {
   bool gated;      // out = silu(act w0) * (act w1), else act w0
   bool out_f32;    // store fp32 instead of bf16 (down projection only)
   int rows_hint;   // typical rows per group, picks the tile shape
+  int ksplit;      // K-slices (1: none); > 1 needs out_f32, slices summed later
 };
 
 hipError_t launch_grouped_gemm(const GemmProblem& prob, hipStream_t stream);
+// K-slices worth using for `prob` on a device with `cus` compute units.
+int grouped_gemm_ksplit_hint(const GemmProblem& prob, int cus);
+int grouped_gemm_device_cus();
 
 // --- combine (combine.hip) ---
-// y_perm/y_shared hold bf16 values (y_f32 == false) or fp32 values.
-hipError_t launch_combine(const void* y_perm, bool y_f32, const int32_t* row_dest,
+// y_perm/y_shared hold bf16 values (y_f32 == false) or fp32 values; with
+// nslices > 1 (fp32 only) they are K-slice partial sums, slice s at
+// y + s*stride, added in slice order.
+hipError_t launch_combine(const void* y_perm, bool y_f32, int nslices,
+                          int64_t y_slice_stride, const int32_t* row_dest,
                           const float* topk_w, int T, int H, int k,
                           const void* y_shared /* [T,H] or null */,
+                          int64_t ysh_slice_stride,
                           const float* shared_gate /* [T] or null */,
                           bf16_t* out, hipStream_t stream);
 

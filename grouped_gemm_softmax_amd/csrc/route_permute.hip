@@ -1,21 +1,21 @@
 // Routing and permutation kernels of the MoE expert layer.
 //
-// route_kernel: one wavefront per token. Each lane holds the logits of the
-// experts e = lane + 64*q as 64-bit keys (order-preserving integer image of
-// the fp32 logit in the high word, ~e in the low word), so k rounds of a
-// wave-wide max give the k largest logits with equal logits in ascending
-// expert order. Top-k routing inside the kernel, with no host round trip,
+// route_kernel: a group of L lanes per token (L = next power of two >= E,
+// clamped to 8..64). Each lane holds the logits of experts e = lane%L + L*q
+// as 64-bit keys (order-preserving integer image of the fp32 logit in the
+// high word, ~e in the low word), so k rounds of a group-wide max give the k
+// largest logits with equal logits in ascending expert order. Top-k routing inside the kernel, with no host round trip,
 // follows the Triton MoE page (setupai.cc), technical deep-dive; the tie rule
 // and the softmax over the k chosen logits are this library's definition.
 // The same kernel optionally counts, per chunk of tokens, how many
 // assignments each expert received (the histogram for the permutation).
 //
 // permute_kernel: a stable counting sort of the assignments (t, j) by expert.
-// Each block owns one chunk of tokens: it derives each expert's first free
-// row for the chunk from the per-chunk histogram table (exclusive scan over
-// experts of the totals, plus the counts of earlier chunks), ranks its own
-// assignments in (t, j) order, writes the row maps and copies its tokens'
-// rows of x into x_perm. Per-expert contiguous activations as in the
+// Each block owns a few consecutive routing chunks: it derives each expert's
+// first free row for each of them from the per-chunk histogram table
+// (exclusive scan over experts of the totals, plus the counts of earlier
+// chunks), ranks its assignments in (t, j) order within their chunk, writes
+// the row maps and copies its tokens' rows of x into x_perm. Per-expert contiguous activations as in the
 // DeepGEMM article (itsolotime.com), section 3.1; re-arrangement before the
 // grouped GEMM as in the HPC-Ops article (ntfzh.com), FusedMoE paragraph.
 #include "common.h"
@@ -26,7 +26,6 @@ namespace moe {
 namespace {
 
 constexpr int kRouteThreads = 256;
-constexpr int kMaxQ = kMaxExperts / kWave;  // logits per lane
 
 // Order-preserving map of an fp32 bit pattern to uint32 (larger float ->
 // larger key); -0.0 is first canonicalised to +0.0 so the two tie.
@@ -41,30 +40,60 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
   return __uint_as_float(u);
 }
 
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    const float* __restrict__ logits, int T, int E, int k, int chunk_tokens,
-    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
-    int32_t* __restrict__ hist /* [nchunks][E] or null */) {
-  __shared__ int s_count[kMaxExperts];
+// Segmented butterfly max over aligned groups of L lanes (L a power of 2).
+template <int L>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) {
+    const uint64_t o = __shfl_xor(v, m, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// L lanes per token (L = the power of two >= E, at least 8, at most 64), so
+// a wave routes 64/L tokens at once; each lane holds the logits of experts
+// lane%L + L*q. The next token's logits are loaded before the current one is
+// ranked, so at most one load latency per pass is exposed.
+template <int L>
+__device__ void route_tokens(const float* __restrict__ logits, int T, int E, int k,
+                             int t_begin, int t_end, int32_t* __restrict__ topk_ids,
+                             float* __restrict__ topk_w, int* s_count) {
+  constexpr int TPW = kWave / L;          // tokens per wave per pass
+  // logits per lane, upper bound: 1 when E <= L < 64, else E <= 1024
+  constexpr int NQ = L < kWave ? 1 : kMaxExperts / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int nwaves = kRouteThreads / kWave;
-  if (hist)
-    for (int e = threadIdx.x; e < E; e += kRouteThreads) s_count[e] = 0;
-  __syncthreads();
-
-  const int t_begin = blockIdx.x * chunk_tokens;
-  const int t_end = min(T, t_begin + chunk_tokens);
-  const int Q = (E + kWave - 1) / kWave;
-  for (int t = t_begin + wave; t < t_end; t += nwaves) {
-    const float* row = logits + static_cast<int64_t>(t) * E;
-    uint64_t key[kMaxQ];
+  const int sub = lane / L;               // token slot in the wave
+  const int gl = lane % L;                // lane within the token group
+  const int Q = (E + L - 1) / L;
+  const int stride = (kRouteThreads / kWave) * TPW;
+  float cur[NQ];
+  auto load = [&](int t, float* dst) {
 #pragma unroll
-    for (int q = 0; q < kMaxQ; ++q) {
-      const int e = lane + q * kWave;
+    for (int q = 0; q < NQ; ++q) {
+      const int e = gl + q * L;
+      dst[q] = (t < t_end && q < Q && e < E) ? logits[static_cast<int64_t>(t) * E + e] : 0.f;
+    }
+  };
+  int t = t_begin + wave * TPW + sub;
+  load(t, cur);
+  for (; t - sub < t_end; t += stride) {
+    float nxt[NQ];
+    load(t + stride, nxt);
+    uint64_t key[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = gl + q * L;
       key[q] = 0;  // below every real key: never chosen while k <= E
       if (q < Q && e < E)
-        key[q] = (static_cast<uint64_t>(order_key(row[e])) << 32) |
+        key[q] = (static_cast<uint64_t>(order_key(cur[q])) << 32) |
                  static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(e));
     }
     int my_id = 0;
@@ -72,27 +101,44 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     for (int j = 0; j < k; ++j) {
       uint64_t best = 0;
 #pragma unroll
-      for (int q = 0; q < kMaxQ; ++q) best = key[q] > best ? key[q] : best;
-      best = wave_max_u64(best);
+      for (int q = 0; q < NQ; ++q) best = key[q] > best ? key[q] : best;
+      best = group_max_u64<L>(best);
 #pragma unroll
-      for (int q = 0; q < kMaxQ; ++q) key[q] = (key[q] == best) ? 0 : key[q];
-      if (lane == j) {
+      for (int q = 0; q < NQ; ++q) key[q] = (key[q] == best) ? 0 : key[q];
+      if (gl == j) {
         my_id = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
         my_logit = key_to_float(static_cast<uint32_t>(best >> 32));
       }
     }
-    // softmax over the k chosen logits; slot 0 (lane 0) holds the largest
-    const float m = __shfl(my_logit, 0, kWave);
-    const float ex = (lane < k) ? expf(my_logit - m) : 0.f;
-    float s = ex;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, kWave);
-    if (lane < k) {
-      topk_ids[static_cast<int64_t>(t) * k + lane] = my_id;
-      topk_w[static_cast<int64_t>(t) * k + lane] = ex / s;
-      if (hist) atomicAdd(&s_count[min(max(my_id, 0), E - 1)], 1);
+    // softmax over the k chosen logits; slot 0 of the group holds the largest
+    const float m = __shfl(my_logit, lane - gl, kWave);
+    const float ex = (gl < k) ? expf(my_logit - m) : 0.f;
+    const float ssum = group_sum<L>(ex);
+    if (t < t_end && gl < k) {
+      topk_ids[static_cast<int64_t>(t) * k + gl] = my_id;
+      topk_w[static_cast<int64_t>(t) * k + gl] = ex / ssum;
+      if (s_count) atomicAdd(&s_count[min(max(my_id, 0), E - 1)], 1);
     }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) cur[q] = nxt[q];
   }
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int chunk_tokens,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+    int32_t* __restrict__ hist /* [nchunks][E] or null */) {
+  __shared__ int s_count[kMaxExperts];
+  if (hist)
+    for (int e = threadIdx.x; e < E; e += kRouteThreads) s_count[e] = 0;
+  __syncthreads();
+  const int t_begin = blockIdx.x * chunk_tokens;
+  const int t_end = min(T, t_begin + chunk_tokens);
+  int* cnt = hist ? s_count : nullptr;
+  if (E <= 8) route_tokens<8>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
+  else if (E <= 16) route_tokens<16>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
+  else if (E <= 32) route_tokens<32>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
+  else route_tokens<64>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
   if (hist) {
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kRouteThreads)
@@ -120,65 +166,100 @@ __global__ __launch_bounds__(kRouteThreads) void hist_kernel(
 }
 
 constexpr int kPermThreads = 256;
-constexpr int kExpPerThread = kMaxExperts / kPermThreads;  // 4
 
+// One block per group of kPermChunks routing chunks (and per column slice of
+// x). Steps:
+//  1. One coalesced pass over the [nchunks][E] histogram gives each expert's
+//     total (hence, by an exclusive scan over experts, expert_offsets) and the
+//     counts of the chunks before this block; then the first free row of
+//     every expert for each of the block's routing chunks.
+//  2. Each assignment's row: that base plus its stable rank among the
+//     assignments of its own routing chunk with the same expert.
+//  3. The block copies its column slice of the assigned rows of x.
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ topk_ids, int T,
     int H, int E, int k, int chunk_tokens, int nchunks, int slice_cols,
     const int32_t* __restrict__ hist, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ row_token, int32_t* __restrict__ row_dest,
     bf16_t* __restrict__ x_perm) {
-  __shared__ int s_base[kMaxExperts];
+  __shared__ int s_total[kMaxExperts];
+  __shared__ int s_base[kPermChunks][kMaxExperts];
   __shared__ int s_wave_total[kPermThreads / kWave];
-  __shared__ int s_ids[kMaxChunkAssign];
-  __shared__ int s_dest[kMaxChunkAssign];
+  __shared__ int s_ids[kPermChunks * kMaxChunkAssign];
+  __shared__ int s_dest[kPermChunks * kMaxChunkAssign];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int chunk = blockIdx.x;
+  const int c0 = blockIdx.x * kPermChunks;               // first routing chunk
+  const int nc = min(kPermChunks, nchunks - c0);         // routing chunks here
 
-  // 1. first free row of each expert for this chunk
-  int before[kExpPerThread], total[kExpPerThread];
-  int my_sum = 0;
+  // 1a. totals and counts before this block (integer LDS atomics: exact and
+  //     order-independent)
+  for (int e = tid; e < E; e += kPermThreads) {
+    s_total[e] = 0;
+    for (int r = 0; r < kPermChunks; ++r) s_base[r][e] = 0;
+  }
+  __syncthreads();
+  const int ncell = nchunks * E;
+  constexpr int U = 8;
+  for (int i0 = tid; i0 < ncell; i0 += kPermThreads * U) {
+    int v[U];
 #pragma unroll
-  for (int i = 0; i < kExpPerThread; ++i) {
-    const int e = tid * kExpPerThread + i;
-    int b = 0, a = 0;
-    if (e < E) {
-      for (int c = 0; c < nchunks; ++c) {
-        const int v = hist[static_cast<int64_t>(c) * E + e];
-        a += v;
-        if (c < chunk) b += v;
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kPermThreads;
+      v[u] = i < ncell ? hist[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * kPermThreads;
+      if (i < ncell && v[u] != 0) {
+        const int c = i / E, e = i - c * E;
+        atomicAdd(&s_total[e], v[u]);
+        // chunks before the block count into every row of s_base; chunk
+        // c0 + r counts into rows r+1 .. nc-1
+        if (c < c0) atomicAdd(&s_base[0][e], v[u]);
+        else if (c < c0 + nc - 1) atomicAdd(&s_base[c - c0 + 1][e], v[u]);
       }
     }
-    before[i] = b;
-    total[i] = a;
-    my_sum += a;
   }
-  // exclusive scan over experts (thread-major order) of the totals
-  int incl = wave_inclusive_scan(my_sum);
+  __syncthreads();
+  // 1b. exclusive scan of the totals over experts (4 experts per thread,
+  //     thread-major), then the per-chunk bases
+  constexpr int EPT = kMaxExperts / kPermThreads;
+  int tot[EPT];
+  int my_sum = 0;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = tid * EPT + i;
+    tot[i] = e < E ? s_total[e] : 0;
+    my_sum += tot[i];
+  }
+  const int incl = wave_inclusive_scan(my_sum);
   if (lane == kWave - 1) s_wave_total[wave] = incl;
   __syncthreads();
-  int wave_off = 0;
-  for (int w = 0; w < wave; ++w) wave_off += s_wave_total[w];
-  int run = wave_off + incl - my_sum;
+  int run = incl - my_sum;
+  for (int w = 0; w < wave; ++w) run += s_wave_total[w];
 #pragma unroll
-  for (int i = 0; i < kExpPerThread; ++i) {
-    const int e = tid * kExpPerThread + i;
+  for (int i = 0; i < EPT; ++i) {
+    const int e = tid * EPT + i;
     if (e < E) {
-      if (chunk == 0 && blockIdx.y == 0) expert_offsets[e] = run;
-      s_base[e] = run + before[i];
+      if (blockIdx.x == 0 && blockIdx.y == 0) expert_offsets[e] = run;
+      int b = run;
+      for (int r = 0; r < nc; ++r) {  // running prefix over the block's chunks
+        b += s_base[r][e];
+        s_base[r][e] = b;
+      }
     }
-    run += total[i];
+    run += tot[i];
   }
-  if (chunk == 0 && blockIdx.y == 0 && tid == 0)
-    expert_offsets[E] = T * k;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) expert_offsets[E] = T * k;
 
-  // 2. stable rank of this chunk's assignments in (t, j) order
-  const int t0 = chunk * chunk_tokens;
-  const int nt = min(T - t0, chunk_tokens);
-  const int n = nt * k;
+  // 2. stable rank inside each routing chunk, in (t, j) order
+  const int t0 = c0 * chunk_tokens;
+  const int ntok = min(T - t0, nc * chunk_tokens);
+  const int n = ntok * k;
   const int64_t a0 = static_cast<int64_t>(t0) * k;
+  const int per_chunk = chunk_tokens * k;
   for (int i = tid; i < n; i += kPermThreads) {
     int e = topk_ids[a0 + i];
     s_ids[i] = e < 0 ? 0 : (e >= E ? E - 1 : e);
@@ -186,9 +267,10 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   __syncthreads();
   for (int i = tid; i < n; i += kPermThreads) {
     const int e = s_ids[i];
+    const int r = i / per_chunk;
     int rank = 0;
-    for (int i2 = 0; i2 < i; ++i2) rank += (s_ids[i2] == e);
-    int p = s_base[e] + rank;
+    for (int i2 = r * per_chunk; i2 < i; ++i2) rank += (s_ids[i2] == e);
+    int p = s_base[r][e] + rank;
     p = p < T * k ? p : T * k - 1;  // in bounds even for out-of-contract ids
     s_dest[i] = p;
     if (blockIdx.y == 0) {
@@ -199,21 +281,37 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   __syncthreads();
 
   // 3. copy this block's column slice of each assigned row: x_perm[p] = x[t]
+  //    (8 independent 16-byte loads in flight per thread before the stores)
   const int c_begin = blockIdx.y * slice_cols;
   const int c_end = min(H, c_begin + slice_cols);
   const int vec_per_row = (c_end - c_begin) / 8;  // 16-byte vectors
-  for (int v = tid; v < n * vec_per_row; v += kPermThreads) {
-    const int i = v / vec_per_row;
-    const int c = c_begin + (v - i * vec_per_row) * 8;
-    const int t = t0 + i / k;
-    const uint4 val = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t) * H + c);
-    *reinterpret_cast<uint4*>(x_perm + static_cast<int64_t>(s_dest[i]) * H + c) = val;
+  const int nvec = n * vec_per_row;
+  for (int v0 = tid; v0 < nvec; v0 += kPermThreads * U) {
+    uint4 val[U];
+    const uint4* src[U];
+    uint4* dst[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // out-of-range slots repeat the last vector (same source, same target)
+      const int v = min(v0 + u * kPermThreads, nvec - 1);
+      const int i = v / vec_per_row;
+      const int c = c_begin + (v - i * vec_per_row) * 8;
+      src[u] = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t0 + i / k) * H + c);
+      dst[u] = reinterpret_cast<uint4*>(x_perm + static_cast<int64_t>(s_dest[i]) * H + c);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) val[u] = *src[u];
+#pragma unroll
+    for (int u = 0; u < U; ++u) *dst[u] = val[u];
   }
 }
 
 }  // namespace
 
-int route_chunk_tokens(int k) { return kMaxChunkAssign / k; }
+int route_chunk_tokens(int k) {
+  const int c = kMaxChunkAssign / k;
+  return c < 32 ? c : 32;
+}
 
 int route_num_chunks(int T, int k) {
   const int c = route_chunk_tokens(k);
@@ -248,7 +346,8 @@ hipError_t launch_permute(const bf16_t* x, const int32_t* topk_ids, int T,
   const int nchunks = route_num_chunks(T, k);
   const int slice = kPermuteSliceCols;
   const int nslices = (H + slice - 1) / slice;
-  hipLaunchKernelGGL(permute_kernel, dim3(nchunks, nslices), dim3(kPermThreads),
+  const int nblocks = (nchunks + kPermChunks - 1) / kPermChunks;
+  hipLaunchKernelGGL(permute_kernel, dim3(nblocks, nslices), dim3(kPermThreads),
                      0, stream, x, topk_ids, T, H, E, k, chunk, nchunks, slice,
                      hist, expert_offsets, row_token, row_dest, x_perm);
   return hipGetLastError();

@@ -101,20 +101,44 @@ def test_forward_validation(L):
                          NULL, NULL, NULL, 0, NULL) == OK
 
 
+def _down_ksplit(T, H, F, E, k, Fs, cus=256):
+    """Re-statement of the host heuristic for K-slices of the fused layer's
+    down projection: only decode-size batches (fewer than 64 rows per
+    expert), doubling while twice the expected item count still fits in
+    2 x CUs and each slice keeps >= 4 K-steps of 64."""
+    A = T * k
+    if A // E >= 64:
+        return 1                                       # large tiles: not split here
+    items = (min(A, E) + A // 32) * -(-H // 64)
+    min_k = F
+    if Fs:
+        items += (1 + T // 32) * -(-H // 64)
+        min_k = min(F, Fs)
+    split = 1
+    while split < 8 and items * split * 2 <= 2 * cus and min_k // (split * 2) >= 256:
+        split *= 2
+    return split
+
+
 def _layout_model(T, H, F, E, k, Fs):
     """Independent re-statement of the documented forward workspace layout."""
     al = lambda v: (v + 255) // 256 * 256
     A = T * k
     chunk = 256 // k
     nch = (T + chunk - 1) // chunk
+    S = _down_ksplit(T, H, F, E, k, Fs)
     parts = [nch * E * 4, A * 4, A * 4, (E + 1) * 4, A * 4, A * 4, A * H * 2,
-             A * F * 2, T * Fs * 2, A * H * 4, T * (H if Fs else 0) * 4]
+             A * F * 2, T * Fs * 2, S * A * H * 4, S * T * (H if Fs else 0) * 4]
     return sum(al(p) for p in parts)
 
 
 @pytest.mark.parametrize("T,H,F,E,k,Fs", [(64, 256, 512, 8, 2, 0), (4096, 7168, 2048, 256, 8, 2048),
-                                          (16384, 2048, 1408, 60, 4, 5632), (1, 4096, 14336, 8, 2, 0)])
+                                          (16384, 2048, 1408, 60, 4, 5632), (1, 4096, 14336, 8, 2, 0),
+                                          (32, 4096, 14336, 8, 2, 0), (16, 2048, 1408, 60, 4, 5632),
+                                          (128, 7168, 2048, 256, 8, 2048)])
 def test_forward_workspace_bytes(T, H, F, E, k, Fs):
     got = B.moe_forward_workspace_bytes(T, H, F, E, k, Fs)
     assert got == _layout_model(T, H, F, E, k, Fs)
+    if (T, H) == (1, 4096):
+        assert _down_ksplit(T, H, F, E, k, Fs) == 4    # two experts: 128 items -> split 4
     assert B.moe_forward_workspace_bytes(T, H, F, E, k, 3) == 0      # Fs % 8
