@@ -103,19 +103,24 @@ def test_forward_validation(L):
 
 def _down_ksplit(T, H, F, E, k, Fs, cus=256):
     """Re-statement of the host heuristic for K-slices of the fused layer's
-    down projection: only decode-size batches (fewer than 64 rows per
-    expert), doubling while twice the expected item count still fits in
-    2 x CUs and each slice keeps >= 4 K-steps of 64."""
+    down projection. Tile: large (256 rows x 256 columns, 32-deep stages) at
+    >= 64 rows per expert, else small (32 x 64, 64-deep). Expected items:
+    one partial row tile per touched expert plus the full ones, times the
+    column tiles (plus the shared expert's). The split doubles while twice
+    the items still fit in 2 x CUs and each slice keeps >= 256 and >= 4
+    stages of K."""
     A = T * k
-    if A // E >= 64:
-        return 1                                       # large tiles: not split here
-    items = (min(A, E) + A // 32) * -(-H // 64)
+    large = A // E >= 64
+    BT, BF, BK = (256, 256, 32) if large else (32, 64, 64)
+    ntile = -(-H // BF)
+    items = (min(A, E) + A // BT) * ntile
     min_k = F
     if Fs:
-        items += (1 + T // 32) * -(-H // 64)
+        items += (1 + T // BT) * ntile
         min_k = min(F, Fs)
     split = 1
-    while split < 8 and items * split * 2 <= 2 * cus and min_k // (split * 2) >= 256:
+    while (split < 8 and items * split * 2 <= 2 * cus and min_k // (split * 2) >= 256
+           and min_k // (split * 2) >= 4 * BK):
         split *= 2
     return split
 
@@ -124,7 +129,7 @@ def _layout_model(T, H, F, E, k, Fs):
     """Independent re-statement of the documented forward workspace layout."""
     al = lambda v: (v + 255) // 256 * 256
     A = T * k
-    chunk = 256 // k
+    chunk = min(32, 256 // k)          # routing chunk (tokens per histogram row)
     nch = (T + chunk - 1) // chunk
     S = _down_ksplit(T, H, F, E, k, Fs)
     parts = [nch * E * 4, A * 4, A * 4, (E + 1) * 4, A * 4, A * 4, A * H * 2,
