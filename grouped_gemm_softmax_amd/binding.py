@@ -16,7 +16,9 @@ from typing import Optional
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmoe.so")
+# MOE_LIBRARY points the binding at another build of the same library (used
+# to compare kernel variants); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(PKG, "libmoe.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
 
 

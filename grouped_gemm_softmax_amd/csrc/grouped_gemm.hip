@@ -78,7 +78,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BT_, int BF_, int BK_, int WT_, int WF_, int STAGES_, bool GATED_>
+template <int BT_, int BF_, int BK_, int WT_, int WF_, int STAGES_, bool GATED_,
+          bool PREFETCH_>
 struct TileCfg {
   static constexpr int BT = BT_;  // activation rows (tokens) per tile
   static constexpr int BF = BF_;  // output columns per tile
@@ -87,6 +88,9 @@ struct TileCfg {
   static constexpr int WF = WF_;  // waves along output columns
   static constexpr int STAGES = STAGES_;
   static constexpr bool GATED = GATED_;
+  // Read the next stage's MFMA fragments into a second register set while
+  // this stage's MFMAs run (costs one more fragment set of registers).
+  static constexpr bool PREFETCH = PREFETCH_;
   static constexpr int NW = WT * WF;
   static constexpr int kThreads = NW * kWave;
   static constexpr int NMAT = GATED ? 2 : 1;
@@ -104,16 +108,23 @@ struct TileCfg {
   static_assert((BK == 32 || BK % 64 == 0) && BF % 64 == 0, "swizzle geometry");
   static_assert(W_BYTES % 1024 == 0 && X_BYTES % 1024 == 0, "1 KB DMA granules");
   static_assert(INSTR % NW == 0, "equal DMA share per wave");
-  static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
+  static_assert(STAGES == 4, "the pipeline is written for a 4-deep ring");
 };
 
-// 16-byte chunk swizzles (chunk index within a row).
+// 16-byte chunk swizzles (chunk index within a row), chosen by measuring
+// LDS throughput of each access pattern on gfx950.
 // Weights: the 4 rows a 16-lane transpose read touches land in 4 distinct
-// chunk pairs. Activations: 8 consecutive token rows at the same K chunk land
-// in 8 distinct 16-byte bank groups: with rows of >= 128 bytes the chunk is
-// XORed with row % 8; with 64-byte rows (BK = 32) two rows share a 128-byte
-// bank window, so row % 2 picks the half and (row / 2) % 4 is XORed in.
-__device__ __forceinline__ int swz_w(int row, int chunk) { return chunk ^ ((row & 3) << 1); }
+// chunk pairs (XOR 2*(row%4)), and the row groups 8 apart that other lanes of
+// the same instruction read land on the other bank half (XOR 8 for rows of
+// >= 256 bytes, XOR 2 for 128-byte rows). Rows r and r+4, read by one lane,
+// share the swizzle. Activations: 8 consecutive token rows at the same K
+// chunk land in 8 distinct 16-byte bank groups: with rows of >= 128 bytes the
+// chunk is XORed with row % 8; with 64-byte rows (BK = 32) two rows share a
+// 128-byte window, so row % 2 picks the half and (row / 2) % 4 is XORed in.
+template <int BF>
+__device__ __forceinline__ int swz_w(int row, int chunk) {
+  return chunk ^ ((row & 3) << 1) ^ (((row >> 3) & 1) << (BF >= 128 ? 3 : 1));
+}
 template <int BK>
 __device__ __forceinline__ int swz_x(int row, int chunk) {
   return BK == 32 ? chunk ^ ((row >> 1) & 3) : chunk ^ (row & 7);
@@ -156,8 +167,8 @@ template <class C, typename OutT, bool KTAIL>
 __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem prob) {
   __shared__ __attribute__((aligned(1024))) char st0[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[C::STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char st2[C::STAGES > 2 ? C::STAGE_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) char st3[C::STAGES > 3 ? C::STAGE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char st2[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char st3[C::STAGE_BYTES];
   extern __shared__ int s_pref[];  // [groups + 1], sized at launch
   __shared__ int s_wave_total[C::NW];
 
@@ -203,7 +214,6 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
   const int G = gridDim.x;
   const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8
                                 : blockIdx.x;
-  char* const ring[4] = {st0, st1, st2, st3};
 
   for (int item = slot; item < total; item += G) {
     // group owning the item: the largest g with s_pref[g] <= item
@@ -251,7 +261,7 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
         if (j < C::W_INSTR) {
           const int mat = j / W_PER_MAT;
           const int r = (j - mat * W_PER_MAT) * RPI_W + lane / (C::BF / 8);
-          const int col = min(n0 + swz_w(r, lane % (C::BF / 8)) * 8, N - 8);
+          const int col = min(n0 + swz_w<C::BF>(r, lane % (C::BF / 8)) * 8, N - 8);
           src = (mat ? wsrc1 : wsrc0) + static_cast<int64_t>(min(k0 + r, K - 1)) * N + col;
         } else {
           const int r = (j - C::W_INSTR) * RPI_X + lane / (C::BK / 8);
@@ -270,10 +280,95 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
 #pragma unroll
         for (int b = 0; b < C::FT; ++b) acc[m][a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // one K-step on a landed ring buffer: per 32-deep substep, the token
-    // fragments once, then column block by column block the weight fragments
-    // and their MFMAs (keeps few fragments live beside the accumulators)
-    auto compute = [&](const char* buf) {
+    // MFMA operand fragments of one stage (all its 32-deep substeps)
+    struct Frags {
+      bf16x8 a[C::BK / 32][C::NMAT][C::FF];
+      bf16x8 b[C::BK / 32][C::FT];
+    };
+    auto load_frags = [&](const char* buf, Frags& F) {
+#pragma unroll
+      for (int s = 0; s < C::BK / 32; ++s) {
+#pragma unroll
+        for (int ti = 0; ti < C::FT; ++ti) {
+          const int tok = wt * C::TT + ti * 16 + i16;
+          const int chunk = swz_x<C::BK>(tok, s * 4 + g16);
+          F.b[s][ti] = *reinterpret_cast<const bf16x8*>(buf + C::NMAT * C::W_BYTES +
+                                                         tok * (C::BK * 2) + chunk * 16);
+        }
+#pragma unroll
+        for (int fi = 0; fi < C::FF; ++fi)
+#pragma unroll
+          for (int m = 0; m < C::NMAT; ++m) {
+            const int row = s * 32 + 8 * g16 + (i16 >> 2);          // k within the stage
+            const int col = wf * C::TF + fi * 16 + 4 * (i16 & 3);   // column within the tile
+            const int chunk = swz_w<C::BF>(row, col >> 3);           // rows row, row+4 share it
+            const char* p = buf + m * C::W_BYTES + row * (C::BF * 2) + chunk * 16 + (col & 7) * 2;
+            const short4_t lo4 = lds_read_tr16(p);
+            const short4_t hi4 = lds_read_tr16(p + 4 * C::BF * 2);
+            typedef short short8_t __attribute__((ext_vector_type(8)));
+            const short8_t s8 = {lo4[0], lo4[1], lo4[2], lo4[3],
+                                 hi4[0], hi4[1], hi4[2], hi4[3]};
+            F.a[s][m][fi] = __builtin_bit_cast(bf16x8, s8);
+          }
+      }
+    };
+    auto mfma = [&](const Frags& F) {
+#pragma unroll
+      for (int s = 0; s < C::BK / 32; ++s)
+#pragma unroll
+        for (int fi = 0; fi < C::FF; ++fi)
+#pragma unroll
+          for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+            for (int ti = 0; ti < C::FT; ++ti)
+              acc[m][fi][ti] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  F.a[s][m][fi], F.b[s][ti], acc[m][fi][ti], 0, 0, 0);
+    };
+
+    // Weight rows past K (only in the last stage of K when K % BK != 0; the
+    // KTAIL instantiation) are zeroed once they have landed and before their
+    // fragments are read, so the clamped activation columns there contribute
+    // exactly 0. The __syncthreads also drains the DMA issued just before;
+    // only the tail step pays for it.
+    auto zero_k_tail = [&](int kt, char* buf) {
+      const int kvalid = K - kt * C::BK;
+      if (kvalid >= C::BK) return;
+      const int nrow = C::BK - kvalid;
+      constexpr int per_row = C::BF * 2 / 16;
+      for (int i = tid; i < C::NMAT * nrow * per_row; i += C::kThreads) {
+        const int m = i / (nrow * per_row);
+        const int rem = i - m * nrow * per_row;
+        const int r = kvalid + rem / per_row;
+        const int c = rem - (rem / per_row) * per_row;
+        *reinterpret_cast<uint4*>(buf + m * C::W_BYTES + r * (C::BF * 2) + c * 16) =
+            uint4{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+    };
+
+    // Pipeline, ring of 4 stages. Refills are issued even past the end of
+    // the item's K range (clamped in bounds; their rows are cached), so the
+    // number of stages in flight, hence every wait count, is a constant.
+    //
+    // PREFETCH: step t waits for stage t+1, refills the buffer stage t-1 used
+    // with stage t+3, then reads stage t+1's fragments while the MFMAs of
+    // stage t (read during step t-1) run.
+    // Otherwise: step t waits for stage t, refills the buffer of stage t-1
+    // with stage t+3, then reads and multiplies stage t.
+    Frags fa, fb;
+    auto step_pf = [&](int t, char* next, char* refill, const Frags& cur, Frags& nxt) {
+      wait_vmcnt<C::IPW>();
+      __builtin_amdgcn_s_barrier();
+      issue(kt_begin + t + 3, refill);
+      if (KTAIL && kt_begin + t + 1 == nk_all - 1) zero_k_tail(kt_begin + t + 1, next);
+      load_frags(next, nxt);
+      mfma(cur);
+    };
+    // Without prefetch, the gated kernel interleaves the weight-fragment
+    // reads column block by column block with the MFMAs that use them; the
+    // plain kernel reads all fragments first (each order measured faster for
+    // its kernel).
+    auto compute_interleaved = [&](const char* buf) {
 #pragma unroll
       for (int s = 0; s < C::BK / 32; ++s) {
         bf16x8 b[C::FT];
@@ -289,9 +384,9 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
           bf16x8 a[C::NMAT];
 #pragma unroll
           for (int m = 0; m < C::NMAT; ++m) {
-            const int row = s * 32 + 8 * g16 + (i16 >> 2);          // k within the stage
-            const int col = wf * C::TF + fi * 16 + 4 * (i16 & 3);   // column within the tile
-            const int chunk = swz_w(row, col >> 3);                  // rows row, row+4 share it
+            const int row = s * 32 + 8 * g16 + (i16 >> 2);
+            const int col = wf * C::TF + fi * 16 + 4 * (i16 & 3);
+            const int chunk = swz_w<C::BF>(row, col >> 3);
             const char* p = buf + m * C::W_BYTES + row * (C::BF * 2) + chunk * 16 + (col & 7) * 2;
             const short4_t lo4 = lds_read_tr16(p);
             const short4_t hi4 = lds_read_tr16(p + 4 * C::BF * 2);
@@ -309,62 +404,59 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
         }
       }
     };
-
-    // Weight rows past K (only in the last stage of K when K % BK != 0; the
-    // KTAIL instantiation) are zeroed once they have landed, so the clamped
-    // activation columns there contribute exactly 0. The __syncthreads also
-    // waits for the refill DMA issued in this step; only the tail step pays.
-    auto zero_k_tail = [&](int kt, char* buf) {
-      const int kvalid = K - kt * C::BK;
-      if (kvalid >= C::BK) return;
-      const int nrow = C::BK - kvalid;
-      constexpr int per_row = C::BF * 2 / 16;
-      for (int i = tid; i < C::NMAT * nrow * per_row; i += C::kThreads) {
-        const int m = i / (nrow * per_row);
-        const int rem = i - m * nrow * per_row;
-        const int r = kvalid + rem / per_row;
-        const int c = rem - (rem / per_row) * per_row;
-        *reinterpret_cast<uint4*>(buf + m * C::W_BYTES + r * (C::BF * 2) + c * 16) =
-            uint4{0u, 0u, 0u, 0u};
-      }
-      __syncthreads();
-    };
-
-    // One pipeline step: wait for stage t, refill the buffer freed by stage
-    // t-1 with stage t+STAGES-1, compute stage t. The refill is issued even
-    // past the end of the item's K range (the clamps keep it in bounds, and
-    // the rows it fetches are cached), so exactly STAGES-2 stages are always
-    // in flight behind stage t and the wait count is one constant.
-    auto step = [&](int t, char* cur, char* refill) {
-      wait_vmcnt<(C::STAGES - 2) * C::IPW>();
+    auto step_np = [&](int t, char* cur, char* refill) {
+      wait_vmcnt<2 * C::IPW>();
       __builtin_amdgcn_s_barrier();
-      issue(kt_begin + t + C::STAGES - 1, refill);
+      issue(kt_begin + t + 3, refill);
       if (KTAIL && kt_begin + t == nk_all - 1) zero_k_tail(kt_begin + t, cur);
-      compute(cur);
+      if (C::GATED) {
+        compute_interleaved(cur);
+      } else {
+        load_frags(cur, fa);
+        mfma(fa);
+      }
     };
 
-    // every wave is done reading the previous item's stages and every DMA
-    // into them has landed
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-#pragma unroll
-    for (int p = 0; p < C::STAGES - 1; ++p) issue(kt_begin + p, ring[p]);
+    wait_vmcnt<0>();               // every DMA into the ring has landed and
+    __builtin_amdgcn_s_barrier();  // every wave is done with the last item
+    issue(kt_begin + 0, st0);
+    issue(kt_begin + 1, st1);
+    issue(kt_begin + 2, st2);
+    if (C::PREFETCH) {
+      wait_vmcnt<2 * C::IPW>();
+      __builtin_amdgcn_s_barrier();  // stage 0 has landed
+      if (KTAIL && kt_begin == nk_all - 1) zero_k_tail(kt_begin, st0);
+      load_frags(st0, fa);
+    }
     // whole turns of the ring, then the remaining steps (no early exits
     // inside the loop: they would keep the accumulators from being updated
     // in place and double their registers)
     {
-      const int full = nk / C::STAGES;
+      const int full = nk / 4;
       int t = 0;
-      for (int it = 0; it < full; ++it, t += C::STAGES) {
-        step(t, ring[0], ring[C::STAGES - 1]);
-        step(t + 1, ring[1], ring[0]);
-        if (C::STAGES > 2) step(t + 2, ring[2], ring[1]);
-        if (C::STAGES > 3) step(t + 3, ring[3], ring[2]);
+      for (int it = 0; it < full; ++it, t += 4) {
+        if (C::PREFETCH) {
+          step_pf(t, st1, st3, fa, fb);
+          step_pf(t + 1, st2, st0, fb, fa);
+          step_pf(t + 2, st3, st1, fa, fb);
+          step_pf(t + 3, st0, st2, fb, fa);
+        } else {
+          step_np(t, st0, st3);
+          step_np(t + 1, st1, st0);
+          step_np(t + 2, st2, st1);
+          step_np(t + 3, st3, st2);
+        }
       }
       const int rem = nk - t;
-      if (rem > 0) step(t, ring[0], ring[C::STAGES - 1]);
-      if (C::STAGES > 2 && rem > 1) step(t + 1, ring[1], ring[0]);
-      if (C::STAGES > 3 && rem > 2) step(t + 2, ring[2], ring[1]);
+      if (C::PREFETCH) {
+        if (rem > 0) step_pf(t, st1, st3, fa, fb);
+        if (rem > 1) step_pf(t + 1, st2, st0, fb, fa);
+        if (rem > 2) step_pf(t + 2, st3, st1, fa, fb);
+      } else {
+        if (rem > 0) step_np(t, st0, st3);
+        if (rem > 1) step_np(t + 1, st1, st0);
+        if (rem > 2) step_np(t + 2, st2, st1);
+      }
     }
 
     // ---- epilogue: lane holds columns 4*g16..+3 of one token per block ----
@@ -405,11 +497,13 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
 // Small batch (decode): gate/up 16 tokens x 64 columns on 2 waves with a
 // 4-deep ring of 18 KB stages (2 workgroups and ~108 KB of weights in flight
 // per CU); down 32 tokens x 64 columns on 4 waves, 4-deep ring of 12 KB
-// stages (3 workgroups per CU).
-using GateUpLarge = TileCfg<256, 128, 32, 4, 2, 4, true>;
-using GateUpSmall = TileCfg<16, 64, 64, 1, 2, 4, true>;
-using DownLarge = TileCfg<256, 256, 32, 4, 2, 4, false>;
-using DownSmall = TileCfg<32, 64, 64, 1, 4, 4, false>;
+// stages (3 workgroups per CU); both read the next stage's fragments while
+// the current stage's MFMAs run (the large tiles have no registers to spare
+// for a second fragment set).
+using GateUpLarge = TileCfg<256, 128, 32, 4, 2, 4, true, false>;
+using GateUpSmall = TileCfg<16, 64, 64, 1, 2, 4, true, true>;
+using DownLarge = TileCfg<256, 256, 32, 4, 2, 4, false, false>;
+using DownSmall = TileCfg<32, 64, 64, 1, 4, 4, false, true>;
 
 int device_cu_count() {
   static int cus[64] = {0};
@@ -482,13 +576,18 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
 
 // Tile shape by typical rows per group: fewer than 64 -> small, else large.
 // MOE_TILE=small|large overrides the choice (for tile sweeps).
-bool grouped_gemm_uses_large_tiles(const GemmProblem& p) {
+int tile_override() {
   static int forced = -2;
   if (forced == -2) {
     const char* e = getenv("MOE_TILE");
     forced = !e ? -1 : (!strcmp(e, "small") ? 0 : !strcmp(e, "large") ? 1 : -1);
   }
-  if (forced >= 0) return forced == 1;
+  return forced;
+}
+
+bool grouped_gemm_uses_large_tiles(const GemmProblem& p) {
+  const int forced = tile_override();
+  if (forced >= 0) return forced >= 1;
   return p.rows_hint >= 64;
 }
 
