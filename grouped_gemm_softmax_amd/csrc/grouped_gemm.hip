@@ -211,11 +211,30 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
   __syncthreads();
   const int total = s_pref[NG];
 
+  // Balanced persistent schedule: with R = ceil(total / grid) rounds, only
+  // ceil(total / R) workgroups take items (spread evenly over the 8 XCDs,
+  // workgroups being dispatched round-robin over them), so every active
+  // workgroup gets R or R-1 items and none works alone through a last,
+  // sparse round. Each XCD's active workgroups take a contiguous run of
+  // slots, so consecutive items (the M-tiles of one weight tile) share an L2.
   const int G = gridDim.x;
-  const int slot = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8
-                                : blockIdx.x;
+  int slot, stride;
+  if (total == 0) return;
+  if (G % 8 == 0) {
+    const int rounds = (total + G - 1) / G;
+    const int per_xcd = ((total + rounds - 1) / rounds + 7) / 8;  // active per XCD
+    if (static_cast<int>(blockIdx.x / 8) >= per_xcd) {
+      wait_vmcnt<0>();
+      return;
+    }
+    slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    stride = 8 * per_xcd;
+  } else {
+    slot = blockIdx.x;
+    stride = G;
+  }
 
-  for (int item = slot; item < total; item += G) {
+  for (int item = slot; item < total; item += stride) {
     // group owning the item: the largest g with s_pref[g] <= item
     int lo = 0, hi = NG;
     while (hi - lo > 1) {
@@ -499,9 +518,12 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
 // per CU); down 32 tokens x 64 columns on 4 waves, 4-deep ring of 12 KB
 // stages (3 workgroups per CU); both read the next stage's fragments while
 // the current stage's MFMAs run (the large tiles have no registers to spare
-// for a second fragment set).
+// for a second fragment set). Mid (gate/up at 16..63 rows per group):
+// 32 tokens x 64 columns, 2 waves, 4-deep ring of 10 KB, 32-deep stages
+// (3 workgroups per CU): half the row tiles per expert of the small tile.
 using GateUpLarge = TileCfg<256, 128, 32, 4, 2, 4, true, false>;
 using GateUpSmall = TileCfg<16, 64, 64, 1, 2, 4, true, true>;
+using GateUpMid = TileCfg<32, 64, 32, 1, 2, 4, true, true>;
 using DownLarge = TileCfg<256, 256, 32, 4, 2, 4, false, false>;
 using DownSmall = TileCfg<32, 64, 64, 1, 4, 4, false, true>;
 
@@ -576,20 +598,23 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
 
 // Tile shape by typical rows per group: fewer than 64 -> small, else large.
 // MOE_TILE=small|large overrides the choice (for tile sweeps).
-int tile_override() {
+// Tile class by typical rows per group: < 16 small, < 64 mid (gate/up only;
+// the down projection keeps the small tile), else large. MOE_TILE=small|mid|
+// large overrides the choice (for tile sweeps).
+enum TileClass { kSmall = 0, kMid = 1, kLarge = 2 };
+
+int tile_class(const GemmProblem& p) {
   static int forced = -2;
   if (forced == -2) {
     const char* e = getenv("MOE_TILE");
-    forced = !e ? -1 : (!strcmp(e, "small") ? 0 : !strcmp(e, "large") ? 1 : -1);
+    forced = !e ? -1 : (!strcmp(e, "small") ? kSmall : !strcmp(e, "mid") ? kMid
+                        : !strcmp(e, "large") ? kLarge : -1);
   }
-  return forced;
+  if (forced >= 0) return forced;
+  return p.rows_hint < 16 ? kSmall : (p.rows_hint < 64 ? kMid : kLarge);
 }
 
-bool grouped_gemm_uses_large_tiles(const GemmProblem& p) {
-  const int forced = tile_override();
-  if (forced >= 0) return forced >= 1;
-  return p.rows_hint >= 64;
-}
+bool grouped_gemm_uses_large_tiles(const GemmProblem& p) { return tile_class(p) == kLarge; }
 
 int grouped_gemm_ksplit_hint(const GemmProblem& p, int cus) {
   // Split K only where the unsplit item count cannot fill the chip: down
@@ -621,10 +646,12 @@ int grouped_gemm_ksplit_hint(const GemmProblem& p, int cus) {
 int grouped_gemm_device_cus() { return device_cu_count(); }
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
-  const bool large = grouped_gemm_uses_large_tiles(p);
+  const int tc = tile_class(p);
+  const bool large = tc == kLarge;
   if (p.gated)
     return large ? launch_cfg<GateUpLarge, bf16_t>(p, stream)
-                 : launch_cfg<GateUpSmall, bf16_t>(p, stream);
+                 : tc == kMid ? launch_cfg<GateUpMid, bf16_t>(p, stream)
+                              : launch_cfg<GateUpSmall, bf16_t>(p, stream);
   if (p.out_f32)
     return large ? launch_cfg<DownLarge, float>(p, stream)
                  : launch_cfg<DownSmall, float>(p, stream);
