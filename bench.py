@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32,
                     help="tokens in the oracle's timed sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (the "
+                         "known-size reference for HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -78,6 +81,23 @@ def work_model(cfg, T, counts):
     return total_b, total_f, m, Et
 
 
+def measured_traffic(workload_is_default: bool):
+    """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE counters (copy-calibrated), or None when they were
+    taken on other kernel sources or another workload."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gateup_swiglu_mixtral_t32_traffic.json")
+    if not workload_is_default or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    h = hashlib.sha256()
+    for src in d["kernel_sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return d["traffic_bytes_per_launch"] if h.hexdigest() == d["kernel_sources_sha256"] else None
+
+
 def roof(bytes_, flops, ms):
     s = ms * 1e-3
     gbs = bytes_ / s / 1e9
@@ -100,6 +120,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = 1 << 29                                  # 2^29 bf16 = 1 GiB
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 2 * n, "launches": 3}))
+        return
 
     from grouped_gemm_softmax_amd import binding as B
     from grouped_gemm_softmax_amd import synth
@@ -183,6 +213,8 @@ def main():
         roofline = dict(bound="mfma", achieved=round(g1r["tflops"], 1), peak=PEAK_BF16_TFLOPS,
                         unit="TFLOP/s", frac=round(g1r["tflops"] / PEAK_BF16_TFLOPS, 4),
                         traffic=None)
+    roofline["traffic"] = measured_traffic(args.config == "mixtral" and args.T == 32 and
+                                           args.seed == 0)
     roofline.update(kernel="grouped_gemm_kernel (gate/up + SwiGLU, routed experts)",
                     kernel_ms=round(g1_ms, 5),
                     alg_bytes=g1["bytes"], alg_flops=g1["flops"])
