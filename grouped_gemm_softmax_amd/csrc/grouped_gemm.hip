@@ -51,6 +51,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -76,6 +78,52 @@ template <int n>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// ... and additionally until every LDS read of this wave has returned.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
+}
+
+// A wave-uniform pointer, moved to scalar registers.
+template <typename T>
+__device__ __forceinline__ T* uniform(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// One wave-wide direct-to-LDS load: lane l copies the 16 bytes at
+// base + voff (base wave-uniform, voff the lane's byte offset) to
+// lds + 16*l; M0 holds the wave's LDS destination. Written as inline
+// assembly: the compiler's own LDS-DMA tracking cannot tell the ring buffers
+// apart for every LDS read and would drain all loads in flight before it,
+// while the kernel waits for exactly the stage it needs (vmcnt).
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, char* lds) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (lds_void_t*)(lds)));
+  asm volatile("global_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(uniform(base)), "{m0}"(__builtin_amdgcn_readfirstlane(m0))
+               : "memory");
+}
+
+// Lambdas of the kernel body are always inlined: their operands (the
+// accumulators, fragment sets and ring buffers) must stay in registers and
+// fixed LDS arrays.
+#define INL __attribute__((always_inline))
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 template <int BT_, int BF_, int BK_, int WT_, int WF_, int STAGES_, bool GATED_,
@@ -107,8 +155,13 @@ struct TileCfg {
   static_assert(BF % (16 * WF) == 0 && BT % (16 * WT) == 0, "wave tiling");
   static_assert((BK == 32 || BK % 64 == 0) && BF % 64 == 0, "swizzle geometry");
   static_assert(W_BYTES % 1024 == 0 && X_BYTES % 1024 == 0, "1 KB DMA granules");
-  static_assert(INSTR % NW == 0, "equal DMA share per wave");
-  static_assert(STAGES == 4, "the pipeline is written for a 4-deep ring");
+  static_assert(INSTR % NW == 0 && (W_BYTES / 1024) % NW == 0,
+                "equal DMA share per wave, one operand kind per instruction slot");
+  static_assert(STAGES >= 3 && STAGES <= 8, "ring depth");
+  // vmcnt holds at most 63 outstanding operations per wave: the K-steps in
+  // flight plus an epilogue's stores must fit
+  static_assert((PREFETCH ? STAGES : STAGES - 1) * IPW + (BF / WF / 16) * (BT / WT / 16) <= 63,
+                "vector-memory counter range");
 };
 
 // 16-byte chunk swizzles (chunk index within a row), chosen by measuring
@@ -169,7 +222,15 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
   __shared__ __attribute__((aligned(1024))) char st1[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st2[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st3[C::STAGE_BYTES];
-  extern __shared__ int s_pref[];  // [groups + 1], sized at launch
+  // deeper rings only (unreferenced otherwise, hence not allocated)
+  __shared__ __attribute__((aligned(1024))) char st4[C::STAGES > 4 ? C::STAGE_BYTES : 1];
+  __shared__ __attribute__((aligned(1024))) char st5[C::STAGES > 5 ? C::STAGE_BYTES : 1];
+  __shared__ __attribute__((aligned(1024))) char st6[C::STAGES > 6 ? C::STAGE_BYTES : 1];
+  __shared__ __attribute__((aligned(1024))) char st7[C::STAGES > 7 ? C::STAGE_BYTES : 1];
+  // sized at launch: item prefix [groups + 1], then (first row, rows) per
+  // group, so that looking up an item reads LDS only (a global load inside
+  // the K pipeline would wait for every DMA in flight)
+  extern __shared__ __attribute__((aligned(16))) int s_pref[];
   __shared__ int s_wave_total[C::NW];
 
   const int tid = threadIdx.x;
@@ -183,6 +244,7 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
 
   // ---- prologue: item prefix over all groups of both segments ----
   const int NG = prob.seg[0].ngroups + (prob.nseg > 1 ? prob.seg[1].ngroups : 0);
+  int2* const s_rows = reinterpret_cast<int2*>(s_pref + ((NG + 2) & ~1));
   constexpr int GPT = (kMaxGroups + C::kThreads - 1) / C::kThreads;
   int cnt[GPT];
   int my_sum = 0;
@@ -194,6 +256,7 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
       const GroupView v = group_view(prob, g);
       const GemmSegment& s = v.seg ? prob.seg[1] : prob.seg[0];
       cnt[i] = ((v.M + C::BT - 1) / C::BT) * ((s.N + C::BF - 1) / C::BF) * ksplit;
+      s_rows[g] = int2{v.r0, v.M};
     }
     my_sum += cnt[i];
   }
@@ -234,64 +297,259 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
     stride = G;
   }
 
-  for (int item = slot; item < total; item += stride) {
+  constexpr int W_PER_MAT = C::W_BYTES / 1024;   // DMA instructions per weight matrix
+  constexpr int RPI_W = 1024 / (C::BF * 2);      // weight rows per instruction
+  constexpr int RPI_X = 1024 / (C::BK * 2);      // activation rows per instruction
+
+  // ---- one work item: where its operands are, its K range, its output ----
+  struct ItemInfo {
+    const bf16_t* w0;
+    const bf16_t* w1;
+    const bf16_t* x;
+    OutT* out;        // output of this item's K-slice
+    int K, N;
+    int n0;           // first output column
+    int row_base;     // first activation row
+    int rows_valid;   // rows of the tile inside the group
+    int kt_begin;     // first K-step (BK each) of the slice
+    int nk;           // K-steps of the slice
+    int nk_all;       // K-steps of the whole K
+    // per-lane byte offsets of this wave's DMA sources within a K-step,
+    // relative to the step's scalar base
+    uint32_t voff[C::IPW];
+  };
+  auto make_item = [&](int item) INL {
     // group owning the item: the largest g with s_pref[g] <= item
     int lo = 0, hi = NG;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (s_pref[mid] <= item) lo = mid; else hi = mid;
     }
-    const GroupView v = group_view(prob, lo);
+    GroupView v;
+    v.seg = lo < prob.seg[0].ngroups ? 0 : 1;
+    v.local = v.seg ? lo - prob.seg[0].ngroups : lo;
+    const int2 rows = s_rows[lo];
+    v.r0 = rows.x;
+    v.M = rows.y;
     const GemmSegment& S = v.seg ? prob.seg[1] : prob.seg[0];
-    const int K = S.K, N = S.N;
+    ItemInfo it;
+    it.K = S.K;
+    it.N = S.N;
     const int mtiles = (v.M + C::BT - 1) / C::BT;
     int local = item - s_pref[lo];
     const int ks = local % ksplit;
     local /= ksplit;
     const int mt = local % mtiles;
-    const int n0 = (local / mtiles) * C::BF;
-    const int row_base = v.r0 + mt * C::BT;
-    const int rows_valid = min(C::BT, v.M - mt * C::BT);
-    // K range of this slice: whole stages (the last stage of K may be short)
-    const int nk_all = (K + C::BK - 1) / C::BK;
+    it.n0 = (local / mtiles) * C::BF;
+    it.row_base = v.r0 + mt * C::BT;
+    it.rows_valid = min(C::BT, v.M - mt * C::BT);
+    // K range of this slice: whole K-steps (the last step of K may be short)
+    const int nk_all = (S.K + C::BK - 1) / C::BK;
     const int per = (nk_all + ksplit - 1) / ksplit;
-    const int kt_begin = ks * per;
-    const int nk = min(nk_all, kt_begin + per) - kt_begin;
-
-    // ---- DMA of one K-step into one ring buffer ----
-    // Instruction i of this wave fills 16-byte slots 64*j .. 64*j+63 of the
-    // stage, j = wave*IPW + i (wave-uniform). The lane's slot is a tile
-    // (row, physical chunk); the swizzle gives the logical chunk, hence the
-    // global source. Rows and columns are clamped to the valid range: clamped
-    // lanes fetch finite in-bounds data whose products only reach masked
-    // outputs or the zeroed K-tail rows.
-    const bf16_t* const wsrc0 = S.w0 + static_cast<int64_t>(v.local) * S.w_stride;
-    const bf16_t* const wsrc1 = C::GATED ? S.w1 + static_cast<int64_t>(v.local) * S.w_stride : wsrc0;
-    const bf16_t* const xsrc = S.act;
-    constexpr int W_PER_MAT = C::W_BYTES / 1024;   // instructions per weight matrix
-    constexpr int RPI_W = 1024 / (C::BF * 2);      // weight rows per instruction
-    constexpr int RPI_X = 1024 / (C::BK * 2);      // activation rows per instruction
-    auto issue = [&](int kt, char* buf) {
-      const int k0 = kt * C::BK;
+    it.kt_begin = ks * per;
+    it.nk = min(nk_all, it.kt_begin + per) - it.kt_begin;
+    it.nk_all = nk_all;
+    it.w0 = S.w0 + static_cast<int64_t>(v.local) * S.w_stride;
+    it.w1 = C::GATED ? S.w1 + static_cast<int64_t>(v.local) * S.w_stride : it.w0;
+    it.x = S.act;
+    it.out = static_cast<OutT*>(S.out) + static_cast<int64_t>(ks) * S.slice_stride;
+    // every field is wave-uniform: keep them in scalar registers
+    it.w0 = uniform(it.w0);
+    it.w1 = uniform(it.w1);
+    it.x = uniform(it.x);
+    it.out = uniform(it.out);
+    it.K = __builtin_amdgcn_readfirstlane(it.K);
+    it.N = __builtin_amdgcn_readfirstlane(it.N);
+    it.n0 = __builtin_amdgcn_readfirstlane(it.n0);
+    it.row_base = __builtin_amdgcn_readfirstlane(it.row_base);
+    it.rows_valid = __builtin_amdgcn_readfirstlane(it.rows_valid);
+    it.kt_begin = __builtin_amdgcn_readfirstlane(it.kt_begin);
+    it.nk = __builtin_amdgcn_readfirstlane(it.nk);
+    it.nk_all = __builtin_amdgcn_readfirstlane(it.nk_all);
+    {
 #pragma unroll
       for (int i = 0; i < C::IPW; ++i) {
-        const int j = wave * C::IPW + i;
-        const bf16_t* src;
-        if (j < C::W_INSTR) {
-          const int mat = j / W_PER_MAT;
+        const int j = i * C::NW + wave;
+        if (i < C::W_INSTR / C::NW) {
+          const int mat = i / (W_PER_MAT / C::NW);
           const int r = (j - mat * W_PER_MAT) * RPI_W + lane / (C::BF / 8);
-          const int col = min(n0 + swz_w<C::BF>(r, lane % (C::BF / 8)) * 8, N - 8);
-          src = (mat ? wsrc1 : wsrc0) + static_cast<int64_t>(min(k0 + r, K - 1)) * N + col;
+          const int col = min(it.n0 + swz_w<C::BF>(r, lane % (C::BF / 8)) * 8, it.N - 8);
+          it.voff[i] = static_cast<uint32_t>(r * it.N + col) * 2u;
         } else {
           const int r = (j - C::W_INSTR) * RPI_X + lane / (C::BK / 8);
-          const int kc = min(k0 + swz_x<C::BK>(r, lane % (C::BK / 8)) * 8, K - 8);
-          src = xsrc + static_cast<int64_t>(row_base + min(r, rows_valid - 1)) * K + kc;
+          const int kc = swz_x<C::BK>(r, lane % (C::BK / 8)) * 8;
+          it.voff[i] = static_cast<uint32_t>(min(r, it.rows_valid - 1) * it.K + kc) * 2u;
         }
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(buf + j * 1024), 16, 0, 0);
       }
-    };
+    }
+    return it;
+  };
 
-    floatx4 acc[C::NMAT][C::FF][C::FT];
+  // ---- DMA of one K-step of an item into one ring buffer ----
+  // Instruction i of this wave fills 16-byte slots 64*j .. 64*j+63 of the
+  // stage, j = i*NW + wave, so whether it loads weights (and which matrix)
+  // or activations is known at compile time. The lane's slot is a tile
+  // (row, physical chunk); the swizzle gives the logical chunk, hence the
+  // global source. Rows and columns are clamped to the valid range: clamped
+  // lanes fetch finite in-bounds data whose products only reach masked
+  // outputs or the zeroed K-tail rows (K-steps past the item's range load
+  // rows that are in bounds and never used).
+  auto issue = [&](const ItemInfo& it, int kt, char* buf) INL {
+    // Steps past the item's range re-load the last step of K. Each source is
+    // a scalar base (matrix, step) plus the item's lane offset; in the last
+    // step of a K that is not a whole number of steps (KTAIL) the rows past K
+    // (weights) and the columns past K (activations) are clamped to the last
+    // ones inside K.
+    const int64_t k0 = static_cast<int64_t>(min(kt, it.nk_all - 1)) * C::BK;
+    const int kleft = it.K - static_cast<int>(k0);  // K values from k0 on
+#pragma unroll
+    for (int i = 0; i < C::IPW; ++i) {
+      const int j = i * C::NW + wave;
+      const bf16_t* base;
+      uint32_t voff = it.voff[i];
+      if (i < C::W_INSTR / C::NW) {
+        const int mat = i / (W_PER_MAT / C::NW);
+        base = (mat ? it.w1 : it.w0) + k0 * it.N;
+        if constexpr (KTAIL) {
+          const int r = (j - mat * W_PER_MAT) * RPI_W + lane / (C::BF / 8);
+          if (r >= kleft) voff -= static_cast<uint32_t>((r - kleft + 1) * it.N) * 2u;
+        }
+      } else {
+        base = it.x + static_cast<int64_t>(it.row_base) * it.K + k0;
+        if constexpr (KTAIL) {
+          const int r = (j - C::W_INSTR) * RPI_X + lane / (C::BK / 8);
+          const int kc = swz_x<C::BK>(r, lane % (C::BK / 8)) * 8;
+          if (kc > kleft - 8) voff -= static_cast<uint32_t>(kc - (kleft - 8)) * 2u;
+        }
+      }
+      dma16(base, voff, buf + j * 1024);
+    }
+  };
+
+  floatx4 acc[C::NMAT][C::FF][C::FT];
+
+  // MFMA operand fragments of one stage (all its 32-deep substeps)
+  struct Frags {
+    bf16x8 a[C::BK / 32][C::NMAT][C::FF];
+    bf16x8 b[C::BK / 32][C::FT];
+  };
+  auto weight_frag = [&](const char* buf, int s, int m, int fi) INL {
+    const int row = s * 32 + 8 * g16 + (i16 >> 2);          // k within the stage
+    const int col = wf * C::TF + fi * 16 + 4 * (i16 & 3);   // column within the tile
+    const int chunk = swz_w<C::BF>(row, col >> 3);           // rows row, row+4 share it
+    const char* p = buf + m * C::W_BYTES + row * (C::BF * 2) + chunk * 16 + (col & 7) * 2;
+    const short4_t lo4 = lds_read_tr16(p);
+    const short4_t hi4 = lds_read_tr16(p + 4 * C::BF * 2);
+    typedef short short8_t __attribute__((ext_vector_type(8)));
+    const short8_t s8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    return __builtin_bit_cast(bf16x8, s8);
+  };
+  // kvalid: K values of the stage inside K. The lane's 8 K values start at a
+  // multiple of 8 and K is a multiple of 8, so they are all valid or all
+  // past K; past K the fragment is zeroed (the DMA loaded clamped, finite
+  // columns there), which makes the products with whatever weight rows the
+  // clamped DMA put beside them exactly 0.
+  auto act_frag = [&](const char* buf, int s, int ti, int kvalid) INL {
+    const int tok = wt * C::TT + ti * 16 + i16;
+    const int chunk = swz_x<C::BK>(tok, s * 4 + g16);
+    bf16x8 v = *reinterpret_cast<const bf16x8*>(buf + C::NMAT * C::W_BYTES +
+                                                 tok * (C::BK * 2) + chunk * 16);
+    if (KTAIL && s * 32 + 8 * g16 >= kvalid) v = bf16x8{};
+    return v;
+  };
+  auto load_frags = [&](const char* buf, Frags& F, int kvalid) INL {
+#pragma unroll
+    for (int s = 0; s < C::BK / 32; ++s) {
+#pragma unroll
+      for (int ti = 0; ti < C::FT; ++ti) F.b[s][ti] = act_frag(buf, s, ti, kvalid);
+#pragma unroll
+      for (int fi = 0; fi < C::FF; ++fi)
+#pragma unroll
+        for (int m = 0; m < C::NMAT; ++m) F.a[s][m][fi] = weight_frag(buf, s, m, fi);
+    }
+  };
+  auto mfma = [&](const Frags& F) INL {
+#pragma unroll
+    for (int s = 0; s < C::BK / 32; ++s)
+#pragma unroll
+      for (int fi = 0; fi < C::FF; ++fi)
+#pragma unroll
+        for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+          for (int ti = 0; ti < C::FT; ++ti)
+            acc[m][fi][ti] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                F.a[s][m][fi], F.b[s][ti], acc[m][fi][ti], 0, 0, 0);
+  };
+  // Without prefetch, the gated kernel interleaves the weight-fragment reads
+  // column block by column block with the MFMAs that use them; the plain
+  // kernel reads all fragments first (each order measured faster for its
+  // kernel).
+  auto compute_interleaved = [&](const char* buf, int kvalid) INL {
+#pragma unroll
+    for (int s = 0; s < C::BK / 32; ++s) {
+      bf16x8 b[C::FT];
+#pragma unroll
+      for (int ti = 0; ti < C::FT; ++ti) b[ti] = act_frag(buf, s, ti, kvalid);
+#pragma unroll
+      for (int fi = 0; fi < C::FF; ++fi) {
+        bf16x8 a[C::NMAT];
+#pragma unroll
+        for (int m = 0; m < C::NMAT; ++m) a[m] = weight_frag(buf, s, m, fi);
+#pragma unroll
+        for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+          for (int ti = 0; ti < C::FT; ++ti)
+            acc[m][fi][ti] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a[m], b[ti], acc[m][fi][ti], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- the ring ----
+  // K-step t of an item lives in buffer t % S. Without prefetch, step t
+  // waits for K-step t, refills the buffer of step t-1 with step t+S-1 and
+  // multiplies step t: S-1 steps in flight. With prefetch, step t waits for
+  // K-step t+1, refills buffer t % S (step t's fragments were read into
+  // registers during step t-1) with step t+S, reads step t+1's fragments and
+  // multiplies step t's: S steps in flight. Either way each wave then has at
+  // most S-2 newer K-steps outstanding, so every wait count is a constant;
+  // the lgkmcnt(0) in the wait makes every wave's reads of the buffer being
+  // refilled complete before the barrier.
+  //
+  // Items are chained (prefetching tiles): when an item's K-steps are a whole number of ring
+  // turns and the next item of this workgroup has at least D of them, the
+  // last refills of the item already fetch the next item's first D steps
+  // (into buffers 0.., as its own prologue would), so the ring never drains
+  // between items. Otherwise refills past the end re-load in-bounds rows of
+  // the item (their values are never used) and the next item starts with a
+  // drained ring.
+  constexpr int S = C::STAGES;
+  constexpr int D = C::PREFETCH ? S : S - 1;  // K-steps in flight after a refill
+  constexpr int WAIT = (S - 2) * C::IPW;
+  // Chaining is used by the decode-size (prefetching) tiles, whose time is
+  // memory latency; the large tiles keep their registers for the MFMA
+  // operands and restart the ring per item.
+  constexpr bool CHAIN = C::PREFETCH && !KTAIL;
+  auto stage_buf = [&](auto I) INL -> char* {
+    constexpr int i = decltype(I)::value % S;
+    if constexpr (i == 0) return st0;
+    else if constexpr (i == 1) return st1;
+    else if constexpr (i == 2) return st2;
+    else if constexpr (i == 3) return st3;
+    else if constexpr (i == 4) return st4;
+    else if constexpr (i == 5) return st5;
+    else if constexpr (i == 6) return st6;
+    else return st7;
+  };
+
+  Frags fa, fb;
+  bool primed = false;  // the current item's first D K-steps are in flight
+  for (int item = slot; item < total; item += stride) {
+    const ItemInfo cur = make_item(item);
+    const bool has_next = CHAIN && item + stride < total;
+    const ItemInfo nx = has_next ? make_item(item + stride) : cur;
+    const bool chain = has_next && cur.nk % S == 0 && nx.nk >= D;
+
 #pragma unroll
     for (int m = 0; m < C::NMAT; ++m)
 #pragma unroll
@@ -299,196 +557,71 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
 #pragma unroll
         for (int b = 0; b < C::FT; ++b) acc[m][a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // MFMA operand fragments of one stage (all its 32-deep substeps)
-    struct Frags {
-      bf16x8 a[C::BK / 32][C::NMAT][C::FF];
-      bf16x8 b[C::BK / 32][C::FT];
-    };
-    auto load_frags = [&](const char* buf, Frags& F) {
-#pragma unroll
-      for (int s = 0; s < C::BK / 32; ++s) {
-#pragma unroll
-        for (int ti = 0; ti < C::FT; ++ti) {
-          const int tok = wt * C::TT + ti * 16 + i16;
-          const int chunk = swz_x<C::BK>(tok, s * 4 + g16);
-          F.b[s][ti] = *reinterpret_cast<const bf16x8*>(buf + C::NMAT * C::W_BYTES +
-                                                         tok * (C::BK * 2) + chunk * 16);
-        }
-#pragma unroll
-        for (int fi = 0; fi < C::FF; ++fi)
-#pragma unroll
-          for (int m = 0; m < C::NMAT; ++m) {
-            const int row = s * 32 + 8 * g16 + (i16 >> 2);          // k within the stage
-            const int col = wf * C::TF + fi * 16 + 4 * (i16 & 3);   // column within the tile
-            const int chunk = swz_w<C::BF>(row, col >> 3);           // rows row, row+4 share it
-            const char* p = buf + m * C::W_BYTES + row * (C::BF * 2) + chunk * 16 + (col & 7) * 2;
-            const short4_t lo4 = lds_read_tr16(p);
-            const short4_t hi4 = lds_read_tr16(p + 4 * C::BF * 2);
-            typedef short short8_t __attribute__((ext_vector_type(8)));
-            const short8_t s8 = {lo4[0], lo4[1], lo4[2], lo4[3],
-                                 hi4[0], hi4[1], hi4[2], hi4[3]};
-            F.a[s][m][fi] = __builtin_bit_cast(bf16x8, s8);
-          }
-      }
-    };
-    auto mfma = [&](const Frags& F) {
-#pragma unroll
-      for (int s = 0; s < C::BK / 32; ++s)
-#pragma unroll
-        for (int fi = 0; fi < C::FF; ++fi)
-#pragma unroll
-          for (int m = 0; m < C::NMAT; ++m)
-#pragma unroll
-            for (int ti = 0; ti < C::FT; ++ti)
-              acc[m][fi][ti] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  F.a[s][m][fi], F.b[s][ti], acc[m][fi][ti], 0, 0, 0);
-    };
-
-    // Weight rows past K (only in the last stage of K when K % BK != 0; the
-    // KTAIL instantiation) are zeroed once they have landed and before their
-    // fragments are read, so the clamped activation columns there contribute
-    // exactly 0. The __syncthreads also drains the DMA issued just before;
-    // only the tail step pays for it.
-    auto zero_k_tail = [&](int kt, char* buf) {
-      const int kvalid = K - kt * C::BK;
-      if (kvalid >= C::BK) return;
-      const int nrow = C::BK - kvalid;
-      constexpr int per_row = C::BF * 2 / 16;
-      for (int i = tid; i < C::NMAT * nrow * per_row; i += C::kThreads) {
-        const int m = i / (nrow * per_row);
-        const int rem = i - m * nrow * per_row;
-        const int r = kvalid + rem / per_row;
-        const int c = rem - (rem / per_row) * per_row;
-        *reinterpret_cast<uint4*>(buf + m * C::W_BYTES + r * (C::BF * 2) + c * 16) =
-            uint4{0u, 0u, 0u, 0u};
-      }
-      __syncthreads();
-    };
-
-    // Pipeline, ring of 4 stages. Refills are issued even past the end of
-    // the item's K range (clamped in bounds; their rows are cached), so the
-    // number of stages in flight, hence every wait count, is a constant.
-    //
-    // PREFETCH: step t waits for stage t+1, refills the buffer stage t-1 used
-    // with stage t+3, then reads stage t+1's fragments while the MFMAs of
-    // stage t (read during step t-1) run.
-    // Otherwise: step t waits for stage t, refills the buffer of stage t-1
-    // with stage t+3, then reads and multiplies stage t.
-    Frags fa, fb;
-    auto step_pf = [&](int t, char* next, char* refill, const Frags& cur, Frags& nxt) {
-      wait_vmcnt<C::IPW>();
-      __builtin_amdgcn_s_barrier();
-      issue(kt_begin + t + 3, refill);
-      if (KTAIL && kt_begin + t + 1 == nk_all - 1) zero_k_tail(kt_begin + t + 1, next);
-      load_frags(next, nxt);
-      mfma(cur);
-    };
-    // Without prefetch, the gated kernel interleaves the weight-fragment
-    // reads column block by column block with the MFMAs that use them; the
-    // plain kernel reads all fragments first (each order measured faster for
-    // its kernel).
-    auto compute_interleaved = [&](const char* buf) {
-#pragma unroll
-      for (int s = 0; s < C::BK / 32; ++s) {
-        bf16x8 b[C::FT];
-#pragma unroll
-        for (int ti = 0; ti < C::FT; ++ti) {
-          const int tok = wt * C::TT + ti * 16 + i16;
-          const int chunk = swz_x<C::BK>(tok, s * 4 + g16);
-          b[ti] = *reinterpret_cast<const bf16x8*>(buf + C::NMAT * C::W_BYTES +
-                                                    tok * (C::BK * 2) + chunk * 16);
-        }
-#pragma unroll
-        for (int fi = 0; fi < C::FF; ++fi) {
-          bf16x8 a[C::NMAT];
-#pragma unroll
-          for (int m = 0; m < C::NMAT; ++m) {
-            const int row = s * 32 + 8 * g16 + (i16 >> 2);
-            const int col = wf * C::TF + fi * 16 + 4 * (i16 & 3);
-            const int chunk = swz_w<C::BF>(row, col >> 3);
-            const char* p = buf + m * C::W_BYTES + row * (C::BF * 2) + chunk * 16 + (col & 7) * 2;
-            const short4_t lo4 = lds_read_tr16(p);
-            const short4_t hi4 = lds_read_tr16(p + 4 * C::BF * 2);
-            typedef short short8_t __attribute__((ext_vector_type(8)));
-            const short8_t s8 = {lo4[0], lo4[1], lo4[2], lo4[3],
-                                 hi4[0], hi4[1], hi4[2], hi4[3]};
-            a[m] = __builtin_bit_cast(bf16x8, s8);
-          }
-#pragma unroll
-          for (int m = 0; m < C::NMAT; ++m)
-#pragma unroll
-            for (int ti = 0; ti < C::FT; ++ti)
-              acc[m][fi][ti] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  a[m], b[ti], acc[m][fi][ti], 0, 0, 0);
-        }
-      }
-    };
-    auto step_np = [&](int t, char* cur, char* refill) {
-      wait_vmcnt<2 * C::IPW>();
-      __builtin_amdgcn_s_barrier();
-      issue(kt_begin + t + 3, refill);
-      if (KTAIL && kt_begin + t == nk_all - 1) zero_k_tail(kt_begin + t, cur);
-      if (C::GATED) {
-        compute_interleaved(cur);
-      } else {
-        load_frags(cur, fa);
-        mfma(fa);
-      }
-    };
-
-    wait_vmcnt<0>();               // every DMA into the ring has landed and
-    __builtin_amdgcn_s_barrier();  // every wave is done with the last item
-    issue(kt_begin + 0, st0);
-    issue(kt_begin + 1, st1);
-    issue(kt_begin + 2, st2);
-    if (C::PREFETCH) {
-      wait_vmcnt<2 * C::IPW>();
-      __builtin_amdgcn_s_barrier();  // stage 0 has landed
-      if (KTAIL && kt_begin == nk_all - 1) zero_k_tail(kt_begin, st0);
-      load_frags(st0, fa);
-    }
-    // whole turns of the ring, then the remaining steps (no early exits
-    // inside the loop: they would keep the accumulators from being updated
-    // in place and double their registers)
-    {
-      const int full = nk / 4;
-      int t = 0;
-      for (int it = 0; it < full; ++it, t += 4) {
-        if (C::PREFETCH) {
-          step_pf(t, st1, st3, fa, fb);
-          step_pf(t + 1, st2, st0, fb, fa);
-          step_pf(t + 2, st3, st1, fa, fb);
-          step_pf(t + 3, st0, st2, fb, fa);
-        } else {
-          step_np(t, st0, st3);
-          step_np(t + 1, st1, st0);
-          step_np(t + 2, st2, st1);
-          step_np(t + 3, st3, st2);
-        }
-      }
-      const int rem = nk - t;
+    if (!primed) {
+      wait_vmcnt<0>();               // every DMA into the ring has landed and
+      __builtin_amdgcn_s_barrier();  // every wave is done with the last item
+      static_for<D>([&](auto I) INL { issue(cur, cur.kt_begin + decltype(I)::value, stage_buf(I)); });
       if (C::PREFETCH) {
-        if (rem > 0) step_pf(t, st1, st3, fa, fb);
-        if (rem > 1) step_pf(t + 1, st2, st0, fb, fa);
-        if (rem > 2) step_pf(t + 2, st3, st1, fa, fb);
-      } else {
-        if (rem > 0) step_np(t, st0, st3);
-        if (rem > 1) step_np(t + 1, st1, st0);
-        if (rem > 2) step_np(t + 2, st2, st1);
+        wait_vmcnt<(D - 1) * C::IPW>();
+        __builtin_amdgcn_s_barrier();  // K-step 0 has landed
+        load_frags(st0, fa, cur.K - cur.kt_begin * C::BK);
       }
+    }
+
+    // step t = S*turn + I; I is a compile-time constant, so every buffer is
+    // a fixed LDS array (no early exits inside the loop: they would keep the
+    // accumulators from being updated in place and double their registers)
+    auto step = [&](int t, auto I) INL {
+      constexpr int i = decltype(I)::value;
+      wait_vmcnt_lgkm0<WAIT>();
+      __builtin_amdgcn_s_barrier();
+      {
+        const int u = t + D;
+        char* const rb = stage_buf(std::integral_constant<int, i + D>{});
+        if (CHAIN && chain && u >= cur.nk) issue(nx, nx.kt_begin + (u - cur.nk), rb);
+        else issue(cur, cur.kt_begin + u, rb);
+      }
+      if constexpr (C::PREFETCH) {
+        char* const nb = stage_buf(std::integral_constant<int, i + 1>{});
+        const int kvalid = cur.K - (cur.kt_begin + t + 1) * C::BK;
+        if constexpr (i % 2 == 0) {
+          load_frags(nb, fb, kvalid);
+          mfma(fa);
+        } else {
+          load_frags(nb, fa, kvalid);
+          mfma(fb);
+        }
+      } else {
+        char* const cb = stage_buf(I);
+        const int kvalid = cur.K - (cur.kt_begin + t) * C::BK;
+        if constexpr (C::GATED) {
+          compute_interleaved(cb, kvalid);
+        } else {
+          load_frags(cb, fa, kvalid);
+          mfma(fa);
+        }
+      }
+    };
+    {
+      const int full = cur.nk / S;
+      int t = 0;
+      for (int turn = 0; turn < full; ++turn, t += S)
+        static_for<S>([&](auto I) INL { step(t + decltype(I)::value, I); });
+      const int rem = cur.nk - t;
+      static_for<S - 1>([&](auto I) INL {
+        if (decltype(I)::value < rem) step(t + decltype(I)::value, I);
+      });
     }
 
     // ---- epilogue: lane holds columns 4*g16..+3 of one token per block ----
     // (bf16 stores round to nearest even; fp32 stores keep the accumulator)
-    OutT* __restrict__ out =
-        static_cast<OutT*>(S.out) + static_cast<int64_t>(ks) * S.slice_stride;
 #pragma unroll
     for (int fi = 0; fi < C::FF; ++fi)
 #pragma unroll
       for (int ti = 0; ti < C::FT; ++ti) {
         const int tok = wt * C::TT + ti * 16 + i16;
-        const int f = n0 + wf * C::TF + fi * 16 + 4 * g16;
-        if (tok < rows_valid && f < N) {
+        const int f = cur.n0 + wf * C::TF + fi * 16 + 4 * g16;
+        if (tok < cur.rows_valid && f < cur.N) {
           float vals[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -500,9 +633,10 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
               vals[r] = acc[0][fi][ti][r];
             }
           }
-          store4(out + static_cast<int64_t>(row_base + tok) * N + f, vals);
+          store4(cur.out + static_cast<int64_t>(cur.row_base + tok) * cur.N + f, vals);
         }
       }
+    primed = chain;
   }
   // no LDS DMA may land after the workgroup ends (its LDS may be reassigned)
   wait_vmcnt<0>();
@@ -575,7 +709,8 @@ template <class C, typename OutT, bool KTAIL>
 hipError_t launch_tail(const GemmProblem& p, int64_t bound, hipStream_t stream) {
   int groups = 0;
   for (int s = 0; s < p.nseg; ++s) groups += p.seg[s].ngroups;
-  const size_t dyn = static_cast<size_t>(groups + 1) * sizeof(int);
+  const size_t dyn = static_cast<size_t>((groups + 2) & ~1) * sizeof(int) +
+                    static_cast<size_t>(groups) * sizeof(int2);
   int64_t grid = static_cast<int64_t>(device_cu_count()) * blocks_per_cu<C, OutT, KTAIL>(dyn);
   if (bound < grid) grid = bound;
   grid = (grid + 7) / 8 * 8;
@@ -596,8 +731,6 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
 
 }  // namespace
 
-// Tile shape by typical rows per group: fewer than 64 -> small, else large.
-// MOE_TILE=small|large overrides the choice (for tile sweeps).
 // Tile class by typical rows per group: < 16 small, < 64 mid (gate/up only;
 // the down projection keeps the small tile), else large. MOE_TILE=small|mid|
 // large overrides the choice (for tile sweeps).
