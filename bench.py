@@ -3,8 +3,11 @@
 
 Workload: the Mixtral-8x7B-shaped MoE layer (H=4096, F=14336, E=8 experts,
 top-2, SwiGLU experts, bf16) at a batch of T=32 tokens, router logits
-~ N(0,1), inputs already resident in HBM. A step is one moe_forward call
-(route -> permute -> gate/up+SwiGLU -> down -> combine, 5 launches).
+~ N(0,1), inputs already resident in HBM. A step is one moe_forward_packed
+call (route -> permute -> gate/up+SwiGLU -> down -> combine, 5 launches) on
+weights packed once beforehand (moe_pack_weights, as at model load; its time
+is reported as `pack_ms`, outside the steps); `rowmajor_ms_per_step` is the
+same step on the row-major weights (moe_forward), for comparison.
 
 Metric: MoE-layer HBM GB/s (algorithmic bytes / time), with TFLOP/s and the
 roofline fractions beside it. `roofline` describes the dominant kernel (the
@@ -45,6 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32,
                     help="tokens in the oracle's timed sample")
+    ap.add_argument("--weights", choices=("packed", "rowmajor"), default="packed",
+                    help="weight layout of the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (the "
                          "known-size reference for HBM byte counters) and exit")
@@ -81,7 +86,7 @@ def work_model(cfg, T, counts):
     return total_b, total_f, m, Et
 
 
-def measured_traffic(workload_is_default: bool):
+def measured_traffic(workload_is_default: bool, weights: str):
     """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
     FETCH_SIZE/WRITE_SIZE counters (copy-calibrated), or None when they were
     taken on other kernel sources or another workload."""
@@ -91,6 +96,8 @@ def measured_traffic(workload_is_default: bool):
         return None
     with open(path) as f:
         d = json.load(f)
+    if d.get("weights", "rowmajor") != weights:
+        return None
     h = hashlib.sha256()
     for src in d["kernel_sources"]:
         with open(os.path.join(ROOT, src), "rb") as f:
@@ -149,8 +156,17 @@ def main():
             lay.shared = dict(weights_from.shared, gate_logits=lay.shared["gate_logits"])
         return lay
 
-    def measure(layer, steps, warmup):
+    def weights_of(layer, packed):
+        """(w_gate, w_up, w_down, shared) of a layer in the timed layout."""
+        if not packed:
+            return layer.w_gate, layer.w_up, layer.w_down, layer.shared
+        return (pk["wg"], pk["wu"], pk["wd"],
+                None if layer.shared is None else dict(pk["shared"],
+                                                       gate_logits=layer.shared["gate_logits"]))
+
+    def measure(layer, steps, warmup, packed):
         T, H, F, E, k = layer.T, cfg.H, cfg.F, cfg.E, cfg.k
+        wg, wu, wd, sh = weights_of(layer, packed)
         Fs = cfg.Fs
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         ids = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -159,8 +175,7 @@ def main():
                          dtype=torch.uint8, device=dev)
 
         def step():
-            B.moe_forward(layer.x, layer.logits, k, layer.w_gate, layer.w_up,
-                          layer.w_down, shared=layer.shared, out=out,
+            B.moe_forward(layer.x, layer.logits, k, wg, wu, wd, shared=sh, out=out,
                           topk_ids=ids, topk_w=w, ws=ws, stream=stream)
 
         for _ in range(warmup):
@@ -177,33 +192,49 @@ def main():
         counts = torch.bincount(ids.flatten().long(), minlength=E).cpu().numpy()
         return ms, counts
 
-    def time_gateup(layer, steps):
+    def time_gateup(layer, steps, packed):
         """Average duration of the gate/up+SwiGLU grouped GEMM alone, with the
-        same inputs and launch configuration as inside moe_forward."""
+        same inputs, weights and launch configuration as inside the step."""
         k = cfg.k
+        wg, wu, _, _ = weights_of(layer, packed)
         ids, w = B.moe_route(layer.logits, k, stream=stream)
         off, rt, rd, xp = B.moe_permute(layer.x, ids, cfg.E, stream=stream)
         h = torch.empty((xp.shape[0], cfg.F), dtype=torch.bfloat16, device=dev)
         for _ in range(3):
-            B.moe_gateup_swiglu(xp, off, layer.w_gate, layer.w_up, h=h, stream=stream)
+            B.moe_gateup_swiglu(xp, off, wg, wu, h=h, stream=stream)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(steps):
-            B.moe_gateup_swiglu(xp, off, layer.w_gate, layer.w_up, h=h, stream=stream)
+            B.moe_gateup_swiglu(xp, off, wg, wu, h=h, stream=stream)
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
     # ---- headline workload ----
     layer = layer_for(args.T)
+    packed = args.weights == "packed"
     torch.cuda.synchronize()
-    ms, counts = measure(layer, args.steps, args.warmup)
+    # one-off weight packing (model-load time), timed on its own
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    pk = dict(wg=B.moe_pack_weights(layer.w_gate, stream=stream),
+              wu=B.moe_pack_weights(layer.w_up, stream=stream),
+              wd=B.moe_pack_weights(layer.w_down, stream=stream))
+    if layer.shared is not None:
+        pk["shared"] = {n: B.moe_pack_weights(layer.shared[n], stream=stream)
+                        for n in ("w_gate", "w_up", "w_down")}
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pack_ms = e0.elapsed_time(e1)
+    ms, counts = measure(layer, args.steps, args.warmup, packed)
+    ms_other, _ = measure(layer, max(10, args.steps // 2), 5, not packed)
     total_b, total_f, per_kernel, Et = work_model(cfg, args.T, counts)
     r = roof(total_b, total_f, ms)
 
-    g1_ms = time_gateup(layer, max(args.steps, 20))
+    g1_ms = time_gateup(layer, max(args.steps, 20), packed)
     g1 = per_kernel["gateup_swiglu_routed"]
     g1r = roof(g1["bytes"], g1["flops"], g1_ms)
     if g1r["bound"] == "hbm":
@@ -214,7 +245,7 @@ def main():
                         unit="TFLOP/s", frac=round(g1r["tflops"] / PEAK_BF16_TFLOPS, 4),
                         traffic=None)
     roofline["traffic"] = measured_traffic(args.config == "mixtral" and args.T == 32 and
-                                           args.seed == 0)
+                                           args.seed == 0, args.weights)
     roofline.update(kernel="grouped_gemm_kernel (gate/up + SwiGLU, routed experts)",
                     kernel_ms=round(g1_ms, 5),
                     alg_bytes=g1["bytes"], alg_flops=g1["flops"])
@@ -225,7 +256,7 @@ def main():
         if tok == args.T:
             continue
         lay = layer_for(tok, weights_from=layer)
-        ms_t, counts_t = measure(lay, max(10, args.steps // 2), 5)
+        ms_t, counts_t = measure(lay, max(10, args.steps // 2), 5, packed)
         b_t, f_t, _, et_t = work_model(cfg, tok, counts_t)
         rr = roof(b_t, f_t, ms_t)
         sweep.append(dict(T=tok, ms_per_step=round(ms_t, 5), GBs=round(rr["gbs"], 1),
@@ -267,7 +298,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; x~N(0,1), weights~N(0,0.02), logits~N(0,1))",
         "config": {"workload": f"{cfg.desc}: T={args.T}, H={cfg.H}, F={cfg.F}, E={cfg.E}, "
-                               f"top-{cfg.k}, bf16",
+                               f"top-{cfg.k}, bf16, {args.weights} weights",
+                   "weights": args.weights,
                    "T": args.T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "k": cfg.k,
                    "Fs": cfg.Fs, "experts_touched": Et, "parallelism": "none (1 GPU)"},
         "TFLOPs": round(r["tflops"], 3),
@@ -277,6 +309,8 @@ def main():
         "layer_roofline_frac": round(r["roofline_frac"], 4),
         "alg_bytes": total_b,
         "alg_flops": total_f,
+        "rowmajor_ms_per_step" if packed else "packed_ms_per_step": round(ms_other, 5),
+        "pack_ms": round(pack_ms, 3),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "sweep": sweep,

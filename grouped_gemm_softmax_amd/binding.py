@@ -50,6 +50,12 @@ _SIGNATURES = {
     "moe_forward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_forward": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P,
                          ctypes.POINTER(SharedExpert), _P, _P, _P, _P, _SZ, _P]),
+    "moe_pack_weights_bytes": (_SZ, [_I, _I, _I]),
+    "moe_pack_weights": (_I, [_P, _I, _I, _I, _P, _SZ, _P]),
+    "moe_gateup_swiglu_packed": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "moe_down_packed": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_forward_packed": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P,
+                                ctypes.POINTER(SharedExpert), _P, _P, _P, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -144,31 +150,73 @@ def moe_permute(x: torch.Tensor, topk_ids: torch.Tensor, E: int, ws=None, out=No
     return offsets, row_token, row_dest, x_perm
 
 
+class PackedWeight:
+    """A [G,K,N] weight tensor in the library's packed block layout (from
+    moe_pack_weights). `data` is the packed device buffer (uint8)."""
+
+    def __init__(self, data: torch.Tensor, G: int, K: int, N: int):
+        self.data, self.G, self.K, self.N = data, G, K, N
+        self.shape = (G, K, N)
+
+    def data_ptr(self) -> int:
+        return self.data.data_ptr()
+
+
+def moe_pack_weights_bytes(G: int, K: int, N: int) -> int:
+    return int(lib().moe_pack_weights_bytes(G, K, N))
+
+
+def moe_pack_weights(w: torch.Tensor, stream=None) -> PackedWeight:
+    """w bf16 [G,K,N] (or [K,N], taken as G = 1) -> PackedWeight."""
+    _need(w, torch.bfloat16, "w")
+    G, K, N = (1, *w.shape) if w.dim() == 2 else w.shape
+    nbytes = moe_pack_weights_bytes(G, K, N)
+    data = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=w.device)
+    _check(lib().moe_pack_weights(_ptr(w), G, K, N, _ptr(data), data.numel(),
+                                  _stream(stream)), "moe_pack_weights")
+    return PackedWeight(data, G, K, N)
+
+
+def _weight(w, name: str, packed: bool):
+    if packed:
+        if not isinstance(w, PackedWeight):
+            raise TypeError(f"{name}: expected a PackedWeight (moe_pack_weights)")
+    else:
+        _need(w, torch.bfloat16, name)
+    return w
+
+
 def moe_gateup_swiglu(x_perm, expert_offsets, w_gate, w_up, h=None, stream=None):
+    """w_gate, w_up: bf16 [E,H,F] tensors, or PackedWeight (packed call)."""
+    packed = isinstance(w_gate, PackedWeight)
     _need(x_perm, torch.bfloat16, "x_perm")
     _need(expert_offsets, torch.int32, "expert_offsets")
-    _need(w_gate, torch.bfloat16, "w_gate")
-    _need(w_up, torch.bfloat16, "w_up")
+    _weight(w_gate, "w_gate", packed)
+    _weight(w_up, "w_up", packed)
     M, H = x_perm.shape
     E, _, F = w_gate.shape
     if h is None:
         h = torch.empty((M, F), dtype=torch.bfloat16, device=x_perm.device)
-    _check(lib().moe_gateup_swiglu(_ptr(x_perm), _ptr(expert_offsets), M, H, F, E,
-                                   _ptr(w_gate), _ptr(w_up), _ptr(h), _stream(stream)),
-           "moe_gateup_swiglu")
+    fn = lib().moe_gateup_swiglu_packed if packed else lib().moe_gateup_swiglu
+    _check(fn(_ptr(x_perm), _ptr(expert_offsets), M, H, F, E, _ptr(w_gate), _ptr(w_up),
+              _ptr(h), _stream(stream)),
+           "moe_gateup_swiglu_packed" if packed else "moe_gateup_swiglu")
     return h
 
 
 def moe_down(h, expert_offsets, w_down, y_perm=None, stream=None):
+    """w_down: bf16 [E,F,H] tensor, or PackedWeight (packed call)."""
+    packed = isinstance(w_down, PackedWeight)
     _need(h, torch.bfloat16, "h")
     _need(expert_offsets, torch.int32, "expert_offsets")
-    _need(w_down, torch.bfloat16, "w_down")
+    _weight(w_down, "w_down", packed)
     M, F = h.shape
     E, _, H = w_down.shape
     if y_perm is None:
         y_perm = torch.empty((M, H), dtype=torch.bfloat16, device=h.device)
-    _check(lib().moe_down(_ptr(h), _ptr(expert_offsets), M, F, H, E, _ptr(w_down),
-                          _ptr(y_perm), _stream(stream)), "moe_down")
+    fn = lib().moe_down_packed if packed else lib().moe_down
+    _check(fn(_ptr(h), _ptr(expert_offsets), M, F, H, E, _ptr(w_down), _ptr(y_perm),
+              _stream(stream)), "moe_down_packed" if packed else "moe_down")
     return y_perm
 
 
@@ -210,17 +258,22 @@ def moe_forward_workspace_bytes(T, H, F, E, k, Fs=0) -> int:
 def moe_forward(x, logits, k, w_gate, w_up, w_down, shared: Optional[dict] = None,
                 out=None, topk_ids=None, topk_w=None, ws=None, stream=None):
     """Whole layer. shared: None or dict(w_gate [H,Fs], w_up [H,Fs],
-    w_down [Fs,H], gate_logits [T] fp32 or None). Returns out [T,H] bf16."""
+    w_down [Fs,H], gate_logits [T] fp32 or None). Returns out [T,H] bf16.
+    With PackedWeight weights (all of them, shared expert included: packed
+    from [1,H,Fs] / [1,Fs,H]) this calls moe_forward_packed."""
+    packed = isinstance(w_gate, PackedWeight)
     _need(x, torch.bfloat16, "x")
     _need(logits, torch.float32, "logits")
     for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
-        _need(t, torch.bfloat16, n)
+        _weight(t, n, packed)
     T, H = x.shape
     E, _, F = w_gate.shape
     sh = None
     Fs = 0
     if shared is not None:
-        Fs = shared["w_gate"].shape[1]
+        for n in ("w_gate", "w_up", "w_down"):
+            _weight(shared[n], "shared " + n, packed)
+        Fs = shared["w_gate"].shape[-1]
         g = shared.get("gate_logits")
         sh = SharedExpert(shared["w_gate"].data_ptr(), shared["w_up"].data_ptr(),
                           shared["w_down"].data_ptr(), Fs,
@@ -230,9 +283,9 @@ def moe_forward(x, logits, k, w_gate, w_up, w_down, shared: Optional[dict] = Non
     if ws is None:
         ws = torch.empty(max(moe_forward_workspace_bytes(T, H, F, E, k, Fs), 16),
                          dtype=torch.uint8, device=x.device)
-    _check(lib().moe_forward(_ptr(x), _ptr(logits), T, H, F, E, k, _ptr(w_gate),
-                             _ptr(w_up), _ptr(w_down),
-                             ctypes.byref(sh) if sh is not None else None, _ptr(out),
-                             _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(),
-                             _stream(stream)), "moe_forward")
+    fn = lib().moe_forward_packed if packed else lib().moe_forward
+    _check(fn(_ptr(x), _ptr(logits), T, H, F, E, k, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+              ctypes.byref(sh) if sh is not None else None, _ptr(out), _ptr(topk_ids),
+              _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_forward_packed" if packed else "moe_forward")
     return out

@@ -71,12 +71,12 @@ struct ForwardLayout {
 };
 
 moe::GemmProblem down_problem(const bf16_t* h, const int32_t* offsets, int M, int F,
-                              int H, int E, const bf16_t* wd, void* y);
+                              int H, int E, const bf16_t* wd, void* y, bool packed);
 
 // The fused layer's down projection (routed + optional shared segment) with
 // fp32 output; pointers may be null when only the shape matters.
 moe::GemmProblem forward_down_problem(int T, int H, int F, int E, int k, int Fs) {
-  moe::GemmProblem g2 = down_problem(nullptr, nullptr, T * k, F, H, E, nullptr, nullptr);
+  moe::GemmProblem g2 = down_problem(nullptr, nullptr, T * k, F, H, E, nullptr, nullptr, false);
   g2.out_f32 = true;
   if (Fs > 0) {
     g2.seg[1] = moe::GemmSegment{nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, T, 1, Fs, H};
@@ -107,12 +107,17 @@ ForwardLayout forward_layout(int T, int H, int F, int E, int k, int Fs, int cus)
   return L;
 }
 
+// Elements between consecutive experts' weight matrices [K][N].
+int64_t weight_stride(int K, int N, bool packed) {
+  return packed ? moe::packed_weight_elems(1, K, N) : static_cast<int64_t>(K) * N;
+}
+
 moe::GemmProblem gateup_problem(const bf16_t* x_perm, const int32_t* offsets, int M,
                                 int H, int F, int E, const bf16_t* wg,
-                                const bf16_t* wu, bf16_t* h) {
+                                const bf16_t* wu, bf16_t* h, bool packed) {
   moe::GemmProblem p{};
   p.seg[0] = moe::GemmSegment{x_perm, offsets, wg, wu, h,
-                              static_cast<int64_t>(H) * F, 0, M, E, H, F};
+                              weight_stride(H, F, packed), 0, M, E, H, F, packed};
   p.nseg = 1;
   p.gated = true;
   p.rows_hint = M / E;
@@ -121,10 +126,10 @@ moe::GemmProblem gateup_problem(const bf16_t* x_perm, const int32_t* offsets, in
 }
 
 moe::GemmProblem down_problem(const bf16_t* h, const int32_t* offsets, int M, int F,
-                              int H, int E, const bf16_t* wd, void* y) {
+                              int H, int E, const bf16_t* wd, void* y, bool packed) {
   moe::GemmProblem p{};
   p.seg[0] = moe::GemmSegment{h, offsets, wd, nullptr, y,
-                              static_cast<int64_t>(F) * H, 0, M, E, F, H};
+                              weight_stride(F, H, packed), 0, M, E, F, H, packed};
   p.nseg = 1;
   p.gated = false;
   p.rows_hint = M / E;
@@ -204,23 +209,64 @@ int moe_permute(const moe_bf16* x, const int32_t* topk_ids, int T, int H, int E,
                                         row_token, row_dest, x_perm, s));
 }
 
-int moe_gateup_swiglu(const moe_bf16* x_perm, const int32_t* expert_offsets, int M,
-                      int H, int F, int E, const moe_bf16* w_gate,
-                      const moe_bf16* w_up, moe_bf16* h, void* stream) {
+static int gateup_impl(const moe_bf16* x_perm, const int32_t* expert_offsets, int M, int H,
+                       int F, int E, const moe_bf16* w_gate, const moe_bf16* w_up, moe_bf16* h,
+                       void* stream, bool packed) {
   MOE_TRY(check_ffn_args(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, true, h));
   if (M == 0) return MOE_OK;
   return hip_status(moe::launch_grouped_gemm(
-      gateup_problem(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, h),
+      gateup_problem(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, h, packed),
       static_cast<hipStream_t>(stream)));
+}
+
+static int down_impl(const moe_bf16* h, const int32_t* expert_offsets, int M, int F, int H,
+                     int E, const moe_bf16* w_down, moe_bf16* y_perm, void* stream,
+                     bool packed) {
+  MOE_TRY(check_ffn_args(h, expert_offsets, M, F, H, E, w_down, nullptr, false, y_perm));
+  if (M == 0) return MOE_OK;
+  return hip_status(moe::launch_grouped_gemm(
+      down_problem(h, expert_offsets, M, F, H, E, w_down, y_perm, packed),
+      static_cast<hipStream_t>(stream)));
+}
+
+int moe_gateup_swiglu(const moe_bf16* x_perm, const int32_t* expert_offsets, int M,
+                      int H, int F, int E, const moe_bf16* w_gate,
+                      const moe_bf16* w_up, moe_bf16* h, void* stream) {
+  return gateup_impl(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, h, stream, false);
+}
+
+int moe_gateup_swiglu_packed(const moe_bf16* x_perm, const int32_t* expert_offsets, int M,
+                             int H, int F, int E, const moe_bf16* w_gate_packed,
+                             const moe_bf16* w_up_packed, moe_bf16* h, void* stream) {
+  return gateup_impl(x_perm, expert_offsets, M, H, F, E, w_gate_packed, w_up_packed, h,
+                     stream, true);
 }
 
 int moe_down(const moe_bf16* h, const int32_t* expert_offsets, int M, int F, int H,
              int E, const moe_bf16* w_down, moe_bf16* y_perm, void* stream) {
-  MOE_TRY(check_ffn_args(h, expert_offsets, M, F, H, E, w_down, nullptr, false, y_perm));
-  if (M == 0) return MOE_OK;
-  return hip_status(moe::launch_grouped_gemm(
-      down_problem(h, expert_offsets, M, F, H, E, w_down, y_perm),
-      static_cast<hipStream_t>(stream)));
+  return down_impl(h, expert_offsets, M, F, H, E, w_down, y_perm, stream, false);
+}
+
+int moe_down_packed(const moe_bf16* h, const int32_t* expert_offsets, int M, int F, int H,
+                    int E, const moe_bf16* w_down_packed, moe_bf16* y_perm, void* stream) {
+  return down_impl(h, expert_offsets, M, F, H, E, w_down_packed, y_perm, stream, true);
+}
+
+size_t moe_pack_weights_bytes(int G, int K, int N) {
+  if (G < 1 || check_width(K) != MOE_OK || check_width(N) != MOE_OK) return 0;
+  return static_cast<size_t>(moe::packed_weight_elems(G, K, N)) * sizeof(bf16_t);
+}
+
+int moe_pack_weights(const moe_bf16* w, int G, int K, int N, moe_bf16* packed,
+                     size_t packed_bytes, void* stream) {
+  if (G < 1) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_width(K));
+  MOE_TRY(check_width(N));
+  MOE_TRY(need_bf16(w));
+  MOE_TRY(need_bf16(packed));
+  if (packed_bytes < moe_pack_weights_bytes(G, K, N)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(moe::launch_pack_weights(w, G, K, N, packed,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 int moe_grouped_ffn(const moe_bf16* x_perm, const int32_t* expert_offsets, int M,
@@ -232,9 +278,9 @@ int moe_grouped_ffn(const moe_bf16* x_perm, const int32_t* expert_offsets, int M
   if (M == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   MOE_TRY(hip_status(moe::launch_grouped_gemm(
-      gateup_problem(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, h), s)));
+      gateup_problem(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, h, false), s)));
   return hip_status(moe::launch_grouped_gemm(
-      down_problem(h, expert_offsets, M, F, H, E, w_down, y_perm), s));
+      down_problem(h, expert_offsets, M, F, H, E, w_down, y_perm, false), s));
 }
 
 int moe_combine(const moe_bf16* y_perm, const int32_t* row_dest, const float* topk_w,
@@ -260,11 +306,11 @@ size_t moe_forward_workspace_bytes(int T, int H, int F, int E, int k, int Fs) {
   return forward_layout(T, H, F, E, k, Fs, moe::grouped_gemm_device_cus()).total;
 }
 
-int moe_forward(const moe_bf16* x, const float* logits, int T, int H, int F, int E,
-                int k, const moe_bf16* w_gate, const moe_bf16* w_up,
-                const moe_bf16* w_down, const moe_shared_expert* shared,
-                moe_bf16* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
-                size_t ws_bytes, void* stream) {
+static int forward_impl(const moe_bf16* x, const float* logits, int T, int H, int F, int E,
+                        int k, const moe_bf16* w_gate, const moe_bf16* w_up,
+                        const moe_bf16* w_down, const moe_shared_expert* shared,
+                        moe_bf16* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                        size_t ws_bytes, void* stream, bool packed) {
   MOE_TRY(check_dims(T, E, k));
   MOE_TRY(check_width(H));
   MOE_TRY(check_width(F));
@@ -314,20 +360,21 @@ int moe_forward(const moe_bf16* x, const float* logits, int T, int H, int F, int
   MOE_TRY(hip_status(moe::launch_permute(x, ids, T, H, E, k, hist, offsets, row_token,
                                          row_dest, x_perm, s)));
   // 3. grouped gate/up + SwiGLU (shared expert as one more group over x)
-  moe::GemmProblem g1 = gateup_problem(x_perm, offsets, M, H, F, E, w_gate, w_up, h);
+  moe::GemmProblem g1 = gateup_problem(x_perm, offsets, M, H, F, E, w_gate, w_up, h, packed);
   if (shared) {
-    g1.seg[1] = moe::GemmSegment{x, nullptr, shared->w_gate, shared->w_up, h_sh, 0, 0, T, 1, H, Fs};
+    g1.seg[1] = moe::GemmSegment{x, nullptr, shared->w_gate, shared->w_up, h_sh, 0, 0, T, 1, H, Fs,
+                                 packed};
     g1.nseg = 2;
   }
   MOE_TRY(hip_status(moe::launch_grouped_gemm(g1, s)));
   // 4. grouped down (shared expert likewise)
-  moe::GemmProblem g2 = down_problem(h, offsets, M, F, H, E, w_down, y);
+  moe::GemmProblem g2 = down_problem(h, offsets, M, F, H, E, w_down, y, packed);
   g2.out_f32 = true;
   g2.ksplit = L.ksplit;
   g2.seg[0].slice_stride = static_cast<int64_t>(M) * H;
   if (shared) {
     g2.seg[1] = moe::GemmSegment{h_sh, nullptr, shared->w_down, nullptr, y_sh, 0,
-                                 static_cast<int64_t>(T) * H, T, 1, Fs, H};
+                                 static_cast<int64_t>(T) * H, T, 1, Fs, H, packed};
     g2.nseg = 2;
   }
   MOE_TRY(hip_status(moe::launch_grouped_gemm(g2, s)));
@@ -336,6 +383,24 @@ int moe_forward(const moe_bf16* x, const float* logits, int T, int H, int F, int
                                         row_dest, w, T, H, k, shared ? y_sh : nullptr,
                                         static_cast<int64_t>(T) * H,
                                         shared ? shared->gate_logits : nullptr, out, s));
+}
+
+int moe_forward(const moe_bf16* x, const float* logits, int T, int H, int F, int E,
+                int k, const moe_bf16* w_gate, const moe_bf16* w_up,
+                const moe_bf16* w_down, const moe_shared_expert* shared,
+                moe_bf16* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                size_t ws_bytes, void* stream) {
+  return forward_impl(x, logits, T, H, F, E, k, w_gate, w_up, w_down, shared, out,
+                      topk_ids_out, topk_w_out, ws, ws_bytes, stream, false);
+}
+
+int moe_forward_packed(const moe_bf16* x, const float* logits, int T, int H, int F, int E,
+                       int k, const moe_bf16* w_gate_packed, const moe_bf16* w_up_packed,
+                       const moe_bf16* w_down_packed, const moe_shared_expert* shared_packed,
+                       moe_bf16* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  return forward_impl(x, logits, T, H, F, E, k, w_gate_packed, w_up_packed, w_down_packed,
+                      shared_packed, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -147,6 +147,8 @@ struct TileCfg {
   static constexpr int FF = TF / 16;  // MFMA blocks per wave (columns)
   static constexpr int FT = TT / 16;  // MFMA blocks per wave (tokens)
   static constexpr int W_BYTES = BK * BF * 2;  // one weight matrix per stage
+  static constexpr int SB = BF / 64;           // 64-column sub-blocks per matrix
+  static constexpr int SB_BYTES = BK * 128;    // one sub-block: BK rows of 128 bytes
   static constexpr int X_BYTES = BT * BK * 2;
   static constexpr int STAGE_BYTES = NMAT * W_BYTES + X_BYTES;
   static constexpr int INSTR = STAGE_BYTES / 1024;  // 1 KB DMA instructions
@@ -166,17 +168,18 @@ struct TileCfg {
 
 // 16-byte chunk swizzles (chunk index within a row), chosen by measuring
 // LDS throughput of each access pattern on gfx950.
-// Weights: the 4 rows a 16-lane transpose read touches land in 4 distinct
-// chunk pairs (XOR 2*(row%4)), and the row groups 8 apart that other lanes of
-// the same instruction read land on the other bank half (XOR 8 for rows of
-// >= 256 bytes, XOR 2 for 128-byte rows). Rows r and r+4, read by one lane,
-// share the swizzle. Activations: 8 consecutive token rows at the same K
+// Weights are held as 64-column sub-blocks with 128-byte rows: the 4 rows a
+// 16-lane transpose read touches land in 4 distinct chunk pairs
+// (XOR 2*(row%4)), and the row groups 8 apart that other lanes of the same
+// instruction read land on the other bank half (XOR 2*((row/8)%2)). Rows r
+// and r+4, read by one lane, share the swizzle (bit 2 of the row is unused;
+// so do rows r and r+32, which lets a 32-deep stage read half of a packed
+// 64-row block). Activations: 8 consecutive token rows at the same K
 // chunk land in 8 distinct 16-byte bank groups: with rows of >= 128 bytes the
 // chunk is XORed with row % 8; with 64-byte rows (BK = 32) two rows share a
 // 128-byte window, so row % 2 picks the half and (row / 2) % 4 is XORed in.
-template <int BF>
 __device__ __forceinline__ int swz_w(int row, int chunk) {
-  return chunk ^ ((row & 3) << 1) ^ (((row >> 3) & 1) << (BF >= 128 ? 3 : 1));
+  return chunk ^ ((row & 3) << 1) ^ (((row >> 3) & 1) << 1);
 }
 template <int BK>
 __device__ __forceinline__ int swz_x(int row, int chunk) {
@@ -216,7 +219,7 @@ __device__ __forceinline__ void store4(float* p, const float v[4]) {
   *reinterpret_cast<float4*>(p) = float4{v[0], v[1], v[2], v[3]};
 }
 
-template <class C, typename OutT, bool KTAIL>
+template <class C, typename OutT, bool KTAIL, bool PACKED>
 __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem prob) {
   __shared__ __attribute__((aligned(1024))) char st0[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[C::STAGE_BYTES];
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
   }
 
   constexpr int W_PER_MAT = C::W_BYTES / 1024;   // DMA instructions per weight matrix
-  constexpr int RPI_W = 1024 / (C::BF * 2);      // weight rows per instruction
+  constexpr int IPS = C::BK / 8;                 // instructions per weight sub-block
   constexpr int RPI_X = 1024 / (C::BK * 2);      // activation rows per instruction
 
   // ---- one work item: where its operands are, its K range, its output ----
@@ -314,6 +317,7 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
     int kt_begin;     // first K-step (BK each) of the slice
     int nk;           // K-steps of the slice
     int nk_all;       // K-steps of the whole K
+    int nblk, kblk;   // packed: 64-column and 64-row blocks of one group
     // per-lane byte offsets of this wave's DMA sources within a K-step,
     // relative to the step's scalar base
     uint32_t voff[C::IPW];
@@ -349,6 +353,8 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
     it.kt_begin = ks * per;
     it.nk = min(nk_all, it.kt_begin + per) - it.kt_begin;
     it.nk_all = nk_all;
+    it.nblk = (S.N + 63) / 64;
+    it.kblk = (S.K + 63) / 64;
     it.w0 = S.w0 + static_cast<int64_t>(v.local) * S.w_stride;
     it.w1 = C::GATED ? S.w1 + static_cast<int64_t>(v.local) * S.w_stride : it.w0;
     it.x = S.act;
@@ -366,15 +372,19 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
     it.kt_begin = __builtin_amdgcn_readfirstlane(it.kt_begin);
     it.nk = __builtin_amdgcn_readfirstlane(it.nk);
     it.nk_all = __builtin_amdgcn_readfirstlane(it.nk_all);
+    it.nblk = __builtin_amdgcn_readfirstlane(it.nblk);
+    it.kblk = __builtin_amdgcn_readfirstlane(it.kblk);
     {
 #pragma unroll
       for (int i = 0; i < C::IPW; ++i) {
         const int j = i * C::NW + wave;
         if (i < C::W_INSTR / C::NW) {
           const int mat = i / (W_PER_MAT / C::NW);
-          const int r = (j - mat * W_PER_MAT) * RPI_W + lane / (C::BF / 8);
-          const int col = min(it.n0 + swz_w<C::BF>(r, lane % (C::BF / 8)) * 8, it.N - 8);
-          it.voff[i] = static_cast<uint32_t>(r * it.N + col) * 2u;
+          const int jj = j - mat * W_PER_MAT;  // instruction within the matrix
+          const int r = (jj % IPS) * 8 + lane / 8;
+          const int col = min(it.n0 + (jj / IPS) * 64 + swz_w(r, lane % 8) * 8, it.N - 8);
+          it.voff[i] = PACKED ? static_cast<uint32_t>(lane) * 16u
+                                 : static_cast<uint32_t>(r * it.N + col) * 2u;
         } else {
           const int r = (j - C::W_INSTR) * RPI_X + lane / (C::BK / 8);
           const int kc = swz_x<C::BK>(r, lane % (C::BK / 8)) * 8;
@@ -388,12 +398,15 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
   // ---- DMA of one K-step of an item into one ring buffer ----
   // Instruction i of this wave fills 16-byte slots 64*j .. 64*j+63 of the
   // stage, j = i*NW + wave, so whether it loads weights (and which matrix)
-  // or activations is known at compile time. The lane's slot is a tile
-  // (row, physical chunk); the swizzle gives the logical chunk, hence the
-  // global source. Rows and columns are clamped to the valid range: clamped
-  // lanes fetch finite in-bounds data whose products only reach masked
-  // outputs or the zeroed K-tail rows (K-steps past the item's range load
-  // rows that are in bounds and never used).
+  // or activations is known at compile time. A weight instruction fills 8
+  // rows of one 64-column sub-block; an activation instruction whole rows of
+  // the [BT][BK] tile. The lane's slot is a tile (row, physical chunk); the
+  // swizzle gives the logical chunk, hence the global source (row-major
+  // weights), or the packed weights hold the block in LDS order already.
+  // Rows and columns are clamped to the valid range: clamped lanes fetch
+  // finite in-bounds data whose products only reach masked outputs or
+  // activation columns past K, whose fragments are zeroed (K-steps past the
+  // item's range load rows that are in bounds and never used).
   auto issue = [&](const ItemInfo& it, int kt, char* buf) INL {
     // Steps past the item's range re-load the last step of K. Each source is
     // a scalar base (matrix, step) plus the item's lane offset; in the last
@@ -409,10 +422,21 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
       uint32_t voff = it.voff[i];
       if (i < C::W_INSTR / C::NW) {
         const int mat = i / (W_PER_MAT / C::NW);
-        base = (mat ? it.w1 : it.w0) + k0 * it.N;
-        if constexpr (KTAIL) {
-          const int r = (j - mat * W_PER_MAT) * RPI_W + lane / (C::BF / 8);
-          if (r >= kleft) voff -= static_cast<uint32_t>((r - kleft + 1) * it.N) * 2u;
+        const int jj = j - mat * W_PER_MAT;  // instruction within the matrix
+        const bf16_t* const w = mat ? it.w1 : it.w0;
+        if constexpr (PACKED) {
+          // 64x64 blocks in LDS order, [n-block][k-block]; the instruction
+          // copies 8 consecutive rows (1 KB) of one block. Sub-blocks past N
+          // re-load the last block (their outputs are masked).
+          const int nb = min(it.n0 / 64 + jj / IPS, it.nblk - 1);
+          const int krow = static_cast<int>(k0) + (jj % IPS) * 8;
+          base = w + (static_cast<int64_t>(nb) * it.kblk + krow / 64) * 4096 + (krow % 64) * 64;
+        } else {
+          base = w + k0 * it.N;
+          if constexpr (KTAIL) {
+            const int r = (jj % IPS) * 8 + lane / 8;
+            if (r >= kleft) voff -= static_cast<uint32_t>((r - kleft + 1) * it.N) * 2u;
+          }
         }
       } else {
         base = it.x + static_cast<int64_t>(it.row_base) * it.K + k0;
@@ -436,10 +460,12 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
   auto weight_frag = [&](const char* buf, int s, int m, int fi) INL {
     const int row = s * 32 + 8 * g16 + (i16 >> 2);          // k within the stage
     const int col = wf * C::TF + fi * 16 + 4 * (i16 & 3);   // column within the tile
-    const int chunk = swz_w<C::BF>(row, col >> 3);           // rows row, row+4 share it
-    const char* p = buf + m * C::W_BYTES + row * (C::BF * 2) + chunk * 16 + (col & 7) * 2;
+    const int c64 = col & 63;                                // column within the sub-block
+    const int chunk = swz_w(row, c64 >> 3);                  // rows row, row+4 share it
+    const char* p = buf + m * C::W_BYTES + (col >> 6) * C::SB_BYTES + row * 128 + chunk * 16 +
+                    (c64 & 7) * 2;
     const short4_t lo4 = lds_read_tr16(p);
-    const short4_t hi4 = lds_read_tr16(p + 4 * C::BF * 2);
+    const short4_t hi4 = lds_read_tr16(p + 4 * 128);
     typedef short short8_t __attribute__((ext_vector_type(8)));
     const short8_t s8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
     return __builtin_bit_cast(bf16x8, s8);
@@ -675,7 +701,7 @@ int device_cu_count() {
 }
 
 // Resident workgroups per CU for a launch with `dyn` bytes of dynamic LDS.
-template <class C, typename OutT, bool KTAIL>
+template <class C, typename OutT, bool KTAIL, bool PACKED>
 int blocks_per_cu(size_t dyn) {
   static int cached_n[64] = {0};
   static size_t cached_dyn[64] = {0};
@@ -684,8 +710,8 @@ int blocks_per_cu(size_t dyn) {
   if (cached_n[dev] == 0 || cached_dyn[dev] != dyn) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(grouped_gemm_kernel<C, OutT, KTAIL>), C::kThreads,
-            dyn) != hipSuccess || n <= 0)
+            &n, reinterpret_cast<const void*>(grouped_gemm_kernel<C, OutT, KTAIL, PACKED>),
+            C::kThreads, dyn) != hipSuccess || n <= 0)
       n = 1;
     cached_n[dev] = n;
     cached_dyn[dev] = dyn;
@@ -705,17 +731,18 @@ int64_t item_bound(const GemmProblem& p) {
   return bound;
 }
 
-template <class C, typename OutT, bool KTAIL>
+template <class C, typename OutT, bool KTAIL, bool PACKED>
 hipError_t launch_tail(const GemmProblem& p, int64_t bound, hipStream_t stream) {
   int groups = 0;
   for (int s = 0; s < p.nseg; ++s) groups += p.seg[s].ngroups;
   const size_t dyn = static_cast<size_t>((groups + 2) & ~1) * sizeof(int) +
                     static_cast<size_t>(groups) * sizeof(int2);
-  int64_t grid = static_cast<int64_t>(device_cu_count()) * blocks_per_cu<C, OutT, KTAIL>(dyn);
+  int64_t grid =
+      static_cast<int64_t>(device_cu_count()) * blocks_per_cu<C, OutT, KTAIL, PACKED>(dyn);
   if (bound < grid) grid = bound;
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL((grouped_gemm_kernel<C, OutT, KTAIL>), dim3(static_cast<unsigned>(grid)),
-                     dim3(C::kThreads), dyn, stream, p);
+  hipLaunchKernelGGL((grouped_gemm_kernel<C, OutT, KTAIL, PACKED>),
+                     dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), dyn, stream, p);
   return hipGetLastError();
 }
 
@@ -725,8 +752,14 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   if (bound <= 0) return hipSuccess;
   bool ktail = false;
   for (int s = 0; s < p.nseg; ++s) ktail = ktail || (p.seg[s].K % C::BK != 0);
-  return ktail ? launch_tail<C, OutT, true>(p, bound, stream)
-               : launch_tail<C, OutT, false>(p, bound, stream);
+  const bool packed = p.seg[0].packed != 0;
+  for (int s = 1; s < p.nseg; ++s)
+    if ((p.seg[s].packed != 0) != packed) return hipErrorInvalidValue;  // one layout per launch
+  if (packed)
+    return ktail ? launch_tail<C, OutT, true, true>(p, bound, stream)
+                 : launch_tail<C, OutT, false, true>(p, bound, stream);
+  return ktail ? launch_tail<C, OutT, true, false>(p, bound, stream)
+               : launch_tail<C, OutT, false, false>(p, bound, stream);
 }
 
 }  // namespace
@@ -777,6 +810,46 @@ int grouped_gemm_ksplit_hint(const GemmProblem& p, int cus) {
 }
 
 int grouped_gemm_device_cus() { return device_cu_count(); }
+
+namespace {
+
+// Packed weights: one thread per 16-byte chunk of the packed tensor, in
+// order (block, row, physical chunk); the chunk holds the 8 columns that the
+// GEMM's LDS swizzle puts there, or zeros past K or N.
+__global__ __launch_bounds__(256) void pack_weights_kernel(
+    const bf16_t* __restrict__ w, int K, int N, int nblk, int kblk, int64_t chunks,
+    bf16_t* __restrict__ out) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= chunks) return;
+  const int pc = static_cast<int>(idx & 7);
+  const int r = static_cast<int>((idx >> 3) & 63);
+  int64_t blk = idx >> 9;
+  const int kb = static_cast<int>(blk % kblk);
+  blk /= kblk;
+  const int nb = static_cast<int>(blk % nblk);
+  const int64_t g = blk / nblk;
+  const int k = kb * 64 + r;
+  const int n = nb * 64 + swz_w(r, pc) * 8;
+  uint4 v = uint4{0u, 0u, 0u, 0u};
+  if (k < K && n < N) v = *reinterpret_cast<const uint4*>(w + (g * K + k) * N + n);
+  reinterpret_cast<uint4*>(out)[idx] = v;
+}
+
+}  // namespace
+
+int64_t packed_weight_elems(int G, int K, int N) {
+  return static_cast<int64_t>(G) * ((N + 63) / 64) * ((K + 63) / 64) * 4096;
+}
+
+hipError_t launch_pack_weights(const bf16_t* w, int G, int K, int N, bf16_t* packed,
+                               hipStream_t stream) {
+  const int64_t chunks = packed_weight_elems(G, K, N) / 8;
+  if (chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)),
+                     dim3(256), 0, stream, w, K, N, (N + 63) / 64, (K + 63) / 64, chunks,
+                     packed);
+  return hipGetLastError();
+}
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
   const int tc = tile_class(p);

@@ -33,7 +33,8 @@ hipError_t launch_permute(const bf16_t* x, const int32_t* topk_ids, int T,
 // A segment is a list of groups that share K, N and the weight layout.
 // Group g owns activation rows [offsets[g], offsets[g+1]) of `act`
 // (offsets == nullptr: one group, rows [0, rows)); its weights are
-// w0 + g*w_stride ([K][N], N contiguous), and w1 likewise when gated.
+// w0 + g*w_stride ([K][N], N contiguous, or the packed block layout of
+// pack_weights), and w1 likewise when gated.
 struct GemmSegment {
   const bf16_t* act;       // [rows, K]
   const int32_t* offsets;  // device [ngroups+1] or nullptr
@@ -46,6 +47,7 @@ struct GemmSegment {
   int ngroups;
   int K;
   int N;
+  int packed;              // weights in the packed block layout
 };
 
 struct GemmProblem {
@@ -61,6 +63,14 @@ hipError_t launch_grouped_gemm(const GemmProblem& prob, hipStream_t stream);
 // K-slices worth using for `prob` on a device with `cus` compute units.
 int grouped_gemm_ksplit_hint(const GemmProblem& prob, int cus);
 int grouped_gemm_device_cus();
+
+// Packed weights: W [G][K][N] as G x ceil(N/64) x ceil(K/64) blocks of
+// 64 x 64 (block (g, nb, kb) at element ((g*NB + nb)*KB + kb)*4096), each
+// in the GEMM's LDS order (128-byte rows, swizzled 16-byte chunks), zero
+// past K and N. A K-step of a decode-size tile is then one contiguous read.
+int64_t packed_weight_elems(int G, int K, int N);
+hipError_t launch_pack_weights(const bf16_t* w, int G, int K, int N, bf16_t* packed,
+                               hipStream_t stream);
 
 // --- combine (combine.hip) ---
 // y_perm/y_shared hold bf16 values (y_f32 == false) or fp32 values; with

@@ -166,13 +166,66 @@ size_t moe_forward_workspace_bytes(int T, int H, int F, int E, int k, int Fs);
  *   topk_ids_out int32 [T,k], topk_w_out fp32 [T,k]: optional device copies
  *   of the routing result (NULL: kept in the workspace);
  *   ws: at least moe_forward_workspace_bytes(...) device bytes of scratch.
- * Results equal route -> permute -> grouped_ffn -> combine through the split
- * calls, plus the shared term. */
+ * Results match route -> permute -> grouped_ffn -> combine through the split
+ * calls, plus the shared term, except that the down projection's output
+ * reaches the combine in fp32 here (the split calls round y_perm to bf16). */
 int moe_forward(const moe_bf16* x, const float* logits, int T, int H, int F,
                 int E, int k, const moe_bf16* w_gate, const moe_bf16* w_up,
                 const moe_bf16* w_down, const moe_shared_expert* shared,
                 moe_bf16* out, int32_t* topk_ids_out, float* topk_w_out,
                 void* ws, size_t ws_bytes, void* stream);
+
+/* ---- Packed weights ----
+ * Expert weights do not change between calls, so they can be re-laid out
+ * once, when they are loaded, into the order in which the grouped GEMM
+ * streams them. With the row-major layout a decode-size tile reads every
+ * K-step as 64 rows of 128 bytes spaced 2*N bytes apart; with the packed
+ * layout it reads one contiguous run, which HBM delivers faster (the layer
+ * at small batch is bound by streaming the weights). Results are identical
+ * to the row-major calls (the same products are summed in the same order).
+ * This re-layout is not on the pages; it is this library's addition.
+ *
+ * The packed form of W [G,K,N] (row-major; G groups: E experts, or 1 for a
+ * shared expert) occupies moe_pack_weights_bytes(G,K,N) =
+ * G * ceil(N/64) * ceil(K/64) * 8192 bytes: blocks of 64 K-rows by 64
+ * columns, block (g, nb, kb) at byte ((g*ceil(N/64) + nb)*ceil(K/64) + kb)*8192,
+ * each row of a block 128 bytes holding the block's 64 columns as eight
+ * 8-column chunks in a swizzled order, zero past K and past N. The order is
+ * private to this library: produce packed tensors with moe_pack_weights. */
+
+/* Packed size in bytes of a [G,K,N] weight tensor; 0 for invalid sizes
+ * (G < 1, K or N not a positive multiple of 8). */
+size_t moe_pack_weights_bytes(int G, int K, int N);
+
+/* w bf16 [G,K,N] (row-major) -> packed (device, at least
+ * moe_pack_weights_bytes(G,K,N) bytes, 16-byte aligned, not overlapping w).
+ * One kernel on `stream`; w is only read. */
+int moe_pack_weights(const moe_bf16* w, int G, int K, int N, moe_bf16* packed,
+                     size_t packed_bytes, void* stream);
+
+/* moe_gateup_swiglu with w_gate, w_up packed from [E,H,F]. */
+int moe_gateup_swiglu_packed(const moe_bf16* x_perm,
+                             const int32_t* expert_offsets, int M, int H,
+                             int F, int E, const moe_bf16* w_gate_packed,
+                             const moe_bf16* w_up_packed, moe_bf16* h,
+                             void* stream);
+
+/* moe_down with w_down packed from [E,F,H]. */
+int moe_down_packed(const moe_bf16* h, const int32_t* expert_offsets, int M,
+                    int F, int H, int E, const moe_bf16* w_down_packed,
+                    moe_bf16* y_perm, void* stream);
+
+/* moe_forward with packed weights: w_gate, w_up packed from [E,H,F],
+ * w_down from [E,F,H]; when a shared expert is given, its w_gate and w_up
+ * are packed from [1,H,Fs] and its w_down from [1,Fs,H]. Same workspace
+ * (moe_forward_workspace_bytes) and outputs as moe_forward. */
+int moe_forward_packed(const moe_bf16* x, const float* logits, int T, int H,
+                       int F, int E, int k, const moe_bf16* w_gate_packed,
+                       const moe_bf16* w_up_packed,
+                       const moe_bf16* w_down_packed,
+                       const moe_shared_expert* shared_packed, moe_bf16* out,
+                       int32_t* topk_ids_out, float* topk_w_out, void* ws,
+                       size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

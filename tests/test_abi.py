@@ -147,3 +147,30 @@ def test_forward_workspace_bytes(T, H, F, E, k, Fs):
     if (T, H) == (1, 4096):
         assert _down_ksplit(T, H, F, E, k, Fs) == 4    # two experts: 128 items -> split 4
     assert B.moe_forward_workspace_bytes(T, H, F, E, k, 3) == 0      # Fs % 8
+
+
+def test_pack_weights_validation(L):
+    # documented size: G * ceil(N/64) * ceil(K/64) blocks of 64 x 64 bf16
+    assert B.moe_pack_weights_bytes(8, 4096, 14336) == 8 * 224 * 64 * 8192
+    assert B.moe_pack_weights_bytes(3, 200, 328) == 3 * 6 * 4 * 8192
+    assert B.moe_pack_weights_bytes(1, 8, 8) == 8192
+    assert B.moe_pack_weights_bytes(0, 64, 64) == 0
+    assert B.moe_pack_weights_bytes(2, 60, 64) == 0                    # K % 8
+    nbytes = B.moe_pack_weights_bytes(2, 64, 128)
+    assert L.moe_pack_weights(P, 0, 64, 128, P, nbytes, NULL) == INVALID
+    assert L.moe_pack_weights(P, 2, 64, 100, P, nbytes, NULL) == SHAPE
+    assert L.moe_pack_weights(NULL, 2, 64, 128, P, nbytes, NULL) == INVALID
+    assert L.moe_pack_weights(P, 2, 64, 128, Q, nbytes, NULL) == MISALIGNED
+    assert L.moe_pack_weights(P, 2, 64, 128, P, nbytes - 1, NULL) == WS_SMALL
+
+
+def test_packed_calls_validation(L):
+    assert L.moe_gateup_swiglu_packed(P, P, 128, 64, 100, 8, P, P, P, NULL) == SHAPE
+    assert L.moe_gateup_swiglu_packed(P, P, 128, 64, 96, 8, P, NULL, P, NULL) == INVALID
+    assert L.moe_down_packed(P, P, 128, 96, 64, 8, Q, P, NULL) == MISALIGNED
+    assert L.moe_forward_packed(NULL, P, 32, 64, 96, 8, 2, P, P, P, None, P, NULL, NULL,
+                                P, 1 << 30, NULL) == INVALID
+    assert L.moe_forward_packed(P, P, 32, 64, 96, 8, 9, P, P, P, None, P, NULL, NULL,
+                                P, 1 << 30, NULL) == SHAPE
+    assert L.moe_forward_packed(NULL, NULL, 0, 64, 96, 8, 2, NULL, NULL, NULL, None, NULL,
+                                NULL, NULL, NULL, 0, NULL) == OK

@@ -41,6 +41,20 @@ def _weights(cache, name):
     return cache[name]
 
 
+def _packed(cache, name):
+    """Packed copies of the cached device weights (made once per config)."""
+    key = name + ":packed"
+    if key not in cache:
+        layer, _ = cache[name]
+        pk = dict(wg=B.moe_pack_weights(layer.w_gate), wu=B.moe_pack_weights(layer.w_up),
+                  wd=B.moe_pack_weights(layer.w_down))
+        if layer.shared is not None:
+            pk["shared"] = {n: B.moe_pack_weights(layer.shared[n])
+                            for n in ("w_gate", "w_up", "w_down")}
+        cache[key] = pk
+    return cache[key]
+
+
 @pytest.mark.parametrize("name,T", CASES, ids=[f"{n}-T{t}" for n, t in CASES])
 def test_full_size_forward(name, T, weights_cache, orc):
     cfg = synth.CONFIGS[name]
@@ -82,3 +96,13 @@ def test_full_size_forward(name, T, weights_cache, orc):
     got = gpu_bf16_f64(out)[toks]
     assert_close(got, ref, f"out[{name}, T={T}]")
     assert rel_l2(got, ref) < 1e-2
+
+    # the packed-weight layer (what bench.py times): bit-identical to the above
+    pk = _packed(weights_cache, name)
+    say("moe_forward_packed full size", name, T)
+    outp = B.moe_forward(layer.x, layer.logits, k, pk["wg"], pk["wu"], pk["wd"],
+                         shared=None if shared is None else dict(pk["shared"],
+                                                                 gate_logits=shared["gate_logits"]))
+    torch.cuda.synchronize()
+    assert torch.equal(outp.view(torch.int16), out.view(torch.int16))
+    assert_close(gpu_bf16_f64(outp)[toks], ref, f"packed out[{name}, T={T}]")
