@@ -67,7 +67,8 @@ size_t permute_ws_bytes(int T, int E, int k) {
 // outputs where the k expert terms cancel.
 struct ForwardLayout {
   size_t hist, ids, w, offsets, row_token, row_dest, x_perm, h, h_sh, y, y_sh, total;
-  int ksplit;  // K-slices of the down projection (y and y_shared hold that many)
+  int ksplit;     // K-slices of the routed down projection (y holds that many)
+  int ksplit_sh;  // K-slices of the shared expert's (y_shared holds that many)
 };
 
 moe::GemmProblem down_problem(const bf16_t* h, const int32_t* offsets, int M, int F,
@@ -87,7 +88,10 @@ moe::GemmProblem forward_down_problem(int T, int H, int F, int E, int k, int Fs)
 
 ForwardLayout forward_layout(int T, int H, int F, int E, int k, int Fs, int cus) {
   ForwardLayout L;
-  L.ksplit = moe::grouped_gemm_ksplit_hint(forward_down_problem(T, H, F, E, k, Fs), cus);
+  moe::GemmProblem g2 = forward_down_problem(T, H, F, E, k, Fs);
+  moe::grouped_gemm_plan_ksplit(g2, cus);
+  L.ksplit = g2.seg[0].ksplit;
+  L.ksplit_sh = g2.nseg > 1 ? g2.seg[1].ksplit : 1;
   const size_t A = static_cast<size_t>(T) * k;
   const size_t S = static_cast<size_t>(L.ksplit);
   size_t o = 0;
@@ -102,7 +106,7 @@ ForwardLayout forward_layout(int T, int H, int F, int E, int k, int Fs, int cus)
   L.h = take(A * F * 2);
   L.h_sh = take(static_cast<size_t>(T) * (Fs > 0 ? Fs : 0) * 2);
   L.y = take(S * A * H * 4);                                       // fp32
-  L.y_sh = take(S * static_cast<size_t>(T) * (Fs > 0 ? H : 0) * 4);  // fp32
+  L.y_sh = take(static_cast<size_t>(L.ksplit_sh) * T * (Fs > 0 ? H : 0) * 4);  // fp32
   L.total = o;
   return L;
 }
@@ -121,7 +125,6 @@ moe::GemmProblem gateup_problem(const bf16_t* x_perm, const int32_t* offsets, in
   p.nseg = 1;
   p.gated = true;
   p.rows_hint = M / E;
-  p.ksplit = 1;
   return p;
 }
 
@@ -133,7 +136,6 @@ moe::GemmProblem down_problem(const bf16_t* h, const int32_t* offsets, int M, in
   p.nseg = 1;
   p.gated = false;
   p.rows_hint = M / E;
-  p.ksplit = 1;
   return p;
 }
 
@@ -295,7 +297,7 @@ int moe_combine(const moe_bf16* y_perm, const int32_t* row_dest, const float* to
   MOE_TRY(need_word(topk_w));
   MOE_TRY(need_bf16(out));
   return hip_status(moe::launch_combine(y_perm, false, 1, 0, row_dest, topk_w, T, H, k,
-                                        nullptr, 0, nullptr, out,
+                                        nullptr, 1, 0, nullptr, out,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -370,18 +372,19 @@ static int forward_impl(const moe_bf16* x, const float* logits, int T, int H, in
   // 4. grouped down (shared expert likewise)
   moe::GemmProblem g2 = down_problem(h, offsets, M, F, H, E, w_down, y, packed);
   g2.out_f32 = true;
-  g2.ksplit = L.ksplit;
+  g2.seg[0].ksplit = L.ksplit;
   g2.seg[0].slice_stride = static_cast<int64_t>(M) * H;
   if (shared) {
     g2.seg[1] = moe::GemmSegment{h_sh, nullptr, shared->w_down, nullptr, y_sh, 0,
                                  static_cast<int64_t>(T) * H, T, 1, Fs, H, packed};
+    g2.seg[1].ksplit = L.ksplit_sh;
     g2.nseg = 2;
   }
   MOE_TRY(hip_status(moe::launch_grouped_gemm(g2, s)));
   // 5. combine (+ gated shared term)
   return hip_status(moe::launch_combine(y, true, L.ksplit, static_cast<int64_t>(M) * H,
                                         row_dest, w, T, H, k, shared ? y_sh : nullptr,
-                                        static_cast<int64_t>(T) * H,
+                                        L.ksplit_sh, static_cast<int64_t>(T) * H,
                                         shared ? shared->gate_logits : nullptr, out, s));
 }
 

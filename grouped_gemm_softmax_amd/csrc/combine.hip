@@ -39,16 +39,22 @@ __device__ __forceinline__ void load8(const float* p, float v[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// One row as the sum of its K-slices (slice order fixed).
+// One row as the sum of its K-slices, added in slice order; the loads of
+// all slices are issued before the first add.
 template <typename YT>
 __device__ __forceinline__ void load8_sum(const YT* p, int nslices, int64_t stride, float v[8]) {
-  load8(p, v);
-  for (int s = 1; s < nslices; ++s) {
-    float u[8];
-    load8(p + s * stride, u);
+  float u[kMaxKSplit][8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] += u[q];
-  }
+  for (int s = 0; s < kMaxKSplit; ++s)
+    if (s < nslices) load8(p + s * stride, u[s]);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) v[q] = u[0][q];
+#pragma unroll
+  for (int s = 1; s < kMaxKSplit; ++s)
+    if (s < nslices) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] += u[s][q];
+    }
 }
 
 template <typename YT>
@@ -56,8 +62,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const YT* __restrict__ y_perm, int nslices, int64_t y_slice_stride,
     const int32_t* __restrict__ row_dest,
     const float* __restrict__ topk_w, int T, int H, int k,
-    const YT* __restrict__ y_shared, int64_t ysh_slice_stride,
+    const YT* __restrict__ y_shared, int nslices_sh, int64_t ysh_slice_stride,
     const float* __restrict__ shared_gate, bf16_t* __restrict__ out) {
+  // block (t, column block): 8 columns per thread
   const int t = blockIdx.x;
   __shared__ int s_row[kMaxTopK];
   __shared__ float s_w[kMaxTopK];
@@ -71,7 +78,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   __syncthreads();
   float s = 1.0f;
   if (y_shared && shared_gate) s = 1.0f / (1.0f + expf(-shared_gate[t]));
-  for (int c = threadIdx.x * 8; c < H; c += kCombineThreads * 8) {
+  {
+    const int c = (blockIdx.y * kCombineThreads + threadIdx.x) * 8;
+    if (c >= H) return;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float v[8];
     for (int j = 0; j < k; ++j) {
@@ -81,7 +90,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       for (int q = 0; q < 8; ++q) acc[q] += w * v[q];
     }
     if (y_shared) {
-      load8_sum(y_shared + static_cast<int64_t>(t) * H + c, nslices, ysh_slice_stride, v);
+      load8_sum(y_shared + static_cast<int64_t>(t) * H + c, nslices_sh, ysh_slice_stride, v);
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] += s * v[q];
     }
@@ -99,18 +108,19 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 hipError_t launch_combine(const void* y_perm, bool y_f32, int nslices,
                           int64_t y_slice_stride, const int32_t* row_dest,
                           const float* topk_w, int T, int H, int k,
-                          const void* y_shared, int64_t ysh_slice_stride,
+                          const void* y_shared, int nslices_sh, int64_t ysh_slice_stride,
                           const float* shared_gate, bf16_t* out, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
+  const dim3 grid(T, (H + kCombineThreads * 8 - 1) / (kCombineThreads * 8));
   if (y_f32)
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(kCombineThreads), 0, stream,
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(kCombineThreads), 0, stream,
                        static_cast<const float*>(y_perm), nslices, y_slice_stride, row_dest,
-                       topk_w, T, H, k, static_cast<const float*>(y_shared),
+                       topk_w, T, H, k, static_cast<const float*>(y_shared), nslices_sh,
                        ysh_slice_stride, shared_gate, out);
   else
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(T), dim3(kCombineThreads), 0, stream,
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, grid, dim3(kCombineThreads), 0, stream,
                        static_cast<const bf16_t*>(y_perm), 1, 0, row_dest, topk_w, T, H, k,
-                       static_cast<const bf16_t*>(y_shared), 0, shared_gate, out);
+                       static_cast<const bf16_t*>(y_shared), 1, 0, shared_gate, out);
   return hipGetLastError();
 }
 

@@ -161,9 +161,11 @@ struct TileCfg {
                 "equal DMA share per wave, one operand kind per instruction slot");
   static_assert(STAGES >= 3 && STAGES <= 8, "ring depth");
   // vmcnt holds at most 63 outstanding operations per wave: the K-steps in
-  // flight plus an epilogue's stores must fit
-  static_assert((PREFETCH ? STAGES : STAGES - 1) * IPW + (BF / WF / 16) * (BT / WT / 16) <= 63,
-                "vector-memory counter range");
+  // flight must fit, and for chaining across items also the epilogue's
+  // stores issued while the next item's first K-steps are in flight
+  static constexpr int STORES = (BF / WF / 16) * (BT / WT / 16);
+  static_assert((PREFETCH ? STAGES : STAGES - 1) * IPW <= 63, "vector-memory counter range");
+  static constexpr bool CHAIN_OK = PREFETCH && STAGES * IPW + STORES <= 63;
 };
 
 // 16-byte chunk swizzles (chunk index within a row), chosen by measuring
@@ -243,7 +245,6 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
   const int wt = wave / C::WF;
   const int g16 = lane >> 4;   // k-group of the lane in an MFMA operand
   const int i16 = lane & 15;   // row/column of the lane in an MFMA operand
-  const int ksplit = prob.ksplit;
 
   // ---- prologue: item prefix over all groups of both segments ----
   const int NG = prob.seg[0].ngroups + (prob.nseg > 1 ? prob.seg[1].ngroups : 0);
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
     if (g < NG) {
       const GroupView v = group_view(prob, g);
       const GemmSegment& s = v.seg ? prob.seg[1] : prob.seg[0];
-      cnt[i] = ((v.M + C::BT - 1) / C::BT) * ((s.N + C::BF - 1) / C::BF) * ksplit;
+      cnt[i] = ((v.M + C::BT - 1) / C::BT) * ((s.N + C::BF - 1) / C::BF) * s.ksplit;
       s_rows[g] = int2{v.r0, v.M};
     }
     my_sum += cnt[i];
@@ -341,6 +342,7 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
     it.N = S.N;
     const int mtiles = (v.M + C::BT - 1) / C::BT;
     int local = item - s_pref[lo];
+    const int ksplit = S.ksplit;
     const int ks = local % ksplit;
     local /= ksplit;
     const int mt = local % mtiles;
@@ -555,7 +557,7 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
   // Chaining is used by the decode-size (prefetching) tiles, whose time is
   // memory latency; the large tiles keep their registers for the MFMA
   // operands and restart the ring per item.
-  constexpr bool CHAIN = C::PREFETCH && !KTAIL;
+  constexpr bool CHAIN = C::CHAIN_OK && !KTAIL;
   auto stage_buf = [&](auto I) INL -> char* {
     constexpr int i = decltype(I)::value % S;
     if constexpr (i == 0) return st0;
@@ -726,7 +728,7 @@ int64_t item_bound(const GemmProblem& p) {
   for (int s = 0; s < p.nseg; ++s) {
     const GemmSegment& S = p.seg[s];
     const int64_t mt = (S.rows + C::BT - 1) / C::BT + (S.offsets ? S.ngroups : 0);
-    bound += mt * ((S.N + C::BF - 1) / C::BF) * p.ksplit;
+    bound += mt * ((S.N + C::BF - 1) / C::BF) * S.ksplit;
   }
   return bound;
 }
@@ -782,11 +784,15 @@ int tile_class(const GemmProblem& p) {
 
 bool grouped_gemm_uses_large_tiles(const GemmProblem& p) { return tile_class(p) == kLarge; }
 
-int grouped_gemm_ksplit_hint(const GemmProblem& p, int cus) {
+void grouped_gemm_plan_ksplit(GemmProblem& p, int cus) {
   // Split K only where the unsplit item count cannot fill the chip: down
   // projections (fp32 partial outputs) with few touched experts or few
-  // row tiles.
-  if (p.gated || !p.out_f32) return 1;
+  // row tiles. A second segment (the shared expert) whose K is longer is
+  // split further while its items are few, so that its items cost about as
+  // many K-steps as the routed ones: the schedule gives every workgroup the
+  // same number of items, so one long item would set the kernel's time.
+  for (int s = 0; s < p.nseg; ++s) p.seg[s].ksplit = 1;
+  if (p.gated || !p.out_f32) return;
   const bool large = grouped_gemm_uses_large_tiles(p);
   const int BT = large ? DownLarge::BT : DownSmall::BT;
   const int BF = large ? DownLarge::BF : DownSmall::BF;
@@ -806,7 +812,16 @@ int grouped_gemm_ksplit_hint(const GemmProblem& p, int cus) {
   while (split < kMaxKSplit && items * split * 2 <= want && min_k / (split * 2) >= 256 &&
          min_k / (split * 2) >= 4 * BK)
     split *= 2;
-  return split;
+  for (int s = 0; s < p.nseg; ++s) p.seg[s].ksplit = split;
+  if (p.nseg > 1) {
+    const GemmSegment& S1 = p.seg[1];
+    const int steps0 = ((p.seg[0].K + BK - 1) / BK + split - 1) / split;  // per routed item
+    const int nk1 = (S1.K + BK - 1) / BK;
+    const int64_t items1 = static_cast<int64_t>((S1.rows + BT - 1) / BT) * ((S1.N + BF - 1) / BF);
+    int ks1 = (nk1 + steps0 / 2) / steps0;
+    ks1 = ks1 < 1 ? 1 : (ks1 > kMaxKSplit ? kMaxKSplit : ks1);
+    if (ks1 > split && items1 < want && nk1 / ks1 >= 4) p.seg[1].ksplit = ks1;
+  }
 }
 
 int grouped_gemm_device_cus() { return device_cu_count(); }

@@ -16,7 +16,7 @@ constexpr int kPermChunks = 8;           // routing chunks per permute block
 constexpr int kMaxKSplit = 8;         // K-slices of a split down projection
 
 // --- routing and permutation (route_permute.hip) ---
-int route_chunk_tokens(int k);
+int route_chunk_tokens(int T, int k);
 int route_num_chunks(int T, int k);
 hipError_t launch_route(const float* logits, int T, int E, int k,
                         int32_t* topk_ids, float* topk_w,
@@ -47,7 +47,8 @@ struct GemmSegment {
   int ngroups;
   int K;
   int N;
-  int packed;              // weights in the packed block layout
+  int packed = 0;          // weights in the packed block layout
+  int ksplit = 1;          // K-slices (> 1 needs fp32 output; the consumer sums them)
 };
 
 struct GemmProblem {
@@ -56,12 +57,12 @@ struct GemmProblem {
   bool gated;      // out = silu(act w0) * (act w1), else act w0
   bool out_f32;    // store fp32 instead of bf16 (down projection only)
   int rows_hint;   // typical rows per group, picks the tile shape
-  int ksplit;      // K-slices (1: none); > 1 needs out_f32, slices summed later
 };
 
 hipError_t launch_grouped_gemm(const GemmProblem& prob, hipStream_t stream);
-// K-slices worth using for `prob` on a device with `cus` compute units.
-int grouped_gemm_ksplit_hint(const GemmProblem& prob, int cus);
+// Sets each segment's K-slices (seg[s].ksplit) for an fp32-output problem on
+// a device with `cus` compute units; gated or bf16 problems keep 1.
+void grouped_gemm_plan_ksplit(GemmProblem& prob, int cus);
 int grouped_gemm_device_cus();
 
 // Packed weights: W [G][K][N] as G x ceil(N/64) x ceil(K/64) blocks of
@@ -75,11 +76,11 @@ hipError_t launch_pack_weights(const bf16_t* w, int G, int K, int N, bf16_t* pac
 // --- combine (combine.hip) ---
 // y_perm/y_shared hold bf16 values (y_f32 == false) or fp32 values; with
 // nslices > 1 (fp32 only) they are K-slice partial sums, slice s at
-// y + s*stride, added in slice order.
+// y + s*stride, added in slice order (nslices_sh likewise for y_shared).
 hipError_t launch_combine(const void* y_perm, bool y_f32, int nslices,
                           int64_t y_slice_stride, const int32_t* row_dest,
                           const float* topk_w, int T, int H, int k,
-                          const void* y_shared /* [T,H] or null */,
+                          const void* y_shared /* [T,H] or null */, int nslices_sh,
                           int64_t ysh_slice_stride,
                           const float* shared_gate /* [T] or null */,
                           bf16_t* out, hipStream_t stream);

@@ -58,16 +58,15 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 // L lanes per token (L = the power of two >= E, at least 8, at most 64), so
-// a wave routes 64/L tokens at once; each lane holds the logits of experts
-// lane%L + L*q. The next token's logits are loaded before the current one is
-// ranked, so at most one load latency per pass is exposed.
-template <int L>
+// a wave routes 64/L tokens at once; each lane holds the logits of NQ
+// experts, lane%L + L*q (NQ = the power of two >= E/L). The next token's
+// logits are loaded before the current one is ranked, so at most one load
+// latency per pass is exposed.
+template <int L, int NQ>
 __device__ void route_tokens(const float* __restrict__ logits, int T, int E, int k,
                              int t_begin, int t_end, int32_t* __restrict__ topk_ids,
                              float* __restrict__ topk_w, int* s_count) {
   constexpr int TPW = kWave / L;          // tokens per wave per pass
-  // logits per lane, upper bound: 1 when E <= L < 64, else E <= 1024
-  constexpr int NQ = L < kWave ? 1 : kMaxExperts / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int sub = lane / L;               // token slot in the wave
@@ -135,10 +134,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   const int t_begin = blockIdx.x * chunk_tokens;
   const int t_end = min(T, t_begin + chunk_tokens);
   int* cnt = hist ? s_count : nullptr;
-  if (E <= 8) route_tokens<8>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
-  else if (E <= 16) route_tokens<16>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
-  else if (E <= 32) route_tokens<32>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
-  else route_tokens<64>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
+  if (E <= 8) route_tokens<8, 1>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
+  else if (E <= 16) route_tokens<16, 1>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
+  else if (E <= 32) route_tokens<32, 1>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
+  else if (E <= 64) route_tokens<64, 1>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
+  else if (E <= 128) route_tokens<64, 2>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
+  else if (E <= 256) route_tokens<64, 4>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
+  else if (E <= 512) route_tokens<64, 8>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
+  else route_tokens<64, 16>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
   if (hist) {
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kRouteThreads)
@@ -308,20 +311,27 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 
 }  // namespace
 
-int route_chunk_tokens(int k) {
-  const int c = kMaxChunkAssign / k;
-  return c < 32 ? c : 32;
+// Tokens per routing chunk (one histogram row, one routing block): at most
+// 32 and kMaxChunkAssign / k; small batches use chunks of down to 4 tokens
+// (one pass of a block at one token per wave) so that more blocks share the
+// routing and the permutation.
+int route_chunk_tokens(int T, int k) {
+  int c = kMaxChunkAssign / k;
+  c = c < 32 ? c : 32;
+  int want = (T + 127) / 128;  // about 128 chunks while T is small
+  want = want < 4 ? 4 : want;
+  return want < c ? want : c;
 }
 
 int route_num_chunks(int T, int k) {
-  const int c = route_chunk_tokens(k);
+  const int c = route_chunk_tokens(T, k);
   return (T + c - 1) / c;
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int k,
                         int32_t* topk_ids, float* topk_w, int32_t* hist,
                         hipStream_t stream) {
-  const int chunk = route_chunk_tokens(k);
+  const int chunk = route_chunk_tokens(T, k);
   const int nchunks = route_num_chunks(T, k);
   hipLaunchKernelGGL(route_kernel, dim3(nchunks), dim3(kRouteThreads), 0,
                      stream, logits, T, E, k, chunk, topk_ids, topk_w, hist);
@@ -330,7 +340,7 @@ hipError_t launch_route(const float* logits, int T, int E, int k,
 
 hipError_t launch_hist(const int32_t* topk_ids, int T, int E, int k,
                        int32_t* hist, hipStream_t stream) {
-  const int chunk = route_chunk_tokens(k);
+  const int chunk = route_chunk_tokens(T, k);
   const int nchunks = route_num_chunks(T, k);
   hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(kRouteThreads), 0,
                      stream, topk_ids, T, E, k, chunk, hist);
@@ -342,7 +352,7 @@ hipError_t launch_permute(const bf16_t* x, const int32_t* topk_ids, int T,
                           int32_t* expert_offsets, int32_t* row_token,
                           int32_t* row_dest, bf16_t* x_perm,
                           hipStream_t stream) {
-  const int chunk = route_chunk_tokens(k);
+  const int chunk = route_chunk_tokens(T, k);
   const int nchunks = route_num_chunks(T, k);
   const int slice = kPermuteSliceCols;
   const int nslices = (H + slice - 1) / slice;

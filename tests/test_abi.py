@@ -103,12 +103,14 @@ def test_forward_validation(L):
 
 def _down_ksplit(T, H, F, E, k, Fs, cus=256):
     """Re-statement of the host heuristic for K-slices of the fused layer's
-    down projection. Tile: large (256 rows x 256 columns, 32-deep stages) at
-    >= 64 rows per expert, else small (32 x 64, 64-deep). Expected items:
-    one partial row tile per touched expert plus the full ones, times the
-    column tiles (plus the shared expert's). The split doubles while twice
-    the items still fit in 2 x CUs and each slice keeps >= 256 and >= 4
-    stages of K."""
+    down projection, as (routed, shared). Tile: large (256 rows x 256
+    columns, 32-deep stages) at >= 64 rows per expert, else small (32 x 64,
+    64-deep). Expected items: one partial row tile per touched expert plus
+    the full ones, times the column tiles (plus the shared expert's). The
+    split doubles while twice the items still fit in 2 x CUs and each slice
+    keeps >= 256 and >= 4 stages of K. The shared expert's items are split
+    further, to about the routed items' K-steps, while they are fewer than
+    2 x CUs and keep >= 4 K-steps each."""
     A = T * k
     large = A // E >= 64
     BT, BF, BK = (256, 256, 32) if large else (32, 64, 64)
@@ -122,30 +124,47 @@ def _down_ksplit(T, H, F, E, k, Fs, cus=256):
     while (split < 8 and items * split * 2 <= 2 * cus and min_k // (split * 2) >= 256
            and min_k // (split * 2) >= 4 * BK):
         split *= 2
-    return split
+    shared = split
+    if Fs:
+        steps0 = -(-(-(-F // BK)) // split)
+        nk1 = -(-Fs // BK)
+        items1 = -(-T // BT) * ntile
+        r = min(8, max(1, (nk1 + steps0 // 2) // steps0))
+        if r > split and items1 < 2 * cus and nk1 // r >= 4:
+            shared = r
+    return split, shared
 
 
 def _layout_model(T, H, F, E, k, Fs):
     """Independent re-statement of the documented forward workspace layout."""
     al = lambda v: (v + 255) // 256 * 256
     A = T * k
-    chunk = min(32, 256 // k)          # routing chunk (tokens per histogram row)
+    # routing chunk (tokens per histogram row): about T/128, within 4 .. min(32, 256/k)
+    chunk = min(max(4, -(-T // 128)), min(32, 256 // k))
     nch = (T + chunk - 1) // chunk
-    S = _down_ksplit(T, H, F, E, k, Fs)
+    S, S_sh = _down_ksplit(T, H, F, E, k, Fs)
     parts = [nch * E * 4, A * 4, A * 4, (E + 1) * 4, A * 4, A * 4, A * H * 2,
-             A * F * 2, T * Fs * 2, S * A * H * 4, S * T * (H if Fs else 0) * 4]
+             A * F * 2, T * Fs * 2, S * A * H * 4, S_sh * T * (H if Fs else 0) * 4]
     return sum(al(p) for p in parts)
 
 
 @pytest.mark.parametrize("T,H,F,E,k,Fs", [(64, 256, 512, 8, 2, 0), (4096, 7168, 2048, 256, 8, 2048),
                                           (16384, 2048, 1408, 60, 4, 5632), (1, 4096, 14336, 8, 2, 0),
                                           (32, 4096, 14336, 8, 2, 0), (16, 2048, 1408, 60, 4, 5632),
-                                          (128, 7168, 2048, 256, 8, 2048)])
+                                          (128, 7168, 2048, 256, 8, 2048),
+                                          (1024, 2048, 1408, 60, 4, 5632),
+                                          (40, 128, 256, 16, 2, 768), (200, 128, 256, 4, 2, 1024)])
 def test_forward_workspace_bytes(T, H, F, E, k, Fs):
     got = B.moe_forward_workspace_bytes(T, H, F, E, k, Fs)
     assert got == _layout_model(T, H, F, E, k, Fs)
     if (T, H) == (1, 4096):
-        assert _down_ksplit(T, H, F, E, k, Fs) == 4    # two experts: 128 items -> split 4
+        assert _down_ksplit(T, H, F, E, k, Fs) == (4, 4)   # two experts: 128 items -> split 4
+    if (T, Fs) in ((16, 5632), (1024, 5632)):
+        assert _down_ksplit(T, H, F, E, k, Fs)[1] == 4   # shared K = 4 x routed K
+    if (T, H, F, Fs) == (40, 128, 256, 768):
+        assert _down_ksplit(T, H, F, E, k, Fs) == (1, 3)   # the GPU test's shared split
+    if (T, H, F, Fs) == (200, 128, 256, 1024):
+        assert _down_ksplit(T, H, F, E, k, Fs) == (1, 4)
     assert B.moe_forward_workspace_bytes(T, H, F, E, k, 3) == 0      # Fs % 8
 
 

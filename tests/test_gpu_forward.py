@@ -17,6 +17,13 @@ SHARED_CASES = {
                                             shared_gated=True), 37),
     "qwen2_like_large_batch": (synth.small_config("q2l", H=128, F=88, E=12, k=4, Fs=176,
                                                   shared_gated=True), 400),
+    # shared K three times the routed K: the shared expert's down projection
+    # is split into 3 K-slices (small tile) ...
+    "shared_long_k": (synth.small_config("slk", H=128, F=256, E=16, k=2, Fs=768,
+                                         shared_gated=True), 40),
+    # ... and into 4 with the large tile
+    "shared_long_k_large_batch": (synth.small_config("slkl", H=128, F=256, E=4, k=2, Fs=1024,
+                                                     shared_gated=True), 200),
 }
 
 
