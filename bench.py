@@ -13,8 +13,8 @@ Metric: MoE-layer HBM GB/s (algorithmic bytes / time), with TFLOP/s and the
 roofline fractions beside it. `roofline` describes the dominant kernel (the
 gate/up+SwiGLU grouped GEMM), timed with HIP events on its launch stream.
 `cpu_baseline` is the CPU oracle timed on a bounded sample of the same
-workload. `sweep` repeats the measurement at the other batch sizes of the
-same layer shape (T = 1, 128, 512).
+workload. `--sweep 1,128,512` repeats the measurement at other batch sizes of
+the same layer shape (listed under `sweep`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -42,8 +42,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="mixtral")
     ap.add_argument("--T", type=int, default=32)
-    ap.add_argument("--sweep", default="1,128,512",
-                    help="other batch sizes to measure ('' to skip)")
+    ap.add_argument("--sweep", default="",
+                    help="other batch sizes of the same layer to measure, e.g. '1,128,512' "
+                         "(off by default, so that a kernel-trace of the default run "
+                         "averages the headline kernels only)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32,
