@@ -127,7 +127,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <int BT_, int BF_, int BK_, int WT_, int WF_, int STAGES_, bool GATED_,
-          bool PREFETCH_>
+          bool PREFETCH_, int MIN_WAVES_ = 1>
 struct TileCfg {
   static constexpr int BT = BT_;  // activation rows (tokens) per tile
   static constexpr int BF = BF_;  // output columns per tile
@@ -139,6 +139,9 @@ struct TileCfg {
   // Read the next stage's MFMA fragments into a second register set while
   // this stage's MFMAs run (costs one more fragment set of registers).
   static constexpr bool PREFETCH = PREFETCH_;
+  // waves per SIMD the register allocation must leave room for (so that
+  // this many fit by registers as well as by LDS)
+  static constexpr int MIN_WAVES = MIN_WAVES_;
   static constexpr int NW = WT * WF;
   static constexpr int kThreads = NW * kWave;
   static constexpr int NMAT = GATED ? 2 : 1;
@@ -222,7 +225,8 @@ __device__ __forceinline__ void store4(float* p, const float v[4]) {
 }
 
 template <class C, typename OutT, bool KTAIL, bool PACKED>
-__global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem prob) {
+__global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel(
+    GemmProblem prob) {
   __shared__ __attribute__((aligned(1024))) char st0[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st1[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char st2[C::STAGE_BYTES];
@@ -683,7 +687,12 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmProblem p
 // for a second fragment set). Mid (gate/up at 16..63 rows per group):
 // 32 tokens x 64 columns, 2 waves, 4-deep ring of 10 KB, 32-deep stages
 // (3 workgroups per CU): half the row tiles per expert of the small tile.
+// Large128 (64..191 rows per group, where a 256-row tile would be about half
+// padding): 128 tokens x 128 (gated) or 256 columns, 8 waves of 32 tokens, a
+// 3-deep ring of 24 KB stages, so that two workgroups share a CU.
 using GateUpLarge = TileCfg<256, 128, 32, 4, 2, 4, true, false>;
+using GateUpLarge128 = TileCfg<128, 128, 32, 4, 2, 3, true, false, 4>;
+using DownLarge128 = TileCfg<128, 256, 32, 4, 2, 3, false, false, 4>;
 using GateUpSmall = TileCfg<16, 64, 64, 1, 2, 4, true, true>;
 using GateUpMid = TileCfg<32, 64, 32, 1, 2, 4, true, true>;
 using DownLarge = TileCfg<256, 256, 32, 4, 2, 4, false, false>;
@@ -767,22 +776,35 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
 }  // namespace
 
 // Tile class by typical rows per group: < 16 small, < 64 mid (gate/up only;
-// the down projection keeps the small tile), else large. MOE_TILE=small|mid|
-// large overrides the choice (for tile sweeps).
-enum TileClass { kSmall = 0, kMid = 1, kLarge = 2 };
+// the down projection keeps the small tile), < 192 large128, else large. A
+// down projection takes large128 only when its expected items (one partial
+// row tile per touched group plus the full ones, times the column tiles) fill
+// the two workgroups per CU that tile runs with; with few groups (e.g. 8
+// experts of 128 rows and a long K) it keeps one 256-row tile per CU.
+// MOE_TILE=small|mid|large128|large overrides the choice (for tile sweeps).
+enum TileClass { kSmall = 0, kMid = 1, kLarge128 = 2, kLarge = 3 };
 
 int tile_class(const GemmProblem& p) {
   static int forced = -2;
   if (forced == -2) {
     const char* e = getenv("MOE_TILE");
     forced = !e ? -1 : (!strcmp(e, "small") ? kSmall : !strcmp(e, "mid") ? kMid
+                        : !strcmp(e, "large128") ? kLarge128
                         : !strcmp(e, "large") ? kLarge : -1);
   }
   if (forced >= 0) return forced;
-  return p.rows_hint < 16 ? kSmall : (p.rows_hint < 64 ? kMid : kLarge);
+  if (p.rows_hint < 16) return kSmall;
+  if (p.rows_hint < 64) return kMid;
+  if (p.rows_hint >= 192) return kLarge;
+  if (p.gated) return kLarge128;
+  int64_t items = 0;
+  for (int s = 0; s < p.nseg; ++s) {
+    const GemmSegment& S = p.seg[s];
+    const int64_t touched = S.ngroups > 1 ? (S.rows < S.ngroups ? S.rows : S.ngroups) : 1;
+    items += (touched + S.rows / DownLarge128::BT) * ((S.N + DownLarge128::BF - 1) / DownLarge128::BF);
+  }
+  return items >= 2 * static_cast<int64_t>(device_cu_count()) ? kLarge128 : kLarge;
 }
-
-bool grouped_gemm_uses_large_tiles(const GemmProblem& p) { return tile_class(p) == kLarge; }
 
 void grouped_gemm_plan_ksplit(GemmProblem& p, int cus) {
   // Split K only where the unsplit item count cannot fill the chip: down
@@ -793,10 +815,10 @@ void grouped_gemm_plan_ksplit(GemmProblem& p, int cus) {
   // same number of items, so one long item would set the kernel's time.
   for (int s = 0; s < p.nseg; ++s) p.seg[s].ksplit = 1;
   if (p.gated || !p.out_f32) return;
-  const bool large = grouped_gemm_uses_large_tiles(p);
-  const int BT = large ? DownLarge::BT : DownSmall::BT;
-  const int BF = large ? DownLarge::BF : DownSmall::BF;
-  const int BK = large ? DownLarge::BK : DownSmall::BK;
+  const int tc = tile_class(p);
+  const int BT = tc == kLarge ? DownLarge::BT : tc == kLarge128 ? DownLarge128::BT : DownSmall::BT;
+  const int BF = tc == kLarge ? DownLarge::BF : tc == kLarge128 ? DownLarge128::BF : DownSmall::BF;
+  const int BK = tc == kLarge ? DownLarge::BK : tc == kLarge128 ? DownLarge128::BK : DownSmall::BK;
   int64_t items = 0;
   int min_k = 1 << 30;
   for (int s = 0; s < p.nseg; ++s) {
@@ -868,16 +890,18 @@ hipError_t launch_pack_weights(const bf16_t* w, int G, int K, int N, bf16_t* pac
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
   const int tc = tile_class(p);
-  const bool large = tc == kLarge;
   if (p.gated)
-    return large ? launch_cfg<GateUpLarge, bf16_t>(p, stream)
-                 : tc == kMid ? launch_cfg<GateUpMid, bf16_t>(p, stream)
-                              : launch_cfg<GateUpSmall, bf16_t>(p, stream);
+    return tc == kLarge      ? launch_cfg<GateUpLarge, bf16_t>(p, stream)
+           : tc == kLarge128 ? launch_cfg<GateUpLarge128, bf16_t>(p, stream)
+           : tc == kMid      ? launch_cfg<GateUpMid, bf16_t>(p, stream)
+                             : launch_cfg<GateUpSmall, bf16_t>(p, stream);
   if (p.out_f32)
-    return large ? launch_cfg<DownLarge, float>(p, stream)
-                 : launch_cfg<DownSmall, float>(p, stream);
-  return large ? launch_cfg<DownLarge, bf16_t>(p, stream)
-               : launch_cfg<DownSmall, bf16_t>(p, stream);
+    return tc == kLarge      ? launch_cfg<DownLarge, float>(p, stream)
+           : tc == kLarge128 ? launch_cfg<DownLarge128, float>(p, stream)
+                             : launch_cfg<DownSmall, float>(p, stream);
+  return tc == kLarge      ? launch_cfg<DownLarge, bf16_t>(p, stream)
+         : tc == kLarge128 ? launch_cfg<DownLarge128, bf16_t>(p, stream)
+                           : launch_cfg<DownSmall, bf16_t>(p, stream);
 }
 
 }  // namespace moe

@@ -1,7 +1,7 @@
 """GPU parity of each step of the layer through the C ABI, against the CPU
 oracle, at sizes the oracle finishes in seconds. Shapes are chosen so that the
 grouped GEMMs see several tiles per expert, ragged M, N and K tails, empty
-experts, and both tile shapes (small-batch and large-batch)."""
+experts, and every tile class (small, mid, large128 and large)."""
 import numpy as np
 import pytest
 import torch
@@ -27,6 +27,11 @@ CASES = {
     "all_equal_logits": (synth.small_config("eq", H=72, F=56, E=12, k=3), 45, "equal"),
     "ties_int": (synth.small_config("ti", H=64, F=64, E=16, k=4), 80, "ties_int"),
     "signed_zero": (synth.small_config("sz", H=64, F=64, E=10, k=3), 50, "signed_zero"),
+    # ~100 rows per expert and enough column tiles: both GEMMs take the
+    # 128-row large tiles; F = 64 is narrower than one 128-column tile
+    "large128_tiles": (synth.small_config("l128", H=2048, F=64, E=64, k=4), 1600, None),
+    # >= 192 rows per expert: the 256-row large tiles, with ragged K and N
+    "ragged_large256": (synth.small_config("rl256", H=200, F=328, E=4, k=2), 500, None),
 }
 
 
