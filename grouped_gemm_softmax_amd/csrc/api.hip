@@ -356,13 +356,26 @@ static int forward_impl(const moe_bf16* x, const float* logits, int T, int H, in
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int M = static_cast<int>(A);
 
-  // 1. route + per-chunk histogram
-  MOE_TRY(hip_status(moe::launch_route(logits, T, E, k, ids, w, hist, s)));
-  // 2. permute: scan, stable rank, row maps, x_perm gather
-  MOE_TRY(hip_status(moe::launch_permute(x, ids, T, H, E, k, hist, offsets, row_token,
-                                         row_dest, x_perm, s)));
-  // 3. grouped gate/up + SwiGLU (shared expert as one more group over x)
+  // 3's problem first: the large-batch tiles read the rows of x through
+  // row_token themselves, and then the permutation copies no rows
   moe::GemmProblem g1 = gateup_problem(x_perm, offsets, M, H, F, E, w_gate, w_up, h, packed);
+  const bool gather = moe::grouped_gemm_gathers(g1);
+  if (gather) {
+    g1.seg[0].act = x;
+    g1.seg[0].gather = row_token;
+  }
+  if (!gather && moe::route_permute_fits_one_launch(T, E, k)) {
+    // 1+2. small batch: routing and the permutation in one launch
+    MOE_TRY(hip_status(moe::launch_route_permute_small(logits, x, T, H, E, k, ids, w, offsets,
+                                                       row_token, row_dest, x_perm, s)));
+  } else {
+    // 1. route + per-chunk histogram
+    MOE_TRY(hip_status(moe::launch_route(logits, T, E, k, ids, w, hist, s)));
+    // 2. permute: scan, stable rank, row maps (+ x_perm rows unless gathered)
+    MOE_TRY(hip_status(moe::launch_permute(x, ids, T, H, E, k, hist, offsets, row_token,
+                                           row_dest, gather ? nullptr : x_perm, s)));
+  }
+  // 3. grouped gate/up + SwiGLU (shared expert as one more group over x)
   if (shared) {
     g1.seg[1] = moe::GemmSegment{x, nullptr, shared->w_gate, shared->w_up, h_sh, 0, 0, T, 1, H, Fs,
                                  packed};

@@ -313,7 +313,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
   struct ItemInfo {
     const bf16_t* w0;
     const bf16_t* w1;
-    const bf16_t* x;
+    const bf16_t* x;  // activations of the tile's first row (x itself when gathering)
     OutT* out;        // output of this item's K-slice
     int K, N;
     int n0;           // first output column
@@ -363,7 +363,8 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     it.kblk = (S.K + 63) / 64;
     it.w0 = S.w0 + static_cast<int64_t>(v.local) * S.w_stride;
     it.w1 = C::GATED ? S.w1 + static_cast<int64_t>(v.local) * S.w_stride : it.w0;
-    it.x = S.act;
+    // gathered rows: row p of the group's block is activation row S.gather[p]
+    it.x = S.gather ? S.act : S.act + static_cast<int64_t>(it.row_base) * it.K;
     it.out = static_cast<OutT*>(S.out) + static_cast<int64_t>(ks) * S.slice_stride;
     // every field is wave-uniform: keep them in scalar registers
     it.w0 = uniform(it.w0);
@@ -394,7 +395,9 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
         } else {
           const int r = (j - C::W_INSTR) * RPI_X + lane / (C::BK / 8);
           const int kc = swz_x<C::BK>(r, lane % (C::BK / 8)) * 8;
-          it.voff[i] = static_cast<uint32_t>(min(r, it.rows_valid - 1) * it.K + kc) * 2u;
+          const int rr = min(r, it.rows_valid - 1);
+          const int row = S.gather ? S.gather[it.row_base + rr] : rr;
+          it.voff[i] = static_cast<uint32_t>(row * it.K + kc) * 2u;
         }
       }
     }
@@ -445,7 +448,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
           }
         }
       } else {
-        base = it.x + static_cast<int64_t>(it.row_base) * it.K + k0;
+        base = it.x + k0;
         if constexpr (KTAIL) {
           const int r = (j - C::W_INSTR) * RPI_X + lane / (C::BK / 8);
           const int kc = swz_x<C::BK>(r, lane % (C::BK / 8)) * 8;
@@ -804,6 +807,11 @@ int tile_class(const GemmProblem& p) {
     items += (touched + S.rows / DownLarge128::BT) * ((S.N + DownLarge128::BF - 1) / DownLarge128::BF);
   }
   return items >= 2 * static_cast<int64_t>(device_cu_count()) ? kLarge128 : kLarge;
+}
+
+bool grouped_gemm_gathers(const GemmProblem& p) {
+  const int tc = tile_class(p);
+  return p.gated && (tc == kLarge || tc == kLarge128);
 }
 
 void grouped_gemm_plan_ksplit(GemmProblem& p, int cus) {

@@ -23,6 +23,14 @@ hipError_t launch_route(const float* logits, int T, int E, int k,
                         int32_t* hist /* nullable */, hipStream_t stream);
 hipError_t launch_hist(const int32_t* topk_ids, int T, int E, int k,
                        int32_t* hist, hipStream_t stream);
+// Route + permute (with the row copy) in one launch, for T*k <= 128 and
+// E <= 256 (where it is faster than route + permute).
+bool route_permute_fits_one_launch(int T, int E, int k);
+hipError_t launch_route_permute_small(const float* logits, const bf16_t* x, int T, int H,
+                                      int E, int k, int32_t* topk_ids, float* topk_w,
+                                      int32_t* expert_offsets, int32_t* row_token,
+                                      int32_t* row_dest, bf16_t* x_perm, hipStream_t stream);
+// x_perm == nullptr: row maps and offsets only (no row copy).
 hipError_t launch_permute(const bf16_t* x, const int32_t* topk_ids, int T,
                           int H, int E, int k, const int32_t* hist,
                           int32_t* expert_offsets, int32_t* row_token,
@@ -48,6 +56,10 @@ struct GemmSegment {
   int K;
   int N;
   int packed = 0;          // weights in the packed block layout
+  // Optional row map: activation row of row p is gather[p] (`act` is then
+  // the un-permuted [*, K] tensor). Only for the tile classes without item
+  // chaining (see grouped_gemm_gathers).
+  const int32_t* gather = nullptr;
   int ksplit = 1;          // K-slices (> 1 needs fp32 output; the consumer sums them)
 };
 
@@ -60,6 +72,11 @@ struct GemmProblem {
 };
 
 hipError_t launch_grouped_gemm(const GemmProblem& prob, hipStream_t stream);
+// Whether the gated problem's tiles can read activations through a row map
+// (GemmSegment::gather): true for the large-batch tile classes, whose items
+// restart their pipeline anyway (the map is read at each item's start).
+bool grouped_gemm_gathers(const GemmProblem& prob);
+
 // Sets each segment's K-slices (seg[s].ksplit) for an fp32-output problem on
 // a device with `cus` compute units; gated or bf16 problems keep 1.
 void grouped_gemm_plan_ksplit(GemmProblem& prob, int cus);

@@ -62,7 +62,7 @@ __device__ __forceinline__ float group_sum(float v) {
 // experts, lane%L + L*q (NQ = the power of two >= E/L). The next token's
 // logits are loaded before the current one is ranked, so at most one load
 // latency per pass is exposed.
-template <int L, int NQ>
+template <int L, int NQ, int NT>
 __device__ void route_tokens(const float* __restrict__ logits, int T, int E, int k,
                              int t_begin, int t_end, int32_t* __restrict__ topk_ids,
                              float* __restrict__ topk_w, int* s_count) {
@@ -72,7 +72,7 @@ __device__ void route_tokens(const float* __restrict__ logits, int T, int E, int
   const int sub = lane / L;               // token slot in the wave
   const int gl = lane % L;                // lane within the token group
   const int Q = (E + L - 1) / L;
-  const int stride = (kRouteThreads / kWave) * TPW;
+  const int stride = (NT / kWave) * TPW;
   float cur[NQ];
   auto load = [&](int t, float* dst) {
 #pragma unroll
@@ -123,6 +123,22 @@ __device__ void route_tokens(const float* __restrict__ logits, int T, int E, int
   }
 }
 
+// Tokens [t_begin, t_end) of an NT-thread block, with the lane group sized to
+// E (E <= 64 * MAXQ).
+template <int NT, int MAXQ = 16>
+__device__ __forceinline__ void route_range(const float* logits, int T, int E, int k,
+                                            int t_begin, int t_end, int32_t* ids, float* w,
+                                            int* cnt) {
+  if (E <= 8) route_tokens<8, 1, NT>(logits, T, E, k, t_begin, t_end, ids, w, cnt);
+  else if (E <= 16) route_tokens<16, 1, NT>(logits, T, E, k, t_begin, t_end, ids, w, cnt);
+  else if (E <= 32) route_tokens<32, 1, NT>(logits, T, E, k, t_begin, t_end, ids, w, cnt);
+  else if (E <= 64) route_tokens<64, 1, NT>(logits, T, E, k, t_begin, t_end, ids, w, cnt);
+  else if (E <= 128) route_tokens<64, 2, NT>(logits, T, E, k, t_begin, t_end, ids, w, cnt);
+  else if (MAXQ <= 4 || E <= 256) route_tokens<64, 4, NT>(logits, T, E, k, t_begin, t_end, ids, w, cnt);
+  else if (MAXQ <= 8 || E <= 512) route_tokens<64, (MAXQ < 8 ? MAXQ : 8), NT>(logits, T, E, k, t_begin, t_end, ids, w, cnt);
+  else route_tokens<64, MAXQ, NT>(logits, T, E, k, t_begin, t_end, ids, w, cnt);
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const float* __restrict__ logits, int T, int E, int k, int chunk_tokens,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
@@ -133,15 +149,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
   __syncthreads();
   const int t_begin = blockIdx.x * chunk_tokens;
   const int t_end = min(T, t_begin + chunk_tokens);
-  int* cnt = hist ? s_count : nullptr;
-  if (E <= 8) route_tokens<8, 1>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
-  else if (E <= 16) route_tokens<16, 1>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
-  else if (E <= 32) route_tokens<32, 1>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
-  else if (E <= 64) route_tokens<64, 1>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
-  else if (E <= 128) route_tokens<64, 2>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
-  else if (E <= 256) route_tokens<64, 4>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
-  else if (E <= 512) route_tokens<64, 8>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
-  else route_tokens<64, 16>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w, cnt);
+  route_range<kRouteThreads>(logits, T, E, k, t_begin, t_end, topk_ids, topk_w,
+                             hist ? s_count : nullptr);
   if (hist) {
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kRouteThreads)
@@ -170,7 +179,7 @@ __global__ __launch_bounds__(kRouteThreads) void hist_kernel(
 
 constexpr int kPermThreads = 256;
 
-// One block per group of kPermChunks routing chunks (and per column slice of
+// One block per group of `cpb` (<= kPermChunks) routing chunks (and per column slice of
 // x). Steps:
 //  1. One coalesced pass over the [nchunks][E] histogram gives each expert's
 //     total (hence, by an exclusive scan over experts, expert_offsets) and the
@@ -181,7 +190,7 @@ constexpr int kPermThreads = 256;
 //  3. The block copies its column slice of the assigned rows of x.
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const bf16_t* __restrict__ x, const int32_t* __restrict__ topk_ids, int T,
-    int H, int E, int k, int chunk_tokens, int nchunks, int slice_cols,
+    int H, int E, int k, int chunk_tokens, int nchunks, int cpb, int slice_cols,
     const int32_t* __restrict__ hist, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ row_token, int32_t* __restrict__ row_dest,
     bf16_t* __restrict__ x_perm) {
@@ -193,8 +202,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int c0 = blockIdx.x * kPermChunks;               // first routing chunk
-  const int nc = min(kPermChunks, nchunks - c0);         // routing chunks here
+  const int c0 = blockIdx.x * cpb;                       // first routing chunk
+  const int nc = min(cpb, nchunks - c0);                 // routing chunks here
 
   // 1a. totals and counts before this block (integer LDS atomics: exact and
   //     order-independent)
@@ -284,7 +293,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   __syncthreads();
 
   // 3. copy this block's column slice of each assigned row: x_perm[p] = x[t]
-  //    (8 independent 16-byte loads in flight per thread before the stores)
+  //    (8 independent 16-byte loads in flight per thread before the stores);
+  //    skipped when the consumer gathers the rows of x itself
+  if (!x_perm) return;
   const int c_begin = blockIdx.y * slice_cols;
   const int c_end = min(H, c_begin + slice_cols);
   const int vec_per_row = (c_end - c_begin) / 8;  // 16-byte vectors
@@ -309,7 +320,124 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   }
 }
 
+// Small batches (all T*k <= kMaxChunkAssign assignments in one routing
+// chunk): routing and the permutation in one launch. Every block routes all
+// T tokens into LDS (block 0 also writes the routing result, the offsets
+// and the row maps), scans the expert counts, ranks the assignments in
+// (t, j) order and copies its own column slice of the assigned rows of x.
+// 16 waves, so that one pass routes up to 16 tokens (E > 32) to 128 (E <= 8);
+// E <= kSmallMaxExperts.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallMaxExperts = 256;
+__global__ __launch_bounds__(kSmallThreads) void route_permute_small_kernel(
+    const float* __restrict__ logits, const bf16_t* __restrict__ x, int T, int H, int E,
+    int k, int slice_cols, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ row_dest, bf16_t* __restrict__ x_perm) {
+  __shared__ int s_count[kMaxExperts];
+  __shared__ int s_off[kMaxExperts];
+  __shared__ int s_ids[kMaxChunkAssign];
+  __shared__ float s_w[kMaxChunkAssign];
+  __shared__ int s_dest[kMaxChunkAssign];
+  __shared__ int s_wave_total[kSmallThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const bool lead = blockIdx.x == 0;
+  const int n = T * k;
+  for (int e = tid; e < E; e += kSmallThreads) s_count[e] = 0;
+  __syncthreads();
+  route_range<kSmallThreads, 4>(logits, T, E, k, 0, T, s_ids, s_w, s_count);
+  __syncthreads();
+  if (lead)
+    for (int i = tid; i < n; i += kSmallThreads) {
+      topk_ids[i] = s_ids[i];
+      topk_w[i] = s_w[i];
+    }
+  // exclusive scan of the expert counts (one expert per thread)
+  constexpr int EPT = kMaxExperts / kSmallThreads;
+  int cnt[EPT];
+  int my_sum = 0;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = tid * EPT + i;
+    cnt[i] = e < E ? s_count[e] : 0;
+    my_sum += cnt[i];
+  }
+  const int incl = wave_inclusive_scan(my_sum);
+  if (lane == kWave - 1) s_wave_total[wave] = incl;
+  __syncthreads();
+  int run = incl - my_sum;
+  for (int w = 0; w < wave; ++w) run += s_wave_total[w];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = tid * EPT + i;
+    if (e < E) {
+      s_off[e] = run;
+      if (lead) expert_offsets[e] = run;
+    }
+    run += cnt[i];
+  }
+  if (lead && tid == 0) expert_offsets[E] = n;
+  __syncthreads();
+  // stable rank of each assignment among the earlier ones with its expert
+  for (int i = tid; i < n; i += kSmallThreads) {
+    const int e = min(max(s_ids[i], 0), E - 1);
+    int rank = 0;
+    for (int i2 = 0; i2 < i; ++i2) rank += (s_ids[i2] == e);
+    const int p = min(s_off[e] + rank, n - 1);
+    s_dest[i] = p;
+    if (lead) {
+      row_dest[i] = p;
+      row_token[p] = i / k;
+    }
+  }
+  __syncthreads();
+  // this block's column slice of every assigned row: x_perm[p] = x[t]
+  // (8 independent 16-byte loads in flight per thread before the stores)
+  const int c_begin = blockIdx.x * slice_cols;
+  const int c_end = min(H, c_begin + slice_cols);
+  const int vec_per_row = (c_end - c_begin) / 8;  // 16-byte vectors
+  const int nvec = n * vec_per_row;
+  constexpr int U = 4;
+  for (int v0 = tid; v0 < nvec; v0 += kSmallThreads * U) {
+    uint4 val[U];
+    int64_t dst[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // out-of-range slots repeat the last vector (same source, same target)
+      const int v = min(v0 + u * kSmallThreads, nvec - 1);
+      const int i = v / vec_per_row;
+      const int c = c_begin + (v - i * vec_per_row) * 8;
+      val[u] = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(i / k) * H + c);
+      dst[u] = static_cast<int64_t>(s_dest[i]) * H + c;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) *reinterpret_cast<uint4*>(x_perm + dst[u]) = val[u];
+  }
+}
+
 }  // namespace
+
+// Measured: one launch wins up to 128 assignments (Mixtral-shaped T = 1 and
+// 32, Qwen2-shaped T = 16); at 256 (Mixtral T = 128) the 16 blocks' row copy
+// makes it slower than the two kernels.
+bool route_permute_fits_one_launch(int T, int E, int k) {
+  return static_cast<int64_t>(T) * k <= kMaxChunkAssign / 2 && E <= kSmallMaxExperts;
+}
+
+hipError_t launch_route_permute_small(const float* logits, const bf16_t* x, int T, int H,
+                                      int E, int k, int32_t* topk_ids, float* topk_w,
+                                      int32_t* expert_offsets, int32_t* row_token,
+                                      int32_t* row_dest, bf16_t* x_perm, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  const int slice = kPermuteSliceCols;
+  const int nslices = (H + slice - 1) / slice;
+  hipLaunchKernelGGL(route_permute_small_kernel, dim3(nslices), dim3(kSmallThreads), 0, stream,
+                     logits, x, T, H, E, k, slice, topk_ids, topk_w, expert_offsets, row_token,
+                     row_dest, x_perm);
+  return hipGetLastError();
+}
 
 // Tokens per routing chunk (one histogram row, one routing block): at most
 // 32 and kMaxChunkAssign / k; small batches use chunks of down to 4 tokens
@@ -355,10 +483,14 @@ hipError_t launch_permute(const bf16_t* x, const int32_t* topk_ids, int T,
   const int chunk = route_chunk_tokens(T, k);
   const int nchunks = route_num_chunks(T, k);
   const int slice = kPermuteSliceCols;
-  const int nslices = (H + slice - 1) / slice;
-  const int nblocks = (nchunks + kPermChunks - 1) / kPermChunks;
+  const int nslices = x_perm ? (H + slice - 1) / slice : 1;
+  // with a row copy, a block amortises its pass over the histogram over
+  // kPermChunks chunks; without one (maps only) it takes a single chunk, so
+  // that more blocks share the passes
+  const int cpb = x_perm ? kPermChunks : 1;
+  const int nblocks = (nchunks + cpb - 1) / cpb;
   hipLaunchKernelGGL(permute_kernel, dim3(nblocks, nslices), dim3(kPermThreads),
-                     0, stream, x, topk_ids, T, H, E, k, chunk, nchunks, slice,
+                     0, stream, x, topk_ids, T, H, E, k, chunk, nchunks, cpb, slice,
                      hist, expert_offsets, row_token, row_dest, x_perm);
   return hipGetLastError();
 }

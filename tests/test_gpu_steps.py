@@ -112,6 +112,9 @@ def test_combine(case, orc):
 
 
 def test_forward(case):
+    """The fused layer; small batches (T*k <= 128, E <= 256) route and
+    permute in one launch, larger ones in two, large-batch tiles gather rows
+    of x."""
     name, layer, d, ref = case
     T, k = ref["ids"].shape
     say("moe_forward", name, (T, layer.cfg.H, layer.cfg.F, layer.cfg.E, k))
@@ -121,4 +124,6 @@ def test_forward(case):
                         topk_ids=ids, topk_w=w)
     torch.cuda.synchronize()
     assert (ids.cpu().numpy() == ref["ids"]).all()
+    bound = route_weight_bound(d["logits"], ref["ids"], ref["w"])
+    assert (np.abs(w.cpu().numpy().astype(np.float64) - ref["w"]) <= bound).all()
     assert_close(gpu_bf16_f64(out), ref["out"], f"out[{name}]")
