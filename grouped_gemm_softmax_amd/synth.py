@@ -18,7 +18,10 @@ project:
   ranks r = 1..E, ranks assigned to experts by a seeded permutation, and
   logit[t, e] = ln p_rank(e) + Gumbel(0, 1) noise. Top-1 is then exactly
   Zipf-distributed, and top-k samples without replacement;
-* the Qwen2 shared expert's gate logits ~ N(0, 1).
+* the Qwen2 shared expert's gate logits ~ N(0, 1);
+* router weights W_r [E, H] ~ N(0, 0.02) in bf16 (logit spread
+  0.02 * sqrt(H): 0.9 at H = 2048, 1.3 at 4096, 1.7 at 7168), or, for the
+  tie tests, small integers (exact logits with many ties).
 
 Tensors are drawn with torch's seeded generator on the requested device.
 The same (config, T, seed) on the same device always gives the same values.
@@ -191,6 +194,28 @@ def make_layer(name: str, T: int, seed: int = 0, device="cpu",
             gate_logits=shared_gate_logits(cfg, T, seed, device),
         )
     return Layer(cfg, T, seed, x, logits, wg, wu, wd, shared)
+
+
+def router_weight(cfg: LayerConfig, seed: int, device, kind: str = "normal") -> torch.Tensor:
+    """bf16 [E, H] router weights (row e is expert e's router vector).
+    kind 'normal': N(0, WEIGHT_STD); 'ties_int': integers in -2..2."""
+    if kind == "normal":
+        return randn_bf16((cfg.E, cfg.H), WEIGHT_STD, device, cfg.name, seed, "w_router")
+    if kind == "ties_int":
+        g = _gen(device, cfg.name, seed, "w_router", kind)
+        return torch.randint(-2, 3, (cfg.E, cfg.H), generator=g, device=device).to(torch.bfloat16)
+    raise ValueError(f"unknown router weight kind {kind!r}")
+
+
+def router_input(cfg: LayerConfig, T: int, seed: int, device, kind: str = "normal") -> torch.Tensor:
+    """bf16 [T, H] token rows for the router. 'normal' is the layer's x
+    (make_layer draws the same values); 'ties_int': integers in -2..2."""
+    if kind == "normal":
+        return randn_bf16((T, cfg.H), 1.0, device, cfg.name, T, seed, "x")
+    if kind == "ties_int":
+        g = _gen(device, cfg.name, T, seed, "x", kind)
+        return torch.randint(-2, 3, (T, cfg.H), generator=g, device=device).to(torch.bfloat16)
+    raise ValueError(f"unknown router input kind {kind!r}")
 
 
 def shared_gate_logits(cfg: LayerConfig, T: int, seed: int, device) -> Optional[torch.Tensor]:

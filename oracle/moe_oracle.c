@@ -7,6 +7,9 @@
  * links, loads or calls it, and it shares no code with the HIP kernels.
  *
  * What it computes (one MoE expert layer, no token dropping):
+ *   router  : logits[t,e] = sum_h x[t,h] * W_r[e,h] (the gating scores the
+ *             routing starts from; the pages do not spell this projection
+ *             out, see router_logits below).
  *   route   : per token, the k largest router logits (ties -> lower expert
  *             index), in descending order, and a softmax over those k logits.
  *   permute : a stable counting sort of the T*k (token, slot) assignments by
@@ -69,6 +72,29 @@ int oracle_num_threads(void) {
 #else
   return 1;
 #endif
+}
+
+/* ----------------------------------------------------------------- router */
+
+/* Router projection: logits[t,e] = sum_h x[t,h] * W_r[e,h], h ascending, in
+ * fp64 (each bf16 product is exact in fp64, so only the sum rounds). The
+ * routing is done on the device from such gating scores in the Triton MoE
+ * page (setupai.cc), technical deep-dive; the pages do not state how the
+ * scores are produced. Reading taken: one bias-free linear map of the token
+ * row, W_r stored [E,H] (row e = expert e's router vector). */
+int oracle_router_logits(const uint16_t* x, int64_t T, int H, int E,
+                         const uint16_t* wr, double* logits) {
+  if (T < 0 || H < 1 || E < 1) return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      const uint16_t* xr = x + t * H;
+      const uint16_t* wrow = wr + (int64_t)e * H;
+      double s = 0.0;
+      for (int h = 0; h < H; ++h) s += bf16_to_f64(xr[h]) * bf16_to_f64(wrow[h]);
+      logits[t * E + e] = s;
+    }
+  return ORC_OK;
 }
 
 /* ------------------------------------------------------------------ route */

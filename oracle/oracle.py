@@ -50,6 +50,7 @@ def lib():
         path = build(force=False)
         L = ctypes.CDLL(path)
         L.oracle_num_threads.restype = _I
+        L.oracle_router_logits.argtypes = [_P, _I64, _I, _I, _P, _P]
         L.oracle_route.argtypes = [_P, _I64, _I, _I, _P, _P]
         L.oracle_permute.argtypes = [_P, _I64, _I, _I, _P, _P, _P]
         L.oracle_gather.argtypes = [_P, _P, _I64, _I, _P]
@@ -89,6 +90,19 @@ def _p(a: Optional[np.ndarray]):
 def _check(rc: int, what: str):
     if rc != 0:
         raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+def router_logits(x: np.ndarray, wr: np.ndarray) -> np.ndarray:
+    """Router projection logits[t,e] = sum_h x[t,h] wr[e,h] in fp64.
+    x [T,H] u16, wr [E,H] u16 -> float64 [T,E]."""
+    x, wr = _c(x, np.uint16), _c(wr, np.uint16)
+    T, H = x.shape
+    E = wr.shape[0]
+    assert wr.shape == (E, H)
+    out = np.empty((T, E), np.float64)
+    _check(lib().oracle_router_logits(_p(x), T, H, E, _p(wr), _p(out)),
+           "router_logits")
+    return out
 
 
 def route(logits: np.ndarray, k: int):
