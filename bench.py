@@ -16,6 +16,9 @@ gate/up+SwiGLU grouped GEMM), timed with HIP events on its launch stream.
 workload. `--sweep 1,128,512` repeats the measurement at other batch sizes of
 the same layer shape (listed under `sweep`).
 
+`--router` instead times the router projection fused with routing
+(moe_router_route) at every layer shape, against the unfused sequence.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 from __future__ import annotations
@@ -52,6 +55,10 @@ def parse():
                     help="tokens in the oracle's timed sample")
     ap.add_argument("--weights", choices=("packed", "rowmajor"), default="packed",
                     help="weight layout of the timed steps")
+    ap.add_argument("--router", action="store_true",
+                    help="only time the router row: moe_router_route (router GEMM + "
+                         "top-k routing) against torch's matmul + fp32 cast + moe_route, "
+                         "for every layer shape, one JSON line each, and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (the "
                          "known-size reference for HBM byte counters) and exit")
@@ -119,6 +126,56 @@ def roof(bytes_, flops, ms):
                 roofline_frac=max(t_hbm, t_mfma) / s)
 
 
+ROUTER_SHAPES = [("mixtral", 1), ("mixtral", 32), ("mixtral", 512), ("mixtral_large", 8192),
+                 ("qwen2", 16), ("qwen2", 1024), ("qwen2", 16384), ("dsv3", 128),
+                 ("dsv3", 4096)]
+
+
+def router_table(args, torch, B, synth):
+    """Router projection + routing of each layer shape: the fused library call
+    and the unfused sequence (bf16 matmul, cast to fp32, moe_route), each timed
+    over a burst of calls with HIP events on the launch stream. At small T the
+    host's call rate can bound both; the kernel trace of this command gives
+    the device times."""
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        for _ in range(5):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    for name, T in ROUTER_SHAPES:
+        cfg = synth.CONFIGS[name]
+        x = synth.router_input(cfg, T, args.seed, "cuda")
+        w = synth.router_weight(cfg, args.seed, "cuda")
+        wt = w.t().contiguous()
+        ids = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+        tw = torch.empty((T, cfg.k), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(B.moe_router_workspace_bytes(T, cfg.H, cfg.E, cfg.k), 16),
+                         dtype=torch.uint8, device="cuda")
+
+        def fused():
+            B.moe_router_route(x, w, cfg.k, ws=ws, out=(ids, tw, None))
+
+        def unfused():
+            B.moe_route(torch.matmul(x, wt).float(), cfg.k, ids, tw)
+
+        n = max(20, args.steps)
+        us_f, us_u = timed(fused, n), timed(unfused, n)
+        nbytes = 2 * (T + cfg.E) * cfg.H + 8 * T * cfg.k
+        print(json.dumps({"router": cfg.name, "T": T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
+                          "fused_us": round(us_f, 2), "matmul_cast_route_us": round(us_u, 2),
+                          "alg_bytes": nbytes, "fused_GBs": round(nbytes / us_f / 1e3, 1),
+                          "workspace_bytes": ws.numel() if ws.numel() > 16 else 0}),
+              flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -142,6 +199,11 @@ def main():
 
     from grouped_gemm_softmax_amd import binding as B
     from grouped_gemm_softmax_amd import synth
+
+    if args.router:
+        torch.cuda.set_device(0)
+        router_table(args, torch, B, synth)
+        return
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -41,6 +41,8 @@ _SZ = ctypes.c_size_t
 _SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "moe_router_workspace_bytes": (_SZ, [_I, _I, _I, _I]),
+    "moe_router_route": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_permute": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_gateup_swiglu": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
@@ -48,6 +50,8 @@ _SIGNATURES = {
     "moe_grouped_ffn": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
     "moe_forward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "moe_forward_routed": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P,
+                                _SZ, _P]),
     "moe_forward": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P,
                          ctypes.POINTER(SharedExpert), _P, _P, _P, _P, _SZ, _P]),
     "moe_pack_weights_bytes": (_SZ, [_I, _I, _I]),
@@ -121,6 +125,35 @@ def moe_route(logits: torch.Tensor, k: int, topk_ids=None, topk_w=None, stream=N
     _check(lib().moe_route(_ptr(logits), T, E, k, _ptr(topk_ids), _ptr(topk_w),
                            _stream(stream)), "moe_route")
     return topk_ids, topk_w
+
+
+def moe_router_workspace_bytes(T: int, H: int, E: int, k: int) -> int:
+    return int(lib().moe_router_workspace_bytes(T, H, E, k))
+
+
+def moe_router_route(x: torch.Tensor, w_router: torch.Tensor, k: int, logits=False,
+                     ws=None, out=None, stream=None):
+    """x bf16 [T,H], w_router bf16 [E,H] -> (topk_ids [T,k], topk_w [T,k]), plus
+    the fp32 logits [T,E] as a third element when `logits` is True."""
+    _need(x, torch.bfloat16, "x")
+    _need(w_router, torch.bfloat16, "w_router")
+    T, H = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != H:
+        raise ValueError(f"w_router: expected [E,{H}], got {tuple(w_router.shape)}")
+    dev = x.device
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev),
+               torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty((T, E), dtype=torch.float32, device=dev) if logits else None)
+    topk_ids, topk_w, lg = out
+    if ws is None:
+        ws = torch.empty(max(moe_router_workspace_bytes(T, H, E, k), 16), dtype=torch.uint8,
+                         device=dev)
+    _check(lib().moe_router_route(_ptr(x), _ptr(w_router), T, H, E, k, _ptr(lg),
+                                  _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "moe_router_route")
+    return (topk_ids, topk_w, lg) if lg is not None else (topk_ids, topk_w)
 
 
 def moe_permute_workspace_bytes(T: int, E: int, k: int) -> int:
@@ -255,6 +288,45 @@ def moe_forward_workspace_bytes(T, H, F, E, k, Fs=0) -> int:
     return int(lib().moe_forward_workspace_bytes(T, H, F, E, k, Fs))
 
 
+def _shared_struct(shared, packed):
+    if shared is None:
+        return None, 0
+    for n in ("w_gate", "w_up", "w_down"):
+        _weight(shared[n], "shared " + n, packed)
+    Fs = shared["w_gate"].shape[-1]
+    g = shared.get("gate_logits")
+    return SharedExpert(shared["w_gate"].data_ptr(), shared["w_up"].data_ptr(),
+                        shared["w_down"].data_ptr(), Fs,
+                        None if g is None else g.data_ptr()), Fs
+
+
+def moe_forward_routed(x, topk_ids, topk_w, w_gate, w_up, w_down,
+                       shared: Optional[dict] = None, out=None, ws=None, stream=None):
+    """Layer steps 2-5 from a given routing (topk_ids int32 [T,k], topk_w
+    fp32 [T,k]); weights row-major or all PackedWeight. Returns out."""
+    packed = isinstance(w_gate, PackedWeight)
+    _need(x, torch.bfloat16, "x")
+    _need(topk_ids, torch.int32, "topk_ids")
+    _need(topk_w, torch.float32, "topk_w")
+    for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _weight(t, n, packed)
+    T, H = x.shape
+    E, _, F = w_gate.shape
+    k = topk_ids.shape[1]
+    sh, Fs = _shared_struct(shared, packed)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(moe_forward_workspace_bytes(T, H, F, E, k, Fs), 16),
+                         dtype=torch.uint8, device=x.device)
+    _check(lib().moe_forward_routed(_ptr(x), _ptr(topk_ids), _ptr(topk_w), T, H, F, E, k,
+                                    _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                    ctypes.byref(sh) if sh is not None else None,
+                                    1 if packed else 0, _ptr(out), _ptr(ws), ws.numel(),
+                                    _stream(stream)), "moe_forward_routed")
+    return out
+
+
 def moe_forward(x, logits, k, w_gate, w_up, w_down, shared: Optional[dict] = None,
                 out=None, topk_ids=None, topk_w=None, ws=None, stream=None):
     """Whole layer. shared: None or dict(w_gate [H,Fs], w_up [H,Fs],
@@ -268,16 +340,7 @@ def moe_forward(x, logits, k, w_gate, w_up, w_down, shared: Optional[dict] = Non
         _weight(t, n, packed)
     T, H = x.shape
     E, _, F = w_gate.shape
-    sh = None
-    Fs = 0
-    if shared is not None:
-        for n in ("w_gate", "w_up", "w_down"):
-            _weight(shared[n], "shared " + n, packed)
-        Fs = shared["w_gate"].shape[-1]
-        g = shared.get("gate_logits")
-        sh = SharedExpert(shared["w_gate"].data_ptr(), shared["w_up"].data_ptr(),
-                          shared["w_down"].data_ptr(), Fs,
-                          None if g is None else g.data_ptr())
+    sh, Fs = _shared_struct(shared, packed)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     if ws is None:

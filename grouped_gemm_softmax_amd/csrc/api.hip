@@ -183,6 +183,35 @@ int moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids,
                                       static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_router_workspace_bytes(int T, int H, int E, int k) {
+  if (check_dims(T, E, k) != MOE_OK || check_width(H) != MOE_OK || T == 0) return 0;
+  const moe::RouterPlan p = moe::router_plan(T, H, E, moe::grouped_gemm_device_cus());
+  return align_up(moe::router_part_elems(p, T, E) * sizeof(float), 256);
+}
+
+int moe_router_route(const moe_bf16* x, const moe_bf16* w_router, int T, int H, int E,
+                     int k, float* logits_out, int32_t* topk_ids, float* topk_w,
+                     void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_dims(T, E, k));
+  MOE_TRY(check_width(H));
+  MOE_TRY(check_elems(T, H));
+  MOE_TRY(check_elems(E, H));
+  MOE_TRY(check_elems(T, E));
+  if (T == 0) return MOE_OK;
+  MOE_TRY(need_bf16(x));
+  MOE_TRY(need_bf16(w_router));
+  if (logits_out) MOE_TRY(need_word(logits_out));
+  MOE_TRY(need_word(topk_ids));
+  MOE_TRY(need_word(topk_w));
+  const moe::RouterPlan p = moe::router_plan(T, H, E, moe::grouped_gemm_device_cus());
+  const size_t need = align_up(moe::router_part_elems(p, T, E) * sizeof(float), 256);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0) MOE_TRY(need_bf16(ws));
+  return hip_status(moe::launch_router(p, x, w_router, T, H, E, k, logits_out,
+                                       static_cast<float*>(ws), topk_ids, topk_w,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 size_t moe_permute_workspace_bytes(int T, int E, int k) {
   if (check_dims(T, E, k) != MOE_OK) return 0;
   return permute_ws_bytes(T, E, k);
@@ -308,7 +337,10 @@ size_t moe_forward_workspace_bytes(int T, int H, int F, int E, int k, int Fs) {
   return forward_layout(T, H, F, E, k, Fs, moe::grouped_gemm_device_cus()).total;
 }
 
-static int forward_impl(const moe_bf16* x, const float* logits, int T, int H, int F, int E,
+// The layer from router logits (logits != null: steps 1-5) or from a routing
+// the caller made (ids_in / w_in: steps 2-5).
+static int forward_impl(const moe_bf16* x, const float* logits, const int32_t* ids_in,
+                        const float* w_in, int T, int H, int F, int E,
                         int k, const moe_bf16* w_gate, const moe_bf16* w_up,
                         const moe_bf16* w_down, const moe_shared_expert* shared,
                         moe_bf16* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
@@ -324,7 +356,12 @@ static int forward_impl(const moe_bf16* x, const float* logits, int T, int H, in
   MOE_TRY(check_elems(T, E));
   if (T == 0) return MOE_OK;
   MOE_TRY(need_bf16(x));
-  MOE_TRY(need_word(logits));
+  if (logits) {
+    MOE_TRY(need_word(logits));
+  } else {
+    MOE_TRY(need_word(ids_in));
+    MOE_TRY(need_word(w_in));
+  }
   MOE_TRY(need_bf16(w_gate));
   MOE_TRY(need_bf16(w_up));
   MOE_TRY(need_bf16(w_down));
@@ -345,6 +382,8 @@ static int forward_impl(const moe_bf16* x, const float* logits, int T, int H, in
   int32_t* hist = reinterpret_cast<int32_t*>(base + L.hist);
   int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(base + L.ids);
   float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(base + L.w);
+  const int32_t* ids_c = logits ? ids : ids_in;
+  const float* w_c = logits ? w : w_in;
   int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
   int32_t* row_token = reinterpret_cast<int32_t*>(base + L.row_token);
   int32_t* row_dest = reinterpret_cast<int32_t*>(base + L.row_dest);
@@ -364,15 +403,18 @@ static int forward_impl(const moe_bf16* x, const float* logits, int T, int H, in
     g1.seg[0].act = x;
     g1.seg[0].gather = row_token;
   }
-  if (!gather && moe::route_permute_fits_one_launch(T, E, k)) {
+  if (logits && !gather && moe::route_permute_fits_one_launch(T, E, k)) {
     // 1+2. small batch: routing and the permutation in one launch
     MOE_TRY(hip_status(moe::launch_route_permute_small(logits, x, T, H, E, k, ids, w, offsets,
                                                        row_token, row_dest, x_perm, s)));
   } else {
-    // 1. route + per-chunk histogram
-    MOE_TRY(hip_status(moe::launch_route(logits, T, E, k, ids, w, hist, s)));
+    // 1. route + per-chunk histogram, or the histogram of the given routing
+    if (logits)
+      MOE_TRY(hip_status(moe::launch_route(logits, T, E, k, ids, w, hist, s)));
+    else
+      MOE_TRY(hip_status(moe::launch_hist(ids_in, T, E, k, hist, s)));
     // 2. permute: scan, stable rank, row maps (+ x_perm rows unless gathered)
-    MOE_TRY(hip_status(moe::launch_permute(x, ids, T, H, E, k, hist, offsets, row_token,
+    MOE_TRY(hip_status(moe::launch_permute(x, ids_c, T, H, E, k, hist, offsets, row_token,
                                            row_dest, gather ? nullptr : x_perm, s)));
   }
   // 3. grouped gate/up + SwiGLU (shared expert as one more group over x)
@@ -396,7 +438,7 @@ static int forward_impl(const moe_bf16* x, const float* logits, int T, int H, in
   MOE_TRY(hip_status(moe::launch_grouped_gemm(g2, s)));
   // 5. combine (+ gated shared term)
   return hip_status(moe::launch_combine(y, true, L.ksplit, static_cast<int64_t>(M) * H,
-                                        row_dest, w, T, H, k, shared ? y_sh : nullptr,
+                                        row_dest, w_c, T, H, k, shared ? y_sh : nullptr,
                                         L.ksplit_sh, static_cast<int64_t>(T) * H,
                                         shared ? shared->gate_logits : nullptr, out, s));
 }
@@ -406,8 +448,8 @@ int moe_forward(const moe_bf16* x, const float* logits, int T, int H, int F, int
                 const moe_bf16* w_down, const moe_shared_expert* shared,
                 moe_bf16* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
                 size_t ws_bytes, void* stream) {
-  return forward_impl(x, logits, T, H, F, E, k, w_gate, w_up, w_down, shared, out,
-                      topk_ids_out, topk_w_out, ws, ws_bytes, stream, false);
+  return forward_impl(x, logits, nullptr, nullptr, T, H, F, E, k, w_gate, w_up, w_down, shared,
+                      out, topk_ids_out, topk_w_out, ws, ws_bytes, stream, false);
 }
 
 int moe_forward_packed(const moe_bf16* x, const float* logits, int T, int H, int F, int E,
@@ -415,8 +457,20 @@ int moe_forward_packed(const moe_bf16* x, const float* logits, int T, int H, int
                        const moe_bf16* w_down_packed, const moe_shared_expert* shared_packed,
                        moe_bf16* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
                        size_t ws_bytes, void* stream) {
-  return forward_impl(x, logits, T, H, F, E, k, w_gate_packed, w_up_packed, w_down_packed,
-                      shared_packed, out, topk_ids_out, topk_w_out, ws, ws_bytes, stream, true);
+  return forward_impl(x, logits, nullptr, nullptr, T, H, F, E, k, w_gate_packed, w_up_packed,
+                      w_down_packed, shared_packed, out, topk_ids_out, topk_w_out, ws, ws_bytes,
+                      stream, true);
+}
+
+int moe_forward_routed(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
+                       int H, int F, int E, int k, const moe_bf16* w_gate, const moe_bf16* w_up,
+                       const moe_bf16* w_down, const moe_shared_expert* shared,
+                       int weights_packed, moe_bf16* out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  if (weights_packed != 0 && weights_packed != 1) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_ids || !topk_w)) return MOE_ERR_INVALID_ARG;
+  return forward_impl(x, nullptr, topk_ids, topk_w, T, H, F, E, k, w_gate, w_up, w_down, shared,
+                      out, nullptr, nullptr, ws, ws_bytes, stream, weights_packed == 1);
 }
 
 }  // extern "C"

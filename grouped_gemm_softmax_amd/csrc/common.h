@@ -59,4 +59,34 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
+// Order-preserving map of an fp32 bit pattern to uint32 (larger float ->
+// larger key); -0.0 is first canonicalised to +0.0 so the two tie.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Segmented butterfly max over aligned groups of L lanes (L a power of 2).
+template <int L>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) {
+    const uint64_t o = __shfl_xor(v, m, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
 }  // namespace moe

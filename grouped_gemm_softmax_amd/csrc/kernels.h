@@ -90,6 +90,25 @@ int64_t packed_weight_elems(int G, int K, int N);
 hipError_t launch_pack_weights(const bf16_t* w, int G, int K, int N, bf16_t* packed,
                                hipStream_t stream);
 
+// --- router GEMM + routing (router.hip) ---
+// logits[t,e] = sum_h x[t,h] * w[e,h] (x [T,H], w [E,H], bf16, H % 8 == 0)
+// and the top-k routing on them. A plan fixes the block tile (16*nt tokens x
+// 16*nb experts) and the K-slices; a fused plan ranks inside the GEMM kernel
+// (one launch, no workspace), otherwise the fp32 slice tiles go to `part`
+// (router_part_elems floats) and a second launch adds and ranks them.
+// logits_out may be null.
+struct RouterPlan {
+  int nb, nt;        // 16-wide expert and token tiles per block
+  int kslice;        // K values per slice (a multiple of 64)
+  int nslices;
+  bool fused;
+};
+RouterPlan router_plan(int T, int H, int E, int cus);
+size_t router_part_elems(const RouterPlan& p, int T, int E);
+hipError_t launch_router(const RouterPlan& p, const bf16_t* x, const bf16_t* w, int T, int H,
+                         int E, int k, float* logits_out, float* part, int32_t* topk_ids,
+                         float* topk_w, hipStream_t stream);
+
 // --- combine (combine.hip) ---
 // y_perm/y_shared hold bf16 values (y_f32 == false) or fp32 values; with
 // nslices > 1 (fp32 only) they are K-slice partial sums, slice s at

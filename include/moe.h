@@ -89,6 +89,28 @@ const char* moe_status_string(int status);
 int moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids,
               float* topk_w, void* stream);
 
+/* Workspace needed by moe_router_route (device bytes) on the current device;
+ * 0 when the call needs none or the sizes are invalid. */
+size_t moe_router_workspace_bytes(int T, int H, int E, int k);
+
+/* Step 1 with the router projection in front of it. x bf16 [T,H] and
+ * w_router bf16 [E,H] (row e is expert e's router vector; both K-contiguous,
+ * H % 8 == 0) give the logits
+ *   logits[t,e] = sum_h x[t,h] * w_router[e,h]
+ * (bf16 products, exact in fp32, accumulated in fp32 in an unspecified
+ * order), and topk_ids / topk_w are exactly what moe_route returns on those
+ * fp32 logits. logits_out fp32 [T,E] receives the logits when it is not
+ * NULL (the routing does not need them in HBM). The routing inside the
+ * kernel follows the Triton MoE page (setupai.cc), technical deep-dive; the
+ * router projection is the step the pages' routing starts from (gating
+ * scores per token and expert) and is not itself given on them.
+ * ws: at least moe_router_workspace_bytes(T, H, E, k) device bytes, 16-byte
+ * aligned (may be NULL when that is 0). Errors as moe_route, plus
+ * MOE_ERR_WORKSPACE_TOO_SMALL. */
+int moe_router_route(const moe_bf16* x, const moe_bf16* w_router, int T, int H, int E,
+                     int k, float* logits_out, int32_t* topk_ids, float* topk_w,
+                     void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace needed by moe_permute (device bytes); 0 for invalid sizes. */
 size_t moe_permute_workspace_bytes(int T, int E, int k);
 
@@ -174,6 +196,25 @@ int moe_forward(const moe_bf16* x, const float* logits, int T, int H, int F,
                 const moe_bf16* w_down, const moe_shared_expert* shared,
                 moe_bf16* out, int32_t* topk_ids_out, float* topk_w_out,
                 void* ws, size_t ws_bytes, void* stream);
+
+/* The layer from a routing the caller already has (steps 2-5): topk_ids
+ * int32 [T,k] (ids in [0,E); ids outside are not checked on the device and
+ * give unspecified but in-bounds results) and topk_w fp32 [T,k], e.g. from
+ * moe_router_route, which computes them from x and the router weights with
+ * no [T,E] logits in HBM. The routing and its weights as an input of the
+ * expert layer follow the DeepGEMM article (itsolotime.com), section 1.3
+ * (the Mega MoE buffer layout's input region holds the top-k ids and
+ * weights next to x). weights_packed:
+ * 0 = row-major weights as in moe_forward, 1 = packed as in
+ * moe_forward_packed. Same workspace (moe_forward_workspace_bytes) and
+ * output as moe_forward; given the same ids and weights, out equals
+ * moe_forward's bit for bit. Four or five launches: expert histogram,
+ * permute, gate/up, down, combine. */
+int moe_forward_routed(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
+                       int H, int F, int E, int k, const moe_bf16* w_gate, const moe_bf16* w_up,
+                       const moe_bf16* w_down, const moe_shared_expert* shared,
+                       int weights_packed, moe_bf16* out, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* ---- Packed weights ----
  * Expert weights do not change between calls, so they can be re-laid out

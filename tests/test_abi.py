@@ -47,6 +47,67 @@ def test_route_validation(L):
     assert L.moe_route(NULL, 0, 8, 2, NULL, NULL, NULL) == OK      # T = 0: no-op
 
 
+def _router_ws_model(T, H, E, k, cus=256):
+    """Router plan as documented: tiles of 16*nt tokens x 16*nb experts; H cut
+    into slices of whole 64-wide chunks, at least 4 chunks each, until the
+    blocks reach 3 per compute unit (one slice when all experts fit a block
+    and the tiles give a block per compute unit); one slice with all experts
+    in the block ranks in the GEMM kernel (no workspace), else
+    nslices*T*E fp32 partials."""
+    if T == 0 or k > E:
+        return 0
+    nb = 1 if E <= 16 else 2 if E <= 32 else 4
+    nt = 1 if T <= 16 else 2 if T <= 32 else 4
+    tiles = -(-T // (16 * nt)) * -(-E // (16 * nb))
+    chunks = -(-H // 64)
+    S = -(-3 * cus // tiles)
+    if E <= 16 * nb and tiles >= cus:
+        S = 1
+    S = min(max(1, S), -(-chunks // 4))
+    per = -(-chunks // S)
+    nslices = -(-chunks // per)
+    if nslices == 1 and E <= 16 * nb:
+        return 0
+    return -(-nslices * T * E * 4 // 256) * 256
+
+
+@pytest.mark.parametrize("T,H,E,k", [(1, 4096, 8, 2), (32, 4096, 8, 2), (16, 2048, 60, 4),
+                                     (128, 7168, 256, 8), (4096, 7168, 256, 8),
+                                     (16384, 2048, 60, 4), (40000, 2048, 60, 4),
+                                     (20, 256, 1024, 16), (70, 200, 33, 3), (5, 64, 1, 1),
+                                     (64, 256, 16, 4), (0, 256, 8, 2), (16, 128, 8, 9)])
+def test_router_workspace_bytes(T, H, E, k):
+    assert B.moe_router_workspace_bytes(T, H, E, k) == _router_ws_model(T, H, E, k)
+
+
+def test_router_workspace_fused_cases():
+    # all experts in one block and one K-slice: no workspace
+    assert B.moe_router_workspace_bytes(64, 256, 16, 4) == 0      # H = 4 chunks
+    assert B.moe_router_workspace_bytes(16384, 2048, 60, 4) == 0  # >= 256 tiles
+    assert B.moe_router_workspace_bytes(16, 60, 8, 2) == 0        # invalid H
+
+
+def test_router_route_validation(L):
+    ws = B.moe_router_workspace_bytes(16, 2048, 60, 4)
+    assert ws > 0
+    args = lambda x=P, w=P, T=16, H=2048, E=60, k=4, lg=NULL, ids=P, ws_p=P, ws_bytes=ws: (
+        x, w, T, H, E, k, lg, ids, P, ws_p, ws_bytes, NULL)
+    assert L.moe_router_route(*args(x=NULL)) == INVALID
+    assert L.moe_router_route(*args(w=NULL)) == INVALID
+    assert L.moe_router_route(*args(ids=NULL)) == INVALID
+    assert L.moe_router_route(*args(x=Q)) == MISALIGNED
+    assert L.moe_router_route(*args(w=Q)) == MISALIGNED
+    assert L.moe_router_route(*args(lg=ctypes.c_void_p(0x10002))) == MISALIGNED
+    assert L.moe_router_route(*args(ws_p=Q)) == MISALIGNED
+    assert L.moe_router_route(*args(H=60)) == SHAPE                  # H % 8 != 0
+    assert L.moe_router_route(*args(k=61)) == SHAPE                  # k > E
+    assert L.moe_router_route(*args(E=2000)) == SHAPE                # E > 1024
+    assert L.moe_router_route(*args(k=0)) == INVALID
+    assert L.moe_router_route(*args(ws_bytes=ws - 1)) == WS_SMALL
+    assert L.moe_router_route(*args(ws_p=NULL)) == INVALID
+    assert L.moe_router_route(NULL, NULL, 0, 64, 8, 2, NULL, NULL, NULL, NULL, 0, NULL) == OK
+
+
 def test_permute_validation(L):
     ws = B.moe_permute_workspace_bytes(100, 8, 2)
     assert ws > 0 and ws % 256 == 0
@@ -99,6 +160,21 @@ def test_forward_validation(L):
     assert _fwd(L, shared=null_shared, ws_bytes=1 << 40) == INVALID
     assert L.moe_forward(NULL, NULL, 0, 64, 96, 8, 2, NULL, NULL, NULL, None, NULL,
                          NULL, NULL, NULL, 0, NULL) == OK
+
+
+def test_forward_routed_validation(L):
+    ws = B.moe_forward_workspace_bytes(10, 64, 96, 8, 2, 0)
+    args = lambda x=P, ids=P, w=P, k=2, packed=0, ws_bytes=ws: (
+        x, ids, w, 10, 64, 96, 8, k, P, P, P, None, packed, P, P, ws_bytes, NULL)
+    assert L.moe_forward_routed(*args(x=NULL)) == INVALID
+    assert L.moe_forward_routed(*args(ids=NULL)) == INVALID
+    assert L.moe_forward_routed(*args(w=NULL)) == INVALID
+    assert L.moe_forward_routed(*args(ids=ctypes.c_void_p(0x10002))) == MISALIGNED
+    assert L.moe_forward_routed(*args(packed=2)) == INVALID
+    assert L.moe_forward_routed(*args(k=9)) == SHAPE
+    assert L.moe_forward_routed(*args(ws_bytes=ws - 1)) == WS_SMALL
+    assert L.moe_forward_routed(NULL, NULL, NULL, 0, 64, 96, 8, 2, NULL, NULL, NULL, None, 0,
+                                NULL, NULL, 0, NULL) == OK
 
 
 def _down_ksplit(T, H, F, E, k, Fs, cus=256):
