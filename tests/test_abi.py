@@ -181,7 +181,7 @@ def _down_ksplit(T, H, F, E, k, Fs, cus=256):
     """Re-statement of the host heuristic for K-slices of the fused layer's
     down projection, as (routed, shared). Tile: large (256 rows x 256
     columns, 32-deep stages) at >= 192 rows per expert, large128 (128 x 256,
-    32-deep) at 64..191 when its expected items reach 2 x CUs, else large;
+    64-deep) at 64..191 when its expected items reach 2 x CUs, else large;
     small (32 x 64, 64-deep) below 64. Expected items: one partial row tile per touched expert plus
     the full ones, times the column tiles (plus the shared expert's). The
     split doubles while twice the items still fit in 2 x CUs and each slice
@@ -190,7 +190,7 @@ def _down_ksplit(T, H, F, E, k, Fs, cus=256):
     2 x CUs and keep >= 4 K-steps each."""
     A = T * k
     rows = A // E
-    BT, BF, BK = (256, 256, 32) if rows >= 192 else (128, 256, 32) if rows >= 64 else (32, 64, 64)
+    BT, BF, BK = (256, 256, 32) if rows >= 192 else (128, 256, 64) if rows >= 64 else (32, 64, 64)
     if BT == 128:
         items128 = (min(A, E) + A // 128) * -(-H // 256)
         if Fs:
