@@ -17,6 +17,9 @@
  *   gate/up : per expert, G = X W_gate, U = X W_up, h = silu(G) * U.
  *   down    : y = h W_down.
  *   combine : out[t] = sum_j w[t,j] * y[row of (t,j)]  (+ s_t * shared(x[t])).
+ *   fp8     : weights as OCP E4M3 codes with one power-of-two scale per
+ *             output column; the layer is then computed on the dequantized
+ *             weights (see the fp8 section below).
  *
  * Sources (restated, not quoted):
  *   - "Triton-MoE-Dispatch-Kernel erreicht 131 % von Megablocks" (lumeric.app),
@@ -95,6 +98,83 @@ int oracle_router_logits(const uint16_t* x, int64_t T, int H, int E,
       logits[t * E + e] = s;
     }
   return ORC_OK;
+}
+
+/* -------------------------------------------------------------------- fp8 */
+
+/* Weights in 8-bit floating point. The DeepGEMM article (itsolotime.com),
+ * sections 1.1 and 5.3, runs the Mega MoE's two expert GEMMs in low
+ * precision (FP8 and FP4 operands) but gives no format details. Readings
+ * taken: the weights are stored as E4M3 codes of the OCP 8-bit floating
+ * point specification (1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+ * bits; exponent field 0 is subnormal, m/8 * 2^-6; S.1111.111 is NaN; no
+ * infinities; largest finite value 448), each output column n of each
+ * matrix g with one scale 2^e[g,n]; the activations stay bf16. Every
+ * dequantized weight code * 2^e is then exactly a bf16 value (8 exponent
+ * bits cover the range), so the layer on fp8 weights is the bf16 layer on
+ * the dequantized weights. */
+
+/* Value of one E4M3 code (NaN for the two NaN codes). */
+double oracle_e4m3_value(uint8_t c) {
+  const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m / 8.0, -6);
+  else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Per column: e = the smallest integer with max_k |w[g,k,n]| <= 448 * 2^e
+ * (0 for an all-zero column), so nothing saturates; then each weight's code
+ * is the E4M3 value nearest to w / 2^e, found by scanning all 127
+ * non-negative finite codes, a tie going to the code with an even mantissa
+ * (round to nearest, ties to even, on the code grid); the sign is the
+ * weight's. w bf16 [G,K,N] -> codes [G,K,N], scales[g*N+n] = 2^e. */
+int oracle_quantize_e4m3(const uint16_t* w, int64_t G, int K, int N, uint8_t* codes,
+                         double* scales) {
+  if (G < 0 || K < 1 || N < 1) return ORC_ERR_ARG;
+  double mag[127];
+  for (int c = 0; c < 127; ++c) mag[c] = oracle_e4m3_value((uint8_t)c);
+#pragma omp parallel for schedule(static)
+  for (int64_t gn = 0; gn < G * N; ++gn) {
+    const int64_t g = gn / N;
+    const int n = (int)(gn % N);
+    const uint16_t* wg = w + g * (int64_t)K * N;
+    double amax = 0.0;
+    for (int k = 0; k < K; ++k) {
+      const double a = fabs(bf16_to_f64(wg[(int64_t)k * N + n]));
+      if (a > amax) amax = a;
+    }
+    int e = 0;
+    if (amax > 0.0) {
+      e = -200;
+      while (amax > ldexp(448.0, e)) ++e;
+    }
+    scales[gn] = ldexp(1.0, e);
+    for (int k = 0; k < K; ++k) {
+      const double x = bf16_to_f64(wg[(int64_t)k * N + n]);
+      const double v = fabs(ldexp(x, -e));
+      int best = 0;
+      for (int c = 1; c < 127; ++c) {
+        const double dc = fabs(mag[c] - v), db = fabs(mag[best] - v);
+        if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+      }
+      codes[g * (int64_t)K * N + (int64_t)k * N + n] =
+          (uint8_t)(best | (signbit(x) ? 0x80 : 0));
+    }
+  }
+  return ORC_OK;
+}
+
+/* w[g,k,n] = value(codes[g,k,n]) * scales[g*N+n]. */
+void oracle_dequant_e4m3(const uint8_t* codes, const double* scales, int64_t G, int K, int N,
+                         double* w) {
+  for (int64_t g = 0; g < G; ++g)
+    for (int k = 0; k < K; ++k)
+      for (int n = 0; n < N; ++n) {
+        const int64_t i = g * (int64_t)K * N + (int64_t)k * N + n;
+        w[i] = oracle_e4m3_value(codes[i]) * scales[g * N + n];
+      }
 }
 
 /* ------------------------------------------------------------------ route */

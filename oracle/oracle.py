@@ -51,6 +51,11 @@ def lib():
         L = ctypes.CDLL(path)
         L.oracle_num_threads.restype = _I
         L.oracle_router_logits.argtypes = [_P, _I64, _I, _I, _P, _P]
+        L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_value.restype = ctypes.c_double
+        L.oracle_quantize_e4m3.argtypes = [_P, _I64, _I, _I, _P, _P]
+        L.oracle_dequant_e4m3.argtypes = [_P, _P, _I64, _I, _I, _P]
+        L.oracle_dequant_e4m3.restype = None
         L.oracle_route.argtypes = [_P, _I64, _I, _I, _P, _P]
         L.oracle_permute.argtypes = [_P, _I64, _I, _I, _P, _P, _P]
         L.oracle_gather.argtypes = [_P, _P, _I64, _I, _P]
@@ -103,6 +108,38 @@ def router_logits(x: np.ndarray, wr: np.ndarray) -> np.ndarray:
     _check(lib().oracle_router_logits(_p(x), T, H, E, _p(wr), _p(out)),
            "router_logits")
     return out
+
+
+def e4m3_values() -> np.ndarray:
+    """Values of the 256 E4M3 codes (float64; NaN for the NaN codes)."""
+    return np.array([lib().oracle_e4m3_value(c) for c in range(256)], np.float64)
+
+
+def quantize_e4m3(w: np.ndarray):
+    """bf16 weights [G,K,N] (or [K,N]: G = 1) -> (codes uint8 same shape,
+    per-column power-of-two scales float64 [G,N])."""
+    w = _c(w, np.uint16)
+    squeeze = w.ndim == 2
+    if squeeze:
+        w = w[None]
+    G, K, N = w.shape
+    codes = np.empty((G, K, N), np.uint8)
+    scales = np.empty((G, N), np.float64)
+    _check(lib().oracle_quantize_e4m3(_p(w), G, K, N, _p(codes), _p(scales)), "quantize_e4m3")
+    return (codes[0], scales[0]) if squeeze else (codes, scales)
+
+
+def dequant_e4m3(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """value(code) * scale per column -> float64, same shape as codes."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float64)
+    squeeze = codes.ndim == 2
+    if squeeze:
+        codes, scales = codes[None], scales[None]
+    G, K, N = codes.shape
+    out = np.empty((G, K, N), np.float64)
+    lib().oracle_dequant_e4m3(_p(codes), _p(scales), G, K, N, _p(out))
+    return out[0] if squeeze else out
 
 
 def route(logits: np.ndarray, k: int):
