@@ -16,6 +16,9 @@ gate/up+SwiGLU grouped GEMM), timed with HIP events on its launch stream.
 workload. `--sweep 1,128,512` repeats the measurement at other batch sizes of
 the same layer shape (listed under `sweep`).
 
+`--weights fp8` times the layer on FP8 (E4M3) weights with per-column
+scales (moe_forward_fp8; bf16 activations and MFMA), which computes exactly
+the bf16 layer on the dequantized weights at half the weight bytes.
 `--router` instead times the router projection fused with routing
 (moe_router_route) at every layer shape, against the unfused sequence.
 
@@ -53,8 +56,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32,
                     help="tokens in the oracle's timed sample")
-    ap.add_argument("--weights", choices=("packed", "rowmajor"), default="packed",
-                    help="weight layout of the timed steps")
+    ap.add_argument("--weights", choices=("packed", "rowmajor", "fp8"), default="packed",
+                    help="weight layout of the timed steps (fp8: E4M3 codes with per-column "
+                         "scales, moe_forward_fp8; bf16 arithmetic)")
     ap.add_argument("--router", action="store_true",
                     help="only time the router row: moe_router_route (router GEMM + "
                          "top-k routing) against torch's matmul + fp32 cast + moe_route, "
@@ -65,26 +69,28 @@ def parse():
     return ap.parse_args()
 
 
-def work_model(cfg, T, counts):
+def work_model(cfg, T, counts, wb=2):
     """Algorithmic FLOPs and HBM bytes of one forward, per kernel.
-    counts: rows per routed expert (E_touched = experts with rows)."""
+    counts: rows per routed expert (E_touched = experts with rows); wb: bytes
+    per weight (2 bf16, 1 fp8; fp8 adds a 4-byte scale per output column)."""
     H, F, E, k, Fs = cfg.H, cfg.F, cfg.E, cfg.k, cfg.Fs
     A = T * k
     Et = int((counts > 0).sum())
     m = {}
     m["route"] = dict(bytes=4 * T * E + 8 * A, flops=0)
     m["permute"] = dict(bytes=4 * A + 2 * T * H + 2 * A * H + 8 * A, flops=0)
-    g1 = 4 * H * F * Et + 2 * A * H + 2 * A * F
+    sc = 4 if wb == 1 else 0                # fp8 column scales
+    g1 = 2 * wb * H * F * Et + 2 * sc * F * Et + 2 * A * H + 2 * A * F
     g1f = 4 * A * H * F
     # routed part of the gate/up GEMM alone (what moe_gateup_swiglu runs)
     m["gateup_swiglu_routed"] = dict(bytes=g1, flops=g1f)
-    g2 = 2 * F * H * Et + 2 * A * F + 2 * A * H
+    g2 = wb * F * H * Et + sc * H * Et + 2 * A * F + 2 * A * H
     g2f = 2 * A * F * H
     cb = 2 * A * H + 8 * A + 2 * T * H
     if Fs:
-        g1 += 4 * H * Fs + 2 * T * H + 2 * T * Fs
+        g1 += 2 * wb * H * Fs + 2 * sc * Fs + 2 * T * H + 2 * T * Fs
         g1f += 4 * T * H * Fs
-        g2 += 2 * Fs * H + 2 * T * Fs + 2 * T * H
+        g2 += wb * Fs * H + sc * H + 2 * T * Fs + 2 * T * H
         g2f += 2 * T * Fs * H
         cb += 2 * T * H + (4 * T if cfg.shared_gated else 0)
     m["gateup_swiglu"] = dict(bytes=g1, flops=g1f)
@@ -220,17 +226,18 @@ def main():
             lay.shared = dict(weights_from.shared, gate_logits=lay.shared["gate_logits"])
         return lay
 
-    def weights_of(layer, packed):
+    def weights_of(layer, mode):
         """(w_gate, w_up, w_down, shared) of a layer in the timed layout."""
-        if not packed:
+        if mode == "rowmajor":
             return layer.w_gate, layer.w_up, layer.w_down, layer.shared
-        return (pk["wg"], pk["wu"], pk["wd"],
-                None if layer.shared is None else dict(pk["shared"],
+        src = pk8 if mode == "fp8" else pk
+        return (src["wg"], src["wu"], src["wd"],
+                None if layer.shared is None else dict(src["shared"],
                                                        gate_logits=layer.shared["gate_logits"]))
 
-    def measure(layer, steps, warmup, packed):
+    def measure(layer, steps, warmup, mode):
         T, H, F, E, k = layer.T, cfg.H, cfg.F, cfg.E, cfg.k
-        wg, wu, wd, sh = weights_of(layer, packed)
+        wg, wu, wd, sh = weights_of(layer, mode)
         Fs = cfg.Fs
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
         ids = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -256,11 +263,11 @@ def main():
         counts = torch.bincount(ids.flatten().long(), minlength=E).cpu().numpy()
         return ms, counts
 
-    def time_gateup(layer, steps, packed):
+    def time_gateup(layer, steps, mode):
         """Average duration of the gate/up+SwiGLU grouped GEMM alone, with the
         same inputs, weights and launch configuration as inside the step."""
         k = cfg.k
-        wg, wu, _, _ = weights_of(layer, packed)
+        wg, wu, _, _ = weights_of(layer, mode)
         ids, w = B.moe_route(layer.logits, k, stream=stream)
         off, rt, rd, xp = B.moe_permute(layer.x, ids, cfg.E, stream=stream)
         h = torch.empty((xp.shape[0], cfg.F), dtype=torch.bfloat16, device=dev)
@@ -278,7 +285,7 @@ def main():
 
     # ---- headline workload ----
     layer = layer_for(args.T)
-    packed = args.weights == "packed"
+    mode = args.weights
     torch.cuda.synchronize()
     # one-off weight packing (model-load time), timed on its own
     e0 = torch.cuda.Event(enable_timing=True)
@@ -293,12 +300,25 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     pack_ms = e0.elapsed_time(e1)
-    ms, counts = measure(layer, args.steps, args.warmup, packed)
-    ms_other, _ = measure(layer, max(10, args.steps // 2), 5, not packed)
-    total_b, total_f, per_kernel, Et = work_model(cfg, args.T, counts)
+    pk8, quant_ms = None, None
+    if mode == "fp8":
+        e0.record(stream)
+        pk8 = dict(wg=B.moe_quantize_fp8(layer.w_gate, stream=stream),
+                   wu=B.moe_quantize_fp8(layer.w_up, stream=stream),
+                   wd=B.moe_quantize_fp8(layer.w_down, stream=stream))
+        if layer.shared is not None:
+            pk8["shared"] = {n: B.moe_quantize_fp8(layer.shared[n], stream=stream)
+                             for n in ("w_gate", "w_up", "w_down")}
+        e1.record(stream)
+        torch.cuda.synchronize()
+        quant_ms = e0.elapsed_time(e1)
+    other = {"packed": "rowmajor", "rowmajor": "packed", "fp8": "packed"}[mode]
+    ms, counts = measure(layer, args.steps, args.warmup, mode)
+    ms_other, _ = measure(layer, max(10, args.steps // 2), 5, other)
+    total_b, total_f, per_kernel, Et = work_model(cfg, args.T, counts, 1 if mode == "fp8" else 2)
     r = roof(total_b, total_f, ms)
 
-    g1_ms = time_gateup(layer, max(args.steps, 20), packed)
+    g1_ms = time_gateup(layer, max(args.steps, 20), mode)
     g1 = per_kernel["gateup_swiglu_routed"]
     g1r = roof(g1["bytes"], g1["flops"], g1_ms)
     if g1r["bound"] == "hbm":
@@ -320,8 +340,8 @@ def main():
         if tok == args.T:
             continue
         lay = layer_for(tok, weights_from=layer)
-        ms_t, counts_t = measure(lay, max(10, args.steps // 2), 5, packed)
-        b_t, f_t, _, et_t = work_model(cfg, tok, counts_t)
+        ms_t, counts_t = measure(lay, max(10, args.steps // 2), 5, mode)
+        b_t, f_t, _, et_t = work_model(cfg, tok, counts_t, 1 if mode == "fp8" else 2)
         rr = roof(b_t, f_t, ms_t)
         sweep.append(dict(T=tok, ms_per_step=round(ms_t, 5), GBs=round(rr["gbs"], 1),
                           TFLOPs=round(rr["tflops"], 2), hbm_frac=round(rr["hbm_frac"], 4),
@@ -360,9 +380,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
+        "weight_dtype": "fp8_e4m3" if mode == "fp8" else "bf16",
         "data": "synthetic (seeded; x~N(0,1), weights~N(0,0.02), logits~N(0,1))",
         "config": {"workload": f"{cfg.desc}: T={args.T}, H={cfg.H}, F={cfg.F}, E={cfg.E}, "
-                               f"top-{cfg.k}, bf16, {args.weights} weights",
+                               f"top-{cfg.k}, bf16, "
+                               + ("fp8 E4M3 weights with per-column scales"
+                                  if mode == "fp8" else f"{args.weights} weights"),
                    "weights": args.weights,
                    "T": args.T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "k": cfg.k,
                    "Fs": cfg.Fs, "experts_touched": Et, "parallelism": "none (1 GPU)"},
@@ -373,8 +396,9 @@ def main():
         "layer_roofline_frac": round(r["roofline_frac"], 4),
         "alg_bytes": total_b,
         "alg_flops": total_f,
-        "rowmajor_ms_per_step" if packed else "packed_ms_per_step": round(ms_other, 5),
+        other + "_ms_per_step": round(ms_other, 5),
         "pack_ms": round(pack_ms, 3),
+        "quantize_ms": None if quant_ms is None else round(quant_ms, 3),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "sweep": sweep,

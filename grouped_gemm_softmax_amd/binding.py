@@ -34,6 +34,13 @@ class SharedExpert(ctypes.Structure):
                 ("gate_logits", ctypes.c_void_p)]
 
 
+class SharedExpertFp8(ctypes.Structure):
+    _fields_ = [("w_gate", ctypes.c_void_p), ("s_gate", ctypes.c_void_p),
+                ("w_up", ctypes.c_void_p), ("s_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p),
+                ("Fs", ctypes.c_int32), ("gate_logits", ctypes.c_void_p)]
+
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _SZ = ctypes.c_size_t
@@ -60,6 +67,12 @@ _SIGNATURES = {
     "moe_down_packed": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "moe_forward_packed": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P,
                                 ctypes.POINTER(SharedExpert), _P, _P, _P, _P, _SZ, _P]),
+    "moe_fp8_weights_bytes": (_SZ, [_I, _I, _I]),
+    "moe_quantize_fp8": (_I, [_P, _I, _I, _I, _P, _SZ, _P, _P]),
+    "moe_gateup_swiglu_fp8": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "moe_down_fp8": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "moe_forward_fp8": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
+                             ctypes.POINTER(SharedExpertFp8), _P, _P, _P, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -86,7 +99,7 @@ def header_symbols(path: str = HEADER):
     """Function names declared in include/moe.h."""
     text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -219,8 +232,54 @@ def _weight(w, name: str, packed: bool):
     return w
 
 
+class Fp8Weight:
+    """A [G,K,N] weight tensor as E4M3 codes in the library's block layout
+    (`codes`, uint8) with per-column fp32 power-of-two scales (`scales`,
+    [G,N]), from moe_quantize_fp8."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, G: int, K: int, N: int):
+        self.codes, self.scales, self.G, self.K, self.N = codes, scales, G, K, N
+        self.shape = (G, K, N)
+
+
+def moe_fp8_weights_bytes(G: int, K: int, N: int) -> int:
+    return int(lib().moe_fp8_weights_bytes(G, K, N))
+
+
+def moe_quantize_fp8(w: torch.Tensor, stream=None) -> Fp8Weight:
+    """w bf16 [G,K,N] (or [K,N], taken as G = 1) -> Fp8Weight."""
+    _need(w, torch.bfloat16, "w")
+    G, K, N = (1, *w.shape) if w.dim() == 2 else w.shape
+    nbytes = moe_fp8_weights_bytes(G, K, N)
+    codes = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((G, N), dtype=torch.float32, device=w.device)
+    _check(lib().moe_quantize_fp8(_ptr(w), G, K, N, _ptr(codes), codes.numel(), _ptr(scales),
+                                  _stream(stream)), "moe_quantize_fp8")
+    return Fp8Weight(codes, scales, G, K, N)
+
+
+def _fp8(w, name):
+    if not isinstance(w, Fp8Weight):
+        raise TypeError(f"{name}: expected an Fp8Weight (moe_quantize_fp8)")
+    return w
+
+
 def moe_gateup_swiglu(x_perm, expert_offsets, w_gate, w_up, h=None, stream=None):
-    """w_gate, w_up: bf16 [E,H,F] tensors, or PackedWeight (packed call)."""
+    """w_gate, w_up: bf16 [E,H,F] tensors, PackedWeight (packed call) or
+    Fp8Weight (fp8 call)."""
+    if isinstance(w_gate, Fp8Weight):
+        _need(x_perm, torch.bfloat16, "x_perm")
+        _need(expert_offsets, torch.int32, "expert_offsets")
+        _fp8(w_up, "w_up")
+        M, H = x_perm.shape
+        E, _, F = w_gate.shape
+        if h is None:
+            h = torch.empty((M, F), dtype=torch.bfloat16, device=x_perm.device)
+        _check(lib().moe_gateup_swiglu_fp8(
+            _ptr(x_perm), _ptr(expert_offsets), M, H, F, E, _ptr(w_gate.codes),
+            _ptr(w_gate.scales), _ptr(w_up.codes), _ptr(w_up.scales), _ptr(h),
+            _stream(stream)), "moe_gateup_swiglu_fp8")
+        return h
     packed = isinstance(w_gate, PackedWeight)
     _need(x_perm, torch.bfloat16, "x_perm")
     _need(expert_offsets, torch.int32, "expert_offsets")
@@ -238,7 +297,18 @@ def moe_gateup_swiglu(x_perm, expert_offsets, w_gate, w_up, h=None, stream=None)
 
 
 def moe_down(h, expert_offsets, w_down, y_perm=None, stream=None):
-    """w_down: bf16 [E,F,H] tensor, or PackedWeight (packed call)."""
+    """w_down: bf16 [E,F,H] tensor, PackedWeight (packed call) or Fp8Weight."""
+    if isinstance(w_down, Fp8Weight):
+        _need(h, torch.bfloat16, "h")
+        _need(expert_offsets, torch.int32, "expert_offsets")
+        M, F = h.shape
+        E, _, H = w_down.shape
+        if y_perm is None:
+            y_perm = torch.empty((M, H), dtype=torch.bfloat16, device=h.device)
+        _check(lib().moe_down_fp8(_ptr(h), _ptr(expert_offsets), M, F, H, E,
+                                  _ptr(w_down.codes), _ptr(w_down.scales), _ptr(y_perm),
+                                  _stream(stream)), "moe_down_fp8")
+        return y_perm
     packed = isinstance(w_down, PackedWeight)
     _need(h, torch.bfloat16, "h")
     _need(expert_offsets, torch.int32, "expert_offsets")
@@ -333,6 +403,9 @@ def moe_forward(x, logits, k, w_gate, w_up, w_down, shared: Optional[dict] = Non
     w_down [Fs,H], gate_logits [T] fp32 or None). Returns out [T,H] bf16.
     With PackedWeight weights (all of them, shared expert included: packed
     from [1,H,Fs] / [1,Fs,H]) this calls moe_forward_packed."""
+    if isinstance(w_gate, Fp8Weight):
+        return _forward_fp8(x, logits, k, w_gate, w_up, w_down, shared, out, topk_ids,
+                            topk_w, ws, stream)
     packed = isinstance(w_gate, PackedWeight)
     _need(x, torch.bfloat16, "x")
     _need(logits, torch.float32, "logits")
@@ -351,4 +424,36 @@ def moe_forward(x, logits, k, w_gate, w_up, w_down, shared: Optional[dict] = Non
               ctypes.byref(sh) if sh is not None else None, _ptr(out), _ptr(topk_ids),
               _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)),
            "moe_forward_packed" if packed else "moe_forward")
+    return out
+
+
+def _forward_fp8(x, logits, k, w_gate, w_up, w_down, shared, out, topk_ids, topk_w, ws,
+                 stream):
+    _need(x, torch.bfloat16, "x")
+    _need(logits, torch.float32, "logits")
+    for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _fp8(t, n)
+    T, H = x.shape
+    E, _, F = w_gate.shape
+    sh, Fs = None, 0
+    if shared is not None:
+        for n in ("w_gate", "w_up", "w_down"):
+            _fp8(shared[n], "shared " + n)
+        Fs = shared["w_gate"].shape[-1]
+        g = shared.get("gate_logits")
+        sh = SharedExpertFp8(shared["w_gate"].codes.data_ptr(), shared["w_gate"].scales.data_ptr(),
+                             shared["w_up"].codes.data_ptr(), shared["w_up"].scales.data_ptr(),
+                             shared["w_down"].codes.data_ptr(),
+                             shared["w_down"].scales.data_ptr(), Fs,
+                             None if g is None else g.data_ptr())
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(moe_forward_workspace_bytes(T, H, F, E, k, Fs), 16),
+                         dtype=torch.uint8, device=x.device)
+    _check(lib().moe_forward_fp8(
+        _ptr(x), _ptr(logits), T, H, F, E, k, _ptr(w_gate.codes), _ptr(w_gate.scales),
+        _ptr(w_up.codes), _ptr(w_up.scales), _ptr(w_down.codes), _ptr(w_down.scales),
+        ctypes.byref(sh) if sh is not None else None, _ptr(out), _ptr(topk_ids), _ptr(topk_w),
+        _ptr(ws), ws.numel(), _stream(stream)), "moe_forward_fp8")
     return out

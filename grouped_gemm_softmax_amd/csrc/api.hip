@@ -72,12 +72,13 @@ struct ForwardLayout {
 };
 
 moe::GemmProblem down_problem(const bf16_t* h, const int32_t* offsets, int M, int F,
-                              int H, int E, const bf16_t* wd, void* y, bool packed);
+                              int H, int E, const bf16_t* wd, void* y, int layout,
+                              const float* sd = nullptr);
 
 // The fused layer's down projection (routed + optional shared segment) with
 // fp32 output; pointers may be null when only the shape matters.
 moe::GemmProblem forward_down_problem(int T, int H, int F, int E, int k, int Fs) {
-  moe::GemmProblem g2 = down_problem(nullptr, nullptr, T * k, F, H, E, nullptr, nullptr, false);
+  moe::GemmProblem g2 = down_problem(nullptr, nullptr, T * k, F, H, E, nullptr, nullptr, 0);
   g2.out_f32 = true;
   if (Fs > 0) {
     g2.seg[1] = moe::GemmSegment{nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, T, 1, Fs, H};
@@ -111,17 +112,33 @@ ForwardLayout forward_layout(int T, int H, int F, int E, int k, int Fs, int cus)
   return L;
 }
 
-// Elements between consecutive experts' weight matrices [K][N].
-int64_t weight_stride(int K, int N, bool packed) {
-  return packed ? moe::packed_weight_elems(1, K, N) : static_cast<int64_t>(K) * N;
+// Weight layouts: 0 [K][N] bf16, 1 packed bf16 blocks, 2 packed fp8 codes
+// (+ per-column scales).
+constexpr int kRowMajor = 0, kPackedBf16 = 1, kFp8 = 2;
+
+// Elements (bf16-sized) between consecutive experts' weight matrices.
+int64_t weight_stride(int K, int N, int layout) {
+  return layout == kFp8        ? moe::fp8_weight_bytes(1, K, N) / 2
+         : layout == kPackedBf16 ? moe::packed_weight_elems(1, K, N)
+                                 : static_cast<int64_t>(K) * N;
+}
+
+moe::GemmSegment segment(const bf16_t* act, const int32_t* offsets, const bf16_t* w0,
+                         const bf16_t* w1, void* out, int rows, int ngroups, int K, int N,
+                         int layout, const float* s0, const float* s1) {
+  moe::GemmSegment g{act, offsets, w0, w1, out, weight_stride(K, N, layout), 0, rows, ngroups,
+                     K, N, layout};
+  g.scale0 = s0;
+  g.scale1 = s1;
+  return g;
 }
 
 moe::GemmProblem gateup_problem(const bf16_t* x_perm, const int32_t* offsets, int M,
                                 int H, int F, int E, const bf16_t* wg,
-                                const bf16_t* wu, bf16_t* h, bool packed) {
+                                const bf16_t* wu, bf16_t* h, int layout,
+                                const float* sg = nullptr, const float* su = nullptr) {
   moe::GemmProblem p{};
-  p.seg[0] = moe::GemmSegment{x_perm, offsets, wg, wu, h,
-                              weight_stride(H, F, packed), 0, M, E, H, F, packed};
+  p.seg[0] = segment(x_perm, offsets, wg, wu, h, M, E, H, F, layout, sg, su);
   p.nseg = 1;
   p.gated = true;
   p.rows_hint = M / E;
@@ -129,10 +146,10 @@ moe::GemmProblem gateup_problem(const bf16_t* x_perm, const int32_t* offsets, in
 }
 
 moe::GemmProblem down_problem(const bf16_t* h, const int32_t* offsets, int M, int F,
-                              int H, int E, const bf16_t* wd, void* y, bool packed) {
+                              int H, int E, const bf16_t* wd, void* y, int layout,
+                              const float* sd) {
   moe::GemmProblem p{};
-  p.seg[0] = moe::GemmSegment{h, offsets, wd, nullptr, y,
-                              weight_stride(F, H, packed), 0, M, E, F, H, packed};
+  p.seg[0] = segment(h, offsets, wd, nullptr, y, M, E, F, H, layout, sd, nullptr);
   p.nseg = 1;
   p.gated = false;
   p.rows_hint = M / E;
@@ -242,45 +259,82 @@ int moe_permute(const moe_bf16* x, const int32_t* topk_ids, int T, int H, int E,
 
 static int gateup_impl(const moe_bf16* x_perm, const int32_t* expert_offsets, int M, int H,
                        int F, int E, const moe_bf16* w_gate, const moe_bf16* w_up, moe_bf16* h,
-                       void* stream, bool packed) {
+                       void* stream, int layout, const float* sg = nullptr,
+                       const float* su = nullptr) {
   MOE_TRY(check_ffn_args(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, true, h));
   if (M == 0) return MOE_OK;
+  if (layout == kFp8) {
+    MOE_TRY(need_bf16(sg));
+    MOE_TRY(need_bf16(su));
+  }
   return hip_status(moe::launch_grouped_gemm(
-      gateup_problem(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, h, packed),
+      gateup_problem(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, h, layout, sg, su),
       static_cast<hipStream_t>(stream)));
 }
 
 static int down_impl(const moe_bf16* h, const int32_t* expert_offsets, int M, int F, int H,
                      int E, const moe_bf16* w_down, moe_bf16* y_perm, void* stream,
-                     bool packed) {
+                     int layout, const float* sd = nullptr) {
   MOE_TRY(check_ffn_args(h, expert_offsets, M, F, H, E, w_down, nullptr, false, y_perm));
   if (M == 0) return MOE_OK;
+  if (layout == kFp8) MOE_TRY(need_bf16(sd));
   return hip_status(moe::launch_grouped_gemm(
-      down_problem(h, expert_offsets, M, F, H, E, w_down, y_perm, packed),
+      down_problem(h, expert_offsets, M, F, H, E, w_down, y_perm, layout, sd),
       static_cast<hipStream_t>(stream)));
 }
 
 int moe_gateup_swiglu(const moe_bf16* x_perm, const int32_t* expert_offsets, int M,
                       int H, int F, int E, const moe_bf16* w_gate,
                       const moe_bf16* w_up, moe_bf16* h, void* stream) {
-  return gateup_impl(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, h, stream, false);
+  return gateup_impl(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, h, stream, kRowMajor);
 }
 
 int moe_gateup_swiglu_packed(const moe_bf16* x_perm, const int32_t* expert_offsets, int M,
                              int H, int F, int E, const moe_bf16* w_gate_packed,
                              const moe_bf16* w_up_packed, moe_bf16* h, void* stream) {
   return gateup_impl(x_perm, expert_offsets, M, H, F, E, w_gate_packed, w_up_packed, h,
-                     stream, true);
+                     stream, kPackedBf16);
 }
 
 int moe_down(const moe_bf16* h, const int32_t* expert_offsets, int M, int F, int H,
              int E, const moe_bf16* w_down, moe_bf16* y_perm, void* stream) {
-  return down_impl(h, expert_offsets, M, F, H, E, w_down, y_perm, stream, false);
+  return down_impl(h, expert_offsets, M, F, H, E, w_down, y_perm, stream, kRowMajor);
 }
 
 int moe_down_packed(const moe_bf16* h, const int32_t* expert_offsets, int M, int F, int H,
                     int E, const moe_bf16* w_down_packed, moe_bf16* y_perm, void* stream) {
-  return down_impl(h, expert_offsets, M, F, H, E, w_down_packed, y_perm, stream, true);
+  return down_impl(h, expert_offsets, M, F, H, E, w_down_packed, y_perm, stream, kPackedBf16);
+}
+
+size_t moe_fp8_weights_bytes(int G, int K, int N) {
+  if (G < 1 || check_width(K) != MOE_OK || check_width(N) != MOE_OK) return 0;
+  return static_cast<size_t>(moe::fp8_weight_bytes(G, K, N));
+}
+
+int moe_quantize_fp8(const moe_bf16* w, int G, int K, int N, uint8_t* codes,
+                     size_t codes_bytes, float* scales, void* stream) {
+  if (G < 1) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_width(K));
+  MOE_TRY(check_width(N));
+  MOE_TRY(need_bf16(w));
+  MOE_TRY(need_bf16(codes));
+  MOE_TRY(need_bf16(scales));
+  if (codes_bytes < moe_fp8_weights_bytes(G, K, N)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(moe::launch_quantize_fp8(w, G, K, N, codes, scales,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int moe_gateup_swiglu_fp8(const moe_bf16* x_perm, const int32_t* expert_offsets, int M, int H,
+                          int F, int E, const uint8_t* w_gate, const float* s_gate,
+                          const uint8_t* w_up, const float* s_up, moe_bf16* h, void* stream) {
+  return gateup_impl(x_perm, expert_offsets, M, H, F, E, reinterpret_cast<const bf16_t*>(w_gate),
+                     reinterpret_cast<const bf16_t*>(w_up), h, stream, kFp8, s_gate, s_up);
+}
+
+int moe_down_fp8(const moe_bf16* h, const int32_t* expert_offsets, int M, int F, int H, int E,
+                 const uint8_t* w_down, const float* s_down, moe_bf16* y_perm, void* stream) {
+  return down_impl(h, expert_offsets, M, F, H, E, reinterpret_cast<const bf16_t*>(w_down),
+                   y_perm, stream, kFp8, s_down);
 }
 
 size_t moe_pack_weights_bytes(int G, int K, int N) {
@@ -337,19 +391,45 @@ size_t moe_forward_workspace_bytes(int T, int H, int F, int E, int k, int Fs) {
   return forward_layout(T, H, F, E, k, Fs, moe::grouped_gemm_device_cus()).total;
 }
 
+// The layer's weights in one layout (the shared expert's too, when Fs > 0).
+struct LayerWeights {
+  int layout;
+  const bf16_t *wg, *wu, *wd;   // fp8: the codes
+  const float *sg, *su, *sd;    // fp8: column scales
+  bool shared;
+  int Fs;
+  const bf16_t *swg, *swu, *swd;
+  const float *ssg, *ssu, *ssd;
+  const float* gate_logits;
+};
+
+LayerWeights bf16_weights(const moe_bf16* wg, const moe_bf16* wu, const moe_bf16* wd,
+                          const moe_shared_expert* sh, int layout) {
+  LayerWeights W{};
+  W.layout = layout;
+  W.wg = wg, W.wu = wu, W.wd = wd;
+  W.shared = sh != nullptr;
+  if (sh) {
+    W.Fs = sh->Fs;
+    W.swg = sh->w_gate, W.swu = sh->w_up, W.swd = sh->w_down;
+    W.gate_logits = sh->gate_logits;
+  }
+  return W;
+}
+
 // The layer from router logits (logits != null: steps 1-5) or from a routing
 // the caller made (ids_in / w_in: steps 2-5).
 static int forward_impl(const moe_bf16* x, const float* logits, const int32_t* ids_in,
-                        const float* w_in, int T, int H, int F, int E,
-                        int k, const moe_bf16* w_gate, const moe_bf16* w_up,
-                        const moe_bf16* w_down, const moe_shared_expert* shared,
-                        moe_bf16* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
-                        size_t ws_bytes, void* stream, bool packed) {
+                        const float* w_in, int T, int H, int F, int E, int k,
+                        const LayerWeights& W, moe_bf16* out, int32_t* topk_ids_out,
+                        float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(check_dims(T, E, k));
   MOE_TRY(check_width(H));
   MOE_TRY(check_width(F));
-  const int Fs = shared ? shared->Fs : 0;
+  const bool shared = W.shared;
+  const int Fs = shared ? W.Fs : 0;
   if (shared) MOE_TRY(check_width(Fs));
+  const bool fp8 = W.layout == kFp8;
   const int64_t A = static_cast<int64_t>(T) * k;
   const int64_t widest = (H > F ? H : F) > Fs ? (H > F ? H : F) : Fs;
   MOE_TRY(check_elems(A, widest));
@@ -362,17 +442,27 @@ static int forward_impl(const moe_bf16* x, const float* logits, const int32_t* i
     MOE_TRY(need_word(ids_in));
     MOE_TRY(need_word(w_in));
   }
-  MOE_TRY(need_bf16(w_gate));
-  MOE_TRY(need_bf16(w_up));
-  MOE_TRY(need_bf16(w_down));
+  MOE_TRY(need_bf16(W.wg));
+  MOE_TRY(need_bf16(W.wu));
+  MOE_TRY(need_bf16(W.wd));
+  if (fp8) {
+    MOE_TRY(need_bf16(W.sg));
+    MOE_TRY(need_bf16(W.su));
+    MOE_TRY(need_bf16(W.sd));
+  }
   MOE_TRY(need_bf16(out));
   if (topk_ids_out) MOE_TRY(need_word(topk_ids_out));
   if (topk_w_out) MOE_TRY(need_word(topk_w_out));
   if (shared) {
-    MOE_TRY(need_bf16(shared->w_gate));
-    MOE_TRY(need_bf16(shared->w_up));
-    MOE_TRY(need_bf16(shared->w_down));
-    if (shared->gate_logits) MOE_TRY(need_word(shared->gate_logits));
+    MOE_TRY(need_bf16(W.swg));
+    MOE_TRY(need_bf16(W.swu));
+    MOE_TRY(need_bf16(W.swd));
+    if (fp8) {
+      MOE_TRY(need_bf16(W.ssg));
+      MOE_TRY(need_bf16(W.ssu));
+      MOE_TRY(need_bf16(W.ssd));
+    }
+    if (W.gate_logits) MOE_TRY(need_word(W.gate_logits));
   }
   MOE_TRY(need_bf16(ws));
   const ForwardLayout L = forward_layout(T, H, F, E, k, Fs, moe::grouped_gemm_device_cus());
@@ -397,7 +487,8 @@ static int forward_impl(const moe_bf16* x, const float* logits, const int32_t* i
 
   // 3's problem first: the large-batch tiles read the rows of x through
   // row_token themselves, and then the permutation copies no rows
-  moe::GemmProblem g1 = gateup_problem(x_perm, offsets, M, H, F, E, w_gate, w_up, h, packed);
+  moe::GemmProblem g1 =
+      gateup_problem(x_perm, offsets, M, H, F, E, W.wg, W.wu, h, W.layout, W.sg, W.su);
   const bool gather = moe::grouped_gemm_gathers(g1);
   if (gather) {
     g1.seg[0].act = x;
@@ -419,19 +510,20 @@ static int forward_impl(const moe_bf16* x, const float* logits, const int32_t* i
   }
   // 3. grouped gate/up + SwiGLU (shared expert as one more group over x)
   if (shared) {
-    g1.seg[1] = moe::GemmSegment{x, nullptr, shared->w_gate, shared->w_up, h_sh, 0, 0, T, 1, H, Fs,
-                                 packed};
+    g1.seg[1] = segment(x, nullptr, W.swg, W.swu, h_sh, T, 1, H, Fs, W.layout, W.ssg, W.ssu);
     g1.nseg = 2;
   }
   MOE_TRY(hip_status(moe::launch_grouped_gemm(g1, s)));
-  // 4. grouped down (shared expert likewise)
-  moe::GemmProblem g2 = down_problem(h, offsets, M, F, H, E, w_down, y, packed);
+  // 4. grouped down (shared expert likewise); the K-split plan is the same
+  // for every weight layout (the workspace size does not depend on it)
+  moe::GemmProblem g2 = down_problem(h, offsets, M, F, H, E, W.wd, y, W.layout, W.sd);
   g2.out_f32 = true;
   g2.seg[0].ksplit = L.ksplit;
   g2.seg[0].slice_stride = static_cast<int64_t>(M) * H;
   if (shared) {
-    g2.seg[1] = moe::GemmSegment{h_sh, nullptr, shared->w_down, nullptr, y_sh, 0,
-                                 static_cast<int64_t>(T) * H, T, 1, Fs, H, packed};
+    g2.seg[1] = segment(h_sh, nullptr, W.swd, nullptr, y_sh, T, 1, Fs, H, W.layout, W.ssd,
+                        nullptr);
+    g2.seg[1].slice_stride = static_cast<int64_t>(T) * H;
     g2.seg[1].ksplit = L.ksplit_sh;
     g2.nseg = 2;
   }
@@ -440,7 +532,7 @@ static int forward_impl(const moe_bf16* x, const float* logits, const int32_t* i
   return hip_status(moe::launch_combine(y, true, L.ksplit, static_cast<int64_t>(M) * H,
                                         row_dest, w_c, T, H, k, shared ? y_sh : nullptr,
                                         L.ksplit_sh, static_cast<int64_t>(T) * H,
-                                        shared ? shared->gate_logits : nullptr, out, s));
+                                        shared ? W.gate_logits : nullptr, out, s));
 }
 
 int moe_forward(const moe_bf16* x, const float* logits, int T, int H, int F, int E,
@@ -448,8 +540,9 @@ int moe_forward(const moe_bf16* x, const float* logits, int T, int H, int F, int
                 const moe_bf16* w_down, const moe_shared_expert* shared,
                 moe_bf16* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
                 size_t ws_bytes, void* stream) {
-  return forward_impl(x, logits, nullptr, nullptr, T, H, F, E, k, w_gate, w_up, w_down, shared,
-                      out, topk_ids_out, topk_w_out, ws, ws_bytes, stream, false);
+  return forward_impl(x, logits, nullptr, nullptr, T, H, F, E, k,
+                      bf16_weights(w_gate, w_up, w_down, shared, kRowMajor), out, topk_ids_out,
+                      topk_w_out, ws, ws_bytes, stream);
 }
 
 int moe_forward_packed(const moe_bf16* x, const float* logits, int T, int H, int F, int E,
@@ -457,9 +550,34 @@ int moe_forward_packed(const moe_bf16* x, const float* logits, int T, int H, int
                        const moe_bf16* w_down_packed, const moe_shared_expert* shared_packed,
                        moe_bf16* out, int32_t* topk_ids_out, float* topk_w_out, void* ws,
                        size_t ws_bytes, void* stream) {
-  return forward_impl(x, logits, nullptr, nullptr, T, H, F, E, k, w_gate_packed, w_up_packed,
-                      w_down_packed, shared_packed, out, topk_ids_out, topk_w_out, ws, ws_bytes,
-                      stream, true);
+  return forward_impl(x, logits, nullptr, nullptr, T, H, F, E, k,
+                      bf16_weights(w_gate_packed, w_up_packed, w_down_packed, shared_packed,
+                                   kPackedBf16),
+                      out, topk_ids_out, topk_w_out, ws, ws_bytes, stream);
+}
+
+int moe_forward_fp8(const moe_bf16* x, const float* logits, int T, int H, int F, int E, int k,
+                    const uint8_t* w_gate, const float* s_gate, const uint8_t* w_up,
+                    const float* s_up, const uint8_t* w_down, const float* s_down,
+                    const moe_shared_expert_fp8* shared, moe_bf16* out, int32_t* topk_ids_out,
+                    float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  LayerWeights W{};
+  W.layout = kFp8;
+  W.wg = reinterpret_cast<const bf16_t*>(w_gate);
+  W.wu = reinterpret_cast<const bf16_t*>(w_up);
+  W.wd = reinterpret_cast<const bf16_t*>(w_down);
+  W.sg = s_gate, W.su = s_up, W.sd = s_down;
+  W.shared = shared != nullptr;
+  if (shared) {
+    W.Fs = shared->Fs;
+    W.swg = reinterpret_cast<const bf16_t*>(shared->w_gate);
+    W.swu = reinterpret_cast<const bf16_t*>(shared->w_up);
+    W.swd = reinterpret_cast<const bf16_t*>(shared->w_down);
+    W.ssg = shared->s_gate, W.ssu = shared->s_up, W.ssd = shared->s_down;
+    W.gate_logits = shared->gate_logits;
+  }
+  return forward_impl(x, logits, nullptr, nullptr, T, H, F, E, k, W, out, topk_ids_out,
+                      topk_w_out, ws, ws_bytes, stream);
 }
 
 int moe_forward_routed(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
@@ -469,8 +587,10 @@ int moe_forward_routed(const moe_bf16* x, const int32_t* topk_ids, const float* 
                        void* stream) {
   if (weights_packed != 0 && weights_packed != 1) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!topk_ids || !topk_w)) return MOE_ERR_INVALID_ARG;
-  return forward_impl(x, nullptr, topk_ids, topk_w, T, H, F, E, k, w_gate, w_up, w_down, shared,
-                      out, nullptr, nullptr, ws, ws_bytes, stream, weights_packed == 1);
+  return forward_impl(x, nullptr, topk_ids, topk_w, T, H, F, E, k,
+                      bf16_weights(w_gate, w_up, w_down, shared,
+                                   weights_packed == 1 ? kPackedBf16 : kRowMajor),
+                      out, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

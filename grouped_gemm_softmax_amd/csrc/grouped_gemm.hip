@@ -111,6 +111,24 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, char* lds
                : "memory");
 }
 
+// Eight E4M3 codes (the bytes of u, in order) widened to bf16. gfx950's
+// v_cvt_pk_f32_fp8 decodes two OCP E4M3 codes (the low or the high pair of
+// a dword) to fp32 exactly; every E4M3 value is a bf16 value, so the upper
+// half of each fp32 is its exact bf16. (Compiler builtins, so that the
+// compiler keeps its hazard waits against MFMAs still reading registers.)
+__device__ __forceinline__ uint32_t hi16_pair(float a, float b) {
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 u) {
+  const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, false);
+  const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, true);
+  const auto f45 = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, false);
+  const auto f67 = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, true);
+  const uint4 v = uint4{hi16_pair(f01[0], f01[1]), hi16_pair(f23[0], f23[1]),
+                        hi16_pair(f45[0], f45[1]), hi16_pair(f67[0], f67[1])};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Lambdas of the kernel body are always inlined: their operands (the
 // accumulators, fragment sets and ring buffers) must stay in registers and
 // fixed LDS arrays.
@@ -127,7 +145,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <int BT_, int BF_, int BK_, int WT_, int WF_, int STAGES_, bool GATED_,
-          bool PREFETCH_, int MIN_WAVES_ = 1>
+          bool PREFETCH_, int MIN_WAVES_ = 1, int WB_ = 2>
 struct TileCfg {
   static constexpr int BT = BT_;  // activation rows (tokens) per tile
   static constexpr int BF = BF_;  // output columns per tile
@@ -142,6 +160,8 @@ struct TileCfg {
   // waves per SIMD the register allocation must leave room for (so that
   // this many fit by registers as well as by LDS)
   static constexpr int MIN_WAVES = MIN_WAVES_;
+  // bytes per weight element: 2 (bf16) or 1 (fp8 E4M3 codes, packed layout)
+  static constexpr int WB = WB_;
   static constexpr int NW = WT * WF;
   static constexpr int kThreads = NW * kWave;
   static constexpr int NMAT = GATED ? 2 : 1;
@@ -149,9 +169,9 @@ struct TileCfg {
   static constexpr int TT = BT / WT;  // tokens per wave
   static constexpr int FF = TF / 16;  // MFMA blocks per wave (columns)
   static constexpr int FT = TT / 16;  // MFMA blocks per wave (tokens)
-  static constexpr int W_BYTES = BK * BF * 2;  // one weight matrix per stage
-  static constexpr int SB = BF / 64;           // 64-column sub-blocks per matrix
-  static constexpr int SB_BYTES = BK * 128;    // one sub-block: BK rows of 128 bytes
+  static constexpr int W_BYTES = BK * BF * WB;  // one weight matrix per stage
+  static constexpr int SB = BF / 64;            // 64-column sub-blocks per matrix
+  static constexpr int SB_BYTES = BK * 64 * WB; // one sub-block: BK rows of 64 columns
   static constexpr int X_BYTES = BT * BK * 2;
   static constexpr int STAGE_BYTES = NMAT * W_BYTES + X_BYTES;
   static constexpr int INSTR = STAGE_BYTES / 1024;  // 1 KB DMA instructions
@@ -160,9 +180,10 @@ struct TileCfg {
   static_assert(BF % (16 * WF) == 0 && BT % (16 * WT) == 0, "wave tiling");
   static_assert((BK == 32 || BK % 64 == 0) && BF % 64 == 0, "swizzle geometry");
   static_assert(W_BYTES % 1024 == 0 && X_BYTES % 1024 == 0, "1 KB DMA granules");
-  static_assert(INSTR % NW == 0 && (W_BYTES / 1024) % NW == 0,
+  static_assert(INSTR % NW == 0 && W_INSTR % NW == 0,
                 "equal DMA share per wave, one operand kind per instruction slot");
   static_assert(STAGES >= 3 && STAGES <= 8, "ring depth");
+  static_assert(WB == 2 || WB == 1, "bf16 or fp8 weights");
   // vmcnt holds at most 63 outstanding operations per wave: the K-steps in
   // flight must fit, and for chaining across items also the epilogue's
   // stores issued while the next item's first K-steps are in flight
@@ -306,7 +327,9 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
   }
 
   constexpr int W_PER_MAT = C::W_BYTES / 1024;   // DMA instructions per weight matrix
-  constexpr int IPS = C::BK / 8;                 // instructions per weight sub-block
+  constexpr int IPS = C::SB_BYTES / 1024;        // instructions per weight sub-block
+  constexpr bool FP8 = C::WB == 1;
+  static_assert(!FP8 || PACKED, "fp8 weights exist only in the packed layout");
   constexpr int RPI_X = 1024 / (C::BK * 2);      // activation rows per instruction
 
   // ---- one work item: where its operands are, its K range, its output ----
@@ -323,6 +346,8 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     int nk;           // K-steps of the slice
     int nk_all;       // K-steps of the whole K
     int nblk, kblk;   // packed: 64-column and 64-row blocks of one group
+    const float* sc0; // fp8: the group's column scales (gate / plain matrix)
+    const float* sc1; // fp8: the group's column scales (up matrix)
     // per-lane byte offsets of this wave's DMA sources within a K-step,
     // relative to the step's scalar base
     uint32_t voff[C::IPW];
@@ -366,11 +391,17 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     // gathered rows: row p of the group's block is activation row S.gather[p]
     it.x = S.gather ? S.act : S.act + static_cast<int64_t>(it.row_base) * it.K;
     it.out = static_cast<OutT*>(S.out) + static_cast<int64_t>(ks) * S.slice_stride;
+    it.sc0 = FP8 ? S.scale0 + static_cast<int64_t>(v.local) * S.N : nullptr;
+    it.sc1 = FP8 && C::GATED ? S.scale1 + static_cast<int64_t>(v.local) * S.N : it.sc0;
     // every field is wave-uniform: keep them in scalar registers
     it.w0 = uniform(it.w0);
     it.w1 = uniform(it.w1);
     it.x = uniform(it.x);
     it.out = uniform(it.out);
+    if constexpr (FP8) {
+      it.sc0 = uniform(it.sc0);
+      it.sc1 = uniform(it.sc1);
+    }
     it.K = __builtin_amdgcn_readfirstlane(it.K);
     it.N = __builtin_amdgcn_readfirstlane(it.N);
     it.n0 = __builtin_amdgcn_readfirstlane(it.n0);
@@ -386,7 +417,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
       for (int i = 0; i < C::IPW; ++i) {
         const int j = i * C::NW + wave;
         if (i < C::W_INSTR / C::NW) {
-          const int mat = i / (W_PER_MAT / C::NW);
+          const int mat = j / W_PER_MAT;
           const int jj = j - mat * W_PER_MAT;  // instruction within the matrix
           const int r = (jj % IPS) * 8 + lane / 8;
           const int col = min(it.n0 + (jj / IPS) * 64 + swz_w(r, lane % 8) * 8, it.N - 8);
@@ -430,7 +461,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
       const bf16_t* base;
       uint32_t voff = it.voff[i];
       if (i < C::W_INSTR / C::NW) {
-        const int mat = i / (W_PER_MAT / C::NW);
+        const int mat = j / W_PER_MAT;  // wave-uniform
         const int jj = j - mat * W_PER_MAT;  // instruction within the matrix
         const bf16_t* const w = mat ? it.w1 : it.w0;
         if constexpr (PACKED) {
@@ -438,8 +469,16 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
           // copies 8 consecutive rows (1 KB) of one block. Sub-blocks past N
           // re-load the last block (their outputs are masked).
           const int nb = min(it.n0 / 64 + jj / IPS, it.nblk - 1);
-          const int krow = static_cast<int>(k0) + (jj % IPS) * 8;
-          base = w + (static_cast<int64_t>(nb) * it.kblk + krow / 64) * 4096 + (krow % 64) * 64;
+          if constexpr (FP8) {
+            // 4 KB blocks of codes: [32-row half][64 columns][32 bytes]; a
+            // 32-deep step reads one half, a 64-deep step both (element
+            // offsets below are in bf16 units, 2 codes each)
+            const int64_t blk = static_cast<int64_t>(nb) * it.kblk + k0 / 64;
+            base = w + blk * 2048 + ((k0 % 64) / 32) * 1024 + (jj % IPS) * 512;
+          } else {
+            const int krow = static_cast<int>(k0) + (jj % IPS) * 8;
+            base = w + (static_cast<int64_t>(nb) * it.kblk + krow / 64) * 4096 + (krow % 64) * 64;
+          }
         } else {
           base = w + k0 * it.N;
           if constexpr (KTAIL) {
@@ -467,6 +506,18 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     bf16x8 b[C::BK / 32][C::FT];
   };
   auto weight_frag = [&](const char* buf, int s, int m, int fi) INL {
+    if constexpr (FP8) {
+      // the lane's column and its 8 consecutive K codes (one 8-byte chunk
+      // of the column's 32 bytes in this 32-row half; chunk q sits at
+      // q ^ ((c >> 2) & 3), so 16 lanes of one q cover all banks), widened
+      // exactly to bf16 (the column's scale is applied in the epilogue)
+      const int col = wf * C::TF + fi * 16 + i16;
+      const int c = col & 63;
+      const char* p = buf + m * C::W_BYTES + (col >> 6) * C::SB_BYTES + s * 2048 + c * 32 +
+                      ((g16 ^ ((c >> 2) & 3)) << 3);
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      return fp8x8_to_bf16(u);
+    }
     const int row = s * 32 + 8 * g16 + (i16 >> 2);          // k within the stage
     const int col = wf * C::TF + fi * 16 + 4 * (i16 & 3);   // column within the tile
     const int c64 = col & 63;                                // column within the sub-block
@@ -656,7 +707,16 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     // ---- epilogue: lane holds columns 4*g16..+3 of one token per block ----
     // (bf16 stores round to nearest even; fp32 stores keep the accumulator)
 #pragma unroll
-    for (int fi = 0; fi < C::FF; ++fi)
+    for (int fi = 0; fi < C::FF; ++fi) {
+      // fp8: the columns' power-of-two scales (exact on the fp32 sums)
+      float4 s0 = float4{1.f, 1.f, 1.f, 1.f}, s1 = s0;
+      if constexpr (FP8) {
+        const int fc = min(cur.n0 + wf * C::TF + fi * 16 + 4 * g16, cur.N - 4);
+        s0 = *reinterpret_cast<const float4*>(cur.sc0 + fc);
+        if (C::GATED) s1 = *reinterpret_cast<const float4*>(cur.sc1 + fc);
+      }
+      const float sc0[4] = {s0.x, s0.y, s0.z, s0.w};
+      const float sc1[4] = {s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
       for (int ti = 0; ti < C::FT; ++ti) {
         const int tok = wt * C::TT + ti * 16 + i16;
@@ -666,16 +726,18 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             if (C::GATED) {
-              const float gt = acc[0][fi][ti][r];
-              const float up = acc[C::NMAT - 1][fi][ti][r];
+              const float gt = FP8 ? acc[0][fi][ti][r] * sc0[r] : acc[0][fi][ti][r];
+              const float up = FP8 ? acc[C::NMAT - 1][fi][ti][r] * sc1[r]
+                                   : acc[C::NMAT - 1][fi][ti][r];
               vals[r] = gt / (1.0f + __expf(-gt)) * up;
             } else {
-              vals[r] = acc[0][fi][ti][r];
+              vals[r] = FP8 ? acc[0][fi][ti][r] * sc0[r] : acc[0][fi][ti][r];
             }
           }
           store4(cur.out + static_cast<int64_t>(cur.row_base + tok) * cur.N + f, vals);
         }
       }
+    }
     primed = chain;
   }
   // no LDS DMA may land after the workgroup ends (its LDS may be reassigned)
@@ -711,6 +773,21 @@ using GateUpSmall = TileCfg<16, 64, 64, 1, 2, 4, true, true>;
 using GateUpMid = TileCfg<32, 64, 64, 1, 2, 3, true, true>;
 using DownLarge = TileCfg<256, 256, 32, 4, 2, 4, false, false>;
 using DownSmall = TileCfg<32, 64, 64, 1, 4, 4, false, true>;
+// FP8 weights: the same tile shapes with half the weight bytes per stage,
+// hence deeper rings in about the same LDS. The 128-row tiles take 32-deep
+// stages (64-deep ones would spill the widened fragments).
+using GateUpLarge8 = TileCfg<256, 128, 32, 4, 2, 5, true, false, 1, 1>;
+using GateUpLarge128_8 = TileCfg<128, 128, 32, 4, 2, 8, true, true, 2, 1>;
+using DownLarge128_8 = TileCfg<128, 256, 32, 4, 2, 8, false, true, 2, 1>;
+using GateUpSmall8 = TileCfg<16, 64, 64, 1, 2, 4, true, true, 1, 1>;
+using GateUpMid8 = TileCfg<32, 64, 64, 1, 2, 4, true, true, 1, 1>;
+using DownLarge8 = TileCfg<256, 256, 32, 4, 2, 5, false, false, 1, 1>;
+using DownSmall8 = TileCfg<32, 64, 64, 1, 4, 4, false, true, 1, 1>;
+static_assert(DownLarge8::BT == DownLarge::BT && DownLarge8::BF == DownLarge::BF &&
+                  DownLarge128_8::BT == DownLarge128::BT &&
+                  DownLarge128_8::BF == DownLarge128::BF && DownSmall8::BT == DownSmall::BT &&
+                  DownSmall8::BF == DownSmall::BF,
+              "fp8 tiles share the bf16 tiles' shapes (the split-K plan and tile classes)");
 
 int device_cu_count() {
   static int cus[64] = {0};
@@ -777,14 +854,21 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   if (bound <= 0) return hipSuccess;
   bool ktail = false;
   for (int s = 0; s < p.nseg; ++s) ktail = ktail || (p.seg[s].K % C::BK != 0);
-  const bool packed = p.seg[0].packed != 0;
+  const int layout = p.seg[0].packed;
   for (int s = 1; s < p.nseg; ++s)
-    if ((p.seg[s].packed != 0) != packed) return hipErrorInvalidValue;  // one layout per launch
-  if (packed)
+    if (p.seg[s].packed != layout) return hipErrorInvalidValue;  // one layout per launch
+  if constexpr (C::WB == 1) {
+    if (layout != 2) return hipErrorInvalidValue;
     return ktail ? launch_tail<C, OutT, true, true>(p, bound, stream)
                  : launch_tail<C, OutT, false, true>(p, bound, stream);
-  return ktail ? launch_tail<C, OutT, true, false>(p, bound, stream)
-               : launch_tail<C, OutT, false, false>(p, bound, stream);
+  } else {
+    if (layout == 2) return hipErrorInvalidValue;
+    if (layout == 1)
+      return ktail ? launch_tail<C, OutT, true, true>(p, bound, stream)
+                   : launch_tail<C, OutT, false, true>(p, bound, stream);
+    return ktail ? launch_tail<C, OutT, true, false>(p, bound, stream)
+                 : launch_tail<C, OutT, false, false>(p, bound, stream);
+  }
 }
 
 }  // namespace
@@ -891,7 +975,110 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(
   reinterpret_cast<uint4*>(out)[idx] = v;
 }
 
+// FP8 quantization, step 1: per (g, n) the column's largest |w| over K and
+// its scale 2^e, e the smallest integer with that max <= 448 * 2^e (1 for a
+// zero column). With max = f * 2^E (frexp, f in [0.5, 1)) and 448 =
+// 0.875 * 2^9: e = E - 9 when f <= 0.875, else E - 8 (exact; bf16
+// magnitudes order like their bit patterns).
+__global__ __launch_bounds__(256) void fp8_scales_kernel(const bf16_t* __restrict__ w, int G,
+                                                         int K, int N,
+                                                         float* __restrict__ scales) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<int64_t>(G) * N) return;
+  const int64_t g = idx / N;
+  const int n = static_cast<int>(idx % N);
+  const bf16_t* p = w + g * K * N + n;
+  uint32_t amax = 0;
+  for (int k = 0; k < K; ++k) {
+    const uint32_t m = p[static_cast<int64_t>(k) * N] & 0x7fffu;
+    amax = m > amax ? m : amax;
+  }
+  float sc = 1.f;
+  if (amax != 0) {
+    int E;
+    const float f = frexpf(__uint_as_float(amax << 16), &E);
+    sc = ldexpf(1.f, f <= 0.875f ? E - 9 : E - 8);
+  }
+  scales[idx] = sc;
+}
+
+// E4M3 code of v (|v| <= 448): round to nearest, ties to even, on the code
+// grid. Below 2^-6 the grid is m * 2^-9 (m = 8 is the least normal code);
+// above, 8 mantissa steps per power of two (a rounding up to the next power
+// carries into the exponent field). The sign is v's (also for zeros).
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = static_cast<uint32_t>(rintf(a * 512.0f));
+  } else {
+    const int E = static_cast<int>((__float_as_uint(a) >> 23) & 0xffu) - 127;
+    code = static_cast<uint32_t>((E + 7) << 3) +
+           static_cast<uint32_t>(rintf((ldexpf(a, -E) - 1.0f) * 8.0f));
+  }
+  return sign | code;
+}
+
+// FP8 quantization, step 2: one thread per 8-byte chunk of the block layout
+// (physical chunk p of column c in half h of block (g, nb, kb)); the chunk
+// holds rows 8q..8q+7, q = p ^ ((c >> 2) & 3), of that column, each weight
+// divided by its column's scale (exact: a power of two) and encoded.
+__global__ __launch_bounds__(256) void fp8_encode_kernel(
+    const bf16_t* __restrict__ w, int K, int N, int nblk, int kblk, int64_t chunks,
+    const float* __restrict__ scales, uint8_t* __restrict__ out) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= chunks) return;
+  const int p = static_cast<int>(idx & 3);
+  const int c = static_cast<int>((idx >> 2) & 63);
+  const int h = static_cast<int>((idx >> 8) & 1);
+  int64_t blk = idx >> 9;
+  const int kb = static_cast<int>(blk % kblk);
+  blk /= kblk;
+  const int nb = static_cast<int>(blk % nblk);
+  const int64_t g = blk / nblk;
+  const int q = p ^ ((c >> 2) & 3);
+  const int n = nb * 64 + c;
+  const int k0 = kb * 64 + h * 32 + q * 8;
+  uint32_t lo = 0, hi = 0;
+  if (n < N) {
+    int e;
+    frexpf(scales[g * N + n], &e);  // scale = 2^(e-1)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = k0 + j;
+      uint32_t code = 0;
+      if (k < K) {
+        const float x = __uint_as_float(static_cast<uint32_t>(w[(g * K + k) * N + n]) << 16);
+        code = e4m3_encode(ldexpf(x, 1 - e));
+      }
+      if (j < 4) lo |= code << (8 * j);
+      else hi |= code << (8 * (j - 4));
+    }
+  }
+  reinterpret_cast<uint2*>(out)[idx] = uint2{lo, hi};
+}
+
 }  // namespace
+
+int64_t fp8_weight_bytes(int G, int K, int N) {
+  return static_cast<int64_t>(G) * ((N + 63) / 64) * ((K + 63) / 64) * 4096;
+}
+
+hipError_t launch_quantize_fp8(const bf16_t* w, int G, int K, int N, uint8_t* codes,
+                               float* scales, hipStream_t stream) {
+  const int64_t cols = static_cast<int64_t>(G) * N;
+  if (cols == 0) return hipSuccess;
+  hipLaunchKernelGGL(fp8_scales_kernel, dim3(static_cast<unsigned>((cols + 255) / 256)),
+                     dim3(256), 0, stream, w, G, K, N, scales);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t chunks = fp8_weight_bytes(G, K, N) / 8;
+  hipLaunchKernelGGL(fp8_encode_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)),
+                     dim3(256), 0, stream, w, K, N, (N + 63) / 64, (K + 63) / 64, chunks, scales,
+                     codes);
+  return hipGetLastError();
+}
 
 int64_t packed_weight_elems(int G, int K, int N) {
   return static_cast<int64_t>(G) * ((N + 63) / 64) * ((K + 63) / 64) * 4096;
@@ -909,6 +1096,20 @@ hipError_t launch_pack_weights(const bf16_t* w, int G, int K, int N, bf16_t* pac
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
   const int tc = tile_class(p);
+  if (p.seg[0].packed == 2) {
+    if (p.gated)
+      return tc == kLarge      ? launch_cfg<GateUpLarge8, bf16_t>(p, stream)
+             : tc == kLarge128 ? launch_cfg<GateUpLarge128_8, bf16_t>(p, stream)
+             : tc == kMid      ? launch_cfg<GateUpMid8, bf16_t>(p, stream)
+                               : launch_cfg<GateUpSmall8, bf16_t>(p, stream);
+    if (p.out_f32)
+      return tc == kLarge      ? launch_cfg<DownLarge8, float>(p, stream)
+             : tc == kLarge128 ? launch_cfg<DownLarge128_8, float>(p, stream)
+                               : launch_cfg<DownSmall8, float>(p, stream);
+    return tc == kLarge      ? launch_cfg<DownLarge8, bf16_t>(p, stream)
+           : tc == kLarge128 ? launch_cfg<DownLarge128_8, bf16_t>(p, stream)
+                             : launch_cfg<DownSmall8, bf16_t>(p, stream);
+  }
   if (p.gated)
     return tc == kLarge      ? launch_cfg<GateUpLarge, bf16_t>(p, stream)
            : tc == kLarge128 ? launch_cfg<GateUpLarge128, bf16_t>(p, stream)

@@ -55,7 +55,11 @@ struct GemmSegment {
   int ngroups;
   int K;
   int N;
-  int packed = 0;          // weights in the packed block layout
+  int packed = 0;          // weight layout: 0 [K][N] bf16, 1 packed bf16, 2 packed fp8
+  // fp8 (packed == 2): E4M3 codes in 4 KB blocks (fp8_weight_bytes), each
+  // group's output columns scaled by scale0/scale1 + g*N (fp32 powers of two)
+  const float* scale0 = nullptr;
+  const float* scale1 = nullptr;
   // Optional row map: activation row of row p is gather[p] (`act` is then
   // the un-permuted [*, K] tensor). Only for the tile classes without item
   // chaining (see grouped_gemm_gathers).
@@ -87,6 +91,15 @@ int grouped_gemm_device_cus();
 // in the GEMM's LDS order (128-byte rows, swizzled 16-byte chunks), zero
 // past K and N. A K-step of a decode-size tile is then one contiguous read.
 int64_t packed_weight_elems(int G, int K, int N);
+
+// FP8 weights: W [G][K][N] as E4M3 codes with one power-of-two scale per
+// (g, n) (the smallest with max_k |W| <= 448 * scale), codes in
+// G x ceil(N/64) x ceil(K/64) blocks of 4 KB: [32-row half][64 columns][32
+// bytes], the 8-byte chunk of rows 8q..8q+7 of column c at chunk position
+// q ^ ((c >> 2) & 3); zero past K and N.
+int64_t fp8_weight_bytes(int G, int K, int N);
+hipError_t launch_quantize_fp8(const bf16_t* w, int G, int K, int N, uint8_t* codes,
+                               float* scales, hipStream_t stream);
 hipError_t launch_pack_weights(const bf16_t* w, int G, int K, int N, bf16_t* packed,
                                hipStream_t stream);
 

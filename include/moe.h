@@ -268,6 +268,62 @@ int moe_forward_packed(const moe_bf16* x, const float* logits, int T, int H,
                        int32_t* topk_ids_out, float* topk_w_out, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* ---- FP8 weights ----
+ * The DeepGEMM article (itsolotime.com), sections 1.1 and 5.3, runs the
+ * expert GEMMs on 8-bit (and 4-bit) floating-point operands. Here the
+ * weights are 8-bit: each matrix W [G,K,N] is stored as OCP E4M3 codes
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no
+ * infinities, largest value 448) with one fp32 scale per (g, n), the
+ * smallest power of two s with max_k |W[g,k,n]| <= 448 * s; a weight is
+ * code_value * s. The activations stay bf16: every dequantized weight is a
+ * bf16 value, so a layer on fp8 weights is exactly the bf16 layer on the
+ * dequantized weights (same accumulation in fp32), at half the weight
+ * bytes. Codes are rounded to nearest, ties to even. Supported scales are
+ * normal fp32 values (columns whose largest |W| is at least 2^-117).
+ *
+ * Layout of the codes: G x ceil(N/64) x ceil(K/64) blocks of 4096 bytes,
+ * block (g, nb, kb) at byte ((g*NB + nb)*KB + kb)*4096; within a block,
+ * byte h*2048 + c*32 + p*8 + j holds the code of W[g, kb*64 + h*32 +
+ * 8*(p ^ ((c >> 2) & 3)) + j, nb*64 + c] (zero past K or N). Scales:
+ * fp32 [G,N]. Both 16-byte aligned; the shared expert's matrices are
+ * quantized as G = 1. */
+
+/* Bytes of the codes of a [G,K,N] weight tensor; 0 for invalid sizes. */
+size_t moe_fp8_weights_bytes(int G, int K, int N);
+
+/* Quantize bf16 W [G,K,N] (K, N multiples of 8) into codes (at least
+ * moe_fp8_weights_bytes bytes) and scales fp32 [G,N]. Once, at load time. */
+int moe_quantize_fp8(const moe_bf16* w, int G, int K, int N, uint8_t* codes,
+                     size_t codes_bytes, float* scales, void* stream);
+
+/* moe_gateup_swiglu / moe_down on fp8 weights: equal, bit for bit, to the
+ * bf16 calls on the dequantized weights. */
+int moe_gateup_swiglu_fp8(const moe_bf16* x_perm, const int32_t* expert_offsets, int M, int H,
+                          int F, int E, const uint8_t* w_gate, const float* s_gate,
+                          const uint8_t* w_up, const float* s_up, moe_bf16* h, void* stream);
+int moe_down_fp8(const moe_bf16* h, const int32_t* expert_offsets, int M, int F, int H, int E,
+                 const uint8_t* w_down, const float* s_down, moe_bf16* y_perm, void* stream);
+
+/* Shared expert with fp8 weights (HOST struct, device pointers): w_gate,
+ * w_up quantized from [1,H,Fs], w_down from [1,Fs,H], with their scales. */
+typedef struct {
+  const uint8_t* w_gate;
+  const float* s_gate;
+  const uint8_t* w_up;
+  const float* s_up;
+  const uint8_t* w_down;
+  const float* s_down;
+  int32_t Fs;
+  const float* gate_logits;
+} moe_shared_expert_fp8;
+
+/* moe_forward on fp8 weights (same workspace and outputs). */
+int moe_forward_fp8(const moe_bf16* x, const float* logits, int T, int H, int F, int E, int k,
+                    const uint8_t* w_gate, const float* s_gate, const uint8_t* w_up,
+                    const float* s_up, const uint8_t* w_down, const float* s_down,
+                    const moe_shared_expert_fp8* shared, moe_bf16* out, int32_t* topk_ids_out,
+                    float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

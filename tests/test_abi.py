@@ -162,6 +162,41 @@ def test_forward_validation(L):
                          NULL, NULL, NULL, 0, NULL) == OK
 
 
+def test_fp8_weights_bytes():
+    assert B.moe_fp8_weights_bytes(2, 200, 328) == 2 * 6 * 4 * 4096   # ceil(N/64) x ceil(K/64)
+    assert B.moe_fp8_weights_bytes(1, 64, 64) == 4096
+    assert B.moe_fp8_weights_bytes(0, 64, 64) == 0
+    assert B.moe_fp8_weights_bytes(1, 60, 64) == 0                   # K % 8 != 0
+
+
+def test_fp8_calls_validation(L):
+    nb = B.moe_fp8_weights_bytes(2, 64, 96)
+    q = lambda w=P, G=2, K=64, N=96, c=P, nbytes=nb, s=P: L.moe_quantize_fp8(w, G, K, N, c, nbytes, s, NULL)
+    assert q(w=NULL) == INVALID
+    assert q(s=NULL) == INVALID
+    assert q(G=0) == INVALID
+    assert q(K=60) == SHAPE
+    assert q(c=Q) == MISALIGNED
+    assert q(s=Q) == MISALIGNED
+    assert q(nbytes=nb - 1) == WS_SMALL
+    g = lambda sg=P, su=P, wg=P: L.moe_gateup_swiglu_fp8(P, P, 16, 64, 96, 2, wg, sg, P, su, P, NULL)
+    assert g(sg=NULL) == INVALID
+    assert g(su=Q) == MISALIGNED
+    assert g(wg=Q) == MISALIGNED
+    assert L.moe_down_fp8(P, P, 16, 96, 64, 2, P, NULL, P, NULL) == INVALID
+    assert L.moe_down_fp8(P, P, 0, 96, 64, 2, NULL, NULL, NULL, NULL) == OK     # M = 0
+    ws = B.moe_forward_workspace_bytes(10, 64, 96, 8, 2, 0)
+    f = lambda sd=P, ws_bytes=ws: L.moe_forward_fp8(P, P, 10, 64, 96, 8, 2, P, P, P, P, P, sd,
+                                                     None, P, NULL, NULL, P, ws_bytes, NULL)
+    assert f(sd=NULL) == INVALID
+    assert f(ws_bytes=ws - 1) == WS_SMALL
+    bad = B.SharedExpertFp8(0x10000, 0x10000, 0x10000, 0x10000, 0x10000, None, 32, None)
+    assert L.moe_forward_fp8(P, P, 10, 64, 96, 8, 2, P, P, P, P, P, P, ctypes.byref(bad), P,
+                             NULL, NULL, P, 1 << 40, NULL) == INVALID          # null shared scale
+    assert L.moe_forward_fp8(NULL, NULL, 0, 64, 96, 8, 2, NULL, NULL, NULL, NULL, NULL, NULL,
+                             None, NULL, NULL, NULL, NULL, 0, NULL) == OK      # T = 0
+
+
 def test_forward_routed_validation(L):
     ws = B.moe_forward_workspace_bytes(10, 64, 96, 8, 2, 0)
     args = lambda x=P, ids=P, w=P, k=2, packed=0, ws_bytes=ws: (
