@@ -43,11 +43,13 @@
 // stage is an explicit vmcnt followed by a bare s_barrier (a __syncthreads
 // fence would drain every outstanding load). Each wave-wide DMA instruction
 // fills 1 KB of LDS in lane order, so tiles are stored in their global
-// layouts (weights [BK][BF] N-contiguous, activations [BT][BK] K-contiguous)
-// with an XOR swizzle of 16-byte chunks chosen on the global side. The
-// weight operand needs K-consecutive values per lane, which the N-contiguous
-// layout does not give; the transposing LDS read ds_read_b64_tr_b16 delivers
-// them. MFMA: v_mfma_f32_16x16x32_bf16, fp32 accumulation.
+// layouts (activations [BT][BK] K-contiguous) with an XOR swizzle of 16-byte
+// chunks chosen on the global side. The weight operand needs K-consecutive
+// values per lane. Row-major weights ([BK][BF], N-contiguous) do not give
+// them, and the transposing LDS read ds_read_b64_tr_b16 delivers them;
+// packed weights (pack_weights_kernel) already hold each column's
+// K-values contiguously, so a lane reads its fragment with one 16-byte LDS
+// read. MFMA: v_mfma_f32_16x16x32_bf16, fp32 accumulation.
 #include <stdlib.h>
 #include <string.h>
 
@@ -145,7 +147,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <int BT_, int BF_, int BK_, int WT_, int WF_, int STAGES_, bool GATED_,
-          bool PREFETCH_, int MIN_WAVES_ = 1, int WB_ = 2>
+          bool PREFETCH_, int MIN_WAVES_ = 1, int WB_ = 2, bool PP_ = false>
 struct TileCfg {
   static constexpr int BT = BT_;  // activation rows (tokens) per tile
   static constexpr int BF = BF_;  // output columns per tile
@@ -162,6 +164,10 @@ struct TileCfg {
   static constexpr int MIN_WAVES = MIN_WAVES_;
   // bytes per weight element: 2 (bf16) or 1 (fp8 E4M3 codes, packed layout)
   static constexpr int WB = WB_;
+  // Ping-pong schedule: the two waves of each SIMD alternate between an
+  // MFMA phase and a memory phase (LDS fragment reads, DMA issue), so one of
+  // them always feeds the matrix core (8 waves, no fragment prefetch).
+  static constexpr bool PP = PP_;
   static constexpr int NW = WT * WF;
   static constexpr int kThreads = NW * kWave;
   static constexpr int NMAT = GATED ? 2 : 1;
@@ -190,6 +196,7 @@ struct TileCfg {
   static constexpr int STORES = (BF / WF / 16) * (BT / WT / 16);
   static_assert((PREFETCH ? STAGES : STAGES - 1) * IPW <= 63, "vector-memory counter range");
   static constexpr bool CHAIN_OK = PREFETCH && STAGES * IPW + STORES <= 63;
+  static_assert(!PP || (NW == 8 && !PREFETCH), "ping-pong: two waves per SIMD");
 };
 
 // 16-byte chunk swizzles (chunk index within a row), chosen by measuring
@@ -476,8 +483,10 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
             const int64_t blk = static_cast<int64_t>(nb) * it.kblk + k0 / 64;
             base = w + blk * 2048 + ((k0 % 64) / 32) * 1024 + (jj % IPS) * 512;
           } else {
-            const int krow = static_cast<int>(k0) + (jj % IPS) * 8;
-            base = w + (static_cast<int64_t>(nb) * it.kblk + krow / 64) * 4096 + (krow % 64) * 64;
+            // 8 KB blocks: [32-row half][64 columns][32 K-values]; a 32-deep
+            // step reads one half, a 64-deep step the whole block
+            const int64_t blk = static_cast<int64_t>(nb) * it.kblk + k0 / 64;
+            base = w + blk * 4096 + ((k0 % 64) / 32) * 2048 + (jj % IPS) * 512;
           }
         } else {
           base = w + k0 * it.N;
@@ -517,6 +526,15 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
                       ((g16 ^ ((c >> 2) & 3)) << 3);
       const uint2 u = *reinterpret_cast<const uint2*>(p);
       return fp8x8_to_bf16(u);
+    } else if constexpr (PACKED) {
+      // packed bf16: each column's 32 K-values of a half are one 64-byte row
+      // (16-byte chunk q at q ^ ((c >> 1) & 3)), so the lane's 8 consecutive
+      // K-values of its column are one 16-byte read
+      const int col = wf * C::TF + fi * 16 + i16;
+      const int c = col & 63;
+      const char* p = buf + m * C::W_BYTES + (col >> 6) * C::SB_BYTES + s * 4096 + c * 64 +
+                      ((g16 ^ ((c >> 1) & 3)) << 4);
+      return *reinterpret_cast<const bf16x8*>(p);
     }
     const int row = s * 32 + 8 * g16 + (i16 >> 2);          // k within the stage
     const int col = wf * C::TF + fi * 16 + 4 * (i16 & 3);   // column within the tile
@@ -635,6 +653,61 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
 
   Frags fa, fb;
   bool primed = false;  // the current item's first D K-steps are in flight
+
+  // ---- ping-pong schedule (C::PP) ----
+  // Waves 0-3 (group 0) and 4-7 (group 1) hold one wave per SIMD each. Every
+  // K-step is a memory phase M (read the step's fragments from LDS, wait for
+  // the wave's own DMA of the next step, issue the DMA of step t+D, wait for
+  // the fragments; issuing the DMA first measured 3 % slower) and an MFMA
+  // phase C, each closed by a workgroup barrier.
+  // Group 1 passes one extra barrier first, so between any two barriers one
+  // group multiplies while the other moves data:
+  //   interval 2t:   group 0 M(t),  group 1 C(t-1)
+  //   interval 2t+1: group 0 C(t),  group 1 M(t)
+  // Step t+1 is read in intervals 2t+2 (group 0) and 2t+3 (group 1); both
+  // groups' DMAs of it have landed by the end of intervals 2t and 2t+1
+  // (each wave waits for its own in M(t)). Step t+D goes into the buffer of
+  // step t-1 (D = S-1), whose last reads were waited for by the end of
+  // interval 2t-1; group 0 issues it in interval 2t, group 1 in 2t+1. Group 0
+  // passes one extra barrier at the end, so both groups leave in step.
+  auto pp_barrier = [&]() INL {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // (Chaining items as the decode tiles do measured 1 % slower here: items
+  // are long, and the chained start must also wait for the epilogue's stores.)
+  auto run_pingpong = [&](const ItemInfo& cur) INL {
+    constexpr int DP = S - 1;
+    const bool grp1 = wave >= 4;
+    wait_vmcnt<0>();               // the last item's stores and DMAs are done and
+    __builtin_amdgcn_s_barrier();  // every wave has finished reading the ring
+    static_for<DP>([&](auto I) INL { issue(cur, cur.kt_begin + decltype(I)::value, stage_buf(I)); });
+    wait_vmcnt<(DP - 1) * C::IPW>();
+    pp_barrier();                  // K-step 0 has landed for every wave
+    if (grp1) pp_barrier();
+    auto pp_step = [&](int t, auto I) INL {
+      constexpr int i = decltype(I)::value;
+      load_frags(stage_buf(I), fa, cur.K - (cur.kt_begin + t) * C::BK);
+      wait_vmcnt<(DP - 2) * C::IPW>();  // this wave's DMA of step t+1 has landed
+      issue(cur, cur.kt_begin + t + DP, stage_buf(std::integral_constant<int, i + DP>{}));
+      wait_vmcnt_lgkm0<63>();           // fragments in registers
+      pp_barrier();
+      mfma(fa);
+      pp_barrier();
+    };
+    const int full = cur.nk / S;
+    int t = 0;
+    for (int turn = 0; turn < full; ++turn, t += S)
+      static_for<S>([&](auto I) INL { pp_step(t + decltype(I)::value, I); });
+    const int rem = cur.nk - t;
+    static_for<S - 1>([&](auto I) INL {
+      if (decltype(I)::value < rem) pp_step(t + decltype(I)::value, I);
+    });
+    if (!grp1) pp_barrier();
+  };
   for (int item = slot; item < total; item += stride) {
     const ItemInfo cur = make_item(item);
     const bool has_next = CHAIN && item + stride < total;
@@ -648,6 +721,9 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
 #pragma unroll
         for (int b = 0; b < C::FT; ++b) acc[m][a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+    if constexpr (C::PP) {
+      run_pingpong(cur);
+    } else {
     if (!primed) {
       wait_vmcnt<0>();               // every DMA into the ring has landed and
       __builtin_amdgcn_s_barrier();  // every wave is done with the last item
@@ -703,6 +779,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
         if (decltype(I)::value < rem) step(t + decltype(I)::value, I);
       });
     }
+    }  // ring schedule
 
     // ---- epilogue: lane holds columns 4*g16..+3 of one token per block ----
     // (bf16 stores round to nearest even; fp32 stores keep the accumulator)
@@ -748,7 +825,12 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
 // Large batch: 256 tokens x 128 columns (gated: 128 columns each of gate and
 // up; down: 256 columns), 8 waves (2 per SIMD) as 4 along tokens x 2 along
 // columns, 128 accumulators per lane, a 4-deep ring of 32-deep, 32 KB stages
-// (three stages of look-ahead).
+// (three stages of look-ahead), on the ping-pong schedule (the ring schedule
+// of the other tiles was 12-16 % slower at 8192 tokens of the Mixtral-shaped
+// layer). Its time is set by the direct-to-LDS stream: the same launch with
+// the MFMAs and fragment reads removed takes about 80 % of the full time,
+// with the DMA removed about 65 %, and the DMA time halves with half the
+// bytes.
 // Small batch (decode): gate/up 16 tokens x 64 columns on 2 waves with a
 // 4-deep ring of 18 KB stages (2 workgroups and ~108 KB of weights in flight
 // per CU); down 32 tokens x 64 columns on 4 waves, 4-deep ring of 12 KB
@@ -766,22 +848,22 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
 // are in flight (measured against 32-deep stages with two workgroups per CU:
 // the DeepSeek-V3-shaped layer at 4096 tokens 8.6 % faster, the
 // Mixtral-shaped one at 512 tokens 3 %).
-using GateUpLarge = TileCfg<256, 128, 32, 4, 2, 4, true, false>;
+using GateUpLarge = TileCfg<256, 128, 32, 4, 2, 4, true, false, 1, 2, true>;
 using GateUpLarge128 = TileCfg<128, 128, 64, 4, 2, 3, true, true, 2>;
 using DownLarge128 = TileCfg<128, 256, 64, 4, 2, 3, false, true, 2>;
 using GateUpSmall = TileCfg<16, 64, 64, 1, 2, 4, true, true>;
 using GateUpMid = TileCfg<32, 64, 64, 1, 2, 3, true, true>;
-using DownLarge = TileCfg<256, 256, 32, 4, 2, 4, false, false>;
+using DownLarge = TileCfg<256, 256, 32, 4, 2, 4, false, false, 1, 2, true>;
 using DownSmall = TileCfg<32, 64, 64, 1, 4, 4, false, true>;
 // FP8 weights: the same tile shapes with half the weight bytes per stage,
 // hence deeper rings in about the same LDS. The 128-row tiles take 32-deep
 // stages (64-deep ones would spill the widened fragments).
-using GateUpLarge8 = TileCfg<256, 128, 32, 4, 2, 5, true, false, 1, 1>;
+using GateUpLarge8 = TileCfg<256, 128, 32, 4, 2, 5, true, false, 1, 1, true>;
 using GateUpLarge128_8 = TileCfg<128, 128, 32, 4, 2, 8, true, true, 2, 1>;
 using DownLarge128_8 = TileCfg<128, 256, 32, 4, 2, 8, false, true, 2, 1>;
 using GateUpSmall8 = TileCfg<16, 64, 64, 1, 2, 4, true, true, 1, 1>;
 using GateUpMid8 = TileCfg<32, 64, 64, 1, 2, 4, true, true, 1, 1>;
-using DownLarge8 = TileCfg<256, 256, 32, 4, 2, 5, false, false, 1, 1>;
+using DownLarge8 = TileCfg<256, 256, 32, 4, 2, 5, false, false, 1, 1, true>;
 using DownSmall8 = TileCfg<32, 64, 64, 1, 4, 4, false, true, 1, 1>;
 static_assert(DownLarge8::BT == DownLarge::BT && DownLarge8::BF == DownLarge::BF &&
                   DownLarge128_8::BT == DownLarge128::BT &&
@@ -954,25 +1036,33 @@ int grouped_gemm_device_cus() { return device_cu_count(); }
 namespace {
 
 // Packed weights: one thread per 16-byte chunk of the packed tensor, in
-// order (block, row, physical chunk); the chunk holds the 8 columns that the
-// GEMM's LDS swizzle puts there, or zeros past K or N.
+// order (block, 32-row half, column, physical chunk p); the chunk holds the
+// column's 8 K-consecutive values 8q..8q+7 of the half, q = p ^ ((c >> 1) & 3)
+// (the GEMM's LDS swizzle), or zeros past K or N.
 __global__ __launch_bounds__(256) void pack_weights_kernel(
     const bf16_t* __restrict__ w, int K, int N, int nblk, int kblk, int64_t chunks,
     bf16_t* __restrict__ out) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= chunks) return;
-  const int pc = static_cast<int>(idx & 7);
-  const int r = static_cast<int>((idx >> 3) & 63);
+  const int pc = static_cast<int>(idx & 3);
+  const int c = static_cast<int>((idx >> 2) & 63);
+  const int h = static_cast<int>((idx >> 8) & 1);
   int64_t blk = idx >> 9;
   const int kb = static_cast<int>(blk % kblk);
   blk /= kblk;
   const int nb = static_cast<int>(blk % nblk);
   const int64_t g = blk / nblk;
-  const int k = kb * 64 + r;
-  const int n = nb * 64 + swz_w(r, pc) * 8;
-  uint4 v = uint4{0u, 0u, 0u, 0u};
-  if (k < K && n < N) v = *reinterpret_cast<const uint4*>(w + (g * K + k) * N + n);
-  reinterpret_cast<uint4*>(out)[idx] = v;
+  const int k0 = kb * 64 + h * 32 + (pc ^ ((c >> 1) & 3)) * 8;
+  const int n = nb * 64 + c;
+  uint32_t v[4] = {0u, 0u, 0u, 0u};
+  if (k0 < K && n < N) {  // K is a multiple of 8: all 8 rows are inside K
+    const bf16_t* src = w + (g * K + k0) * N + n;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = static_cast<uint32_t>(src[(2 * e) * static_cast<int64_t>(N)]) |
+             (static_cast<uint32_t>(src[(2 * e + 1) * static_cast<int64_t>(N)]) << 16);
+  }
+  reinterpret_cast<uint4*>(out)[idx] = uint4{v[0], v[1], v[2], v[3]};
 }
 
 // FP8 quantization, step 1: per (g, n) the column's largest |w| over K and

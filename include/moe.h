@@ -230,9 +230,11 @@ int moe_forward_routed(const moe_bf16* x, const int32_t* topk_ids, const float* 
  * shared expert) occupies moe_pack_weights_bytes(G,K,N) =
  * G * ceil(N/64) * ceil(K/64) * 8192 bytes: blocks of 64 K-rows by 64
  * columns, block (g, nb, kb) at byte ((g*ceil(N/64) + nb)*ceil(K/64) + kb)*8192,
- * each row of a block 128 bytes holding the block's 64 columns as eight
- * 8-column chunks in a swizzled order, zero past K and past N. The order is
- * private to this library: produce packed tensors with moe_pack_weights. */
+ * each block two 32-row halves of 64 column rows of 64 bytes, a column row
+ * holding that column's 32 K-values as four 8-value chunks in a swizzled
+ * order, zero past K and past N (a lane's MFMA fragment, 8 K-consecutive
+ * values of one column, is one 16-byte read). The order is private to this
+ * library: produce packed tensors with moe_pack_weights. */
 
 /* Packed size in bytes of a [G,K,N] weight tensor; 0 for invalid sizes
  * (G < 1, K or N not a positive multiple of 8). */

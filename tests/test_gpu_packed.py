@@ -1,6 +1,8 @@
 """GPU tests of the packed weight layout (moe_pack_weights and the *_packed
-calls). The packed tensor must hold every weight exactly once, in the row of
-its 64 x 64 block, in whole 8-column chunks, with zeros past K and N; every
+calls). The packed tensor must hold every weight exactly once, in its 64 x 64
+block, each block as two 32-row halves of 64 column rows, each column row the
+column's 32 K-values in whole chunks of 8 K-consecutive values, with zeros
+past K and N; every
 packed call must return bit for bit what the row-major call returns (the
 kernels stage identical data in LDS and sum the same products in the same
 order); and the packed layer must match the oracle like the row-major one."""
@@ -35,12 +37,12 @@ def test_pack_layout_block_rows(G, K, N):
     torch.cuda.synchronize()
     NB, KB = -(-N // 64), -(-K // 64)
     assert p.data.numel() == G * NB * KB * 8192
-    got = p.data.cpu().numpy().view(np.uint16).reshape(G, NB, KB, 64, 8, 8)
-    # expected block rows, columns in natural order, zero-padded
+    got = p.data.cpu().numpy().view(np.uint16).reshape(G, NB, KB, 2, 64, 4, 8)
+    # expected: per block, half h, column c, chunk q: W[kb*64 + 32h + 8q + e, nb*64 + c]
     exp = np.zeros((G, KB * 64, NB * 64), np.uint16)
     exp[:, :K, :N] = w_host
-    exp = exp.reshape(G, KB, 64, NB, 8, 8).transpose(0, 3, 1, 2, 4, 5)   # [G,NB,KB,64,8,8]
-    # each packed 8-column chunk is one whole chunk of its row: order the
+    exp = exp.reshape(G, KB, 2, 4, 8, NB, 64).transpose(0, 5, 1, 2, 6, 3, 4)  # [G,NB,KB,2,64,4,8]
+    # each packed chunk is one whole chunk of its column row: order the
     # chunks of both by their first element (zero chunks are equal anyway)
     key_g = np.argsort(got[..., 0], axis=-1, kind="stable")
     key_e = np.argsort(exp[..., 0], axis=-1, kind="stable")
