@@ -56,6 +56,13 @@ def lib():
         L.oracle_quantize_e4m3.argtypes = [_P, _I64, _I, _I, _P, _P]
         L.oracle_dequant_e4m3.argtypes = [_P, _P, _I64, _I, _I, _P]
         L.oracle_dequant_e4m3.restype = None
+        L.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e2m1_value.restype = ctypes.c_double
+        L.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e8m0_value.restype = ctypes.c_double
+        L.oracle_quantize_mxfp4.argtypes = [_P, _I64, _I, _I, _P, _P]
+        L.oracle_dequant_mxfp4.argtypes = [_P, _P, _I64, _I, _I, _P]
+        L.oracle_dequant_mxfp4.restype = None
         L.oracle_route.argtypes = [_P, _I64, _I, _I, _P, _P]
         L.oracle_permute.argtypes = [_P, _I64, _I, _I, _P, _P, _P]
         L.oracle_gather.argtypes = [_P, _P, _I64, _I, _P]
@@ -139,6 +146,42 @@ def dequant_e4m3(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     G, K, N = codes.shape
     out = np.empty((G, K, N), np.float64)
     lib().oracle_dequant_e4m3(_p(codes), _p(scales), G, K, N, _p(out))
+    return out[0] if squeeze else out
+
+
+def e2m1_values() -> np.ndarray:
+    """Values of the 16 E2M1 codes (float64)."""
+    return np.array([lib().oracle_e2m1_value(c) for c in range(16)], np.float64)
+
+
+def e8m0_value(s: int) -> float:
+    return lib().oracle_e8m0_value(s)
+
+
+def quantize_mxfp4(w: np.ndarray):
+    """bf16 weights [G,K,N] (or [K,N]: G = 1) -> (codes uint8 0..15 same
+    shape, scale bytes uint8 [G, ceil(K/32), N]; scale = 2^(byte - 127))."""
+    w = _c(w, np.uint16)
+    squeeze = w.ndim == 2
+    if squeeze:
+        w = w[None]
+    G, K, N = w.shape
+    codes = np.empty((G, K, N), np.uint8)
+    sb = np.empty((G, -(-K // 32), N), np.uint8)
+    _check(lib().oracle_quantize_mxfp4(_p(w), G, K, N, _p(codes), _p(sb)), "quantize_mxfp4")
+    return (codes[0], sb[0]) if squeeze else (codes, sb)
+
+
+def dequant_mxfp4(codes: np.ndarray, scale_bytes: np.ndarray) -> np.ndarray:
+    """value(code) * 2^(scale byte - 127) of its 32-row block -> float64."""
+    codes = _c(codes, np.uint8)
+    scale_bytes = _c(scale_bytes, np.uint8)
+    squeeze = codes.ndim == 2
+    if squeeze:
+        codes, scale_bytes = codes[None], scale_bytes[None]
+    G, K, N = codes.shape
+    out = np.empty((G, K, N), np.float64)
+    lib().oracle_dequant_mxfp4(_p(codes), _p(scale_bytes), G, K, N, _p(out))
     return out[0] if squeeze else out
 
 
