@@ -16,6 +16,8 @@ gate/up+SwiGLU grouped GEMM), timed with HIP events on its launch stream.
 workload. `--sweep 1,128,512` repeats the measurement at other batch sizes of
 the same layer shape (listed under `sweep`).
 
+`--weights mxfp4` likewise on MXFP4 weights (E2M1 codes, one E8M0 scale per
+32 K-values of a column; moe_forward_mxfp4), 4.25 bits per weight.
 `--weights fp8` times the layer on FP8 (E4M3) weights with per-column
 scales (moe_forward_fp8; bf16 activations and MFMA), which computes exactly
 the bf16 layer on the dequantized weights at half the weight bytes.
@@ -56,9 +58,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=32,
                     help="tokens in the oracle's timed sample")
-    ap.add_argument("--weights", choices=("packed", "rowmajor", "fp8"), default="packed",
+    ap.add_argument("--weights", choices=("packed", "rowmajor", "fp8", "mxfp4"),
+                    default="packed",
                     help="weight layout of the timed steps (fp8: E4M3 codes with per-column "
-                         "scales, moe_forward_fp8; bf16 arithmetic)")
+                         "scales, moe_forward_fp8; mxfp4: E2M1 codes with a scale byte per "
+                         "32 K-values, moe_forward_mxfp4; bf16 arithmetic in every case)")
     ap.add_argument("--router", action="store_true",
                     help="only time the router row: moe_router_route (router GEMM + "
                          "top-k routing) against torch's matmul + fp32 cast + moe_route, "
@@ -72,7 +76,8 @@ def parse():
 def work_model(cfg, T, counts, wb=2):
     """Algorithmic FLOPs and HBM bytes of one forward, per kernel.
     counts: rows per routed expert (E_touched = experts with rows); wb: bytes
-    per weight (2 bf16, 1 fp8; fp8 adds a 4-byte scale per output column)."""
+    per weight (2 bf16, 1 fp8, 0.5 + 1/32 mxfp4: a 4-bit code and a scale
+    byte per 32 K-values; fp8 adds a 4-byte scale per output column)."""
     H, F, E, k, Fs = cfg.H, cfg.F, cfg.E, cfg.k, cfg.Fs
     A = T * k
     Et = int((counts > 0).sum())
@@ -80,10 +85,11 @@ def work_model(cfg, T, counts, wb=2):
     m["route"] = dict(bytes=4 * T * E + 8 * A, flops=0)
     m["permute"] = dict(bytes=4 * A + 2 * T * H + 2 * A * H + 8 * A, flops=0)
     sc = 4 if wb == 1 else 0                # fp8 column scales
+    # (mxfp4's scale bytes are inside wb; byte counts are rounded to integers)
     g1 = 2 * wb * H * F * Et + 2 * sc * F * Et + 2 * A * H + 2 * A * F
     g1f = 4 * A * H * F
     # routed part of the gate/up GEMM alone (what moe_gateup_swiglu runs)
-    m["gateup_swiglu_routed"] = dict(bytes=g1, flops=g1f)
+    m["gateup_swiglu_routed"] = dict(bytes=int(g1), flops=g1f)
     g2 = wb * F * H * Et + sc * H * Et + 2 * A * F + 2 * A * H
     g2f = 2 * A * F * H
     cb = 2 * A * H + 8 * A + 2 * T * H
@@ -93,8 +99,8 @@ def work_model(cfg, T, counts, wb=2):
         g2 += wb * Fs * H + sc * H + 2 * T * Fs + 2 * T * H
         g2f += 2 * T * Fs * H
         cb += 2 * T * H + (4 * T if cfg.shared_gated else 0)
-    m["gateup_swiglu"] = dict(bytes=g1, flops=g1f)
-    m["down"] = dict(bytes=g2, flops=g2f)
+    m["gateup_swiglu"] = dict(bytes=int(g1), flops=g1f)
+    m["down"] = dict(bytes=int(g2), flops=g2f)
     m["combine"] = dict(bytes=cb, flops=0)
     total_b = sum(v["bytes"] for n, v in m.items() if n != "gateup_swiglu_routed")
     total_f = sum(v["flops"] for n, v in m.items() if n != "gateup_swiglu_routed")
@@ -230,7 +236,7 @@ def main():
         """(w_gate, w_up, w_down, shared) of a layer in the timed layout."""
         if mode == "rowmajor":
             return layer.w_gate, layer.w_up, layer.w_down, layer.shared
-        src = pk8 if mode == "fp8" else pk
+        src = pk8 if mode in ("fp8", "mxfp4") else pk
         return (src["wg"], src["wu"], src["wd"],
                 None if layer.shared is None else dict(src["shared"],
                                                        gate_logits=layer.shared["gate_logits"]))
@@ -301,21 +307,23 @@ def main():
     torch.cuda.synchronize()
     pack_ms = e0.elapsed_time(e1)
     pk8, quant_ms = None, None
-    if mode == "fp8":
+    if mode in ("fp8", "mxfp4"):
+        quant = B.moe_quantize_fp8 if mode == "fp8" else B.moe_quantize_mxfp4
         e0.record(stream)
-        pk8 = dict(wg=B.moe_quantize_fp8(layer.w_gate, stream=stream),
-                   wu=B.moe_quantize_fp8(layer.w_up, stream=stream),
-                   wd=B.moe_quantize_fp8(layer.w_down, stream=stream))
+        pk8 = dict(wg=quant(layer.w_gate, stream=stream),
+                   wu=quant(layer.w_up, stream=stream),
+                   wd=quant(layer.w_down, stream=stream))
         if layer.shared is not None:
-            pk8["shared"] = {n: B.moe_quantize_fp8(layer.shared[n], stream=stream)
+            pk8["shared"] = {n: quant(layer.shared[n], stream=stream)
                              for n in ("w_gate", "w_up", "w_down")}
         e1.record(stream)
         torch.cuda.synchronize()
         quant_ms = e0.elapsed_time(e1)
-    other = {"packed": "rowmajor", "rowmajor": "packed", "fp8": "packed"}[mode]
+    other = {"packed": "rowmajor", "rowmajor": "packed", "fp8": "packed", "mxfp4": "packed"}[mode]
+    WBYTES = {"fp8": 1, "mxfp4": 0.5 + 1 / 32}.get(mode, 2)
     ms, counts = measure(layer, args.steps, args.warmup, mode)
     ms_other, _ = measure(layer, max(10, args.steps // 2), 5, other)
-    total_b, total_f, per_kernel, Et = work_model(cfg, args.T, counts, 1 if mode == "fp8" else 2)
+    total_b, total_f, per_kernel, Et = work_model(cfg, args.T, counts, WBYTES)
     r = roof(total_b, total_f, ms)
 
     g1_ms = time_gateup(layer, max(args.steps, 20), mode)
@@ -341,7 +349,7 @@ def main():
             continue
         lay = layer_for(tok, weights_from=layer)
         ms_t, counts_t = measure(lay, max(10, args.steps // 2), 5, mode)
-        b_t, f_t, _, et_t = work_model(cfg, tok, counts_t, 1 if mode == "fp8" else 2)
+        b_t, f_t, _, et_t = work_model(cfg, tok, counts_t, WBYTES)
         rr = roof(b_t, f_t, ms_t)
         sweep.append(dict(T=tok, ms_per_step=round(ms_t, 5), GBs=round(rr["gbs"], 1),
                           TFLOPs=round(rr["tflops"], 2), hbm_frac=round(rr["hbm_frac"], 4),
@@ -380,12 +388,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "weight_dtype": "fp8_e4m3" if mode == "fp8" else "bf16",
+        "weight_dtype": {"fp8": "fp8_e4m3", "mxfp4": "mxfp4_e2m1"}.get(mode, "bf16"),
         "data": "synthetic (seeded; x~N(0,1), weights~N(0,0.02), logits~N(0,1))",
         "config": {"workload": f"{cfg.desc}: T={args.T}, H={cfg.H}, F={cfg.F}, E={cfg.E}, "
                                f"top-{cfg.k}, bf16, "
-                               + ("fp8 E4M3 weights with per-column scales"
-                                  if mode == "fp8" else f"{args.weights} weights"),
+                               + ({"fp8": "fp8 E4M3 weights with per-column scales",
+                                   "mxfp4": "MXFP4 weights (E2M1, E8M0 scale per 32)"}
+                                  .get(mode, f"{args.weights} weights")),
                    "weights": args.weights,
                    "T": args.T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "k": cfg.k,
                    "Fs": cfg.Fs, "experts_touched": Et, "parallelism": "none (1 GPU)"},

@@ -41,6 +41,13 @@ class SharedExpertFp8(ctypes.Structure):
                 ("Fs", ctypes.c_int32), ("gate_logits", ctypes.c_void_p)]
 
 
+class SharedExpertMxfp4(ctypes.Structure):
+    _fields_ = [("w_gate", ctypes.c_void_p), ("s_gate", ctypes.c_void_p),
+                ("w_up", ctypes.c_void_p), ("s_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p),
+                ("Fs", ctypes.c_int32), ("gate_logits", ctypes.c_void_p)]
+
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _SZ = ctypes.c_size_t
@@ -73,6 +80,13 @@ _SIGNATURES = {
     "moe_down_fp8": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_forward_fp8": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
                              ctypes.POINTER(SharedExpertFp8), _P, _P, _P, _P, _SZ, _P]),
+    "moe_mxfp4_weights_bytes": (_SZ, [_I, _I, _I]),
+    "moe_mxfp4_scales_bytes": (_SZ, [_I, _I, _I]),
+    "moe_quantize_mxfp4": (_I, [_P, _I, _I, _I, _P, _SZ, _P, _SZ, _P]),
+    "moe_gateup_swiglu_mxfp4": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "moe_down_mxfp4": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "moe_forward_mxfp4": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
+                               ctypes.POINTER(SharedExpertMxfp4), _P, _P, _P, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -264,21 +278,67 @@ def _fp8(w, name):
     return w
 
 
+class Mxfp4Weight:
+    """A [G,K,N] weight tensor in MXFP4: E2M1 codes in the library's block
+    layout (`codes`, uint8, two per byte) and E8M0 scale bytes, one per 32
+    K-values of a column (`scales`, uint8), from moe_quantize_mxfp4."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, G: int, K: int, N: int):
+        self.codes, self.scales, self.G, self.K, self.N = codes, scales, G, K, N
+        self.shape = (G, K, N)
+
+
+def moe_mxfp4_weights_bytes(G: int, K: int, N: int) -> int:
+    return int(lib().moe_mxfp4_weights_bytes(G, K, N))
+
+
+def moe_mxfp4_scales_bytes(G: int, K: int, N: int) -> int:
+    return int(lib().moe_mxfp4_scales_bytes(G, K, N))
+
+
+def moe_quantize_mxfp4(w: torch.Tensor, stream=None) -> Mxfp4Weight:
+    """w bf16 [G,K,N] (or [K,N], taken as G = 1) -> Mxfp4Weight."""
+    _need(w, torch.bfloat16, "w")
+    G, K, N = (1, *w.shape) if w.dim() == 2 else w.shape
+    nc, ns = moe_mxfp4_weights_bytes(G, K, N), moe_mxfp4_scales_bytes(G, K, N)
+    codes = torch.empty(max(nc, 16), dtype=torch.uint8, device=w.device)
+    scales = torch.empty(max(ns, 16), dtype=torch.uint8, device=w.device)
+    _check(lib().moe_quantize_mxfp4(_ptr(w), G, K, N, _ptr(codes), codes.numel(), _ptr(scales),
+                                    scales.numel(), _stream(stream)), "moe_quantize_mxfp4")
+    return Mxfp4Weight(codes, scales, G, K, N)
+
+
+_QUANT = {Fp8Weight: "fp8", Mxfp4Weight: "mxfp4"}
+
+
+def _quant_kind(w):
+    """'fp8' / 'mxfp4' for quantized weights, None otherwise."""
+    return _QUANT.get(type(w))
+
+
+def _same_kind(kind, w, name):
+    if _quant_kind(w) != kind:
+        raise TypeError(f"{name}: expected {kind} weights like the others")
+    return w
+
+
 def moe_gateup_swiglu(x_perm, expert_offsets, w_gate, w_up, h=None, stream=None):
     """w_gate, w_up: bf16 [E,H,F] tensors, PackedWeight (packed call) or
     Fp8Weight (fp8 call)."""
-    if isinstance(w_gate, Fp8Weight):
+    kind = _quant_kind(w_gate)
+    if kind:
         _need(x_perm, torch.bfloat16, "x_perm")
         _need(expert_offsets, torch.int32, "expert_offsets")
-        _fp8(w_up, "w_up")
+        _same_kind(kind, w_up, "w_up")
         M, H = x_perm.shape
         E, _, F = w_gate.shape
         if h is None:
             h = torch.empty((M, F), dtype=torch.bfloat16, device=x_perm.device)
-        _check(lib().moe_gateup_swiglu_fp8(
+        name = "moe_gateup_swiglu_" + kind
+        _check(getattr(lib(), name)(
             _ptr(x_perm), _ptr(expert_offsets), M, H, F, E, _ptr(w_gate.codes),
             _ptr(w_gate.scales), _ptr(w_up.codes), _ptr(w_up.scales), _ptr(h),
-            _stream(stream)), "moe_gateup_swiglu_fp8")
+            _stream(stream)), name)
         return h
     packed = isinstance(w_gate, PackedWeight)
     _need(x_perm, torch.bfloat16, "x_perm")
@@ -298,16 +358,18 @@ def moe_gateup_swiglu(x_perm, expert_offsets, w_gate, w_up, h=None, stream=None)
 
 def moe_down(h, expert_offsets, w_down, y_perm=None, stream=None):
     """w_down: bf16 [E,F,H] tensor, PackedWeight (packed call) or Fp8Weight."""
-    if isinstance(w_down, Fp8Weight):
+    kind = _quant_kind(w_down)
+    if kind:
         _need(h, torch.bfloat16, "h")
         _need(expert_offsets, torch.int32, "expert_offsets")
         M, F = h.shape
         E, _, H = w_down.shape
         if y_perm is None:
             y_perm = torch.empty((M, H), dtype=torch.bfloat16, device=h.device)
-        _check(lib().moe_down_fp8(_ptr(h), _ptr(expert_offsets), M, F, H, E,
-                                  _ptr(w_down.codes), _ptr(w_down.scales), _ptr(y_perm),
-                                  _stream(stream)), "moe_down_fp8")
+        name = "moe_down_" + kind
+        _check(getattr(lib(), name)(_ptr(h), _ptr(expert_offsets), M, F, H, E,
+                                    _ptr(w_down.codes), _ptr(w_down.scales), _ptr(y_perm),
+                                    _stream(stream)), name)
         return y_perm
     packed = isinstance(w_down, PackedWeight)
     _need(h, torch.bfloat16, "h")
@@ -403,9 +465,9 @@ def moe_forward(x, logits, k, w_gate, w_up, w_down, shared: Optional[dict] = Non
     w_down [Fs,H], gate_logits [T] fp32 or None). Returns out [T,H] bf16.
     With PackedWeight weights (all of them, shared expert included: packed
     from [1,H,Fs] / [1,Fs,H]) this calls moe_forward_packed."""
-    if isinstance(w_gate, Fp8Weight):
-        return _forward_fp8(x, logits, k, w_gate, w_up, w_down, shared, out, topk_ids,
-                            topk_w, ws, stream)
+    if _quant_kind(w_gate):
+        return _forward_quant(x, logits, k, w_gate, w_up, w_down, shared, out, topk_ids,
+                              topk_w, ws, stream)
     packed = isinstance(w_gate, PackedWeight)
     _need(x, torch.bfloat16, "x")
     _need(logits, torch.float32, "logits")
@@ -427,33 +489,36 @@ def moe_forward(x, logits, k, w_gate, w_up, w_down, shared: Optional[dict] = Non
     return out
 
 
-def _forward_fp8(x, logits, k, w_gate, w_up, w_down, shared, out, topk_ids, topk_w, ws,
-                 stream):
+def _forward_quant(x, logits, k, w_gate, w_up, w_down, shared, out, topk_ids, topk_w, ws,
+                   stream):
+    """moe_forward_fp8 or moe_forward_mxfp4, by the weights' kind."""
+    kind = _quant_kind(w_gate)
     _need(x, torch.bfloat16, "x")
     _need(logits, torch.float32, "logits")
     for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
-        _fp8(t, n)
+        _same_kind(kind, t, n)
     T, H = x.shape
     E, _, F = w_gate.shape
     sh, Fs = None, 0
     if shared is not None:
         for n in ("w_gate", "w_up", "w_down"):
-            _fp8(shared[n], "shared " + n)
+            _same_kind(kind, shared[n], "shared " + n)
         Fs = shared["w_gate"].shape[-1]
         g = shared.get("gate_logits")
-        sh = SharedExpertFp8(shared["w_gate"].codes.data_ptr(), shared["w_gate"].scales.data_ptr(),
-                             shared["w_up"].codes.data_ptr(), shared["w_up"].scales.data_ptr(),
-                             shared["w_down"].codes.data_ptr(),
-                             shared["w_down"].scales.data_ptr(), Fs,
-                             None if g is None else g.data_ptr())
+        cls = SharedExpertFp8 if kind == "fp8" else SharedExpertMxfp4
+        sh = cls(shared["w_gate"].codes.data_ptr(), shared["w_gate"].scales.data_ptr(),
+                 shared["w_up"].codes.data_ptr(), shared["w_up"].scales.data_ptr(),
+                 shared["w_down"].codes.data_ptr(), shared["w_down"].scales.data_ptr(), Fs,
+                 None if g is None else g.data_ptr())
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     if ws is None:
         ws = torch.empty(max(moe_forward_workspace_bytes(T, H, F, E, k, Fs), 16),
                          dtype=torch.uint8, device=x.device)
-    _check(lib().moe_forward_fp8(
+    name = "moe_forward_" + kind
+    _check(getattr(lib(), name)(
         _ptr(x), _ptr(logits), T, H, F, E, k, _ptr(w_gate.codes), _ptr(w_gate.scales),
         _ptr(w_up.codes), _ptr(w_up.scales), _ptr(w_down.codes), _ptr(w_down.scales),
         ctypes.byref(sh) if sh is not None else None, _ptr(out), _ptr(topk_ids), _ptr(topk_w),
-        _ptr(ws), ws.numel(), _stream(stream)), "moe_forward_fp8")
+        _ptr(ws), ws.numel(), _stream(stream)), name)
     return out

@@ -73,7 +73,7 @@ struct ForwardLayout {
 
 moe::GemmProblem down_problem(const bf16_t* h, const int32_t* offsets, int M, int F,
                               int H, int E, const bf16_t* wd, void* y, int layout,
-                              const float* sd = nullptr);
+                              const void* sd = nullptr);
 
 // The fused layer's down projection (routed + optional shared segment) with
 // fp32 output; pointers may be null when only the shape matters.
@@ -113,19 +113,20 @@ ForwardLayout forward_layout(int T, int H, int F, int E, int k, int Fs, int cus)
 }
 
 // Weight layouts: 0 [K][N] bf16, 1 packed bf16 blocks, 2 packed fp8 codes
-// (+ per-column scales).
-constexpr int kRowMajor = 0, kPackedBf16 = 1, kFp8 = 2;
+// (+ per-column scales), 3 packed mxfp4 codes (+ scale bytes).
+constexpr int kRowMajor = 0, kPackedBf16 = 1, kFp8 = 2, kMxfp4 = 3;
 
 // Elements (bf16-sized) between consecutive experts' weight matrices.
 int64_t weight_stride(int K, int N, int layout) {
   return layout == kFp8        ? moe::fp8_weight_bytes(1, K, N) / 2
+         : layout == kMxfp4      ? moe::mxfp4_weight_bytes(1, K, N) / 2
          : layout == kPackedBf16 ? moe::packed_weight_elems(1, K, N)
                                  : static_cast<int64_t>(K) * N;
 }
 
 moe::GemmSegment segment(const bf16_t* act, const int32_t* offsets, const bf16_t* w0,
                          const bf16_t* w1, void* out, int rows, int ngroups, int K, int N,
-                         int layout, const float* s0, const float* s1) {
+                         int layout, const void* s0, const void* s1) {
   moe::GemmSegment g{act, offsets, w0, w1, out, weight_stride(K, N, layout), 0, rows, ngroups,
                      K, N, layout};
   g.scale0 = s0;
@@ -136,7 +137,7 @@ moe::GemmSegment segment(const bf16_t* act, const int32_t* offsets, const bf16_t
 moe::GemmProblem gateup_problem(const bf16_t* x_perm, const int32_t* offsets, int M,
                                 int H, int F, int E, const bf16_t* wg,
                                 const bf16_t* wu, bf16_t* h, int layout,
-                                const float* sg = nullptr, const float* su = nullptr) {
+                                const void* sg = nullptr, const void* su = nullptr) {
   moe::GemmProblem p{};
   p.seg[0] = segment(x_perm, offsets, wg, wu, h, M, E, H, F, layout, sg, su);
   p.nseg = 1;
@@ -147,7 +148,7 @@ moe::GemmProblem gateup_problem(const bf16_t* x_perm, const int32_t* offsets, in
 
 moe::GemmProblem down_problem(const bf16_t* h, const int32_t* offsets, int M, int F,
                               int H, int E, const bf16_t* wd, void* y, int layout,
-                              const float* sd) {
+                              const void* sd) {
   moe::GemmProblem p{};
   p.seg[0] = segment(h, offsets, wd, nullptr, y, M, E, F, H, layout, sd, nullptr);
   p.nseg = 1;
@@ -259,11 +260,11 @@ int moe_permute(const moe_bf16* x, const int32_t* topk_ids, int T, int H, int E,
 
 static int gateup_impl(const moe_bf16* x_perm, const int32_t* expert_offsets, int M, int H,
                        int F, int E, const moe_bf16* w_gate, const moe_bf16* w_up, moe_bf16* h,
-                       void* stream, int layout, const float* sg = nullptr,
-                       const float* su = nullptr) {
+                       void* stream, int layout, const void* sg = nullptr,
+                       const void* su = nullptr) {
   MOE_TRY(check_ffn_args(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, true, h));
   if (M == 0) return MOE_OK;
-  if (layout == kFp8) {
+  if (layout == kFp8 || layout == kMxfp4) {
     MOE_TRY(need_bf16(sg));
     MOE_TRY(need_bf16(su));
   }
@@ -274,10 +275,10 @@ static int gateup_impl(const moe_bf16* x_perm, const int32_t* expert_offsets, in
 
 static int down_impl(const moe_bf16* h, const int32_t* expert_offsets, int M, int F, int H,
                      int E, const moe_bf16* w_down, moe_bf16* y_perm, void* stream,
-                     int layout, const float* sd = nullptr) {
+                     int layout, const void* sd = nullptr) {
   MOE_TRY(check_ffn_args(h, expert_offsets, M, F, H, E, w_down, nullptr, false, y_perm));
   if (M == 0) return MOE_OK;
-  if (layout == kFp8) MOE_TRY(need_bf16(sd));
+  if (layout == kFp8 || layout == kMxfp4) MOE_TRY(need_bf16(sd));
   return hip_status(moe::launch_grouped_gemm(
       down_problem(h, expert_offsets, M, F, H, E, w_down, y_perm, layout, sd),
       static_cast<hipStream_t>(stream)));
@@ -337,6 +338,45 @@ int moe_down_fp8(const moe_bf16* h, const int32_t* expert_offsets, int M, int F,
                    y_perm, stream, kFp8, s_down);
 }
 
+size_t moe_mxfp4_weights_bytes(int G, int K, int N) {
+  if (G < 1 || check_width(K) != MOE_OK || check_width(N) != MOE_OK) return 0;
+  return static_cast<size_t>(moe::mxfp4_weight_bytes(G, K, N));
+}
+
+size_t moe_mxfp4_scales_bytes(int G, int K, int N) {
+  if (G < 1 || check_width(K) != MOE_OK || check_width(N) != MOE_OK) return 0;
+  return static_cast<size_t>(moe::mxfp4_scale_bytes(G, K, N));
+}
+
+int moe_quantize_mxfp4(const moe_bf16* w, int G, int K, int N, uint8_t* codes,
+                       size_t codes_bytes, uint8_t* scales, size_t scales_bytes, void* stream) {
+  if (G < 1) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_width(K));
+  MOE_TRY(check_width(N));
+  MOE_TRY(need_bf16(w));
+  MOE_TRY(need_bf16(codes));
+  MOE_TRY(need_bf16(scales));
+  if (codes_bytes < moe_mxfp4_weights_bytes(G, K, N) ||
+      scales_bytes < moe_mxfp4_scales_bytes(G, K, N))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(moe::launch_quantize_mxfp4(w, G, K, N, codes, scales,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int moe_gateup_swiglu_mxfp4(const moe_bf16* x_perm, const int32_t* expert_offsets, int M, int H,
+                            int F, int E, const uint8_t* w_gate, const uint8_t* s_gate,
+                            const uint8_t* w_up, const uint8_t* s_up, moe_bf16* h,
+                            void* stream) {
+  return gateup_impl(x_perm, expert_offsets, M, H, F, E, reinterpret_cast<const bf16_t*>(w_gate),
+                     reinterpret_cast<const bf16_t*>(w_up), h, stream, kMxfp4, s_gate, s_up);
+}
+
+int moe_down_mxfp4(const moe_bf16* h, const int32_t* expert_offsets, int M, int F, int H, int E,
+                   const uint8_t* w_down, const uint8_t* s_down, moe_bf16* y_perm, void* stream) {
+  return down_impl(h, expert_offsets, M, F, H, E, reinterpret_cast<const bf16_t*>(w_down),
+                   y_perm, stream, kMxfp4, s_down);
+}
+
 size_t moe_pack_weights_bytes(int G, int K, int N) {
   if (G < 1 || check_width(K) != MOE_OK || check_width(N) != MOE_OK) return 0;
   return static_cast<size_t>(moe::packed_weight_elems(G, K, N)) * sizeof(bf16_t);
@@ -394,12 +434,12 @@ size_t moe_forward_workspace_bytes(int T, int H, int F, int E, int k, int Fs) {
 // The layer's weights in one layout (the shared expert's too, when Fs > 0).
 struct LayerWeights {
   int layout;
-  const bf16_t *wg, *wu, *wd;   // fp8: the codes
-  const float *sg, *su, *sd;    // fp8: column scales
+  const bf16_t *wg, *wu, *wd;   // fp8, mxfp4: the codes
+  const void *sg, *su, *sd;     // fp8: column scales; mxfp4: scale bytes
   bool shared;
   int Fs;
   const bf16_t *swg, *swu, *swd;
-  const float *ssg, *ssu, *ssd;
+  const void *ssg, *ssu, *ssd;
   const float* gate_logits;
 };
 
@@ -429,7 +469,7 @@ static int forward_impl(const moe_bf16* x, const float* logits, const int32_t* i
   const bool shared = W.shared;
   const int Fs = shared ? W.Fs : 0;
   if (shared) MOE_TRY(check_width(Fs));
-  const bool fp8 = W.layout == kFp8;
+  const bool fp8 = W.layout == kFp8 || W.layout == kMxfp4;  // codes + scales
   const int64_t A = static_cast<int64_t>(T) * k;
   const int64_t widest = (H > F ? H : F) > Fs ? (H > F ? H : F) : Fs;
   MOE_TRY(check_elems(A, widest));
@@ -563,6 +603,31 @@ int moe_forward_fp8(const moe_bf16* x, const float* logits, int T, int H, int F,
                     float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
   LayerWeights W{};
   W.layout = kFp8;
+  W.wg = reinterpret_cast<const bf16_t*>(w_gate);
+  W.wu = reinterpret_cast<const bf16_t*>(w_up);
+  W.wd = reinterpret_cast<const bf16_t*>(w_down);
+  W.sg = s_gate, W.su = s_up, W.sd = s_down;
+  W.shared = shared != nullptr;
+  if (shared) {
+    W.Fs = shared->Fs;
+    W.swg = reinterpret_cast<const bf16_t*>(shared->w_gate);
+    W.swu = reinterpret_cast<const bf16_t*>(shared->w_up);
+    W.swd = reinterpret_cast<const bf16_t*>(shared->w_down);
+    W.ssg = shared->s_gate, W.ssu = shared->s_up, W.ssd = shared->s_down;
+    W.gate_logits = shared->gate_logits;
+  }
+  return forward_impl(x, logits, nullptr, nullptr, T, H, F, E, k, W, out, topk_ids_out,
+                      topk_w_out, ws, ws_bytes, stream);
+}
+
+int moe_forward_mxfp4(const moe_bf16* x, const float* logits, int T, int H, int F, int E, int k,
+                      const uint8_t* w_gate, const uint8_t* s_gate, const uint8_t* w_up,
+                      const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
+                      const moe_shared_expert_mxfp4* shared, moe_bf16* out,
+                      int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                      void* stream) {
+  LayerWeights W{};
+  W.layout = kMxfp4;
   W.wg = reinterpret_cast<const bf16_t*>(w_gate);
   W.wu = reinterpret_cast<const bf16_t*>(w_up);
   W.wd = reinterpret_cast<const bf16_t*>(w_down);

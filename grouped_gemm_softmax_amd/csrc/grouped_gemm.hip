@@ -131,6 +131,25 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 u) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Eight E2M1 codes (the nibbles of u, low nibble first) times a power-of-two
+// scale, widened to bf16: gfx950's v_cvt_scalef32_pk_f32_fp4 decodes the two
+// codes of one byte to fp32 and applies the scale; every such product is a
+// bf16 value, so the upper half of each fp32 is exact.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t u, float scale) {
+  const auto f01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, scale, 0);
+  const auto f23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, scale, 1);
+  const auto f45 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, scale, 2);
+  const auto f67 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, scale, 3);
+  const uint4 v = uint4{hi16_pair(f01[0], f01[1]), hi16_pair(f23[0], f23[1]),
+                        hi16_pair(f45[0], f45[1]), hi16_pair(f67[0], f67[1])};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// MXFP4 scale bytes per 64-column block: K-blocks of 32, rounded up to a
+// whole number of 128-value steps, so a stage up to 128 deep stays inside
+// its block's scales.
+__host__ __device__ __forceinline__ int mx_scale_kblocks(int K) { return 4 * ((K + 127) / 128); }
+
 // Lambdas of the kernel body are always inlined: their operands (the
 // accumulators, fragment sets and ring buffers) must stay in registers and
 // fixed LDS arrays.
@@ -147,7 +166,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <int BT_, int BF_, int BK_, int WT_, int WF_, int STAGES_, bool GATED_,
-          bool PREFETCH_, int MIN_WAVES_ = 1, int WB_ = 2, bool PP_ = false>
+          bool PREFETCH_, int MIN_WAVES_ = 1, int WBITS_ = 16, bool PP_ = false>
 struct TileCfg {
   static constexpr int BT = BT_;  // activation rows (tokens) per tile
   static constexpr int BF = BF_;  // output columns per tile
@@ -162,8 +181,10 @@ struct TileCfg {
   // waves per SIMD the register allocation must leave room for (so that
   // this many fit by registers as well as by LDS)
   static constexpr int MIN_WAVES = MIN_WAVES_;
-  // bytes per weight element: 2 (bf16) or 1 (fp8 E4M3 codes, packed layout)
-  static constexpr int WB = WB_;
+  // bits per weight element: 16 (bf16), 8 (fp8 E4M3 codes) or 4 (MXFP4
+  // E2M1 codes); the 8- and 4-bit codes exist in their packed layouts only
+  static constexpr int WBITS = WBITS_;
+  static constexpr bool MX = WBITS == 4;
   // Ping-pong schedule: the two waves of each SIMD alternate between an
   // MFMA phase and a memory phase (LDS fragment reads, DMA issue), so one of
   // them always feeds the matrix core (8 waves, no fragment prefetch).
@@ -175,13 +196,21 @@ struct TileCfg {
   static constexpr int TT = BT / WT;  // tokens per wave
   static constexpr int FF = TF / 16;  // MFMA blocks per wave (columns)
   static constexpr int FT = TT / 16;  // MFMA blocks per wave (tokens)
-  static constexpr int W_BYTES = BK * BF * WB;  // one weight matrix per stage
-  static constexpr int SB = BF / 64;            // 64-column sub-blocks per matrix
-  static constexpr int SB_BYTES = BK * 64 * WB; // one sub-block: BK rows of 64 columns
+  static constexpr int W_BYTES = BK * BF * WBITS / 8;  // one weight matrix per stage
+  static constexpr int SB = BF / 64;                   // 64-column sub-blocks per matrix
+  static constexpr int SB_BYTES = BK * 64 * WBITS / 8; // one sub-block: BK rows of 64 columns
   static constexpr int X_BYTES = BT * BK * 2;
-  static constexpr int STAGE_BYTES = NMAT * W_BYTES + X_BYTES;
-  static constexpr int INSTR = STAGE_BYTES / 1024;  // 1 KB DMA instructions
-  static constexpr int IPW = INSTR / NW;            // per wave per stage
+  static constexpr int OP_BYTES = NMAT * W_BYTES + X_BYTES;  // the MFMA operands
+  // MXFP4: the scale bytes of the stage's weights after the operands, as
+  // pieces (matrix, sub-block) of BK/32 K-blocks x 64 columns; each wave
+  // loads one slot of SC_SLOT bytes (one partial DMA instruction)
+  static constexpr int SC_PIECE = MX ? (BK / 32) * 64 : 0;
+  static constexpr int SC_BYTES = MX ? NMAT * SB * SC_PIECE : 0;
+  static constexpr int SC_SLOT = SC_BYTES / NW;
+  static constexpr int STAGE_BYTES = OP_BYTES + SC_BYTES;
+  static constexpr int INSTR = OP_BYTES / 1024;     // 1 KB operand DMA instructions
+  static constexpr int OPW = INSTR / NW;            // per wave per stage
+  static constexpr int IPW = OPW + (MX ? 1 : 0);    // vector-memory operations per wave per stage
   static constexpr int W_INSTR = NMAT * W_BYTES / 1024;
   static_assert(BF % (16 * WF) == 0 && BT % (16 * WT) == 0, "wave tiling");
   static_assert((BK == 32 || BK % 64 == 0) && BF % 64 == 0, "swizzle geometry");
@@ -189,7 +218,9 @@ struct TileCfg {
   static_assert(INSTR % NW == 0 && W_INSTR % NW == 0,
                 "equal DMA share per wave, one operand kind per instruction slot");
   static_assert(STAGES >= 3 && STAGES <= 8, "ring depth");
-  static_assert(WB == 2 || WB == 1, "bf16 or fp8 weights");
+  static_assert(WBITS == 16 || WBITS == 8 || WBITS == 4, "bf16, fp8 or mxfp4 weights");
+  static_assert(!MX || (SC_SLOT % 16 == 0 && SC_SLOT > 0 && SC_PIECE % SC_SLOT == 0),
+                "each wave's scale slot: whole 16-byte chunks inside one piece");
   // vmcnt holds at most 63 outstanding operations per wave: the K-steps in
   // flight must fit, and for chaining across items also the epilogue's
   // stores issued while the next item's first K-steps are in flight
@@ -335,8 +366,9 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
 
   constexpr int W_PER_MAT = C::W_BYTES / 1024;   // DMA instructions per weight matrix
   constexpr int IPS = C::SB_BYTES / 1024;        // instructions per weight sub-block
-  constexpr bool FP8 = C::WB == 1;
-  static_assert(!FP8 || PACKED, "fp8 weights exist only in the packed layout");
+  constexpr bool FP8 = C::WBITS == 8;
+  constexpr bool MX = C::MX;
+  static_assert(!(FP8 || MX) || PACKED, "fp8 and mxfp4 weights exist only in packed layouts");
   constexpr int RPI_X = 1024 / (C::BK * 2);      // activation rows per instruction
 
   // ---- one work item: where its operands are, its K range, its output ----
@@ -353,11 +385,11 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     int nk;           // K-steps of the slice
     int nk_all;       // K-steps of the whole K
     int nblk, kblk;   // packed: 64-column and 64-row blocks of one group
-    const float* sc0; // fp8: the group's column scales (gate / plain matrix)
-    const float* sc1; // fp8: the group's column scales (up matrix)
+    const void* sc0;  // fp8: the group's column scales (gate / plain matrix);
+    const void* sc1;  // mxfp4: its scale bytes (gate / plain, up)
     // per-lane byte offsets of this wave's DMA sources within a K-step,
     // relative to the step's scalar base
-    uint32_t voff[C::IPW];
+    uint32_t voff[C::OPW];
   };
   auto make_item = [&](int item) INL {
     // group owning the item: the largest g with s_pref[g] <= item
@@ -398,14 +430,24 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     // gathered rows: row p of the group's block is activation row S.gather[p]
     it.x = S.gather ? S.act : S.act + static_cast<int64_t>(it.row_base) * it.K;
     it.out = static_cast<OutT*>(S.out) + static_cast<int64_t>(ks) * S.slice_stride;
-    it.sc0 = FP8 ? S.scale0 + static_cast<int64_t>(v.local) * S.N : nullptr;
-    it.sc1 = FP8 && C::GATED ? S.scale1 + static_cast<int64_t>(v.local) * S.N : it.sc0;
+    if constexpr (FP8) {
+      it.sc0 = static_cast<const float*>(S.scale0) + static_cast<int64_t>(v.local) * S.N;
+      it.sc1 = C::GATED ? static_cast<const float*>(S.scale1) + static_cast<int64_t>(v.local) * S.N
+                        : it.sc0;
+    } else if constexpr (MX) {
+      // scale bytes [G][nblk][4 * ceil(K/128)][64]
+      const int64_t per_group = static_cast<int64_t>(it.nblk) * mx_scale_kblocks(S.K) * 64;
+      it.sc0 = static_cast<const uint8_t*>(S.scale0) + v.local * per_group;
+      it.sc1 = C::GATED ? static_cast<const uint8_t*>(S.scale1) + v.local * per_group : it.sc0;
+    } else {
+      it.sc0 = it.sc1 = nullptr;
+    }
     // every field is wave-uniform: keep them in scalar registers
     it.w0 = uniform(it.w0);
     it.w1 = uniform(it.w1);
     it.x = uniform(it.x);
     it.out = uniform(it.out);
-    if constexpr (FP8) {
+    if constexpr (FP8 || MX) {
       it.sc0 = uniform(it.sc0);
       it.sc1 = uniform(it.sc1);
     }
@@ -421,7 +463,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     it.kblk = __builtin_amdgcn_readfirstlane(it.kblk);
     {
 #pragma unroll
-      for (int i = 0; i < C::IPW; ++i) {
+      for (int i = 0; i < C::OPW; ++i) {
         const int j = i * C::NW + wave;
         if (i < C::W_INSTR / C::NW) {
           const int mat = j / W_PER_MAT;
@@ -463,7 +505,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     const int64_t k0 = static_cast<int64_t>(min(kt, it.nk_all - 1)) * C::BK;
     const int kleft = it.K - static_cast<int>(k0);  // K values from k0 on
 #pragma unroll
-    for (int i = 0; i < C::IPW; ++i) {
+    for (int i = 0; i < C::OPW; ++i) {
       const int j = i * C::NW + wave;
       const bf16_t* base;
       uint32_t voff = it.voff[i];
@@ -482,6 +524,11 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
             // offsets below are in bf16 units, 2 codes each)
             const int64_t blk = static_cast<int64_t>(nb) * it.kblk + k0 / 64;
             base = w + blk * 2048 + ((k0 % 64) / 32) * 1024 + (jj % IPS) * 512;
+          } else if constexpr (MX) {
+            // 2 KB blocks of E2M1 codes: [32-row half][64 columns][16 bytes]
+            // (bf16-unit offsets: 4 codes each)
+            const int64_t blk = static_cast<int64_t>(nb) * it.kblk + k0 / 64;
+            base = w + blk * 1024 + ((k0 % 64) / 32) * 512 + (jj % IPS) * 512;
           } else {
             // 8 KB blocks: [32-row half][64 columns][32 K-values]; a 32-deep
             // step reads one half, a 64-deep step the whole block
@@ -505,6 +552,19 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
       }
       dma16(base, voff, buf + j * 1024);
     }
+    if constexpr (MX) {
+      // this wave's slot of the stage's scale bytes: piece (matrix m,
+      // sub-block sb), BK/32 K-blocks of 64 columns from K-block k0/32
+      constexpr int LANES = C::SC_SLOT / 16;
+      const int pw = (wave * C::SC_SLOT) / C::SC_PIECE;
+      const int m = pw / C::SB, sb = pw % C::SB;
+      const int nb = min(it.n0 / 64 + sb, it.nblk - 1);
+      const uint8_t* sbase = static_cast<const uint8_t*>(m ? it.sc1 : it.sc0) +
+                             (static_cast<int64_t>(nb) * mx_scale_kblocks(it.K) + k0 / 32) * 64 +
+                             (wave * C::SC_SLOT) % C::SC_PIECE;
+      char* const dst = buf + C::OP_BYTES + wave * C::SC_SLOT;
+      if (LANES == kWave || lane < LANES) dma16(sbase, static_cast<uint32_t>(lane) * 16u, dst);
+    }
   };
 
   floatx4 acc[C::NMAT][C::FF][C::FT];
@@ -526,6 +586,17 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
                       ((g16 ^ ((c >> 2) & 3)) << 3);
       const uint2 u = *reinterpret_cast<const uint2*>(p);
       return fp8x8_to_bf16(u);
+    } else if constexpr (MX) {
+      // the lane's column and its 8 consecutive K codes (one dword of the
+      // column's 16 bytes in this 32-row half; 16 consecutive columns' rows
+      // fill all 64 banks), widened exactly to bf16 with the K-block's scale
+      const int col = wf * C::TF + fi * 16 + i16;
+      const int c = col & 63;
+      const char* sub = buf + m * C::W_BYTES + (col >> 6) * C::SB_BYTES;
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(sub + s * 1024 + c * 16 + g16 * 4);
+      const uint32_t e8 = *reinterpret_cast<const uint8_t*>(
+          buf + C::OP_BYTES + ((m * C::SB + (col >> 6)) * (C::BK / 32) + s) * 64 + c);
+      return fp4x8_to_bf16(u, __uint_as_float(e8 << 23));
     } else if constexpr (PACKED) {
       // packed bf16: each column's 32 K-values of a half are one 64-byte row
       // (16-byte chunk q at q ^ ((c >> 1) & 3)), so the lane's 8 consecutive
@@ -587,7 +658,8 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
   // Without prefetch, the gated kernel interleaves the weight-fragment reads
   // column block by column block with the MFMAs that use them; the plain
   // kernel reads all fragments first (each order measured faster for its
-  // kernel).
+  // kernel), except on mxfp4 weights, where all widened fragments of a
+  // 64-deep stage would not fit the registers.
   auto compute_interleaved = [&](const char* buf, int kvalid) INL {
 #pragma unroll
     for (int s = 0; s < C::BK / 32; ++s) {
@@ -761,7 +833,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
       } else {
         char* const cb = stage_buf(I);
         const int kvalid = cur.K - (cur.kt_begin + t) * C::BK;
-        if constexpr (C::GATED) {
+        if constexpr (C::GATED || C::MX) {
           compute_interleaved(cb, kvalid);
         } else {
           load_frags(cb, fa, kvalid);
@@ -789,8 +861,8 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
       float4 s0 = float4{1.f, 1.f, 1.f, 1.f}, s1 = s0;
       if constexpr (FP8) {
         const int fc = min(cur.n0 + wf * C::TF + fi * 16 + 4 * g16, cur.N - 4);
-        s0 = *reinterpret_cast<const float4*>(cur.sc0 + fc);
-        if (C::GATED) s1 = *reinterpret_cast<const float4*>(cur.sc1 + fc);
+        s0 = *reinterpret_cast<const float4*>(static_cast<const float*>(cur.sc0) + fc);
+        if (C::GATED) s1 = *reinterpret_cast<const float4*>(static_cast<const float*>(cur.sc1) + fc);
       }
       const float sc0[4] = {s0.x, s0.y, s0.z, s0.w};
       const float sc1[4] = {s1.x, s1.y, s1.z, s1.w};
@@ -848,23 +920,44 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
 // are in flight (measured against 32-deep stages with two workgroups per CU:
 // the DeepSeek-V3-shaped layer at 4096 tokens 8.6 % faster, the
 // Mixtral-shaped one at 512 tokens 3 %).
-using GateUpLarge = TileCfg<256, 128, 32, 4, 2, 4, true, false, 1, 2, true>;
+using GateUpLarge = TileCfg<256, 128, 32, 4, 2, 4, true, false, 1, 16, true>;
 using GateUpLarge128 = TileCfg<128, 128, 64, 4, 2, 3, true, true, 2>;
 using DownLarge128 = TileCfg<128, 256, 64, 4, 2, 3, false, true, 2>;
 using GateUpSmall = TileCfg<16, 64, 64, 1, 2, 4, true, true>;
 using GateUpMid = TileCfg<32, 64, 64, 1, 2, 3, true, true>;
-using DownLarge = TileCfg<256, 256, 32, 4, 2, 4, false, false, 1, 2, true>;
+using DownLarge = TileCfg<256, 256, 32, 4, 2, 4, false, false, 1, 16, true>;
 using DownSmall = TileCfg<32, 64, 64, 1, 4, 4, false, true>;
 // FP8 weights: the same tile shapes with half the weight bytes per stage,
 // hence deeper rings in about the same LDS. The 128-row tiles take 32-deep
 // stages (64-deep ones would spill the widened fragments).
-using GateUpLarge8 = TileCfg<256, 128, 32, 4, 2, 5, true, false, 1, 1, true>;
-using GateUpLarge128_8 = TileCfg<128, 128, 32, 4, 2, 8, true, true, 2, 1>;
-using DownLarge128_8 = TileCfg<128, 256, 32, 4, 2, 8, false, true, 2, 1>;
-using GateUpSmall8 = TileCfg<16, 64, 64, 1, 2, 4, true, true, 1, 1>;
-using GateUpMid8 = TileCfg<32, 64, 64, 1, 2, 4, true, true, 1, 1>;
-using DownLarge8 = TileCfg<256, 256, 32, 4, 2, 5, false, false, 1, 1, true>;
-using DownSmall8 = TileCfg<32, 64, 64, 1, 4, 4, false, true, 1, 1>;
+using GateUpLarge8 = TileCfg<256, 128, 32, 4, 2, 5, true, false, 1, 8, true>;
+using GateUpLarge128_8 = TileCfg<128, 128, 32, 4, 2, 8, true, true, 2, 8>;
+using DownLarge128_8 = TileCfg<128, 256, 32, 4, 2, 8, false, true, 2, 8>;
+using GateUpSmall8 = TileCfg<16, 64, 64, 1, 2, 4, true, true, 1, 8>;
+using GateUpMid8 = TileCfg<32, 64, 64, 1, 2, 4, true, true, 1, 8>;
+using DownLarge8 = TileCfg<256, 256, 32, 4, 2, 5, false, false, 1, 8, true>;
+using DownSmall8 = TileCfg<32, 64, 64, 1, 4, 4, false, true, 1, 8>;
+// MXFP4 weights: a quarter of the bf16 weight bytes per stage plus the
+// scale bytes, 64-deep stages wherever a 32-deep one would not give every
+// wave a whole number of 1 KB DMA instructions. The decode tiles widen every
+// weight fragment with VALU work, so they run at up to four waves per SIMD
+// (registers bounded for that, 4-stage rings of ~7 KB: five workgroups per
+// CU); with 8-stage rings and one wave per SIMD the Mixtral-shaped layer at
+// 32 tokens took 17 % longer. The down tile has 16 rows (half the
+// activation bytes of a 32-row one at decode; the K-split plan, made for
+// 32-row tiles, stays valid for any tile). The 128-row tiles keep
+// one fragment set (prefetching fragments of 64-deep stages spill) and read
+// each weight fragment just before its MFMAs; they also serve the 256-row
+// class (a 256-row tile with 64-deep stages spills even so; the down
+// projection's K-split plan is valid for any tile, only tuned for another).
+using GateUpSmall4 = TileCfg<16, 64, 64, 1, 2, 4, true, true, 4, 4>;
+using GateUpMid4 = TileCfg<32, 64, 64, 1, 2, 4, true, true, 4, 4>;
+using DownSmall4 = TileCfg<16, 64, 64, 1, 2, 4, false, true, 4, 4>;
+using GateUpLarge128_4 = TileCfg<128, 128, 64, 4, 2, 4, true, false, 2, 4>;
+using DownLarge128_4 = TileCfg<128, 256, 64, 4, 2, 4, false, false, 2, 4>;
+static_assert(DownLarge128_4::BT == DownLarge128::BT &&
+                  DownLarge128_4::BF == DownLarge128::BF && DownSmall4::BF == DownSmall::BF,
+              "mxfp4 tiles share the bf16 tiles' shapes (the split-K plan and tile classes)");
 static_assert(DownLarge8::BT == DownLarge::BT && DownLarge8::BF == DownLarge::BF &&
                   DownLarge128_8::BT == DownLarge128::BT &&
                   DownLarge128_8::BF == DownLarge128::BF && DownSmall8::BT == DownSmall::BT &&
@@ -939,12 +1032,16 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   const int layout = p.seg[0].packed;
   for (int s = 1; s < p.nseg; ++s)
     if (p.seg[s].packed != layout) return hipErrorInvalidValue;  // one layout per launch
-  if constexpr (C::WB == 1) {
+  if constexpr (C::MX) {
+    if (layout != 3) return hipErrorInvalidValue;
+    return ktail ? launch_tail<C, OutT, true, true>(p, bound, stream)
+                 : launch_tail<C, OutT, false, true>(p, bound, stream);
+  } else if constexpr (C::WBITS == 8) {
     if (layout != 2) return hipErrorInvalidValue;
     return ktail ? launch_tail<C, OutT, true, true>(p, bound, stream)
                  : launch_tail<C, OutT, false, true>(p, bound, stream);
   } else {
-    if (layout == 2) return hipErrorInvalidValue;
+    if (layout >= 2) return hipErrorInvalidValue;
     if (layout == 1)
       return ktail ? launch_tail<C, OutT, true, true>(p, bound, stream)
                    : launch_tail<C, OutT, false, true>(p, bound, stream);
@@ -1149,7 +1246,110 @@ __global__ __launch_bounds__(256) void fp8_encode_kernel(
   reinterpret_cast<uint2*>(out)[idx] = uint2{lo, hi};
 }
 
+// MXFP4 quantization, step 1: one thread per scale byte of the padded
+// layout [G][nblk][skb][64]: for column n and K-block b (K-values 32b ..
+// 32b+31 inside K) the largest |w| (bf16 magnitudes order like their bit
+// patterns); X = floor(log2 amax) - 2 = exponent field - 129 for a normal
+// amax, raised to -125 (also for a subnormal amax), 0 for an all-zero block
+// and past K or N; the byte is X + 127.
+__global__ __launch_bounds__(256) void mxfp4_scales_kernel(const bf16_t* __restrict__ w, int K,
+                                                           int N, int nblk, int skb,
+                                                           int64_t total,
+                                                           uint8_t* __restrict__ out) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int c = static_cast<int>(idx & 63);
+  int64_t rest = idx >> 6;
+  const int b = static_cast<int>(rest % skb);
+  rest /= skb;
+  const int nb = static_cast<int>(rest % nblk);
+  const int64_t g = rest / nblk;
+  const int n = nb * 64 + c;
+  int X = 0;
+  if (n < N && 32 * b < K) {
+    const bf16_t* p = w + (g * K + 32 * b) * N + n;
+    const int rows = min(32, K - 32 * b);
+    uint32_t amax = 0;
+    for (int k = 0; k < rows; ++k) {
+      const uint32_t m = p[static_cast<int64_t>(k) * N] & 0x7fffu;
+      amax = m > amax ? m : amax;
+    }
+    if (amax != 0) {
+      const int e = static_cast<int>(amax >> 7);
+      X = e == 0 ? -125 : max(e - 129, -125);
+    }
+  }
+  out[idx] = static_cast<uint8_t>(X + 127);
+}
+
+// E2M1 code of v (v = w / 2^X, |v| < 8): round to nearest on the grid 0,
+// 0.5, 1, 1.5, 2, 3, 4, 6, a tie going to the code with mantissa bit 0,
+// magnitudes above 6 saturating to 6; the sign is v's (also for zeros).
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
+  const float a = fabsf(v);
+  const uint32_t m = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                     : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return sign | m;
+}
+
+// MXFP4 quantization, step 2: one thread per dword of the code blocks
+// (dword q of column c in half h of block (g, nb, kb)): the codes of rows
+// kb*64 + h*32 + 8q + i, i = 0..7, nibble i (low nibble first), each weight
+// divided by its K-block's scale (exact: a power of two) and encoded.
+__global__ __launch_bounds__(256) void mxfp4_encode_kernel(
+    const bf16_t* __restrict__ w, int K, int N, int nblk, int kblk, int skb, int64_t words,
+    const uint8_t* __restrict__ scales, uint32_t* __restrict__ out) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= words) return;
+  const int q = static_cast<int>(idx & 3);
+  const int c = static_cast<int>((idx >> 2) & 63);
+  const int h = static_cast<int>((idx >> 8) & 1);
+  int64_t blk = idx >> 9;
+  const int kb = static_cast<int>(blk % kblk);
+  blk /= kblk;
+  const int nb = static_cast<int>(blk % nblk);
+  const int64_t g = blk / nblk;
+  const int n = nb * 64 + c;
+  const int k0 = kb * 64 + h * 32 + q * 8;
+  uint32_t word = 0;
+  if (n < N && k0 < K) {  // K is a multiple of 8: all 8 rows are inside K
+    const int X = static_cast<int>(scales[((g * nblk + nb) * skb + k0 / 32) * 64 + c]) - 127;
+    const bf16_t* p = w + (g * K + k0) * N + n;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = __uint_as_float(static_cast<uint32_t>(p[static_cast<int64_t>(i) * N]) << 16);
+      word |= e2m1_encode(ldexpf(x, -X)) << (4 * i);
+    }
+  }
+  out[idx] = word;
+}
+
 }  // namespace
+
+int64_t mxfp4_weight_bytes(int G, int K, int N) {
+  return static_cast<int64_t>(G) * ((N + 63) / 64) * ((K + 63) / 64) * 2048;
+}
+
+int64_t mxfp4_scale_bytes(int G, int K, int N) {
+  return static_cast<int64_t>(G) * ((N + 63) / 64) * mx_scale_kblocks(K) * 64;
+}
+
+hipError_t launch_quantize_mxfp4(const bf16_t* w, int G, int K, int N, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t stream) {
+  const int nblk = (N + 63) / 64, kblk = (K + 63) / 64, skb = mx_scale_kblocks(K);
+  const int64_t total = mxfp4_scale_bytes(G, K, N);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(mxfp4_scales_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
+                     dim3(256), 0, stream, w, K, N, nblk, skb, total, scales);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t words = mxfp4_weight_bytes(G, K, N) / 4;
+  hipLaunchKernelGGL(mxfp4_encode_kernel, dim3(static_cast<unsigned>((words + 255) / 256)),
+                     dim3(256), 0, stream, w, K, N, nblk, kblk, skb, words, scales,
+                     reinterpret_cast<uint32_t*>(codes));
+  return hipGetLastError();
+}
 
 int64_t fp8_weight_bytes(int G, int K, int N) {
   return static_cast<int64_t>(G) * ((N + 63) / 64) * ((K + 63) / 64) * 4096;
@@ -1186,6 +1386,18 @@ hipError_t launch_pack_weights(const bf16_t* w, int G, int K, int N, bf16_t* pac
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
   const int tc = tile_class(p);
+  if (p.seg[0].packed == 3) {
+    const bool big = tc == kLarge || tc == kLarge128;
+    if (p.gated)
+      return big ? launch_cfg<GateUpLarge128_4, bf16_t>(p, stream)
+             : tc == kMid ? launch_cfg<GateUpMid4, bf16_t>(p, stream)
+                          : launch_cfg<GateUpSmall4, bf16_t>(p, stream);
+    if (p.out_f32)
+      return big ? launch_cfg<DownLarge128_4, float>(p, stream)
+                 : launch_cfg<DownSmall4, float>(p, stream);
+    return big ? launch_cfg<DownLarge128_4, bf16_t>(p, stream)
+               : launch_cfg<DownSmall4, bf16_t>(p, stream);
+  }
   if (p.seg[0].packed == 2) {
     if (p.gated)
       return tc == kLarge      ? launch_cfg<GateUpLarge8, bf16_t>(p, stream)

@@ -55,11 +55,14 @@ struct GemmSegment {
   int ngroups;
   int K;
   int N;
-  int packed = 0;          // weight layout: 0 [K][N] bf16, 1 packed bf16, 2 packed fp8
+  int packed = 0;          // weight layout: 0 [K][N] bf16, 1 packed bf16, 2 packed fp8,
+                           // 3 packed mxfp4
   // fp8 (packed == 2): E4M3 codes in 4 KB blocks (fp8_weight_bytes), each
-  // group's output columns scaled by scale0/scale1 + g*N (fp32 powers of two)
-  const float* scale0 = nullptr;
-  const float* scale1 = nullptr;
+  // group's output columns scaled by scale0/scale1 + g*N (fp32 powers of two).
+  // mxfp4 (packed == 3): E2M1 codes in 2 KB blocks (mxfp4_weight_bytes) and
+  // E8M0 scale bytes per 32 K-values of a column (mxfp4_scale_bytes).
+  const void* scale0 = nullptr;
+  const void* scale1 = nullptr;
   // Optional row map: activation row of row p is gather[p] (`act` is then
   // the un-permuted [*, K] tensor). Only for the tile classes without item
   // chaining (see grouped_gemm_gathers).
@@ -100,6 +103,17 @@ int64_t packed_weight_elems(int G, int K, int N);
 int64_t fp8_weight_bytes(int G, int K, int N);
 hipError_t launch_quantize_fp8(const bf16_t* w, int G, int K, int N, uint8_t* codes,
                                float* scales, hipStream_t stream);
+
+// MXFP4 weights (OCP microscaling): W [G][K][N] as E2M1 codes in
+// G x ceil(N/64) x ceil(K/64) blocks of 2 KB: [32-row half][64 columns][16
+// bytes], byte h*1024 + c*16 + q*4 + i/2 holding rows kb*64 + h*32 + 8q + i
+// of column nb*64 + c (low nibble: even i), zero past K and N; and one E8M0
+// scale byte per 32 K-values of a column, [G][ceil(N/64)][4*ceil(K/128)][64]
+// (127 = 1.0 past K and N).
+int64_t mxfp4_weight_bytes(int G, int K, int N);
+int64_t mxfp4_scale_bytes(int G, int K, int N);
+hipError_t launch_quantize_mxfp4(const bf16_t* w, int G, int K, int N, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t stream);
 hipError_t launch_pack_weights(const bf16_t* w, int G, int K, int N, bf16_t* packed,
                                hipStream_t stream);
 

@@ -326,6 +326,66 @@ int moe_forward_fp8(const moe_bf16* x, const float* logits, int T, int H, int F,
                     const moe_shared_expert_fp8* shared, moe_bf16* out, int32_t* topk_ids_out,
                     float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- MXFP4 weights ----
+ * The 4-bit weights of the same sections of the DeepGEMM article, read as
+ * the OCP Microscaling format MXFP4: each matrix W [G,K,N] is stored as E2M1
+ * codes (1 sign, 2 exponent bits with bias 1, 1 mantissa bit: magnitudes 0,
+ * 0.5, 1, 1.5, 2, 3, 4, 6) and one E8M0 scale byte per 32 K-values of a
+ * column, the scale 2^X with X = floor(log2(max |W| of the 32)) - 2 (raised
+ * to -125, so dequantized weights stay normal bf16 values; 0 for an all-zero
+ * block). A weight is code_value * 2^X, codes rounded to nearest with ties
+ * to even and saturating at 6. The activations stay bf16: every dequantized
+ * weight is a bf16 value, so a layer on mxfp4 weights is exactly the bf16
+ * layer on the dequantized weights, at 4.25 bits per weight.
+ *
+ * Layout of the codes: G x ceil(N/64) x ceil(K/64) blocks of 2048 bytes,
+ * block (g, nb, kb) at byte ((g*NB + nb)*KB + kb)*2048; within a block, byte
+ * h*1024 + c*16 + q*4 + i/2 holds, in its low nibble for even i and its high
+ * nibble for odd i, the code of W[g, kb*64 + h*32 + 8q + i, nb*64 + c] (zero
+ * past K or N). Scale bytes: [G][ceil(N/64)][4*ceil(K/128)][64], byte
+ * ((g*NB + nb)*SKB + b)*64 + c for column nb*64 + c and K-values 32b ..
+ * 32b+31 (127 past K or N). Both 16-byte aligned; the shared expert's
+ * matrices are quantized as G = 1. */
+
+/* Bytes of the codes and of the scale bytes of a [G,K,N] weight tensor; 0
+ * for invalid sizes. */
+size_t moe_mxfp4_weights_bytes(int G, int K, int N);
+size_t moe_mxfp4_scales_bytes(int G, int K, int N);
+
+/* Quantize bf16 W [G,K,N] (K, N multiples of 8) into codes and scale bytes.
+ * Once, at load time. Errors as moe_quantize_fp8. */
+int moe_quantize_mxfp4(const moe_bf16* w, int G, int K, int N, uint8_t* codes,
+                       size_t codes_bytes, uint8_t* scales, size_t scales_bytes, void* stream);
+
+/* moe_gateup_swiglu / moe_down on mxfp4 weights: equal, bit for bit, to the
+ * bf16 calls on the dequantized weights. */
+int moe_gateup_swiglu_mxfp4(const moe_bf16* x_perm, const int32_t* expert_offsets, int M, int H,
+                            int F, int E, const uint8_t* w_gate, const uint8_t* s_gate,
+                            const uint8_t* w_up, const uint8_t* s_up, moe_bf16* h,
+                            void* stream);
+int moe_down_mxfp4(const moe_bf16* h, const int32_t* expert_offsets, int M, int F, int H, int E,
+                   const uint8_t* w_down, const uint8_t* s_down, moe_bf16* y_perm, void* stream);
+
+/* Shared expert with mxfp4 weights (HOST struct, device pointers). */
+typedef struct {
+  const uint8_t* w_gate;
+  const uint8_t* s_gate;
+  const uint8_t* w_up;
+  const uint8_t* s_up;
+  const uint8_t* w_down;
+  const uint8_t* s_down;
+  int32_t Fs;
+  const float* gate_logits;
+} moe_shared_expert_mxfp4;
+
+/* moe_forward on mxfp4 weights (same workspace and outputs). */
+int moe_forward_mxfp4(const moe_bf16* x, const float* logits, int T, int H, int F, int E, int k,
+                      const uint8_t* w_gate, const uint8_t* s_gate, const uint8_t* w_up,
+                      const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
+                      const moe_shared_expert_mxfp4* shared, moe_bf16* out,
+                      int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif
