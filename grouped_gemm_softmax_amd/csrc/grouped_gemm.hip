@@ -189,6 +189,11 @@ struct TileCfg {
   // MFMA phase and a memory phase (LDS fragment reads, DMA issue), so one of
   // them always feeds the matrix core (8 waves, no fragment prefetch).
   static constexpr bool PP = PP_;
+  // Ping-pong tiles on fp8 codes widen each stage's weights once into a
+  // double-buffered bf16 tile (packed bf16 layout), instead of every wave
+  // widening the fragments it reads.
+  static constexpr bool WIDEN = PP_ && WBITS_ == 8;
+  static constexpr int WW_BYTES = WIDEN ? (GATED_ ? 2 : 1) * BK_ * BF_ * 2 : 1;
   static constexpr int NW = WT * WF;
   static constexpr int kThreads = NW * kWave;
   static constexpr int NMAT = GATED ? 2 : 1;
@@ -228,6 +233,8 @@ struct TileCfg {
   static_assert((PREFETCH ? STAGES : STAGES - 1) * IPW <= 63, "vector-memory counter range");
   static constexpr bool CHAIN_OK = PREFETCH && STAGES * IPW + STORES <= 63;
   static_assert(!PP || (NW == 8 && !PREFETCH), "ping-pong: two waves per SIMD");
+  static_assert(!WIDEN || (BK == 32 && NMAT * SB * 64 * 2 == kThreads && STAGES >= 5),
+                "widening: one 16-code unit per thread, two steps of look-ahead");
 };
 
 // 16-byte chunk swizzles (chunk index within a row), chosen by measuring
@@ -295,6 +302,8 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
   __shared__ __attribute__((aligned(1024))) char st5[C::STAGES > 5 ? C::STAGE_BYTES : 1];
   __shared__ __attribute__((aligned(1024))) char st6[C::STAGES > 6 ? C::STAGE_BYTES : 1];
   __shared__ __attribute__((aligned(1024))) char st7[C::STAGES > 7 ? C::STAGE_BYTES : 1];
+  __shared__ __attribute__((aligned(1024))) char wide0[C::WW_BYTES];  // widened weights
+  __shared__ __attribute__((aligned(1024))) char wide1[C::WW_BYTES];
   // sized at launch: item prefix [groups + 1], then (first row, rows) per
   // group, so that looking up an item reads LDS only (a global load inside
   // the K pipeline would wait for every DMA in flight)
@@ -632,6 +641,29 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     if (KTAIL && s * 32 + 8 * g16 >= kvalid) v = bf16x8{};
     return v;
   };
+  // widened (bf16, packed-layout) weight fragment: [matrix][sub-block]
+  // [64 columns][32 K-values], 16-byte chunk q at q ^ ((c >> 1) & 3)
+  auto wide_frag = [&](const char* wbuf, int m, int fi) INL {
+    const int col = wf * C::TF + fi * 16 + i16;
+    const int c = col & 63;
+    return *reinterpret_cast<const bf16x8*>(wbuf + m * (C::BK * C::BF * 2) + (col >> 6) * 4096 +
+                                            c * 64 + ((g16 ^ ((c >> 1) & 3)) << 4));
+  };
+  // this thread's unit of a stage's fp8 codes (16 codes: two 8-code chunks of
+  // one column's 32) widened into the bf16 tile; unit = thread index, so
+  // threads 0-255 (waves 0-3) cover one half of the stage, 256-511 the other
+  auto widen = [&](const char* codes, char* wbuf) INL {
+    const int cr = tid >> 1, hr = tid & 1;
+    const int m = cr / (C::SB * 64), sb = (cr >> 6) % C::SB, c = cr & 63;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q = 2 * hr + h;
+      const uint2 u = *reinterpret_cast<const uint2*>(codes + m * C::W_BYTES + sb * C::SB_BYTES +
+                                                      c * 32 + ((q ^ ((c >> 2) & 3)) << 3));
+      *reinterpret_cast<bf16x8*>(wbuf + m * (C::BK * C::BF * 2) + sb * 4096 + c * 64 +
+                                 ((q ^ ((c >> 1) & 3)) << 4)) = fp8x8_to_bf16(u);
+    }
+  };
   auto load_frags = [&](const char* buf, Frags& F, int kvalid) INL {
 #pragma unroll
     for (int s = 0; s < C::BK / 32; ++s) {
@@ -751,31 +783,67 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
   };
   // (Chaining items as the decode tiles do measured 1 % slower here: items
   // are long, and the chained start must also wait for the epilogue's stores.)
+  // Widening (C::WIDEN): the memory phase M(t) also converts this group's
+  // half of step t+1's codes into the bf16 tile wide[(t+1) % 2] and reads
+  // step t's weight fragments from wide[t % 2]. Step t+1's codes must have
+  // landed for every wave before interval 2t, so each wave waits for its DMA
+  // of step t+2 in M(t) (step t+1's in M(t-1)); the prologue lands steps 0
+  // and 1 and widens step 0. wide[(t+1) % 2] last held step t-1, read in
+  // intervals 2t-2 and 2t-1; step t+1's halves are written in 2t and 2t+1
+  // and read from 2t+2 on. The ring buffer refilled in M(t) held step t-1,
+  // whose codes were widened in M(t-2) and its activations read in M(t-1).
   auto run_pingpong = [&](const ItemInfo& cur) INL {
     constexpr int DP = S - 1;
+    constexpr bool WD = C::WIDEN;
+    constexpr int PTURN = (WD && S % 2 == 1) ? 2 * S : S;  // wide buffer = step parity
     const bool grp1 = wave >= 4;
     wait_vmcnt<0>();               // the last item's stores and DMAs are done and
     __builtin_amdgcn_s_barrier();  // every wave has finished reading the ring
     static_for<DP>([&](auto I) INL { issue(cur, cur.kt_begin + decltype(I)::value, stage_buf(I)); });
-    wait_vmcnt<(DP - 1) * C::IPW>();
-    pp_barrier();                  // K-step 0 has landed for every wave
+    if constexpr (WD) {
+      wait_vmcnt<(DP - 2) * C::IPW>();
+      pp_barrier();                // K-steps 0 and 1 have landed for every wave
+      widen(st0, wide0);
+      wait_vmcnt_lgkm0<63>();
+    } else {
+      wait_vmcnt<(DP - 1) * C::IPW>();
+    }
+    pp_barrier();                  // K-step 0 has landed (and is widened) for every wave
     if (grp1) pp_barrier();
     auto pp_step = [&](int t, auto I) INL {
       constexpr int i = decltype(I)::value;
-      load_frags(stage_buf(I), fa, cur.K - (cur.kt_begin + t) * C::BK);
-      wait_vmcnt<(DP - 2) * C::IPW>();  // this wave's DMA of step t+1 has landed
+      if constexpr (WD) {
+        char* const wcur = i % 2 == 0 ? wide0 : wide1;
+        char* const wnext = i % 2 == 0 ? wide1 : wide0;
+        // widen step t+1 first, so its temporaries are dead before the
+        // fragments are read (registers)
+        widen(stage_buf(std::integral_constant<int, i + 1>{}), wnext);
+        __builtin_amdgcn_sched_barrier(0);
+        const char* const sb = stage_buf(I);
+        const int kvalid = cur.K - (cur.kt_begin + t) * C::BK;
+#pragma unroll
+        for (int ti = 0; ti < C::FT; ++ti) fa.b[0][ti] = act_frag(sb, 0, ti, kvalid);
+#pragma unroll
+        for (int fi = 0; fi < C::FF; ++fi)
+#pragma unroll
+          for (int m = 0; m < C::NMAT; ++m) fa.a[0][m][fi] = wide_frag(wcur, m, fi);
+        wait_vmcnt<(DP - 3) * C::IPW>();  // this wave's DMA of step t+2 has landed
+      } else {
+        load_frags(stage_buf(I), fa, cur.K - (cur.kt_begin + t) * C::BK);
+        wait_vmcnt<(DP - 2) * C::IPW>();  // this wave's DMA of step t+1 has landed
+      }
       issue(cur, cur.kt_begin + t + DP, stage_buf(std::integral_constant<int, i + DP>{}));
-      wait_vmcnt_lgkm0<63>();           // fragments in registers
+      wait_vmcnt_lgkm0<63>();           // fragments in registers (and widened codes written)
       pp_barrier();
       mfma(fa);
       pp_barrier();
     };
-    const int full = cur.nk / S;
+    const int full = cur.nk / PTURN;
     int t = 0;
-    for (int turn = 0; turn < full; ++turn, t += S)
-      static_for<S>([&](auto I) INL { pp_step(t + decltype(I)::value, I); });
+    for (int turn = 0; turn < full; ++turn, t += PTURN)
+      static_for<PTURN>([&](auto I) INL { pp_step(t + decltype(I)::value, I); });
     const int rem = cur.nk - t;
-    static_for<S - 1>([&](auto I) INL {
+    static_for<PTURN - 1>([&](auto I) INL {
       if (decltype(I)::value < rem) pp_step(t + decltype(I)::value, I);
     });
     if (!grp1) pp_barrier();
@@ -1399,17 +1467,21 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
                : launch_cfg<DownSmall4, bf16_t>(p, stream);
   }
   if (p.seg[0].packed == 2) {
+    // the widening 256-row tiles leave ~8 KB of LDS for the per-group item
+    // table (12 bytes a group): with more groups the 128-row tiles serve
+    const int groups = p.seg[0].ngroups + (p.nseg > 1 ? p.seg[1].ngroups : 0);
+    const int tc8 = (tc == kLarge && groups > 600) ? static_cast<int>(kLarge128) : tc;
     if (p.gated)
-      return tc == kLarge      ? launch_cfg<GateUpLarge8, bf16_t>(p, stream)
-             : tc == kLarge128 ? launch_cfg<GateUpLarge128_8, bf16_t>(p, stream)
-             : tc == kMid      ? launch_cfg<GateUpMid8, bf16_t>(p, stream)
+      return tc8 == kLarge      ? launch_cfg<GateUpLarge8, bf16_t>(p, stream)
+             : tc8 == kLarge128 ? launch_cfg<GateUpLarge128_8, bf16_t>(p, stream)
+             : tc8 == kMid      ? launch_cfg<GateUpMid8, bf16_t>(p, stream)
                                : launch_cfg<GateUpSmall8, bf16_t>(p, stream);
     if (p.out_f32)
-      return tc == kLarge      ? launch_cfg<DownLarge8, float>(p, stream)
-             : tc == kLarge128 ? launch_cfg<DownLarge128_8, float>(p, stream)
+      return tc8 == kLarge      ? launch_cfg<DownLarge8, float>(p, stream)
+             : tc8 == kLarge128 ? launch_cfg<DownLarge128_8, float>(p, stream)
                                : launch_cfg<DownSmall8, float>(p, stream);
-    return tc == kLarge      ? launch_cfg<DownLarge8, bf16_t>(p, stream)
-           : tc == kLarge128 ? launch_cfg<DownLarge128_8, bf16_t>(p, stream)
+    return tc8 == kLarge      ? launch_cfg<DownLarge8, bf16_t>(p, stream)
+           : tc8 == kLarge128 ? launch_cfg<DownLarge128_8, bf16_t>(p, stream)
                              : launch_cfg<DownSmall8, bf16_t>(p, stream);
   }
   if (p.gated)

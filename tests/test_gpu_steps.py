@@ -32,6 +32,9 @@ CASES = {
     "large128_tiles": (synth.small_config("l128", H=2048, F=64, E=64, k=4), 1600, None),
     # >= 192 rows per expert: the 256-row large tiles, with ragged K and N
     "ragged_large256": (synth.small_config("rl256", H=200, F=328, E=4, k=2), 500, None),
+    # ... and with K a whole number of steps (the ping-pong tiles' main path,
+    # fp8's widening one included)
+    "large256_whole_k": (synth.small_config("l256", H=256, F=384, E=4, k=2), 500, None),
 }
 
 
