@@ -551,6 +551,154 @@ done:
   return rc;
 }
 
+/* ---------------------------------------------------------------- backward */
+
+/* Training backward of the routed layer (the grouped-GEMM news page says the
+ * kernel serves training as well as inference; the pages give no backward,
+ * so this is the derivative of the forward above, by the chain rule). With
+ * the routing (ids, w) fixed and out[t] = sum_j w[t,j] y(t,j),
+ * y = h W_down[e], h = silu(G) * U, G = x W_gate[e], U = x W_up[e]:
+ *   dw[t,j]   = <dout[t], y(t,j)>
+ *   dy        = w[t,j] dout[t]
+ *   dh[f]     = sum_c dy[c] W_down[e][f][c]
+ *   dG        = dh U silu'(G),  silu'(z) = s(z) (1 + z (1 - s(z))), s the logistic
+ *   dU        = dh silu(G)
+ *   dx[t]     = sum_j (dG W_gate[e]^T + dU W_up[e]^T)          (j ascending)
+ *   dW_gate[e] = sum over e's rows of x^T dG, dW_up[e] likewise with dU,
+ *   dW_down[e] = sum over e's rows of h^T dy                      (rows ascending)
+ * x, weights and dout bf16, w fp32, everything else fp64. */
+int oracle_backward(const uint16_t* x, const int32_t* ids, const float* w, int64_t T, int H,
+                    int F, int E, int k, const uint16_t* wg, const uint16_t* wu,
+                    const uint16_t* wd, const uint16_t* dout, double* dx, double* dw,
+                    double* dwg, double* dwu, double* dwd) {
+  if (T < 0 || H < 1 || F < 1 || E < 1 || k < 1 || k > E) return ORC_ERR_ARG;
+  const int64_t A = T * k;
+  int rc = ORC_ERR_NOMEM;
+  int32_t* offsets = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
+  int32_t* row_token = (int32_t*)malloc(sizeof(int32_t) * (size_t)(A + 1));
+  int32_t* row_dest = (int32_t*)malloc(sizeof(int32_t) * (size_t)(A + 1));
+  int32_t* row_slot = (int32_t*)malloc(sizeof(int32_t) * (size_t)(A + 1));
+  double* hr = (double*)malloc(sizeof(double) * (size_t)(A * F + 1));
+  double* dGr = (double*)malloc(sizeof(double) * (size_t)(A * F + 1));
+  double* dUr = (double*)malloc(sizeof(double) * (size_t)(A * F + 1));
+  double* dyr = (double*)malloc(sizeof(double) * (size_t)(A * H + 1));
+  double* dxr = (double*)malloc(sizeof(double) * (size_t)(A * H + 1));
+  if (!offsets || !row_token || !row_dest || !row_slot || !hr || !dGr || !dUr || !dyr || !dxr)
+    goto done;
+  for (int64_t i = 0; i < A; ++i)
+    if (ids[i] < 0 || ids[i] >= E) { rc = ORC_ERR_ARG; goto done; }
+  rc = oracle_permute(ids, T, E, k, offsets, row_token, row_dest);
+  if (rc) goto done;
+  for (int64_t i = 0; i < A; ++i) row_slot[row_dest[i]] = (int32_t)(i % k);
+  rc = ORC_OK;
+  /* per assignment row: forward, then the row's backward */
+#pragma omp parallel
+  {
+    double* G = (double*)malloc(sizeof(double) * (size_t)F * 2);
+    double* y = (double*)malloc(sizeof(double) * (size_t)H);
+    double* dh = (double*)malloc(sizeof(double) * (size_t)F);
+    if (!G || !y || !dh) {
+#pragma omp atomic write
+      rc = ORC_ERR_NOMEM;
+    } else {
+      double* U = G + F;
+#pragma omp for schedule(static)
+      for (int64_t p = 0; p < A; ++p) {
+        const int64_t t = row_token[p];
+        const int j = row_slot[p];
+        int e = 0;
+        while (offsets[e + 1] <= p) ++e;
+        const uint16_t* xt = x + t * H;
+        const uint16_t* wge = wg + (int64_t)e * H * F;
+        const uint16_t* wue = wu + (int64_t)e * H * F;
+        const uint16_t* wde = wd + (int64_t)e * F * H;
+        double* h = hr + p * F;
+        gateup_row(xt, H, F, wge, wue, h, G, U);
+        down_row(h, F, H, wde, y);
+        const double wj = (double)w[t * k + j];
+        double d = 0.0;
+        for (int c = 0; c < H; ++c) d += bf16_to_f64(dout[t * H + c]) * y[c];
+        dw[t * k + j] = d;
+        double* dy = dyr + p * H;
+        for (int c = 0; c < H; ++c) dy[c] = wj * bf16_to_f64(dout[t * H + c]);
+        for (int f = 0; f < F; ++f) {
+          double a = 0.0;
+          const uint16_t* rd = wde + (int64_t)f * H;
+          for (int c = 0; c < H; ++c) a += dy[c] * bf16_to_f64(rd[c]);
+          dh[f] = a;
+        }
+        double* dG = dGr + p * F;
+        double* dU = dUr + p * F;
+        for (int f = 0; f < F; ++f) {
+          const double z = G[f], sg = 1.0 / (1.0 + exp(-z));
+          dG[f] = dh[f] * U[f] * sg * (1.0 + z * (1.0 - sg));
+          dU[f] = dh[f] * silu(z);
+        }
+        double* dxp = dxr + p * H;
+        for (int i = 0; i < H; ++i) {
+          double a = 0.0;
+          const uint16_t* rg = wge + (int64_t)i * F;
+          const uint16_t* ru = wue + (int64_t)i * F;
+          for (int f = 0; f < F; ++f) a += dG[f] * bf16_to_f64(rg[f]) + dU[f] * bf16_to_f64(ru[f]);
+          dxp[i] = a;
+        }
+      }
+    }
+    free(G); free(y); free(dh);
+  }
+  if (rc) goto done;
+  /* dx: the k rows of each token, slots ascending */
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    for (int i = 0; i < H; ++i) {
+      double a = 0.0;
+      for (int j = 0; j < k; ++j) a += dxr[(int64_t)row_dest[t * k + j] * H + i];
+      dx[t * H + i] = a;
+    }
+  /* weight gradients: each expert's rows in ascending order */
+#pragma omp parallel for schedule(dynamic)
+  for (int e = 0; e < E; ++e) {
+    double* gg = dwg + (int64_t)e * H * F;
+    double* gu = dwu + (int64_t)e * H * F;
+    double* gd = dwd + (int64_t)e * F * H;
+    for (int64_t i = 0; i < (int64_t)H * F; ++i) gg[i] = 0.0, gu[i] = 0.0, gd[i] = 0.0;
+    for (int64_t p = offsets[e]; p < offsets[e + 1]; ++p) {
+      const uint16_t* xp = x + (int64_t)row_token[p] * H;
+      const double* dG = dGr + p * F;
+      const double* dU = dUr + p * F;
+      const double* h = hr + p * F;
+      const double* dy = dyr + p * H;
+      for (int i = 0; i < H; ++i) {
+        const double xv = bf16_to_f64(xp[i]);
+        for (int f = 0; f < F; ++f) {
+          gg[(int64_t)i * F + f] += xv * dG[f];
+          gu[(int64_t)i * F + f] += xv * dU[f];
+        }
+      }
+      for (int f = 0; f < F; ++f)
+        for (int c = 0; c < H; ++c) gd[(int64_t)f * H + c] += h[f] * dy[c];
+    }
+  }
+done:
+  free(offsets); free(row_token); free(row_dest); free(row_slot);
+  free(hr); free(dGr); free(dUr); free(dyr); free(dxr);
+  return rc;
+}
+
+/* Backward of the routing weights: w = softmax over the k selected logits,
+ * so dl[t, ids[t,j]] = w_j (dw_j - sum_i w_i dw_i) (i ascending) and 0 for
+ * the experts not selected. dl [T,E] fp64. */
+void oracle_route_backward(const int32_t* ids, const float* w, const double* dw, int64_t T,
+                           int E, int k, double* dl) {
+  for (int64_t t = 0; t < T; ++t) {
+    double s = 0.0;
+    for (int j = 0; j < k; ++j) s += (double)w[t * k + j] * dw[t * k + j];
+    for (int e = 0; e < E; ++e) dl[t * E + e] = 0.0;
+    for (int j = 0; j < k; ++j)
+      dl[t * E + ids[t * k + j]] = (double)w[t * k + j] * (dw[t * k + j] - s);
+  }
+}
+
 /* Output rows of selected tokens only. Every token's output depends on that
  * token alone, so out[i] for token tokens[i] equals row tokens[i] of
  * oracle_forward; it is computed here with the same per-row functions, one

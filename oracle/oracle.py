@@ -80,6 +80,10 @@ def lib():
         L.oracle_forward_tokens.argtypes = ([_P, _P, _I64, _I, _I, _I, _I, _P,
                                              _P, _P, _I, _P, _P, _P, _P, _P,
                                              _I64, _P, _P, _P])
+        L.oracle_backward.argtypes = [_P, _P, _P, _I64, _I, _I, _I, _I, _P, _P, _P, _P,
+                                      _P, _P, _P, _P, _P]
+        L.oracle_route_backward.argtypes = [_P, _P, _P, _I64, _I, _I, _P]
+        L.oracle_route_backward.restype = None
         _lib = L
     return _lib
 
@@ -183,6 +187,34 @@ def dequant_mxfp4(codes: np.ndarray, scale_bytes: np.ndarray) -> np.ndarray:
     out = np.empty((G, K, N), np.float64)
     lib().oracle_dequant_mxfp4(_p(codes), _p(scale_bytes), G, K, N, _p(out))
     return out[0] if squeeze else out
+
+
+def backward(x, ids, w, wg, wu, wd, dout):
+    """Backward of the routed layer for a fixed routing (ids int32 [T,k], w
+    fp32 [T,k]); x, weights, dout bf16. Returns dict(dx [T,H], dw [T,k],
+    dwg [E,H,F], dwu [E,H,F], dwd [E,F,H]), float64."""
+    x = _c(x, np.uint16)
+    ids, w = _c(ids, np.int32), _c(w, np.float32)
+    wg, wu, wd = _c(wg, np.uint16), _c(wu, np.uint16), _c(wd, np.uint16)
+    dout = _c(dout, np.uint16)
+    T, H = x.shape
+    k = ids.shape[1]
+    E, _, F = wg.shape
+    r = dict(dx=np.empty((T, H)), dw=np.empty((T, k)), dwg=np.empty((E, H, F)),
+             dwu=np.empty((E, H, F)), dwd=np.empty((E, F, H)))
+    _check(lib().oracle_backward(_p(x), _p(ids), _p(w), T, H, F, E, k, _p(wg), _p(wu), _p(wd),
+                                 _p(dout), _p(r["dx"]), _p(r["dw"]), _p(r["dwg"]), _p(r["dwu"]),
+                                 _p(r["dwd"])), "backward")
+    return r
+
+
+def route_backward(ids, w, dw, E: int) -> np.ndarray:
+    """d logits [T,E] of the softmax over the k selected logits."""
+    ids, w, dw = _c(ids, np.int32), _c(w, np.float32), _c(dw, np.float64)
+    T, k = ids.shape
+    dl = np.empty((T, E))
+    lib().oracle_route_backward(_p(ids), _p(w), _p(dw), T, E, k, _p(dl))
+    return dl
 
 
 def route(logits: np.ndarray, k: int):
