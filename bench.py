@@ -23,6 +23,7 @@ scales (moe_forward_fp8; bf16 activations and MFMA), which computes exactly
 the bf16 layer on the dequantized weights at half the weight bytes.
 `--router` instead times the router projection fused with routing
 (moe_router_route) at every layer shape, against the unfused sequence.
+`--backward` times the training backward (moe_backward) of --config at --T.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -67,6 +68,10 @@ def parse():
                     help="only time the router row: moe_router_route (router GEMM + "
                          "top-k routing) against torch's matmul + fp32 cast + moe_route, "
                          "for every layer shape, one JSON line each, and exit")
+    ap.add_argument("--backward", action="store_true",
+                    help="only time the training backward (moe_backward: forward "
+                         "recompute, dx and the weight gradients) at --config/--T against "
+                         "the forward on the same row-major weights, one JSON line, and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (the "
                          "known-size reference for HBM byte counters) and exit")
@@ -188,6 +193,58 @@ def router_table(args, torch, B, synth):
               flush=True)
 
 
+def backward_line(args, torch, B, synth):
+    """moe_backward of the routed layer at one batch size: HIP events around
+    `steps` calls on the launch stream. Its work is nine A*H*F products
+    (2*A*H*F FLOPs each, A = T*k): the recomputed forward (gate, up, down),
+    dh, the two dx products and the three weight gradients."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.CONFIGS[args.config]
+    T, H, F, E, k = args.T, cfg.H, cfg.F, cfg.E, cfg.k
+    stream = torch.cuda.current_stream()
+    layer = synth.make_layer(cfg.name, T, seed=args.seed, device=dev, with_shared=False)
+    ids, w = B.moe_route(layer.logits, k, stream=stream)
+    g = torch.Generator(device=dev).manual_seed(args.seed + 1)
+    dout = torch.randn((T, H), generator=g, device=dev).to(torch.bfloat16)
+    ws = torch.empty(B.moe_backward_workspace_bytes(T, H, F, E, k), dtype=torch.uint8,
+                     device=dev)
+    fws = torch.empty(B.moe_forward_workspace_bytes(T, H, F, E, k, 0), dtype=torch.uint8,
+                      device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def bwd():
+        B.moe_backward(layer.x, ids, w, layer.w_gate, layer.w_up, layer.w_down, dout, ws=ws,
+                       stream=stream)
+
+    def fwd():
+        B.moe_forward_routed(layer.x, ids, w, layer.w_gate, layer.w_up, layer.w_down,
+                             out=out, ws=fws, stream=stream)
+
+    def timed(fn, n, warm):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / n
+
+    ms_b = timed(bwd, args.steps, args.warmup)
+    ms_f = timed(fwd, args.steps, args.warmup)
+    A = T * k
+    flops = 9 * 2 * A * H * F
+    print(json.dumps({"backward": cfg.name, "T": T, "H": H, "F": F, "E": E, "k": k,
+                      "ms": round(ms_b, 4), "TFLOPs": round(flops / ms_b / 1e9, 1),
+                      "mfma_frac": round(flops / ms_b / 1e9 / PEAK_BF16_TFLOPS, 4),
+                      "forward_rowmajor_ms": round(ms_f, 4), "alg_flops": flops,
+                      "workspace_bytes": ws.numel(), "dtype": "bf16 (fp32 weight gradients)",
+                      "data": "synthetic"}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -215,6 +272,9 @@ def main():
     if args.router:
         torch.cuda.set_device(0)
         router_table(args, torch, B, synth)
+        return
+    if args.backward:
+        backward_line(args, torch, B, synth)
         return
 
     dev = torch.device("cuda:0")

@@ -87,6 +87,10 @@ _SIGNATURES = {
     "moe_down_mxfp4": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_forward_mxfp4": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
                                ctypes.POINTER(SharedExpertMxfp4), _P, _P, _P, _P, _SZ, _P]),
+    "moe_backward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "moe_backward": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                          _P, _P, _SZ, _P]),
+    "moe_route_backward": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
 }
 
 _lib = None
@@ -522,3 +526,51 @@ def _forward_quant(x, logits, k, w_gate, w_up, w_down, shared, out, topk_ids, to
         ctypes.byref(sh) if sh is not None else None, _ptr(out), _ptr(topk_ids), _ptr(topk_w),
         _ptr(ws), ws.numel(), _stream(stream)), name)
     return out
+
+
+def moe_backward_workspace_bytes(T, H, F, E, k) -> int:
+    return int(lib().moe_backward_workspace_bytes(T, H, F, E, k))
+
+
+def moe_backward(x, topk_ids, topk_w, w_gate, w_up, w_down, dout, ws=None, stream=None):
+    """Gradients of the routed layer (row-major bf16 weights) for the routing
+    (topk_ids int32 [T,k], topk_w fp32 [T,k]) and the output gradient dout
+    [T,H] bf16. Returns dict(dx [T,H] bf16, d_topk_w [T,k] fp32, dw_gate,
+    dw_up [E,H,F] fp32, dw_down [E,F,H] fp32)."""
+    for n, t, dt in (("x", x, torch.bfloat16), ("topk_ids", topk_ids, torch.int32),
+                     ("topk_w", topk_w, torch.float32), ("w_gate", w_gate, torch.bfloat16),
+                     ("w_up", w_up, torch.bfloat16), ("w_down", w_down, torch.bfloat16),
+                     ("dout", dout, torch.bfloat16)):
+        _need(t, dt, n)
+    T, H = x.shape
+    E, _, F = w_gate.shape
+    k = topk_ids.shape[1]
+    dev = x.device
+    g = dict(dx=torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+             d_topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+             dw_gate=torch.empty((E, H, F), dtype=torch.float32, device=dev),
+             dw_up=torch.empty((E, H, F), dtype=torch.float32, device=dev),
+             dw_down=torch.empty((E, F, H), dtype=torch.float32, device=dev))
+    if ws is None:
+        ws = torch.empty(max(moe_backward_workspace_bytes(T, H, F, E, k), 16),
+                         dtype=torch.uint8, device=dev)
+    _check(lib().moe_backward(_ptr(x), _ptr(topk_ids), _ptr(topk_w), T, H, F, E, k,
+                              _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(dout),
+                              _ptr(g["dx"]), _ptr(g["d_topk_w"]), _ptr(g["dw_gate"]),
+                              _ptr(g["dw_up"]), _ptr(g["dw_down"]), _ptr(ws), ws.numel(),
+                              _stream(stream)), "moe_backward")
+    return g
+
+
+def moe_route_backward(topk_ids, topk_w, d_topk_w, E, d_logits=None, stream=None):
+    """Router-logit gradient [T,E] fp32 through the softmax over the k
+    selected logits."""
+    _need(topk_ids, torch.int32, "topk_ids")
+    _need(topk_w, torch.float32, "topk_w")
+    _need(d_topk_w, torch.float32, "d_topk_w")
+    T, k = topk_ids.shape
+    if d_logits is None:
+        d_logits = torch.empty((T, E), dtype=torch.float32, device=topk_ids.device)
+    _check(lib().moe_route_backward(_ptr(topk_ids), _ptr(topk_w), _ptr(d_topk_w), T, E, k,
+                                    _ptr(d_logits), _stream(stream)), "moe_route_backward")
+    return d_logits

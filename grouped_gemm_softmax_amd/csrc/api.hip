@@ -658,4 +658,157 @@ int moe_forward_routed(const moe_bf16* x, const int32_t* topk_ids, const float* 
                       out, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
+
+// ---- training backward ------------------------------------------------------
+// Workspace of moe_backward (each piece 256-byte aligned from ws):
+// [hist | offsets | row_token | row_dest | x_perm | h | G | U | dy | dG | dU |
+//  y (fp32) | dx parts (fp32, 2 slices)].
+struct BackwardLayout {
+  size_t hist, offsets, row_token, row_dest, x_perm, h, g, u, dy, dg, du, y, dxp, total;
+};
+
+static BackwardLayout backward_layout(int T, int H, int F, int E, int k) {
+  BackwardLayout L;
+  const size_t A = static_cast<size_t>(T) * k;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+  L.hist = take(static_cast<size_t>(moe::route_num_chunks(T, k)) * E * 4);
+  L.offsets = take((static_cast<size_t>(E) + 1) * 4);
+  L.row_token = take(A * 4);
+  L.row_dest = take(A * 4);
+  L.x_perm = take(A * H * 2);
+  L.h = take(A * F * 2);
+  L.g = take(A * F * 2);
+  L.u = take(A * F * 2);
+  L.dy = take(A * H * 2);
+  L.dg = take(A * F * 2);
+  L.du = take(A * F * 2);
+  L.y = take(A * H * 4);
+  L.dxp = take(2 * A * H * 4);
+  L.total = o;
+  return L;
+}
+
+size_t moe_backward_workspace_bytes(int T, int H, int F, int E, int k) {
+  if (check_dims(T, E, k) != MOE_OK || check_width(H) != MOE_OK || check_width(F) != MOE_OK)
+    return 0;
+  return backward_layout(T, H, F, E, k).total;
+}
+
+int moe_backward(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w, int T, int H,
+                 int F, int E, int k, const moe_bf16* w_gate, const moe_bf16* w_up,
+                 const moe_bf16* w_down, const moe_bf16* dout, moe_bf16* dx, float* d_topk_w,
+                 float* dw_gate, float* dw_up, float* dw_down, void* ws, size_t ws_bytes,
+                 void* stream) {
+  MOE_TRY(check_dims(T, E, k));
+  MOE_TRY(check_width(H));
+  MOE_TRY(check_width(F));
+  const int64_t A = static_cast<int64_t>(T) * k;
+  MOE_TRY(check_elems(A, H > F ? H : F));
+  if (static_cast<int64_t>(H) * F >= kIndexLimit) return MOE_ERR_UNSUPPORTED_SHAPE;
+  MOE_TRY(need_word(dw_gate));
+  MOE_TRY(need_word(dw_up));
+  MOE_TRY(need_word(dw_down));
+  if (T > 0) {
+    MOE_TRY(need_bf16(x));
+    MOE_TRY(need_word(topk_ids));
+    MOE_TRY(need_word(topk_w));
+    MOE_TRY(need_bf16(w_gate));
+    MOE_TRY(need_bf16(w_up));
+    MOE_TRY(need_bf16(w_down));
+    MOE_TRY(need_bf16(dout));
+    MOE_TRY(need_bf16(dx));
+    MOE_TRY(need_word(d_topk_w));
+    MOE_TRY(need_bf16(ws));
+  }
+  const BackwardLayout L = backward_layout(T, H, F, E, k);
+  if (T > 0 && ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {
+    // no tokens: every weight gradient is zero
+    using moe::launch_kgrouped_gemm;
+    MOE_TRY(hip_status(launch_kgrouped_gemm(nullptr, nullptr, nullptr, E, H, F, dw_gate, s)));
+    MOE_TRY(hip_status(launch_kgrouped_gemm(nullptr, nullptr, nullptr, E, H, F, dw_up, s)));
+    return hip_status(launch_kgrouped_gemm(nullptr, nullptr, nullptr, E, F, H, dw_down, s));
+  }
+  char* base = static_cast<char*>(ws);
+  int32_t* hist = reinterpret_cast<int32_t*>(base + L.hist);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  int32_t* row_token = reinterpret_cast<int32_t*>(base + L.row_token);
+  int32_t* row_dest = reinterpret_cast<int32_t*>(base + L.row_dest);
+  bf16_t* x_perm = reinterpret_cast<bf16_t*>(base + L.x_perm);
+  bf16_t* h = reinterpret_cast<bf16_t*>(base + L.h);
+  bf16_t* g = reinterpret_cast<bf16_t*>(base + L.g);
+  bf16_t* u = reinterpret_cast<bf16_t*>(base + L.u);
+  bf16_t* dy = reinterpret_cast<bf16_t*>(base + L.dy);
+  bf16_t* dg = reinterpret_cast<bf16_t*>(base + L.dg);
+  bf16_t* du = reinterpret_cast<bf16_t*>(base + L.du);
+  float* y = reinterpret_cast<float*>(base + L.y);
+  float* dxp = reinterpret_cast<float*>(base + L.dxp);
+  const int M = static_cast<int>(A);
+
+  // forward recompute: permutation (x_perm is kept for the weight
+  // gradients), gate/up storing G and U beside h, down into fp32 y
+  MOE_TRY(hip_status(moe::launch_hist(topk_ids, T, E, k, hist, s)));
+  MOE_TRY(hip_status(moe::launch_permute(x, topk_ids, T, H, E, k, hist, offsets, row_token,
+                                         row_dest, x_perm, s)));
+  moe::GemmProblem g1 =
+      gateup_problem(x_perm, offsets, M, H, F, E, w_gate, w_up, h, kRowMajor);
+  g1.epi = moe::kStoreGUH;
+  g1.seg[0].out2 = g;
+  g1.seg[0].out3 = u;
+  MOE_TRY(hip_status(moe::launch_grouped_gemm(g1, s)));
+  moe::GemmProblem g2 = down_problem(h, offsets, M, F, H, E, w_down, y, kRowMajor);
+  g2.out_f32 = true;
+  MOE_TRY(hip_status(moe::launch_grouped_gemm(g2, s)));
+  // combine backward: dy = w dout per row, d_topk_w = <dout, y>
+  MOE_TRY(hip_status(
+      moe::launch_combine_backward(dout, y, row_dest, topk_w, T, H, k, dy, d_topk_w, s)));
+  // dh = dy W_down^T (W_down [F][H] is the [N][K] operand), with the SwiGLU
+  // backward in the epilogue: dG, dU
+  moe::GemmProblem g3{};
+  g3.seg[0] = segment(dy, offsets, w_down, nullptr, dg, M, E, H, F, moe::kWeightsTransposed,
+                      nullptr, nullptr);
+  g3.seg[0].aux0 = g;
+  g3.seg[0].aux1 = u;
+  g3.seg[0].out2 = du;
+  g3.nseg = 1;
+  g3.gated = false;
+  g3.rows_hint = M / E;
+  g3.epi = moe::kSwigluBwd;
+  MOE_TRY(hip_status(moe::launch_grouped_gemm(g3, s)));
+  // dx: dG W_gate^T and dU W_up^T per row (fp32 slices), summed over the
+  // token's k rows and the two slices by the combine with unit weights
+  for (int part = 0; part < 2; ++part) {
+    moe::GemmProblem g4{};
+    g4.seg[0] = segment(part ? du : dg, offsets, part ? w_up : w_gate, nullptr,
+                        dxp + static_cast<int64_t>(part) * M * H, M, E, F, H,
+                        moe::kWeightsTransposed, nullptr, nullptr);
+    g4.nseg = 1;
+    g4.gated = false;
+    g4.out_f32 = true;
+    g4.rows_hint = M / E;
+    MOE_TRY(hip_status(moe::launch_grouped_gemm(g4, s)));
+  }
+  MOE_TRY(hip_status(moe::launch_combine(dxp, true, 2, static_cast<int64_t>(M) * H, row_dest,
+                                         nullptr, T, H, k, nullptr, 1, 0, nullptr, dx, s)));
+  // weight gradients over each expert's rows
+  MOE_TRY(hip_status(moe::launch_kgrouped_gemm(x_perm, dg, offsets, E, H, F, dw_gate, s)));
+  MOE_TRY(hip_status(moe::launch_kgrouped_gemm(x_perm, du, offsets, E, H, F, dw_up, s)));
+  return hip_status(moe::launch_kgrouped_gemm(h, dy, offsets, E, F, H, dw_down, s));
+}
+
+int moe_route_backward(const int32_t* topk_ids, const float* topk_w, const float* d_topk_w,
+                       int T, int E, int k, float* d_logits, void* stream) {
+  MOE_TRY(check_dims(T, E, k));
+  MOE_TRY(check_elems(T, E));
+  if (T == 0) return MOE_OK;
+  MOE_TRY(need_word(topk_ids));
+  MOE_TRY(need_word(topk_w));
+  MOE_TRY(need_word(d_topk_w));
+  MOE_TRY(need_word(d_logits));
+  return hip_status(moe::launch_route_backward(topk_ids, topk_w, d_topk_w, T, E, k, d_logits,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

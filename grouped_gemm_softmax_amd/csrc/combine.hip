@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     int p = row_dest[static_cast<int64_t>(t) * k + threadIdx.x];
     p = p < 0 ? 0 : (p >= A ? static_cast<int>(A - 1) : p);  // stay in bounds
     s_row[threadIdx.x] = p;
-    s_w[threadIdx.x] = topk_w[static_cast<int64_t>(t) * k + threadIdx.x];
+    s_w[threadIdx.x] = topk_w ? topk_w[static_cast<int64_t>(t) * k + threadIdx.x] : 1.0f;
   }
   __syncthreads();
   float s = 1.0f;

@@ -290,7 +290,7 @@ __device__ __forceinline__ void store4(float* p, const float v[4]) {
   *reinterpret_cast<float4*>(p) = float4{v[0], v[1], v[2], v[3]};
 }
 
-template <class C, typename OutT, bool KTAIL, bool PACKED>
+template <class C, typename OutT, bool KTAIL, bool PACKED, bool TRANSW = false>
 __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel(
     GemmProblem prob) {
   __shared__ __attribute__((aligned(1024))) char st0[C::STAGE_BYTES];
@@ -386,6 +386,10 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     const bf16_t* w1;
     const bf16_t* x;  // activations of the tile's first row (x itself when gathering)
     OutT* out;        // output of this item's K-slice
+    bf16_t* out2;     // backward epilogues: second and third outputs, G and U inputs
+    bf16_t* out3;
+    const bf16_t* aux0;
+    const bf16_t* aux1;
     int K, N;
     int n0;           // first output column
     int row_base;     // first activation row
@@ -439,6 +443,10 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     // gathered rows: row p of the group's block is activation row S.gather[p]
     it.x = S.gather ? S.act : S.act + static_cast<int64_t>(it.row_base) * it.K;
     it.out = static_cast<OutT*>(S.out) + static_cast<int64_t>(ks) * S.slice_stride;
+    it.out2 = uniform(static_cast<bf16_t*>(S.out2));
+    it.out3 = uniform(static_cast<bf16_t*>(S.out3));
+    it.aux0 = uniform(S.aux0);
+    it.aux1 = uniform(S.aux1);
     if constexpr (FP8) {
       it.sc0 = static_cast<const float*>(S.scale0) + static_cast<int64_t>(v.local) * S.N;
       it.sc1 = C::GATED ? static_cast<const float*>(S.scale1) + static_cast<int64_t>(v.local) * S.N
@@ -481,6 +489,16 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
           const int col = min(it.n0 + (jj / IPS) * 64 + swz_w(r, lane % 8) * 8, it.N - 8);
           it.voff[i] = PACKED ? static_cast<uint32_t>(lane) * 16u
                                  : static_cast<uint32_t>(r * it.N + col) * 2u;
+          if constexpr (TRANSW) {
+            // [N][K] weights into the packed LDS order: the instruction fills
+            // 16 column rows (64 bytes: 32 K-values) of half q / 4 of its
+            // sub-block; the lane's chunk holds logical chunk p ^ ((c >> 1) & 3)
+            const int q = jj % IPS;
+            const int c = (q % 4) * 16 + lane / 4;
+            const int n = min(it.n0 + (jj / IPS) * 64 + c, it.N - 1);
+            const int kc = (q / 4) * 32 + ((lane % 4) ^ ((c >> 1) & 3)) * 8;
+            it.voff[i] = static_cast<uint32_t>(n * it.K + kc) * 2u;
+          }
         } else {
           const int r = (j - C::W_INSTR) * RPI_X + lane / (C::BK / 8);
           const int kc = swz_x<C::BK>(r, lane % (C::BK / 8)) * 8;
@@ -544,6 +562,14 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
             const int64_t blk = static_cast<int64_t>(nb) * it.kblk + k0 / 64;
             base = w + blk * 4096 + ((k0 % 64) / 32) * 2048 + (jj % IPS) * 512;
           }
+        } else if constexpr (TRANSW) {
+          base = w + k0;
+          if constexpr (KTAIL) {
+            const int q = jj % IPS;
+            const int c = (q % 4) * 16 + lane / 4;
+            const int kc = (q / 4) * 32 + ((lane % 4) ^ ((c >> 1) & 3)) * 8;
+            if (kc > kleft - 8) voff -= static_cast<uint32_t>(kc - (kleft - 8)) * 2u;
+          }
         } else {
           base = w + k0 * it.N;
           if constexpr (KTAIL) {
@@ -606,8 +632,9 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
       const uint32_t e8 = *reinterpret_cast<const uint8_t*>(
           buf + C::OP_BYTES + ((m * C::SB + (col >> 6)) * (C::BK / 32) + s) * 64 + c);
       return fp4x8_to_bf16(u, __uint_as_float(e8 << 23));
-    } else if constexpr (PACKED) {
-      // packed bf16: each column's 32 K-values of a half are one 64-byte row
+    } else if constexpr (PACKED || TRANSW) {
+      // packed bf16 (and [N][K] weights, staged in the same order): each
+      // column's 32 K-values of a half are one 64-byte row
       // (16-byte chunk q at q ^ ((c >> 1) & 3)), so the lane's 8 consecutive
       // K-values of its column are one 16-byte read
       const int col = wf * C::TF + fi * 16 + i16;
@@ -939,7 +966,30 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
         const int tok = wt * C::TT + ti * 16 + i16;
         const int f = cur.n0 + wf * C::TF + fi * 16 + 4 * g16;
         if (tok < cur.rows_valid && f < cur.N) {
+          const int64_t o = static_cast<int64_t>(cur.row_base + tok) * cur.N + f;
           float vals[4];
+          if constexpr (!C::GATED && !FP8 && !MX && sizeof(OutT) == 2) {
+            if (prob.epi == kSwigluBwd) {
+              // acc = dh; with the forward's G and U: dG = dh U silu'(G),
+              // dU = dh silu(G), silu'(z) = s (1 + z (1 - s)), s = 1/(1+e^-z)
+              const uint2 gq = *reinterpret_cast<const uint2*>(cur.aux0 + o);
+              const uint2 uq = *reinterpret_cast<const uint2*>(cur.aux1 + o);
+              const uint32_t gw[2] = {gq.x, gq.y}, uw[2] = {uq.x, uq.y};
+              float dg[4], du[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float g = bf16_to_f32(static_cast<bf16_t>(gw[r / 2] >> (16 * (r % 2))));
+                const float u = bf16_to_f32(static_cast<bf16_t>(uw[r / 2] >> (16 * (r % 2))));
+                const float sg = 1.0f / (1.0f + __expf(-g));
+                const float dh = acc[0][fi][ti][r];
+                dg[r] = dh * u * sg * (1.0f + g * (1.0f - sg));
+                du[r] = dh * g * sg;
+              }
+              store4(cur.out + o, dg);
+              store4(cur.out2 + o, du);
+              continue;
+            }
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             if (C::GATED) {
@@ -951,7 +1001,16 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
               vals[r] = FP8 ? acc[0][fi][ti][r] * sc0[r] : acc[0][fi][ti][r];
             }
           }
-          store4(cur.out + static_cast<int64_t>(cur.row_base + tok) * cur.N + f, vals);
+          if constexpr (C::GATED && !FP8 && !MX) {
+            if (prob.epi == kStoreGUH) {  // the forward's G and U for the backward
+              float g4[4], u4[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) g4[r] = acc[0][fi][ti][r], u4[r] = acc[1][fi][ti][r];
+              store4(cur.out2 + o, g4);
+              store4(cur.out3 + o, u4);
+            }
+          }
+          store4(cur.out + o, vals);
         }
       }
     }
@@ -1050,7 +1109,7 @@ int device_cu_count() {
 }
 
 // Resident workgroups per CU for a launch with `dyn` bytes of dynamic LDS.
-template <class C, typename OutT, bool KTAIL, bool PACKED>
+template <class C, typename OutT, bool KTAIL, bool PACKED, bool TRANSW>
 int blocks_per_cu(size_t dyn) {
   static int cached_n[64] = {0};
   static size_t cached_dyn[64] = {0};
@@ -1059,7 +1118,7 @@ int blocks_per_cu(size_t dyn) {
   if (cached_n[dev] == 0 || cached_dyn[dev] != dyn) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(grouped_gemm_kernel<C, OutT, KTAIL, PACKED>),
+            &n, reinterpret_cast<const void*>(grouped_gemm_kernel<C, OutT, KTAIL, PACKED, TRANSW>),
             C::kThreads, dyn) != hipSuccess || n <= 0)
       n = 1;
     cached_n[dev] = n;
@@ -1080,17 +1139,17 @@ int64_t item_bound(const GemmProblem& p) {
   return bound;
 }
 
-template <class C, typename OutT, bool KTAIL, bool PACKED>
+template <class C, typename OutT, bool KTAIL, bool PACKED, bool TRANSW = false>
 hipError_t launch_tail(const GemmProblem& p, int64_t bound, hipStream_t stream) {
   int groups = 0;
   for (int s = 0; s < p.nseg; ++s) groups += p.seg[s].ngroups;
   const size_t dyn = static_cast<size_t>((groups + 2) & ~1) * sizeof(int) +
                     static_cast<size_t>(groups) * sizeof(int2);
   int64_t grid =
-      static_cast<int64_t>(device_cu_count()) * blocks_per_cu<C, OutT, KTAIL, PACKED>(dyn);
+      static_cast<int64_t>(device_cu_count()) * blocks_per_cu<C, OutT, KTAIL, PACKED, TRANSW>(dyn);
   if (bound < grid) grid = bound;
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL((grouped_gemm_kernel<C, OutT, KTAIL, PACKED>),
+  hipLaunchKernelGGL((grouped_gemm_kernel<C, OutT, KTAIL, PACKED, TRANSW>),
                      dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), dyn, stream, p);
   return hipGetLastError();
 }
@@ -1113,6 +1172,12 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
     return ktail ? launch_tail<C, OutT, true, true>(p, bound, stream)
                  : launch_tail<C, OutT, false, true>(p, bound, stream);
   } else {
+    if (layout == kWeightsTransposed) {
+      if constexpr (!C::GATED)
+        return ktail ? launch_tail<C, OutT, true, false, true>(p, bound, stream)
+                     : launch_tail<C, OutT, false, false, true>(p, bound, stream);
+      return hipErrorInvalidValue;
+    }
     if (layout >= 2) return hipErrorInvalidValue;
     if (layout == 1)
       return ktail ? launch_tail<C, OutT, true, true>(p, bound, stream)

@@ -68,7 +68,20 @@ struct GemmSegment {
   // chaining (see grouped_gemm_gathers).
   const int32_t* gather = nullptr;
   int ksplit = 1;          // K-slices (> 1 needs fp32 output; the consumer sums them)
+  // Epilogues of the training backward (GemmProblem::epi): kStoreGUH also
+  // writes G to out2 and U to out3; kSwigluBwd reads G, U from aux0, aux1
+  // ([rows, N] bf16, like out) and writes dG to out, dU to out2.
+  void* out2 = nullptr;
+  void* out3 = nullptr;
+  const bf16_t* aux0 = nullptr;
+  const bf16_t* aux1 = nullptr;
 };
+
+// Weight layout 4 (GemmSegment::packed): row-major [N][K] per group (K
+// contiguous), i.e. the transpose of a [K][N] weight as it is stored; plain
+// (not gated) bf16 problems only.
+constexpr int kWeightsTransposed = 4;
+enum GemmEpilogue { kEpiDefault = 0, kStoreGUH = 1, kSwigluBwd = 2 };
 
 struct GemmProblem {
   GemmSegment seg[2];
@@ -76,6 +89,7 @@ struct GemmProblem {
   bool gated;      // out = silu(act w0) * (act w1), else act w0
   bool out_f32;    // store fp32 instead of bf16 (down projection only)
   int rows_hint;   // typical rows per group, picks the tile shape
+  int epi = kEpiDefault;  // GemmEpilogue (kStoreGUH: gated; kSwigluBwd: plain, bf16 out)
 };
 
 hipError_t launch_grouped_gemm(const GemmProblem& prob, hipStream_t stream);
@@ -136,10 +150,27 @@ hipError_t launch_router(const RouterPlan& p, const bf16_t* x, const bf16_t* w, 
                          int E, int k, float* logits_out, float* part, int32_t* topk_ids,
                          float* topk_w, hipStream_t stream);
 
+// --- training backward (backward.hip) ---
+// dy[row_dest[t,j]] = bf16(topk_w[t,j] * dout[t]); d_topk_w[t,j] =
+// <dout[t], y[row_dest[t,j]]> (y fp32 [A,H]).
+hipError_t launch_combine_backward(const bf16_t* dout, const float* y, const int32_t* row_dest,
+                                   const float* topk_w, int T, int H, int k, bf16_t* dy,
+                                   float* d_topk_w, hipStream_t stream);
+// d_logits [T,E] of the softmax over the k selected logits.
+hipError_t launch_route_backward(const int32_t* topk_ids, const float* topk_w,
+                                 const float* d_topk_w, int T, int E, int k, float* d_logits,
+                                 hipStream_t stream);
+// out[e] = sum over rows p in [offsets[e], offsets[e+1]) of a[p]^T b[p]:
+// a [rows, M], b [rows, N] bf16, out fp32 [E][M][N] (zero for empty groups;
+// offsets == nullptr: every group is empty).
+hipError_t launch_kgrouped_gemm(const bf16_t* a, const bf16_t* b, const int32_t* offsets,
+                                int E, int M, int N, float* out, hipStream_t stream);
+
 // --- combine (combine.hip) ---
 // y_perm/y_shared hold bf16 values (y_f32 == false) or fp32 values; with
 // nslices > 1 (fp32 only) they are K-slice partial sums, slice s at
 // y + s*stride, added in slice order (nslices_sh likewise for y_shared).
+// topk_w == nullptr: every weight is 1.
 hipError_t launch_combine(const void* y_perm, bool y_f32, int nslices,
                           int64_t y_slice_stride, const int32_t* row_dest,
                           const float* topk_w, int T, int H, int k,

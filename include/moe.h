@@ -386,6 +386,50 @@ int moe_forward_mxfp4(const moe_bf16* x, const float* logits, int T, int H, int 
                       int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
                       void* stream);
 
+/* ---- Training backward ----
+ * The news page "Triton-Optimierter BF16 Grouped GEMM Kernel beschleunigt
+ * MoE-Modelle" (meineki.news), introduction, presents its grouped GEMM for
+ * training as well as inference; no page gives the backward, so these calls
+ * are the chain rule through steps 2-5 and through the softmax of step 1.
+ * With G = x_perm W_gate, U = x_perm W_up, h = silu(G) U, y = h W_down per
+ * expert row, and the gradient dout of the layer's output out:
+ *   dy       = w * dout[token]                  (per row, bf16)
+ *   d_topk_w = <dout[t], y[row of (t,j)]>       (fp32)
+ *   dh       = dy W_down^T
+ *   dG       = dh * U * silu'(G),  dU = dh * silu(G),
+ *              silu'(z) = s(z) (1 + z (1 - s(z))), s the logistic function
+ *   dx[t]    = sum_j (dG W_gate^T + dU W_up^T)[row of (t,j)]
+ *   dW_gate[e] = x_perm_e^T dG_e, dW_up[e] = x_perm_e^T dU_e,
+ *   dW_down[e] = h_e^T dy_e   (sums over the expert's rows; 0 for an expert
+ *                              with no rows).
+ * The forward is recomputed inside (nothing is kept from moe_forward); h,
+ * G, U, dy, dG and dU are rounded to bf16 between the steps, every product
+ * accumulates in fp32. Routed experts only (no shared expert); weights in
+ * the row-major layout of moe_forward. */
+
+/* Bytes of the workspace moe_backward needs (0 for invalid sizes):
+ * about T*k*(16 H + 10 F) bytes. */
+size_t moe_backward_workspace_bytes(int T, int H, int F, int E, int k);
+
+/* Gradients of the routed layer for a given routing (topk_ids, topk_w
+ * [T,k], as moe_forward returns them) and output gradient dout [T,H] bf16.
+ * Outputs: dx [T,H] bf16; d_topk_w [T,k] fp32; dw_gate, dw_up [E,H,F] and
+ * dw_down [E,F,H] fp32 (every element written; all zero when T = 0, which
+ * is then the only work and needs only the three weight-gradient pointers).
+ * Extra limit: H*F < 2^31. Deterministic. */
+int moe_backward(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w, int T, int H,
+                 int F, int E, int k, const moe_bf16* w_gate, const moe_bf16* w_up,
+                 const moe_bf16* w_down, const moe_bf16* dout, moe_bf16* dx, float* d_topk_w,
+                 float* dw_gate, float* dw_up, float* dw_down, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/* Gradient of the router logits through the softmax over each token's k
+ * selected logits (step 1): d_logits [T,E] fp32, with
+ * d_logits[t, id_j] = w_j (d_w_j - sum_i w_i d_w_i) and 0 for the experts
+ * not selected (the selection itself has no gradient). */
+int moe_route_backward(const int32_t* topk_ids, const float* topk_w, const float* d_topk_w,
+                       int T, int E, int k, float* d_logits, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

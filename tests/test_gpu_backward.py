@@ -1,0 +1,197 @@
+"""GPU parity of the training backward (moe_backward, moe_route_backward)
+through the C ABI against the CPU oracle's fp64 chain rule, at sizes the
+oracle finishes in seconds. The shapes make the backward's GEMMs (dh with the
+SwiGLU backward, the two dx products, the three K-grouped weight gradients)
+see every tile class, ragged M, N and K tails, empty experts, and a token
+count of zero.
+
+Tolerance, derived from the arithmetic: the GPU rounds G, U, h, dy, dG, dU
+and dx to bf16 (relative error at most u = 2^-8 each) and accumulates every product
+in fp32 (error ~K 2^-24, far below u); the oracle keeps fp64 throughout. To
+first order each gradient element's error is then at most u times the same
+chain evaluated on absolute values (each rounded quantity replaced by its
+magnitude, each sum by the sum of magnitudes: grad_bounds below), so the
+test allows twice that, plus 1e-6 of the tensor's rms. The gradients are
+also checked in relative L2 norm (1e-2, under three bf16 unit roundoffs), which a
+wrong tile, tail or term would exceed by orders of magnitude. A flat
+per-element tolerance does not fit here: an expert with few rows has
+weight-gradient elements set by one row, whose three stacked roundings
+(dy, U, dG) reach ~1 % of that row's term."""
+import numpy as np
+import pytest
+import torch
+
+from grouped_gemm_softmax_amd import binding as B
+from grouped_gemm_softmax_amd import synth
+from helpers import bf16_to_f64, gpu_bf16_f64, host_layer, rel_l2, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny": (synth.CONFIGS["tiny"], 64),
+    "ragged_small_batch": (synth.small_config("rs", H=200, F=328, E=6, k=2), 90),
+    "ragged_large128": (synth.small_config("rl", H=200, F=328, E=6, k=2), 500),
+    "ragged_large256": (synth.small_config("rl256", H=200, F=328, E=4, k=2), 500),
+    "large256_whole_k": (synth.small_config("l256", H=256, F=384, E=4, k=2), 500),
+    "zipf_empty_experts": (synth.small_config("zm", H=256, F=128, E=64, k=8, logits="zipf"), 60),
+    "single_token": (synth.small_config("st", H=136, F=72, E=8, k=2), 1),
+    "k_equals_E": (synth.small_config("ke", H=64, F=48, E=5, k=5), 23),
+}
+
+
+def dout_bf16(T, H, seed):
+    g = torch.Generator().manual_seed(1000 + seed)
+    return torch.randn((T, H), generator=g).to(torch.bfloat16)
+
+
+U_BF16 = 2.0 ** -8   # bf16 unit roundoff (8-bit significand)
+
+
+def grad_bounds(orc, x, ids, w, wg, wu, wd, dout):
+    """First-order bounds of the GPU's rounding error on each gradient,
+    divided by u: the backward chain evaluated on magnitudes (float64,
+    dense per row; for the tolerance only, never as an expected value)."""
+    f = lambda a: bf16_to_f64(a)
+    x, wg, wu, wd, dout = f(x), f(wg), f(wu), f(wd), f(dout)
+    w = np.asarray(w, np.float64)
+    T, H = x.shape
+    E, _, F = wg.shape
+    k = ids.shape[1]
+    offsets, row_token, row_dest = orc.permute(ids, E)
+    A = T * k
+    eid = np.repeat(np.arange(E), np.diff(offsets))
+    wrow = np.empty(A)
+    wrow[row_dest.reshape(-1)] = w.reshape(-1)
+    xp = x[row_token]
+    G = np.einsum("ph,phf->pf", xp, wg[eid])
+    U = np.einsum("ph,phf->pf", xp, wu[eid])
+    sg = 1.0 / (1.0 + np.exp(-G))
+    silu, dsilu = G * sg, sg * (1.0 + G * (1.0 - sg))
+    h = silu * U
+    dy = wrow[:, None] * dout[row_token]
+    dh = np.einsum("pc,pfc->pf", dy, wd[eid])
+    dha = np.einsum("pc,pfc->pf", np.abs(dy), np.abs(wd[eid]))
+    dG, dU = dh * U * dsilu, dh * silu
+    # dh from rounded dy; U, G rounded (|d silu'/dz| <= 1/2, |d silu/dz| <= 1.1)
+    dGa = dha * np.abs(U * dsilu) + np.abs(dh * U) * (np.abs(dsilu) + np.abs(G)) + np.abs(dG)
+    dUa = dha * np.abs(silu) + 1.1 * np.abs(dh * G) + np.abs(dU)
+    b = dict(dwg=np.zeros((E, H, F)), dwu=np.zeros((E, H, F)), dwd=np.zeros((E, F, H)))
+    for e in range(E):
+        r = slice(offsets[e], offsets[e + 1])
+        b["dwg"][e] = np.abs(xp[r]).T @ dGa[r]
+        b["dwu"][e] = np.abs(xp[r]).T @ dUa[r]
+        b["dwd"][e] = 2 * np.abs(h[r]).T @ np.abs(dy[r])    # h and dy rounded
+    dxr = np.einsum("pf,phf->ph", dGa, np.abs(wg[eid])) + np.einsum("pf,phf->ph", dUa,
+                                                                   np.abs(wu[eid]))
+    dx_abs = np.einsum("pf,phf->ph", np.abs(dG), np.abs(wg[eid])) + np.einsum(
+        "pf,phf->ph", np.abs(dU), np.abs(wu[eid]))
+    b["dx"] = np.zeros((T, H))
+    np.add.at(b["dx"], row_token, dxr + dx_abs)       # + the final bf16 rounding of dx
+    # <dout, y>, y from rounded h: |y| error <= u sum_f |h| |W_down|
+    ya = np.einsum("pf,pfc->pc", np.abs(h), np.abs(wd[eid]))
+    dwa = (np.abs(dout[row_token]) * ya).sum(axis=1)
+    b["dw"] = np.empty((T, k))
+    b["dw"].reshape(-1)[:] = dwa[row_dest.reshape(-1)]
+    return b
+
+
+def check_grad(gpu, ref, bound, what, l2=1e-2):
+    gpu = np.asarray(gpu, np.float64)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    assert np.isfinite(gpu).all(), what
+    if ref.size == 0:
+        return
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    allowed = 2 * U_BF16 * bound + 1e-6 * rms + 1e-30
+    err = np.abs(gpu - ref)
+    bad = err > allowed
+    if bad.any():
+        i = np.unravel_index(np.argmax(err / allowed), err.shape)
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {err.size} out of tolerance; worst at {i}: "
+            f"gpu={gpu[i]!r} ref={ref[i]!r} allowed={allowed[i]:.3e} (rms {rms:.3e})")
+    r = rel_l2(gpu, ref)
+    assert r <= l2, f"{what}: relative L2 error {r:.3e} > {l2}"
+
+
+@pytest.fixture(scope="module", params=sorted(CASES))
+def case(request, orc):
+    cfg, T = CASES[request.param]
+    layer = synth.make_layer(cfg.name, T, seed=2, device="cuda", cfg=cfg,
+                             with_shared=False)
+    d, _ = host_layer(layer)
+    ids, w = orc.route(d["logits"], cfg.k)
+    w32 = w.astype(np.float32)
+    dout = dout_bf16(T, cfg.H, 2)
+    dout_u = synth.u16(dout)
+    ref = orc.backward(d["x"], ids, w32, d["wg"], d["wu"], d["wd"], dout_u)
+    ref["bound"] = grad_bounds(orc, d["x"], ids, w32, d["wg"], d["wu"], d["wd"], dout_u)
+    return request.param, layer, ids, w32, dout.cuda(), ref
+
+
+def test_backward(case):
+    name, layer, ids, w32, dout, ref = case
+    say("moe_backward", name, tuple(layer.x.shape), tuple(layer.w_gate.shape))
+    g = B.moe_backward(layer.x, to_dev(ids), to_dev(w32), layer.w_gate, layer.w_up,
+                       layer.w_down, dout)
+    torch.cuda.synchronize()
+    b = ref["bound"]
+    check_grad(gpu_bf16_f64(g["dx"]), ref["dx"], b["dx"], f"dx[{name}]")
+    check_grad(g["d_topk_w"].cpu().numpy(), ref["dw"], b["dw"], f"d_topk_w[{name}]")
+    check_grad(g["dw_gate"].cpu().numpy(), ref["dwg"], b["dwg"], f"dw_gate[{name}]")
+    check_grad(g["dw_up"].cpu().numpy(), ref["dwu"], b["dwu"], f"dw_up[{name}]")
+    check_grad(g["dw_down"].cpu().numpy(), ref["dwd"], b["dwd"], f"dw_down[{name}]")
+    # experts no token chose: exactly zero weight gradients
+    used = np.zeros(layer.cfg.E, bool)
+    used[np.unique(ids)] = True
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        assert not g[n][torch.from_numpy(~used).cuda()].any(), n
+
+
+def test_backward_deterministic(case):
+    name, layer, ids, w32, dout, _ = case
+    say("moe_backward twice", name)
+    a = B.moe_backward(layer.x, to_dev(ids), to_dev(w32), layer.w_gate, layer.w_up,
+                       layer.w_down, dout)
+    b = B.moe_backward(layer.x, to_dev(ids), to_dev(w32), layer.w_gate, layer.w_up,
+                       layer.w_down, dout)
+    torch.cuda.synchronize()
+    for n in a:
+        assert torch.equal(a[n].view(torch.int16) if a[n].dtype == torch.bfloat16 else a[n],
+                           b[n].view(torch.int16) if b[n].dtype == torch.bfloat16 else b[n]), n
+
+
+def test_backward_no_tokens():
+    cfg = synth.small_config("z0", H=64, F=48, E=3, k=2)
+    layer = synth.make_layer(cfg.name, 0, seed=0, device="cuda", cfg=cfg, with_shared=False)
+    say("moe_backward T=0")
+    ids = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    w = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    dout = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    g = B.moe_backward(layer.x, ids, w, layer.w_gate, layer.w_up, layer.w_down, dout)
+    torch.cuda.synchronize()
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        assert g[n].numel() > 0 and not g[n].any(), n
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (300, 64, 8), (77, 5, 5), (50, 16, 1)])
+def test_route_backward(orc, T, E, k):
+    rng = np.random.default_rng(T + E + k)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    ids, w = orc.route(logits, k)
+    w32 = w.astype(np.float32)
+    dw = rng.standard_normal((T, k)).astype(np.float32)
+    say("moe_route_backward", T, E, k)
+    got = B.moe_route_backward(to_dev(ids), to_dev(w32), to_dev(dw), E)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().astype(np.float64)
+    ref = orc.route_backward(ids, w32, dw.astype(np.float64), E)
+    # fp32 arithmetic: k products and sums, one product and difference
+    s = np.abs(w32.astype(np.float64) * dw).sum(axis=1, keepdims=True)
+    bound = np.zeros_like(ref)
+    wd = np.abs(w32.astype(np.float64)) * (np.abs(dw) + s) * (k + 4) * 2.0 ** -24
+    np.put_along_axis(bound, ids.astype(np.int64), wd, 1)
+    assert (np.abs(got - ref) <= bound + 1e-30).all(), np.abs(got - ref).max()
+    mask = np.zeros((T, E), bool)
+    np.put_along_axis(mask, ids.astype(np.int64), True, 1)
+    assert not got[~mask].any()
