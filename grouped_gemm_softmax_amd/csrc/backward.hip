@@ -13,12 +13,11 @@
 //     expert): dW_down = h^T dy, dW_gate = x^T dG, dW_up = x^T dU.
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace moe {
 
 namespace {
-
-typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
 // --- combine backward ---------------------------------------------------
 // One block per token; 256 threads, 8 columns each per pass. The dot
@@ -96,39 +95,45 @@ __global__ __launch_bounds__(256) void route_backward_kernel(
 
 // --- K-grouped GEMM -------------------------------------------------------
 // out[e][i][j] = sum_{p in e} a[p][i] b[p][j]. A workgroup owns one
-// (expert, 128-row i tile, 128-column j tile) and walks the expert's rows
-// 32 at a time. Both operands are staged in LDS as [32 rows p][128 columns]
-// in two 64-column sub-blocks of 128-byte rows (16-byte chunks XOR-swizzled
-// by 2*(p % 4) ^ 2*((p / 8) % 2)), double-buffered with plain loads (rows
-// past the expert and columns past M or N are zeros); the MFMA operands
+// (expert, 256-row i tile, 256-column j tile) and walks the expert's rows
+// 32 at a time. Each step's operands are staged in LDS as [32 rows p][256
+// columns] in four 64-column sub-blocks of 128-byte rows (16-byte chunks
+// XOR-swizzled by 2*(p % 4) ^ 2*((p / 8) % 2)) by direct-to-LDS loads, in a
+// 4-deep ring (three steps in flight while one is computed; one barrier per
+// step). Rows past the expert load its last row and columns past M or N the
+// last 8 columns, all in bounds: the a-fragments of rows past the expert
+// are zeroed, and the outputs past M or N are not stored. The MFMA operands
 // need 8 consecutive p per lane, which the transposing LDS read
-// ds_read_b64_tr_b16 delivers from that layout. 4 waves as 2 x 2, each
-// 64 x 64 (4 x 4 blocks of v_mfma_f32_16x16x32_bf16).
-constexpr int kKgThreads = 256;
-constexpr int kKgTile = 128;
+// ds_read_b64_tr_b16 delivers from that layout. 8 waves as 4 (i) x 2 (j),
+// each 64 x 128 (4 x 8 blocks of v_mfma_f32_16x16x32_bf16): a 256 x 256
+// tile loads 32 KB per 32-row step for 4 MFLOP, twice the arithmetic per
+// loaded byte of a 128 x 128 tile; the global-load path bounds this kernel.
+constexpr int kKgThreads = 512;
+constexpr int kKgTile = 256;
 constexpr int kKgBK = 32;
+constexpr int kKgStages = 4;
+constexpr int kKgSub = kKgBK * 128;               // bytes of one 64-column sub-block
+constexpr int kKgOp = kKgTile / 64 * kKgSub;      // bytes of one operand's stage (16 KB)
+constexpr int kKgStage = 2 * kKgOp;               // a then b
+constexpr int kKgIpw = kKgStage / 1024 / (kKgThreads / kWave);  // DMA instructions per wave
 
 __device__ __forceinline__ int kg_swz(int row, int chunk) {
   return chunk ^ ((row & 3) << 1) ^ (((row >> 3) & 1) << 1);
 }
 
-__device__ __forceinline__ short4_t kg_tr16(const void* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p));
-}
-
-// Fragment of 16 columns (c0 .. c0+15) of a staged [32][128] tile: lane
-// (i16, g16) gets rows 8*g16 .. 8*g16+7 of column c0 + i16. Within each
-// 16-lane group, lane i of a transposing read receives element i % 4 of the
-// 8-byte pieces read by lanes 4r + i / 4.
+// Fragment of 16 columns (c0 .. c0+15) of a staged [32][256] operand: lane
+// (i16, g16) gets rows 8*g16 .. 8*g16+7 of column c0 + i16 (the transposing
+// read gives lane i of each 16-lane group element i % 4 of the 8-byte
+// pieces read by lanes 4r + i / 4).
 __device__ __forceinline__ bf16x8 kg_frag(const char* tile, int c0, int lane) {
   const int i16 = lane & 15, g16 = lane >> 4;
   const int row = 8 * g16 + (i16 >> 2);
   const int col = c0 + 4 * (i16 & 3);
   const int c64 = col & 63;
-  const char* p = tile + (col >> 6) * (kKgBK * 128) + row * 128 + kg_swz(row, c64 >> 3) * 16 +
+  const char* p = tile + (col >> 6) * kKgSub + row * 128 + kg_swz(row, c64 >> 3) * 16 +
                   (c64 & 7) * 2;
-  const short4_t lo = kg_tr16(p);
-  const short4_t hi = kg_tr16(p + 4 * 128);
+  const short4_t lo = lds_read_tr16(p);
+  const short4_t hi = lds_read_tr16(p + 4 * 128);
   typedef short short8_t __attribute__((ext_vector_type(8)));
   const short8_t s8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, s8);
@@ -138,76 +143,86 @@ __global__ __launch_bounds__(kKgThreads) void kgrouped_gemm_kernel(
     const bf16_t* __restrict__ a, const bf16_t* __restrict__ b,
     const int32_t* __restrict__ offsets, int E, int M, int N, int tiles_i, int tiles_j,
     float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) char sa[2][kKgBK * kKgTile * 2];
-  __shared__ __attribute__((aligned(16))) char sb[2][kKgBK * kKgTile * 2];
+  __shared__ __attribute__((aligned(1024))) char ring[kKgStages][kKgStage];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int wave = tid / kWave, wi = wave / 2, wj = wave % 2;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wi = wave / 2, wj = wave % 2;
   const int tiles = tiles_i * tiles_j;
   const int e = blockIdx.x / tiles;
   const int i0 = (blockIdx.x % tiles) / tiles_j * kKgTile;
   const int j0 = (blockIdx.x % tiles) % tiles_j * kKgTile;
   const int rows = offsets ? max(0, offsets[e + 1] - offsets[e]) : 0;  // null: no rows
   const int64_t r0 = offsets ? offsets[e] : 0;
+  const int nk = (rows + kKgBK - 1) / kKgBK;
 
-  // this thread's 2 chunks of each operand per step: chunk q = tid + 256 s
-  // -> sub-block q / 256, row (q / 8) % 32, logical column chunk q % 8.
-  // The next step's chunks are loaded into registers before the current
-  // step's MFMAs and written to the other LDS buffer after them.
-  uint4 ra[2], rb[2];
-  auto load = [&](int kk) {
+  // DMA instruction j = wave + 8 i of a stage fills its 1 KB at j * 1024:
+  // operand j / 16, sub-block (j % 16) / 4, rows 8 (j % 4) .. +7; the lane's
+  // slot (row, physical chunk lane % 8) holds logical chunk kg_swz(row, .)
+  int rrow[kKgIpw], rcol[kKgIpw];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int q = tid + kKgThreads * s;
-      const int sbk = q / 256, row = (q / 8) % 32, ch = q % 8;
-      const int p = kk + row;
-      const int ci = i0 + sbk * 64 + ch * 8;
-      const int cj = j0 + sbk * 64 + ch * 8;
-      ra[s] = uint4{0u, 0u, 0u, 0u};
-      rb[s] = uint4{0u, 0u, 0u, 0u};
-      if (p < rows) {
-        if (ci < M) ra[s] = *reinterpret_cast<const uint4*>(a + (r0 + p) * M + ci);
-        if (cj < N) rb[s] = *reinterpret_cast<const uint4*>(b + (r0 + p) * N + cj);
-      }
-    }
-  };
-  auto store = [&](int buf) {
+  for (int i = 0; i < kKgIpw; ++i) {
+    const int j = wave + (kKgThreads / kWave) * i;
+    const int jj = j % 16;
+    const int row = (jj % 4) * 8 + lane / 8;
+    const int col = (j < 16 ? i0 : j0) + (jj / 4) * 64 + kg_swz(row, lane % 8) * 8;
+    rrow[i] = row;
+    rcol[i] = min(col, (j < 16 ? M : N) - 8);
+  }
+  auto issue = [&](int t) {
+    // steps past the last re-load the last one (a fixed count in flight)
+    const int kk = min(t, nk - 1) * kKgBK;
+    char* const dst = ring[t % kKgStages];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int q = tid + kKgThreads * s;
-      const int sbk = q / 256, row = (q / 8) % 32, ch = q % 8;
-      const int off = sbk * (kKgBK * 128) + row * 128 + kg_swz(row, ch) * 16;
-      *reinterpret_cast<uint4*>(sa[buf] + off) = ra[s];
-      *reinterpret_cast<uint4*>(sb[buf] + off) = rb[s];
+    for (int i = 0; i < kKgIpw; ++i) {
+      const int j = wave + (kKgThreads / kWave) * i;
+      const bool is_a = j < 16;  // wave-uniform
+      const int ld = is_a ? M : N;
+      const bf16_t* base = (is_a ? a : b) + (r0 + kk) * ld;
+      const int prow = min(rrow[i], rows - 1 - kk);
+      dma16(base, static_cast<uint32_t>(prow * ld + rcol[i]) * 2u, dst + j * 1024);
     }
   };
 
-  floatx4 acc[4][4];
+  floatx4 acc[4][8];
 #pragma unroll
   for (int x = 0; x < 4; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int y = 0; y < 8; ++y) acc[x][y] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (rows + kKgBK - 1) / kKgBK;
   if (nk > 0) {
-    load(0);
-    store(0);
-  }
-  __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nk) load((s + 1) * kKgBK);
-    bf16x8 fa[4], fb[4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) fa[x] = kg_frag(sa[buf], wi * 64 + x * 16, lane);
+    for (int t = 0; t < kKgStages - 1; ++t) issue(t);
+    const int g16 = lane >> 4;
+    for (int t = 0; t < nk; ++t) {
+      // this wave's loads of step t have landed (two later steps may be in
+      // flight); after the barrier every wave's have, and every wave is done
+      // reading the buffer that step t + 3 refills
+      wait_vmcnt_lgkm0<(kKgStages - 2) * kKgIpw>();
+      __builtin_amdgcn_s_barrier();
+      issue(t + kKgStages - 1);
+      const char* sa = ring[t % kKgStages];
+      const char* sb = sa + kKgOp;
+      bf16x8 fa[4], fb[8];
 #pragma unroll
-    for (int y = 0; y < 4; ++y) fb[y] = kg_frag(sb[buf], wj * 64 + y * 16, lane);
+      for (int x = 0; x < 4; ++x) fa[x] = kg_frag(sa, wi * 64 + x * 16, lane);
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+      for (int y = 0; y < 8; ++y) fb[y] = kg_frag(sb, wj * 128 + y * 16, lane);
+      const int left = rows - t * kKgBK - 8 * g16;  // valid rows among the lane's 8
+      if (left < 8) {
 #pragma unroll
-      for (int y = 0; y < 4; ++y)
-        acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
-    if (s + 1 < nk) store(buf ^ 1);
-    __syncthreads();
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int r = 0; r < 8; ++r)
+            if (r >= left) fa[x][r] = __bf16(0.0f);
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 8; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
+    }
+    // no LDS DMA may land after the workgroup ends
+    wait_vmcnt<0>();
   }
   // lane (i16, g16) holds rows 4*g16 .. 4*g16+3 of column i16 of each block
   const int i16 = lane & 15, g16 = lane >> 4;
@@ -215,8 +230,8 @@ __global__ __launch_bounds__(kKgThreads) void kgrouped_gemm_kernel(
 #pragma unroll
   for (int x = 0; x < 4; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int j = j0 + wj * 64 + y * 16 + i16;
+    for (int y = 0; y < 8; ++y) {
+      const int j = j0 + wj * 128 + y * 16 + i16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + wi * 64 + x * 16 + 4 * g16 + r;
