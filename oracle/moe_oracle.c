@@ -699,6 +699,142 @@ void oracle_route_backward(const int32_t* ids, const float* w, const double* dw,
   }
 }
 
+/* Backward for selected tokens only: dx[i] and dw[i] (the routing-weight
+ * gradient) of token tokens[i]. A token's input and routing-weight
+ * gradients depend on that token alone, so they equal rows tokens[i] of
+ * oracle_backward's dx and dw: the same per-row arithmetic in the same
+ * order (its k rows in slot order), one token at a time. */
+int oracle_backward_tokens(const uint16_t* x, const int32_t* ids, const float* w, int64_t T,
+                           int H, int F, int E, int k, const uint16_t* wg, const uint16_t* wu,
+                           const uint16_t* wd, const uint16_t* dout, const int64_t* tokens,
+                           int64_t n, double* dx, double* dw) {
+  if (T < 0 || H < 1 || F < 1 || E < 1 || k < 1 || k > E) return ORC_ERR_ARG;
+  for (int64_t i = 0; i < n; ++i)
+    if (tokens[i] < 0 || tokens[i] >= T) return ORC_ERR_ARG;
+  for (int64_t i = 0; i < n * k; ++i) {
+    const int32_t e = ids[tokens[i / k] * k + i % k];
+    if (e < 0 || e >= E) return ORC_ERR_ARG;
+  }
+  int rc = ORC_OK;
+#pragma omp parallel
+  {
+    double* buf = (double*)malloc(sizeof(double) * ((size_t)F * 5 + (size_t)H * 3));
+    if (!buf) {
+#pragma omp atomic write
+      rc = ORC_ERR_NOMEM;
+    } else {
+      double *G = buf, *U = G + F, *hrow = U + F, *dG = hrow + F, *dU = dG + F;
+      double *y = dU + F, *dy = y + H, *dxp = dy + H;
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t s = 0; s < n; ++s) {
+        const int64_t t = tokens[s];
+        const uint16_t* xt = x + t * H;
+        for (int i = 0; i < H; ++i) dx[s * H + i] = 0.0;
+        for (int j = 0; j < k; ++j) {
+          const int e = ids[t * k + j];
+          const uint16_t* wge = wg + (int64_t)e * H * F;
+          const uint16_t* wue = wu + (int64_t)e * H * F;
+          const uint16_t* wde = wd + (int64_t)e * F * H;
+          gateup_row(xt, H, F, wge, wue, hrow, G, U);
+          down_row(hrow, F, H, wde, y);
+          const double wj = (double)w[t * k + j];
+          double d = 0.0;
+          for (int c = 0; c < H; ++c) d += bf16_to_f64(dout[t * H + c]) * y[c];
+          dw[s * k + j] = d;
+          for (int c = 0; c < H; ++c) dy[c] = wj * bf16_to_f64(dout[t * H + c]);
+          for (int f = 0; f < F; ++f) {
+            double a = 0.0;
+            const uint16_t* rd = wde + (int64_t)f * H;
+            for (int c = 0; c < H; ++c) a += dy[c] * bf16_to_f64(rd[c]);
+            const double z = G[f], sg = 1.0 / (1.0 + exp(-z));
+            dG[f] = a * U[f] * sg * (1.0 + z * (1.0 - sg));
+            dU[f] = a * silu(z);
+          }
+          for (int i = 0; i < H; ++i) {
+            double a = 0.0;
+            const uint16_t* rg = wge + (int64_t)i * F;
+            const uint16_t* ru = wue + (int64_t)i * F;
+            for (int f = 0; f < F; ++f)
+              a += dG[f] * bf16_to_f64(rg[f]) + dU[f] * bf16_to_f64(ru[f]);
+            dxp[i] = a;
+          }
+          /* slots in ascending order, as oracle_backward adds them */
+          for (int i = 0; i < H; ++i) dx[s * H + i] += dxp[i];
+        }
+      }
+      free(buf);
+    }
+  }
+  return rc;
+}
+
+/* Selected columns of the weight gradients: for each pair (ecol[i],
+ * fcol[i]) = (e, f), column f of dW_gate[e] and dW_up[e] ([H] each) and row
+ * f of dW_down[e] ([H]). Each is a sum over expert e's rows in ascending
+ * permuted order (oracle_permute) of the same per-row quantities as in
+ * oracle_backward, restricted to column f: G, U and dh at f are the same
+ * dot products in the same order, so the results equal oracle_backward's
+ * elements. */
+int oracle_backward_wcols(const uint16_t* x, const int32_t* ids, const float* w, int64_t T,
+                          int H, int F, int E, int k, const uint16_t* wg, const uint16_t* wu,
+                          const uint16_t* wd, const uint16_t* dout, const int32_t* ecol,
+                          const int32_t* fcol, int64_t n, double* dwg, double* dwu,
+                          double* dwd) {
+  if (T < 0 || H < 1 || F < 1 || E < 1 || k < 1 || k > E) return ORC_ERR_ARG;
+  for (int64_t i = 0; i < n; ++i)
+    if (ecol[i] < 0 || ecol[i] >= E || fcol[i] < 0 || fcol[i] >= F) return ORC_ERR_ARG;
+  const int64_t A = T * k;
+  for (int64_t i = 0; i < A; ++i)
+    if (ids[i] < 0 || ids[i] >= E) return ORC_ERR_ARG;
+  int32_t* offsets = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
+  int32_t* row_token = (int32_t*)malloc(sizeof(int32_t) * (size_t)(A + 1));
+  int32_t* row_dest = (int32_t*)malloc(sizeof(int32_t) * (size_t)(A + 1));
+  int32_t* row_slot = (int32_t*)malloc(sizeof(int32_t) * (size_t)(A + 1));
+  int rc = ORC_ERR_NOMEM;
+  if (!offsets || !row_token || !row_dest || !row_slot) goto done;
+  rc = oracle_permute(ids, T, E, k, offsets, row_token, row_dest);
+  if (rc) goto done;
+  for (int64_t i = 0; i < A; ++i) row_slot[row_dest[i]] = (int32_t)(i % k);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t s = 0; s < n; ++s) {
+    const int e = ecol[s], f = fcol[s];
+    const uint16_t* wge = wg + (int64_t)e * H * F;
+    const uint16_t* wue = wu + (int64_t)e * H * F;
+    const uint16_t* rd = wd + ((int64_t)e * F + f) * H;
+    double* gg = dwg + s * H;
+    double* gu = dwu + s * H;
+    double* gd = dwd + s * H;
+    for (int i = 0; i < H; ++i) gg[i] = 0.0, gu[i] = 0.0, gd[i] = 0.0;
+    for (int64_t p = offsets[e]; p < offsets[e + 1]; ++p) {
+      const int64_t t = row_token[p];
+      const uint16_t* xt = x + t * H;
+      double G = 0.0, U = 0.0;
+      for (int h = 0; h < H; ++h) {
+        const double xv = bf16_to_f64(xt[h]);
+        G += xv * bf16_to_f64(wge[(int64_t)h * F + f]);
+        U += xv * bf16_to_f64(wue[(int64_t)h * F + f]);
+      }
+      const double wj = (double)w[t * k + row_slot[p]];
+      double a = 0.0;
+      for (int c = 0; c < H; ++c) a += wj * bf16_to_f64(dout[t * H + c]) * bf16_to_f64(rd[c]);
+      const double sg = 1.0 / (1.0 + exp(-G));
+      const double dG = a * U * sg * (1.0 + G * (1.0 - sg));
+      const double dU = a * silu(G);
+      const double hv = silu(G) * U;
+      for (int i = 0; i < H; ++i) {
+        const double xv = bf16_to_f64(xt[i]);
+        gg[i] += xv * dG;
+        gu[i] += xv * dU;
+        gd[i] += hv * (wj * bf16_to_f64(dout[t * H + i]));
+      }
+    }
+  }
+  rc = ORC_OK;
+done:
+  free(offsets); free(row_token); free(row_dest); free(row_slot);
+  return rc;
+}
+
 /* Output rows of selected tokens only. Every token's output depends on that
  * token alone, so out[i] for token tokens[i] equals row tokens[i] of
  * oracle_forward; it is computed here with the same per-row functions, one

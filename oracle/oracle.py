@@ -82,6 +82,10 @@ def lib():
                                              _I64, _P, _P, _P])
         L.oracle_backward.argtypes = [_P, _P, _P, _I64, _I, _I, _I, _I, _P, _P, _P, _P,
                                       _P, _P, _P, _P, _P]
+        L.oracle_backward_tokens.argtypes = [_P, _P, _P, _I64, _I, _I, _I, _I, _P, _P, _P,
+                                             _P, _P, _I64, _P, _P]
+        L.oracle_backward_wcols.argtypes = [_P, _P, _P, _I64, _I, _I, _I, _I, _P, _P, _P,
+                                            _P, _P, _P, _I64, _P, _P, _P]
         L.oracle_route_backward.argtypes = [_P, _P, _P, _I64, _I, _I, _P]
         L.oracle_route_backward.restype = None
         _lib = L
@@ -206,6 +210,44 @@ def backward(x, ids, w, wg, wu, wd, dout):
                                  _p(dout), _p(r["dx"]), _p(r["dw"]), _p(r["dwg"]), _p(r["dwu"]),
                                  _p(r["dwd"])), "backward")
     return r
+
+
+def backward_tokens(x, ids, w, wg, wu, wd, dout, tokens):
+    """dx [n,H] and the routing-weight gradient [n,k] of the listed tokens
+    only (equal to those rows of backward()), float64."""
+    x, dout = _c(x, np.uint16), _c(dout, np.uint16)
+    ids, w = _c(ids, np.int32), _c(w, np.float32)
+    wg, wu, wd = _c(wg, np.uint16), _c(wu, np.uint16), _c(wd, np.uint16)
+    tokens = _c(np.asarray(tokens, dtype=np.int64), np.int64)
+    T, H = x.shape
+    k = ids.shape[1]
+    E, _, F = wg.shape
+    n = tokens.shape[0]
+    dx, dw = np.empty((n, H)), np.empty((n, k))
+    _check(lib().oracle_backward_tokens(_p(x), _p(ids), _p(w), T, H, F, E, k, _p(wg), _p(wu),
+                                        _p(wd), _p(dout), _p(tokens), n, _p(dx), _p(dw)),
+           "backward_tokens")
+    return dx, dw
+
+
+def backward_wcols(x, ids, w, wg, wu, wd, dout, ecol, fcol):
+    """For each pair (e, f): column f of dW_gate[e] and dW_up[e] and row f
+    of dW_down[e], each [n,H] float64 (equal to those elements of
+    backward())."""
+    x, dout = _c(x, np.uint16), _c(dout, np.uint16)
+    ids, w = _c(ids, np.int32), _c(w, np.float32)
+    wg, wu, wd = _c(wg, np.uint16), _c(wu, np.uint16), _c(wd, np.uint16)
+    ecol = _c(np.asarray(ecol, dtype=np.int32), np.int32)
+    fcol = _c(np.asarray(fcol, dtype=np.int32), np.int32)
+    T, H = x.shape
+    k = ids.shape[1]
+    E, _, F = wg.shape
+    n = ecol.shape[0]
+    g, u, d = np.empty((n, H)), np.empty((n, H)), np.empty((n, H))
+    _check(lib().oracle_backward_wcols(_p(x), _p(ids), _p(w), T, H, F, E, k, _p(wg), _p(wu),
+                                       _p(wd), _p(dout), _p(ecol), _p(fcol), n, _p(g), _p(u),
+                                       _p(d)), "backward_wcols")
+    return g, u, d
 
 
 def route_backward(ids, w, dw, E: int) -> np.ndarray:

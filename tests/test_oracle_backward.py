@@ -123,3 +123,22 @@ def test_route_backward(orc):
     ids1, w1 = orc.route(logits, 1)
     w1 = w1.astype(np.float32)
     assert not orc.route_backward(ids1, w1, rng.standard_normal((T, 1)), E).any()
+
+
+def test_sampled_backward_equals_full(orc):
+    # the per-token and per-column forms repeat the full backward's
+    # arithmetic in the same order: equal bit for bit, empty experts included
+    x, ids, w, wg, wu, wd, dout = make_case(6, T=9, H=16, F=24, E=5, k=2)
+    ids[:, :] = np.where(ids == 4, 3, ids)          # expert 4 gets no rows
+    ids[:, 1] = np.where(ids[:, 1] == ids[:, 0], (ids[:, 0] + 1) % 4, ids[:, 1])
+    g = orc.backward(x, ids, w, wg, wu, wd, dout)
+    toks = [0, 3, 8, 3]
+    dx, dw = orc.backward_tokens(x, ids, w, wg, wu, wd, dout, toks)
+    assert np.array_equal(dx, g["dx"][toks]) and np.array_equal(dw, g["dw"][toks])
+    ecol, fcol = [0, 1, 3, 4, 2], [0, 23, 7, 5, 11]
+    cg, cu, cd = orc.backward_wcols(x, ids, w, wg, wu, wd, dout, ecol, fcol)
+    for s, (e, f) in enumerate(zip(ecol, fcol)):
+        assert np.array_equal(cg[s], g["dwg"][e, :, f])
+        assert np.array_equal(cu[s], g["dwu"][e, :, f])
+        assert np.array_equal(cd[s], g["dwd"][e, f, :])
+    assert not cg[3].any() and not cd[3].any()      # expert 4: no rows
