@@ -6,17 +6,21 @@ see every tile class, ragged M, N and K tails, empty experts, and a token
 count of zero.
 
 Tolerance, derived from the arithmetic: the GPU rounds G, U, h, dy, dG, dU
-and dx to bf16 (relative error at most u = 2^-8 each) and accumulates every product
-in fp32 (error ~K 2^-24, far below u); the oracle keeps fp64 throughout. To
-first order each gradient element's error is then at most u times the same
-chain evaluated on absolute values (each rounded quantity replaced by its
-magnitude, each sum by the sum of magnitudes: grad_bounds below), so the
-test allows twice that, plus 1e-6 of the tensor's rms. The gradients are
-also checked in relative L2 norm (1e-2, under three bf16 unit roundoffs), which a
-wrong tile, tail or term would exceed by orders of magnitude. A flat
-per-element tolerance does not fit here: an expert with few rows has
-weight-gradient elements set by one row, whose three stacked roundings
-(dy, U, dG) reach ~1 % of that row's term."""
+and dx to bf16 (relative error at most u = 2^-8 each, spread evenly) and
+accumulates every product in fp32 (error ~K 2^-24, far below u); the oracle
+keeps fp64. Each rounding is an independent error of at most u times the
+rounded value, so an element's error is a sum of such terms weighted by how
+they propagate; its root-sum-square, u * rss (grad_bounds below: the
+backward chain with every sum of products replaced by the root of the sum
+of squares), sets the scale. The test allows 5 u * rss per element (the
+uniform rounding model's standard deviation is u * rss / sqrt(3), so 5 u *
+rss is 8.7 of them; measured maxima are 1.4 - 2.4 u * rss over millions of
+elements), plus a relative L2 error under 1e-2 per gradient. A flat
+per-element tolerance does not fit: gradients are not O(1), and with few
+rows per expert one row's three stacked roundings (dy, U, dG; ~1 % of that
+row's term) can set a weight-gradient element, while a worst-case
+(absolute-value) bound is 3 - 60 times the values themselves because of
+the cancellation in the long sums."""
 import numpy as np
 import pytest
 import torch
@@ -45,12 +49,16 @@ def dout_bf16(T, H, seed):
 
 
 U_BF16 = 2.0 ** -8   # bf16 unit roundoff (8-bit significand)
+LAMBDA = 5.0
 
 
 def grad_bounds(orc, x, ids, w, wg, wu, wd, dout):
-    """First-order bounds of the GPU's rounding error on each gradient,
-    divided by u: the backward chain evaluated on magnitudes (float64,
-    dense per row; for the tolerance only, never as an expected value)."""
+    """Root-sum-square scale (divided by u) of the GPU's rounding error on
+    each gradient: the backward chain in float64, dense per row, with each
+    rounded quantity contributing its own magnitude and each sum of products
+    the root of the sum of their squares (for the tolerance only, never as
+    an expected value). |d silu'/dz| <= 1/2 and |d silu/dz| <= 1.1 carry the
+    rounding of G."""
     f = lambda a: bf16_to_f64(a)
     x, wg, wu, wd, dout = f(x), f(wg), f(wu), f(wd), f(dout)
     w = np.asarray(w, np.float64)
@@ -70,28 +78,29 @@ def grad_bounds(orc, x, ids, w, wg, wu, wd, dout):
     h = silu * U
     dy = wrow[:, None] * dout[row_token]
     dh = np.einsum("pc,pfc->pf", dy, wd[eid])
-    dha = np.einsum("pc,pfc->pf", np.abs(dy), np.abs(wd[eid]))
+    dhr = np.sqrt(np.einsum("pc,pfc->pf", dy ** 2, wd[eid] ** 2))   # from dy's rounding
     dG, dU = dh * U * dsilu, dh * silu
-    # dh from rounded dy; U, G rounded (|d silu'/dz| <= 1/2, |d silu/dz| <= 1.1)
-    dGa = dha * np.abs(U * dsilu) + np.abs(dh * U) * (np.abs(dsilu) + np.abs(G)) + np.abs(dG)
-    dUa = dha * np.abs(silu) + 1.1 * np.abs(dh * G) + np.abs(dU)
+    dGr2 = (dhr * U * dsilu) ** 2 + dG ** 2 + (dh * U * dsilu) ** 2 + (0.5 * dh * U * G) ** 2
+    dUr2 = (dhr * silu) ** 2 + dU ** 2 + (1.1 * dh * G) ** 2
     b = dict(dwg=np.zeros((E, H, F)), dwu=np.zeros((E, H, F)), dwd=np.zeros((E, F, H)))
     for e in range(E):
         r = slice(offsets[e], offsets[e + 1])
-        b["dwg"][e] = np.abs(xp[r]).T @ dGa[r]
-        b["dwu"][e] = np.abs(xp[r]).T @ dUa[r]
-        b["dwd"][e] = 2 * np.abs(h[r]).T @ np.abs(dy[r])    # h and dy rounded
-    dxr = np.einsum("pf,phf->ph", dGa, np.abs(wg[eid])) + np.einsum("pf,phf->ph", dUa,
-                                                                   np.abs(wu[eid]))
-    dx_abs = np.einsum("pf,phf->ph", np.abs(dG), np.abs(wg[eid])) + np.einsum(
-        "pf,phf->ph", np.abs(dU), np.abs(wu[eid]))
-    b["dx"] = np.zeros((T, H))
-    np.add.at(b["dx"], row_token, dxr + dx_abs)       # + the final bf16 rounding of dx
-    # <dout, y>, y from rounded h: |y| error <= u sum_f |h| |W_down|
-    ya = np.einsum("pf,pfc->pc", np.abs(h), np.abs(wd[eid]))
-    dwa = (np.abs(dout[row_token]) * ya).sum(axis=1)
+        b["dwg"][e] = np.sqrt((xp[r] ** 2).T @ dGr2[r])
+        b["dwu"][e] = np.sqrt((xp[r] ** 2).T @ dUr2[r])
+        b["dwd"][e] = np.sqrt(2 * (h[r] ** 2).T @ dy[r] ** 2)       # h and dy rounded
+    dxr2 = np.einsum("pf,phf->ph", dGr2, wg[eid] ** 2) + np.einsum("pf,phf->ph", dUr2,
+                                                                   wu[eid] ** 2)
+    dx2 = np.zeros((T, H))
+    np.add.at(dx2, row_token, dxr2)
+    dx = np.zeros((T, H))
+    np.add.at(dx, row_token, np.einsum("pf,phf->ph", dG, wg[eid]) +
+              np.einsum("pf,phf->ph", dU, wu[eid]))
+    b["dx"] = np.sqrt(dx2 + dx ** 2)                                 # + dx's own rounding
+    # <dout, y>, y from rounded h
+    ya2 = np.einsum("pf,pfc->pc", h ** 2, wd[eid] ** 2)
+    dwr = np.sqrt((dout[row_token] ** 2 * ya2).sum(axis=1))
     b["dw"] = np.empty((T, k))
-    b["dw"].reshape(-1)[:] = dwa[row_dest.reshape(-1)]
+    b["dw"].reshape(-1)[:] = dwr[row_dest.reshape(-1)]
     return b
 
 
@@ -102,7 +111,7 @@ def check_grad(gpu, ref, bound, what, l2=1e-2):
     if ref.size == 0:
         return
     rms = float(np.sqrt(np.mean(ref * ref)))
-    allowed = 2 * U_BF16 * bound + 1e-6 * rms + 1e-30
+    allowed = LAMBDA * U_BF16 * bound + 1e-6 * rms + 1e-30
     err = np.abs(gpu - ref)
     bad = err > allowed
     if bad.any():
