@@ -99,15 +99,14 @@ __global__ __launch_bounds__(256) void route_backward_kernel(
 // 32 at a time. Each step's operands are staged in LDS as [32 rows p][256
 // columns] in four 64-column sub-blocks of 128-byte rows (16-byte chunks
 // XOR-swizzled by 2*(p % 4) ^ 2*((p / 8) % 2)) by direct-to-LDS loads, in a
-// 4-deep ring (three steps in flight while one is computed; one barrier per
-// step). Rows past the expert load its last row and columns past M or N the
+// 4-deep ring (up to three steps in flight). Rows past the expert load its last row and columns past M or N the
 // last 8 columns, all in bounds: the a-fragments of rows past the expert
 // are zeroed, and the outputs past M or N are not stored. The MFMA operands
 // need 8 consecutive p per lane, which the transposing LDS read
 // ds_read_b64_tr_b16 delivers from that layout. 8 waves as 4 (i) x 2 (j),
-// each 64 x 128 (4 x 8 blocks of v_mfma_f32_16x16x32_bf16): a 256 x 256
-// tile loads 32 KB per 32-row step for 4 MFLOP, twice the arithmetic per
-// loaded byte of a 128 x 128 tile; the global-load path bounds this kernel.
+// each 64 x 128 (4 x 8 blocks of v_mfma_f32_16x16x32_bf16), on a ping-pong
+// schedule (below): a 256 x 256 tile loads 32 KB per 32-row step for
+// 4 MFLOP, twice the arithmetic per loaded byte of a 128 x 128 tile.
 constexpr int kKgThreads = 512;
 constexpr int kKgTile = 256;
 constexpr int kKgBK = 32;
@@ -189,24 +188,42 @@ __global__ __launch_bounds__(kKgThreads) void kgrouped_gemm_kernel(
 #pragma unroll
     for (int y = 0; y < 8; ++y) acc[x][y] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // Ping-pong schedule: waves 0-3 and 4-7 (one of each per SIMD) alternate
+  // between a memory phase M(t) (fragment reads of step t, the wait for the
+  // wave's own loads of step t+1, the loads of step t+3) and a compute
+  // phase C(t) (32 MFMAs), each closed by a workgroup barrier; waves 4-7
+  // pass one extra barrier first, so in interval 2t waves 0-3 run M(t) while
+  // waves 4-7 run C(t-1), and in 2t+1 the reverse: one wave of each SIMD
+  // keeps the matrix core busy while the other moves data. Step t+1 is read
+  // from interval 2t+2 on, after both groups have waited for their loads of
+  // it (in 2t and 2t+1); the buffer refilled in M(t) held step t-1, whose
+  // fragments both groups read in intervals 2t-2 and 2t-1.
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
   if (nk > 0) {
+    const bool grp1 = wave >= 4;
+    const int g16 = lane >> 4;
 #pragma unroll
     for (int t = 0; t < kKgStages - 1; ++t) issue(t);
-    const int g16 = lane >> 4;
+    wait_vmcnt<(kKgStages - 2) * kKgIpw>();  // this wave's loads of step 0 have landed
+    barrier();                               // ... and every wave's
+    if (grp1) barrier();
+    bf16x8 fa[4], fb[8];
     for (int t = 0; t < nk; ++t) {
-      // this wave's loads of step t have landed (two later steps may be in
-      // flight); after the barrier every wave's have, and every wave is done
-      // reading the buffer that step t + 3 refills
-      wait_vmcnt_lgkm0<(kKgStages - 2) * kKgIpw>();
-      __builtin_amdgcn_s_barrier();
-      issue(t + kKgStages - 1);
       const char* sa = ring[t % kKgStages];
       const char* sb = sa + kKgOp;
-      bf16x8 fa[4], fb[8];
 #pragma unroll
       for (int x = 0; x < 4; ++x) fa[x] = kg_frag(sa, wi * 64 + x * 16, lane);
 #pragma unroll
       for (int y = 0; y < 8; ++y) fb[y] = kg_frag(sb, wj * 128 + y * 16, lane);
+      wait_vmcnt<(kKgStages - 3) * kKgIpw>();  // this wave's loads of step t+1 have landed
+      issue(t + kKgStages - 1);
+      wait_vmcnt_lgkm0<63>();                  // fragments in registers
       const int left = rows - t * kKgBK - 8 * g16;  // valid rows among the lane's 8
       if (left < 8) {
 #pragma unroll
@@ -215,12 +232,15 @@ __global__ __launch_bounds__(kKgThreads) void kgrouped_gemm_kernel(
           for (int r = 0; r < 8; ++r)
             if (r >= left) fa[x][r] = __bf16(0.0f);
       }
+      barrier();
 #pragma unroll
       for (int x = 0; x < 4; ++x)
 #pragma unroll
         for (int y = 0; y < 8; ++y)
           acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
+      barrier();
     }
+    if (!grp1) barrier();
     // no LDS DMA may land after the workgroup ends
     wait_vmcnt<0>();
   }
