@@ -412,7 +412,8 @@ int moe_forward_mxfp4(const moe_bf16* x, const float* logits, int T, int H, int 
 size_t moe_backward_workspace_bytes(int T, int H, int F, int E, int k);
 
 /* Gradients of the routed layer for a given routing (topk_ids, topk_w
- * [T,k], as moe_forward returns them) and output gradient dout [T,H] bf16.
+ * [T,k], as moe_forward returns them: ids in [0,E), distinct within a
+ * token) and output gradient dout [T,H] bf16.
  * Outputs: dx [T,H] bf16; d_topk_w [T,k] fp32; dw_gate, dw_up [E,H,F] and
  * dw_down [E,F,H] fp32 (every element written; all zero when T = 0, which
  * is then the only work and needs only the three weight-gradient pointers).
