@@ -398,7 +398,12 @@ def main():
                         traffic=None)
     roofline["traffic"] = measured_traffic(args.config == "mixtral" and args.T == 32 and
                                            args.seed == 0, args.weights)
-    roofline.update(kernel="grouped_gemm_kernel (gate/up + SwiGLU, routed experts)",
+    # the gate/up launch of the step: rs_gateup_kernel (register-streaming)
+    # for packed bf16 weights at decode sizes, grouped_gemm_kernel otherwise
+    roofline.update(kernel="gate/up + SwiGLU grouped GEMM over the routed experts "
+                           "(moe_gateup_swiglu" + ("" if mode == "rowmajor" else "_" + mode) +
+                           "; rs_gateup_kernel for packed bf16 weights at up to 16 items "
+                           "per CU, grouped_gemm_kernel otherwise)",
                     kernel_ms=round(g1_ms, 5),
                     alg_bytes=g1["bytes"], alg_flops=g1["flops"])
 

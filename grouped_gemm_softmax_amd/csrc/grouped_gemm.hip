@@ -235,11 +235,18 @@ __device__ __forceinline__ GroupView group_view(const GemmProblem& p, int g) {
   return v;
 }
 
+// Output stores go through the global address space with builtin vector
+// types: a flat store (what a generic pointer, or a HIP vector class whose
+// assignment takes a generic `this`, compiles to) also counts as an LDS
+// access, so every later LDS wait would wait for the store as well.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store4(bf16_t* p, const float v[4]) {
-  *reinterpret_cast<uint2*>(p) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  *(__attribute__((address_space(1))) u32x2_t*)(p) =
+      u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 __device__ __forceinline__ void store4(float* p, const float v[4]) {
-  *reinterpret_cast<float4*>(p) = float4{v[0], v[1], v[2], v[3]};
+  *(__attribute__((address_space(1))) f32x4_t*)(p) = f32x4_t{v[0], v[1], v[2], v[3]};
 }
 
 template <class C, typename OutT, bool KTAIL, bool PACKED, bool TRANSW = false>
@@ -972,6 +979,235 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
   wait_vmcnt<0>();
 }
 
+// ---- register-streaming gate/up for decode-size groups ----
+// Packed bf16 weights only. Each wave owns 16 output columns of a 16-row x
+// 64-column item (4 waves per workgroup) and streams its weight fragments
+// straight from global memory into registers: in the packed layout a
+// lane's MFMA operand (8 K-consecutive values of one column) is one
+// 16-byte load, and 16 lanes of one column group read 1 KB contiguously.
+// No LDS and no barriers: every wave keeps kRsD K-steps (64 deep) of loads
+// in flight in a ring of registers, and its step sequence runs across its
+// items without draining (the loads of the next item start while the
+// current one is finished). The compiler's own waits (vmcnt, in load order)
+// hold each step back until its loads have landed. Activations (16 rows of
+// the item) are read the same way; they are small and come from L2.
+int device_cu_count();
+
+constexpr int kRsWaves = 4;
+constexpr int kRsThreads = kRsWaves * kWave;
+constexpr int kRsD = 6;      // K-steps in flight per wave
+constexpr int kRsBT = 16;    // rows per item
+constexpr int kRsBF = 64;    // columns per item (16 per wave)
+
+__global__ __launch_bounds__(kRsThreads) void rs_gateup_kernel(GemmProblem prob) {
+  extern __shared__ __attribute__((aligned(16))) int s_pref[];
+  __shared__ int s_wave_total[kRsWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int g16 = lane >> 4, i16 = lane & 15;
+
+  // item prefix over all groups of both segments (as in grouped_gemm_kernel)
+  const int NG = prob.seg[0].ngroups + (prob.nseg > 1 ? prob.seg[1].ngroups : 0);
+  int2* const s_rows = reinterpret_cast<int2*>(s_pref + ((NG + 2) & ~1));
+  constexpr int GPT = (kMaxGroups + kRsThreads - 1) / kRsThreads;
+  int cnt[GPT];
+  int my_sum = 0;
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) {
+    const int g = tid * GPT + i;
+    cnt[i] = 0;
+    if (g < NG) {
+      const GroupView v = group_view(prob, g);
+      const GemmSegment& S = v.seg ? prob.seg[1] : prob.seg[0];
+      cnt[i] = ((v.M + kRsBT - 1) / kRsBT) * ((S.N + kRsBF - 1) / kRsBF);
+      s_rows[g] = int2{v.r0, v.M};
+    }
+    my_sum += cnt[i];
+  }
+  const int incl = wave_inclusive_scan(my_sum);
+  if (lane == kWave - 1) s_wave_total[wave] = incl;
+  __syncthreads();
+  int run = incl - my_sum;
+  for (int w = 0; w < wave; ++w) run += s_wave_total[w];
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) {
+    const int g = tid * GPT + i;
+    if (g <= NG) s_pref[g] = run;
+    run += cnt[i];
+  }
+  __syncthreads();
+  const int total = s_pref[NG];
+  if (total == 0) return;
+  // balanced persistent slots, XCD-contiguous (as in grouped_gemm_kernel)
+  const int G = gridDim.x;
+  int slot, stride;
+  if (G % 8 == 0) {
+    const int rounds = (total + G - 1) / G;
+    const int per_xcd = ((total + rounds - 1) / rounds + 7) / 8;
+    if (static_cast<int>(blockIdx.x / 8) >= per_xcd) return;
+    slot = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    stride = 8 * per_xcd;
+  } else {
+    slot = blockIdx.x;
+    stride = G;
+  }
+  if (slot >= total) return;
+  const int K = prob.seg[0].K;           // one K for both segments (host-checked)
+  const int nk = (K + 63) / 64;
+  const int kblk = nk;
+  const int nitems = (total - slot + stride - 1) / stride;
+  const int nsteps = nitems * nk;
+
+  struct Cur {
+    const bf16_t* w0;
+    const bf16_t* w1;
+    const bf16_t* x;     // the item's first activation row
+    bf16_t* out;
+    int N, n0, row_base, rows_valid;
+  };
+  auto item_info = [&](int item) INL {
+    int lo = 0, hi = NG;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pref[mid] <= item) lo = mid; else hi = mid;
+    }
+    const int segi = lo < prob.seg[0].ngroups ? 0 : 1;
+    const int local_g = segi ? lo - prob.seg[0].ngroups : lo;
+    const GemmSegment& S = segi ? prob.seg[1] : prob.seg[0];
+    const int2 rows = s_rows[lo];
+    const int mtiles = (rows.y + kRsBT - 1) / kRsBT;
+    const int local = item - s_pref[lo];
+    const int mt = local % mtiles;
+    Cur c;
+    c.N = S.N;
+    c.n0 = (local / mtiles) * kRsBF;
+    c.row_base = rows.x + mt * kRsBT;
+    c.rows_valid = min(kRsBT, rows.y - mt * kRsBT);
+    const int64_t blk0 = static_cast<int64_t>(c.n0 / 64) * kblk * 4096;  // first K-block
+    c.w0 = uniform(S.w0 + static_cast<int64_t>(local_g) * S.w_stride + blk0);
+    c.w1 = uniform(S.w1 + static_cast<int64_t>(local_g) * S.w_stride + blk0);
+    c.x = uniform(S.act + static_cast<int64_t>(c.row_base) * K);
+    c.out = uniform(static_cast<bf16_t*>(S.out));
+    c.N = __builtin_amdgcn_readfirstlane(c.N);
+    c.n0 = __builtin_amdgcn_readfirstlane(c.n0);
+    c.row_base = __builtin_amdgcn_readfirstlane(c.row_base);
+    c.rows_valid = __builtin_amdgcn_readfirstlane(c.rows_valid);
+    return c;
+  };
+
+  // the lane's offsets inside a K-block: column c of the wave's 16, chunk
+  // g16 of each 32-deep half at its swizzled place; activation row i16
+  const int col = wave * 16 + i16;
+  const uint32_t woff = static_cast<uint32_t>(col * 32 + ((g16 ^ ((col >> 1) & 3)) << 3));
+  struct Slot {
+    bf16x8 w[2][2];  // [matrix][half]
+    bf16x8 x[2];     // [half]
+  };
+  // loads through the global address space (not flat: a flat load also
+  // counts as an LDS access, and its waits would drain every load in flight)
+  typedef __attribute__((address_space(1))) const bf16x8 gvec_t;
+  auto gload = [](const bf16_t* p) INL { return *(gvec_t*)(p); };
+  Slot ring[kRsD];
+  // issue cursor
+  int is_item = slot, is_k = 0, is_n = 0;
+  Cur ic = item_info(is_item);
+  auto issue = [&](Slot& sl) INL {
+    // steps past the wave's last one re-load its last step
+    const int kb = is_k;
+    const bf16_t* wb0 = ic.w0 + static_cast<int64_t>(kb) * 4096;
+    const bf16_t* wb1 = ic.w1 + static_cast<int64_t>(kb) * 4096;
+    const int xrow = min(i16, ic.rows_valid - 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      sl.w[0][h] = gload(wb0 + h * 2048 + woff);
+      sl.w[1][h] = gload(wb1 + h * 2048 + woff);
+      const int k = min(kb * 64 + h * 32 + g16 * 8, K - 8);  // past K: weights are zero
+      sl.x[h] = gload(ic.x + static_cast<int64_t>(xrow) * K + k);
+    }
+    if (is_n + 1 < nsteps) {
+      ++is_n;
+      if (++is_k == nk) {
+        is_k = 0;
+        is_item += stride;
+        ic = item_info(is_item);
+      }
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kRsD; ++i) issue(ring[i]);
+
+  floatx4 acc[2];
+  acc[0] = acc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+  int c_item = slot, c_k = 0;
+  Cur cc = item_info(c_item);
+  auto step = [&](Slot& sl) INL {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl.w[m][h], sl.x[h], acc[m], 0, 0, 0);
+    issue(sl);
+    if (++c_k == nk) {
+      // epilogue: lane holds columns 4*g16 .. +3 of token i16
+      const int f = cc.n0 + col - i16 + 4 * g16;
+      if (i16 < cc.rows_valid && f < cc.N) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[0][r] / (1.0f + __expf(-acc[0][r])) * acc[1][r];
+        store4(cc.out + static_cast<int64_t>(cc.row_base + i16) * cc.N + f, v);
+      }
+      acc[0] = acc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      c_k = 0;
+      c_item += stride;
+      if (c_item < total) cc = item_info(c_item);
+    }
+  };
+  int s0 = 0;
+  for (; s0 + kRsD <= nsteps; s0 += kRsD)
+    static_for<kRsD>([&](auto I) INL { step(ring[decltype(I)::value]); });
+  static_for<kRsD - 1>([&](auto I) INL {
+    if (s0 + decltype(I)::value < nsteps) step(ring[decltype(I)::value]);
+  });
+}
+
+int rs_blocks_per_cu(size_t dyn) {
+  static int cached_n[64] = {0};
+  static size_t cached_dyn[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached_n[dev] == 0 || cached_dyn[dev] != dyn) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(rs_gateup_kernel), kRsThreads, dyn) != hipSuccess ||
+        n <= 0)
+      n = 1;
+    cached_n[dev] = n;
+    cached_dyn[dev] = dyn;
+  }
+  return cached_n[dev];
+}
+
+hipError_t launch_rs_gateup(const GemmProblem& p, hipStream_t stream) {
+  int groups = 0;
+  int64_t bound = 0;
+  for (int s = 0; s < p.nseg; ++s) {
+    const GemmSegment& S = p.seg[s];
+    groups += S.ngroups;
+    bound += ((S.rows + kRsBT - 1) / kRsBT + (S.offsets ? S.ngroups : 0)) *
+             static_cast<int64_t>((S.N + kRsBF - 1) / kRsBF);
+  }
+  if (bound <= 0) return hipSuccess;
+  const size_t dyn = static_cast<size_t>((groups + 2) & ~1) * sizeof(int) +
+                     static_cast<size_t>(groups) * sizeof(int2);
+  int64_t grid = static_cast<int64_t>(device_cu_count()) * rs_blocks_per_cu(dyn);
+  if (bound < grid) grid = bound;
+  grid = (grid + 7) / 8 * 8;
+  hipLaunchKernelGGL(rs_gateup_kernel, dim3(static_cast<unsigned>(grid)), dim3(kRsThreads), dyn,
+                     stream, p);
+  return hipGetLastError();
+}
+
 // Tile shapes (BT tokens x BF columns, BK per stage, waves, ring depth).
 // Large batch: 256 tokens x 128 columns (gated: 128 columns each of gate and
 // up; down: 256 columns), 8 waves (2 per SIMD) as 4 along tokens x 2 along
@@ -1473,6 +1709,33 @@ hipError_t launch_pack_weights(const bf16_t* w, int G, int K, int N, bf16_t* pac
   return hipGetLastError();
 }
 
+// The register-streaming gate/up serves packed bf16 weights of small
+// groups when both segments share K, nothing but h is written, and the
+// expected items (one partial row tile per touched group plus the full
+// ones, times the column tiles) are at most 16 per CU. Measured against the
+// LDS-ring tile: 7-8 % faster at 1 and 2 items per workgroup slot (Mixtral-
+// shaped T = 1, Qwen2-shaped T = 16), 2 % at 4 (Mixtral-shaped T = 32),
+// 3-7 % slower at 11 (DeepSeek-V3-shaped T = 128), where the ring's shared
+// activation tile and its longer streams win. MOE_RS=0 / MOE_RS=1 force it
+// off / on (for comparisons).
+bool use_rs_gateup(const GemmProblem& p) {
+  static int forced = -2;
+  if (forced == -2) {
+    const char* e = getenv("MOE_RS");
+    forced = e ? atoi(e) : -1;
+  }
+  if (forced == 0) return false;
+  if (p.epi != kEpiDefault) return false;
+  int64_t items = 0;
+  for (int s = 0; s < p.nseg; ++s) {
+    const GemmSegment& S = p.seg[s];
+    if (S.packed != 1 || S.gather || S.ksplit != 1 || S.K != p.seg[0].K || S.K < 8) return false;
+    const int64_t touched = S.ngroups > 1 ? (S.rows < S.ngroups ? S.rows : S.ngroups) : 1;
+    items += (touched + S.rows / kRsBT) * ((S.N + kRsBF - 1) / kRsBF);
+  }
+  return forced == 1 || items <= 16 * static_cast<int64_t>(device_cu_count());
+}
+
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
   const int tc = tile_class(p);
   if (p.seg[0].packed == 3) {
@@ -1505,6 +1768,8 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
            : tc8 == kLarge128 ? launch_cfg<DownLarge128_8, bf16_t>(p, stream)
                              : launch_cfg<DownSmall8, bf16_t>(p, stream);
   }
+  if (p.gated && tc == kSmall && use_rs_gateup(p))
+    return launch_rs_gateup(p, stream);
   if (p.gated)
     return tc == kLarge      ? launch_cfg<GateUpLarge, bf16_t>(p, stream)
            : tc == kLarge128 ? launch_cfg<GateUpLarge128, bf16_t>(p, stream)
