@@ -980,11 +980,13 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
 }
 
 // ---- register-streaming gate/up for decode-size groups ----
-// Packed bf16 weights only. Each wave owns 16 output columns of a 16-row x
+// Packed bf16 or fp8 weights. Each wave owns 16 output columns of a 16-row x
 // 64-column item (4 waves per workgroup) and streams its weight fragments
-// straight from global memory into registers: in the packed layout a
-// lane's MFMA operand (8 K-consecutive values of one column) is one
-// 16-byte load, and 16 lanes of one column group read 1 KB contiguously.
+// straight from global memory into registers: in the packed layouts a
+// lane's MFMA operand (8 K-consecutive values of one column) is one 16-byte
+// load (bf16) or one 8-byte load of codes widened in registers (fp8, the
+// column scales applied in the epilogue), and the 16 columns of a wave
+// read one contiguous run.
 // No LDS and no barriers: every wave keeps kRsD K-steps (64 deep) of loads
 // in flight in a ring of registers, and its step sequence runs across its
 // items without draining (the loads of the next item start while the
@@ -999,7 +1001,12 @@ constexpr int kRsD = 6;      // K-steps in flight per wave
 constexpr int kRsBT = 16;    // rows per item
 constexpr int kRsBF = 64;    // columns per item (16 per wave)
 
+template <int WBITS>
 __global__ __launch_bounds__(kRsThreads) void rs_gateup_kernel(GemmProblem prob) {
+  static_assert(WBITS == 16 || WBITS == 8, "bf16 or fp8 weights");
+  constexpr bool FP8 = WBITS == 8;
+  // bytes of a 64 x 64 weight block and of one 32-deep half of it
+  constexpr int BLK = 64 * 64 * WBITS / 8, HALF = BLK / 2;
   extern __shared__ __attribute__((aligned(16))) int s_pref[];
   __shared__ int s_wave_total[kRsWaves];
   const int tid = threadIdx.x;
@@ -1060,10 +1067,12 @@ __global__ __launch_bounds__(kRsThreads) void rs_gateup_kernel(GemmProblem prob)
   const int nsteps = nitems * nk;
 
   struct Cur {
-    const bf16_t* w0;
-    const bf16_t* w1;
+    const char* w0;      // the item's 64-column block row (bytes)
+    const char* w1;
     const bf16_t* x;     // the item's first activation row
     bf16_t* out;
+    const float* sc0;    // fp8: the group's column scales (gate, up)
+    const float* sc1;
     int N, n0, row_base, rows_valid;
   };
   auto item_info = [&](int item) INL {
@@ -1084,11 +1093,16 @@ __global__ __launch_bounds__(kRsThreads) void rs_gateup_kernel(GemmProblem prob)
     c.n0 = (local / mtiles) * kRsBF;
     c.row_base = rows.x + mt * kRsBT;
     c.rows_valid = min(kRsBT, rows.y - mt * kRsBT);
-    const int64_t blk0 = static_cast<int64_t>(c.n0 / 64) * kblk * 4096;  // first K-block
-    c.w0 = uniform(S.w0 + static_cast<int64_t>(local_g) * S.w_stride + blk0);
-    c.w1 = uniform(S.w1 + static_cast<int64_t>(local_g) * S.w_stride + blk0);
+    const int64_t blk0 = static_cast<int64_t>(c.n0 / 64) * kblk * BLK;  // first K-block
+    c.w0 = uniform(reinterpret_cast<const char*>(S.w0 + static_cast<int64_t>(local_g) * S.w_stride) + blk0);
+    c.w1 = uniform(reinterpret_cast<const char*>(S.w1 + static_cast<int64_t>(local_g) * S.w_stride) + blk0);
     c.x = uniform(S.act + static_cast<int64_t>(c.row_base) * K);
     c.out = uniform(static_cast<bf16_t*>(S.out));
+    c.sc0 = c.sc1 = nullptr;
+    if constexpr (FP8) {
+      c.sc0 = uniform(static_cast<const float*>(S.scale0) + static_cast<int64_t>(local_g) * S.N);
+      c.sc1 = uniform(static_cast<const float*>(S.scale1) + static_cast<int64_t>(local_g) * S.N);
+    }
     c.N = __builtin_amdgcn_readfirstlane(c.N);
     c.n0 = __builtin_amdgcn_readfirstlane(c.n0);
     c.row_base = __builtin_amdgcn_readfirstlane(c.row_base);
@@ -1098,16 +1112,24 @@ __global__ __launch_bounds__(kRsThreads) void rs_gateup_kernel(GemmProblem prob)
 
   // the lane's offsets inside a K-block: column c of the wave's 16, chunk
   // g16 of each 32-deep half at its swizzled place; activation row i16
+  // (bf16: 16 bytes at chunk g16 ^ ((c >> 1) & 3) of the column's 64-byte
+  // row; fp8: 8 bytes at chunk g16 ^ ((c >> 2) & 3) of its 32 bytes)
   const int col = wave * 16 + i16;
-  const uint32_t woff = static_cast<uint32_t>(col * 32 + ((g16 ^ ((col >> 1) & 3)) << 3));
+  const uint32_t woff = static_cast<uint32_t>(
+      FP8 ? col * 32 + ((g16 ^ ((col >> 2) & 3)) << 3)
+          : (col * 32 + ((g16 ^ ((col >> 1) & 3)) << 3)) * 2);
+  typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
+  typedef typename std::conditional<FP8, u32x2v_t, bf16x8>::type wvec_t;
   struct Slot {
-    bf16x8 w[2][2];  // [matrix][half]
-    bf16x8 x[2];     // [half]
+    wvec_t w[2][2];   // [matrix][half]: the lane's weights (fp8: codes)
+    bf16x8 x[2];      // [half]
   };
   // loads through the global address space (not flat: a flat load also
   // counts as an LDS access, and its waits would drain every load in flight)
   typedef __attribute__((address_space(1))) const bf16x8 gvec_t;
+  typedef __attribute__((address_space(1))) const wvec_t gw_t;
   auto gload = [](const bf16_t* p) INL { return *(gvec_t*)(p); };
+  auto wload = [](const char* p) INL { return *(gw_t*)(p); };
   Slot ring[kRsD];
   // issue cursor
   int is_item = slot, is_k = 0, is_n = 0;
@@ -1115,13 +1137,13 @@ __global__ __launch_bounds__(kRsThreads) void rs_gateup_kernel(GemmProblem prob)
   auto issue = [&](Slot& sl) INL {
     // steps past the wave's last one re-load its last step
     const int kb = is_k;
-    const bf16_t* wb0 = ic.w0 + static_cast<int64_t>(kb) * 4096;
-    const bf16_t* wb1 = ic.w1 + static_cast<int64_t>(kb) * 4096;
+    const char* wb0 = ic.w0 + static_cast<int64_t>(kb) * BLK;
+    const char* wb1 = ic.w1 + static_cast<int64_t>(kb) * BLK;
     const int xrow = min(i16, ic.rows_valid - 1);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      sl.w[0][h] = gload(wb0 + h * 2048 + woff);
-      sl.w[1][h] = gload(wb1 + h * 2048 + woff);
+      sl.w[0][h] = wload(wb0 + h * HALF + woff);
+      sl.w[1][h] = wload(wb1 + h * HALF + woff);
       const int k = min(kb * 64 + h * 32 + g16 * 8, K - 8);  // past K: weights are zero
       sl.x[h] = gload(ic.x + static_cast<int64_t>(xrow) * K + k);
     }
@@ -1141,12 +1163,33 @@ __global__ __launch_bounds__(kRsThreads) void rs_gateup_kernel(GemmProblem prob)
   acc[0] = acc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
   int c_item = slot, c_k = 0;
   Cur cc = item_info(c_item);
+  // fp8: the current item's column scales of the lane's 4 columns, loaded
+  // when its first step is computed (power-of-two, exact on the fp32 sums;
+  // loaded early so that the in-order load counter never has to wait for
+  // them behind the weight stream)
+  f32x4_t csc0 = f32x4_t{1.f, 1.f, 1.f, 1.f}, csc1 = csc0;
+  auto load_scales = [&]() INL {
+    if constexpr (FP8) {
+      typedef __attribute__((address_space(1))) const f32x4_t gf4_t;
+      const int f = min(cc.n0 + col - i16 + 4 * g16, cc.N - 4);
+      csc0 = *(gf4_t*)(cc.sc0 + f);
+      csc1 = *(gf4_t*)(cc.sc1 + f);
+    }
+  };
+  load_scales();
+  auto wfrag = [&](const Slot& sl, int m, int h) INL {
+    if constexpr (FP8) {
+      return fp8x8_to_bf16(uint2{sl.w[m][h].x, sl.w[m][h].y});
+    } else {
+      return sl.w[m][h];
+    }
+  };
   auto step = [&](Slot& sl) INL {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int m = 0; m < 2; ++m)
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl.w[m][h], sl.x[h], acc[m], 0, 0, 0);
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfrag(sl, m, h), sl.x[h], acc[m], 0, 0, 0);
     issue(sl);
     if (++c_k == nk) {
       // epilogue: lane holds columns 4*g16 .. +3 of token i16
@@ -1154,13 +1197,20 @@ __global__ __launch_bounds__(kRsThreads) void rs_gateup_kernel(GemmProblem prob)
       if (i16 < cc.rows_valid && f < cc.N) {
         float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[0][r] / (1.0f + __expf(-acc[0][r])) * acc[1][r];
+        for (int r = 0; r < 4; ++r) {
+          const float gt = FP8 ? acc[0][r] * csc0[r] : acc[0][r];
+          const float up = FP8 ? acc[1][r] * csc1[r] : acc[1][r];
+          v[r] = gt / (1.0f + __expf(-gt)) * up;
+        }
         store4(cc.out + static_cast<int64_t>(cc.row_base + i16) * cc.N + f, v);
       }
       acc[0] = acc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
       c_k = 0;
       c_item += stride;
-      if (c_item < total) cc = item_info(c_item);
+      if (c_item < total) {
+        cc = item_info(c_item);
+        load_scales();
+      }
     }
   };
   int s0 = 0;
@@ -1171,6 +1221,7 @@ __global__ __launch_bounds__(kRsThreads) void rs_gateup_kernel(GemmProblem prob)
   });
 }
 
+template <int WBITS>
 int rs_blocks_per_cu(size_t dyn) {
   static int cached_n[64] = {0};
   static size_t cached_dyn[64] = {0};
@@ -1179,7 +1230,8 @@ int rs_blocks_per_cu(size_t dyn) {
   if (cached_n[dev] == 0 || cached_dyn[dev] != dyn) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void*>(rs_gateup_kernel), kRsThreads, dyn) != hipSuccess ||
+            &n, reinterpret_cast<const void*>(rs_gateup_kernel<WBITS>), kRsThreads, dyn) !=
+                hipSuccess ||
         n <= 0)
       n = 1;
     cached_n[dev] = n;
@@ -1188,6 +1240,7 @@ int rs_blocks_per_cu(size_t dyn) {
   return cached_n[dev];
 }
 
+template <int WBITS>
 hipError_t launch_rs_gateup(const GemmProblem& p, hipStream_t stream) {
   int groups = 0;
   int64_t bound = 0;
@@ -1200,11 +1253,11 @@ hipError_t launch_rs_gateup(const GemmProblem& p, hipStream_t stream) {
   if (bound <= 0) return hipSuccess;
   const size_t dyn = static_cast<size_t>((groups + 2) & ~1) * sizeof(int) +
                      static_cast<size_t>(groups) * sizeof(int2);
-  int64_t grid = static_cast<int64_t>(device_cu_count()) * rs_blocks_per_cu(dyn);
+  int64_t grid = static_cast<int64_t>(device_cu_count()) * rs_blocks_per_cu<WBITS>(dyn);
   if (bound < grid) grid = bound;
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL(rs_gateup_kernel, dim3(static_cast<unsigned>(grid)), dim3(kRsThreads), dyn,
-                     stream, p);
+  hipLaunchKernelGGL((rs_gateup_kernel<WBITS>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kRsThreads), dyn, stream, p);
   return hipGetLastError();
 }
 
@@ -1709,15 +1762,18 @@ hipError_t launch_pack_weights(const bf16_t* w, int G, int K, int N, bf16_t* pac
   return hipGetLastError();
 }
 
-// The register-streaming gate/up serves packed bf16 weights of small
-// groups when both segments share K, nothing but h is written, and the
-// expected items (one partial row tile per touched group plus the full
-// ones, times the column tiles) are at most 16 per CU. Measured against the
-// LDS-ring tile: 7-8 % faster at 1 and 2 items per workgroup slot (Mixtral-
-// shaped T = 1, Qwen2-shaped T = 16), 2 % at 4 (Mixtral-shaped T = 32),
-// 3-7 % slower at 11 (DeepSeek-V3-shaped T = 128), where the ring's shared
-// activation tile and its longer streams win. MOE_RS=0 / MOE_RS=1 force it
-// off / on (for comparisons).
+// The register-streaming gate/up serves packed bf16 or fp8 weights of
+// small groups when both segments share K, nothing but h is written, and
+// the expected items (one partial row tile per touched group plus the full
+// ones, times the column tiles) are at most 16 (bf16) or 8 (fp8) per CU.
+// Measured against the LDS-ring tiles: bf16 7-8 % faster at 1 and 2 items
+// per workgroup slot (Mixtral-shaped T = 1, Qwen2-shaped T = 16), 2-4 % at
+// 4 (Mixtral-shaped T = 32), 3-7 % slower at 11 (DeepSeek-V3-shaped
+// T = 128), where the ring's shared activation tile and longer streams
+// win; fp8 22 % faster at T = 1 and 19 % at Qwen2-shaped T = 16, but 13 %
+// slower at Mixtral-shaped T = 32. On mxfp4 codes (one scale byte per 32
+// K-values of a column to load beside them) it was slower everywhere.
+// MOE_RS=0 / MOE_RS=1 force it off / on (for comparisons).
 bool use_rs_gateup(const GemmProblem& p) {
   static int forced = -2;
   if (forced == -2) {
@@ -1729,15 +1785,23 @@ bool use_rs_gateup(const GemmProblem& p) {
   int64_t items = 0;
   for (int s = 0; s < p.nseg; ++s) {
     const GemmSegment& S = p.seg[s];
-    if (S.packed != 1 || S.gather || S.ksplit != 1 || S.K != p.seg[0].K || S.K < 8) return false;
+    if (S.packed < 1 || S.packed > 2 || S.packed != p.seg[0].packed || S.gather ||
+        S.ksplit != 1 || S.K != p.seg[0].K || S.K < 8)
+      return false;
     const int64_t touched = S.ngroups > 1 ? (S.rows < S.ngroups ? S.rows : S.ngroups) : 1;
     items += (touched + S.rows / kRsBT) * ((S.N + kRsBF - 1) / kRsBF);
   }
-  return forced == 1 || items <= 16 * static_cast<int64_t>(device_cu_count());
+  // fp8 codes: the column scales make each item's epilogue wait for the
+  // weight stream in flight, so the bound is tighter
+  const int per_cu = p.seg[0].packed == 2 ? 8 : 16;
+  return forced == 1 || items <= per_cu * static_cast<int64_t>(device_cu_count());
 }
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
   const int tc = tile_class(p);
+  if (p.gated && tc == kSmall && use_rs_gateup(p))
+    return p.seg[0].packed == 2 ? launch_rs_gateup<8>(p, stream)
+                                : launch_rs_gateup<16>(p, stream);
   if (p.seg[0].packed == 3) {
     const bool big = tc == kLarge || tc == kLarge128;
     if (p.gated)
@@ -1768,8 +1832,6 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
            : tc8 == kLarge128 ? launch_cfg<DownLarge128_8, bf16_t>(p, stream)
                              : launch_cfg<DownSmall8, bf16_t>(p, stream);
   }
-  if (p.gated && tc == kSmall && use_rs_gateup(p))
-    return launch_rs_gateup(p, stream);
   if (p.gated)
     return tc == kLarge      ? launch_cfg<GateUpLarge, bf16_t>(p, stream)
            : tc == kLarge128 ? launch_cfg<GateUpLarge128, bf16_t>(p, stream)
