@@ -1431,9 +1431,10 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
 }  // namespace
 
 // Tile class by typical rows per group: < 16 small, < 64 mid (gate/up only;
-// the down projection keeps the small tile), < 192 large128, else large. A
-// down projection takes large128 only when its expected items (one partial
-// row tile per touched group plus the full ones, times the column tiles) fill
+// the down projection keeps the small tile; bf16 weights take large128 from
+// 24 rows on), < 192 large128, else large. A down projection from 96 rows
+// per group on takes large128 only when its expected items (one partial row
+// tile per touched group plus the full ones, times the column tiles) fill
 // the two workgroups per CU that tile runs with; with few groups (e.g. 8
 // experts of 128 rows and a long K) it keeps one 256-row tile per CU.
 // MOE_TILE=small|mid|large128|large overrides the choice (for tile sweeps).
@@ -1448,10 +1449,21 @@ int tile_class(const GemmProblem& p) {
                         : !strcmp(e, "large") ? kLarge : -1);
   }
   if (forced >= 0) return forced;
+  const bool bf16 = p.seg[0].packed == 0 || p.seg[0].packed == 1;
   if (p.rows_hint < 16) return kSmall;
-  if (p.rows_hint < 64) return kMid;
+  // bf16 weights: from 24 rows per group on, the 128-row tiles stream the
+  // weights faster than the mid tile (gate/up) and the small tile (down),
+  // padding notwithstanding (the MFMAs are not the bound there): layer
+  // 583 -> 531 us at the Mixtral-shaped T = 128, 4950 -> 4355 us at the
+  // DeepSeek-V3-shaped T = 1024, 364 -> 310 us at the Qwen2-shaped T = 512;
+  // at 16-17 rows the mid and small tiles were ahead (Mixtral-shaped T = 64:
+  // 494 against 524 us)
+  if (p.rows_hint < 64) return bf16 && p.rows_hint >= 24 ? kLarge128 : kMid;
   if (p.rows_hint >= 192) return kLarge;
   if (p.gated) return kLarge128;
+  // bf16 down projections below 96 rows per group: the 256-row tile would
+  // be three-quarters padding (Mixtral-shaped T = 256: layer 580 -> 544 us)
+  if (bf16 && p.rows_hint < 96) return kLarge128;
   int64_t items = 0;
   for (int s = 0; s < p.nseg; ++s) {
     const GemmSegment& S = p.seg[s];
