@@ -431,14 +431,22 @@ def main():
         x = synth.u16(layer.x[:n])
         lg = synth.f32(layer.logits[:n])
         wg, wu, wd = synth.u16(layer.w_gate), synth.u16(layer.w_up), synth.u16(layer.w_down)
-        t0 = time.perf_counter()
-        oracle.forward(x, lg, cfg.k, wg, wu, wd, keep_intermediates=False)
-        t_cpu = time.perf_counter() - t0
+        # repeated until about 10 s of CPU work have been timed (a short
+        # sample is run several times and averaged)
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            oracle.forward(x, lg, cfg.k, wg, wu, wd, keep_intermediates=False)
+            runs += 1
+            t_all = time.perf_counter() - t0
+            if t_all >= 10.0 or runs >= 500:
+                break
+        t_cpu = t_all / runs
         t_full = t_cpu * args.T / n        # the oracle's cost is linear in tokens
         cpu = dict(value=round(total_b / t_full / 1e9, 3), unit="GB/s",
                    cores=oracle.num_threads(), kind="oracle",
                    sample=f"first {n} of {args.T} tokens, whole layer (oracle.forward, fp64), "
-                          f"{t_cpu:.2f} s; scaled linearly to the {args.T}-token step",
+                          f"{runs} runs in {t_all:.1f} s ({t_cpu:.3f} s each); scaled "
+                          f"linearly to the {args.T}-token step",
                    seconds_sample=round(t_cpu, 3))
 
     line = {
