@@ -1163,17 +1163,35 @@ __global__ __launch_bounds__(kRsThreads) void rs_gateup_kernel(GemmProblem prob)
   acc[0] = acc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
   int c_item = slot, c_k = 0;
   Cur cc = item_info(c_item);
-  // fp8: the current item's column scales of the lane's 4 columns, loaded
-  // when its first step is computed (power-of-two, exact on the fp32 sums;
-  // loaded early so that the in-order load counter never has to wait for
-  // them behind the weight stream)
+  // fp8: the current item's column scales of the lane's 4 columns (powers
+  // of two, exact on the fp32 sums). The wave's 16 columns' scales are
+  // wave-uniform, so they are read with scalar loads (a separate counter):
+  // a vector load here would make the epilogue wait, in load order, for the
+  // whole weight stream in flight. Each lane then picks its 4 of the 16.
   f32x4_t csc0 = f32x4_t{1.f, 1.f, 1.f, 1.f}, csc1 = csc0;
   auto load_scales = [&]() INL {
     if constexpr (FP8) {
-      typedef __attribute__((address_space(1))) const f32x4_t gf4_t;
-      const int f = min(cc.n0 + col - i16 + 4 * g16, cc.N - 4);
-      csc0 = *(gf4_t*)(cc.sc0 + f);
-      csc1 = *(gf4_t*)(cc.sc1 + f);
+      typedef __attribute__((address_space(4))) const f32x4_t cf4_t;
+      // columns n0 + 16 wave .. +15, clamped inside the group's N scales
+      const int c0 = min(cc.n0 + wave * 16, cc.N - 16);
+      const int sel = cc.n0 + wave * 16 + 4 * g16 - c0;   // 0, 4, 8 or 12 (or less near N)
+      f32x4_t a[4], b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a[q] = *(cf4_t*)(cc.sc0 + c0 + 4 * q);
+        b[q] = *(cf4_t*)(cc.sc1 + c0 + 4 * q);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // element sel + r of the 16, chosen without dynamic register indexing
+        const int e = min(sel + r, 15);
+        float x = a[0][0], y = b[0][0];
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (e == q) x = a[q / 4][q % 4], y = b[q / 4][q % 4];
+        csc0[r] = x;
+        csc1[r] = y;
+      }
     }
   };
   load_scales();
@@ -1800,6 +1818,7 @@ bool use_rs_gateup(const GemmProblem& p) {
     if (S.packed < 1 || S.packed > 2 || S.packed != p.seg[0].packed || S.gather ||
         S.ksplit != 1 || S.K != p.seg[0].K || S.K < 8)
       return false;
+    if (S.packed == 2 && S.N < 16) return false;   // a wave reads 16 columns' scales
     const int64_t touched = S.ngroups > 1 ? (S.rows < S.ngroups ? S.rows : S.ngroups) : 1;
     items += (touched + S.rows / kRsBT) * ((S.N + kRsBF - 1) / kRsBF);
   }
