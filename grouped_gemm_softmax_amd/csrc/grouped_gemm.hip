@@ -1805,11 +1805,9 @@ hipError_t launch_pack_weights(const bf16_t* w, int G, int K, int N, bf16_t* pac
 // K-values of a column to load beside them) it was slower everywhere.
 // MOE_RS=0 / MOE_RS=1 force it off / on (for comparisons).
 bool use_rs_gateup(const GemmProblem& p) {
-  static int forced = -2;
-  if (forced == -2) {
-    const char* e = getenv("MOE_RS");
-    forced = e ? atoi(e) : -1;
-  }
+  // read at every launch, so that a process can compare both paths
+  const char* env = getenv("MOE_RS");
+  const int forced = env ? atoi(env) : -1;
   if (forced == 0) return false;
   if (p.epi != kEpiDefault) return false;
   int64_t items = 0;
