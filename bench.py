@@ -195,9 +195,10 @@ def router_table(args, torch, B, synth):
 
 def backward_line(args, torch, B, synth):
     """moe_backward of the routed layer at one batch size: HIP events around
-    `steps` calls on the launch stream. Its work is nine A*H*F products
-    (2*A*H*F FLOPs each, A = T*k): the recomputed forward (gate, up, down),
-    dh, the two dx products and the three weight gradients."""
+    `steps` calls on the launch stream. Its work is eight A*H*F products
+    (2*A*H*F FLOPs each, A = T*k): the recomputed gate and up products, dh
+    (on the unweighted dout), the two dx products and the three weight
+    gradients."""
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = synth.CONFIGS[args.config]
@@ -236,7 +237,7 @@ def backward_line(args, torch, B, synth):
     ms_b = timed(bwd, args.steps, args.warmup)
     ms_f = timed(fwd, args.steps, args.warmup)
     A = T * k
-    flops = 9 * 2 * A * H * F
+    flops = 8 * 2 * A * H * F
     print(json.dumps({"backward": cfg.name, "T": T, "H": H, "F": F, "E": E, "k": k,
                       "ms": round(ms_b, 4), "TFLOPs": round(flops / ms_b / 1e9, 1),
                       "mfma_frac": round(flops / ms_b / 1e9 / PEAK_BF16_TFLOPS, 4),

@@ -661,10 +661,12 @@ int moe_forward_routed(const moe_bf16* x, const int32_t* topk_ids, const float* 
 
 // ---- training backward ------------------------------------------------------
 // Workspace of moe_backward (each piece 256-byte aligned from ws):
-// [hist | offsets | row_token | row_dest | x_perm | h | G | U | dy | dG | dU |
-//  y (fp32) | dx parts (fp32, 2 slices)].
+// [hist | offsets | row_token | row_dest | x_perm | h | G | U | dy |
+//  dout_perm | dG | dU | wrow (fp32) | part (fp32 [A][ceil(F/16)]) |
+//  dx parts (fp32, 2 slices)].
 struct BackwardLayout {
-  size_t hist, offsets, row_token, row_dest, x_perm, h, g, u, dy, dg, du, y, dxp, total;
+  size_t hist, offsets, row_token, row_dest, x_perm, h, g, u, dy, dop, dg, du, wrow, part, dxp,
+      total;
 };
 
 static BackwardLayout backward_layout(int T, int H, int F, int E, int k) {
@@ -681,9 +683,11 @@ static BackwardLayout backward_layout(int T, int H, int F, int E, int k) {
   L.g = take(A * F * 2);
   L.u = take(A * F * 2);
   L.dy = take(A * H * 2);
+  L.dop = take(A * H * 2);
   L.dg = take(A * F * 2);
   L.du = take(A * F * 2);
-  L.y = take(A * H * 4);
+  L.wrow = take(A * 4);
+  L.part = take(A * ((static_cast<size_t>(F) + 15) / 16) * 4);
   L.dxp = take(2 * A * H * 4);
   L.total = o;
   return L;
@@ -741,14 +745,17 @@ int moe_backward(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w
   bf16_t* g = reinterpret_cast<bf16_t*>(base + L.g);
   bf16_t* u = reinterpret_cast<bf16_t*>(base + L.u);
   bf16_t* dy = reinterpret_cast<bf16_t*>(base + L.dy);
+  bf16_t* dop = reinterpret_cast<bf16_t*>(base + L.dop);
   bf16_t* dg = reinterpret_cast<bf16_t*>(base + L.dg);
   bf16_t* du = reinterpret_cast<bf16_t*>(base + L.du);
-  float* y = reinterpret_cast<float*>(base + L.y);
+  float* wrow = reinterpret_cast<float*>(base + L.wrow);
+  float* part = reinterpret_cast<float*>(base + L.part);
   float* dxp = reinterpret_cast<float*>(base + L.dxp);
   const int M = static_cast<int>(A);
 
   // forward recompute: permutation (x_perm is kept for the weight
-  // gradients), gate/up storing G and U beside h, down into fp32 y
+  // gradients) and gate/up storing G and U beside h (the down projection is
+  // not needed: the routing-weight gradient comes from dh's epilogue)
   MOE_TRY(hip_status(moe::launch_hist(topk_ids, T, E, k, hist, s)));
   MOE_TRY(hip_status(moe::launch_permute(x, topk_ids, T, H, E, k, hist, offsets, row_token,
                                          row_dest, x_perm, s)));
@@ -758,25 +765,27 @@ int moe_backward(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w
   g1.seg[0].out2 = g;
   g1.seg[0].out3 = u;
   MOE_TRY(hip_status(moe::launch_grouped_gemm(g1, s)));
-  moe::GemmProblem g2 = down_problem(h, offsets, M, F, H, E, w_down, y, kRowMajor);
-  g2.out_f32 = true;
-  MOE_TRY(hip_status(moe::launch_grouped_gemm(g2, s)));
-  // combine backward: dy = w dout per row, d_topk_w = <dout, y>
+  // per row: dy = w dout (for dW_down), dout itself and w
   MOE_TRY(hip_status(
-      moe::launch_combine_backward(dout, y, row_dest, topk_w, T, H, k, dy, d_topk_w, s)));
-  // dh = dy W_down^T (W_down [F][H] is the [N][K] operand), with the SwiGLU
-  // backward in the epilogue: dG, dU
+      moe::launch_backward_prep(dout, row_dest, topk_w, T, H, k, dy, dop, wrow, s)));
+  // g = dout W_down^T per row (W_down [F][H] is the [N][K] operand), with
+  // the SwiGLU backward in the epilogue: dG, dU from dh = w g, and the
+  // partial sums of <h, g> for the routing-weight gradient
   moe::GemmProblem g3{};
-  g3.seg[0] = segment(dy, offsets, w_down, nullptr, dg, M, E, H, F, moe::kWeightsTransposed,
+  g3.seg[0] = segment(dop, offsets, w_down, nullptr, dg, M, E, H, F, moe::kWeightsTransposed,
                       nullptr, nullptr);
   g3.seg[0].aux0 = g;
   g3.seg[0].aux1 = u;
+  g3.seg[0].aux2 = h;
+  g3.seg[0].wrow = wrow;
+  g3.seg[0].part = part;
   g3.seg[0].out2 = du;
   g3.nseg = 1;
   g3.gated = false;
   g3.rows_hint = M / E;
   g3.epi = moe::kSwigluBwd;
   MOE_TRY(hip_status(moe::launch_grouped_gemm(g3, s)));
+  MOE_TRY(hip_status(moe::launch_topk_w_grad(part, (F + 15) / 16, row_dest, T, k, d_topk_w, s)));
   // dx: dG W_gate^T and dU W_up^T per row (fp32 slices), summed over the
   // token's k rows and the two slices by the combine with unit weights
   for (int part = 0; part < 2; ++part) {

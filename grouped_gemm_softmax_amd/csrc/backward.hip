@@ -3,9 +3,12 @@
 // the kernel serves training as well as inference; the pages give no
 // backward, so these are the chain rule through the forward's steps).
 //
-//   combine backward: dy[row(t,j)] = w[t,j] dout[t], and the routing-weight
-//     gradient d_w[t,j] = <dout[t], y[row(t,j)]>: a gather through the
-//     inverse map with a deterministic block reduction.
+//   preparation: per row p of (t,j), dy[p] = w[t,j] dout[t] (bf16, for
+//     dW_down), dout[t] itself and w[t,j]; the dh product runs on the
+//     unweighted dout, g = dout W_down^T, so that the routing-weight gradient
+//     d_w[t,j] = <dout[t], y[p]> = <h[p], g[p]> comes out of its epilogue
+//     (per-fragment partial sums, added in a fixed order) and the forward's
+//     down projection need not be recomputed.
 //   route backward: the softmax over the k selected logits,
 //     d_logit[t, id_j] = w_j (d_w_j - sum_i w_i d_w_i), 0 elsewhere.
 //   K-grouped GEMM: dW[e] = sum over the expert's rows p of a[p]^T b[p]
@@ -19,38 +22,33 @@ namespace moe {
 
 namespace {
 
-// --- combine backward ---------------------------------------------------
-// One block per token; 256 threads, 8 columns each per pass. The dot
-// product is reduced per thread in column order, then across the block in a
-// fixed tree: the result does not depend on timing.
-constexpr int kCbThreads = 256;
+// --- backward preparation -------------------------------------------------
+// Per token (one block of 256 threads, 8 columns each per pass) and slot j,
+// with p = row_dest[t,j]: dy[p] = bf16(w dout[t]) (for dW_down),
+// dout_perm[p] = dout[t] (the unweighted operand of dh), wrow[p] = w.
+constexpr int kPrepThreads = 256;
 
-__global__ __launch_bounds__(kCbThreads) void combine_backward_kernel(
-    const bf16_t* __restrict__ dout, const float* __restrict__ y,
-    const int32_t* __restrict__ row_dest, const float* __restrict__ topk_w, int T, int H, int k,
-    bf16_t* __restrict__ dy, float* __restrict__ d_topk_w) {
+__global__ __launch_bounds__(kPrepThreads) void backward_prep_kernel(
+    const bf16_t* __restrict__ dout, const int32_t* __restrict__ row_dest,
+    const float* __restrict__ topk_w, int T, int H, int k, bf16_t* __restrict__ dy,
+    bf16_t* __restrict__ dout_perm, float* __restrict__ wrow) {
   const int t = blockIdx.x;
-  __shared__ float s_red[kCbThreads / kWave];
   const int64_t A = static_cast<int64_t>(T) * k;
   for (int j = 0; j < k; ++j) {
     int p = row_dest[static_cast<int64_t>(t) * k + j];
     p = p < 0 ? 0 : (p >= A ? static_cast<int>(A - 1) : p);  // stay in bounds
     const float w = topk_w[static_cast<int64_t>(t) * k + j];
-    float dot = 0.f;
-    for (int c = threadIdx.x * 8; c < H; c += kCbThreads * 8) {
+    if (threadIdx.x == 0) wrow[p] = w;
+    for (int c = threadIdx.x * 8; c < H; c += kPrepThreads * 8) {
       const uint4 q = *reinterpret_cast<const uint4*>(dout + static_cast<int64_t>(t) * H + c);
-      const float4 ya = *reinterpret_cast<const float4*>(y + static_cast<int64_t>(p) * H + c);
-      const float4 yb = *reinterpret_cast<const float4*>(y + static_cast<int64_t>(p) * H + c + 4);
+      *reinterpret_cast<uint4*>(dout_perm + static_cast<int64_t>(p) * H + c) = q;
       const uint32_t u[4] = {q.x, q.y, q.z, q.w};
-      const float yv[8] = {ya.x, ya.y, ya.z, ya.w, yb.x, yb.y, yb.z, yb.w};
       float d[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         d[2 * i] = bf16_to_f32(static_cast<bf16_t>(u[i] & 0xffffu));
         d[2 * i + 1] = bf16_to_f32(static_cast<bf16_t>(u[i] >> 16));
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dot += d[i] * yv[i];
       uint4 o;
       o.x = pack_bf16x2(w * d[0], w * d[1]);
       o.y = pack_bf16x2(w * d[2], w * d[3]);
@@ -58,18 +56,23 @@ __global__ __launch_bounds__(kCbThreads) void combine_backward_kernel(
       o.w = pack_bf16x2(w * d[6], w * d[7]);
       *reinterpret_cast<uint4*>(dy + static_cast<int64_t>(p) * H + c) = o;
     }
-    // block sum: butterfly within each wave, then the waves in order
-#pragma unroll
-    for (int m = kWave / 2; m >= 1; m >>= 1) dot += __shfl_xor(dot, m, kWave);
-    if ((threadIdx.x & (kWave - 1)) == 0) s_red[threadIdx.x / kWave] = dot;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float s = 0.f;
-      for (int i = 0; i < kCbThreads / kWave; ++i) s += s_red[i];
-      d_topk_w[static_cast<int64_t>(t) * k + j] = s;
-    }
-    __syncthreads();
   }
+}
+
+// --- routing-weight gradient --------------------------------------------------
+// d_topk_w[t,j] = <dout[t], y[p]> = <h[p], g[p]> (g = dout W_down^T), as the
+// sum of the dh GEMM's per-fragment partial sums of row p, in fragment order.
+__global__ __launch_bounds__(256) void topk_w_grad_kernel(
+    const float* __restrict__ part, int nq, const int32_t* __restrict__ row_dest, int64_t n,
+    float* __restrict__ d_topk_w) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  int64_t p = row_dest[i];
+  p = p < 0 ? 0 : (p >= n ? n - 1 : p);
+  const float* r = part + p * nq;
+  float s = 0.f;
+  for (int q = 0; q < nq; ++q) s += r[q];
+  d_topk_w[i] = s;
 }
 
 // --- route backward -----------------------------------------------------
@@ -262,12 +265,21 @@ __global__ __launch_bounds__(kKgThreads) void kgrouped_gemm_kernel(
 
 }  // namespace
 
-hipError_t launch_combine_backward(const bf16_t* dout, const float* y, const int32_t* row_dest,
-                                   const float* topk_w, int T, int H, int k, bf16_t* dy,
-                                   float* d_topk_w, hipStream_t stream) {
+hipError_t launch_backward_prep(const bf16_t* dout, const int32_t* row_dest,
+                                const float* topk_w, int T, int H, int k, bf16_t* dy,
+                                bf16_t* dout_perm, float* wrow, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_backward_kernel, dim3(T), dim3(kCbThreads), 0, stream, dout, y,
-                     row_dest, topk_w, T, H, k, dy, d_topk_w);
+  hipLaunchKernelGGL(backward_prep_kernel, dim3(T), dim3(kPrepThreads), 0, stream, dout,
+                     row_dest, topk_w, T, H, k, dy, dout_perm, wrow);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_w_grad(const float* part, int nq, const int32_t* row_dest, int T, int k,
+                              float* d_topk_w, hipStream_t stream) {
+  const int64_t n = static_cast<int64_t>(T) * k;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_w_grad_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                     0, stream, part, nq, row_dest, n, d_topk_w);
   return hipGetLastError();
 }
 

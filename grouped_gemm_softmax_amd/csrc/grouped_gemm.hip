@@ -349,6 +349,9 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     bf16_t* out3;
     const bf16_t* aux0;
     const bf16_t* aux1;
+    const bf16_t* aux2;
+    const float* wrow;
+    float* part;
     int K, N;
     int n0;           // first output column
     int row_base;     // first activation row
@@ -406,6 +409,9 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     it.out3 = uniform(static_cast<bf16_t*>(S.out3));
     it.aux0 = uniform(S.aux0);
     it.aux1 = uniform(S.aux1);
+    it.aux2 = uniform(S.aux2);
+    it.wrow = uniform(S.wrow);
+    it.part = uniform(S.part);
     if constexpr (FP8) {
       it.sc0 = static_cast<const float*>(S.scale0) + static_cast<int64_t>(v.local) * S.N;
       it.sc1 = C::GATED ? static_cast<const float*>(S.scale1) + static_cast<int64_t>(v.local) * S.N
@@ -924,31 +930,52 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
       for (int ti = 0; ti < C::FT; ++ti) {
         const int tok = wt * C::TT + ti * 16 + i16;
         const int f = cur.n0 + wf * C::TF + fi * 16 + 4 * g16;
-        if (tok < cur.rows_valid && f < cur.N) {
-          const int64_t o = static_cast<int64_t>(cur.row_base + tok) * cur.N + f;
-          float vals[4];
-          if constexpr (!C::GATED && !FP8 && !MX && sizeof(OutT) == 2) {
-            if (prob.epi == kSwigluBwd) {
-              // acc = dh; with the forward's G and U: dG = dh U silu'(G),
-              // dU = dh silu(G), silu'(z) = s (1 + z (1 - s)), s = 1/(1+e^-z)
+        // (only in the transposed-weight bf16 kernels, which the backward's
+        // dh product runs: the forward's kernels carry no code for it)
+        if constexpr (TRANSW && !C::GATED && sizeof(OutT) == 2) {
+          if (prob.epi == kSwigluBwd) {
+            // acc = g = dout W_down^T for the row; with its routing weight w
+            // and the forward's G, U, h: dh = w g, dG = dh U silu'(G),
+            // dU = dh silu(G), silu'(z) = s (1 + z (1 - s)), s = 1/(1+e^-z);
+            // and the fragment's partial sum of h g (the routing-weight
+            // gradient <dout, y> = <h, g>), summed over its 16 columns
+            // across the four lanes of the token
+            float part = 0.f;
+            if (tok < cur.rows_valid && f < cur.N) {
+              const int64_t o = static_cast<int64_t>(cur.row_base + tok) * cur.N + f;
               const uint2 gq = *reinterpret_cast<const uint2*>(cur.aux0 + o);
               const uint2 uq = *reinterpret_cast<const uint2*>(cur.aux1 + o);
-              const uint32_t gw[2] = {gq.x, gq.y}, uw[2] = {uq.x, uq.y};
+              const uint2 hq = *reinterpret_cast<const uint2*>(cur.aux2 + o);
+              const float w = cur.wrow[cur.row_base + tok];
+              const uint32_t gw[2] = {gq.x, gq.y}, uw[2] = {uq.x, uq.y}, hw[2] = {hq.x, hq.y};
               float dg[4], du[4];
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const float g = bf16_to_f32(static_cast<bf16_t>(gw[r / 2] >> (16 * (r % 2))));
                 const float u = bf16_to_f32(static_cast<bf16_t>(uw[r / 2] >> (16 * (r % 2))));
+                const float hv = bf16_to_f32(static_cast<bf16_t>(hw[r / 2] >> (16 * (r % 2))));
                 const float sg = 1.0f / (1.0f + __expf(-g));
-                const float dh = acc[0][fi][ti][r];
+                const float gr = acc[0][fi][ti][r];
+                const float dh = w * gr;
                 dg[r] = dh * u * sg * (1.0f + g * (1.0f - sg));
                 du[r] = dh * g * sg;
+                part += hv * gr;
               }
               store4(cur.out + o, dg);
               store4(cur.out2 + o, du);
-              continue;
             }
+            part += __shfl_xor(part, 16, kWave);
+            part += __shfl_xor(part, 32, kWave);
+            const int fc = cur.n0 + wf * C::TF + fi * 16;  // the fragment's first column
+            if (g16 == 0 && tok < cur.rows_valid && fc < cur.N)
+              cur.part[static_cast<int64_t>(cur.row_base + tok) * ((cur.N + 15) / 16) + fc / 16] =
+                  part;
+            continue;
           }
+        }
+        if (tok < cur.rows_valid && f < cur.N) {
+          const int64_t o = static_cast<int64_t>(cur.row_base + tok) * cur.N + f;
+          float vals[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             if (C::GATED) {
@@ -1827,6 +1854,10 @@ bool use_rs_gateup(const GemmProblem& p) {
 }
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
+  // the backward epilogue exists in the transposed-weight bf16 kernels only
+  if (p.epi == kSwigluBwd &&
+      (p.gated || p.out_f32 || p.seg[0].packed != kWeightsTransposed || p.nseg != 1))
+    return hipErrorInvalidValue;
   const int tc = tile_class(p);
   if (p.gated && tc == kSmall && use_rs_gateup(p))
     return p.seg[0].packed == 2 ? launch_rs_gateup<8>(p, stream)

@@ -69,12 +69,18 @@ struct GemmSegment {
   const int32_t* gather = nullptr;
   int ksplit = 1;          // K-slices (> 1 needs fp32 output; the consumer sums them)
   // Epilogues of the training backward (GemmProblem::epi): kStoreGUH also
-  // writes G to out2 and U to out3; kSwigluBwd reads G, U from aux0, aux1
-  // ([rows, N] bf16, like out) and writes dG to out, dU to out2.
+  // writes G to out2 and U to out3. kSwigluBwd takes the product as
+  // g = dout W_down^T (unweighted), reads G, U, h from aux0..aux2 ([rows, N]
+  // bf16, like out) and each row's routing weight from wrow, writes
+  // dG = w g U silu'(G) to out and dU = w g silu(G) to out2, and for each
+  // 16-column fragment the partial sum of h g to part [rows][ceil(N/16)].
   void* out2 = nullptr;
   void* out3 = nullptr;
   const bf16_t* aux0 = nullptr;
   const bf16_t* aux1 = nullptr;
+  const bf16_t* aux2 = nullptr;
+  const float* wrow = nullptr;
+  float* part = nullptr;
 };
 
 // Weight layout 4 (GemmSegment::packed): row-major [N][K] per group (K
@@ -151,11 +157,15 @@ hipError_t launch_router(const RouterPlan& p, const bf16_t* x, const bf16_t* w, 
                          float* topk_w, hipStream_t stream);
 
 // --- training backward (backward.hip) ---
-// dy[row_dest[t,j]] = bf16(topk_w[t,j] * dout[t]); d_topk_w[t,j] =
-// <dout[t], y[row_dest[t,j]]> (y fp32 [A,H]).
-hipError_t launch_combine_backward(const bf16_t* dout, const float* y, const int32_t* row_dest,
-                                   const float* topk_w, int T, int H, int k, bf16_t* dy,
-                                   float* d_topk_w, hipStream_t stream);
+// Per assignment row p = row_dest[t,j]: dy[p] = bf16(topk_w[t,j] * dout[t]),
+// dout_perm[p] = dout[t], wrow[p] = topk_w[t,j].
+hipError_t launch_backward_prep(const bf16_t* dout, const int32_t* row_dest,
+                                const float* topk_w, int T, int H, int k, bf16_t* dy,
+                                bf16_t* dout_perm, float* wrow, hipStream_t stream);
+// d_topk_w[t,j] = sum over q of part[p][q], p = row_dest[t,j], in q order
+// (part [A][nq]: the fragments' partial sums of h g).
+hipError_t launch_topk_w_grad(const float* part, int nq, const int32_t* row_dest, int T, int k,
+                              float* d_topk_w, hipStream_t stream);
 // d_logits [T,E] of the softmax over the k selected logits.
 hipError_t launch_route_backward(const int32_t* topk_ids, const float* topk_w,
                                  const float* d_topk_w, int T, int E, int k, float* d_logits,

@@ -402,13 +402,15 @@ int moe_forward_mxfp4(const moe_bf16* x, const float* logits, int T, int H, int 
  *   dW_gate[e] = x_perm_e^T dG_e, dW_up[e] = x_perm_e^T dU_e,
  *   dW_down[e] = h_e^T dy_e   (sums over the expert's rows; 0 for an expert
  *                              with no rows).
- * The forward is recomputed inside (nothing is kept from moe_forward); h,
- * G, U, dy, dG and dU are rounded to bf16 between the steps, every product
- * accumulates in fp32. Routed experts only (no shared expert); weights in
- * the row-major layout of moe_forward. */
+ * The gate/up half of the forward is recomputed inside (nothing is kept
+ * from moe_forward); the product with W_down^T is taken on the unweighted
+ * dout (g = dout W_down^T, dh = w g), so d_topk_w = <h, g> needs no
+ * recomputed y. h, G, U, dy (for dW_down), dG and dU are rounded to bf16
+ * between the steps, every product accumulates in fp32. Routed experts
+ * only (no shared expert); weights in the row-major layout of moe_forward. */
 
 /* Bytes of the workspace moe_backward needs (0 for invalid sizes):
- * about T*k*(16 H + 10 F) bytes. */
+ * about T*k*(14 H + 10.25 F) bytes. */
 size_t moe_backward_workspace_bytes(int T, int H, int F, int E, int k);
 
 /* Gradients of the routed layer for a given routing (topk_ids, topk_w
