@@ -753,7 +753,7 @@ int moe_backward(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w
   float* dxp = reinterpret_cast<float*>(base + L.dxp);
   const int M = static_cast<int>(A);
 
-  // forward recompute: permutation (x_perm is kept for the weight
+  // recompute: permutation (x_perm is kept for the weight
   // gradients) and gate/up storing G and U beside h (the down projection is
   // not needed: the routing-weight gradient comes from dh's epilogue)
   MOE_TRY(hip_status(moe::launch_hist(topk_ids, T, E, k, hist, s)));
