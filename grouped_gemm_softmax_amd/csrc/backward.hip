@@ -60,19 +60,24 @@ __global__ __launch_bounds__(kPrepThreads) void backward_prep_kernel(
 }
 
 // --- routing-weight gradient --------------------------------------------------
-// d_topk_w[t,j] = <dout[t], y[p]> = <h[p], g[p]> (g = dout W_down^T), as the
-// sum of the dh GEMM's per-fragment partial sums of row p, in fragment order.
+// d_topk_w[t,j] = <dout[t], y[p]> = <h[p], g[p]> (g = dout W_down^T), the sum
+// of the dh GEMM's per-fragment partial sums of row p. One wave per
+// assignment: lane l adds fragments l, l + 64, ... in order, then the lanes
+// are added by a fixed butterfly, so the result does not depend on timing.
 __global__ __launch_bounds__(256) void topk_w_grad_kernel(
     const float* __restrict__ part, int nq, const int32_t* __restrict__ row_dest, int64_t n,
     float* __restrict__ d_topk_w) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= n) return;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (i >= n) return;  // whole waves
   int64_t p = row_dest[i];
   p = p < 0 ? 0 : (p >= n ? n - 1 : p);
   const float* r = part + p * nq;
   float s = 0.f;
-  for (int q = 0; q < nq; ++q) s += r[q];
-  d_topk_w[i] = s;
+  for (int q = lane; q < nq; q += kWave) s += r[q];
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, kWave);
+  if (lane == 0) d_topk_w[i] = s;
 }
 
 // --- route backward -----------------------------------------------------
@@ -278,8 +283,8 @@ hipError_t launch_topk_w_grad(const float* part, int nq, const int32_t* row_dest
                               float* d_topk_w, hipStream_t stream) {
   const int64_t n = static_cast<int64_t>(T) * k;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_w_grad_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
-                     0, stream, part, nq, row_dest, n, d_topk_w);
+  hipLaunchKernelGGL(topk_w_grad_kernel, dim3(static_cast<unsigned>((n + 3) / 4)), dim3(256), 0,
+                     stream, part, nq, row_dest, n, d_topk_w);
   return hipGetLastError();
 }
 

@@ -162,7 +162,7 @@ hipError_t launch_router(const RouterPlan& p, const bf16_t* x, const bf16_t* w, 
 hipError_t launch_backward_prep(const bf16_t* dout, const int32_t* row_dest,
                                 const float* topk_w, int T, int H, int k, bf16_t* dy,
                                 bf16_t* dout_perm, float* wrow, hipStream_t stream);
-// d_topk_w[t,j] = sum over q of part[p][q], p = row_dest[t,j], in q order
+// d_topk_w[t,j] = sum over q of part[p][q], p = row_dest[t,j], in a fixed order
 // (part [A][nq]: the fragments' partial sums of h g).
 hipError_t launch_topk_w_grad(const float* part, int nq, const int32_t* row_dest, int T, int k,
                               float* d_topk_w, hipStream_t stream);
