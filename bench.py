@@ -1,37 +1,46 @@
 #!/usr/bin/env python3
-"""Throughput of the fused MoE expert layer on one MI355X.
+"""Throughput of the fused MoE expert layer on one MI355X, against T.
 
-Workload: the Mixtral-8x7B-shaped MoE layer (H=4096, F=14336, E=8 experts,
-top-2, SwiGLU experts, bf16) at a batch of T=32 tokens, router logits
-~ N(0,1), inputs already resident in HBM. A step is one moe_forward_packed
-call (route -> permute -> gate/up+SwiGLU -> down -> combine, 5 launches) on
-weights packed once beforehand (moe_pack_weights, as at model load; its time
-is reported as `pack_ms`, outside the steps); `rowmajor_ms_per_step` is the
-same step on the row-major weights (moe_forward), for comparison.
+Headline workload: the Mixtral-8x7B-shaped MoE layer at large batch (H=4096,
+F=14336, E=8 experts, top-2, SwiGLU experts, bf16) at T=8192 tokens, router
+logits ~ N(0,1) plus a per-expert bias ~ N(0,0.5), inputs already resident in
+HBM: the largest-FLOP configuration, bound by the matrix cores. A step is one
+moe_forward_packed call (route -> permute -> gate/up+SwiGLU -> down ->
+combine, 5 launches) on weights packed once beforehand (moe_pack_weights, as
+at model load; `pack_ms`, outside the steps); `rowmajor_ms_per_step` is the
+same step on the row-major weights (moe_forward).
 
-Metric: MoE-layer HBM GB/s (algorithmic bytes / time), with TFLOP/s and the
-roofline fractions beside it. `roofline` describes the dominant kernel (the
-gate/up+SwiGLU grouped GEMM), timed with HIP events on its launch stream.
-`cpu_baseline` is the CPU oracle timed on a bounded sample of the same
-workload. `--sweep 1,128,512` repeats the measurement at other batch sizes of
-the same layer shape (listed under `sweep`).
+Timing: before every timed step a 512 MiB buffer is read (outside the timed
+interval), so that neither the 4 MB L2s nor the 256 MB Infinity Cache hold
+the previous step's weights; each step is timed alone with HIP events on
+its stream. `ms_per_step` is the median, with p10/p90 and the mean beside it.
+`value` is the layer's algorithmic TFLOP/s at the median. `roofline`
+describes the dominant kernel (the gate/up+SwiGLU grouped GEMM, 2/3 of the
+FLOPs and of the weight bytes), its launches timed the same way.
 
-`--weights mxfp4` likewise on MXFP4 weights (E2M1 codes, one E8M0 scale per
-32 K-values of a column; moe_forward_mxfp4), 4.25 bits per weight.
-`--weights fp8` times the layer on FP8 (E4M3) weights with per-column
-scales (moe_forward_fp8; bf16 activations and MFMA), which computes exactly
-the bf16 layer on the dequantized weights at half the weight bytes.
-`--router` instead times the router projection fused with routing
-(moe_router_route) at every layer shape, against the unfused sequence.
-`--backward` times the training backward (moe_backward) of --config at --T.
+`sweep` (default: every configured layer and batch size, `--sweep none` to
+skip) repeats the measurement for the tiny, Mixtral-, DeepSeek-V3- and
+Qwen2-MoE-shaped layers at each of their batch sizes: ms, TFLOP/s, GB/s,
+binding roof, roofline fraction, gate/up kernel time, and the row-major
+step. `cpu_baseline` is the CPU oracle timed on a bounded sample of the
+headline workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+`--weights fp8` / `--weights mxfp4` time the layer on FP8 (E4M3, per-column
+scales; moe_forward_fp8) or MXFP4 (E2M1 with an E8M0 scale per 32 K-values
+of a column; moe_forward_mxfp4) weights instead, which compute exactly the
+bf16 layer on the dequantized weights. `--router` instead times the router
+projection fused with routing (moe_router_route) at every layer shape,
+against the unfused sequence. `--backward` times the training backward
+(moe_backward) of --config at --T.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C --T t]
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -42,22 +51,26 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer TFLOP/s and HBM GB/s (roofline %) vs tokens T, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+FLUSH_BYTES = 512 << 20     # read before every timed step (L2 + MALL flush)
+SWEEP_ALL = [("tiny", 64), ("mixtral", 1), ("mixtral", 32), ("mixtral", 128), ("mixtral", 512),
+             ("mixtral_large", 2048), ("mixtral_large", 8192), ("dsv3", 128), ("dsv3", 4096),
+             ("qwen2", 16), ("qwen2", 1024), ("qwen2", 16384)]
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="mixtral")
-    ap.add_argument("--T", type=int, default=32)
-    ap.add_argument("--sweep", default="",
-                    help="other batch sizes of the same layer to measure, e.g. '1,128,512' "
-                         "(off by default, so that a kernel-trace of the default run "
-                         "averages the headline kernels only)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral_large")
+    ap.add_argument("--T", type=int, default=8192)
+    ap.add_argument("--sweep", default="all",
+                    help="'all' (every configured layer and batch size), 'none', or a list "
+                         "like 'mixtral:1,qwen2:16'")
+    ap.add_argument("--sweep-steps", type=int, default=10)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=32,
+    ap.add_argument("--cpu-tokens", type=int, default=64,
                     help="tokens in the oracle's timed sample")
     ap.add_argument("--weights", choices=("packed", "rowmajor", "fp8", "mxfp4"),
                     default="packed",
@@ -112,13 +125,14 @@ def work_model(cfg, T, counts, wb=2):
     return total_b, total_f, m, Et
 
 
-def measured_traffic(workload_is_default: bool, weights: str):
-    """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
-    FETCH_SIZE/WRITE_SIZE counters (copy-calibrated), or None when they were
-    taken on other kernel sources or another workload."""
+def measured_traffic(config: str, T: int, weights: str):
+    """HBM bytes per launch of the gate/up kernel of this workload from the
+    committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters (copy-calibrated,
+    profiles/gateup_swiglu_<config>_t<T>_traffic.json), or None when there
+    are none or they were taken on other kernel sources or weights."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "gateup_swiglu_mixtral_t32_traffic.json")
-    if not workload_is_default or not os.path.exists(path):
+    path = os.path.join(ROOT, "profiles", f"gateup_swiglu_{config}_t{T}_traffic.json")
+    if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
@@ -129,6 +143,27 @@ def measured_traffic(workload_is_default: bool, weights: str):
         with open(os.path.join(ROOT, src), "rb") as f:
             h.update(f.read())
     return d["traffic_bytes_per_launch"] if h.hexdigest() == d["kernel_sources_sha256"] else None
+
+
+def activation_bytes(cfg, T):
+    """Activation bytes moved between the layer's steps (weights excluded):
+    the fused path as built against an unfused one. Fused, large batch: the
+    gate/up tiles read x through the row map (no x_perm copy), h is written
+    and read once in bf16, the down projection's fp32 output is written and
+    read once by the combine, out written once. Unfused (each step its own
+    kernel over HBM): x_perm written, read by the gate and by the up GEMM, G
+    and U written and read by a SwiGLU kernel that writes h, h read by the
+    down GEMM, y written and read by the combine (all bf16), out written.
+    Shared expert and routing excluded (the same in both)."""
+    A, H, F = T * cfg.k, cfg.H, cfg.F
+    unfused = 2 * A * (5 * H + 6 * F) + 2 * T * H
+    fused = 2 * A * H + 4 * A * F + 8 * A * H + 2 * T * H
+    return fused, unfused
+
+
+def pct(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
 
 
 def roof(bytes_, flops, ms):
@@ -246,6 +281,23 @@ def backward_line(args, torch, B, synth):
                       "data": "synthetic"}), flush=True)
 
 
+def host_cpu():
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return model, usable
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -280,208 +332,272 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = synth.CONFIGS[args.config]
     stream = torch.cuda.current_stream()
+    flush_buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    mode = args.weights
+    WBYTES = {"fp8": 1, "mxfp4": 0.5 + 1 / 32}.get(mode, 2)
 
-    def layer_for(T, weights_from=None):
-        if weights_from is None:
-            return synth.make_layer(cfg.name, T, seed=args.seed, device=dev)
-        lay = synth.make_layer(cfg.name, T, seed=args.seed, device=dev, with_weights=False)
-        lay.w_gate, lay.w_up, lay.w_down = (weights_from.w_gate, weights_from.w_up,
-                                            weights_from.w_down)
-        if lay.shared is not None:
-            lay.shared = dict(weights_from.shared, gate_logits=lay.shared["gate_logits"])
-        return lay
+    def flush():
+        # read (not write) the buffer: the caches then hold other, clean lines,
+        # and no write-back of dirty flush data competes with the timed step
+        torch.sum(flush_buf)
 
-    def weights_of(layer, mode):
-        """(w_gate, w_up, w_down, shared) of a layer in the timed layout."""
-        if mode == "rowmajor":
-            return layer.w_gate, layer.w_up, layer.w_down, layer.shared
-        src = pk8 if mode in ("fp8", "mxfp4") else pk
-        return (src["wg"], src["wu"], src["wd"],
-                None if layer.shared is None else dict(src["shared"],
-                                                       gate_logits=layer.shared["gate_logits"]))
+    def timed_steps(fn, steps, warmup):
+        """Per-step milliseconds (HIP events on the launch stream around each
+        step alone, the cache flush before it outside the events), and the
+        wall time of the whole timed region (flushes included)."""
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        t0 = time.perf_counter()
+        for a, b in ev:
+            flush()
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return [a.elapsed_time(b) for a, b in ev], wall
 
-    def measure(layer, steps, warmup, mode):
-        T, H, F, E, k = layer.T, cfg.H, cfg.F, cfg.E, cfg.k
-        wg, wu, wd, sh = weights_of(layer, mode)
-        Fs = cfg.Fs
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-        w = torch.empty((T, k), dtype=torch.float32, device=dev)
-        ws = torch.empty(B.moe_forward_workspace_bytes(T, H, F, E, k, Fs),
-                         dtype=torch.uint8, device=dev)
+    def stats(ms):
+        return dict(ms_median=round(pct(ms, 50), 5), ms_p10=round(pct(ms, 10), 5),
+                    ms_p90=round(pct(ms, 90), 5), ms_mean=round(float(np.mean(ms)), 5))
+
+    class Workload:
+        """One layer's weights (row-major and in the timed layout)."""
+
+        def __init__(self, cfg_name):
+            self.cfg = synth.CONFIGS[cfg_name]
+            self.layer = synth.make_layer(cfg_name, 1, seed=args.seed, device=dev)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pack = B.moe_pack_weights
+            L = self.layer
+            self.pk = dict(wg=pack(L.w_gate), wu=pack(L.w_up), wd=pack(L.w_down))
+            if L.shared is not None:
+                self.pk["shared"] = {n: pack(L.shared[n]) for n in ("w_gate", "w_up", "w_down")}
+            e1.record(stream)
+            torch.cuda.synchronize()
+            self.pack_ms = e0.elapsed_time(e1)
+            self.q, self.quant_ms = None, None
+            if mode in ("fp8", "mxfp4"):
+                quant = B.moe_quantize_fp8 if mode == "fp8" else B.moe_quantize_mxfp4
+                e0.record(stream)
+                self.q = dict(wg=quant(L.w_gate), wu=quant(L.w_up), wd=quant(L.w_down))
+                if L.shared is not None:
+                    self.q["shared"] = {n: quant(L.shared[n]) for n in ("w_gate", "w_up", "w_down")}
+                e1.record(stream)
+                torch.cuda.synchronize()
+                self.quant_ms = e0.elapsed_time(e1)
+
+        def weights(self, m, batch):
+            L = self.layer
+            if m == "rowmajor":
+                src = dict(wg=L.w_gate, wu=L.w_up, wd=L.w_down,
+                           shared=None if L.shared is None else
+                           {n: L.shared[n] for n in ("w_gate", "w_up", "w_down")})
+            else:
+                src = self.q if m in ("fp8", "mxfp4") else self.pk
+            sh = None
+            if self.cfg.Fs:
+                sh = dict(src["shared"], gate_logits=batch.shared["gate_logits"])
+            return src["wg"], src["wu"], src["wd"], sh
+
+        def batch(self, T):
+            return synth.make_layer(self.cfg.name, T, seed=args.seed, device=dev,
+                                    with_weights=False)
+
+    def measure(wl, batch, m, steps, warmup):
+        cfg, T = wl.cfg, batch.T
+        wg, wu, wd, sh = wl.weights(m, batch)
+        out = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+        ids = torch.empty((T, cfg.k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, cfg.k), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(B.moe_forward_workspace_bytes(T, cfg.H, cfg.F, cfg.E, cfg.k, cfg.Fs),
+                             16), dtype=torch.uint8, device=dev)
 
         def step():
-            B.moe_forward(layer.x, layer.logits, k, wg, wu, wd, shared=sh, out=out,
+            B.moe_forward(batch.x, batch.logits, cfg.k, wg, wu, wd, shared=sh, out=out,
                           topk_ids=ids, topk_w=w, ws=ws, stream=stream)
 
-        for _ in range(warmup):
-            step()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
-        counts = torch.bincount(ids.flatten().long(), minlength=E).cpu().numpy()
-        return ms, counts
+        ms, wall = timed_steps(step, steps, warmup)
+        counts = torch.bincount(ids.flatten().long(), minlength=cfg.E).cpu().numpy()
+        return ms, wall, counts
 
-    def time_gateup(layer, steps, mode):
-        """Average duration of the gate/up+SwiGLU grouped GEMM alone, with the
-        same inputs, weights and launch configuration as inside the step."""
-        k = cfg.k
-        wg, wu, _, _ = weights_of(layer, mode)
-        ids, w = B.moe_route(layer.logits, k, stream=stream)
-        off, rt, rd, xp = B.moe_permute(layer.x, ids, cfg.E, stream=stream)
+    def gateup_ms(wl, batch, m, steps):
+        """Launches of the gate/up+SwiGLU grouped GEMM over the routed experts
+        alone (moe_gateup_swiglu with the layer's weights and routing), each
+        timed like a step."""
+        cfg = wl.cfg
+        wg, wu, _, _ = wl.weights(m, batch)
+        ids, _ = B.moe_route(batch.logits, cfg.k, stream=stream)
+        off, _, _, xp = B.moe_permute(batch.x, ids, cfg.E, stream=stream)
         h = torch.empty((xp.shape[0], cfg.F), dtype=torch.bfloat16, device=dev)
-        for _ in range(3):
-            B.moe_gateup_swiglu(xp, off, wg, wu, h=h, stream=stream)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            B.moe_gateup_swiglu(xp, off, wg, wu, h=h, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
+        ms, _ = timed_steps(lambda: B.moe_gateup_swiglu(xp, off, wg, wu, h=h, stream=stream),
+                            steps, 2)
+        return ms
+
+    def row(wl, T, steps, warmup, with_rowmajor=True):
+        batch = wl.batch(T)
+        ms, wall, counts = measure(wl, batch, mode, steps, warmup)
+        st = stats(ms)
+        tb, tf, per, et = work_model(wl.cfg, T, counts, WBYTES)
+        r = roof(tb, tf, st["ms_median"])
+        g_ms = gateup_ms(wl, batch, mode, steps)
+        g = per["gateup_swiglu_routed"]
+        gr = roof(g["bytes"], g["flops"], float(np.mean(g_ms)))
+        d = dict(config=wl.cfg.name, T=T, **st, TFLOPs=round(r["tflops"], 2),
+                 GBs=round(r["gbs"], 1), bound=r["bound"], hbm_frac=round(r["hbm_frac"], 4),
+                 mfma_frac=round(r["mfma_frac"], 4), roofline_frac=round(r["roofline_frac"], 4),
+                 gateup_ms=round(float(np.mean(g_ms)), 5), gateup_bound=gr["bound"],
+                 gateup_frac=round(gr["hbm_frac"] if gr["bound"] == "hbm" else gr["mfma_frac"], 4),
+                 experts_touched=et)
+        if with_rowmajor and mode == "packed":
+            ms_rm, _, _ = measure(wl, batch, "rowmajor", max(3, steps // 2), 2)
+            d["rowmajor_ms_median"] = round(pct(ms_rm, 50), 5)
+        return d, dict(ms=ms, wall=wall, counts=counts, work=(tb, tf, per, et), r=r,
+                       g_ms=g_ms, g=g, gr=gr)
 
     # ---- headline workload ----
-    layer = layer_for(args.T)
-    mode = args.weights
-    torch.cuda.synchronize()
-    # one-off weight packing (model-load time), timed on its own
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    pk = dict(wg=B.moe_pack_weights(layer.w_gate, stream=stream),
-              wu=B.moe_pack_weights(layer.w_up, stream=stream),
-              wd=B.moe_pack_weights(layer.w_down, stream=stream))
-    if layer.shared is not None:
-        pk["shared"] = {n: B.moe_pack_weights(layer.shared[n], stream=stream)
-                        for n in ("w_gate", "w_up", "w_down")}
-    e1.record(stream)
-    torch.cuda.synchronize()
-    pack_ms = e0.elapsed_time(e1)
-    pk8, quant_ms = None, None
-    if mode in ("fp8", "mxfp4"):
-        quant = B.moe_quantize_fp8 if mode == "fp8" else B.moe_quantize_mxfp4
-        e0.record(stream)
-        pk8 = dict(wg=quant(layer.w_gate, stream=stream),
-                   wu=quant(layer.w_up, stream=stream),
-                   wd=quant(layer.w_down, stream=stream))
-        if layer.shared is not None:
-            pk8["shared"] = {n: quant(layer.shared[n], stream=stream)
-                             for n in ("w_gate", "w_up", "w_down")}
-        e1.record(stream)
-        torch.cuda.synchronize()
-        quant_ms = e0.elapsed_time(e1)
-    other = {"packed": "rowmajor", "rowmajor": "packed", "fp8": "packed", "mxfp4": "packed"}[mode]
-    WBYTES = {"fp8": 1, "mxfp4": 0.5 + 1 / 32}.get(mode, 2)
-    ms, counts = measure(layer, args.steps, args.warmup, mode)
-    ms_other, _ = measure(layer, max(10, args.steps // 2), 5, other)
-    total_b, total_f, per_kernel, Et = work_model(cfg, args.T, counts, WBYTES)
-    r = roof(total_b, total_f, ms)
-
-    g1_ms = time_gateup(layer, max(args.steps, 20), mode)
-    g1 = per_kernel["gateup_swiglu_routed"]
-    g1r = roof(g1["bytes"], g1["flops"], g1_ms)
-    if g1r["bound"] == "hbm":
-        roofline = dict(bound="hbm", achieved=round(g1r["gbs"], 1), peak=PEAK_HBM_GBS,
-                        unit="GB/s", frac=round(g1r["gbs"] / PEAK_HBM_GBS, 4), traffic=None)
+    wl = Workload(args.config)
+    cfg, T = wl.cfg, args.T
+    head, raw = row(wl, T, args.steps, args.warmup)
+    tb, tf, per, Et = raw["work"]
+    r, gr, g = raw["r"], raw["gr"], raw["g"]
+    g_mean = float(np.mean(raw["g_ms"]))
+    if gr["bound"] == "hbm":
+        roofline = dict(bound="hbm", achieved=round(gr["gbs"], 1), peak=PEAK_HBM_GBS,
+                        unit="GB/s", frac=round(gr["gbs"] / PEAK_HBM_GBS, 4))
     else:
-        roofline = dict(bound="mfma", achieved=round(g1r["tflops"], 1), peak=PEAK_BF16_TFLOPS,
-                        unit="TFLOP/s", frac=round(g1r["tflops"] / PEAK_BF16_TFLOPS, 4),
-                        traffic=None)
-    roofline["traffic"] = measured_traffic(args.config == "mixtral" and args.T == 32 and
-                                           args.seed == 0, args.weights)
-    # the gate/up launch of the step: rs_gateup_kernel (register-streaming)
-    # for packed bf16 weights at decode sizes, grouped_gemm_kernel otherwise
+        roofline = dict(bound="mfma", achieved=round(gr["tflops"], 1), peak=PEAK_BF16_TFLOPS,
+                        unit="TFLOP/s", frac=round(gr["tflops"] / PEAK_BF16_TFLOPS, 4))
+    roofline["traffic"] = measured_traffic(args.config, T, mode)
     roofline.update(kernel="gate/up + SwiGLU grouped GEMM over the routed experts "
                            "(moe_gateup_swiglu" + ("" if mode == "rowmajor" else "_" + mode) +
-                           "; rs_gateup_kernel for packed bf16 weights at up to 16 items "
-                           "per CU, grouped_gemm_kernel otherwise)",
-                    kernel_ms=round(g1_ms, 5),
-                    alg_bytes=g1["bytes"], alg_flops=g1["flops"])
+                           "; grouped_gemm_kernel, or rs_gateup_kernel for packed bf16/fp8 "
+                           "weights at decode sizes)",
+                    kernel_ms=round(g_mean, 5), kernel_ms_p10=round(pct(raw["g_ms"], 10), 5),
+                    kernel_ms_p90=round(pct(raw["g_ms"], 90), 5),
+                    alg_bytes=g["bytes"], alg_flops=g["flops"])
+    act_f, act_u = activation_bytes(cfg, T)
+    pack_ms, quant_ms = wl.pack_ms, wl.quant_ms
+    host_layer = wl.layer if not args.no_cpu_baseline else None
+    head_batch = wl.batch(min(T, args.cpu_tokens)) if host_layer is not None else None
+    del wl
+    torch.cuda.empty_cache()
 
-    # ---- the other batch sizes of the same layer shape ----
+    # ---- every configured layer and batch size ----
     sweep = []
-    for tok in [int(s) for s in args.sweep.split(",") if s.strip()]:
-        if tok == args.T:
-            continue
-        lay = layer_for(tok, weights_from=layer)
-        ms_t, counts_t = measure(lay, max(10, args.steps // 2), 5, mode)
-        b_t, f_t, _, et_t = work_model(cfg, tok, counts_t, WBYTES)
-        rr = roof(b_t, f_t, ms_t)
-        sweep.append(dict(T=tok, ms_per_step=round(ms_t, 5), GBs=round(rr["gbs"], 1),
-                          TFLOPs=round(rr["tflops"], 2), hbm_frac=round(rr["hbm_frac"], 4),
-                          mfma_frac=round(rr["mfma_frac"], 4), bound=rr["bound"],
-                          roofline_frac=round(rr["roofline_frac"], 4),
-                          experts_touched=et_t))
-        del lay
+    if args.sweep != "none":
+        if args.sweep == "all":
+            todo = SWEEP_ALL
+        else:
+            todo = [(a.split(":")[0], int(a.split(":")[1])) for a in args.sweep.split(",") if a]
+        cur = None
+        for name, t in todo:
+            if cur is None or cur.cfg.name != name:
+                cur = None
+                torch.cuda.empty_cache()
+                cur = Workload(name)
+            d, _ = row(cur, t, args.sweep_steps, 3)
+            sweep.append(d)
+            print(json.dumps({"sweep_row": d}), file=sys.stderr, flush=True)
+        cur = None
+        torch.cuda.empty_cache()
 
     # ---- CPU oracle on a bounded sample of the headline workload ----
     cpu = None
-    if not args.no_cpu_baseline:
+    if host_layer is not None:
         from oracle import oracle
-        n = min(args.cpu_tokens, args.T)
-        x = synth.u16(layer.x[:n])
-        lg = synth.f32(layer.logits[:n])
-        wg, wu, wd = synth.u16(layer.w_gate), synth.u16(layer.w_up), synth.u16(layer.w_down)
-        # repeated until about 10 s of CPU work have been timed (a short
-        # sample is run several times and averaged)
-        runs, t0 = 0, time.perf_counter()
-        while True:
-            oracle.forward(x, lg, cfg.k, wg, wu, wd, keep_intermediates=False)
-            runs += 1
-            t_all = time.perf_counter() - t0
-            if t_all >= 10.0 or runs >= 500:
-                break
+        n = head_batch.T
+        x = synth.u16(head_batch.x)
+        lg = synth.f32(head_batch.logits)
+        wg, wu, wd = (synth.u16(host_layer.w_gate), synth.u16(host_layer.w_up),
+                      synth.u16(host_layer.w_down))
+        sh = None
+        if cfg.Fs:
+            gl = head_batch.shared["gate_logits"]
+            sh = dict(w_gate=synth.u16(host_layer.shared["w_gate"]),
+                      w_up=synth.u16(host_layer.shared["w_up"]),
+                      w_down=synth.u16(host_layer.shared["w_down"]),
+                      gate_logits=None if gl is None else synth.f32(gl))
+        # the sample's FLOPs: the same per-token work as the layer
+        f_tok = tf / T
+
+        def run_for(seconds, ntok):
+            shn = None if sh is None else dict(
+                sh, gate_logits=None if sh["gate_logits"] is None else sh["gate_logits"][:ntok])
+            runs, t0 = 0, time.perf_counter()
+            while True:
+                oracle.forward(x[:ntok], lg[:ntok], cfg.k, wg, wu, wd, shared=shn,
+                               keep_intermediates=False)
+                runs += 1
+                t_all = time.perf_counter() - t0
+                if t_all >= seconds or runs >= 500:
+                    return runs, t_all
+
+        runs, t_all = run_for(10.0, n)
         t_cpu = t_all / runs
-        t_full = t_cpu * args.T / n        # the oracle's cost is linear in tokens
-        cpu = dict(value=round(total_b / t_full / 1e9, 3), unit="GB/s",
-                   cores=oracle.num_threads(), kind="oracle",
-                   sample=f"first {n} of {args.T} tokens, whole layer (oracle.forward, fp64), "
-                          f"{runs} runs in {t_all:.1f} s ({t_cpu:.3f} s each); scaled "
-                          f"linearly to the {args.T}-token step",
-                   seconds_sample=round(t_cpu, 3))
+        threads = oracle.num_threads()
+        oracle.set_num_threads(1)
+        n1 = min(n, 4)                      # single thread: a 4-token sample
+        runs1, t_all1 = run_for(2.0, n1)
+        oracle.set_num_threads(threads)
+        model, usable = host_cpu()
+        cpu = dict(value=round(f_tok * n / t_cpu / 1e12, 5), unit="TFLOP/s", cores=threads,
+                   kind="oracle",
+                   sample=f"first {n} of {T} tokens of the headline layer, whole layer "
+                          f"(oracle.forward, fp64, OpenMP over rows), {runs} runs in "
+                          f"{t_all:.1f} s ({t_cpu:.3f} s each); the layer's FLOPs per token "
+                          f"times {n} tokens per run",
+                   seconds_sample=round(t_cpu, 4),
+                   single_thread_value=round(f_tok * n1 / (t_all1 / runs1) / 1e12, 5),
+                   single_thread_sample=f"first {n1} tokens, {runs1} runs in {t_all1:.1f} s",
+                   host_cpu=model, host_cpus_usable=usable)
 
     line = {
         "metric": METRIC,
-        "value": round(r["gbs"], 2),
-        "unit": "GB/s",
+        "value": head["TFLOPs"],
+        "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": head["ms_median"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "weight_dtype": {"fp8": "fp8_e4m3", "mxfp4": "mxfp4_e2m1"}.get(mode, "bf16"),
-        "data": "synthetic (seeded; x~N(0,1), weights~N(0,0.02), logits~N(0,1))",
-        "config": {"workload": f"{cfg.desc}: T={args.T}, H={cfg.H}, F={cfg.F}, E={cfg.E}, "
-                               f"top-{cfg.k}, bf16, "
-                               + ({"fp8": "fp8 E4M3 weights with per-column scales",
-                                   "mxfp4": "MXFP4 weights (E2M1, E8M0 scale per 32)"}
-                                  .get(mode, f"{args.weights} weights")),
-                   "weights": args.weights,
-                   "T": args.T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "k": cfg.k,
+        "data": "synthetic (seeded; x~N(0,1), weights~N(0,0.02), logits~N(0,1) "
+                "(+ per-expert bias N(0,0.5) at large batch, Zipf(1.2)+Gumbel for the "
+                "DeepSeek-V3 shape))",
+        "config": {"workload": f"{cfg.desc}: T={T}, H={cfg.H}, F={cfg.F}, E={cfg.E}, "
+                               f"top-{cfg.k}, bf16, " +
+                               ({"fp8": "fp8 E4M3 weights with per-column scales",
+                                 "mxfp4": "MXFP4 weights (E2M1, E8M0 scale per 32)"}
+                                .get(mode, f"{mode} weights")),
+                   "weights": mode, "T": T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "k": cfg.k,
                    "Fs": cfg.Fs, "experts_touched": Et, "parallelism": "none (1 GPU)"},
-        "TFLOPs": round(r["tflops"], 3),
-        "hbm_frac": round(r["hbm_frac"], 4),
-        "mfma_frac": round(r["mfma_frac"], 4),
-        "layer_bound": r["bound"],
-        "layer_roofline_frac": round(r["roofline_frac"], 4),
-        "alg_bytes": total_b,
-        "alg_flops": total_f,
-        other + "_ms_per_step": round(ms_other, 5),
+        "timing": "median of per-step HIP-event times, a 512 MiB read before each step to "
+                  "flush L2 and the Infinity Cache (outside the events)",
+        "ms_p10": head["ms_p10"], "ms_p90": head["ms_p90"], "ms_mean": head["ms_mean"],
+        "timed_region_s": round(raw["wall"], 4),
+        "GBs": head["GBs"],
+        "hbm_frac": head["hbm_frac"],
+        "mfma_frac": head["mfma_frac"],
+        "layer_bound": head["bound"],
+        "layer_roofline_frac": head["roofline_frac"],
+        "alg_bytes": tb,
+        "alg_flops": tf,
+        "rowmajor_ms_per_step": head.get("rowmajor_ms_median"),
         "pack_ms": round(pack_ms, 3),
         "quantize_ms": None if quant_ms is None else round(quant_ms, 3),
+        "activation_bytes_fused": act_f,
+        "activation_bytes_unfused": act_u,
+        "activation_bytes_ratio": round(act_f / act_u, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "sweep": sweep,

@@ -9,6 +9,8 @@ raises MoeError with the library's status text.
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 import re
 from typing import Optional
@@ -61,9 +63,11 @@ _SIGNATURES = {
     "moe_permute": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_gateup_swiglu": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_down": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
-    "moe_grouped_ffn": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "moe_grouped_ffn_workspace_bytes": (_SZ, [_I, _I]),
+    "moe_grouped_ffn": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
     "moe_forward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "moe_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "moe_forward_routed": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _P, _P,
                                 _SZ, _P]),
     "moe_forward": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P,
@@ -91,6 +95,7 @@ _SIGNATURES = {
     "moe_backward": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                           _P, _P, _SZ, _P]),
     "moe_route_backward": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
+    "moe_set_dispatch_override": (_I, [_I, _I]),
 }
 
 _lib = None
@@ -130,6 +135,26 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run a wrapper with `stream` (when one is given) as torch's current
+    stream, so that the tensors it allocates (outputs it creates, workspace it
+    frees on return) belong to the stream the library enqueues on: the caching
+    allocator then reuses a freed workspace block only for later work of that
+    stream, never while its kernels may still read or write it."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        bound = sig.bind(*args, **kwargs)
+        stream = bound.arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, **kwargs)
+
+    return wrapper
+
+
 def _check(status: int, call: str):
     if status != 0:
         raise MoeError(status, lib().moe_status_string(status).decode(), call)
@@ -146,6 +171,7 @@ def moe_status_string(status: int) -> str:
     return lib().moe_status_string(status).decode()
 
 
+@_on_stream
 def moe_route(logits: torch.Tensor, k: int, topk_ids=None, topk_w=None, stream=None):
     _need(logits, torch.float32, "logits")
     T, E = logits.shape
@@ -162,6 +188,7 @@ def moe_router_workspace_bytes(T: int, H: int, E: int, k: int) -> int:
     return int(lib().moe_router_workspace_bytes(T, H, E, k))
 
 
+@_on_stream
 def moe_router_route(x: torch.Tensor, w_router: torch.Tensor, k: int, logits=False,
                      ws=None, out=None, stream=None):
     """x bf16 [T,H], w_router bf16 [E,H] -> (topk_ids [T,k], topk_w [T,k]), plus
@@ -191,6 +218,7 @@ def moe_permute_workspace_bytes(T: int, E: int, k: int) -> int:
     return int(lib().moe_permute_workspace_bytes(T, E, k))
 
 
+@_on_stream
 def moe_permute(x: torch.Tensor, topk_ids: torch.Tensor, E: int, ws=None, out=None,
                 stream=None):
     """Returns (expert_offsets [E+1], row_token [T*k], row_dest [T,k], x_perm [T*k,H])."""
@@ -230,6 +258,7 @@ def moe_pack_weights_bytes(G: int, K: int, N: int) -> int:
     return int(lib().moe_pack_weights_bytes(G, K, N))
 
 
+@_on_stream
 def moe_pack_weights(w: torch.Tensor, stream=None) -> PackedWeight:
     """w bf16 [G,K,N] (or [K,N], taken as G = 1) -> PackedWeight."""
     _need(w, torch.bfloat16, "w")
@@ -264,6 +293,7 @@ def moe_fp8_weights_bytes(G: int, K: int, N: int) -> int:
     return int(lib().moe_fp8_weights_bytes(G, K, N))
 
 
+@_on_stream
 def moe_quantize_fp8(w: torch.Tensor, stream=None) -> Fp8Weight:
     """w bf16 [G,K,N] (or [K,N], taken as G = 1) -> Fp8Weight."""
     _need(w, torch.bfloat16, "w")
@@ -300,6 +330,7 @@ def moe_mxfp4_scales_bytes(G: int, K: int, N: int) -> int:
     return int(lib().moe_mxfp4_scales_bytes(G, K, N))
 
 
+@_on_stream
 def moe_quantize_mxfp4(w: torch.Tensor, stream=None) -> Mxfp4Weight:
     """w bf16 [G,K,N] (or [K,N], taken as G = 1) -> Mxfp4Weight."""
     _need(w, torch.bfloat16, "w")
@@ -326,6 +357,7 @@ def _same_kind(kind, w, name):
     return w
 
 
+@_on_stream
 def moe_gateup_swiglu(x_perm, expert_offsets, w_gate, w_up, h=None, stream=None):
     """w_gate, w_up: bf16 [E,H,F] tensors, PackedWeight (packed call) or
     Fp8Weight (fp8 call)."""
@@ -360,6 +392,7 @@ def moe_gateup_swiglu(x_perm, expert_offsets, w_gate, w_up, h=None, stream=None)
     return h
 
 
+@_on_stream
 def moe_down(h, expert_offsets, w_down, y_perm=None, stream=None):
     """w_down: bf16 [E,F,H] tensor, PackedWeight (packed call) or Fp8Weight."""
     kind = _quant_kind(w_down)
@@ -389,24 +422,34 @@ def moe_down(h, expert_offsets, w_down, y_perm=None, stream=None):
     return y_perm
 
 
-def moe_grouped_ffn(x_perm, expert_offsets, w_gate, w_up, w_down, h=None, y_perm=None,
+def moe_grouped_ffn_workspace_bytes(M: int, F: int) -> int:
+    return int(lib().moe_grouped_ffn_workspace_bytes(M, F))
+
+
+@_on_stream
+def moe_grouped_ffn(x_perm, expert_offsets, w_gate, w_up, w_down, y_perm=None, ws=None,
                     stream=None):
+    """Steps 3+4 with h in the workspace. Returns (h, y_perm): h [M,F] bf16 is
+    a view of the start of ws, where the library leaves it."""
     _need(x_perm, torch.bfloat16, "x_perm")
     _need(expert_offsets, torch.int32, "expert_offsets")
     for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
         _need(t, torch.bfloat16, n)
     M, H = x_perm.shape
     E, _, F = w_gate.shape
-    if h is None:
-        h = torch.empty((M, F), dtype=torch.bfloat16, device=x_perm.device)
     if y_perm is None:
         y_perm = torch.empty((M, H), dtype=torch.bfloat16, device=x_perm.device)
+    if ws is None:
+        ws = torch.empty(max(moe_grouped_ffn_workspace_bytes(M, F), 16), dtype=torch.uint8,
+                         device=x_perm.device)
     _check(lib().moe_grouped_ffn(_ptr(x_perm), _ptr(expert_offsets), M, H, F, E,
-                                 _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h),
-                                 _ptr(y_perm), _stream(stream)), "moe_grouped_ffn")
+                                 _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y_perm),
+                                 _ptr(ws), ws.numel(), _stream(stream)), "moe_grouped_ffn")
+    h = ws[:M * F * 2].view(torch.bfloat16).view(M, F)
     return h, y_perm
 
 
+@_on_stream
 def moe_combine(y_perm, row_dest, topk_w, out=None, stream=None):
     _need(y_perm, torch.bfloat16, "y_perm")
     _need(row_dest, torch.int32, "row_dest")
@@ -424,6 +467,18 @@ def moe_forward_workspace_bytes(T, H, F, E, k, Fs=0) -> int:
     return int(lib().moe_forward_workspace_bytes(T, H, F, E, k, Fs))
 
 
+def moe_workspace_bytes(T, H, F, E, k, Fs=0) -> int:
+    return int(lib().moe_workspace_bytes(T, H, F, E, k, Fs))
+
+
+def moe_set_dispatch_override(decode_path: int = -1, tile_class: int = -1):
+    """Testing hook: force the decode-size gate/up path (0 LDS ring, 1
+    register streaming) and the tile class (0 small, 1 mid, 2 128-row,
+    3 256-row) of later calls in this process; -1 is the automatic choice."""
+    _check(lib().moe_set_dispatch_override(decode_path, tile_class),
+           "moe_set_dispatch_override")
+
+
 def _shared_struct(shared, packed):
     if shared is None:
         return None, 0
@@ -436,6 +491,7 @@ def _shared_struct(shared, packed):
                         None if g is None else g.data_ptr()), Fs
 
 
+@_on_stream
 def moe_forward_routed(x, topk_ids, topk_w, w_gate, w_up, w_down,
                        shared: Optional[dict] = None, out=None, ws=None, stream=None):
     """Layer steps 2-5 from a given routing (topk_ids int32 [T,k], topk_w
@@ -463,6 +519,7 @@ def moe_forward_routed(x, topk_ids, topk_w, w_gate, w_up, w_down,
     return out
 
 
+@_on_stream
 def moe_forward(x, logits, k, w_gate, w_up, w_down, shared: Optional[dict] = None,
                 out=None, topk_ids=None, topk_w=None, ws=None, stream=None):
     """Whole layer. shared: None or dict(w_gate [H,Fs], w_up [H,Fs],
@@ -493,6 +550,7 @@ def moe_forward(x, logits, k, w_gate, w_up, w_down, shared: Optional[dict] = Non
     return out
 
 
+@_on_stream
 def _forward_quant(x, logits, k, w_gate, w_up, w_down, shared, out, topk_ids, topk_w, ws,
                    stream):
     """moe_forward_fp8 or moe_forward_mxfp4, by the weights' kind."""
@@ -532,6 +590,7 @@ def moe_backward_workspace_bytes(T, H, F, E, k) -> int:
     return int(lib().moe_backward_workspace_bytes(T, H, F, E, k))
 
 
+@_on_stream
 def moe_backward(x, topk_ids, topk_w, w_gate, w_up, w_down, dout, ws=None, stream=None):
     """Gradients of the routed layer (row-major bf16 weights) for the routing
     (topk_ids int32 [T,k], topk_w fp32 [T,k]) and the output gradient dout
@@ -562,6 +621,7 @@ def moe_backward(x, topk_ids, topk_w, w_gate, w_up, w_down, dout, ws=None, strea
     return g
 
 
+@_on_stream
 def moe_route_backward(topk_ids, topk_w, d_topk_w, E, d_logits=None, stream=None):
     """Router-logit gradient [T,E] fp32 through the softmax over the k
     selected logits."""

@@ -394,18 +394,27 @@ int moe_pack_weights(const moe_bf16* w, int G, int K, int N, moe_bf16* packed,
                                              static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_grouped_ffn_workspace_bytes(int M, int F) {
+  if (M < 0 || check_width(F) != MOE_OK || check_elems(M, F) != MOE_OK) return 0;
+  return align_up(static_cast<size_t>(M) * F * sizeof(bf16_t), 256);
+}
+
 int moe_grouped_ffn(const moe_bf16* x_perm, const int32_t* expert_offsets, int M,
                     int H, int F, int E, const moe_bf16* w_gate,
-                    const moe_bf16* w_up, const moe_bf16* w_down, moe_bf16* h,
-                    moe_bf16* y_perm, void* stream) {
-  MOE_TRY(check_ffn_args(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, true, h));
-  MOE_TRY(check_ffn_args(h, expert_offsets, M, F, H, E, w_down, nullptr, false, y_perm));
+                    const moe_bf16* w_up, const moe_bf16* w_down, moe_bf16* y_perm,
+                    void* ws, size_t ws_bytes, void* stream) {
+  // h lives at the start of the workspace
+  moe_bf16* h = static_cast<moe_bf16*>(ws);
+  MOE_TRY(check_ffn_args(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, true,
+                         M == 0 ? nullptr : h));
+  MOE_TRY(check_ffn_args(x_perm, expert_offsets, M, F, H, E, w_down, nullptr, false, y_perm));
   if (M == 0) return MOE_OK;
+  if (ws_bytes < moe_grouped_ffn_workspace_bytes(M, F)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   MOE_TRY(hip_status(moe::launch_grouped_gemm(
-      gateup_problem(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, h, false), s)));
+      gateup_problem(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, h, kRowMajor), s)));
   return hip_status(moe::launch_grouped_gemm(
-      down_problem(h, expert_offsets, M, F, H, E, w_down, y_perm, false), s));
+      down_problem(h, expert_offsets, M, F, H, E, w_down, y_perm, kRowMajor), s));
 }
 
 int moe_combine(const moe_bf16* y_perm, const int32_t* row_dest, const float* topk_w,
@@ -429,6 +438,17 @@ size_t moe_forward_workspace_bytes(int T, int H, int F, int E, int k, int Fs) {
       check_width(F) != MOE_OK || Fs < 0 || (Fs > 0 && check_width(Fs) != MOE_OK))
     return 0;
   return forward_layout(T, H, F, E, k, Fs, moe::grouped_gemm_device_cus()).total;
+}
+
+size_t moe_workspace_bytes(int T, int H, int F, int E, int k, int Fs) {
+  return moe_forward_workspace_bytes(T, H, F, E, k, Fs);
+}
+
+int moe_set_dispatch_override(int decode_path, int tile_class) {
+  if (decode_path < -1 || decode_path > 1 || tile_class < -1 || tile_class > 3)
+    return MOE_ERR_INVALID_ARG;
+  moe::set_dispatch_override(decode_path, tile_class);
+  return MOE_OK;
 }
 
 // The layer's weights in one layout (the shared expert's too, when Fs > 0).
@@ -788,10 +808,10 @@ int moe_backward(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w
   MOE_TRY(hip_status(moe::launch_topk_w_grad(part, (F + 15) / 16, row_dest, T, k, d_topk_w, s)));
   // dx: dG W_gate^T and dU W_up^T per row (fp32 slices), summed over the
   // token's k rows and the two slices by the combine with unit weights
-  for (int part = 0; part < 2; ++part) {
+  for (int slice = 0; slice < 2; ++slice) {
     moe::GemmProblem g4{};
-    g4.seg[0] = segment(part ? du : dg, offsets, part ? w_up : w_gate, nullptr,
-                        dxp + static_cast<int64_t>(part) * M * H, M, E, F, H,
+    g4.seg[0] = segment(slice ? du : dg, offsets, slice ? w_up : w_gate, nullptr,
+                        dxp + static_cast<int64_t>(slice) * M * H, M, E, F, H,
                         moe::kWeightsTransposed, nullptr, nullptr);
     g4.nseg = 1;
     g4.gated = false;

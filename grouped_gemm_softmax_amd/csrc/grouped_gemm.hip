@@ -50,9 +50,7 @@
 // packed weights (pack_weights_kernel) already hold each column's
 // K-values contiguously, so a lane reads its fragment with one 16-byte LDS
 // read. MFMA: v_mfma_f32_16x16x32_bf16, fp32 accumulation.
-#include <stdlib.h>
-#include <string.h>
-
+#include <atomic>
 #include <utility>
 
 #include "common.h"
@@ -392,11 +390,12 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     it.n0 = (local / mtiles) * C::BF;
     it.row_base = v.r0 + mt * C::BT;
     it.rows_valid = min(C::BT, v.M - mt * C::BT);
-    // K range of this slice: whole K-steps (the last step of K may be short)
+    // K range of this slice: whole K-steps (the last step of K may be short),
+    // split as evenly as the steps allow, so that no slice is empty when
+    // there are at least as many steps as slices (the plan keeps >= 4 per slice)
     const int nk_all = (S.K + C::BK - 1) / C::BK;
-    const int per = (nk_all + ksplit - 1) / ksplit;
-    it.kt_begin = ks * per;
-    it.nk = min(nk_all, it.kt_begin + per) - it.kt_begin;
+    it.kt_begin = ks * nk_all / ksplit;
+    it.nk = (ks + 1) * nk_all / ksplit - it.kt_begin;
     it.nk_all = nk_all;
     it.nblk = (S.N + 63) / 64;
     it.kblk = (S.K + 63) / 64;
@@ -1482,17 +1481,22 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
 // tile per touched group plus the full ones, times the column tiles) fill
 // the two workgroups per CU that tile runs with; with few groups (e.g. 8
 // experts of 128 rows and a long K) it keeps one 256-row tile per CU.
-// MOE_TILE=small|mid|large128|large overrides the choice (for tile sweeps).
+// set_dispatch_override (the library's testing hook) can force a class.
 enum TileClass { kSmall = 0, kMid = 1, kLarge128 = 2, kLarge = 3 };
 
+namespace {
+// Dispatch overrides (-1: automatic), set only through the testing hook.
+std::atomic<int> g_forced_tile{-1};
+std::atomic<int> g_forced_rs{-1};
+}  // namespace
+
+void set_dispatch_override(int decode_path, int tile_class) {
+  g_forced_rs.store(decode_path, std::memory_order_relaxed);
+  g_forced_tile.store(tile_class, std::memory_order_relaxed);
+}
+
 int tile_class(const GemmProblem& p) {
-  static int forced = -2;
-  if (forced == -2) {
-    const char* e = getenv("MOE_TILE");
-    forced = !e ? -1 : (!strcmp(e, "small") ? kSmall : !strcmp(e, "mid") ? kMid
-                        : !strcmp(e, "large128") ? kLarge128
-                        : !strcmp(e, "large") ? kLarge : -1);
-  }
+  const int forced = g_forced_tile.load(std::memory_order_relaxed);
   if (forced >= 0) return forced;
   const bool bf16 = p.seg[0].packed == 0 || p.seg[0].packed == 1;
   if (p.rows_hint < 16) return kSmall;
@@ -1830,11 +1834,9 @@ hipError_t launch_pack_weights(const bf16_t* w, int G, int K, int N, bf16_t* pac
 // win; fp8 22 % faster at T = 1 and 19 % at Qwen2-shaped T = 16, but 13 %
 // slower at Mixtral-shaped T = 32. On mxfp4 codes (one scale byte per 32
 // K-values of a column to load beside them) it was slower everywhere.
-// MOE_RS=0 / MOE_RS=1 force it off / on (for comparisons).
+// The testing hook's decode_path 0 / 1 forces it off / on (for comparisons).
 bool use_rs_gateup(const GemmProblem& p) {
-  // read at every launch, so that a process can compare both paths
-  const char* env = getenv("MOE_RS");
-  const int forced = env ? atoi(env) : -1;
+  const int forced = g_forced_rs.load(std::memory_order_relaxed);
   if (forced == 0) return false;
   if (p.epi != kEpiDefault) return false;
   int64_t items = 0;

@@ -108,6 +108,10 @@ bool grouped_gemm_gathers(const GemmProblem& prob);
 // a device with `cus` compute units; gated or bf16 problems keep 1.
 void grouped_gemm_plan_ksplit(GemmProblem& prob, int cus);
 int grouped_gemm_device_cus();
+// Testing hook: force the decode-size gate/up path (0 LDS-ring tile, 1
+// register-streaming kernel) and the tile class (0 small, 1 mid, 2 large128,
+// 3 large) of later launches; -1 restores the automatic choice.
+void set_dispatch_override(int decode_path, int tile_class);
 
 // Packed weights: W [G][K][N] as G x ceil(N/64) x ceil(K/64) blocks of
 // 64 x 64 (block (g, nb, kb) at element ((g*NB + nb)*KB + kb)*4096), each

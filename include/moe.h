@@ -32,15 +32,20 @@
  *   - `stream` is a hipStream_t (NULL = the default stream). Every call only
  *     enqueues work on it and returns without synchronising. Per-expert
  *     counts never travel to the host.
- *   - Arguments are validated on the host before anything is enqueued. On an
- *     error nothing is enqueued and no output is touched; the call returns a
- *     negative moe_status. MOE_ERR_HIP reports a failed kernel launch.
+ *   - Arguments are validated on the host before anything is enqueued: on a
+ *     validation error (every negative moe_status except MOE_ERR_HIP) nothing
+ *     is enqueued and no output is touched. MOE_ERR_HIP reports a HIP runtime
+ *     failure at a kernel launch; a call that makes several launches may then
+ *     have enqueued the ones before it, so its outputs and workspace are
+ *     unspecified.
  *   - Size limits: 0 <= T; 1 <= k <= min(E, 16); 1 <= E <= 1024;
  *     H, F (and Fs) multiples of 8; T*k*max(H, F, Fs) < 2^31. T = 0 is a
  *     successful no-op (then pointers are not inspected).
  *   - Alignment: bf16 tensors and workspaces 16 bytes; fp32 and int32
  *     arrays 4 bytes (MOE_ERR_MISALIGNED otherwise).
- *   - Calls are re-entrant; the only cached state is per-device properties.
+ *   - Calls are re-entrant; the only cached state is per-device properties
+ *     (and the process-wide setting of the testing hook
+ *     moe_set_dispatch_override, which only tests and benchmarks call).
  *   - Results are deterministic: the same inputs give bit-identical outputs.
  */
 #ifndef MOE_H_
@@ -156,13 +161,20 @@ int moe_down(const moe_bf16* h, const int32_t* expert_offsets, int M, int F,
              int H, int E, const moe_bf16* w_down, moe_bf16* y_perm,
              void* stream);
 
-/* Steps 3+4: moe_gateup_swiglu into h (caller-owned [M,F]), then moe_down
- * into y_perm [M,H]. Block-scheduled grouped GEMM over variable expert batch
- * sizes: the Triton MoE page (setupai.cc), key points. */
+/* Workspace needed by moe_grouped_ffn (device bytes): h bf16 [M,F] rounded
+ * up to 256 bytes; 0 for invalid sizes. */
+size_t moe_grouped_ffn_workspace_bytes(int M, int F);
+
+/* Steps 3+4: the gate/up+SwiGLU grouped GEMM (as moe_gateup_swiglu) into h,
+ * then the down grouped GEMM (as moe_down) into y_perm [M,H]. h lives in the
+ * workspace: ws (at least moe_grouped_ffn_workspace_bytes(M,F) device bytes,
+ * 16-byte aligned) holds h bf16 [M,F] at its start when the call's work is
+ * done. Block-scheduled grouped GEMM over variable expert batch sizes: the
+ * Triton MoE page (setupai.cc), key points. */
 int moe_grouped_ffn(const moe_bf16* x_perm, const int32_t* expert_offsets,
                     int M, int H, int F, int E, const moe_bf16* w_gate,
-                    const moe_bf16* w_up, const moe_bf16* w_down, moe_bf16* h,
-                    moe_bf16* y_perm, void* stream);
+                    const moe_bf16* w_up, const moe_bf16* w_down, moe_bf16* y_perm,
+                    void* ws, size_t ws_bytes, void* stream);
 
 /* Step 5, combine. out[t,c] = bf16( sum_{j<k} topk_w[t,j] * y_perm[row_dest[t,j], c] ),
  * fp32 accumulation in ascending j. y_perm bf16 [T*k,H]; row_dest int32 [T,k]
@@ -174,8 +186,9 @@ int moe_combine(const moe_bf16* y_perm, const int32_t* row_dest,
                 void* stream);
 
 /* Workspace needed by moe_forward (device bytes); Fs = 0 without a shared
- * expert; 0 for invalid sizes. */
+ * expert; 0 for invalid sizes. moe_workspace_bytes is the same function. */
 size_t moe_forward_workspace_bytes(int T, int H, int F, int E, int k, int Fs);
+size_t moe_workspace_bytes(int T, int H, int F, int E, int k, int Fs);
 
 /* The whole layer, steps 1-5, as five kernel launches on `stream` (the
  * launch count of the dispatch-kernel post (lumeric.app), summary paragraph):
@@ -392,21 +405,23 @@ int moe_forward_mxfp4(const moe_bf16* x, const float* logits, int T, int H, int 
  * training as well as inference; no page gives the backward, so these calls
  * are the chain rule through steps 2-5 and through the softmax of step 1.
  * With G = x_perm W_gate, U = x_perm W_up, h = silu(G) U, y = h W_down per
- * expert row, and the gradient dout of the layer's output out:
- *   dy       = w * dout[token]                  (per row, bf16)
- *   d_topk_w = <dout[t], y[row of (t,j)]>       (fp32)
- *   dh       = dy W_down^T
+ * expert row, w the row's routing weight and the gradient dout of the
+ * layer's output out:
+ *   g        = dout[token] W_down^T             (fp32, from the bf16 dout)
+ *   dh       = w * g                            (fp32)
+ *   d_topk_w = <dout[t], y[row of (t,j)]> = <h, g>   (fp32)
  *   dG       = dh * U * silu'(G),  dU = dh * silu(G),
  *              silu'(z) = s(z) (1 + z (1 - s(z))), s the logistic function
  *   dx[t]    = sum_j (dG W_gate^T + dU W_up^T)[row of (t,j)]
  *   dW_gate[e] = x_perm_e^T dG_e, dW_up[e] = x_perm_e^T dU_e,
- *   dW_down[e] = h_e^T dy_e   (sums over the expert's rows; 0 for an expert
+ *   dW_down[e] = h_e^T dy_e,  dy = bf16(w * dout[token]) per row
+ *                             (sums over the expert's rows; 0 for an expert
  *                              with no rows).
  * The gate/up half of the forward is recomputed inside (nothing is kept
  * from moe_forward); the product with W_down^T is taken on the unweighted
- * dout (g = dout W_down^T, dh = w g), so d_topk_w = <h, g> needs no
- * recomputed y. h, G, U, dy (for dW_down), dG and dU are rounded to bf16
- * between the steps, every product accumulates in fp32. Routed experts
+ * dout, so d_topk_w = <h, g> needs no recomputed y and no rounding of dy
+ * reaches dh. h, G, U, dy (for dW_down only), dG and dU are rounded to bf16
+ * between the steps; every product accumulates in fp32. Routed experts
  * only (no shared expert); weights in the row-major layout of moe_forward. */
 
 /* Bytes of the workspace moe_backward needs (0 for invalid sizes):
@@ -432,6 +447,17 @@ int moe_backward(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w
  * not selected (the selection itself has no gradient). */
 int moe_route_backward(const int32_t* topk_ids, const float* topk_w, const float* d_topk_w,
                        int T, int E, int k, float* d_logits, void* stream);
+
+/* ---- Testing hook ----
+ * Not part of the layer's contract: for tests and benchmarks that compare
+ * the library's own kernel variants. Forces, for every later call in this
+ * process, the gate/up path of decode-size groups (decode_path: 0 the
+ * LDS-ring tile, 1 the register-streaming kernel where it applies) and the
+ * grouped GEMMs' tile class (tile_class: 0 small, 1 mid, 2 128-row, 3
+ * 256-row); -1 restores the automatic choice. Process-wide and not
+ * synchronised with calls in other threads. Returns MOE_OK, or
+ * MOE_ERR_INVALID_ARG for values outside those ranges. */
+int moe_set_dispatch_override(int decode_path, int tile_class);
 
 #ifdef __cplusplus
 }

@@ -79,6 +79,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads of the later parallel loops (the CPU baseline's single-thread
+ * figure); no effect on any result, rows being independent. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ----------------------------------------------------------------- router */
 
 /* Router projection: logits[t,e] = sum_h x[t,h] * W_r[e,h], h ascending, in

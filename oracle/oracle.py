@@ -50,6 +50,8 @@ def lib():
         path = build(force=False)
         L = ctypes.CDLL(path)
         L.oracle_num_threads.restype = _I
+        L.oracle_set_num_threads.argtypes = [_I]
+        L.oracle_set_num_threads.restype = None
         L.oracle_router_logits.argtypes = [_P, _I64, _I, _I, _P, _P]
         L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_value.restype = ctypes.c_double
@@ -94,6 +96,11 @@ def lib():
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of later oracle calls (results do not depend on it)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def _c(a: np.ndarray, dtype) -> np.ndarray:

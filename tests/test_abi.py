@@ -29,6 +29,19 @@ def test_library_exports_every_header_symbol(L):
     assert set(names) == set(B._SIGNATURES)
 
 
+def test_workspace_bytes_alias():
+    for args in [(32, 4096, 14336, 8, 2, 0), (4096, 7168, 2048, 256, 8, 2048), (0, 64, 96, 8, 2, 0)]:
+        assert B.moe_workspace_bytes(*args) == B.moe_forward_workspace_bytes(*args)
+
+
+def test_dispatch_override_hook(L):
+    assert L.moe_set_dispatch_override(2, -1) == INVALID
+    assert L.moe_set_dispatch_override(-1, 4) == INVALID
+    assert L.moe_set_dispatch_override(-2, -1) == INVALID
+    assert L.moe_set_dispatch_override(1, 3) == OK
+    assert L.moe_set_dispatch_override(-1, -1) == OK
+
+
 def test_status_strings(L):
     for s in (OK, INVALID, SHAPE, MISALIGNED, WS_SMALL, HIP):
         txt = B.moe_status_string(s)
@@ -129,8 +142,16 @@ def test_ffn_validation(L):
     assert L.moe_down(P, P, 128, 96, 64, 8, P, Q, NULL) == MISALIGNED
     assert L.moe_down(P, NULL, 128, 96, 64, 8, P, P, NULL) == INVALID
     assert L.moe_down(P, P, 1 << 20, 4096, 4096, 8, P, P, NULL) == SHAPE        # > 2^31 elements
-    assert L.moe_grouped_ffn(P, P, 128, 64, 96, 8, P, P, NULL, P, P, NULL) == INVALID
-    assert L.moe_grouped_ffn(NULL, NULL, 0, 64, 96, 8, NULL, NULL, NULL, NULL, NULL, NULL) == OK
+    ws = B.moe_grouped_ffn_workspace_bytes(128, 96)
+    assert ws == 128 * 96 * 2
+    assert B.moe_grouped_ffn_workspace_bytes(3, 8) == 256                       # 256-byte units
+    assert B.moe_grouped_ffn_workspace_bytes(3, 12) == 0                        # F % 8
+    assert L.moe_grouped_ffn(P, P, 128, 64, 96, 8, P, P, NULL, P, P, ws, NULL) == INVALID
+    assert L.moe_grouped_ffn(P, P, 128, 64, 96, 8, P, P, P, P, NULL, ws, NULL) == INVALID
+    assert L.moe_grouped_ffn(P, P, 128, 64, 96, 8, P, P, P, P, Q, ws, NULL) == MISALIGNED
+    assert L.moe_grouped_ffn(P, P, 128, 64, 96, 8, P, P, P, P, P, ws - 1, NULL) == WS_SMALL
+    assert L.moe_grouped_ffn(NULL, NULL, 0, 64, 96, 8, NULL, NULL, NULL, NULL, NULL, 0,
+                             NULL) == OK
 
 
 def test_combine_validation(L):

@@ -2,10 +2,12 @@
 DeepSeek-V3- and Qwen2-MoE-shaped), in the configuration `bench.py
 --backward` times: moe_backward on row-major weights for the routing of the
 layer's own logits. The oracle computes sampled outputs one by one: dx and
-the routing-weight gradient of a few tokens (each depends on that token
-alone) and a few whole columns of the three weight gradients (each is a sum
-over one expert's rows). The tolerance is the one derived in
-test_gpu_backward.py (5 u times the root-sum-square of the GPU's bf16
+the routing-weight gradient of sampled tokens (each depends on that token
+alone: at least 1024 tokens, all of them when T <= 1024, with every 16-row
+block of every expert's rows holding a sampled assignment) and 64 whole
+columns of the three weight gradients (each a sum over one expert's rows:
+the first, last, most and least loaded experts among them). The tolerance
+is the one derived in test_gpu_backward.py (5 u times the root-sum-square of the GPU's bf16
 rounding errors as they propagate, u = 2^-8), evaluated here for the
 sampled elements only."""
 import numpy as np
@@ -14,34 +16,18 @@ import torch
 
 from grouped_gemm_softmax_amd import binding as B
 from grouped_gemm_softmax_amd import synth
-from helpers import gpu_bf16_f64, rel_l2, say
+from helpers import check_block_coverage, gpu_bf16_f64, rel_l2, say, stratified_tokens
 
 pytestmark = pytest.mark.gpu
 
 U_BF16 = 2.0 ** -8
 LAMBDA = 5.0
 CASES = [("mixtral", 512), ("mixtral_large", 2048), ("dsv3", 4096), ("qwen2", 1024)]
-N_TOK = 6
-N_COL = 6
+N_COL = 64
 
 
 def f32w(u):
     return (np.asarray(u, np.uint16).astype(np.uint32) << 16).view(np.float32)
-
-
-class Experts:
-    """float32 copies of single experts' matrices and of their squares,
-    made on demand (for the bounds only; float32 is ample for a bound)."""
-
-    def __init__(self, wg, wu, wd):
-        self.w = dict(g=wg, u=wu, d=wd)
-        self.cache = {}
-
-    def get(self, m, e):
-        if (m, e) not in self.cache:
-            v = f32w(self.w[m][e])
-            self.cache[(m, e)] = (v, v * v)
-        return self.cache[(m, e)]
 
 
 def silu_parts(G):
@@ -49,34 +35,35 @@ def silu_parts(G):
     return G * sg, sg * (1.0 + G * (1.0 - sg))
 
 
-def token_bounds(ex, x, ids, w, dout, toks, dx_ref):
+def token_bounds(x, wg, wu, wd, ids, w, dout, toks, dx_ref):
     """Root-sum-square rounding scales (divided by u) of dx and d_topk_w for
-    the sampled tokens, from each token's rows."""
+    the sampled tokens, from each token's rows, taken expert by expert (a
+    token picks an expert at most once; float32 is ample for a bound)."""
     H = x.shape[1]
     k = ids.shape[1]
     bdx2, bdw = np.zeros((len(toks), H)), np.zeros((len(toks), k))
     f32 = lambda v: v.astype(np.float32)
-    for s, t in enumerate(toks):
-        xr = f32w(x[t])
-        dr = f32w(dout[t])
-        for j in range(k):
-            e = int(ids[t, j])
-            (Wg, Wg2), (Wu, Wu2), (Wd, Wd2) = ex.get("g", e), ex.get("u", e), ex.get("d", e)
-            G, U = (xr @ Wg).astype(np.float64), (xr @ Wu).astype(np.float64)
-            silu, dsilu = silu_parts(G)
-            h = silu * U
-            dy = np.float32(w[t, j]) * dr
-            dh = (Wd @ dy).astype(np.float64)
-            dhr = np.sqrt((Wd2 @ (dy * dy)).astype(np.float64))
-            dG, dU = dh * U * dsilu, dh * silu
-            dGr2 = (dhr * U * dsilu) ** 2 + dG ** 2 + (dh * U * dsilu) ** 2 + (0.5 * dh * U * G) ** 2
-            dUr2 = (dhr * silu) ** 2 + dU ** 2 + (1.1 * dh * G) ** 2
-            bdx2[s] += Wg2 @ f32(dGr2) + Wu2 @ f32(dUr2)
-            bdw[s, j] = np.sqrt(float((dr * dr) @ (f32(h * h) @ Wd2)))
+    sel = ids[toks]
+    for e in np.unique(sel):
+        si, sj = np.nonzero(sel == e)
+        t = toks[si]
+        X, DR = f32w(x[t]), f32w(dout[t])
+        DY = w[t, sj][:, None].astype(np.float32) * DR
+        Wg, Wu, Wd = f32w(wg[e]), f32w(wu[e]), f32w(wd[e])
+        G, U = (X @ Wg).astype(np.float64), (X @ Wu).astype(np.float64)
+        silu, dsilu = silu_parts(G)
+        h = silu * U
+        Wd2 = Wd * Wd
+        dh = (DY @ Wd.T).astype(np.float64)
+        dG, dU = dh * U * dsilu, dh * silu
+        dGr2 = dG ** 2 + (dh * U * dsilu) ** 2 + (0.5 * dh * U * G) ** 2
+        dUr2 = dU ** 2 + (1.1 * dh * G) ** 2
+        bdx2[si] += f32(dGr2) @ (Wg * Wg).T + f32(dUr2) @ (Wu * Wu).T
+        bdw[si, sj] = np.sqrt(np.sum((DR * DR) * (f32(h * h) @ Wd2), axis=1, dtype=np.float64))
     return np.sqrt(bdx2 + dx_ref ** 2), bdw
 
 
-def column_bounds(ex, x, ids, w, dout, ecol, fcol, offsets, row_token, row_dest):
+def column_bounds(x, wg, wu, wd, w, dout, ecol, fcol, offsets, row_token, row_dest):
     """Root-sum-square rounding scales (divided by u) of the sampled
     weight-gradient columns, from the expert's rows."""
     H = x.shape[1]
@@ -87,14 +74,14 @@ def column_bounds(ex, x, ids, w, dout, ecol, fcol, offsets, row_token, row_dest)
         r = slice(offsets[e], offsets[e + 1])
         xs = f32w(x[row_token[r]]).astype(np.float64)
         ds = f32w(dout[row_token[r]]).astype(np.float64) * wrow[r][:, None]   # dy rows
-        (Wg, _), (Wu, _), (Wd, Wd2) = ex.get("g", e), ex.get("u", e), ex.get("d", e)
-        G, U = xs @ Wg[:, f].astype(np.float64), xs @ Wu[:, f].astype(np.float64)
+        wgc, wuc = f32w(wg[e][:, f]).astype(np.float64), f32w(wu[e][:, f]).astype(np.float64)
+        wdr = f32w(wd[e][f]).astype(np.float64)
+        G, U = xs @ wgc, xs @ wuc
         silu, dsilu = silu_parts(G)
-        dh = ds @ Wd[f].astype(np.float64)
-        dhr = np.sqrt((ds * ds) @ Wd2[f].astype(np.float64))
+        dh = ds @ wdr
         dG, dU = dh * U * dsilu, dh * silu
-        dGr2 = (dhr * U * dsilu) ** 2 + dG ** 2 + (dh * U * dsilu) ** 2 + (0.5 * dh * U * G) ** 2
-        dUr2 = (dhr * silu) ** 2 + dU ** 2 + (1.1 * dh * G) ** 2
+        dGr2 = dG ** 2 + (dh * U * dsilu) ** 2 + (0.5 * dh * U * G) ** 2
+        dUr2 = dU ** 2 + (1.1 * dh * G) ** 2
         bg[s] = np.sqrt((xs * xs).T @ dGr2)
         bu[s] = np.sqrt((xs * xs).T @ dUr2)
         bd[s] = np.sqrt(2 * (ds * ds).T @ (silu * U) ** 2)
@@ -130,11 +117,17 @@ def test_full_size_backward(name, T, orc):
                 wd=synth.u16(layer.w_down), dout=synth.u16(dout))
     offsets, row_token, row_dest = orc.permute(ids_h, E)
     rng = np.random.default_rng(T + E)
-    toks = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, N_TOK)]))[:N_TOK]
+    toks, _ = stratified_tokens(offsets, row_token, T, rng)
+    check_block_coverage(toks, offsets, row_dest)
     used = np.flatnonzero(np.diff(offsets) > 0)
-    ecol = rng.choice(used, N_COL)
+    # columns: the first and last used expert, the most and least loaded,
+    # then random used experts; the first and last column among them
+    cnt = np.diff(offsets)[used]
+    ecol = np.concatenate([used[[0, -1, np.argmax(cnt), np.argmin(cnt)]],
+                           rng.choice(used, N_COL - 4)])
     fcol = rng.integers(0, F, N_COL)
-    fcol[0] = F - 1
+    fcol[0], fcol[1] = F - 1, 0
+    say("oracle samples", name, T, len(toks), "tokens,", N_COL, "weight-gradient columns")
     dx_g = gpu_bf16_f64(grads["dx"])[toks]
     dw_g = grads["d_topk_w"].cpu().numpy().astype(np.float64)[toks]
     ei, fi = torch.from_numpy(ecol).long().cuda(), torch.from_numpy(fcol).long().cuda()
@@ -148,10 +141,10 @@ def test_full_size_backward(name, T, orc):
                                  host["dout"], toks)
     cg, cu, cd = orc.backward_wcols(host["x"], ids_h, w_h, host["wg"], host["wu"], host["wd"],
                                     host["dout"], ecol, fcol)
-    ex = Experts(host["wg"], host["wu"], host["wd"])
-    bdx, bdw = token_bounds(ex, host["x"], ids_h, w_h, host["dout"], toks, dx)
-    bg, bu, bd = column_bounds(ex, host["x"], ids_h, w_h, host["dout"], ecol, fcol, offsets,
-                               row_token, row_dest)
+    bdx, bdw = token_bounds(host["x"], host["wg"], host["wu"], host["wd"], ids_h, w_h,
+                            host["dout"], toks, dx)
+    bg, bu, bd = column_bounds(host["x"], host["wg"], host["wu"], host["wd"], w_h, host["dout"],
+                               ecol, fcol, offsets, row_token, row_dest)
     check(dx_g, dx, bdx, f"dx[{name}, T={T}]")
     check(dw_g, dw, bdw, f"d_topk_w[{name}, T={T}]")
     check(cg_g, cg, bg, f"dw_gate columns[{name}, T={T}]")

@@ -115,3 +115,46 @@ def test_shared_gate_zero_logit_is_half(orc):
     out = _fwd(layer)
     torch.cuda.synchronize()
     assert_close(gpu_bf16_f64(out), ref["out"], "out[gate=0]")
+
+
+def test_down_projection_k_slices_all_nonempty(orc):
+    """A down projection whose K = F = 2056 is 33 steps of 64 for the small
+    tile, split 8 ways (a handful of output tiles): each slice covers
+    floor((s+1) 33 / 8) - floor(s 33 / 8) >= 4 steps (an equal ceil-sized
+    split would leave the last slice at -2 steps). The layer still matches
+    the oracle."""
+    nk, ks = 33, 8
+    sizes = [(s + 1) * nk // ks - s * nk // ks for s in range(ks)]
+    assert min(sizes) >= 4 and sum(sizes) == nk
+    cfg = synth.small_config("kss", H=128, F=2056, E=4, k=1)
+    T = 2
+    layer = synth.make_layer("kss", T, seed=4, device="cuda", cfg=cfg)
+    # the workspace holds 8 fp32 K-slices of y [T*k, H] (beside the rest)
+    assert B.moe_forward_workspace_bytes(T, cfg.H, cfg.F, cfg.E, cfg.k, 0) >= 8 * T * cfg.H * 4
+    d, _ = host_layer(layer)
+    ref = orc.forward(d["x"], d["logits"], cfg.k, d["wg"], d["wu"], d["wd"],
+                      keep_intermediates=False)
+    say("moe_forward uneven K-slices", cfg.F)
+    out = _fwd(layer)
+    torch.cuda.synchronize()
+    assert_close(gpu_bf16_f64(out), ref["out"], "out[K-split 8 of 33 steps]")
+
+
+def test_side_stream_call_keeps_its_workspace():
+    """A call on a stream other than torch's current one allocates its
+    workspace on that stream: current-stream allocations made right after the
+    call (while its kernels may still run) cannot take that memory, and the
+    result equals the same call on the current stream."""
+    layer = _layer(T=300)
+    say("side stream")
+    ref = _fwd(layer).clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    out = B.moe_forward(layer.x, layer.logits, layer.cfg.k, layer.w_gate, layer.w_up,
+                        layer.w_down, shared=layer.shared, stream=side)
+    junk = [torch.full((1 << 20,), 3.0, device="cuda") for _ in range(8)]   # current stream
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))

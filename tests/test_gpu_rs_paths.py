@@ -1,13 +1,12 @@
 """The two decode-size gate/up paths give the same bits: the
 register-streaming kernel (weights streamed straight into registers) and
 the LDS-ring small tile compute the same products in the same order. Both
-are selected per launch through the MOE_RS environment variable (1: the
-register-streaming kernel, 0: the ring tile), on packed bf16 and FP8
+are selected per launch through the library's testing hook
+moe_set_dispatch_override (1: the register-streaming kernel, 0: the ring
+tile), on packed bf16 and FP8
 weights, with ragged K and N, several row tiles per group and empty
 groups. The values themselves are checked against the oracle by the other
 GPU tests (which run whichever path the launch rules pick)."""
-import os
-
 import pytest
 import torch
 
@@ -27,12 +26,12 @@ CASES = {
 
 
 def gateup(x_perm, off, wg, wu, rs):
-    os.environ["MOE_RS"] = rs
+    B.moe_set_dispatch_override(rs, -1)
     try:
         h = B.moe_gateup_swiglu(x_perm, off, wg, wu)
         torch.cuda.synchronize()
     finally:
-        del os.environ["MOE_RS"]
+        B.moe_set_dispatch_override(-1, -1)
     return h
 
 
@@ -48,6 +47,6 @@ def test_decode_paths_bit_identical(name, fmt, orc):
     else:
         wg, wu = B.moe_pack_weights(layer.w_gate), B.moe_pack_weights(layer.w_up)
     say("gate/up decode paths", name, fmt, tuple(xp.shape))
-    h_rs = gateup(xp, off, wg, wu, "1")
-    h_ring = gateup(xp, off, wg, wu, "0")
+    h_rs = gateup(xp, off, wg, wu, 1)
+    h_ring = gateup(xp, off, wg, wu, 0)
     assert torch.equal(h_rs.view(torch.int16), h_ring.view(torch.int16)), (name, fmt)
