@@ -78,6 +78,8 @@ _SIGNATURES = {
     "moe_down_packed": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
     "moe_forward_packed": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P,
                                 ctypes.POINTER(SharedExpert), _P, _P, _P, _P, _SZ, _P]),
+    "moe_forward_packed_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P,
+                                        ctypes.POINTER(SharedExpert), _P, _P, _P, _P]),
     "moe_fp8_weights_bytes": (_SZ, [_I, _I, _I]),
     "moe_quantize_fp8": (_I, [_P, _I, _I, _I, _P, _SZ, _P, _P]),
     "moe_gateup_swiglu_fp8": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
@@ -547,6 +549,29 @@ def moe_forward(x, logits, k, w_gate, w_up, w_down, shared: Optional[dict] = Non
               ctypes.byref(sh) if sh is not None else None, _ptr(out), _ptr(topk_ids),
               _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)),
            "moe_forward_packed" if packed else "moe_forward")
+    return out
+
+
+@_on_stream
+def moe_forward_packed_noalloc(x, logits, k, w_gate, w_up, w_down,
+                               shared: Optional[dict] = None, out=None, topk_ids=None,
+                               topk_w=None, stream=None):
+    """moe_forward_packed with the library's fixed device workspace (no
+    workspace is allocated; `out` and the optional routing outputs are
+    allocated here only when not given). All weights PackedWeight."""
+    _need(x, torch.bfloat16, "x")
+    _need(logits, torch.float32, "logits")
+    for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _weight(t, n, True)
+    T, H = x.shape
+    E, _, F = w_gate.shape
+    sh, _ = _shared_struct(shared, True)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _check(lib().moe_forward_packed_noalloc(
+        _ptr(x), _ptr(logits), T, H, F, E, k, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+        ctypes.byref(sh) if sh is not None else None, _ptr(out), _ptr(topk_ids), _ptr(topk_w),
+        _stream(stream)), "moe_forward_packed_noalloc")
     return out
 
 

@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "kernels.h"
 
@@ -173,6 +175,38 @@ int check_ffn_args(const void* act, const int32_t* offsets, int M, int K, int N,
   return MOE_OK;
 }
 
+}  // namespace
+
+// ---- the forward without allocation ---------------------------------------
+// A fixed device array serves as moe_forward_packed's workspace, for callers
+// that cannot allocate (graph capture, tight serving loops). Each GPU holds
+// its own copy from the library's load until the process ends. In host code
+// the array's name only stands for the symbol: its device address is taken
+// once per device with hipGetSymbolAddress, and only that address is passed
+// to kernels.
+constexpr size_t kStaticWorkspaceBytes = size_t(128) << 20;  // 128 MiB
+static __device__ __align__(256) char scratch[kStaticWorkspaceBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device, with the device current).
+int scratch_address(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED_SHAPE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -663,6 +697,21 @@ int moe_forward_mxfp4(const moe_bf16* x, const float* logits, int T, int H, int 
   }
   return forward_impl(x, logits, nullptr, nullptr, T, H, F, E, k, W, out, topk_ids_out,
                       topk_w_out, ws, ws_bytes, stream);
+}
+
+int moe_forward_packed_noalloc(const moe_bf16* x, const float* logits, int T, int H, int F,
+                               int E, int k, const moe_bf16* w_gate_packed,
+                               const moe_bf16* w_up_packed, const moe_bf16* w_down_packed,
+                               const moe_shared_expert* shared_packed, moe_bf16* out,
+                               int32_t* topk_ids_out, float* topk_w_out, void* stream) {
+  void* ws = nullptr;
+  MOE_TRY(scratch_address(&ws));
+  // forward_impl checks the arguments first, then that the layer's
+  // workspace fits the array (MOE_ERR_WORKSPACE_TOO_SMALL otherwise)
+  return forward_impl(x, logits, nullptr, nullptr, T, H, F, E, k,
+                      bf16_weights(w_gate_packed, w_up_packed, w_down_packed, shared_packed,
+                                   kPackedBf16),
+                      out, topk_ids_out, topk_w_out, ws, kStaticWorkspaceBytes, stream);
 }
 
 int moe_forward_routed(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,

@@ -283,6 +283,25 @@ int moe_forward_packed(const moe_bf16* x, const float* logits, int T, int H,
                        int32_t* topk_ids_out, float* topk_w_out, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* moe_forward_packed without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the call allocates nothing and uses a
+ * fixed 128 MiB device array of the library as its workspace, which each GPU
+ * holds from the library's load until the process ends. Limit: the layer's
+ * workspace, moe_forward_workspace_bytes(T, H, F, E, k, Fs), must be at most
+ * 128 MiB (134217728 bytes; e.g. the Mixtral-8x7B-shaped layer up to a few
+ * hundred tokens), else the call returns MOE_ERR_WORKSPACE_TOO_SMALL with
+ * nothing enqueued. All calls on one GPU share that GPU's array and leave
+ * their intermediates in it: calls whose work may overlap on one GPU (on
+ * different streams, or from several threads without ordering) race and
+ * give unspecified results. Arguments, outputs and errors otherwise as
+ * moe_forward_packed; given the same inputs the outputs are bit-identical. */
+int moe_forward_packed_noalloc(const moe_bf16* x, const float* logits, int T, int H, int F,
+                               int E, int k, const moe_bf16* w_gate_packed,
+                               const moe_bf16* w_up_packed, const moe_bf16* w_down_packed,
+                               const moe_shared_expert* shared_packed, moe_bf16* out,
+                               int32_t* topk_ids_out, float* topk_w_out, void* stream);
+
 /* ---- FP8 weights ----
  * The DeepGEMM article (itsolotime.com), sections 1.1 and 5.3, runs the
  * expert GEMMs on 8-bit (and 4-bit) floating-point operands. Here the
