@@ -22,6 +22,8 @@
  *             weights (see the fp8 section below).
  *   mxfp4   : weights as E2M1 codes with one power-of-two scale per 32
  *             K-values of a column (OCP MX); likewise (mxfp4 section).
+ *   mxfp8   : weights as E4M3 codes with one power-of-two scale per 32
+ *             K-values of a column (OCP MX); likewise (mxfp8 section).
  *
  * Sources (restated, not quoted):
  *   - "Triton-MoE-Dispatch-Kernel erreicht 131 % von Megablocks" (lumeric.app),
@@ -273,6 +275,83 @@ void oracle_dequant_mxfp4(const uint8_t* codes, const uint8_t* scale_bytes, int6
       for (int n = 0; n < N; ++n) {
         const int64_t i = g * (int64_t)K * N + (int64_t)k * N + n;
         w[i] = oracle_e2m1_value(codes[i]) *
+               oracle_e8m0_value(scale_bytes[(g * KB + k / 32) * (int64_t)N + n]);
+      }
+}
+
+/* ------------------------------------------------------------------ mxfp8 */
+
+/* Weights in 8-bit floating point with block scales: the FP8 expert GEMM
+ * "with block scales" of the DeepGEMM article (itsolotime.com), sections 1.1
+ * and 5.3, which fixes no format. Reading taken: the OCP Microscaling (MX)
+ * format MXFP8 with E4M3 elements. Every block of 32 consecutive K-values of
+ * one output column shares one E8M0 scale 2^X (scale byte X + 127), and each
+ * weight is an E4M3 code (see the fp8 section) of w / 2^X. The activations
+ * stay bf16; every dequantized weight code * 2^X is exactly a bf16 value, so
+ * the layer on MXFP8 weights is the bf16 layer on the dequantized weights. */
+
+/* Per column n and K-block b (K-values 32b .. 32b+31, the last block of a
+ * K that is not a multiple of 32 shorter): with amax the block's largest
+ * |w|, X = floor(log2(amax)) - 8 (8 = the exponent of the largest E4M3
+ * value, 1.75 * 2^8), the MX rule, raised to -117 where it is smaller (the
+ * smallest nonzero code, 2^-9, times 2^-117 is the least normal bf16 value;
+ * it only matters for blocks whose largest weight is below 2^-109); an
+ * all-zero block takes X = 0. Each weight's code is the finite E4M3 value
+ * nearest to w / 2^X, found by scanning the 127 non-negative finite codes, a
+ * tie going to the code with an even mantissa (round to nearest, ties to
+ * even), so magnitudes above 448 become 448 (the MX rule saturates); the
+ * sign is the weight's (also for zeros). w bf16 [G,K,N] -> codes [G,K,N],
+ * scale bytes [G, ceil(K/32), N]. */
+int oracle_quantize_mxfp8(const uint16_t* w, int64_t G, int K, int N, uint8_t* codes,
+                          uint8_t* scale_bytes) {
+  if (G < 0 || K < 1 || N < 1) return ORC_ERR_ARG;
+  const int KB = (K + 31) / 32;
+  double mag[127];
+  for (int c = 0; c < 127; ++c) mag[c] = oracle_e4m3_value((uint8_t)c);
+#pragma omp parallel for schedule(static)
+  for (int64_t gbn = 0; gbn < G * KB * (int64_t)N; ++gbn) {
+    const int64_t g = gbn / ((int64_t)KB * N);
+    const int b = (int)((gbn / N) % KB);
+    const int n = (int)(gbn % N);
+    const uint16_t* wg = w + g * (int64_t)K * N;
+    const int k_end = 32 * b + 32 < K ? 32 * b + 32 : K;
+    double amax = 0.0;
+    for (int k = 32 * b; k < k_end; ++k) {
+      const double a = fabs(bf16_to_f64(wg[(int64_t)k * N + n]));
+      if (a > amax) amax = a;
+    }
+    int X = 0;
+    if (amax > 0.0) {
+      int E;
+      frexp(amax, &E);  /* amax = f * 2^E, f in [0.5, 1): floor(log2(amax)) = E - 1 */
+      X = E - 1 - 8;
+      if (X < -117) X = -117;
+    }
+    scale_bytes[gbn] = (uint8_t)(X + 127);
+    for (int k = 32 * b; k < k_end; ++k) {
+      const double x = bf16_to_f64(wg[(int64_t)k * N + n]);
+      const double v = fabs(ldexp(x, -X));
+      int best = 0;
+      for (int c = 1; c < 127; ++c) {
+        const double dc = fabs(mag[c] - v), db = fabs(mag[best] - v);
+        if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+      }
+      codes[g * (int64_t)K * N + (int64_t)k * N + n] =
+          (uint8_t)(best | (signbit(x) ? 0x80 : 0));
+    }
+  }
+  return ORC_OK;
+}
+
+/* w[g,k,n] = value(codes[g,k,n]) * value(scale_bytes[g, k/32, n]). */
+void oracle_dequant_mxfp8(const uint8_t* codes, const uint8_t* scale_bytes, int64_t G, int K,
+                          int N, double* w) {
+  const int KB = (K + 31) / 32;
+  for (int64_t g = 0; g < G; ++g)
+    for (int k = 0; k < K; ++k)
+      for (int n = 0; n < N; ++n) {
+        const int64_t i = g * (int64_t)K * N + (int64_t)k * N + n;
+        w[i] = oracle_e4m3_value(codes[i]) *
                oracle_e8m0_value(scale_bytes[(g * KB + k / 32) * (int64_t)N + n]);
       }
 }

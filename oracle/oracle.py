@@ -65,6 +65,9 @@ def lib():
         L.oracle_quantize_mxfp4.argtypes = [_P, _I64, _I, _I, _P, _P]
         L.oracle_dequant_mxfp4.argtypes = [_P, _P, _I64, _I, _I, _P]
         L.oracle_dequant_mxfp4.restype = None
+        L.oracle_quantize_mxfp8.argtypes = [_P, _I64, _I, _I, _P, _P]
+        L.oracle_dequant_mxfp8.argtypes = [_P, _P, _I64, _I, _I, _P]
+        L.oracle_dequant_mxfp8.restype = None
         L.oracle_route.argtypes = [_P, _I64, _I, _I, _P, _P]
         L.oracle_permute.argtypes = [_P, _I64, _I, _I, _P, _P, _P]
         L.oracle_gather.argtypes = [_P, _P, _I64, _I, _P]
@@ -197,6 +200,33 @@ def dequant_mxfp4(codes: np.ndarray, scale_bytes: np.ndarray) -> np.ndarray:
     G, K, N = codes.shape
     out = np.empty((G, K, N), np.float64)
     lib().oracle_dequant_mxfp4(_p(codes), _p(scale_bytes), G, K, N, _p(out))
+    return out[0] if squeeze else out
+
+
+def quantize_mxfp8(w: np.ndarray):
+    """bf16 weights [G,K,N] (or [K,N]: G = 1) -> (E4M3 codes uint8 same
+    shape, scale bytes uint8 [G, ceil(K/32), N]; scale = 2^(byte - 127))."""
+    w = _c(w, np.uint16)
+    squeeze = w.ndim == 2
+    if squeeze:
+        w = w[None]
+    G, K, N = w.shape
+    codes = np.empty((G, K, N), np.uint8)
+    sb = np.empty((G, -(-K // 32), N), np.uint8)
+    _check(lib().oracle_quantize_mxfp8(_p(w), G, K, N, _p(codes), _p(sb)), "quantize_mxfp8")
+    return (codes[0], sb[0]) if squeeze else (codes, sb)
+
+
+def dequant_mxfp8(codes: np.ndarray, scale_bytes: np.ndarray) -> np.ndarray:
+    """value(code) * 2^(scale byte - 127) of its 32-row block -> float64."""
+    codes = _c(codes, np.uint8)
+    scale_bytes = _c(scale_bytes, np.uint8)
+    squeeze = codes.ndim == 2
+    if squeeze:
+        codes, scale_bytes = codes[None], scale_bytes[None]
+    G, K, N = codes.shape
+    out = np.empty((G, K, N), np.float64)
+    lib().oracle_dequant_mxfp8(_p(codes), _p(scale_bytes), G, K, N, _p(out))
     return out[0] if squeeze else out
 
 
