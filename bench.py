@@ -72,11 +72,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64,
                     help="tokens in the oracle's timed sample")
-    ap.add_argument("--weights", choices=("packed", "rowmajor", "fp8", "mxfp4"),
+    ap.add_argument("--weights", choices=("packed", "rowmajor", "fp8", "mxfp4", "mxfp8"),
                     default="packed",
                     help="weight layout of the timed steps (fp8: E4M3 codes with per-column "
-                         "scales, moe_forward_fp8; mxfp4: E2M1 codes with a scale byte per "
-                         "32 K-values, moe_forward_mxfp4; bf16 arithmetic in every case)")
+                         "scales, moe_forward_fp8; mxfp4 / mxfp8: E2M1 / E4M3 codes with a "
+                         "scale byte per 32 K-values, moe_forward_mxfp4 / _mxfp8; bf16 "
+                         "arithmetic in every case)")
     ap.add_argument("--router", action="store_true",
                     help="only time the router row: moe_router_route (router GEMM + "
                          "top-k routing) against torch's matmul + fp32 cast + moe_route, "
@@ -335,7 +336,7 @@ def main():
     stream = torch.cuda.current_stream()
     flush_buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     mode = args.weights
-    WBYTES = {"fp8": 1, "mxfp4": 0.5 + 1 / 32}.get(mode, 2)
+    WBYTES = {"fp8": 1, "mxfp4": 0.5 + 1 / 32, "mxfp8": 1 + 1 / 32}.get(mode, 2)
 
     def flush():
         # read (not write) the buffer: the caches then hold other, clean lines,
@@ -383,8 +384,9 @@ def main():
             torch.cuda.synchronize()
             self.pack_ms = e0.elapsed_time(e1)
             self.q, self.quant_ms = None, None
-            if mode in ("fp8", "mxfp4"):
-                quant = B.moe_quantize_fp8 if mode == "fp8" else B.moe_quantize_mxfp4
+            if mode in ("fp8", "mxfp4", "mxfp8"):
+                quant = {"fp8": B.moe_quantize_fp8, "mxfp4": B.moe_quantize_mxfp4,
+                         "mxfp8": B.moe_quantize_mxfp8}[mode]
                 e0.record(stream)
                 self.q = dict(wg=quant(L.w_gate), wu=quant(L.w_up), wd=quant(L.w_down))
                 if L.shared is not None:
@@ -400,7 +402,7 @@ def main():
                            shared=None if L.shared is None else
                            {n: L.shared[n] for n in ("w_gate", "w_up", "w_down")})
             else:
-                src = self.q if m in ("fp8", "mxfp4") else self.pk
+                src = self.q if m in ("fp8", "mxfp4", "mxfp8") else self.pk
             sh = None
             if self.cfg.Fs:
                 sh = dict(src["shared"], gate_logits=batch.shared["gate_logits"])
@@ -570,14 +572,16 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "weight_dtype": {"fp8": "fp8_e4m3", "mxfp4": "mxfp4_e2m1"}.get(mode, "bf16"),
+        "weight_dtype": {"fp8": "fp8_e4m3", "mxfp4": "mxfp4_e2m1",
+                         "mxfp8": "mxfp8_e4m3"}.get(mode, "bf16"),
         "data": "synthetic (seeded; x~N(0,1), weights~N(0,0.02), logits~N(0,1) "
                 "(+ per-expert bias N(0,0.5) at large batch, Zipf(1.2)+Gumbel for the "
                 "DeepSeek-V3 shape))",
         "config": {"workload": f"{cfg.desc}: T={T}, H={cfg.H}, F={cfg.F}, E={cfg.E}, "
                                f"top-{cfg.k}, bf16, " +
                                ({"fp8": "fp8 E4M3 weights with per-column scales",
-                                 "mxfp4": "MXFP4 weights (E2M1, E8M0 scale per 32)"}
+                                 "mxfp4": "MXFP4 weights (E2M1, E8M0 scale per 32)",
+                                 "mxfp8": "MXFP8 weights (E4M3, E8M0 scale per 32)"}
                                 .get(mode, f"{mode} weights")),
                    "weights": mode, "T": T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "k": cfg.k,
                    "Fs": cfg.Fs, "experts_touched": Et, "parallelism": "none (1 GPU)"},

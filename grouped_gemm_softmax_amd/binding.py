@@ -50,6 +50,13 @@ class SharedExpertMxfp4(ctypes.Structure):
                 ("Fs", ctypes.c_int32), ("gate_logits", ctypes.c_void_p)]
 
 
+class SharedExpertMxfp8(ctypes.Structure):
+    _fields_ = [("w_gate", ctypes.c_void_p), ("s_gate", ctypes.c_void_p),
+                ("w_up", ctypes.c_void_p), ("s_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p), ("s_down", ctypes.c_void_p),
+                ("Fs", ctypes.c_int32), ("gate_logits", ctypes.c_void_p)]
+
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _SZ = ctypes.c_size_t
@@ -93,6 +100,13 @@ _SIGNATURES = {
     "moe_down_mxfp4": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_forward_mxfp4": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
                                ctypes.POINTER(SharedExpertMxfp4), _P, _P, _P, _P, _SZ, _P]),
+    "moe_mxfp8_weights_bytes": (_SZ, [_I, _I, _I]),
+    "moe_mxfp8_scales_bytes": (_SZ, [_I, _I, _I]),
+    "moe_quantize_mxfp8": (_I, [_P, _I, _I, _I, _P, _SZ, _P, _SZ, _P]),
+    "moe_gateup_swiglu_mxfp8": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "moe_down_mxfp8": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "moe_forward_mxfp8": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
+                               ctypes.POINTER(SharedExpertMxfp8), _P, _P, _P, _P, _SZ, _P]),
     "moe_backward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "moe_backward": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                           _P, _P, _SZ, _P]),
@@ -345,11 +359,42 @@ def moe_quantize_mxfp4(w: torch.Tensor, stream=None) -> Mxfp4Weight:
     return Mxfp4Weight(codes, scales, G, K, N)
 
 
-_QUANT = {Fp8Weight: "fp8", Mxfp4Weight: "mxfp4"}
+class Mxfp8Weight:
+    """A [G,K,N] weight tensor in MXFP8: E4M3 codes in the fp8 block layout
+    (`codes`, uint8) and E8M0 scale bytes, one per 32 K-values of a column
+    (`scales`, uint8, the mxfp4 layout), from moe_quantize_mxfp8."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, G: int, K: int, N: int):
+        self.codes, self.scales, self.G, self.K, self.N = codes, scales, G, K, N
+        self.shape = (G, K, N)
+
+
+def moe_mxfp8_weights_bytes(G: int, K: int, N: int) -> int:
+    return int(lib().moe_mxfp8_weights_bytes(G, K, N))
+
+
+def moe_mxfp8_scales_bytes(G: int, K: int, N: int) -> int:
+    return int(lib().moe_mxfp8_scales_bytes(G, K, N))
+
+
+@_on_stream
+def moe_quantize_mxfp8(w: torch.Tensor, stream=None) -> Mxfp8Weight:
+    """w bf16 [G,K,N] (or [K,N], taken as G = 1) -> Mxfp8Weight."""
+    _need(w, torch.bfloat16, "w")
+    G, K, N = (1, *w.shape) if w.dim() == 2 else w.shape
+    nc, ns = moe_mxfp8_weights_bytes(G, K, N), moe_mxfp8_scales_bytes(G, K, N)
+    codes = torch.empty(max(nc, 16), dtype=torch.uint8, device=w.device)
+    scales = torch.empty(max(ns, 16), dtype=torch.uint8, device=w.device)
+    _check(lib().moe_quantize_mxfp8(_ptr(w), G, K, N, _ptr(codes), codes.numel(), _ptr(scales),
+                                    scales.numel(), _stream(stream)), "moe_quantize_mxfp8")
+    return Mxfp8Weight(codes, scales, G, K, N)
+
+
+_QUANT = {Fp8Weight: "fp8", Mxfp4Weight: "mxfp4", Mxfp8Weight: "mxfp8"}
 
 
 def _quant_kind(w):
-    """'fp8' / 'mxfp4' for quantized weights, None otherwise."""
+    """'fp8' / 'mxfp4' / 'mxfp8' for quantized weights, None otherwise."""
     return _QUANT.get(type(w))
 
 
@@ -578,7 +623,7 @@ def moe_forward_packed_noalloc(x, logits, k, w_gate, w_up, w_down,
 @_on_stream
 def _forward_quant(x, logits, k, w_gate, w_up, w_down, shared, out, topk_ids, topk_w, ws,
                    stream):
-    """moe_forward_fp8 or moe_forward_mxfp4, by the weights' kind."""
+    """moe_forward_fp8, moe_forward_mxfp4 or moe_forward_mxfp8, by the weights' kind."""
     kind = _quant_kind(w_gate)
     _need(x, torch.bfloat16, "x")
     _need(logits, torch.float32, "logits")
@@ -592,7 +637,8 @@ def _forward_quant(x, logits, k, w_gate, w_up, w_down, shared, out, topk_ids, to
             _same_kind(kind, shared[n], "shared " + n)
         Fs = shared["w_gate"].shape[-1]
         g = shared.get("gate_logits")
-        cls = SharedExpertFp8 if kind == "fp8" else SharedExpertMxfp4
+        cls = {"fp8": SharedExpertFp8, "mxfp4": SharedExpertMxfp4,
+               "mxfp8": SharedExpertMxfp8}[kind]
         sh = cls(shared["w_gate"].codes.data_ptr(), shared["w_gate"].scales.data_ptr(),
                  shared["w_up"].codes.data_ptr(), shared["w_up"].scales.data_ptr(),
                  shared["w_down"].codes.data_ptr(), shared["w_down"].scales.data_ptr(), Fs,

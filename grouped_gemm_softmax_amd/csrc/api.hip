@@ -115,12 +115,16 @@ ForwardLayout forward_layout(int T, int H, int F, int E, int k, int Fs, int cus)
 }
 
 // Weight layouts: 0 [K][N] bf16, 1 packed bf16 blocks, 2 packed fp8 codes
-// (+ per-column scales), 3 packed mxfp4 codes (+ scale bytes).
-constexpr int kRowMajor = 0, kPackedBf16 = 1, kFp8 = 2, kMxfp4 = 3;
+// (+ per-column scales), 3 packed mxfp4 codes (+ scale bytes), 5 packed
+// mxfp8 codes (the fp8 blocks, + mxfp4-layout scale bytes).
+constexpr int kRowMajor = 0, kPackedBf16 = 1, kFp8 = 2, kMxfp4 = 3, kMxfp8 = 5;
+
+// layouts whose codes come with scales (a second pointer per matrix)
+bool has_scales(int layout) { return layout == kFp8 || layout == kMxfp4 || layout == kMxfp8; }
 
 // Elements (bf16-sized) between consecutive experts' weight matrices.
 int64_t weight_stride(int K, int N, int layout) {
-  return layout == kFp8        ? moe::fp8_weight_bytes(1, K, N) / 2
+  return layout == kFp8 || layout == kMxfp8 ? moe::fp8_weight_bytes(1, K, N) / 2
          : layout == kMxfp4      ? moe::mxfp4_weight_bytes(1, K, N) / 2
          : layout == kPackedBf16 ? moe::packed_weight_elems(1, K, N)
                                  : static_cast<int64_t>(K) * N;
@@ -298,7 +302,7 @@ static int gateup_impl(const moe_bf16* x_perm, const int32_t* expert_offsets, in
                        const void* su = nullptr) {
   MOE_TRY(check_ffn_args(x_perm, expert_offsets, M, H, F, E, w_gate, w_up, true, h));
   if (M == 0) return MOE_OK;
-  if (layout == kFp8 || layout == kMxfp4) {
+  if (has_scales(layout)) {
     MOE_TRY(need_bf16(sg));
     MOE_TRY(need_bf16(su));
   }
@@ -312,7 +316,7 @@ static int down_impl(const moe_bf16* h, const int32_t* expert_offsets, int M, in
                      int layout, const void* sd = nullptr) {
   MOE_TRY(check_ffn_args(h, expert_offsets, M, F, H, E, w_down, nullptr, false, y_perm));
   if (M == 0) return MOE_OK;
-  if (layout == kFp8 || layout == kMxfp4) MOE_TRY(need_bf16(sd));
+  if (has_scales(layout)) MOE_TRY(need_bf16(sd));
   return hip_status(moe::launch_grouped_gemm(
       down_problem(h, expert_offsets, M, F, H, E, w_down, y_perm, layout, sd),
       static_cast<hipStream_t>(stream)));
@@ -409,6 +413,45 @@ int moe_down_mxfp4(const moe_bf16* h, const int32_t* expert_offsets, int M, int 
                    const uint8_t* w_down, const uint8_t* s_down, moe_bf16* y_perm, void* stream) {
   return down_impl(h, expert_offsets, M, F, H, E, reinterpret_cast<const bf16_t*>(w_down),
                    y_perm, stream, kMxfp4, s_down);
+}
+
+size_t moe_mxfp8_weights_bytes(int G, int K, int N) {
+  if (G < 1 || check_width(K) != MOE_OK || check_width(N) != MOE_OK) return 0;
+  return static_cast<size_t>(moe::fp8_weight_bytes(G, K, N));
+}
+
+size_t moe_mxfp8_scales_bytes(int G, int K, int N) {
+  if (G < 1 || check_width(K) != MOE_OK || check_width(N) != MOE_OK) return 0;
+  return static_cast<size_t>(moe::mxfp4_scale_bytes(G, K, N));
+}
+
+int moe_quantize_mxfp8(const moe_bf16* w, int G, int K, int N, uint8_t* codes,
+                       size_t codes_bytes, uint8_t* scales, size_t scales_bytes, void* stream) {
+  if (G < 1) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_width(K));
+  MOE_TRY(check_width(N));
+  MOE_TRY(need_bf16(w));
+  MOE_TRY(need_bf16(codes));
+  MOE_TRY(need_bf16(scales));
+  if (codes_bytes < moe_mxfp8_weights_bytes(G, K, N) ||
+      scales_bytes < moe_mxfp8_scales_bytes(G, K, N))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(moe::launch_quantize_mxfp8(w, G, K, N, codes, scales,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int moe_gateup_swiglu_mxfp8(const moe_bf16* x_perm, const int32_t* expert_offsets, int M, int H,
+                            int F, int E, const uint8_t* w_gate, const uint8_t* s_gate,
+                            const uint8_t* w_up, const uint8_t* s_up, moe_bf16* h,
+                            void* stream) {
+  return gateup_impl(x_perm, expert_offsets, M, H, F, E, reinterpret_cast<const bf16_t*>(w_gate),
+                     reinterpret_cast<const bf16_t*>(w_up), h, stream, kMxfp8, s_gate, s_up);
+}
+
+int moe_down_mxfp8(const moe_bf16* h, const int32_t* expert_offsets, int M, int F, int H, int E,
+                   const uint8_t* w_down, const uint8_t* s_down, moe_bf16* y_perm, void* stream) {
+  return down_impl(h, expert_offsets, M, F, H, E, reinterpret_cast<const bf16_t*>(w_down),
+                   y_perm, stream, kMxfp8, s_down);
 }
 
 size_t moe_pack_weights_bytes(int G, int K, int N) {
@@ -523,7 +566,7 @@ static int forward_impl(const moe_bf16* x, const float* logits, const int32_t* i
   const bool shared = W.shared;
   const int Fs = shared ? W.Fs : 0;
   if (shared) MOE_TRY(check_width(Fs));
-  const bool fp8 = W.layout == kFp8 || W.layout == kMxfp4;  // codes + scales
+  const bool fp8 = has_scales(W.layout);  // codes + scales
   const int64_t A = static_cast<int64_t>(T) * k;
   const int64_t widest = (H > F ? H : F) > Fs ? (H > F ? H : F) : Fs;
   MOE_TRY(check_elems(A, widest));
@@ -712,6 +755,31 @@ int moe_forward_packed_noalloc(const moe_bf16* x, const float* logits, int T, in
                       bf16_weights(w_gate_packed, w_up_packed, w_down_packed, shared_packed,
                                    kPackedBf16),
                       out, topk_ids_out, topk_w_out, ws, kStaticWorkspaceBytes, stream);
+}
+
+int moe_forward_mxfp8(const moe_bf16* x, const float* logits, int T, int H, int F, int E, int k,
+                      const uint8_t* w_gate, const uint8_t* s_gate, const uint8_t* w_up,
+                      const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
+                      const moe_shared_expert_mxfp8* shared, moe_bf16* out,
+                      int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                      void* stream) {
+  LayerWeights W{};
+  W.layout = kMxfp8;
+  W.wg = reinterpret_cast<const bf16_t*>(w_gate);
+  W.wu = reinterpret_cast<const bf16_t*>(w_up);
+  W.wd = reinterpret_cast<const bf16_t*>(w_down);
+  W.sg = s_gate, W.su = s_up, W.sd = s_down;
+  W.shared = shared != nullptr;
+  if (shared) {
+    W.Fs = shared->Fs;
+    W.swg = reinterpret_cast<const bf16_t*>(shared->w_gate);
+    W.swu = reinterpret_cast<const bf16_t*>(shared->w_up);
+    W.swd = reinterpret_cast<const bf16_t*>(shared->w_down);
+    W.ssg = shared->s_gate, W.ssu = shared->s_up, W.ssd = shared->s_down;
+    W.gate_logits = shared->gate_logits;
+  }
+  return forward_impl(x, logits, nullptr, nullptr, T, H, F, E, k, W, out, topk_ids_out,
+                      topk_w_out, ws, ws_bytes, stream);
 }
 
 int moe_forward_routed(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void fp8_scales_kernel(const bf16_t* __restric
 // carries into the exponent field). The sign is v's (also for zeros).
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {
   const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
+  const float a = fminf(fabsf(v), 448.0f);  // saturate (only MXFP8 blocks reach past 448)
   uint32_t code;
   if (a < 0.015625f) {
     code = static_cast<uint32_t>(rintf(a * 512.0f));
@@ -296,7 +296,94 @@ __global__ __launch_bounds__(256) void mxfp4_encode_kernel(
   out[idx] = word;
 }
 
+// MXFP8 quantization, step 1: one thread per scale byte of the padded layout
+// [G][nblk][skb][64]: for column n and K-block b the largest |w| (bf16
+// magnitudes order like their bit patterns); X = floor(log2 amax) - 8 =
+// exponent field - 135 for a normal amax, raised to -117 (also for a
+// subnormal amax), 0 for an all-zero block and past K or N; the byte is
+// X + 127.
+__global__ __launch_bounds__(256) void mxfp8_scales_kernel(const bf16_t* __restrict__ w, int K,
+                                                           int N, int nblk, int skb,
+                                                           int64_t total,
+                                                           uint8_t* __restrict__ out) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int c = static_cast<int>(idx & 63);
+  int64_t rest = idx >> 6;
+  const int b = static_cast<int>(rest % skb);
+  rest /= skb;
+  const int nb = static_cast<int>(rest % nblk);
+  const int64_t g = rest / nblk;
+  const int n = nb * 64 + c;
+  int X = 0;
+  if (n < N && 32 * b < K) {
+    const bf16_t* p = w + (g * K + 32 * b) * N + n;
+    const int rows = min(32, K - 32 * b);
+    uint32_t amax = 0;
+    for (int k = 0; k < rows; ++k) {
+      const uint32_t m = p[static_cast<int64_t>(k) * N] & 0x7fffu;
+      amax = m > amax ? m : amax;
+    }
+    if (amax != 0) {
+      const int e = static_cast<int>(amax >> 7);
+      X = e == 0 ? -117 : max(e - 135, -117);
+    }
+  }
+  out[idx] = static_cast<uint8_t>(X + 127);
+}
+
+// MXFP8 quantization, step 2: one thread per 8-byte chunk of the fp8 block
+// layout (physical chunk p of column c in half h of block (g, nb, kb), rows
+// 8q..8q+7, q = p ^ ((c >> 2) & 3)), each weight divided by its K-block's
+// scale (exact: a power of two) and encoded, saturating at 448, with the
+// weight's own sign.
+__global__ __launch_bounds__(256) void mxfp8_encode_kernel(
+    const bf16_t* __restrict__ w, int K, int N, int nblk, int kblk, int skb, int64_t chunks,
+    const uint8_t* __restrict__ scales, uint8_t* __restrict__ out) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= chunks) return;
+  const int p = static_cast<int>(idx & 3);
+  const int c = static_cast<int>((idx >> 2) & 63);
+  const int h = static_cast<int>((idx >> 8) & 1);
+  int64_t blk = idx >> 9;
+  const int kb = static_cast<int>(blk % kblk);
+  blk /= kblk;
+  const int nb = static_cast<int>(blk % nblk);
+  const int64_t g = blk / nblk;
+  const int q = p ^ ((c >> 2) & 3);
+  const int n = nb * 64 + c;
+  const int k0 = kb * 64 + h * 32 + q * 8;
+  uint32_t lo = 0, hi = 0;
+  if (n < N && k0 < K) {  // K is a multiple of 8: all 8 rows are inside K
+    const int X = static_cast<int>(scales[((g * nblk + nb) * skb + k0 / 32) * 64 + c]) - 127;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t bits = static_cast<uint32_t>(w[(g * K + k0 + j) * N + n]);
+      const float x = __uint_as_float(bits << 16);
+      const uint32_t code = (e4m3_encode(ldexpf(fabsf(x), -X)) & 0x7fu) | ((bits >> 8) & 0x80u);
+      if (j < 4) lo |= code << (8 * j);
+      else hi |= code << (8 * (j - 4));
+    }
+  }
+  reinterpret_cast<uint2*>(out)[idx] = uint2{lo, hi};
+}
+
 }  // namespace
+
+hipError_t launch_quantize_mxfp8(const bf16_t* w, int G, int K, int N, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t stream) {
+  const int nblk = (N + 63) / 64, kblk = (K + 63) / 64, skb = mx_scale_kblocks(K);
+  const int64_t total = mxfp4_scale_bytes(G, K, N);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(mxfp8_scales_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
+                     dim3(256), 0, stream, w, K, N, nblk, skb, total, scales);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t chunks = fp8_weight_bytes(G, K, N) / 8;
+  hipLaunchKernelGGL(mxfp8_encode_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)),
+                     dim3(256), 0, stream, w, K, N, nblk, kblk, skb, chunks, scales, codes);
+  return hipGetLastError();
+}
 
 int64_t mxfp4_weight_bytes(int G, int K, int N) {
   return static_cast<int64_t>(G) * ((N + 63) / 64) * ((K + 63) / 64) * 2048;
@@ -395,6 +482,7 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
   const int tc = tile_class(p);
   if (p.gated && tc == kSmall && use_rs_gateup(p)) return launch_rs(p, stream);
   if (p.seg[0].packed == 3) return launch_mxfp4(p, tc, stream);
+  if (p.seg[0].packed == 5) return launch_mxfp8(p, tc, stream);
   if (p.seg[0].packed == 2) return launch_fp8(p, tc, stream);
   if (p.gated) return launch_bf16_gated(p, tc, stream);
   if (p.out_f32) return launch_bf16_plain_f32(p, tc, stream);

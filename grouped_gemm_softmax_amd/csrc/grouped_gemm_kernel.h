@@ -84,6 +84,21 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 u) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Eight E4M3 codes (the bytes of u, in order) times a power-of-two scale,
+// widened to bf16: gfx950's v_cvt_scalef32_pk_f32_fp8 decodes two codes of
+// the low or the high word of a dword to fp32 and applies the scale; every
+// such product of an MXFP8 weight is a bf16 value, so the upper half of each
+// fp32 is exact.
+__device__ __forceinline__ bf16x8 fp8x8_scaled_to_bf16(uint2 u, float scale) {
+  const auto f01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u.x, scale, false);
+  const auto f23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u.x, scale, true);
+  const auto f45 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u.y, scale, false);
+  const auto f67 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u.y, scale, true);
+  const uint4 v = uint4{hi16_pair(f01[0], f01[1]), hi16_pair(f23[0], f23[1]),
+                        hi16_pair(f45[0], f45[1]), hi16_pair(f67[0], f67[1])};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Eight E2M1 codes (the nibbles of u, low nibble first) times a power-of-two
 // scale, widened to bf16: gfx950's v_cvt_scalef32_pk_f32_fp4 decodes the two
 // codes of one byte to fp32 and applies the scale; every such product is a
@@ -119,7 +134,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <int BT_, int BF_, int BK_, int WT_, int WF_, int STAGES_, bool GATED_,
-          bool PREFETCH_, int MIN_WAVES_ = 1, int WBITS_ = 16, bool PP_ = false>
+          bool PREFETCH_, int MIN_WAVES_ = 1, int WBITS_ = 16, bool PP_ = false,
+          bool MX_ = (WBITS_ == 4)>
 struct TileCfg {
   static constexpr int BT = BT_;  // activation rows (tokens) per tile
   static constexpr int BF = BF_;  // output columns per tile
@@ -137,7 +153,10 @@ struct TileCfg {
   // bits per weight element: 16 (bf16), 8 (fp8 E4M3 codes) or 4 (MXFP4
   // E2M1 codes); the 8- and 4-bit codes exist in their packed layouts only
   static constexpr int WBITS = WBITS_;
-  static constexpr bool MX = WBITS == 4;
+  // block scales: one E8M0 scale byte per 32 K-values of a column (MXFP4,
+  // and MXFP8 on 8-bit codes), carried in the ring behind each stage's
+  // operands; 8-bit codes without them have per-column fp32 scales
+  static constexpr bool MX = MX_;
   // Ping-pong schedule: the two waves of each SIMD alternate between an
   // MFMA phase and a memory phase (LDS fragment reads, DMA issue), so one of
   // them always feeds the matrix core (8 waves, no fragment prefetch).
@@ -145,7 +164,7 @@ struct TileCfg {
   // Ping-pong tiles on fp8 codes widen each stage's weights once into a
   // double-buffered bf16 tile (packed bf16 layout), instead of every wave
   // widening the fragments it reads.
-  static constexpr bool WIDEN = PP_ && WBITS_ == 8;
+  static constexpr bool WIDEN = PP_ && WBITS_ == 8 && !MX_;
   static constexpr int WW_BYTES = WIDEN ? (GATED_ ? 2 : 1) * BK_ * BF_ * 2 : 1;
   static constexpr int NW = WT * WF;
   static constexpr int kThreads = NW * kWave;
@@ -177,6 +196,7 @@ struct TileCfg {
                 "equal DMA share per wave, one operand kind per instruction slot");
   static_assert(STAGES >= 3 && STAGES <= 8, "ring depth");
   static_assert(WBITS == 16 || WBITS == 8 || WBITS == 4, "bf16, fp8 or mxfp4 weights");
+  static_assert((WBITS == 4) <= MX && !(WBITS == 16 && MX), "4-bit codes carry block scales");
   static_assert(!MX || (SC_SLOT % 16 == 0 && SC_SLOT > 0 && SC_PIECE % SC_SLOT == 0),
                 "each wave's scale slot: whole 16-byte chunks inside one piece");
   // vmcnt holds at most 63 outstanding operations per wave: the K-steps in
@@ -335,8 +355,8 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
 
   constexpr int W_PER_MAT = C::W_BYTES / 1024;   // DMA instructions per weight matrix
   constexpr int IPS = C::SB_BYTES / 1024;        // instructions per weight sub-block
-  constexpr bool FP8 = C::WBITS == 8;
-  constexpr bool MX = C::MX;
+  constexpr bool FP8 = C::WBITS == 8 && !C::MX;  // per-column fp32 scales
+  constexpr bool MX = C::MX;                     // block scale bytes (MXFP4, MXFP8)
   static_assert(!(FP8 || MX) || PACKED, "fp8 and mxfp4 weights exist only in packed layouts");
   constexpr int RPI_X = 1024 / (C::BK * 2);      // activation rows per instruction
 
@@ -512,13 +532,13 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
           // copies 8 consecutive rows (1 KB) of one block. Sub-blocks past N
           // re-load the last block (their outputs are masked).
           const int nb = min(it.n0 / 64 + jj / IPS, it.nblk - 1);
-          if constexpr (FP8) {
+          if constexpr (C::WBITS == 8) {
             // 4 KB blocks of codes: [32-row half][64 columns][32 bytes]; a
             // 32-deep step reads one half, a 64-deep step both (element
             // offsets below are in bf16 units, 2 codes each)
             const int64_t blk = static_cast<int64_t>(nb) * it.kblk + k0 / 64;
             base = w + blk * 2048 + ((k0 % 64) / 32) * 1024 + (jj % IPS) * 512;
-          } else if constexpr (MX) {
+          } else if constexpr (C::WBITS == 4) {
             // 2 KB blocks of E2M1 codes: [32-row half][64 columns][16 bytes]
             // (bf16-unit offsets: 4 codes each)
             const int64_t blk = static_cast<int64_t>(nb) * it.kblk + k0 / 64;
@@ -588,6 +608,18 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
                       ((g16 ^ ((c >> 2) & 3)) << 3);
       const uint2 u = *reinterpret_cast<const uint2*>(p);
       return fp8x8_to_bf16(u);
+    } else if constexpr (MX && C::WBITS == 8) {
+      // MXFP8: the lane's column and its 8 consecutive K codes (one 8-byte
+      // chunk, as for fp8 above), widened exactly to bf16 with the
+      // K-block's scale byte (behind the stage's operands, as for mxfp4)
+      const int col = wf * C::TF + fi * 16 + i16;
+      const int c = col & 63;
+      const char* p = buf + m * C::W_BYTES + (col >> 6) * C::SB_BYTES + s * 2048 + c * 32 +
+                      ((g16 ^ ((c >> 2) & 3)) << 3);
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      const uint32_t e8 = *reinterpret_cast<const uint8_t*>(
+          buf + C::OP_BYTES + ((m * C::SB + (col >> 6)) * (C::BK / 32) + s) * 64 + c);
+      return fp8x8_scaled_to_bf16(u, __uint_as_float(e8 << 23));
     } else if constexpr (MX) {
       // the lane's column and its 8 consecutive K codes (one dword of the
       // column's 16 bytes in this 32-row half; 16 consecutive columns' rows
@@ -1374,6 +1406,17 @@ using GateUpMid4 = TileCfg<32, 64, 64, 1, 2, 4, true, true, 4, 4>;
 using DownSmall4 = TileCfg<16, 64, 64, 1, 2, 4, false, true, 4, 4>;
 using GateUpLarge128_4 = TileCfg<128, 128, 64, 4, 2, 4, true, false, 2, 4>;
 using DownLarge128_4 = TileCfg<128, 256, 64, 4, 2, 4, false, false, 2, 4>;
+// MXFP8 weights (E4M3 codes with a scale byte per 32 K-values of a column):
+// the fp8 decode tiles' shapes with the mxfp4 tiles' scale handling; the
+// 128-row tiles serve every larger class, as for mxfp4.
+using GateUpSmallM8 = TileCfg<16, 64, 64, 1, 2, 4, true, true, 1, 8, false, true>;
+using GateUpMidM8 = TileCfg<32, 64, 64, 1, 2, 4, true, true, 1, 8, false, true>;
+using DownSmallM8 = TileCfg<32, 64, 64, 1, 4, 4, false, true, 1, 8, false, true>;
+using GateUpLarge128_M8 = TileCfg<128, 128, 64, 4, 2, 4, true, false, 2, 8, false, true>;
+using DownLarge128_M8 = TileCfg<128, 256, 64, 4, 2, 4, false, false, 2, 8, false, true>;
+static_assert(DownLarge128_M8::BT == DownLarge128::BT && DownLarge128_M8::BF == DownLarge128::BF &&
+                  DownSmallM8::BT == DownSmall::BT && DownSmallM8::BF == DownSmall::BF,
+              "mxfp8 tiles share the bf16 tiles' shapes (the split-K plan and tile classes)");
 static_assert(DownLarge128_4::BT == DownLarge128::BT &&
                   DownLarge128_4::BF == DownLarge128::BF && DownSmall4::BF == DownSmall::BF,
               "mxfp4 tiles share the bf16 tiles' shapes (the split-K plan and tile classes)");
@@ -1452,7 +1495,7 @@ hipError_t launch_cfg(const GemmProblem& p, hipStream_t stream) {
   for (int s = 1; s < p.nseg; ++s)
     if (p.seg[s].packed != layout) return hipErrorInvalidValue;  // one layout per launch
   if constexpr (C::MX) {
-    if (layout != 3) return hipErrorInvalidValue;
+    if (layout != (C::WBITS == 4 ? 3 : 5)) return hipErrorInvalidValue;
     return ktail ? launch_tail<C, OutT, true, true>(p, bound, stream)
                  : launch_tail<C, OutT, false, true>(p, bound, stream);
   } else if constexpr (C::WBITS == 8) {
@@ -1488,6 +1531,7 @@ hipError_t launch_bf16_plain_f32(const GemmProblem& p, int tc, hipStream_t strea
 hipError_t launch_bf16_plain_bf16(const GemmProblem& p, int tc, hipStream_t stream);
 hipError_t launch_fp8(const GemmProblem& p, int tc, hipStream_t stream);
 hipError_t launch_mxfp4(const GemmProblem& p, int tc, hipStream_t stream);
+hipError_t launch_mxfp8(const GemmProblem& p, int tc, hipStream_t stream);
 hipError_t launch_rs(const GemmProblem& p, hipStream_t stream);
 
 }  // namespace moe

@@ -56,11 +56,13 @@ struct GemmSegment {
   int K;
   int N;
   int packed = 0;          // weight layout: 0 [K][N] bf16, 1 packed bf16, 2 packed fp8,
-                           // 3 packed mxfp4
+                           // 3 packed mxfp4, 5 packed mxfp8
   // fp8 (packed == 2): E4M3 codes in 4 KB blocks (fp8_weight_bytes), each
   // group's output columns scaled by scale0/scale1 + g*N (fp32 powers of two).
   // mxfp4 (packed == 3): E2M1 codes in 2 KB blocks (mxfp4_weight_bytes) and
   // E8M0 scale bytes per 32 K-values of a column (mxfp4_scale_bytes).
+  // mxfp8 (packed == 5): E4M3 codes in the fp8 4 KB blocks and the mxfp4
+  // scale-byte layout.
   const void* scale0 = nullptr;
   const void* scale1 = nullptr;
   // Optional row map: activation row of row p is gather[p] (`act` is then
@@ -137,6 +139,14 @@ hipError_t launch_quantize_fp8(const bf16_t* w, int G, int K, int N, uint8_t* co
 int64_t mxfp4_weight_bytes(int G, int K, int N);
 int64_t mxfp4_scale_bytes(int G, int K, int N);
 hipError_t launch_quantize_mxfp4(const bf16_t* w, int G, int K, int N, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t stream);
+
+// MXFP8 weights (OCP microscaling, E4M3 elements): W [G][K][N] as E4M3 codes
+// in the fp8 block layout (fp8_weight_bytes) and one E8M0 scale byte per 32
+// K-values of a column in the mxfp4 scale layout (mxfp4_scale_bytes): scale
+// 2^X with X = floor(log2 max|w| of the 32) - 8, at least -117 (0 for an
+// all-zero block); codes round to nearest, ties to even, saturating at 448.
+hipError_t launch_quantize_mxfp8(const bf16_t* w, int G, int K, int N, uint8_t* codes,
                                  uint8_t* scales, hipStream_t stream);
 hipError_t launch_pack_weights(const bf16_t* w, int G, int K, int N, bf16_t* packed,
                                hipStream_t stream);

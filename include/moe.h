@@ -418,6 +418,63 @@ int moe_forward_mxfp4(const moe_bf16* x, const float* logits, int T, int H, int 
                       int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
                       void* stream);
 
+/* ---- MXFP8 weights ----
+ * The FP8 expert GEMMs of the same sections of the DeepGEMM article with
+ * block scales, read as the OCP Microscaling format MXFP8 with E4M3
+ * elements, for the weights only: each matrix W [G,K,N] is stored as E4M3
+ * codes (as for moe_quantize_fp8) and one E8M0 scale byte per 32 K-values
+ * of a column, the scale 2^X with X = floor(log2(max |W| of the 32)) - 8
+ * (the OCP rule: the largest magnitude lands in [256, 512); raised to -117,
+ * so dequantized weights stay normal bf16 values; 0 for an all-zero block).
+ * A weight is code_value * 2^X, codes rounded to nearest with ties to even
+ * and saturating at 448. The activations stay bf16: every dequantized weight
+ * is a bf16 value, so a layer on mxfp8 weights is exactly the bf16 layer on
+ * the dequantized weights, at 8.25 bits per weight.
+ *
+ * Layout of the codes: the fp8 block layout above (G x ceil(N/64) x
+ * ceil(K/64) blocks of 4096 bytes). Scale bytes: the mxfp4 layout above
+ * ([G][ceil(N/64)][4*ceil(K/128)][64], 127 past K or N). Both 16-byte
+ * aligned; the shared expert's matrices are quantized as G = 1. */
+
+/* Bytes of the codes and of the scale bytes of a [G,K,N] weight tensor; 0
+ * for invalid sizes. */
+size_t moe_mxfp8_weights_bytes(int G, int K, int N);
+size_t moe_mxfp8_scales_bytes(int G, int K, int N);
+
+/* Quantize bf16 W [G,K,N] (K, N multiples of 8) into codes and scale bytes.
+ * Once, at load time. Errors as moe_quantize_fp8. */
+int moe_quantize_mxfp8(const moe_bf16* w, int G, int K, int N, uint8_t* codes,
+                       size_t codes_bytes, uint8_t* scales, size_t scales_bytes, void* stream);
+
+/* moe_gateup_swiglu / moe_down on mxfp8 weights: equal, bit for bit, to the
+ * bf16 calls on the dequantized weights. */
+int moe_gateup_swiglu_mxfp8(const moe_bf16* x_perm, const int32_t* expert_offsets, int M, int H,
+                            int F, int E, const uint8_t* w_gate, const uint8_t* s_gate,
+                            const uint8_t* w_up, const uint8_t* s_up, moe_bf16* h,
+                            void* stream);
+int moe_down_mxfp8(const moe_bf16* h, const int32_t* expert_offsets, int M, int F, int H, int E,
+                   const uint8_t* w_down, const uint8_t* s_down, moe_bf16* y_perm, void* stream);
+
+/* Shared expert with mxfp8 weights (HOST struct, device pointers). */
+typedef struct {
+  const uint8_t* w_gate;
+  const uint8_t* s_gate;
+  const uint8_t* w_up;
+  const uint8_t* s_up;
+  const uint8_t* w_down;
+  const uint8_t* s_down;
+  int32_t Fs;
+  const float* gate_logits;
+} moe_shared_expert_mxfp8;
+
+/* moe_forward on mxfp8 weights (same workspace and outputs). */
+int moe_forward_mxfp8(const moe_bf16* x, const float* logits, int T, int H, int F, int E, int k,
+                      const uint8_t* w_gate, const uint8_t* s_gate, const uint8_t* w_up,
+                      const uint8_t* s_up, const uint8_t* w_down, const uint8_t* s_down,
+                      const moe_shared_expert_mxfp8* shared, moe_bf16* out,
+                      int32_t* topk_ids_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                      void* stream);
+
 /* ---- Training backward ----
  * The news page "Triton-Optimierter BF16 Grouped GEMM Kernel beschleunigt
  * MoE-Modelle" (meineki.news), introduction, presents its grouped GEMM for

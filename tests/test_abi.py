@@ -260,6 +260,48 @@ def test_mxfp4_calls_validation(L):
                                None, NULL, NULL, NULL, NULL, 0, NULL) == OK    # T = 0
 
 
+def test_mxfp8_bytes():
+    # codes: the fp8 layout, ceil(N/64) x ceil(K/64) blocks of 4 KB; scales:
+    # the mxfp4 layout, ceil(N/64) x 4*ceil(K/128) x 64 bytes
+    assert B.moe_mxfp8_weights_bytes(2, 200, 328) == 2 * 6 * 4 * 4096
+    assert B.moe_mxfp8_scales_bytes(2, 200, 328) == 2 * 6 * 8 * 64
+    assert B.moe_mxfp8_weights_bytes(1, 64, 64) == 4096
+    assert B.moe_mxfp8_scales_bytes(1, 64, 64) == 4 * 64
+    assert B.moe_mxfp8_weights_bytes(0, 64, 64) == 0
+    assert B.moe_mxfp8_scales_bytes(1, 60, 64) == 0                   # K % 8 != 0
+
+
+def test_mxfp8_calls_validation(L):
+    nc, ns = B.moe_mxfp8_weights_bytes(2, 64, 96), B.moe_mxfp8_scales_bytes(2, 64, 96)
+    q = lambda w=P, G=2, K=64, N=96, c=P, ncb=nc, s=P, nsb=ns: L.moe_quantize_mxfp8(
+        w, G, K, N, c, ncb, s, nsb, NULL)
+    assert q(w=NULL) == INVALID
+    assert q(s=NULL) == INVALID
+    assert q(G=0) == INVALID
+    assert q(N=100) == SHAPE
+    assert q(c=Q) == MISALIGNED
+    assert q(s=Q) == MISALIGNED
+    assert q(ncb=nc - 1) == WS_SMALL
+    assert q(nsb=ns - 1) == WS_SMALL
+    g = lambda sg=P, su=P, wg=P: L.moe_gateup_swiglu_mxfp8(P, P, 16, 64, 96, 2, wg, sg, P, su, P,
+                                                           NULL)
+    assert g(sg=NULL) == INVALID
+    assert g(su=Q) == MISALIGNED
+    assert g(wg=Q) == MISALIGNED
+    assert L.moe_down_mxfp8(P, P, 16, 96, 64, 2, P, NULL, P, NULL) == INVALID
+    assert L.moe_down_mxfp8(P, P, 0, 96, 64, 2, NULL, NULL, NULL, NULL) == OK   # M = 0
+    ws = B.moe_forward_workspace_bytes(10, 64, 96, 8, 2, 0)
+    f = lambda sd=P, ws_bytes=ws: L.moe_forward_mxfp8(P, P, 10, 64, 96, 8, 2, P, P, P, P, P, sd,
+                                                       None, P, NULL, NULL, P, ws_bytes, NULL)
+    assert f(sd=NULL) == INVALID
+    assert f(ws_bytes=ws - 1) == WS_SMALL
+    bad = B.SharedExpertMxfp8(0x10000, 0x10000, 0x10000, None, 0x10000, 0x10000, 32, None)
+    assert L.moe_forward_mxfp8(P, P, 10, 64, 96, 8, 2, P, P, P, P, P, P, ctypes.byref(bad), P,
+                               NULL, NULL, P, 1 << 40, NULL) == INVALID        # null shared scale
+    assert L.moe_forward_mxfp8(NULL, NULL, 0, 64, 96, 8, 2, NULL, NULL, NULL, NULL, NULL, NULL,
+                               None, NULL, NULL, NULL, NULL, 0, NULL) == OK    # T = 0
+
+
 def test_forward_routed_validation(L):
     ws = B.moe_forward_workspace_bytes(10, 64, 96, 8, 2, 0)
     args = lambda x=P, ids=P, w=P, k=2, packed=0, ws_bytes=ws: (
