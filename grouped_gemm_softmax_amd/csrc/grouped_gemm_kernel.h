@@ -54,6 +54,7 @@
 // packed weights (pack_weights_kernel) already hold each column's
 // K-values contiguously, so a lane reads its fragment with one 16-byte LDS
 // read. MFMA: v_mfma_f32_16x16x32_bf16, fp32 accumulation.
+#include <algorithm>
 #include <utility>
 
 #include "common.h"
@@ -161,10 +162,10 @@ struct TileCfg {
   // MFMA phase and a memory phase (LDS fragment reads, DMA issue), so one of
   // them always feeds the matrix core (8 waves, no fragment prefetch).
   static constexpr bool PP = PP_;
-  // Ping-pong tiles on fp8 codes widen each stage's weights once into a
-  // double-buffered bf16 tile (packed bf16 layout), instead of every wave
-  // widening the fragments it reads.
-  static constexpr bool WIDEN = PP_ && WBITS_ == 8 && !MX_;
+  // Ping-pong tiles on 8-bit codes (fp8, mxfp8) widen each stage's weights
+  // once into a double-buffered bf16 tile (packed bf16 layout), instead of
+  // every wave widening the fragments it reads.
+  static constexpr bool WIDEN = PP_ && WBITS_ == 8;
   static constexpr int WW_BYTES = WIDEN ? (GATED_ ? 2 : 1) * BK_ * BF_ * 2 : 1;
   static constexpr int NW = WT * WF;
   static constexpr int kThreads = NW * kWave;
@@ -381,8 +382,8 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     int nk;           // K-steps of the slice
     int nk_all;       // K-steps of the whole K
     int nblk, kblk;   // packed: 64-column and 64-row blocks of one group
-    const void* sc0;  // fp8: the group's column scales (gate / plain matrix);
-    const void* sc1;  // mxfp4: its scale bytes (gate / plain, up)
+    const void* sc0;  // fp8: the group's column scales (gate / plain matrix, up);
+    const void* sc1;  // mxfp4/mxfp8: sc0 = this wave's slot source of the scale bytes
     // per-lane byte offsets of this wave's DMA sources within a K-step,
     // relative to the step's scalar base
     uint32_t voff[C::OPW];
@@ -439,10 +440,17 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
       it.sc1 = C::GATED ? static_cast<const float*>(S.scale1) + static_cast<int64_t>(v.local) * S.N
                         : it.sc0;
     } else if constexpr (MX) {
-      // scale bytes [G][nblk][4 * ceil(K/128)][64]
-      const int64_t per_group = static_cast<int64_t>(it.nblk) * mx_scale_kblocks(S.K) * 64;
-      it.sc0 = static_cast<const uint8_t*>(S.scale0) + v.local * per_group;
-      it.sc1 = C::GATED ? static_cast<const uint8_t*>(S.scale1) + v.local * per_group : it.sc0;
+      // scale bytes [G][nblk][4 * ceil(K/128)][64]; each wave loads one slot
+      // of every stage's scales: piece (matrix m, sub-block sb), so the item
+      // keeps only that slot's source at K-block 0 (a stage adds its K-block)
+      const int kb = mx_scale_kblocks(S.K);
+      const int64_t per_group = static_cast<int64_t>(it.nblk) * kb * 64;
+      const int pw = (wave * C::SC_SLOT) / C::SC_PIECE;
+      const int m = pw / C::SB, sb = pw % C::SB;
+      const int nb = min(it.n0 / 64 + sb, it.nblk - 1);  // sub-blocks past N: the last
+      it.sc0 = static_cast<const uint8_t*>(m ? S.scale1 : S.scale0) + v.local * per_group +
+               static_cast<int64_t>(nb) * kb * 64 + (wave * C::SC_SLOT) % C::SC_PIECE;
+      it.sc1 = it.sc0;
     } else {
       it.sc0 = it.sc1 = nullptr;
     }
@@ -575,15 +583,10 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
       dma16(base, voff, buf + j * 1024);
     }
     if constexpr (MX) {
-      // this wave's slot of the stage's scale bytes: piece (matrix m,
-      // sub-block sb), BK/32 K-blocks of 64 columns from K-block k0/32
+      // this wave's slot of the stage's scale bytes (piece and offset fixed
+      // per item, in sc0), BK/32 K-blocks of 64 columns from K-block k0/32
       constexpr int LANES = C::SC_SLOT / 16;
-      const int pw = (wave * C::SC_SLOT) / C::SC_PIECE;
-      const int m = pw / C::SB, sb = pw % C::SB;
-      const int nb = min(it.n0 / 64 + sb, it.nblk - 1);
-      const uint8_t* sbase = static_cast<const uint8_t*>(m ? it.sc1 : it.sc0) +
-                             (static_cast<int64_t>(nb) * mx_scale_kblocks(it.K) + k0 / 32) * 64 +
-                             (wave * C::SC_SLOT) % C::SC_PIECE;
+      const uint8_t* sbase = static_cast<const uint8_t*>(it.sc0) + (k0 / 32) * 64;
       char* const dst = buf + C::OP_BYTES + wave * C::SC_SLOT;
       if (LANES == kWave || lane < LANES) dma16(sbase, static_cast<uint32_t>(lane) * 16u, dst);
     }
@@ -675,20 +678,34 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     return *reinterpret_cast<const bf16x8*>(wbuf + m * (C::BK * C::BF * 2) + (col >> 6) * 4096 +
                                             c * 64 + ((g16 ^ ((c >> 1) & 3)) << 4));
   };
-  // this thread's unit of a stage's fp8 codes (16 codes: two 8-code chunks of
-  // one column's 32) widened into the bf16 tile; unit = thread index, so
-  // threads 0-255 (waves 0-3) cover one half of the stage, 256-511 the other
+  // this thread's unit of a stage's 8-bit codes (16 codes: two 8-code chunks
+  // of one column's 32) widened into the bf16 tile; unit = thread index, so
+  // threads 0-255 (waves 0-3) cover one half of the stage, 256-511 the other.
+  // Unit cr = (matrix, sub-block, column) is the column's row of codes at
+  // cr * 32 and of bf16 values at cr * 64. Its logical chunks 2hr and 2hr+1
+  // sit at physical positions 2hr ^ x and (2hr ^ x) ^ 1, x = (c >> 2) & 3:
+  // one aligned 16-byte pair, read with one instruction (one address
+  // register per ring stage instead of two). mxfp8: the 32 codes are one
+  // K-block, whose scale byte is byte cr of the stage's scales.
   auto widen = [&](const char* codes, char* wbuf) INL {
     const int cr = tid >> 1, hr = tid & 1;
-    const int m = cr / (C::SB * 64), sb = (cr >> 6) % C::SB, c = cr & 63;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int q = 2 * hr + h;
-      const uint2 u = *reinterpret_cast<const uint2*>(codes + m * C::W_BYTES + sb * C::SB_BYTES +
-                                                      c * 32 + ((q ^ ((c >> 2) & 3)) << 3));
-      *reinterpret_cast<bf16x8*>(wbuf + m * (C::BK * C::BF * 2) + sb * 4096 + c * 64 +
-                                 ((q ^ ((c >> 1) & 3)) << 4)) = fp8x8_to_bf16(u);
+    const int c = cr & 63;
+    const int x = (c >> 2) & 3;
+    const int p0 = (2 * hr) ^ (x & 2);  // even position of the pair
+    const uint4 u = *reinterpret_cast<const uint4*>(codes + cr * 32 + p0 * 8);
+    float scale = 1.f;
+    if constexpr (MX) {
+      const uint32_t e8 = *reinterpret_cast<const uint8_t*>(codes + C::OP_BYTES + cr);
+      scale = __uint_as_float(e8 << 23);
     }
+    const int qlo = p0 ^ x, qhi = qlo ^ 1;  // logical chunks of the low and high half
+    const int y = (c >> 1) & 3;             // the bf16 tile's chunk rotation
+    char* const wb = wbuf + cr * 64;
+    const uint2 lo = uint2{u.x, u.y}, hi = uint2{u.z, u.w};
+    *reinterpret_cast<bf16x8*>(wb + ((qlo ^ y) << 4)) =
+        MX ? fp8x8_scaled_to_bf16(lo, scale) : fp8x8_to_bf16(lo);
+    *reinterpret_cast<bf16x8*>(wb + ((qhi ^ y) << 4)) =
+        MX ? fp8x8_scaled_to_bf16(hi, scale) : fp8x8_to_bf16(hi);
   };
   auto load_frags = [&](const char* buf, Frags& F, int kvalid) INL {
 #pragma unroll
@@ -1407,14 +1424,19 @@ using DownSmall4 = TileCfg<16, 64, 64, 1, 2, 4, false, true, 4, 4>;
 using GateUpLarge128_4 = TileCfg<128, 128, 64, 4, 2, 4, true, false, 2, 4>;
 using DownLarge128_4 = TileCfg<128, 256, 64, 4, 2, 4, false, false, 2, 4>;
 // MXFP8 weights (E4M3 codes with a scale byte per 32 K-values of a column):
-// the fp8 decode tiles' shapes with the mxfp4 tiles' scale handling; the
-// 128-row tiles serve every larger class, as for mxfp4.
+// the fp8 tiles' shapes with the mxfp4 tiles' scale handling. The 128- and
+// 256-row tiles widen each 32-deep stage once, as for fp8; a stage's 32
+// K-values are one scale block, so the stage carries one scale byte per
+// column and matrix (256 bytes behind the operands).
 using GateUpSmallM8 = TileCfg<16, 64, 64, 1, 2, 4, true, true, 1, 8, false, true>;
 using GateUpMidM8 = TileCfg<32, 64, 64, 1, 2, 4, true, true, 1, 8, false, true>;
 using DownSmallM8 = TileCfg<32, 64, 64, 1, 4, 4, false, true, 1, 8, false, true>;
-using GateUpLarge128_M8 = TileCfg<128, 128, 64, 4, 2, 4, true, false, 2, 8, false, true>;
-using DownLarge128_M8 = TileCfg<128, 256, 64, 4, 2, 4, false, false, 2, 8, false, true>;
+using GateUpLargeM8 = TileCfg<256, 128, 32, 4, 2, 5, true, false, 1, 8, true, true>;
+using GateUpLarge128_M8 = TileCfg<128, 128, 32, 4, 2, 5, true, false, 1, 8, true, true>;
+using DownLarge128_M8 = TileCfg<128, 256, 32, 4, 2, 5, false, false, 1, 8, true, true>;
+using DownLargeM8 = TileCfg<256, 256, 32, 4, 2, 5, false, false, 1, 8, true, true>;
 static_assert(DownLarge128_M8::BT == DownLarge128::BT && DownLarge128_M8::BF == DownLarge128::BF &&
+                  DownLargeM8::BT == DownLarge::BT && DownLargeM8::BF == DownLarge::BF &&
                   DownSmallM8::BT == DownSmall::BT && DownSmallM8::BF == DownSmall::BF,
               "mxfp8 tiles share the bf16 tiles' shapes (the split-K plan and tile classes)");
 static_assert(DownLarge128_4::BT == DownLarge128::BT &&
@@ -1456,6 +1478,16 @@ int blocks_per_cu(size_t dyn) {
     cached_dyn[dev] = dyn;
   }
   return cached_n[dev];
+}
+
+// The most groups whose item table (dynamic LDS: 12 bytes a group, 8 more)
+// fits beside a tile's static LDS (its ring stages and widened tiles, each
+// array aligned to 1 KB, plus 1 KB for the rest) in the CU's 160 KB.
+template <class C>
+constexpr int max_groups_in_lds() {
+  constexpr int up = (C::STAGE_BYTES + 1023) / 1024 * 1024;
+  constexpr int wide = C::WIDEN ? 2 * ((C::WW_BYTES + 1023) / 1024 * 1024) : 0;
+  return (160 * 1024 - C::STAGES * up - wide - 1024 - 8) / 12;
 }
 
 template <class C>
