@@ -24,6 +24,10 @@ LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(PKG, "libmoe.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
 
 
+# moe_status values the binding tests for (include/moe.h)
+MOE_ERR_BAD_IDS = -6
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, text: str, call: str):
         super().__init__(f"{call}: {text} (status {status})")
@@ -112,6 +116,8 @@ _SIGNATURES = {
                           _P, _P, _SZ, _P]),
     "moe_route_backward": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
     "moe_set_dispatch_override": (_I, [_I, _I]),
+    "moe_set_diagnostics": (_I, [_I, _I]),
+    "moe_check_topk_ids": (_I, [_P, _I, _I, _I, _P]),
 }
 
 _lib = None
@@ -524,6 +530,26 @@ def moe_set_dispatch_override(decode_path: int = -1, tile_class: int = -1):
     3 256-row) of later calls in this process; -1 is the automatic choice."""
     _check(lib().moe_set_dispatch_override(decode_path, tile_class),
            "moe_set_dispatch_override")
+
+
+def moe_set_diagnostics(trace: int = -1, check_ids: int = -1):
+    """Launch trace to stderr (trace=1, as MOE_TRACE=1) and the id check of
+    the calls that take caller expert ids (check_ids=1, as MOE_DEBUG=1); 0
+    turns either off, -1 restores the environment's setting."""
+    _check(lib().moe_set_diagnostics(trace, check_ids), "moe_set_diagnostics")
+
+
+@_on_stream
+def moe_check_topk_ids(topk_ids: torch.Tensor, E: int, stream=None) -> bool:
+    """True when every id of topk_ids [T, k] lies in [0, E) (checked on the
+    GPU; waits for the result)."""
+    _need(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    st = lib().moe_check_topk_ids(_ptr(topk_ids), T, k, E, _stream(stream))
+    if st == MOE_ERR_BAD_IDS:
+        return False
+    _check(st, "moe_check_topk_ids")
+    return True
 
 
 def _shared_struct(shared, packed):

@@ -51,5 +51,46 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host code of the C ABI (argument validation, workspace carving, the
+# diagnostics) under AddressSanitizer and UndefinedBehaviorSanitizer; the
+# device code is unchanged. Each sanitizer flag applies to the host pass only.
+SANITIZED_SOURCES = ("api.hip", "diagnostics.hip")
+HOST_SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                       "-Xarch_host", "-fno-sanitize-recover=undefined",
+                       "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """The compiler's AddressSanitizer runtime, to preload into a process
+    that loads a sanitized build."""
+    hits = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib",
+                                         "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so next to " + HIPCC)
+    return hits[-1]
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """libmoe with its host-side C ABI layer sanitized, in `out_dir`; the
+    kernels' objects are those of the in-tree build (made first if missing)."""
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objs = [os.path.join(OUT_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    os.makedirs(out_dir, exist_ok=True)
+    flags = [f for f in HIP_FLAGS if f != "-O3"] + ["-O1", "-g"] + HOST_SANITIZE_FLAGS
+    link = []
+    for s, o in zip(srcs, objs):
+        if os.path.basename(s) in SANITIZED_SOURCES:
+            o = os.path.join(out_dir, os.path.basename(s)[:-4] + ".san.o")
+            _run([HIPCC, *flags, "-c", s, "-o", o])
+        link.append(o)
+    lib = os.path.join(out_dir, "libmoe_sanitized.so")
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *HOST_SANITIZE_FLAGS[:4],
+          "-shared-libsan", "-o", lib, *link])
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

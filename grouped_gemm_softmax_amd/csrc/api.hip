@@ -40,6 +40,17 @@ int check_elems(int64_t rows, int64_t cols) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// The debug check of caller-given expert ids (on with MOE_DEBUG=1 or
+// moe_set_diagnostics): counts the ids outside [0, E) and waits for the
+// count. Off, it costs nothing and enqueues nothing.
+int debug_check_ids(const int32_t* ids, int64_t n, int E, void* stream) {
+  if (!moe::check_ids_enabled()) return MOE_OK;
+  int bad = 0;
+  if (moe::count_bad_ids(ids, n, E, static_cast<hipStream_t>(stream), &bad) != hipSuccess)
+    return MOE_ERR_HIP;
+  return bad ? MOE_ERR_BAD_IDS : MOE_OK;
+}
+
 #define MOE_TRY(expr)            \
   do {                           \
     const int rc_ = (expr);      \
@@ -223,6 +234,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED: pointer not aligned (bf16 tensors need 16 bytes)";
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL: workspace below the required size";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case MOE_ERR_BAD_IDS: return "MOE_ERR_BAD_IDS: an expert id outside [0, E) (debug check)";
     default: return "unknown moe status";
   }
 }
@@ -289,6 +301,7 @@ int moe_permute(const moe_bf16* x, const int32_t* topk_ids, int T, int H, int E,
   MOE_TRY(need_bf16(x_perm));
   MOE_TRY(need_bf16(ws));
   if (ws_bytes < permute_ws_bytes(T, E, k)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  MOE_TRY(debug_check_ids(topk_ids, static_cast<int64_t>(T) * k, E, stream));
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* hist = static_cast<int32_t*>(ws);
   MOE_TRY(hip_status(moe::launch_hist(topk_ids, T, E, k, hist, s)));
@@ -521,6 +534,23 @@ size_t moe_workspace_bytes(int T, int H, int F, int E, int k, int Fs) {
   return moe_forward_workspace_bytes(T, H, F, E, k, Fs);
 }
 
+int moe_set_diagnostics(int trace, int check_ids) {
+  if (trace < -1 || trace > 1 || check_ids < -1 || check_ids > 1) return MOE_ERR_INVALID_ARG;
+  moe::set_diagnostics(trace, check_ids);
+  return MOE_OK;
+}
+
+int moe_check_topk_ids(const int32_t* topk_ids, int T, int k, int E, void* stream) {
+  MOE_TRY(check_dims(T, E, k));
+  if (T == 0) return MOE_OK;
+  MOE_TRY(need_word(topk_ids));
+  int bad = 0;
+  if (moe::count_bad_ids(topk_ids, static_cast<int64_t>(T) * k, E,
+                         static_cast<hipStream_t>(stream), &bad) != hipSuccess)
+    return MOE_ERR_HIP;
+  return bad ? MOE_ERR_BAD_IDS : MOE_OK;
+}
+
 int moe_set_dispatch_override(int decode_path, int tile_class) {
   if (decode_path < -1 || decode_path > 1 || tile_class < -1 || tile_class > 3)
     return MOE_ERR_INVALID_ARG;
@@ -604,6 +634,7 @@ static int forward_impl(const moe_bf16* x, const float* logits, const int32_t* i
   MOE_TRY(need_bf16(ws));
   const ForwardLayout L = forward_layout(T, H, F, E, k, Fs, moe::grouped_gemm_device_cus());
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!logits) MOE_TRY(debug_check_ids(ids_in, A, E, stream));
 
   char* base = static_cast<char*>(ws);
   int32_t* hist = reinterpret_cast<int32_t*>(base + L.hist);
@@ -864,6 +895,7 @@ int moe_backward(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w
   }
   const BackwardLayout L = backward_layout(T, H, F, E, k);
   if (T > 0 && ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (T > 0) MOE_TRY(debug_check_ids(topk_ids, A, E, stream));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (T == 0) {
     // no tokens: every weight gradient is zero
@@ -953,6 +985,7 @@ int moe_route_backward(const int32_t* topk_ids, const float* topk_w, const float
   MOE_TRY(need_word(topk_w));
   MOE_TRY(need_word(d_topk_w));
   MOE_TRY(need_word(d_logits));
+  MOE_TRY(debug_check_ids(topk_ids, static_cast<int64_t>(T) * k, E, stream));
   return hip_status(moe::launch_route_backward(topk_ids, topk_w, d_topk_w, T, E, k, d_logits,
                                                static_cast<hipStream_t>(stream)));
 }

@@ -274,6 +274,8 @@ hipError_t launch_backward_prep(const bf16_t* dout, const int32_t* row_dest,
                                 const float* topk_w, int T, int H, int k, bf16_t* dy,
                                 bf16_t* dout_perm, float* wrow, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
+  MOE_TRACE_LAUNCH("backward_prep_kernel", dim3(T), dim3(kPrepThreads), 0, "T=%d H=%d k=%d", T, H,
+                   k);
   hipLaunchKernelGGL(backward_prep_kernel, dim3(T), dim3(kPrepThreads), 0, stream, dout,
                      row_dest, topk_w, T, H, k, dy, dout_perm, wrow);
   return hipGetLastError();
@@ -283,6 +285,8 @@ hipError_t launch_topk_w_grad(const float* part, int nq, const int32_t* row_dest
                               float* d_topk_w, hipStream_t stream) {
   const int64_t n = static_cast<int64_t>(T) * k;
   if (n <= 0) return hipSuccess;
+  MOE_TRACE_LAUNCH("topk_w_grad_kernel", dim3(static_cast<unsigned>((n + 3) / 4)), dim3(256), 0,
+                   "assignments=%lld partials=%d", static_cast<long long>(n), nq);
   hipLaunchKernelGGL(topk_w_grad_kernel, dim3(static_cast<unsigned>((n + 3) / 4)), dim3(256), 0,
                      stream, part, nq, row_dest, n, d_topk_w);
   return hipGetLastError();
@@ -293,6 +297,8 @@ hipError_t launch_route_backward(const int32_t* topk_ids, const float* topk_w,
                                  hipStream_t stream) {
   const int64_t n = static_cast<int64_t>(T) * E;
   if (n <= 0) return hipSuccess;
+  MOE_TRACE_LAUNCH("route_backward_kernel", dim3(static_cast<unsigned>((n + 255) / 256)),
+                   dim3(256), 0, "T=%d E=%d k=%d", T, E, k);
   hipLaunchKernelGGL(route_backward_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
                      dim3(256), 0, stream, topk_ids, topk_w, d_topk_w, T, E, k, d_logits);
   return hipGetLastError();
@@ -304,6 +310,8 @@ hipError_t launch_kgrouped_gemm(const bf16_t* a, const bf16_t* b, const int32_t*
   const int64_t blocks = static_cast<int64_t>(E) * ti * tj;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  MOE_TRACE_LAUNCH("kgrouped_gemm_kernel", dim3(static_cast<unsigned>(blocks)), dim3(kKgThreads),
+                   0, "tile=%dx%d groups=%d M=%d N=%d", kKgTile, kKgTile, E, M, N);
   hipLaunchKernelGGL(kgrouped_gemm_kernel, dim3(static_cast<unsigned>(blocks)),
                      dim3(kKgThreads), 0, stream, a, b, offsets, E, M, N, ti, tj, out);
   return hipGetLastError();

@@ -112,6 +112,9 @@ hipError_t launch_combine(const void* y_perm, bool y_f32, int nslices,
                           const float* shared_gate, bf16_t* out, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   const dim3 grid(T, (H + kCombineThreads * 8 - 1) / (kCombineThreads * 8));
+  MOE_TRACE_LAUNCH("combine_kernel", grid, dim3(kCombineThreads), 0,
+                   "T=%d H=%d k=%d y=%s slices=%d shared=%d", T, H, k, y_f32 ? "f32" : "bf16",
+                   nslices, y_shared ? 1 : 0);
   if (y_f32)
     hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(kCombineThreads), 0, stream,
                        static_cast<const float*>(y_perm), nslices, y_slice_stride, row_dest,

@@ -375,11 +375,17 @@ hipError_t launch_quantize_mxfp8(const bf16_t* w, int G, int K, int N, uint8_t* 
   const int nblk = (N + 63) / 64, kblk = (K + 63) / 64, skb = mx_scale_kblocks(K);
   const int64_t total = mxfp4_scale_bytes(G, K, N);
   if (total == 0) return hipSuccess;
+  MOE_TRACE_LAUNCH("mxfp8_scales_kernel",
+                   dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
+                   "G=%d K=%d N=%d", G, K, N);
   hipLaunchKernelGGL(mxfp8_scales_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
                      dim3(256), 0, stream, w, K, N, nblk, skb, total, scales);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t chunks = fp8_weight_bytes(G, K, N) / 8;
+  MOE_TRACE_LAUNCH("mxfp8_encode_kernel",
+                   dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0,
+                   "G=%d K=%d N=%d", G, K, N);
   hipLaunchKernelGGL(mxfp8_encode_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)),
                      dim3(256), 0, stream, w, K, N, nblk, kblk, skb, chunks, scales, codes);
   return hipGetLastError();
@@ -398,11 +404,17 @@ hipError_t launch_quantize_mxfp4(const bf16_t* w, int G, int K, int N, uint8_t* 
   const int nblk = (N + 63) / 64, kblk = (K + 63) / 64, skb = mx_scale_kblocks(K);
   const int64_t total = mxfp4_scale_bytes(G, K, N);
   if (total == 0) return hipSuccess;
+  MOE_TRACE_LAUNCH("mxfp4_scales_kernel",
+                   dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
+                   "G=%d K=%d N=%d", G, K, N);
   hipLaunchKernelGGL(mxfp4_scales_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
                      dim3(256), 0, stream, w, K, N, nblk, skb, total, scales);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t words = mxfp4_weight_bytes(G, K, N) / 4;
+  MOE_TRACE_LAUNCH("mxfp4_encode_kernel",
+                   dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256), 0,
+                   "G=%d K=%d N=%d", G, K, N);
   hipLaunchKernelGGL(mxfp4_encode_kernel, dim3(static_cast<unsigned>((words + 255) / 256)),
                      dim3(256), 0, stream, w, K, N, nblk, kblk, skb, words, scales,
                      reinterpret_cast<uint32_t*>(codes));
@@ -417,11 +429,17 @@ hipError_t launch_quantize_fp8(const bf16_t* w, int G, int K, int N, uint8_t* co
                                float* scales, hipStream_t stream) {
   const int64_t cols = static_cast<int64_t>(G) * N;
   if (cols == 0) return hipSuccess;
+  MOE_TRACE_LAUNCH("fp8_scales_kernel",
+                   dim3(static_cast<unsigned>((cols + 255) / 256)), dim3(256), 0,
+                   "G=%d K=%d N=%d", G, K, N);
   hipLaunchKernelGGL(fp8_scales_kernel, dim3(static_cast<unsigned>((cols + 255) / 256)),
                      dim3(256), 0, stream, w, G, K, N, scales);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t chunks = fp8_weight_bytes(G, K, N) / 8;
+  MOE_TRACE_LAUNCH("fp8_encode_kernel",
+                   dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0,
+                   "G=%d K=%d N=%d", G, K, N);
   hipLaunchKernelGGL(fp8_encode_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)),
                      dim3(256), 0, stream, w, K, N, (N + 63) / 64, (K + 63) / 64, chunks, scales,
                      codes);
@@ -436,6 +454,9 @@ hipError_t launch_pack_weights(const bf16_t* w, int G, int K, int N, bf16_t* pac
                                hipStream_t stream) {
   const int64_t chunks = packed_weight_elems(G, K, N) / 8;
   if (chunks == 0) return hipSuccess;
+  MOE_TRACE_LAUNCH("pack_weights_kernel",
+                   dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0,
+                   "G=%d K=%d N=%d", G, K, N);
   hipLaunchKernelGGL(pack_weights_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)),
                      dim3(256), 0, stream, w, K, N, (N + 63) / 64, (K + 63) / 64, chunks,
                      packed);

@@ -1352,6 +1352,9 @@ hipError_t launch_rs_gateup(const GemmProblem& p, hipStream_t stream) {
   int64_t grid = static_cast<int64_t>(device_cu_count()) * rs_blocks_per_cu<WBITS>(dyn);
   if (bound < grid) grid = bound;
   grid = (grid + 7) / 8 * 8;
+  MOE_TRACE_LAUNCH("rs_gateup_kernel", dim3(static_cast<unsigned>(grid)), dim3(kRsThreads), dyn,
+                   "tile=%dx%d wbits=%d segments=%d groups=%d items<=%lld", kRsBT, kRsBF, WBITS,
+                   p.nseg, groups, static_cast<long long>(bound));
   hipLaunchKernelGGL((rs_gateup_kernel<WBITS>), dim3(static_cast<unsigned>(grid)),
                      dim3(kRsThreads), dyn, stream, p);
   return hipGetLastError();
@@ -1512,6 +1515,17 @@ hipError_t launch_tail(const GemmProblem& p, int64_t bound, hipStream_t stream) 
       static_cast<int64_t>(device_cu_count()) * blocks_per_cu<C, OutT, KTAIL, PACKED, TRANSW>(dyn);
   if (bound < grid) grid = bound;
   grid = (grid + 7) / 8 * 8;
+  MOE_TRACE_LAUNCH("grouped_gemm_kernel", dim3(static_cast<unsigned>(grid)), dim3(C::kThreads),
+                   dyn,
+                   "tile=%dx%dx%d stages=%d schedule=%s wbits=%d%s gated=%d out=%s ktail=%d "
+                   "layout=%d segments=%d groups=%d items<=%lld ksplit=%d",
+                   C::BT, C::BF, C::BK, C::STAGES,
+                   C::PP ? (C::WIDEN ? "pingpong-widen" : "pingpong")
+                         : (C::PREFETCH ? "ring-prefetch" : "ring"),
+                   C::WBITS, C::MX ? "+mx" : "", C::GATED ? 1 : 0,
+                   sizeof(OutT) == 4 ? "f32" : "bf16", KTAIL ? 1 : 0,
+                   TRANSW ? kWeightsTransposed : p.seg[0].packed, p.nseg, groups,
+                   static_cast<long long>(bound), p.seg[0].ksplit);
   hipLaunchKernelGGL((grouped_gemm_kernel<C, OutT, KTAIL, PACKED, TRANSW>),
                      dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), dyn, stream, p);
   return hipGetLastError();

@@ -15,6 +15,23 @@ constexpr int kPermuteSliceCols = 256;   // x columns copied per permute block
 constexpr int kPermChunks = 8;           // routing chunks per permute block
 constexpr int kMaxKSplit = 8;         // K-slices of a split down projection
 
+// --- diagnostics (diagnostics.hip) ---
+// Launch trace (MOE_TRACE) and the debug check of caller-given ids
+// (MOE_DEBUG); both read from the environment at first use, or set by
+// moe_set_diagnostics (-1: back to the environment's setting).
+bool trace_enabled();
+bool check_ids_enabled();
+void set_diagnostics(int trace, int check_ids);
+void trace_launch(const char* kernel, dim3 grid, dim3 block, size_t lds, const char* fmt, ...)
+    __attribute__((format(printf, 5, 6)));
+// Counts the ids of ids[0, n) outside [0, E) on `stream` and waits for the
+// count (so never inside a captured graph).
+hipError_t count_bad_ids(const int32_t* ids, int64_t n, int E, hipStream_t stream, int* bad);
+#define MOE_TRACE_LAUNCH(...)                                    \
+  do {                                                           \
+    if (::moe::trace_enabled()) ::moe::trace_launch(__VA_ARGS__); \
+  } while (0)
+
 // --- routing and permutation (route_permute.hip) ---
 int route_chunk_tokens(int T, int k);
 int route_num_chunks(int T, int k);

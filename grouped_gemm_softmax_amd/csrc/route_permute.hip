@@ -403,6 +403,8 @@ hipError_t launch_route_permute_small(const float* logits, const bf16_t* x, int 
   if (T <= 0) return hipSuccess;
   const int slice = kPermuteSliceCols;
   const int nslices = (H + slice - 1) / slice;
+  MOE_TRACE_LAUNCH("route_permute_small_kernel", dim3(nslices), dim3(kSmallThreads), 0,
+                   "T=%d H=%d E=%d k=%d", T, H, E, k);
   hipLaunchKernelGGL(route_permute_small_kernel, dim3(nslices), dim3(kSmallThreads), 0, stream,
                      logits, x, T, H, E, k, slice, topk_ids, topk_w, expert_offsets, row_token,
                      row_dest, x_perm);
@@ -431,6 +433,8 @@ hipError_t launch_route(const float* logits, int T, int E, int k,
                         hipStream_t stream) {
   const int chunk = route_chunk_tokens(T, k);
   const int nchunks = route_num_chunks(T, k);
+  MOE_TRACE_LAUNCH("route_kernel", dim3(nchunks), dim3(kRouteThreads), 0,
+                   "T=%d E=%d k=%d chunk=%d hist=%d", T, E, k, chunk, hist ? 1 : 0);
   hipLaunchKernelGGL(route_kernel, dim3(nchunks), dim3(kRouteThreads), 0,
                      stream, logits, T, E, k, chunk, topk_ids, topk_w, hist);
   return hipGetLastError();
@@ -440,6 +444,8 @@ hipError_t launch_hist(const int32_t* topk_ids, int T, int E, int k,
                        int32_t* hist, hipStream_t stream) {
   const int chunk = route_chunk_tokens(T, k);
   const int nchunks = route_num_chunks(T, k);
+  MOE_TRACE_LAUNCH("hist_kernel", dim3(nchunks), dim3(kRouteThreads), 0, "T=%d E=%d k=%d chunk=%d",
+                   T, E, k, chunk);
   hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(kRouteThreads), 0,
                      stream, topk_ids, T, E, k, chunk, hist);
   return hipGetLastError();
@@ -459,6 +465,8 @@ hipError_t launch_permute(const bf16_t* x, const int32_t* topk_ids, int T,
   // that more blocks share the passes
   const int cpb = x_perm ? kPermChunks : 1;
   const int nblocks = (nchunks + cpb - 1) / cpb;
+  MOE_TRACE_LAUNCH("permute_kernel", dim3(nblocks, nslices), dim3(kPermThreads), 0,
+                   "T=%d H=%d E=%d k=%d chunk=%d copy=%d", T, H, E, k, chunk, x_perm ? 1 : 0);
   hipLaunchKernelGGL(permute_kernel, dim3(nblocks, nslices), dim3(kPermThreads),
                      0, stream, x, topk_ids, T, H, E, k, chunk, nchunks, cpb, slice,
                      hist, expert_offsets, row_token, row_dest, x_perm);

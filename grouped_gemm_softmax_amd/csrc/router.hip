@@ -295,6 +295,9 @@ void launch_gemm(const RouterPlan& p, const bf16_t* x, const bf16_t* w, int T, i
                  int k, float* logits_out, float* part, int32_t* ids, float* tw,
                  hipStream_t stream) {
   const dim3 grid((T + 16 * NT - 1) / (16 * NT), (E + 16 * NB - 1) / (16 * NB), p.nslices);
+  MOE_TRACE_LAUNCH("router_gemm_kernel", grid, dim3(kRouterThreads), 0,
+                   "tile=%dx%d T=%d H=%d E=%d k=%d kslices=%d fused=%d", 16 * NT, 16 * NB, T, H,
+                   E, k, p.nslices, p.fused ? 1 : 0);
   hipLaunchKernelGGL((router_gemm_kernel<NB, NT>), grid, dim3(kRouterThreads), 0, stream, x,
                      w, T, H, E, k, p.kslice, p.fused, logits_out, part, ids, tw);
 }
@@ -357,6 +360,8 @@ hipError_t launch_router(const RouterPlan& p, const bf16_t* x, const bf16_t* w, 
   if (err != hipSuccess || p.fused) return err;
   const dim3 grid2((T + kRouterWaves - 1) / kRouterWaves);
   auto fin = [&](auto kernel) {
+    MOE_TRACE_LAUNCH("router_finalize_kernel", grid2, dim3(kRouterThreads), 0,
+                     "T=%d E=%d k=%d kslices=%d", T, E, k, p.nslices);
     hipLaunchKernelGGL(kernel, grid2, dim3(kRouterThreads), 0, stream, part, p.nslices, T, E,
                        k, logits_out, topk_ids, topk_w);
   };

@@ -44,8 +44,18 @@
  *   - Alignment: bf16 tensors and workspaces 16 bytes; fp32 and int32
  *     arrays 4 bytes (MOE_ERR_MISALIGNED otherwise).
  *   - Calls are re-entrant; the only cached state is per-device properties
- *     (and the process-wide setting of the testing hook
- *     moe_set_dispatch_override, which only tests and benchmarks call).
+ *     (and the process-wide settings of moe_set_diagnostics and of the
+ *     testing hook moe_set_dispatch_override).
+ *   - Diagnostics (read from the environment at the library's first use,
+ *     or set with moe_set_diagnostics): MOE_TRACE=1 writes one line per
+ *     kernel launch to stderr (kernel, grid, block, LDS, tile shape and
+ *     schedule of the grouped GEMMs); MOE_DEBUG=1 makes every call that
+ *     takes expert ids from the caller (moe_permute, moe_forward_routed,
+ *     moe_backward, moe_route_backward) check them on the GPU first and
+ *     return MOE_ERR_BAD_IDS if one lies outside [0, E). The check waits for
+ *     its result (the call synchronises its stream, so it cannot be captured
+ *     into a graph); with MOE_DEBUG off, ids outside [0, E) are undefined
+ *     behaviour.
  *   - Results are deterministic: the same inputs give bit-identical outputs.
  */
 #ifndef MOE_H_
@@ -66,7 +76,9 @@ typedef enum {
   MOE_ERR_UNSUPPORTED_SHAPE = -2,   /* outside the size limits above */
   MOE_ERR_MISALIGNED = -3,          /* a pointer below its required alignment */
   MOE_ERR_WORKSPACE_TOO_SMALL = -4, /* ws_bytes below the required size */
-  MOE_ERR_HIP = -5                  /* a HIP runtime call or launch failed */
+  MOE_ERR_HIP = -5,                 /* a HIP runtime call or launch failed */
+  MOE_ERR_BAD_IDS = -6              /* an expert id outside [0, E) (debug check):
+                                       only the check itself was enqueued */
 } moe_status;
 
 /* Optional always-on shared expert, added to every token's output. The
@@ -523,6 +535,24 @@ int moe_backward(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w
  * not selected (the selection itself has no gradient). */
 int moe_route_backward(const int32_t* topk_ids, const float* topk_w, const float* d_topk_w,
                        int T, int E, int k, float* d_logits, void* stream);
+
+/* ---- Diagnostics ----
+ * Not part of the layer's arithmetic; for debugging and tuning (the survey of
+ * the method's tooling: a launch log and an id check on demand).
+ *
+ * moe_set_diagnostics: trace = 1 logs every later kernel launch to stderr
+ * (MOE_TRACE), check_ids = 1 turns on the id check of the calls that take
+ * caller ids (MOE_DEBUG); 0 turns either off and -1 restores the
+ * environment's setting. Process-wide. MOE_OK, or MOE_ERR_INVALID_ARG for
+ * values outside -1..1. */
+int moe_set_diagnostics(int trace, int check_ids);
+
+/* Counts the entries of topk_ids [T,k] (device, int32) outside [0, E) on
+ * `stream`, waits for the count (synchronising the stream) and returns
+ * MOE_OK when there are none, MOE_ERR_BAD_IDS otherwise. Needs no
+ * workspace (a small device array of the library holds the count). Size
+ * limits as for moe_permute; T = 0 is MOE_OK. The check MOE_DEBUG runs. */
+int moe_check_topk_ids(const int32_t* topk_ids, int T, int k, int E, void* stream);
 
 /* ---- Testing hook ----
  * Not part of the layer's contract: for tests and benchmarks that compare

@@ -26,6 +26,10 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 # every operation rounds as written; OpenMP only distributes independent rows.
 GCC_FLAGS = ["-O3", "-march=x86-64-v3", "-ffp-contract=off", "-fno-fast-math",
              "-fopenmp", "-shared", "-fPIC", "-std=c11", "-Wall"]
+# the same arithmetic under AddressSanitizer and UndefinedBehaviorSanitizer
+# (any report aborts); such a build is loaded with gcc's libasan preloaded
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=undefined"]
 
 
 def build(force: bool = True) -> str:
@@ -38,6 +42,13 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def build_sanitized(path: str) -> str:
+    """Compile moe_oracle.c with the sanitizers into `path`."""
+    flags = [f for f in GCC_FLAGS if f != "-O3"] + SANITIZE_FLAGS
+    subprocess.run(["gcc", *flags, "-o", path, _SRC, "-lm"], check=True)
+    return path
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -47,7 +58,8 @@ _I = ctypes.c_int
 def lib():
     global _lib
     if _lib is None:
-        path = build(force=False)
+        # MOE_ORACLE_LIBRARY: another build of the same source (the sanitized one)
+        path = os.environ.get("MOE_ORACLE_LIBRARY") or build(force=False)
         L = ctypes.CDLL(path)
         L.oracle_num_threads.restype = _I
         L.oracle_set_num_threads.argtypes = [_I]

@@ -10,7 +10,7 @@ import pytest
 
 from grouped_gemm_softmax_amd import binding as B
 
-OK, INVALID, SHAPE, MISALIGNED, WS_SMALL, HIP = 0, -1, -2, -3, -4, -5
+OK, INVALID, SHAPE, MISALIGNED, WS_SMALL, HIP, BAD_IDS = 0, -1, -2, -3, -4, -5, -6
 P = ctypes.c_void_p(0x10000)        # 16-byte aligned fake address (never read)
 Q = ctypes.c_void_p(0x10008)        # 8 mod 16: misaligned for bf16 tensors
 NULL = None
@@ -42,8 +42,30 @@ def test_dispatch_override_hook(L):
     assert L.moe_set_dispatch_override(-1, -1) == OK
 
 
+def test_diagnostics_hook(L):
+    assert L.moe_set_diagnostics(2, 0) == INVALID
+    assert L.moe_set_diagnostics(0, -2) == INVALID
+    assert L.moe_set_diagnostics(0, 1) == OK
+    # with the id check on, argument validation still comes first: these
+    # calls fail before anything (the check included) reaches the GPU
+    ws = B.moe_permute_workspace_bytes(100, 8, 2)
+    assert L.moe_permute(P, P, 100, 64, 8, 2, P, P, P, P, P, ws - 1, NULL) == WS_SMALL
+    assert L.moe_route_backward(P, P, P, 4, 8, 9, P, NULL) == SHAPE
+    assert L.moe_check_topk_ids(P, 4, 9, 8, NULL) == SHAPE
+    assert L.moe_set_diagnostics(-1, -1) == OK
+
+
+def test_check_topk_ids_validation(L):
+    assert L.moe_check_topk_ids(P, -1, 2, 8, NULL) == INVALID       # T < 0
+    assert L.moe_check_topk_ids(P, 4, 0, 8, NULL) == INVALID        # k < 1
+    assert L.moe_check_topk_ids(P, 4, 2, 2000, NULL) == SHAPE       # E > 1024
+    assert L.moe_check_topk_ids(NULL, 4, 2, 8, NULL) == INVALID     # null ids
+    assert L.moe_check_topk_ids(ctypes.c_void_p(0x10002), 4, 2, 8, NULL) == MISALIGNED
+    assert L.moe_check_topk_ids(NULL, 0, 2, 8, NULL) == OK          # T = 0: no-op
+
+
 def test_status_strings(L):
-    for s in (OK, INVALID, SHAPE, MISALIGNED, WS_SMALL, HIP):
+    for s in (OK, INVALID, SHAPE, MISALIGNED, WS_SMALL, HIP, BAD_IDS):
         txt = B.moe_status_string(s)
         assert txt and txt != "unknown moe status"
     assert B.moe_status_string(7) == "unknown moe status"
