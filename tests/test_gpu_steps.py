@@ -35,6 +35,13 @@ CASES = {
     # ... and with K a whole number of steps (the ping-pong tiles' main path,
     # fp8's widening one included)
     "large256_whole_k": (synth.small_config("l256", H=256, F=384, E=4, k=2), 500, None),
+    # 96..191 rows per expert on average, Zipf-skewed (128-row tiles): hot
+    # experts with several row tiles beside cold ones far below one
+    "skewed_mid_zipf": (synth.small_config("srz", H=256, F=384, E=16, k=2, logits="zipf"), 1000,
+                        None),
+    # ... with K and N not whole tiles (the K-tail kernels)
+    "skewed_mid_ragged": (synth.small_config("srr", H=200, F=328, E=12, k=2, logits="zipf"),
+                          700, None),
 }
 
 
