@@ -42,11 +42,14 @@ int tile_class(const GemmProblem& p) {
   if (p.rows_hint < 64) return bf16 && p.rows_hint >= 24 ? kLarge128 : kMid;
   if (p.rows_hint >= 192) return kLarge;
   if (p.gated) return kLarge128;
-  // bf16 down projections below 192 rows per group: the 256-row tile would
-  // be half padding or more (Mixtral-shaped T = 256: layer 580 -> 544 us;
-  // T = 512, 115-140 rows per expert: down 318 -> 264 us; DeepSeek-V3-shaped
-  // T = 4096: 2067 -> 2022 us)
-  if (bf16) return kLarge128;
+  // bf16 down projections below 96 rows per group: the 256-row tile would
+  // be three-quarters padding (Mixtral-shaped T = 256: layer 580 -> 544 us).
+  // From 96 rows on, the 256-row tiles stay ahead inside the layer (fp32
+  // K-slices): 128-row tiles there took the Mixtral-shaped layer at T = 512
+  // (115-140 rows per expert) from 0.67 to 0.72 ms and the DeepSeek-V3-shaped
+  // one at T = 4096 from 6.19 to 6.31 ms, although a lone bf16 down
+  // projection without K-slices ran faster on them (318 -> 264 us at T = 512)
+  if (bf16 && p.rows_hint < 96) return kLarge128;
   int64_t items = 0;
   for (int s = 0; s < p.nseg; ++s) {
     const GemmSegment& S = p.seg[s];
