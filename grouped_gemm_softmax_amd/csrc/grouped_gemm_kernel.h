@@ -162,10 +162,10 @@ struct TileCfg {
   // MFMA phase and a memory phase (LDS fragment reads, DMA issue), so one of
   // them always feeds the matrix core (8 waves, no fragment prefetch).
   static constexpr bool PP = PP_;
-  // Ping-pong tiles on 8-bit codes (fp8, mxfp8) widen each stage's weights
-  // once into a double-buffered bf16 tile (packed bf16 layout), instead of
-  // every wave widening the fragments it reads.
-  static constexpr bool WIDEN = PP_ && WBITS_ == 8;
+  // Ping-pong tiles on 8- or 4-bit codes (fp8, mxfp8, mxfp4) widen each
+  // stage's weights once into a double-buffered bf16 tile (packed bf16
+  // layout), instead of every wave widening the fragments it reads.
+  static constexpr bool WIDEN = PP_ && WBITS_ != 16;
   static constexpr int WW_BYTES = WIDEN ? (GATED_ ? 2 : 1) * BK_ * BF_ * 2 : 1;
   static constexpr int NW = WT * WF;
   static constexpr int kThreads = NW * kWave;
@@ -207,8 +207,8 @@ struct TileCfg {
   static_assert((PREFETCH ? STAGES : STAGES - 1) * IPW <= 63, "vector-memory counter range");
   static constexpr bool CHAIN_OK = PREFETCH && STAGES * IPW + STORES <= 63;
   static_assert(!PP || (NW == 8 && !PREFETCH), "ping-pong: two waves per SIMD");
-  static_assert(!WIDEN || (BK == 32 && NMAT * SB * 64 * 2 == kThreads && STAGES >= 5),
-                "widening: one 16-code unit per thread, two steps of look-ahead");
+  static_assert(!WIDEN || (BK == 32 && (NMAT * SB * 64 * 2) % kThreads == 0 && STAGES >= 5),
+                "widening: whole 16-code units per thread, two steps of look-ahead");
 };
 
 // 16-byte chunk swizzles (chunk index within a row), chosen by measuring
@@ -678,34 +678,49 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     return *reinterpret_cast<const bf16x8*>(wbuf + m * (C::BK * C::BF * 2) + (col >> 6) * 4096 +
                                             c * 64 + ((g16 ^ ((c >> 1) & 3)) << 4));
   };
-  // this thread's unit of a stage's 8-bit codes (16 codes: two 8-code chunks
-  // of one column's 32) widened into the bf16 tile; unit = thread index, so
-  // threads 0-255 (waves 0-3) cover one half of the stage, 256-511 the other.
-  // Unit cr = (matrix, sub-block, column) is the column's row of codes at
-  // cr * 32 and of bf16 values at cr * 64. Its logical chunks 2hr and 2hr+1
-  // sit at physical positions 2hr ^ x and (2hr ^ x) ^ 1, x = (c >> 2) & 3:
-  // one aligned 16-byte pair, read with one instruction (one address
-  // register per ring stage instead of two). mxfp8: the 32 codes are one
-  // K-block, whose scale byte is byte cr of the stage's scales.
+  // A stage's codes widened into the bf16 tile, in units of 16 codes (half
+  // of one column's 32); unit u = thread index (+ kThreads), so the first
+  // threads' units cover the first columns. Unit cr = (matrix, sub-block,
+  // column) is the column's row of bf16 values at cr * 64; block scales
+  // (mxfp8, mxfp4): the 32 codes are one K-block, whose scale byte is byte
+  // cr of the stage's scales.
+  //  - 8-bit codes: the column's codes at cr * 32; its logical chunks 2hr
+  //    and 2hr+1 sit at physical positions 2hr ^ x and (2hr ^ x) ^ 1,
+  //    x = (c >> 2) & 3: one aligned 16-byte pair, read with one instruction
+  //    (one address register per ring stage instead of two).
+  //  - 4-bit codes: the column's codes at cr * 16, dword q holding K rows
+  //    8q .. 8q+7; the unit's rows 16hr .. 16hr+15 are dwords 2hr and 2hr+1.
   auto widen = [&](const char* codes, char* wbuf) INL {
-    const int cr = tid >> 1, hr = tid & 1;
-    const int c = cr & 63;
-    const int x = (c >> 2) & 3;
-    const int p0 = (2 * hr) ^ (x & 2);  // even position of the pair
-    const uint4 u = *reinterpret_cast<const uint4*>(codes + cr * 32 + p0 * 8);
-    float scale = 1.f;
-    if constexpr (MX) {
-      const uint32_t e8 = *reinterpret_cast<const uint8_t*>(codes + C::OP_BYTES + cr);
-      scale = __uint_as_float(e8 << 23);
+    constexpr int UNITS = C::NMAT * C::SB * 64 * 2;
+#pragma unroll
+    for (int u0 = 0; u0 < UNITS; u0 += C::kThreads) {
+      const int unit = u0 + tid;
+      const int cr = unit >> 1, hr = unit & 1;
+      const int c = cr & 63;
+      float scale = 1.f;
+      if constexpr (MX) {
+        const uint32_t e8 = *reinterpret_cast<const uint8_t*>(codes + C::OP_BYTES + cr);
+        scale = __uint_as_float(e8 << 23);
+      }
+      const int y = (c >> 1) & 3;             // the bf16 tile's chunk rotation
+      char* const wb = wbuf + cr * 64;
+      if constexpr (C::WBITS == 4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(codes + cr * 16 + hr * 8);
+        const int q0 = 2 * hr;
+        *reinterpret_cast<bf16x8*>(wb + ((q0 ^ y) << 4)) = fp4x8_to_bf16(v.x, scale);
+        *reinterpret_cast<bf16x8*>(wb + (((q0 + 1) ^ y) << 4)) = fp4x8_to_bf16(v.y, scale);
+      } else {
+        const int x = (c >> 2) & 3;
+        const int p0 = (2 * hr) ^ (x & 2);  // even position of the pair
+        const uint4 v = *reinterpret_cast<const uint4*>(codes + cr * 32 + p0 * 8);
+        const int qlo = p0 ^ x, qhi = qlo ^ 1;  // logical chunks of the low and high half
+        const uint2 lo = uint2{v.x, v.y}, hi = uint2{v.z, v.w};
+        *reinterpret_cast<bf16x8*>(wb + ((qlo ^ y) << 4)) =
+            MX ? fp8x8_scaled_to_bf16(lo, scale) : fp8x8_to_bf16(lo);
+        *reinterpret_cast<bf16x8*>(wb + ((qhi ^ y) << 4)) =
+            MX ? fp8x8_scaled_to_bf16(hi, scale) : fp8x8_to_bf16(hi);
+      }
     }
-    const int qlo = p0 ^ x, qhi = qlo ^ 1;  // logical chunks of the low and high half
-    const int y = (c >> 1) & 3;             // the bf16 tile's chunk rotation
-    char* const wb = wbuf + cr * 64;
-    const uint2 lo = uint2{u.x, u.y}, hi = uint2{u.z, u.w};
-    *reinterpret_cast<bf16x8*>(wb + ((qlo ^ y) << 4)) =
-        MX ? fp8x8_scaled_to_bf16(lo, scale) : fp8x8_to_bf16(lo);
-    *reinterpret_cast<bf16x8*>(wb + ((qhi ^ y) << 4)) =
-        MX ? fp8x8_scaled_to_bf16(hi, scale) : fp8x8_to_bf16(hi);
   };
   auto load_frags = [&](const char* buf, Frags& F, int kvalid) INL {
 #pragma unroll
@@ -1426,6 +1441,16 @@ using GateUpMid4 = TileCfg<32, 64, 64, 1, 2, 4, true, true, 4, 4>;
 using DownSmall4 = TileCfg<16, 64, 64, 1, 2, 4, false, true, 4, 4>;
 using GateUpLarge128_4 = TileCfg<128, 128, 64, 4, 2, 4, true, false, 2, 4>;
 using DownLarge128_4 = TileCfg<128, 256, 64, 4, 2, 4, false, false, 2, 4>;
+// ... and, for the 128- and 256-row classes, FP8's widen-once ping-pong
+// schedule on 32-deep stages. 4-bit codes fill a 1 KB DMA instruction per
+// wave only with twice the columns: 128 rows x 256 columns (gated, each
+// matrix) or 512 columns (down), waves 2 along tokens x 4 along columns
+// (the same 64 x 64 per wave, accumulators and fragments as the 256 x 128
+// tiles), two widening units per thread. The down tile's 512 columns differ
+// from the bf16 tile's 256; the K-split plan (made for 256) is valid for
+// any tile.
+using GateUpLarge_4W = TileCfg<128, 256, 32, 2, 4, 5, true, false, 1, 4, true>;
+using DownLarge_4W = TileCfg<128, 512, 32, 2, 4, 5, false, false, 1, 4, true>;
 // MXFP8 weights (E4M3 codes with a scale byte per 32 K-values of a column):
 // the fp8 tiles' shapes with the mxfp4 tiles' scale handling. The 128- and
 // 256-row tiles widen each 32-deep stage once, as for fp8; a stage's 32
