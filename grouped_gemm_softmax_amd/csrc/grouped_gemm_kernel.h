@@ -1426,10 +1426,17 @@ using DownSmall8 = TileCfg<32, 64, 64, 1, 4, 4, false, true, 1, 8>;
 // MXFP4 weights: a quarter of the bf16 weight bytes per stage plus the
 // scale bytes, 64-deep stages wherever a 32-deep one would not give every
 // wave a whole number of 1 KB DMA instructions. The decode tiles widen every
-// weight fragment with VALU work, so they run at up to four waves per SIMD
-// (registers bounded for that, 4-stage rings of ~7 KB: five workgroups per
-// CU); with 8-stage rings and one wave per SIMD the Mixtral-shaped layer at
-// 32 tokens took 17 % longer. The down tile has 16 rows (half the
+// weight fragment with VALU work, so they run as many waves per SIMD as
+// their LDS allows: the gate/up tiles' 4-stage rings (27 and 35 KB a
+// workgroup of two waves) fit five and four workgroups per CU (2-3 and 2
+// waves per SIMD), the down tile's (19 KB) eight (4 waves per SIMD). Their
+// registers are bounded for four waves per SIMD all the same (so that the
+// register file is never the limit; the compiler reports the LDS-bound
+// occupancy below that target): bounding the gate/up tiles for the two
+// waves their LDS allows let them take 160-200 registers and measured no
+// faster (DeepSeek-V3-shaped T = 128 gate/up 0.61 -> 0.62 ms, Mixtral-
+// shaped T = 128 layer 0.323 -> 0.327 ms). With 8-stage rings and one wave
+// per SIMD the Mixtral-shaped layer at 32 tokens took 17 % longer. The down tile has 16 rows (half the
 // activation bytes of a 32-row one at decode; the K-split plan, made for
 // 32-row tiles, stays valid for any tile). The 128-row tiles keep
 // one fragment set (prefetching fragments of 64-deep stages spill) and read
