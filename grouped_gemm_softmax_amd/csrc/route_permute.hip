@@ -290,13 +290,18 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   }
 }
 
-// Small batches (all T*k <= kMaxChunkAssign assignments in one routing
+// Small batches (all T*k <= kMaxChunkAssign / 2 assignments in one routing
 // chunk): routing and the permutation in one launch. Every block routes all
 // T tokens into LDS (block 0 also writes the routing result, the offsets
 // and the row maps), scans the expert counts, ranks the assignments in
 // (t, j) order and copies its own column slice of the assigned rows of x.
 // 16 waves, so that one pass routes up to 16 tokens (E > 32) to 128 (E <= 8);
-// E <= kSmallMaxExperts.
+// E <= kSmallMaxExperts. The rank of assignment i (its position among the
+// earlier assignments of its expert) comes from the wave holding it: the
+// lanes with the same expert are found with one ballot per bit of the id,
+// the earlier lanes among them counted, and the first wave's per-expert
+// counts added for the second (instead of each lane scanning all earlier
+// assignments in LDS, up to 127 dependent reads).
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallMaxExperts = 256;
 __global__ __launch_bounds__(kSmallThreads) void route_permute_small_kernel(
@@ -310,12 +315,16 @@ __global__ __launch_bounds__(kSmallThreads) void route_permute_small_kernel(
   __shared__ float s_w[kMaxChunkAssign];
   __shared__ int s_dest[kMaxChunkAssign];
   __shared__ int s_wave_total[kSmallThreads / kWave];
+  __shared__ int s_first_wave[kSmallMaxExperts];  // wave 0's assignments per expert
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const bool lead = blockIdx.x == 0;
   const int n = T * k;
-  for (int e = tid; e < E; e += kSmallThreads) s_count[e] = 0;
+  for (int e = tid; e < E; e += kSmallThreads) {
+    s_count[e] = 0;
+    s_first_wave[e] = 0;
+  }
   __syncthreads();
   route_range<kSmallThreads, 4>(logits, T, E, k, 0, T, s_ids, s_w, s_count);
   __syncthreads();
@@ -337,29 +346,48 @@ __global__ __launch_bounds__(kSmallThreads) void route_permute_small_kernel(
   const int incl = wave_inclusive_scan(my_sum);
   if (lane == kWave - 1) s_wave_total[wave] = incl;
   __syncthreads();
-  int run = incl - my_sum;
-  for (int w = 0; w < wave; ++w) run += s_wave_total[w];
+  // (only the waves holding experts: E <= 256 of them, so waves 0-3)
+  if (wave * kWave * EPT < E) {
+    int run = incl - my_sum;
+    for (int w = 0; w < wave; ++w) run += s_wave_total[w];
 #pragma unroll
-  for (int i = 0; i < EPT; ++i) {
-    const int e = tid * EPT + i;
-    if (e < E) {
-      s_off[e] = run;
-      if (lead) expert_offsets[e] = run;
+    for (int i = 0; i < EPT; ++i) {
+      const int e = tid * EPT + i;
+      if (e < E) {
+        s_off[e] = run;
+        if (lead) expert_offsets[e] = run;
+      }
+      run += cnt[i];
     }
-    run += cnt[i];
   }
   if (lead && tid == 0) expert_offsets[E] = n;
   __syncthreads();
   // stable rank of each assignment among the earlier ones with its expert
-  for (int i = tid; i < n; i += kSmallThreads) {
-    const int e = min(max(s_ids[i], 0), E - 1);
-    int rank = 0;
-    for (int i2 = 0; i2 < i; ++i2) rank += (s_ids[i2] == e);
+  // (n <= 128: the assignments are lanes of waves 0 and 1)
+  const bool valid = wave < 2 && tid < n;
+  const int e = valid ? min(max(s_ids[tid], 0), E - 1) : 0;
+  int rank = 0;
+  if (wave < 2) {
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {  // E <= 256: ids have 8 bits
+      const bool bit = (e >> b) & 1;
+      const uint64_t set = __ballot(valid && bit);
+      same &= bit ? set : ~set;
+    }
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+    rank = __popcll(same & below);
+    // the last lane of each expert in wave 0 records the wave's count
+    if (wave == 0 && valid && (same >> lane) == 1ull) s_first_wave[e] = rank + 1;
+  }
+  __syncthreads();
+  if (valid) {
+    if (wave == 1) rank += s_first_wave[e];
     const int p = min(s_off[e] + rank, n - 1);
-    s_dest[i] = p;
+    s_dest[tid] = p;
     if (lead) {
-      row_dest[i] = p;
-      row_token[p] = i / k;
+      row_dest[tid] = p;
+      row_token[p] = tid / k;
     }
   }
   __syncthreads();

@@ -24,6 +24,11 @@ CASES = {
     "one_expert": (synth.small_config("oe", H=64, F=64, E=1, k=1), 40, None),
     "k_equals_E": (synth.small_config("ke", H=64, F=48, E=5, k=5), 23, None),
     "k16": (synth.small_config("k16", H=64, F=40, E=32, k=16), 17, None),
+    # 120 assignments over 200 experts with Zipf-skewed logits: the forward
+    # routes and permutes them in one launch (two waves of assignments, hot
+    # experts in both)
+    "small_batch_many_experts": (synth.small_config("sbm", H=64, F=64, E=200, k=4,
+                                                    logits="zipf"), 30, None),
     "all_equal_logits": (synth.small_config("eq", H=72, F=56, E=12, k=3), 45, "equal"),
     "ties_int": (synth.small_config("ti", H=64, F=64, E=16, k=4), 80, "ties_int"),
     "signed_zero": (synth.small_config("sz", H=64, F=64, E=10, k=3), 50, "signed_zero"),
