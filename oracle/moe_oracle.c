@@ -24,6 +24,9 @@
  *             K-values of a column (OCP MX); likewise (mxfp4 section).
  *   mxfp8   : weights as E4M3 codes with one power-of-two scale per 32
  *             K-values of a column (OCP MX); likewise (mxfp8 section).
+ *   backward: the chain rule through the routed layer for a fixed routing,
+ *             through the softmax over the k selected logits, and through
+ *             the shared expert and its gate (backward section).
  *
  * Sources (restated, not quoted):
  *   - "Triton-MoE-Dispatch-Kernel erreicht 131 % von Megablocks" (lumeric.app),
@@ -771,6 +774,115 @@ int oracle_backward(const uint16_t* x, const int32_t* ids, const float* w, int64
 done:
   free(offsets); free(row_token); free(row_dest); free(row_slot);
   free(hr); free(dGr); free(dUr); free(dyr); free(dxr);
+  return rc;
+}
+
+/* Backward of the shared expert (the always-on FFN of the DeepSeek-V3- and
+ * Qwen2-MoE-shaped layers; the pages give no backward, so this is the chain
+ * rule through the forward's shared term). With out[t] += s_t y_sh[t],
+ * s_t = 1 without gate logits, else the logistic sigmoid of g_t (as
+ * oracle_shared_gate), and y_sh[t] = (silu(x_t W_sg) * (x_t W_su)) W_sd:
+ *   d g_t   = <dout[t], y_sh[t]> s_t (1 - s_t)        (with gate logits only)
+ *   dy      = s_t dout[t]
+ *   dh, dG, dU as for a routed row (oracle_backward)
+ *   dx[t]   = dG W_sg^T + dU W_su^T                     (the shared part only)
+ *   dW_sg = sum_t x_t^T dG_t, dW_su likewise with dU, dW_sd = sum_t h_t^T dy_t
+ *   (t ascending).
+ * x, weights and dout bf16, gate logits fp32, everything else fp64.
+ * dx [T,H], dg [T] (written only with gate logits), dwsg, dwsu [H,Fs],
+ * dwsd [Fs,H]. */
+int oracle_shared_backward(const uint16_t* x, int64_t T, int H, int Fs, const uint16_t* wsg,
+                           const uint16_t* wsu, const uint16_t* wsd, const float* gate_logits,
+                           const uint16_t* dout, double* dx, double* dg, double* dwsg,
+                           double* dwsu, double* dwsd) {
+  if (T < 0 || H < 1 || Fs < 1) return ORC_ERR_ARG;
+  int rc = ORC_ERR_NOMEM;
+  double* s = (double*)malloc(sizeof(double) * (size_t)(T + 1));
+  double* hr = (double*)malloc(sizeof(double) * (size_t)(T * Fs + 1));
+  double* dGr = (double*)malloc(sizeof(double) * (size_t)(T * Fs + 1));
+  double* dUr = (double*)malloc(sizeof(double) * (size_t)(T * Fs + 1));
+  double* dyr = (double*)malloc(sizeof(double) * (size_t)(T * H + 1));
+  if (!s || !hr || !dGr || !dUr || !dyr) goto done;
+  oracle_shared_gate(gate_logits, T, s);
+  rc = ORC_OK;
+#pragma omp parallel
+  {
+    double* G = (double*)malloc(sizeof(double) * (size_t)Fs * 2);
+    double* y = (double*)malloc(sizeof(double) * (size_t)H);
+    double* dh = (double*)malloc(sizeof(double) * (size_t)Fs);
+    if (!G || !y || !dh) {
+#pragma omp atomic write
+      rc = ORC_ERR_NOMEM;
+    } else {
+      double* U = G + Fs;
+#pragma omp for schedule(static)
+      for (int64_t t = 0; t < T; ++t) {
+        const uint16_t* xt = x + t * H;
+        double* h = hr + t * Fs;
+        gateup_row(xt, H, Fs, wsg, wsu, h, G, U);
+        down_row(h, Fs, H, wsd, y);
+        if (gate_logits) {
+          double d = 0.0;
+          for (int c = 0; c < H; ++c) d += bf16_to_f64(dout[t * H + c]) * y[c];
+          dg[t] = d * s[t] * (1.0 - s[t]);
+        }
+        double* dy = dyr + t * H;
+        for (int c = 0; c < H; ++c) dy[c] = s[t] * bf16_to_f64(dout[t * H + c]);
+        for (int f = 0; f < Fs; ++f) {
+          double a = 0.0;
+          const uint16_t* rd = wsd + (int64_t)f * H;
+          for (int c = 0; c < H; ++c) a += dy[c] * bf16_to_f64(rd[c]);
+          dh[f] = a;
+        }
+        double* dG = dGr + t * Fs;
+        double* dU = dUr + t * Fs;
+        for (int f = 0; f < Fs; ++f) {
+          const double z = G[f], sg = 1.0 / (1.0 + exp(-z));
+          dG[f] = dh[f] * U[f] * sg * (1.0 + z * (1.0 - sg));
+          dU[f] = dh[f] * silu(z);
+        }
+        for (int i = 0; i < H; ++i) {
+          double a = 0.0;
+          const uint16_t* rg = wsg + (int64_t)i * Fs;
+          const uint16_t* ru = wsu + (int64_t)i * Fs;
+          for (int f = 0; f < Fs; ++f)
+            a += dG[f] * bf16_to_f64(rg[f]) + dU[f] * bf16_to_f64(ru[f]);
+          dx[t * H + i] = a;
+        }
+      }
+    }
+    free(G); free(y); free(dh);
+  }
+  if (rc) goto done;
+  /* weight gradients over the tokens in ascending order (one output row of
+   * each matrix per iteration, so the rows can run in parallel) */
+#pragma omp parallel for schedule(static)
+  for (int i = 0; i < H; ++i) {
+    double* gg = dwsg + (int64_t)i * Fs;
+    double* gu = dwsu + (int64_t)i * Fs;
+    for (int f = 0; f < Fs; ++f) gg[f] = 0.0, gu[f] = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      const double xv = bf16_to_f64(x[t * H + i]);
+      const double* dG = dGr + t * Fs;
+      const double* dU = dUr + t * Fs;
+      for (int f = 0; f < Fs; ++f) {
+        gg[f] += xv * dG[f];
+        gu[f] += xv * dU[f];
+      }
+    }
+  }
+#pragma omp parallel for schedule(static)
+  for (int f = 0; f < Fs; ++f) {
+    double* gd = dwsd + (int64_t)f * H;
+    for (int c = 0; c < H; ++c) gd[c] = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      const double hv = hr[t * Fs + f];
+      const double* dy = dyr + t * H;
+      for (int c = 0; c < H; ++c) gd[c] += hv * dy[c];
+    }
+  }
+done:
+  free(s); free(hr); free(dGr); free(dUr); free(dyr);
   return rc;
 }
 

@@ -99,6 +99,8 @@ def lib():
                                              _I64, _P, _P, _P])
         L.oracle_backward.argtypes = [_P, _P, _P, _I64, _I, _I, _I, _I, _P, _P, _P, _P,
                                       _P, _P, _P, _P, _P]
+        L.oracle_shared_backward.argtypes = [_P, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P,
+                                             _P, _P, _P]
         L.oracle_backward_tokens.argtypes = [_P, _P, _P, _I64, _I, _I, _I, _I, _P, _P, _P,
                                              _P, _P, _I64, _P, _P]
         L.oracle_backward_wcols.argtypes = [_P, _P, _P, _I64, _I, _I, _I, _I, _P, _P, _P,
@@ -258,6 +260,27 @@ def backward(x, ids, w, wg, wu, wd, dout):
     _check(lib().oracle_backward(_p(x), _p(ids), _p(w), T, H, F, E, k, _p(wg), _p(wu), _p(wd),
                                  _p(dout), _p(r["dx"]), _p(r["dw"]), _p(r["dwg"]), _p(r["dwu"]),
                                  _p(r["dwd"])), "backward")
+    return r
+
+
+def shared_backward(x, wsg, wsu, wsd, gate_logits, dout):
+    """Backward of the shared expert's term s_t * y_sh[t] (s_t = 1 without
+    gate logits, else the sigmoid of gate_logits [T] fp32); x, weights
+    (W_sg, W_su [H,Fs], W_sd [Fs,H]) and dout bf16. Returns dict(dx [T,H]
+    (the shared expert's part of the input gradient), dg [T] (the gate-logit
+    gradient, zeros without gate logits), dwsg, dwsu [H,Fs], dwsd [Fs,H]),
+    float64."""
+    x, dout = _c(x, np.uint16), _c(dout, np.uint16)
+    wsg, wsu, wsd = _c(wsg, np.uint16), _c(wsu, np.uint16), _c(wsd, np.uint16)
+    T, H = x.shape
+    Fs = wsg.shape[1]
+    g = None if gate_logits is None else _c(gate_logits, np.float32)
+    r = dict(dx=np.empty((T, H)), dg=np.zeros(T), dwsg=np.empty((H, Fs)),
+             dwsu=np.empty((H, Fs)), dwsd=np.empty((Fs, H)))
+    _check(lib().oracle_shared_backward(_p(x), T, H, Fs, _p(wsg), _p(wsu), _p(wsd),
+                                        None if g is None else _p(g), _p(dout), _p(r["dx"]),
+                                        _p(r["dg"]), _p(r["dwsg"]), _p(r["dwsu"]),
+                                        _p(r["dwsd"])), "shared_backward")
     return r
 
 

@@ -142,3 +142,72 @@ def test_sampled_backward_equals_full(orc):
         assert np.array_equal(cu[s], g["dwu"][e, :, f])
         assert np.array_equal(cd[s], g["dwd"][e, f, :])
     assert not cg[3].any() and not cd[3].any()      # expert 4: no rows
+
+
+# ---- the shared expert's backward -------------------------------------------
+
+def dense_shared(x, g, wsg, wsu, wsd):
+    """s_t * (silu(x_t Wsg) * (x_t Wsu)) Wsd, float64; s_t = sigmoid(g_t), or 1
+    when g is None."""
+    a = x @ wsg
+    y = (a / (1 + np.exp(-a)) * (x @ wsu)) @ wsd
+    s = np.ones(x.shape[0]) if g is None else 1.0 / (1.0 + np.exp(-g))
+    return s[:, None] * y
+
+
+def make_shared(seed, T=6, H=12, Fs=14):
+    rng = np.random.default_rng(seed)
+    x = bf16(rng.standard_normal((T, H)))
+    wsg = bf16(rng.standard_normal((H, Fs)) * 0.3)
+    wsu = bf16(rng.standard_normal((H, Fs)) * 0.3)
+    wsd = bf16(rng.standard_normal((Fs, H)) * 0.3)
+    g = rng.standard_normal(T).astype(np.float32)
+    dout = bf16(rng.standard_normal((T, H)))
+    return x, wsg, wsu, wsd, g, dout
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_shared_backward_matches_finite_differences(orc, gated):
+    x, wsg, wsu, wsd, g, dout = make_shared(11)
+    g = g if gated else None
+    r = orc.shared_backward(x, wsg, wsu, wsd, g, dout)
+    X, WG, WU, WD, R = f64(x), f64(wsg), f64(wsu), f64(wsd), f64(dout)
+    G = None if g is None else g.astype(np.float64)
+    loss = lambda X, G, WG, WU, WD: float((dense_shared(X, G, WG, WU, WD) * R).sum())
+    args = [X, G, WG, WU, WD]
+    rng = np.random.default_rng(7)
+    for name, pos in (("dx", 0), ("dg", 1), ("dwsg", 2), ("dwsu", 3), ("dwsd", 4)):
+        a = args[pos]
+        if a is None:
+            assert not r["dg"].any()
+            continue
+        for _ in range(10):
+            idx = tuple(rng.integers(0, s) for s in a.shape)
+            eps = 1e-5 * max(1.0, abs(a[idx]))
+            plus = [None if v is None else v.copy() for v in args]
+            minus = [None if v is None else v.copy() for v in args]
+            plus[pos][idx] += eps
+            minus[pos][idx] -= eps
+            fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+            assert abs(r[name][idx] - fd) <= 1e-6 * max(1.0, abs(fd)), (name, idx, r[name][idx], fd)
+
+
+def test_shared_backward_is_one_expert_layer(orc):
+    """The shared term is a one-expert, top-1 layer with routing weight s_t:
+    with s_t = 1 (no gate logits) and with s_t = 1/2 (gate logits 0, so s_t,
+    1 - s_t and their product are exact) the shared backward equals the
+    routed backward on those weights bit for bit, and the gate gradient is
+    the routing-weight gradient times s (1 - s) = 1/4."""
+    x, wsg, wsu, wsd, _, dout = make_shared(12)
+    T = x.shape[0]
+    ids = np.zeros((T, 1), np.int32)
+    for g, w in ((None, 1.0), (np.zeros(T, np.float32), 0.5)):
+        r = orc.shared_backward(x, wsg, wsu, wsd, g, dout)
+        ref = orc.backward(x, ids, np.full((T, 1), w, np.float32), wsg[None], wsu[None],
+                           wsd[None], dout)
+        assert np.array_equal(r["dx"], ref["dx"])
+        assert np.array_equal(r["dwsg"], ref["dwg"][0])
+        assert np.array_equal(r["dwsu"], ref["dwu"][0])
+        assert np.array_equal(r["dwsd"], ref["dwd"][0])
+        if g is not None:
+            assert np.array_equal(r["dg"], ref["dw"][:, 0] / 4)
