@@ -230,33 +230,36 @@ def router_table(args, torch, B, synth):
 
 
 def backward_line(args, torch, B, synth):
-    """moe_backward of the routed layer at one batch size: HIP events around
-    `steps` calls on the launch stream. Its work is eight A*H*F products
-    (2*A*H*F FLOPs each, A = T*k): the recomputed gate and up products, dh
-    (on the unweighted dout), the two dx products and the three weight
-    gradients."""
+    """moe_backward of the layer at one batch size (with its shared expert,
+    through moe_backward_shared, where the config has one): HIP events
+    around `steps` calls on the launch stream. Its work is eight A*H*F
+    products (2*A*H*F FLOPs each, A = T*k): the recomputed gate and up
+    products, dh (on the unweighted dout), the two dx products and the three
+    weight gradients; the shared expert adds eight T*H*Fs products."""
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = synth.CONFIGS[args.config]
     T, H, F, E, k = args.T, cfg.H, cfg.F, cfg.E, cfg.k
     stream = torch.cuda.current_stream()
-    layer = synth.make_layer(cfg.name, T, seed=args.seed, device=dev, with_shared=False)
+    Fs = cfg.Fs or 0
+    layer = synth.make_layer(cfg.name, T, seed=args.seed, device=dev, with_shared=Fs > 0)
+    shared = layer.shared if Fs > 0 else None
     ids, w = B.moe_route(layer.logits, k, stream=stream)
     g = torch.Generator(device=dev).manual_seed(args.seed + 1)
     dout = torch.randn((T, H), generator=g, device=dev).to(torch.bfloat16)
-    ws = torch.empty(B.moe_backward_workspace_bytes(T, H, F, E, k), dtype=torch.uint8,
+    ws = torch.empty(B.moe_backward_shared_workspace_bytes(T, H, F, E, k, Fs), dtype=torch.uint8,
                      device=dev)
-    fws = torch.empty(B.moe_forward_workspace_bytes(T, H, F, E, k, 0), dtype=torch.uint8,
+    fws = torch.empty(B.moe_forward_workspace_bytes(T, H, F, E, k, Fs), dtype=torch.uint8,
                       device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
     def bwd():
-        B.moe_backward(layer.x, ids, w, layer.w_gate, layer.w_up, layer.w_down, dout, ws=ws,
-                       stream=stream)
+        B.moe_backward(layer.x, ids, w, layer.w_gate, layer.w_up, layer.w_down, dout,
+                       shared=shared, ws=ws, stream=stream)
 
     def fwd():
         B.moe_forward_routed(layer.x, ids, w, layer.w_gate, layer.w_up, layer.w_down,
-                             out=out, ws=fws, stream=stream)
+                             shared=shared, out=out, ws=fws, stream=stream)
 
     def timed(fn, n, warm):
         for _ in range(warm):
@@ -273,8 +276,8 @@ def backward_line(args, torch, B, synth):
     ms_b = timed(bwd, args.steps, args.warmup)
     ms_f = timed(fwd, args.steps, args.warmup)
     A = T * k
-    flops = 8 * 2 * A * H * F
-    print(json.dumps({"backward": cfg.name, "T": T, "H": H, "F": F, "E": E, "k": k,
+    flops = 8 * 2 * A * H * F + 8 * 2 * T * H * Fs
+    print(json.dumps({"backward": cfg.name, "T": T, "H": H, "F": F, "E": E, "k": k, "Fs": Fs,
                       "ms": round(ms_b, 4), "TFLOPs": round(flops / ms_b / 1e9, 1),
                       "mfma_frac": round(flops / ms_b / 1e9 / PEAK_BF16_TFLOPS, 4),
                       "forward_rowmajor_ms": round(ms_f, 4), "alg_flops": flops,

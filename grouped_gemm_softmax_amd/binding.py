@@ -40,6 +40,11 @@ class SharedExpert(ctypes.Structure):
                 ("gate_logits", ctypes.c_void_p)]
 
 
+class SharedExpertGrads(ctypes.Structure):
+    _fields_ = [("dw_gate", ctypes.c_void_p), ("dw_up", ctypes.c_void_p),
+                ("dw_down", ctypes.c_void_p), ("d_gate_logits", ctypes.c_void_p)]
+
+
 class SharedExpertFp8(ctypes.Structure):
     _fields_ = [("w_gate", ctypes.c_void_p), ("s_gate", ctypes.c_void_p),
                 ("w_up", ctypes.c_void_p), ("s_up", ctypes.c_void_p),
@@ -115,6 +120,10 @@ _SIGNATURES = {
     "moe_backward": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                           _P, _P, _SZ, _P]),
     "moe_route_backward": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
+    "moe_backward_shared_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "moe_backward_shared": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P,
+                                 ctypes.POINTER(SharedExpert), _P, _P, _P, _P, _P, _P,
+                                 ctypes.POINTER(SharedExpertGrads), _P, _SZ, _P]),
     "moe_set_dispatch_override": (_I, [_I, _I]),
     "moe_set_diagnostics": (_I, [_I, _I]),
     "moe_check_topk_ids": (_I, [_P, _I, _I, _I, _P]),
@@ -688,11 +697,20 @@ def moe_backward_workspace_bytes(T, H, F, E, k) -> int:
 
 
 @_on_stream
-def moe_backward(x, topk_ids, topk_w, w_gate, w_up, w_down, dout, ws=None, stream=None):
-    """Gradients of the routed layer (row-major bf16 weights) for the routing
+def moe_backward_shared_workspace_bytes(T, H, F, E, k, Fs) -> int:
+    return lib().moe_backward_shared_workspace_bytes(T, H, F, E, k, Fs)
+
+
+def moe_backward(x, topk_ids, topk_w, w_gate, w_up, w_down, dout, shared: Optional[dict] = None,
+                 ws=None, stream=None):
+    """Gradients of the layer (row-major bf16 weights) for the routing
     (topk_ids int32 [T,k], topk_w fp32 [T,k]) and the output gradient dout
     [T,H] bf16. Returns dict(dx [T,H] bf16, d_topk_w [T,k] fp32, dw_gate,
-    dw_up [E,H,F] fp32, dw_down [E,F,H] fp32)."""
+    dw_up [E,H,F] fp32, dw_down [E,F,H] fp32). With `shared` (dict(w_gate,
+    w_up [H,Fs], w_down [Fs,H] bf16, gate_logits [T] fp32 or None), as for
+    moe_forward) dx includes the shared expert's part and the dict adds
+    dw_gate_sh, dw_up_sh [H,Fs], dw_down_sh [Fs,H] and d_gate_logits [T]
+    (None without gate logits), all fp32."""
     for n, t, dt in (("x", x, torch.bfloat16), ("topk_ids", topk_ids, torch.int32),
                      ("topk_w", topk_w, torch.float32), ("w_gate", w_gate, torch.bfloat16),
                      ("w_up", w_up, torch.bfloat16), ("w_down", w_down, torch.bfloat16),
@@ -707,14 +725,40 @@ def moe_backward(x, topk_ids, topk_w, w_gate, w_up, w_down, dout, ws=None, strea
              dw_gate=torch.empty((E, H, F), dtype=torch.float32, device=dev),
              dw_up=torch.empty((E, H, F), dtype=torch.float32, device=dev),
              dw_down=torch.empty((E, F, H), dtype=torch.float32, device=dev))
+    if shared is None:
+        if ws is None:
+            ws = torch.empty(max(moe_backward_workspace_bytes(T, H, F, E, k), 16),
+                             dtype=torch.uint8, device=dev)
+        _check(lib().moe_backward(_ptr(x), _ptr(topk_ids), _ptr(topk_w), T, H, F, E, k,
+                                  _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(dout),
+                                  _ptr(g["dx"]), _ptr(g["d_topk_w"]), _ptr(g["dw_gate"]),
+                                  _ptr(g["dw_up"]), _ptr(g["dw_down"]), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "moe_backward")
+        return g
+    sw = {n: shared[n] for n in ("w_gate", "w_up", "w_down")}
+    for n, t in sw.items():
+        _need(t, torch.bfloat16, "shared " + n)
+    gl = shared.get("gate_logits")
+    if gl is not None:
+        _need(gl, torch.float32, "shared gate_logits")
+    Fs = sw["w_gate"].shape[1]
+    g.update(dw_gate_sh=torch.empty((H, Fs), dtype=torch.float32, device=dev),
+             dw_up_sh=torch.empty((H, Fs), dtype=torch.float32, device=dev),
+             dw_down_sh=torch.empty((Fs, H), dtype=torch.float32, device=dev),
+             d_gate_logits=None if gl is None else torch.empty(T, dtype=torch.float32,
+                                                               device=dev))
+    st = SharedExpert(_ptr(sw["w_gate"]), _ptr(sw["w_up"]), _ptr(sw["w_down"]), Fs, _ptr(gl))
+    sg = SharedExpertGrads(_ptr(g["dw_gate_sh"]), _ptr(g["dw_up_sh"]), _ptr(g["dw_down_sh"]),
+                           _ptr(g["d_gate_logits"]))
     if ws is None:
-        ws = torch.empty(max(moe_backward_workspace_bytes(T, H, F, E, k), 16),
+        ws = torch.empty(max(moe_backward_shared_workspace_bytes(T, H, F, E, k, Fs), 16),
                          dtype=torch.uint8, device=dev)
-    _check(lib().moe_backward(_ptr(x), _ptr(topk_ids), _ptr(topk_w), T, H, F, E, k,
-                              _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(dout),
-                              _ptr(g["dx"]), _ptr(g["d_topk_w"]), _ptr(g["dw_gate"]),
-                              _ptr(g["dw_up"]), _ptr(g["dw_down"]), _ptr(ws), ws.numel(),
-                              _stream(stream)), "moe_backward")
+    _check(lib().moe_backward_shared(_ptr(x), _ptr(topk_ids), _ptr(topk_w), T, H, F, E, k,
+                                     _ptr(w_gate), _ptr(w_up), _ptr(w_down), ctypes.byref(st),
+                                     _ptr(dout), _ptr(g["dx"]), _ptr(g["d_topk_w"]),
+                                     _ptr(g["dw_gate"]), _ptr(g["dw_up"]), _ptr(g["dw_down"]),
+                                     ctypes.byref(sg), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_backward_shared")
     return g
 
 

@@ -831,15 +831,18 @@ int moe_forward_routed(const moe_bf16* x, const int32_t* topk_ids, const float* 
 // Workspace of moe_backward (each piece 256-byte aligned from ws):
 // [hist | offsets | row_token | row_dest | x_perm | h | G | U | dy |
 //  dout_perm | dG | dU | wrow (fp32) | part (fp32 [A][ceil(F/16)]) |
-//  dx parts (fp32, 2 slices)].
+//  dx parts (fp32, 2 slices)], and for the shared expert (Fs > 0) its own
+// [h | G | U | dy | dG | dU (T rows) | wrow | part | dx parts | offsets].
 struct BackwardLayout {
-  size_t hist, offsets, row_token, row_dest, x_perm, h, g, u, dy, dop, dg, du, wrow, part, dxp,
-      total;
+  size_t hist, offsets, row_token, row_dest, x_perm, h, g, u, dy, dop, dg, du, wrow, part, dxp;
+  size_t hsh, gsh, ush, dysh, dgsh, dush, wsh, psh, dxsh, offsh;
+  size_t total;
 };
 
-static BackwardLayout backward_layout(int T, int H, int F, int E, int k) {
+static BackwardLayout backward_layout(int T, int H, int F, int E, int k, int Fs) {
   BackwardLayout L;
   const size_t A = static_cast<size_t>(T) * k;
+  const size_t Ts = Fs > 0 ? static_cast<size_t>(T) : 0;  // rows of the shared expert
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
   L.hist = take(static_cast<size_t>(moe::route_num_chunks(T, k)) * E * 4);
@@ -857,6 +860,16 @@ static BackwardLayout backward_layout(int T, int H, int F, int E, int k) {
   L.wrow = take(A * 4);
   L.part = take(A * ((static_cast<size_t>(F) + 15) / 16) * 4);
   L.dxp = take(2 * A * H * 4);
+  L.hsh = take(Ts * Fs * 2);
+  L.gsh = take(Ts * Fs * 2);
+  L.ush = take(Ts * Fs * 2);
+  L.dysh = take(Ts * H * 2);
+  L.dgsh = take(Ts * Fs * 2);
+  L.dush = take(Ts * Fs * 2);
+  L.wsh = take(Ts * 4);
+  L.psh = take(Ts * ((static_cast<size_t>(Fs > 0 ? Fs : 0) + 15) / 16) * 4);
+  L.dxsh = take(2 * Ts * H * 4);
+  L.offsh = take(Fs > 0 ? 2 * 4 : 0);
   L.total = o;
   return L;
 }
@@ -864,20 +877,41 @@ static BackwardLayout backward_layout(int T, int H, int F, int E, int k) {
 size_t moe_backward_workspace_bytes(int T, int H, int F, int E, int k) {
   if (check_dims(T, E, k) != MOE_OK || check_width(H) != MOE_OK || check_width(F) != MOE_OK)
     return 0;
-  return backward_layout(T, H, F, E, k).total;
+  return backward_layout(T, H, F, E, k, 0).total;
 }
 
-int moe_backward(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w, int T, int H,
-                 int F, int E, int k, const moe_bf16* w_gate, const moe_bf16* w_up,
-                 const moe_bf16* w_down, const moe_bf16* dout, moe_bf16* dx, float* d_topk_w,
-                 float* dw_gate, float* dw_up, float* dw_down, void* ws, size_t ws_bytes,
-                 void* stream) {
+size_t moe_backward_shared_workspace_bytes(int T, int H, int F, int E, int k, int Fs) {
+  if (check_dims(T, E, k) != MOE_OK || check_width(H) != MOE_OK || check_width(F) != MOE_OK ||
+      Fs < 0 || (Fs > 0 && check_width(Fs) != MOE_OK))
+    return 0;
+  return backward_layout(T, H, F, E, k, Fs).total;
+}
+
+// The routed layer's backward, and the shared expert's when `sh` is given.
+static int backward_impl(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
+                         int H, int F, int E, int k, const moe_bf16* w_gate,
+                         const moe_bf16* w_up, const moe_bf16* w_down,
+                         const moe_shared_expert* sh, moe_shared_expert_grads* sg,
+                         const moe_bf16* dout, moe_bf16* dx, float* d_topk_w, float* dw_gate,
+                         float* dw_up, float* dw_down, void* ws, size_t ws_bytes,
+                         void* stream) {
   MOE_TRY(check_dims(T, E, k));
   MOE_TRY(check_width(H));
   MOE_TRY(check_width(F));
   const int64_t A = static_cast<int64_t>(T) * k;
   MOE_TRY(check_elems(A, H > F ? H : F));
   if (static_cast<int64_t>(H) * F >= kIndexLimit) return MOE_ERR_UNSUPPORTED_SHAPE;
+  const int Fs = sh ? sh->Fs : 0;
+  const float* gate = sh ? sh->gate_logits : nullptr;
+  if (sh) {
+    MOE_TRY(check_width(Fs));
+    MOE_TRY(check_elems(T, H > Fs ? H : Fs));
+    if (static_cast<int64_t>(H) * Fs >= kIndexLimit) return MOE_ERR_UNSUPPORTED_SHAPE;
+    if (!sg) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(need_word(sg->dw_gate));
+    MOE_TRY(need_word(sg->dw_up));
+    MOE_TRY(need_word(sg->dw_down));
+  }
   MOE_TRY(need_word(dw_gate));
   MOE_TRY(need_word(dw_up));
   MOE_TRY(need_word(dw_down));
@@ -891,40 +925,54 @@ int moe_backward(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w
     MOE_TRY(need_bf16(dout));
     MOE_TRY(need_bf16(dx));
     MOE_TRY(need_word(d_topk_w));
+    if (sh) {
+      MOE_TRY(need_bf16(sh->w_gate));
+      MOE_TRY(need_bf16(sh->w_up));
+      MOE_TRY(need_bf16(sh->w_down));
+      if (gate) {
+        MOE_TRY(need_word(gate));
+        MOE_TRY(need_word(sg->d_gate_logits));
+      }
+    }
     MOE_TRY(need_bf16(ws));
   }
-  const BackwardLayout L = backward_layout(T, H, F, E, k);
+  const BackwardLayout L = backward_layout(T, H, F, E, k, Fs);
   if (T > 0 && ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (T > 0) MOE_TRY(debug_check_ids(topk_ids, A, E, stream));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  using moe::launch_kgrouped_gemm;
   if (T == 0) {
     // no tokens: every weight gradient is zero
-    using moe::launch_kgrouped_gemm;
     MOE_TRY(hip_status(launch_kgrouped_gemm(nullptr, nullptr, nullptr, E, H, F, dw_gate, s)));
     MOE_TRY(hip_status(launch_kgrouped_gemm(nullptr, nullptr, nullptr, E, H, F, dw_up, s)));
-    return hip_status(launch_kgrouped_gemm(nullptr, nullptr, nullptr, E, F, H, dw_down, s));
+    MOE_TRY(hip_status(launch_kgrouped_gemm(nullptr, nullptr, nullptr, E, F, H, dw_down, s)));
+    if (sh) {
+      MOE_TRY(hip_status(launch_kgrouped_gemm(nullptr, nullptr, nullptr, 1, H, Fs, sg->dw_gate, s)));
+      MOE_TRY(hip_status(launch_kgrouped_gemm(nullptr, nullptr, nullptr, 1, H, Fs, sg->dw_up, s)));
+      MOE_TRY(hip_status(launch_kgrouped_gemm(nullptr, nullptr, nullptr, 1, Fs, H, sg->dw_down, s)));
+    }
+    return MOE_OK;
   }
   char* base = static_cast<char*>(ws);
+  auto bf = [&](size_t off) { return reinterpret_cast<bf16_t*>(base + off); };
+  auto fp = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
   int32_t* hist = reinterpret_cast<int32_t*>(base + L.hist);
   int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
   int32_t* row_token = reinterpret_cast<int32_t*>(base + L.row_token);
   int32_t* row_dest = reinterpret_cast<int32_t*>(base + L.row_dest);
-  bf16_t* x_perm = reinterpret_cast<bf16_t*>(base + L.x_perm);
-  bf16_t* h = reinterpret_cast<bf16_t*>(base + L.h);
-  bf16_t* g = reinterpret_cast<bf16_t*>(base + L.g);
-  bf16_t* u = reinterpret_cast<bf16_t*>(base + L.u);
-  bf16_t* dy = reinterpret_cast<bf16_t*>(base + L.dy);
-  bf16_t* dop = reinterpret_cast<bf16_t*>(base + L.dop);
-  bf16_t* dg = reinterpret_cast<bf16_t*>(base + L.dg);
-  bf16_t* du = reinterpret_cast<bf16_t*>(base + L.du);
-  float* wrow = reinterpret_cast<float*>(base + L.wrow);
-  float* part = reinterpret_cast<float*>(base + L.part);
-  float* dxp = reinterpret_cast<float*>(base + L.dxp);
+  bf16_t *x_perm = bf(L.x_perm), *h = bf(L.h), *g = bf(L.g), *u = bf(L.u), *dy = bf(L.dy);
+  bf16_t *dop = bf(L.dop), *dg = bf(L.dg), *du = bf(L.du);
+  float *wrow = fp(L.wrow), *part = fp(L.part), *dxp = fp(L.dxp);
+  bf16_t *hsh = bf(L.hsh), *gsh = bf(L.gsh), *ush = bf(L.ush), *dysh = bf(L.dysh);
+  bf16_t *dgsh = bf(L.dgsh), *dush = bf(L.dush);
+  float *wsh = fp(L.wsh), *psh = fp(L.psh), *dxsh = fp(L.dxsh);
+  int32_t* offsh = reinterpret_cast<int32_t*>(base + L.offsh);
   const int M = static_cast<int>(A);
 
   // recompute: permutation (x_perm is kept for the weight
   // gradients) and gate/up storing G and U beside h (the down projection is
-  // not needed: the routing-weight gradient comes from dh's epilogue)
+  // not needed: the routing-weight gradient comes from dh's epilogue); the
+  // shared expert is a second segment over x
   MOE_TRY(hip_status(moe::launch_hist(topk_ids, T, E, k, hist, s)));
   MOE_TRY(hip_status(moe::launch_permute(x, topk_ids, T, H, E, k, hist, offsets, row_token,
                                          row_dest, x_perm, s)));
@@ -933,30 +981,53 @@ int moe_backward(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w
   g1.epi = moe::kStoreGUH;
   g1.seg[0].out2 = g;
   g1.seg[0].out3 = u;
+  if (sh) {
+    g1.seg[1] = segment(x, nullptr, sh->w_gate, sh->w_up, hsh, T, 1, H, Fs, kRowMajor, nullptr,
+                        nullptr);
+    g1.seg[1].out2 = gsh;
+    g1.seg[1].out3 = ush;
+    g1.nseg = 2;
+  }
   MOE_TRY(hip_status(moe::launch_grouped_gemm(g1, s)));
-  // per row: dy = w dout (for dW_down), dout itself and w
+  // per row: dy = w dout (for dW_down), dout itself and w; the shared
+  // expert's rows are the tokens, with s_t for w
   MOE_TRY(hip_status(
       moe::launch_backward_prep(dout, row_dest, topk_w, T, H, k, dy, dop, wrow, s)));
+  if (sh) MOE_TRY(hip_status(moe::launch_shared_prep(dout, gate, T, H, dysh, wsh, offsh, s)));
   // g = dout W_down^T per row (W_down [F][H] is the [N][K] operand), with
   // the SwiGLU backward in the epilogue: dG, dU from dh = w g, and the
   // partial sums of <h, g> for the routing-weight gradient
-  moe::GemmProblem g3{};
-  g3.seg[0] = segment(dop, offsets, w_down, nullptr, dg, M, E, H, F, moe::kWeightsTransposed,
-                      nullptr, nullptr);
-  g3.seg[0].aux0 = g;
-  g3.seg[0].aux1 = u;
-  g3.seg[0].aux2 = h;
-  g3.seg[0].wrow = wrow;
-  g3.seg[0].part = part;
-  g3.seg[0].out2 = du;
-  g3.nseg = 1;
-  g3.gated = false;
-  g3.rows_hint = M / E;
-  g3.epi = moe::kSwigluBwd;
-  MOE_TRY(hip_status(moe::launch_grouped_gemm(g3, s)));
+  auto dh_problem = [&](const bf16_t* act, const int32_t* offs, const bf16_t* wd, bf16_t* dG,
+                        int rows, int groups, int n, const bf16_t* G_, const bf16_t* U_,
+                        const bf16_t* h_, const float* wr, float* pt, bf16_t* dU) {
+    moe::GemmProblem q{};
+    q.seg[0] = segment(act, offs, wd, nullptr, dG, rows, groups, H, n, moe::kWeightsTransposed,
+                       nullptr, nullptr);
+    q.seg[0].aux0 = G_;
+    q.seg[0].aux1 = U_;
+    q.seg[0].aux2 = h_;
+    q.seg[0].wrow = wr;
+    q.seg[0].part = pt;
+    q.seg[0].out2 = dU;
+    q.nseg = 1;
+    q.gated = false;
+    q.rows_hint = rows / groups;
+    q.epi = moe::kSwigluBwd;
+    return q;
+  };
+  MOE_TRY(hip_status(moe::launch_grouped_gemm(
+      dh_problem(dop, offsets, w_down, dg, M, E, F, g, u, h, wrow, part, du), s)));
   MOE_TRY(hip_status(moe::launch_topk_w_grad(part, (F + 15) / 16, row_dest, T, k, d_topk_w, s)));
+  if (sh) {
+    MOE_TRY(hip_status(moe::launch_grouped_gemm(
+        dh_problem(dout, nullptr, sh->w_down, dgsh, T, 1, Fs, gsh, ush, hsh, wsh, psh, dush), s)));
+    if (gate)
+      MOE_TRY(hip_status(
+          moe::launch_shared_gate_grad(psh, (Fs + 15) / 16, gate, T, sg->d_gate_logits, s)));
+  }
   // dx: dG W_gate^T and dU W_up^T per row (fp32 slices), summed over the
   // token's k rows and the two slices by the combine with unit weights
+  // (plus the shared expert's two slices per token)
   for (int slice = 0; slice < 2; ++slice) {
     moe::GemmProblem g4{};
     g4.seg[0] = segment(slice ? du : dg, offsets, slice ? w_up : w_gate, nullptr,
@@ -967,13 +1038,52 @@ int moe_backward(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w
     g4.out_f32 = true;
     g4.rows_hint = M / E;
     MOE_TRY(hip_status(moe::launch_grouped_gemm(g4, s)));
+    if (sh) {
+      moe::GemmProblem g5{};
+      g5.seg[0] = segment(slice ? dush : dgsh, nullptr, slice ? sh->w_up : sh->w_gate, nullptr,
+                          dxsh + static_cast<int64_t>(slice) * T * H, T, 1, Fs, H,
+                          moe::kWeightsTransposed, nullptr, nullptr);
+      g5.nseg = 1;
+      g5.gated = false;
+      g5.out_f32 = true;
+      g5.rows_hint = T;
+      MOE_TRY(hip_status(moe::launch_grouped_gemm(g5, s)));
+    }
   }
   MOE_TRY(hip_status(moe::launch_combine(dxp, true, 2, static_cast<int64_t>(M) * H, row_dest,
-                                         nullptr, T, H, k, nullptr, 1, 0, nullptr, dx, s)));
-  // weight gradients over each expert's rows
-  MOE_TRY(hip_status(moe::launch_kgrouped_gemm(x_perm, dg, offsets, E, H, F, dw_gate, s)));
-  MOE_TRY(hip_status(moe::launch_kgrouped_gemm(x_perm, du, offsets, E, H, F, dw_up, s)));
-  return hip_status(moe::launch_kgrouped_gemm(h, dy, offsets, E, F, H, dw_down, s));
+                                         nullptr, T, H, k, sh ? dxsh : nullptr, 2,
+                                         static_cast<int64_t>(T) * H, nullptr, dx, s)));
+  // weight gradients over each expert's rows (the shared expert's: all tokens)
+  MOE_TRY(hip_status(launch_kgrouped_gemm(x_perm, dg, offsets, E, H, F, dw_gate, s)));
+  MOE_TRY(hip_status(launch_kgrouped_gemm(x_perm, du, offsets, E, H, F, dw_up, s)));
+  MOE_TRY(hip_status(launch_kgrouped_gemm(h, dy, offsets, E, F, H, dw_down, s)));
+  if (sh) {
+    MOE_TRY(hip_status(launch_kgrouped_gemm(x, dgsh, offsh, 1, H, Fs, sg->dw_gate, s)));
+    MOE_TRY(hip_status(launch_kgrouped_gemm(x, dush, offsh, 1, H, Fs, sg->dw_up, s)));
+    MOE_TRY(hip_status(launch_kgrouped_gemm(hsh, dysh, offsh, 1, Fs, H, sg->dw_down, s)));
+  }
+  return MOE_OK;
+}
+
+int moe_backward(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w, int T, int H,
+                 int F, int E, int k, const moe_bf16* w_gate, const moe_bf16* w_up,
+                 const moe_bf16* w_down, const moe_bf16* dout, moe_bf16* dx, float* d_topk_w,
+                 float* dw_gate, float* dw_up, float* dw_down, void* ws, size_t ws_bytes,
+                 void* stream) {
+  return backward_impl(x, topk_ids, topk_w, T, H, F, E, k, w_gate, w_up, w_down, nullptr,
+                       nullptr, dout, dx, d_topk_w, dw_gate, dw_up, dw_down, ws, ws_bytes,
+                       stream);
+}
+
+int moe_backward_shared(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
+                        int H, int F, int E, int k, const moe_bf16* w_gate, const moe_bf16* w_up,
+                        const moe_bf16* w_down, const moe_shared_expert* shared,
+                        const moe_bf16* dout, moe_bf16* dx, float* d_topk_w, float* dw_gate,
+                        float* dw_up, float* dw_down, moe_shared_expert_grads* shared_grads,
+                        void* ws, size_t ws_bytes, void* stream) {
+  return backward_impl(x, topk_ids, topk_w, T, H, F, E, k, w_gate, w_up, w_down, shared,
+                       shared_grads, dout, dx, d_topk_w, dw_gate, dw_up, dw_down, ws, ws_bytes,
+                       stream);
 }
 
 int moe_route_backward(const int32_t* topk_ids, const float* topk_w, const float* d_topk_w,

@@ -59,6 +59,60 @@ __global__ __launch_bounds__(kPrepThreads) void backward_prep_kernel(
   }
 }
 
+// --- the shared expert's preparation ------------------------------------------
+// Per token (one block): s = 1, or the logistic sigmoid of the gate logit
+// (the forward's combine computes it the same way), wrow[t] = s and
+// dy[t] = bf16(s dout[t]); block 0 also writes the single group's offsets.
+__global__ __launch_bounds__(kPrepThreads) void shared_prep_kernel(
+    const bf16_t* __restrict__ dout, const float* __restrict__ gate_logits, int T, int H,
+    bf16_t* __restrict__ dy, float* __restrict__ wrow, int32_t* __restrict__ offsets) {
+  const int t = blockIdx.x;
+  const float s = gate_logits ? 1.0f / (1.0f + expf(-gate_logits[t])) : 1.0f;
+  if (threadIdx.x == 0) {
+    wrow[t] = s;
+    if (t == 0) {
+      offsets[0] = 0;
+      offsets[1] = T;
+    }
+  }
+  for (int c = threadIdx.x * 8; c < H; c += kPrepThreads * 8) {
+    const uint4 q = *reinterpret_cast<const uint4*>(dout + static_cast<int64_t>(t) * H + c);
+    const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+    float d[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      d[2 * i] = bf16_to_f32(static_cast<bf16_t>(u[i] & 0xffffu));
+      d[2 * i + 1] = bf16_to_f32(static_cast<bf16_t>(u[i] >> 16));
+    }
+    uint4 o;
+    o.x = pack_bf16x2(s * d[0], s * d[1]);
+    o.y = pack_bf16x2(s * d[2], s * d[3]);
+    o.z = pack_bf16x2(s * d[4], s * d[5]);
+    o.w = pack_bf16x2(s * d[6], s * d[7]);
+    *reinterpret_cast<uint4*>(dy + static_cast<int64_t>(t) * H + c) = o;
+  }
+}
+
+// Gate-logit gradient of the shared expert: <dout[t], y_sh[t]> s (1 - s),
+// the inner product being the sum of the dh product's per-fragment partial
+// sums of row t (in order, then a fixed butterfly), one wave per token.
+__global__ __launch_bounds__(256) void shared_gate_grad_kernel(
+    const float* __restrict__ part, int nq, const float* __restrict__ gate_logits, int T,
+    float* __restrict__ d_gate) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (t >= T) return;  // whole waves
+  const float* r = part + t * nq;
+  float acc = 0.f;
+  for (int q = lane; q < nq; q += kWave) acc += r[q];
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, kWave);
+  if (lane == 0) {
+    const float s = 1.0f / (1.0f + expf(-gate_logits[t]));
+    d_gate[t] = acc * s * (1.0f - s);
+  }
+}
+
 // --- routing-weight gradient --------------------------------------------------
 // d_topk_w[t,j] = <dout[t], y[p]> = <h[p], g[p]> (g = dout W_down^T), the sum
 // of the dh GEMM's per-fragment partial sums of row p. One wave per
@@ -278,6 +332,27 @@ hipError_t launch_backward_prep(const bf16_t* dout, const int32_t* row_dest,
                    k);
   hipLaunchKernelGGL(backward_prep_kernel, dim3(T), dim3(kPrepThreads), 0, stream, dout,
                      row_dest, topk_w, T, H, k, dy, dout_perm, wrow);
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_prep(const bf16_t* dout, const float* gate_logits, int T, int H,
+                              bf16_t* dy, float* wrow, int32_t* offsets, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  MOE_TRACE_LAUNCH("shared_prep_kernel", dim3(T), dim3(kPrepThreads), 0, "T=%d H=%d gated=%d", T,
+                   H, gate_logits ? 1 : 0);
+  hipLaunchKernelGGL(shared_prep_kernel, dim3(T), dim3(kPrepThreads), 0, stream, dout,
+                     gate_logits, T, H, dy, wrow, offsets);
+  return hipGetLastError();
+}
+
+hipError_t launch_shared_gate_grad(const float* part, int nq, const float* gate_logits, int T,
+                                   float* d_gate, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>((T + 3) / 4);
+  MOE_TRACE_LAUNCH("shared_gate_grad_kernel", dim3(blocks), dim3(256), 0, "T=%d partials=%d", T,
+                   nq);
+  hipLaunchKernelGGL(shared_gate_grad_kernel, dim3(blocks), dim3(256), 0, stream, part, nq,
+                     gate_logits, T, d_gate);
   return hipGetLastError();
 }
 

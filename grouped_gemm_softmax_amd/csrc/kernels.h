@@ -195,6 +195,15 @@ hipError_t launch_backward_prep(const bf16_t* dout, const int32_t* row_dest,
                                 bf16_t* dout_perm, float* wrow, hipStream_t stream);
 // d_topk_w[t,j] = sum over q of part[p][q], p = row_dest[t,j], in a fixed order
 // (part [A][nq]: the fragments' partial sums of h g).
+// The shared expert's term s_t y_sh[t] (s_t = 1, or the sigmoid of the
+// gate logit): wrow[t] = s_t, dy[t] = bf16(s_t dout[t]) (for its W_down
+// gradient) and offsets = {0, T} (its single group).
+hipError_t launch_shared_prep(const bf16_t* dout, const float* gate_logits, int T, int H,
+                              bf16_t* dy, float* wrow, int32_t* offsets, hipStream_t stream);
+// d_gate[t] = (sum of part[t][0..nq) in order) s_t (1 - s_t): the
+// gate-logit gradient from the shared dh product's per-fragment <h, g> sums.
+hipError_t launch_shared_gate_grad(const float* part, int nq, const float* gate_logits, int T,
+                                   float* d_gate, hipStream_t stream);
 hipError_t launch_topk_w_grad(const float* part, int nq, const int32_t* row_dest, int T, int k,
                               float* d_topk_w, hipStream_t stream);
 // d_logits [T,E] of the softmax over the k selected logits.

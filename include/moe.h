@@ -509,8 +509,9 @@ int moe_forward_mxfp8(const moe_bf16* x, const float* logits, int T, int H, int 
  * from moe_forward); the product with W_down^T is taken on the unweighted
  * dout, so d_topk_w = <h, g> needs no recomputed y and no rounding of dy
  * reaches dh. h, G, U, dy (for dW_down only), dG and dU are rounded to bf16
- * between the steps; every product accumulates in fp32. Routed experts
- * only (no shared expert); weights in the row-major layout of moe_forward. */
+ * between the steps; every product accumulates in fp32. moe_backward
+ * covers the routed experts; moe_backward_shared adds the shared expert
+ * (below). Weights in the row-major layout of moe_forward. */
 
 /* Bytes of the workspace moe_backward needs (0 for invalid sizes):
  * about T*k*(14 H + 10.25 F) bytes. */
@@ -535,6 +536,44 @@ int moe_backward(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w
  * not selected (the selection itself has no gradient). */
 int moe_route_backward(const int32_t* topk_ids, const float* topk_w, const float* d_topk_w,
                        int T, int E, int k, float* d_logits, void* stream);
+
+/* The shared expert's gradients (a HOST struct of DEVICE pointers): dw_gate,
+ * dw_up [H,Fs] and dw_down [Fs,H] fp32 (every element written; zero when
+ * T = 0), and d_gate_logits [T] fp32, the gradient of the gate logits
+ * (written only when the expert has gate logits; may be NULL otherwise). */
+typedef struct {
+  float* dw_gate;
+  float* dw_up;
+  float* dw_down;
+  float* d_gate_logits;
+} moe_shared_expert_grads;
+
+/* Bytes of the workspace moe_backward_shared needs (0 for invalid sizes):
+ * moe_backward's plus about T*(10 H + 10.25 Fs) bytes for the shared
+ * expert. Fs = 0 gives moe_backward's. */
+size_t moe_backward_shared_workspace_bytes(int T, int H, int F, int E, int k, int Fs);
+
+/* moe_backward with the shared expert of moe_forward (its term
+ * s_t * y_sh[t] of the output, s_t = 1 without gate logits, else the
+ * logistic sigmoid of the token's gate logit). Not on the pages (the
+ * DeepSeek-V3 and Qwen2-MoE layer shapes of the workload definitions carry
+ * the shared expert); the chain rule through that term, as the routed
+ * rows': the shared expert is one more group over all T tokens with s_t for
+ * its routing weight, so
+ *   dx[t]        += dG_sh W_sg^T + dU_sh W_su^T   (dx is the layer's whole
+ *                                                 input gradient)
+ *   d_gate_logits[t] = <dout[t], y_sh[t]> s_t (1 - s_t)
+ *   dW_sg = x^T dG_sh, dW_su = x^T dU_sh, dW_sd = h_sh^T bf16(s dout)
+ * with the same roundings as the routed rows. shared == NULL: exactly
+ * moe_backward (shared_grads is not read). Otherwise shared_grads is
+ * required and its pointers are validated like the routed gradients'.
+ * Deterministic. */
+int moe_backward_shared(const moe_bf16* x, const int32_t* topk_ids, const float* topk_w, int T,
+                        int H, int F, int E, int k, const moe_bf16* w_gate, const moe_bf16* w_up,
+                        const moe_bf16* w_down, const moe_shared_expert* shared,
+                        const moe_bf16* dout, moe_bf16* dx, float* d_topk_w, float* dw_gate,
+                        float* dw_up, float* dw_down, moe_shared_expert_grads* shared_grads,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* ---- Diagnostics ----
  * Not part of the layer's arithmetic; for debugging and tuning (the survey of

@@ -438,3 +438,32 @@ def test_packed_calls_validation(L):
                                 P, 1 << 30, NULL) == SHAPE
     assert L.moe_forward_packed(NULL, NULL, 0, 64, 96, 8, 2, NULL, NULL, NULL, None, NULL,
                                 NULL, NULL, NULL, 0, NULL) == OK
+
+
+def test_backward_workspace_bytes():
+    for args in [(64, 128, 96, 8, 2), (4096, 7168, 2048, 256, 8), (1, 64, 48, 3, 1)]:
+        base = B.moe_backward_workspace_bytes(*args)
+        assert base > 0 and base % 256 == 0
+        assert B.moe_backward_shared_workspace_bytes(*args, 0) == base
+        assert B.moe_backward_shared_workspace_bytes(*args, 256) > base
+    assert B.moe_backward_shared_workspace_bytes(64, 128, 96, 8, 2, 60) == 0   # Fs % 8 != 0
+    assert B.moe_backward_shared_workspace_bytes(64, 128, 96, 8, 2, -8) == 0
+
+
+def test_backward_shared_validation(L):
+    ws = B.moe_backward_shared_workspace_bytes(10, 64, 48, 4, 2, 32)
+    sh = B.SharedExpert(0x10000, 0x10000, 0x10000, 32, None)
+    sg = B.SharedExpertGrads(0x10000, 0x10000, 0x10000, None)
+    args = lambda shared, grads, T=10, ws_bytes=ws: (
+        P, P, P, T, 64, 48, 4, 2, P, P, P, shared, P, P, P, P, P, P, grads, P, ws_bytes, NULL)
+    assert L.moe_backward_shared(*args(ctypes.byref(sh), None)) == INVALID        # no grads
+    assert L.moe_backward_shared(*args(ctypes.byref(sh), ctypes.byref(sg), ws_bytes=ws - 1)) == WS_SMALL
+    bad = B.SharedExpert(0x10000, 0x10000, 0x10000, 36, None)                        # Fs % 8
+    assert L.moe_backward_shared(*args(ctypes.byref(bad), ctypes.byref(sg))) == SHAPE
+    mis = B.SharedExpertGrads(0x10002, 0x10000, 0x10000, None)                       # dw_gate
+    assert L.moe_backward_shared(*args(ctypes.byref(sh), ctypes.byref(mis))) == MISALIGNED
+    gated = B.SharedExpert(0x10000, 0x10000, 0x10000, 32, 0x10000)                   # needs d_gate
+    assert L.moe_backward_shared(*args(ctypes.byref(gated), ctypes.byref(sg))) == INVALID
+    # without the shared expert it validates as moe_backward
+    assert L.moe_backward_shared(*args(None, None, ws_bytes=B.moe_backward_workspace_bytes(
+        10, 64, 48, 4, 2) - 1)) == WS_SMALL

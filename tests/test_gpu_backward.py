@@ -29,6 +29,7 @@ import torch
 from grouped_gemm_softmax_amd import binding as B
 from grouped_gemm_softmax_amd import synth
 from helpers import bf16_to_f64, gpu_bf16_f64, host_layer, rel_l2, say, to_dev
+from test_gpu_fp8 import to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -204,3 +205,78 @@ def test_route_backward(orc, T, E, k):
     mask = np.zeros((T, E), bool)
     np.put_along_axis(mask, ids.astype(np.int64), True, 1)
     assert not got[~mask].any()
+
+
+# ---- with the shared expert (moe_backward_shared) ---------------------------
+
+SHARED_CASES = {
+    # Qwen2-MoE-like: a sigmoid gate on a shared expert 4x wider than F
+    "gated_wide_shared": (synth.small_config("gw", H=128, F=96, E=8, k=2), 70, 384, True),
+    # DeepSeek-V3-like: an always-on shared expert (s = 1), ragged sizes
+    "ungated_ragged": (synth.small_config("ur", H=200, F=136, E=6, k=2), 90, 264, False),
+    # many rows per expert: the 128- and 256-row tiles for both segments
+    "gated_large_tiles": (synth.small_config("gl", H=256, F=128, E=4, k=2), 520, 256, True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SHARED_CASES))
+def test_backward_shared(orc, name):
+    """The shared expert's term is a one-expert layer over all tokens with
+    routing weight s_t: its bounds are grad_bounds of that layer (s_t as the
+    weight), and dx, the sum of the routed and the shared parts, is bounded
+    by the root-sum-square of both."""
+    cfg, T, Fs, gated = SHARED_CASES[name]
+    layer = synth.make_layer(cfg.name, T, seed=4, device="cuda", cfg=cfg, with_shared=False)
+    d, _ = host_layer(layer)
+    rng = np.random.default_rng(T + Fs)
+    mk = lambda *s: synth.u16(torch.from_numpy(rng.standard_normal(s) * 0.05).to(torch.bfloat16))
+    wsg, wsu, wsd = mk(cfg.H, Fs), mk(cfg.H, Fs), mk(Fs, cfg.H)
+    gl = rng.standard_normal(T).astype(np.float32) if gated else None
+    ids, w = orc.route(d["logits"], cfg.k)
+    w32 = w.astype(np.float32)
+    dout = dout_bf16(T, cfg.H, 4)
+    dout_u = synth.u16(dout)
+    say("moe_backward_shared", name, T, Fs, gated)
+    shared = dict(w_gate=to_dev_bf16(wsg), w_up=to_dev_bf16(wsu), w_down=to_dev_bf16(wsd),
+                  gate_logits=None if gl is None else to_dev(gl))
+    g = B.moe_backward(layer.x, to_dev(ids), to_dev(w32), layer.w_gate, layer.w_up,
+                       layer.w_down, dout.cuda(), shared=shared)
+    g0 = B.moe_backward(layer.x, to_dev(ids), to_dev(w32), layer.w_gate, layer.w_up,
+                        layer.w_down, dout.cuda())
+    torch.cuda.synchronize()
+    ref = orc.backward(d["x"], ids, w32, d["wg"], d["wu"], d["wd"], dout_u)
+    rs = orc.shared_backward(d["x"], wsg, wsu, wsd, gl, dout_u)
+    b = grad_bounds(orc, d["x"], ids, w32, d["wg"], d["wu"], d["wd"], dout_u)
+    s = np.ones(T) if gl is None else 1.0 / (1.0 + np.exp(-gl.astype(np.float64)))
+    bs = grad_bounds(orc, d["x"], np.zeros((T, 1), np.int32), s.astype(np.float32)[:, None],
+                     wsg[None], wsu[None], wsd[None], dout_u)
+    check_grad(gpu_bf16_f64(g["dx"]), ref["dx"] + rs["dx"], np.sqrt(b["dx"] ** 2 + bs["dx"] ** 2),
+               f"dx[{name}]")
+    check_grad(g["dw_gate_sh"].cpu().numpy(), rs["dwsg"], bs["dwg"][0], f"dw_gate_sh[{name}]")
+    check_grad(g["dw_up_sh"].cpu().numpy(), rs["dwsu"], bs["dwu"][0], f"dw_up_sh[{name}]")
+    check_grad(g["dw_down_sh"].cpu().numpy(), rs["dwsd"], bs["dwd"][0], f"dw_down_sh[{name}]")
+    if gated:
+        check_grad(g["d_gate_logits"].cpu().numpy(), rs["dg"], bs["dw"][:, 0] * s * (1 - s),
+                   f"d_gate_logits[{name}]")
+    else:
+        assert g["d_gate_logits"] is None
+    # the routed gradients do not change with the shared expert beside them
+    for n in ("d_topk_w", "dw_gate", "dw_up", "dw_down"):
+        assert torch.equal(g[n], g0[n]), n
+
+
+def test_backward_shared_no_tokens():
+    cfg = synth.small_config("zs", H=64, F=48, E=3, k=2)
+    layer = synth.make_layer(cfg.name, 0, seed=0, device="cuda", cfg=cfg, with_shared=False)
+    say("moe_backward_shared T=0")
+    ids = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    w = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    dout = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    sh = dict(w_gate=torch.ones((64, 32), dtype=torch.bfloat16, device="cuda"),
+              w_up=torch.ones((64, 32), dtype=torch.bfloat16, device="cuda"),
+              w_down=torch.ones((32, 64), dtype=torch.bfloat16, device="cuda"),
+              gate_logits=torch.empty(0, dtype=torch.float32, device="cuda"))
+    g = B.moe_backward(layer.x, ids, w, layer.w_gate, layer.w_up, layer.w_down, dout, shared=sh)
+    torch.cuda.synchronize()
+    for n in ("dw_gate", "dw_up", "dw_down", "dw_gate_sh", "dw_up_sh", "dw_down_sh"):
+        assert g[n].numel() > 0 and not g[n].any(), n
