@@ -661,6 +661,7 @@ static int forward_impl(const moe_bf16* x, const float* logits, const int32_t* i
   if (gather) {
     g1.seg[0].act = x;
     g1.seg[0].gather = row_token;
+    g1.seg[0].gather_rows = T;
   }
   if (logits && !gather && moe::route_permute_fits_one_launch(T, E, k)) {
     // 1+2. small batch: routing and the permutation in one launch

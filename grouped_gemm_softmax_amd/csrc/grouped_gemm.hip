@@ -501,6 +501,8 @@ bool use_rs_gateup(const GemmProblem& p) {
 }
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
+  for (int s = 0; s < p.nseg; ++s)  // a row map needs the rows it may name
+    if (p.seg[s].gather && p.seg[s].gather_rows < 1) return hipErrorInvalidValue;
   // the backward epilogue exists in the transposed-weight bf16 kernels only
   if (p.epi == kSwigluBwd &&
       (p.gated || p.out_f32 || p.seg[0].packed != kWeightsTransposed || p.nseg != 1))

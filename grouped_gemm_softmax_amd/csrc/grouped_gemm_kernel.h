@@ -498,7 +498,8 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
           const int r = (j - C::W_INSTR) * RPI_X + lane / (C::BK / 8);
           const int kc = swz_x<C::BK>(r, lane % (C::BK / 8)) * 8;
           const int rr = min(r, it.rows_valid - 1);
-          const int row = S.gather ? S.gather[it.row_base + rr] : rr;
+          const int row = S.gather ? min(max(S.gather[it.row_base + rr], 0), S.gather_rows - 1)
+                                   : rr;
           it.voff[i] = static_cast<uint32_t>(row * it.K + kc) * 2u;
         }
       }

@@ -83,9 +83,11 @@ struct GemmSegment {
   const void* scale0 = nullptr;
   const void* scale1 = nullptr;
   // Optional row map: activation row of row p is gather[p] (`act` is then
-  // the un-permuted [*, K] tensor). Only for the tile classes without item
-  // chaining (see grouped_gemm_gathers).
+  // the un-permuted [gather_rows, K] tensor; map entries are clamped to its
+  // rows, so a corrupted map cannot make a load leave it). Only for the tile
+  // classes without item chaining (see grouped_gemm_gathers).
   const int32_t* gather = nullptr;
+  int gather_rows = 0;
   int ksplit = 1;          // K-slices (> 1 needs fp32 output; the consumer sums them)
   // Epilogues of the training backward (GemmProblem::epi): kStoreGUH also
   // writes G to out2 and U to out3. kSwigluBwd takes the product as
