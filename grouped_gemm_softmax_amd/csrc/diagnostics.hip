@@ -11,8 +11,8 @@
 // take expert ids from the caller (moe_permute, moe_forward_routed,
 // moe_backward, moe_route_backward) first count the ids outside [0, E) on
 // the GPU, wait for the count and return MOE_ERR_BAD_IDS, with nothing more
-// enqueued, if it is not zero. The count lives in a small device array of
-// the library (one per GPU), so the check allocates nothing.
+// enqueued, if it is not zero. The count lives in a device integer of the
+// library (one per GPU), so the check allocates nothing.
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -25,7 +25,7 @@
 // Per-GPU counter of the id check (its device address is looked up once per
 // device with hipGetSymbolAddress; host code never uses the name itself as
 // an address).
-static __device__ __align__(256) int id_check_count[64];
+static __device__ __align__(256) int id_check_count;
 
 namespace moe {
 namespace {

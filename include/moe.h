@@ -589,7 +589,7 @@ int moe_set_diagnostics(int trace, int check_ids);
 /* Counts the entries of topk_ids [T,k] (device, int32) outside [0, E) on
  * `stream`, waits for the count (synchronising the stream) and returns
  * MOE_OK when there are none, MOE_ERR_BAD_IDS otherwise. Needs no
- * workspace (a small device array of the library holds the count). Size
+ * workspace (a device integer of the library holds the count). Size
  * limits as for moe_permute; T = 0 is MOE_OK. The check MOE_DEBUG runs. */
 int moe_check_topk_ids(const int32_t* topk_ids, int T, int k, int E, void* stream);
 
