@@ -734,24 +734,55 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
         for (int m = 0; m < C::NMAT; ++m) F.a[s][m][fi] = weight_frag(buf, s, m, fi);
     }
   };
-  auto mfma = [&](const Frags& F) INL {
+  // live: the wave's 16-row token blocks that hold at least one row of the
+  // item (blocks 0 .. live-1). In the widening tiles the MFMAs of the other
+  // blocks are skipped: the epilogue stores none of their rows, and each
+  // accumulator still takes its K-substeps in order, so the stored sums are
+  // unchanged (FP8 layer at the DeepSeek-V3-shaped T = 4096 6.57 -> 6.41 ms,
+  // Mixtral-shaped T = 512 0.77 -> 0.73 ms, T = 8192 5.39 -> 5.28 ms). The
+  // bf16 tiles keep the whole burst: the branch cost the 256-row ping-pong
+  // tile 2-3 % at T = 8192 (a uniform skip of whole bands as well), and among
+  // the prefetching tiles' interleaved fragment reads it made them spill.
+  constexpr bool kSkipDeadBlocks = C::FT > 1 && C::WIDEN;
+  auto mfma = [&](const Frags& F, int live) INL {
+    if constexpr (kSkipDeadBlocks) {
 #pragma unroll
-    for (int s = 0; s < C::BK / 32; ++s)
+      for (int ti = 0; ti < C::FT; ++ti) {
+        if (ti >= live) break;
 #pragma unroll
-      for (int fi = 0; fi < C::FF; ++fi)
+        for (int s = 0; s < C::BK / 32; ++s)
 #pragma unroll
-        for (int m = 0; m < C::NMAT; ++m)
+          for (int fi = 0; fi < C::FF; ++fi)
 #pragma unroll
-          for (int ti = 0; ti < C::FT; ++ti)
-            acc[m][fi][ti] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                F.a[s][m][fi], F.b[s][ti], acc[m][fi][ti], 0, 0, 0);
+            for (int m = 0; m < C::NMAT; ++m)
+              acc[m][fi][ti] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  F.a[s][m][fi], F.b[s][ti], acc[m][fi][ti], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < C::BK / 32; ++s)
+#pragma unroll
+        for (int fi = 0; fi < C::FF; ++fi)
+#pragma unroll
+          for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+            for (int ti = 0; ti < C::FT; ++ti)
+              acc[m][fi][ti] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  F.a[s][m][fi], F.b[s][ti], acc[m][fi][ti], 0, 0, 0);
+    }
+  };
+
+  // the wave's live token blocks of an item (wave-uniform)
+  auto live_blocks = [&](const ItemInfo& it) INL {
+    const int r = it.rows_valid - wt * C::TT;
+    return __builtin_amdgcn_readfirstlane(r <= 0 ? 0 : min(C::FT, (r + 15) / 16));
   };
   // Without prefetch, the gated kernel interleaves the weight-fragment reads
   // column block by column block with the MFMAs that use them; the plain
   // kernel reads all fragments first (each order measured faster for its
   // kernel), except on mxfp4 weights, where all widened fragments of a
   // 64-deep stage would not fit the registers.
-  auto compute_interleaved = [&](const char* buf, int kvalid) INL {
+  auto compute_interleaved = [&](const char* buf, int kvalid, int live) INL {
 #pragma unroll
     for (int s = 0; s < C::BK / 32; ++s) {
       bf16x8 b[C::FT];
@@ -765,9 +796,11 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
 #pragma unroll
         for (int m = 0; m < C::NMAT; ++m)
 #pragma unroll
-          for (int ti = 0; ti < C::FT; ++ti)
+          for (int ti = 0; ti < C::FT; ++ti) {
+            if (kSkipDeadBlocks && ti >= live) break;
             acc[m][fi][ti] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 a[m], b[ti], acc[m][fi][ti], 0, 0, 0);
+          }
       }
     }
   };
@@ -856,6 +889,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     constexpr bool WD = C::WIDEN;
     constexpr int PTURN = (WD && S % 2 == 1) ? 2 * S : S;  // wide buffer = step parity
     const bool grp1 = wave >= 4;
+    const int live = kSkipDeadBlocks ? live_blocks(cur) : C::FT;
     wait_vmcnt<0>();               // the last item's stores and DMAs are done and
     __builtin_amdgcn_s_barrier();  // every wave has finished reading the ring
     static_for<DP>([&](auto I) INL { issue(cur, cur.kt_begin + decltype(I)::value, stage_buf(I)); });
@@ -894,7 +928,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
       issue(cur, cur.kt_begin + t + DP, stage_buf(std::integral_constant<int, i + DP>{}));
       wait_vmcnt_lgkm0<63>();           // fragments in registers (and widened codes written)
       pp_barrier();
-      mfma(fa);
+      mfma(fa, live);
       pp_barrier();
     };
     const int full = cur.nk / PTURN;
@@ -923,6 +957,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     if constexpr (C::PP) {
       run_pingpong(cur);
     } else {
+    const int live = kSkipDeadBlocks ? live_blocks(cur) : C::FT;
     if (!primed) {
       wait_vmcnt<0>();               // every DMA into the ring has landed and
       __builtin_amdgcn_s_barrier();  // every wave is done with the last item
@@ -952,19 +987,19 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
         const int kvalid = cur.K - (cur.kt_begin + t + 1) * C::BK;
         if constexpr (i % 2 == 0) {
           load_frags(nb, fb, kvalid);
-          mfma(fa);
+          mfma(fa, live);
         } else {
           load_frags(nb, fa, kvalid);
-          mfma(fb);
+          mfma(fb, live);
         }
       } else {
         char* const cb = stage_buf(I);
         const int kvalid = cur.K - (cur.kt_begin + t) * C::BK;
         if constexpr (C::GATED || C::MX) {
-          compute_interleaved(cb, kvalid);
+          compute_interleaved(cb, kvalid, live);
         } else {
           load_frags(cb, fa, kvalid);
-          mfma(fa);
+          mfma(fa, live);
         }
       }
     };
