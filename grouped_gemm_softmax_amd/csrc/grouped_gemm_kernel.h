@@ -55,6 +55,7 @@
 // K-values contiguously, so a lane reads its fragment with one 16-byte LDS
 // read. MFMA: v_mfma_f32_16x16x32_bf16, fp32 accumulation.
 #include <algorithm>
+#include <cmath>
 #include <utility>
 
 #include "common.h"
@@ -1445,6 +1446,39 @@ using GateUpSmall = TileCfg<16, 64, 64, 1, 2, 4, true, true>;
 using GateUpMid = TileCfg<32, 64, 64, 1, 2, 3, true, true>;
 using DownLarge = TileCfg<256, 256, 32, 4, 2, 4, false, false, 1, 16, true>;
 using DownSmall = TileCfg<32, 64, 64, 1, 4, 4, false, true>;
+// Row-major weights at decode sizes. A stage of a row-major tile reads 128
+// contiguous bytes of each weight row per 64 columns, and consecutive rows
+// lie a whole matrix width apart, so a wider tile reads longer runs of every
+// row: 32 rows x 128 or 256 columns (gate/up) and 32 x 128 (down) instead of
+// 16 x 64 and 32 x 64 (Mixtral-shaped layer at T = 32 on row-major weights:
+// gate/up 393 -> 342 us at 128 columns and 316 us at 256, down 198 ->
+// 169 us). Wider tiles make fewer items, so the widest is taken whose
+// expected items still fill the chip (rowmajor_decode_width).
+using GateUpSmallRM128 = TileCfg<32, 128, 64, 1, 4, 3, true, true>;
+using GateUpSmallRM256 = TileCfg<32, 256, 32, 1, 2, 3, true, true>;
+using DownSmallRM = TileCfg<32, 128, 64, 1, 4, 4, false, true>;
+
+// Column width (64, 128 or 256) of the decode-size tile on row-major
+// weights: 256 when the expected items fill 1.5 per CU, else 128 when they
+// fill half of the CUs (at the Mixtral-shaped T = 1, two experts' 224 items
+// of 128 columns still beat 448 of 64: gate/up 104 -> 91 us, but 112 items
+// of 256 columns took 112 us), else 64. A group of G with R routed rows
+// touches G (1 - (1 - 1/G)^R) groups on average.
+inline int rowmajor_decode_width(const GemmProblem& p, int max_width) {
+  double items128 = 0, items256 = 0;
+  for (int s = 0; s < p.nseg; ++s) {
+    const GemmSegment& S = p.seg[s];
+    const double g = S.ngroups > 0 ? S.ngroups : 1;
+    const double touched = g > 1 ? g * (1.0 - std::pow(1.0 - 1.0 / g, S.rows)) : 1.0;
+    const double tiles = (touched + S.rows / 32) * (S.ksplit > 0 ? S.ksplit : 1);
+    items128 += tiles * ((S.N + 127) / 128);
+    items256 += tiles * ((S.N + 255) / 256);
+  }
+  const double cus = device_cu_count();
+  if (max_width >= 256 && items256 >= 1.5 * cus) return 256;
+  if (items128 >= 0.5 * cus) return 128;
+  return 64;
+}
 // FP8 weights: the same tile shapes with half the weight bytes per stage,
 // hence deeper rings in about the same LDS. The 128- and 256-row tiles run
 // the ping-pong schedule with 32-deep stages and widen each stage's codes

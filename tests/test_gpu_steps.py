@@ -47,6 +47,12 @@ CASES = {
     # ... with K and N not whole tiles (the K-tail kernels)
     "skewed_mid_ragged": (synth.small_config("srr", H=200, F=328, E=12, k=2, logits="zipf"),
                           700, None),
+    # decode-size groups on row-major weights with enough expected items for
+    # the 256-column gate/up tile and the 128-column down tile (64 touched
+    # experts), K and N not whole tiles
+    "rowmajor_wide256": (synth.small_config("rw256", H=200, F=1480, E=64, k=2), 200, None),
+    # ... few tokens: the 128-column gate/up tile (about 7 touched experts)
+    "rowmajor_wide128": (synth.small_config("rw128", H=328, F=2344, E=8, k=2), 8, None),
 }
 
 
