@@ -125,6 +125,7 @@ _SIGNATURES = {
                                  ctypes.POINTER(SharedExpert), _P, _P, _P, _P, _P, _P,
                                  ctypes.POINTER(SharedExpertGrads), _P, _SZ, _P]),
     "moe_set_dispatch_override": (_I, [_I, _I]),
+    "moe_set_combine_override": (_I, [_I]),
     "moe_set_diagnostics": (_I, [_I, _I]),
     "moe_check_topk_ids": (_I, [_P, _I, _I, _I, _P]),
 }
@@ -539,6 +540,13 @@ def moe_set_dispatch_override(decode_path: int = -1, tile_class: int = -1):
     3 256-row) of later calls in this process; -1 is the automatic choice."""
     _check(lib().moe_set_dispatch_override(decode_path, tile_class),
            "moe_set_dispatch_override")
+
+
+def moe_set_combine_override(mode: int = -1):
+    """Testing hook: 1 lets decode-size down projections of the fused layer
+    combine in their epilogue; 0 or -1 (automatic) keeps the combine in a
+    launch of its own."""
+    _check(lib().moe_set_combine_override(mode), "moe_set_combine_override")
 
 
 def moe_set_diagnostics(trace: int = -1, check_ids: int = -1):

@@ -79,7 +79,7 @@ size_t permute_ws_bytes(int T, int E, int k) {
 // error (half an ulp of |y|, up to ~0.03 at |y| ~ 10) would otherwise reach
 // outputs where the k expert terms cancel.
 struct ForwardLayout {
-  size_t hist, ids, w, offsets, row_token, row_dest, x_perm, h, h_sh, y, y_sh, total;
+  size_t hist, ids, w, offsets, row_token, row_dest, x_perm, h, h_sh, y, y_sh, cnt, total;
   int ksplit;     // K-slices of the routed down projection (y holds that many)
   int ksplit_sh;  // K-slices of the shared expert's (y_shared holds that many)
 };
@@ -121,6 +121,9 @@ ForwardLayout forward_layout(int T, int H, int F, int E, int k, int Fs, int cus)
   L.h_sh = take(static_cast<size_t>(T) * (Fs > 0 ? Fs : 0) * 2);
   L.y = take(S * A * H * 4);                                       // fp32
   L.y_sh = take(static_cast<size_t>(L.ksplit_sh) * T * (Fs > 0 ? H : 0) * 4);  // fp32
+  // arrival counters of a down projection that combines in its epilogue:
+  // one per token and 64-column tile of the output
+  L.cnt = take(static_cast<size_t>(T) * ((H + 63) / 64) * 4);
   L.total = o;
   return L;
 }
@@ -558,6 +561,12 @@ int moe_set_dispatch_override(int decode_path, int tile_class) {
   return MOE_OK;
 }
 
+int moe_set_combine_override(int mode) {
+  if (mode < -1 || mode > 1) return MOE_ERR_INVALID_ARG;
+  moe::set_scatter_override(mode);
+  return MOE_OK;
+}
+
 // The layer's weights in one layout (the shared expert's too, when Fs > 0).
 struct LayerWeights {
   int layout;
@@ -650,8 +659,45 @@ static int forward_impl(const moe_bf16* x, const float* logits, const int32_t* i
   bf16_t* h_sh = reinterpret_cast<bf16_t*>(base + L.h_sh);
   float* y = reinterpret_cast<float*>(base + L.y);
   float* y_sh = reinterpret_cast<float*>(base + L.y_sh);
+  int32_t* cnt = reinterpret_cast<int32_t*>(base + L.cnt);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int M = static_cast<int>(A);
+
+  // 4's problem (grouped down, shared expert likewise) before any launch:
+  // when its tiles also combine (at decode sizes, through the testing hook),
+  // the permutation clears their arrival counters. The K-split plan is the
+  // same for every weight layout (the workspace size does not depend on it).
+  moe::GemmProblem g2 = down_problem(h, offsets, M, F, H, E, W.wd, y, W.layout, W.sd);
+  g2.out_f32 = true;
+  g2.seg[0].ksplit = L.ksplit;
+  g2.seg[0].slice_stride = static_cast<int64_t>(M) * H;
+  if (shared) {
+    g2.seg[1] = segment(h_sh, nullptr, W.swd, nullptr, y_sh, T, 1, Fs, H, W.layout, W.ssd,
+                        nullptr);
+    g2.seg[1].slice_stride = static_cast<int64_t>(T) * H;
+    g2.seg[1].ksplit = L.ksplit_sh;
+    g2.nseg = 2;
+  }
+  const bool scatter = moe::grouped_gemm_scatters(g2);
+  const int64_t ncnt = scatter ? static_cast<int64_t>(T) * ((H + 63) / 64) : 0;
+  if (scatter) {
+    moe::ScatterArgs& sa = g2.scat;
+    sa.cnt = cnt;
+    sa.target = k * L.ksplit + (shared ? L.ksplit_sh : 0);
+    sa.T = T;
+    sa.k = k;
+    sa.row_token = row_token;
+    sa.row_dest = row_dest;
+    sa.topk_w = w_c;
+    sa.y = y;
+    sa.y_slice_stride = static_cast<int64_t>(M) * H;
+    sa.y_slices = L.ksplit;
+    sa.y_sh = shared ? y_sh : nullptr;
+    sa.ysh_slice_stride = static_cast<int64_t>(T) * H;
+    sa.ysh_slices = L.ksplit_sh;
+    sa.gate_logits = shared ? W.gate_logits : nullptr;
+    sa.out = out;
+  }
 
   // 3's problem first: the large-batch tiles read the rows of x through
   // row_token themselves, and then the permutation copies no rows
@@ -666,7 +712,8 @@ static int forward_impl(const moe_bf16* x, const float* logits, const int32_t* i
   if (logits && !gather && moe::route_permute_fits_one_launch(T, E, k)) {
     // 1+2. small batch: routing and the permutation in one launch
     MOE_TRY(hip_status(moe::launch_route_permute_small(logits, x, T, H, E, k, ids, w, offsets,
-                                                       row_token, row_dest, x_perm, s)));
+                                                       row_token, row_dest, x_perm, s,
+                                                       scatter ? cnt : nullptr, ncnt)));
   } else {
     // 1. route + per-chunk histogram, or the histogram of the given routing
     if (logits)
@@ -675,7 +722,8 @@ static int forward_impl(const moe_bf16* x, const float* logits, const int32_t* i
       MOE_TRY(hip_status(moe::launch_hist(ids_in, T, E, k, hist, s)));
     // 2. permute: scan, stable rank, row maps (+ x_perm rows unless gathered)
     MOE_TRY(hip_status(moe::launch_permute(x, ids_c, T, H, E, k, hist, offsets, row_token,
-                                           row_dest, gather ? nullptr : x_perm, s)));
+                                           row_dest, gather ? nullptr : x_perm, s,
+                                           scatter ? cnt : nullptr, ncnt)));
   }
   // 3. grouped gate/up + SwiGLU (shared expert as one more group over x)
   if (shared) {
@@ -683,20 +731,9 @@ static int forward_impl(const moe_bf16* x, const float* logits, const int32_t* i
     g1.nseg = 2;
   }
   MOE_TRY(hip_status(moe::launch_grouped_gemm(g1, s)));
-  // 4. grouped down (shared expert likewise); the K-split plan is the same
-  // for every weight layout (the workspace size does not depend on it)
-  moe::GemmProblem g2 = down_problem(h, offsets, M, F, H, E, W.wd, y, W.layout, W.sd);
-  g2.out_f32 = true;
-  g2.seg[0].ksplit = L.ksplit;
-  g2.seg[0].slice_stride = static_cast<int64_t>(M) * H;
-  if (shared) {
-    g2.seg[1] = segment(h_sh, nullptr, W.swd, nullptr, y_sh, T, 1, Fs, H, W.layout, W.ssd,
-                        nullptr);
-    g2.seg[1].slice_stride = static_cast<int64_t>(T) * H;
-    g2.seg[1].ksplit = L.ksplit_sh;
-    g2.nseg = 2;
-  }
+  // 4. grouped down (+ 5. when its tiles combine)
   MOE_TRY(hip_status(moe::launch_grouped_gemm(g2, s)));
+  if (scatter) return MOE_OK;
   // 5. combine (+ gated shared term)
   return hip_status(moe::launch_combine(y, true, L.ksplit, static_cast<int64_t>(M) * H,
                                         row_dest, w_c, T, H, k, shared ? y_sh : nullptr,

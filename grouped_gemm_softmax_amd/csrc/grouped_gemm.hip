@@ -20,12 +20,15 @@ namespace {
 // Dispatch overrides (-1: automatic), set only through the testing hook.
 std::atomic<int> g_forced_tile{-1};
 std::atomic<int> g_forced_rs{-1};
+std::atomic<int> g_forced_scatter{-1};
 }  // namespace
 
 void set_dispatch_override(int decode_path, int tile_class) {
   g_forced_rs.store(decode_path, std::memory_order_relaxed);
   g_forced_tile.store(tile_class, std::memory_order_relaxed);
 }
+
+void set_scatter_override(int mode) { g_forced_scatter.store(mode, std::memory_order_relaxed); }
 
 int tile_class(const GemmProblem& p) {
   const int forced = g_forced_tile.load(std::memory_order_relaxed);
@@ -62,6 +65,23 @@ int tile_class(const GemmProblem& p) {
 bool grouped_gemm_gathers(const GemmProblem& p) {
   const int tc = tile_class(p);
   return p.gated && (tc == kLarge || tc == kLarge128);
+}
+
+// The decode-size tiles of a plain fp32-output problem on the forward's
+// weight layouts (their 16- or 32-row tiles carry the hand-over epilogue),
+// when the testing hook asks for it. By default the layer combines in a
+// launch of its own: against it, the hand-over measured equal at the
+// Mixtral-shaped T = 1 (0.143 ms) and slower wherever a workgroup runs
+// several items (Qwen2-shaped T = 16 0.166 -> 0.177 ms, DeepSeek-V3-shaped
+// T = 128 2.64 -> 2.80 ms): each item waits for its device-scope stores, its
+// counter atomics and its device-scope loads in turn, a few microseconds,
+// about the whole combine launch it replaces. Ordinary stores with
+// agent-scope fences instead (an L2 write-back and invalidation per item)
+// made those layers 1.7-4x slower.
+bool grouped_gemm_scatters(const GemmProblem& p) {
+  if (g_forced_scatter.load(std::memory_order_relaxed) != 1) return false;
+  if (p.gated || !p.out_f32 || p.seg[0].packed == kWeightsTransposed) return false;
+  return tile_class(p) == kSmall;
 }
 
 void grouped_gemm_plan_ksplit(GemmProblem& p, int cus) {
@@ -506,6 +526,12 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream) {
   // the backward epilogue exists in the transposed-weight bf16 kernels only
   if (p.epi == kSwigluBwd &&
       (p.gated || p.out_f32 || p.seg[0].packed != kWeightsTransposed || p.nseg != 1))
+    return hipErrorInvalidValue;
+  // the hand-over epilogue exists in the decode-size fp32 tiles only
+  if (p.scat.cnt && (!grouped_gemm_scatters(p) || p.scat.T < 1 || p.scat.k < 1 ||
+                     p.scat.target < 1 || !p.scat.out || !p.scat.y || !p.scat.row_token ||
+                     !p.scat.row_dest || p.scat.y_slices < 1 || p.scat.ysh_slices < 1 ||
+                     (p.nseg > 1 && p.seg[1].N != p.seg[0].N)))
     return hipErrorInvalidValue;
   const int tc = tile_class(p);
   if (p.gated && tc == kSmall && use_rs_gateup(p)) return launch_rs(p, stream);

@@ -271,6 +271,22 @@ __device__ __forceinline__ void store4(bf16_t* p, const float v[4]) {
 __device__ __forceinline__ void store4(float* p, const float v[4]) {
   *(__attribute__((address_space(1))) f32x4_t*)(p) = f32x4_t{v[0], v[1], v[2], v[3]};
 }
+// Device-scope stores and loads (relaxed atomics at agent scope): they
+// write through to, and read from, the memory all eight XCDs share, instead
+// of an XCD's own L2, so partial sums handed to another workgroup need no
+// write-back or invalidation of the whole L2 (which agent-scope fences do).
+__device__ __forceinline__ void store4_device(float* p, const float v[4]) {
+  typedef __attribute__((address_space(1))) float gfloat_t;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __hip_atomic_store((gfloat_t*)(p) + i, v[i], __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_device(const float* p) {
+  typedef __attribute__((address_space(1))) const float gcfloat_t;
+  return __hip_atomic_load((gcfloat_t*)(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
 
 template <class C, typename OutT, bool KTAIL, bool PACKED, bool TRANSW = false>
 __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel(
@@ -291,6 +307,11 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
   // the K pipeline would wait for every DMA in flight)
   extern __shared__ __attribute__((aligned(16))) int s_pref[];
   __shared__ int s_wave_total[C::NW];
+  // decode-size fp32 tiles: the combine folded into the epilogue
+  // (ScatterArgs); the token of each row of the item whose column tile this
+  // workgroup completes, else -1
+  constexpr bool kScatterTile = !C::GATED && sizeof(OutT) == 4 && !TRANSW && C::BT <= 32;
+  __shared__ int s_scat[kScatterTile ? C::BT : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -376,6 +397,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     const float* wrow;
     float* part;
     int K, N;
+    int seg;          // segment of the item's group (0 routed, 1 shared)
     int n0;           // first output column
     int row_base;     // first activation row
     int rows_valid;   // rows of the tile inside the group
@@ -406,6 +428,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     ItemInfo it;
     it.K = S.K;
     it.N = S.N;
+    it.seg = v.seg;
     const int mtiles = (v.M + C::BT - 1) / C::BT;
     int local = item - s_pref[lo];
     const int ksplit = S.ksplit;
@@ -466,6 +489,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
     }
     it.K = __builtin_amdgcn_readfirstlane(it.K);
     it.N = __builtin_amdgcn_readfirstlane(it.N);
+    it.seg = __builtin_amdgcn_readfirstlane(it.seg);
     it.n0 = __builtin_amdgcn_readfirstlane(it.n0);
     it.row_base = __builtin_amdgcn_readfirstlane(it.row_base);
     it.rows_valid = __builtin_amdgcn_readfirstlane(it.rows_valid);
@@ -1099,8 +1123,68 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
               store4(cur.out3 + o, u4);
             }
           }
-          store4(cur.out + o, vals);
+          if constexpr (kScatterTile) {
+            if (prob.scat.cnt) store4_device(reinterpret_cast<float*>(cur.out) + o, vals);
+            else store4(cur.out + o, vals);
+          } else {
+            store4(cur.out + o, vals);
+          }
         }
+      }
+    }
+    if constexpr (kScatterTile) {
+      if (prob.scat.cnt) {
+        const ScatterArgs& sa = prob.scat;
+        // this thread's partial sums (device-scope stores) have completed
+        // before any row of the item is counted
+        wait_vmcnt<0>();
+        __syncthreads();
+        const int ncb = (cur.N + C::BF - 1) / C::BF;
+        const int cb = cur.n0 / C::BF;
+        if (tid < C::BT) {
+          int tok = -1;
+          if (tid < cur.rows_valid) {
+            int t = cur.seg ? cur.row_base + tid : sa.row_token[cur.row_base + tid];
+            t = min(max(t, 0), sa.T - 1);
+            const int before = atomicAdd(sa.cnt + static_cast<int64_t>(t) * ncb + cb, 1);
+            if (before == sa.target - 1) tok = t;
+          }
+          s_scat[tid] = tok;
+        }
+        __syncthreads();
+        // the completed tokens' partial sums, read at device scope (every one
+        // was stored before its row was counted)
+        const int64_t A = static_cast<int64_t>(sa.T) * sa.k;
+        for (int r = wave; r < cur.rows_valid; r += C::NW) {
+          const int t = s_scat[r];
+          if (t < 0) continue;
+          for (int c = lane; c < C::BF; c += kWave) {
+            const int col = cur.n0 + c;
+            if (col >= cur.N) break;
+            float a = 0.f;
+            for (int j = 0; j < sa.k; ++j) {
+              int p = sa.row_dest[static_cast<int64_t>(t) * sa.k + j];
+              p = p < 0 ? 0 : (p >= A ? static_cast<int>(A - 1) : p);
+              const float w = sa.topk_w ? sa.topk_w[static_cast<int64_t>(t) * sa.k + j] : 1.0f;
+              const float* yp = sa.y + static_cast<int64_t>(p) * cur.N + col;
+              float v = load_device(yp);
+              for (int sl = 1; sl < sa.y_slices; ++sl) v += load_device(yp + sl * sa.y_slice_stride);
+              a += w * v;
+            }
+            if (sa.y_sh) {
+              const float sg =
+                  sa.gate_logits ? 1.0f / (1.0f + expf(-sa.gate_logits[t])) : 1.0f;
+              const float* yp = sa.y_sh + static_cast<int64_t>(t) * cur.N + col;
+              float v = load_device(yp);
+              for (int sl = 1; sl < sa.ysh_slices; ++sl)
+                v += load_device(yp + sl * sa.ysh_slice_stride);
+              a += sg * v;
+            }
+            sa.out[static_cast<int64_t>(t) * cur.N + col] = f32_to_bf16(a);
+          }
+        }
+        wait_vmcnt<0>();  // the next item's ring waits count its own loads only
+        __syncthreads();  // s_scat is rewritten by the next item
       }
     }
     primed = chain;
@@ -1620,14 +1704,14 @@ hipError_t launch_tail(const GemmProblem& p, int64_t bound, hipStream_t stream) 
   MOE_TRACE_LAUNCH("grouped_gemm_kernel", dim3(static_cast<unsigned>(grid)), dim3(C::kThreads),
                    dyn,
                    "tile=%dx%dx%d stages=%d schedule=%s wbits=%d%s gated=%d out=%s ktail=%d "
-                   "layout=%d segments=%d groups=%d items<=%lld ksplit=%d",
+                   "layout=%d segments=%d groups=%d items<=%lld ksplit=%d combine=%d",
                    C::BT, C::BF, C::BK, C::STAGES,
                    C::PP ? (C::WIDEN ? "pingpong-widen" : "pingpong")
                          : (C::PREFETCH ? "ring-prefetch" : "ring"),
                    C::WBITS, C::MX ? "+mx" : "", C::GATED ? 1 : 0,
                    sizeof(OutT) == 4 ? "f32" : "bf16", KTAIL ? 1 : 0,
                    TRANSW ? kWeightsTransposed : p.seg[0].packed, p.nseg, groups,
-                   static_cast<long long>(bound), p.seg[0].ksplit);
+                   static_cast<long long>(bound), p.seg[0].ksplit, p.scat.cnt ? 1 : 0);
   hipLaunchKernelGGL((grouped_gemm_kernel<C, OutT, KTAIL, PACKED, TRANSW>),
                      dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), dyn, stream, p);
   return hipGetLastError();

@@ -43,16 +43,19 @@ hipError_t launch_hist(const int32_t* topk_ids, int T, int E, int k,
 // Route + permute (with the row copy) in one launch, for T*k <= 128 and
 // E <= 256 (where it is faster than route + permute).
 bool route_permute_fits_one_launch(int T, int E, int k);
+// Both permutation launches also zero clear[0, nclear) (the arrival counters
+// of a down projection that combines in its epilogue; nullptr: nothing).
 hipError_t launch_route_permute_small(const float* logits, const bf16_t* x, int T, int H,
                                       int E, int k, int32_t* topk_ids, float* topk_w,
                                       int32_t* expert_offsets, int32_t* row_token,
-                                      int32_t* row_dest, bf16_t* x_perm, hipStream_t stream);
+                                      int32_t* row_dest, bf16_t* x_perm, hipStream_t stream,
+                                      int32_t* clear = nullptr, int64_t nclear = 0);
 // x_perm == nullptr: row maps and offsets only (no row copy).
 hipError_t launch_permute(const bf16_t* x, const int32_t* topk_ids, int T,
                           int H, int E, int k, const int32_t* hist,
                           int32_t* expert_offsets, int32_t* row_token,
                           int32_t* row_dest, bf16_t* x_perm,
-                          hipStream_t stream);
+                          hipStream_t stream, int32_t* clear = nullptr, int64_t nclear = 0);
 
 // --- grouped GEMM (grouped_gemm.hip) ---
 // A segment is a list of groups that share K, N and the weight layout.
@@ -110,6 +113,37 @@ struct GemmSegment {
 constexpr int kWeightsTransposed = 4;
 enum GemmEpilogue { kEpiDefault = 0, kStoreGUH = 1, kSwigluBwd = 2 };
 
+// The combine folded into a decode-size down projection of the fused layer
+// (GemmProblem::scat, on when cnt != nullptr; see grouped_gemm_scatters).
+// The routed segment's rows are the permuted assignments, the shared
+// segment's (if any) the tokens. After storing its fp32 partial sums, a
+// workgroup publishes them at device scope and counts each of its rows into
+// cnt[token * ceil(N / BF) + column tile] (one vector-memory integer atomic
+// per row); the workgroup whose count completes the token's column tile
+// (target = k * routed K-slices + shared K-slices) reads every partial sum
+// of it and writes out[token] over the tile's columns, with the combine's
+// arithmetic in the combine's order: for j < k the slices of row
+// row_dest[t*k + j] added in slice order, times topk_w[t*k + j] (1 when
+// null), accumulated in ascending j; then the shared rows' slices times the
+// sigmoid of gate_logits[t] (1 when null). Nothing waits on another
+// workgroup, and the result does not depend on which one completes a tile.
+struct ScatterArgs {
+  int32_t* cnt = nullptr;  // [T * ceil(N / 64)], zero before the launch
+  int target = 0;
+  int T = 0, k = 0;
+  const int32_t* row_token = nullptr;
+  const int32_t* row_dest = nullptr;
+  const float* topk_w = nullptr;
+  const float* y = nullptr;       // the routed segment's output (slice 0)
+  int64_t y_slice_stride = 0;
+  int y_slices = 1;
+  const float* y_sh = nullptr;    // the shared segment's output, or null
+  int64_t ysh_slice_stride = 0;
+  int ysh_slices = 1;
+  const float* gate_logits = nullptr;
+  bf16_t* out = nullptr;          // [T, N]
+};
+
 struct GemmProblem {
   GemmSegment seg[2];
   int nseg;
@@ -117,6 +151,7 @@ struct GemmProblem {
   bool out_f32;    // store fp32 instead of bf16 (down projection only)
   int rows_hint;   // typical rows per group, picks the tile shape
   int epi = kEpiDefault;  // GemmEpilogue (kStoreGUH: gated; kSwigluBwd: plain, bf16 out)
+  ScatterArgs scat;
 };
 
 hipError_t launch_grouped_gemm(const GemmProblem& prob, hipStream_t stream);
@@ -124,6 +159,11 @@ hipError_t launch_grouped_gemm(const GemmProblem& prob, hipStream_t stream);
 // (GemmSegment::gather): true for the large-batch tile classes, whose items
 // restart their pipeline anyway (the map is read at each item's start).
 bool grouped_gemm_gathers(const GemmProblem& prob);
+// Whether the plain fp32-output problem combines in its epilogue
+// (GemmProblem::scat): only the decode-size class can, and only when the
+// testing hook asks for it (set_scatter_override(1); the reason is at the
+// definition).
+bool grouped_gemm_scatters(const GemmProblem& prob);
 
 // Sets each segment's K-slices (seg[s].ksplit) for an fp32-output problem on
 // a device with `cus` compute units; gated or bf16 problems keep 1.
@@ -133,6 +173,9 @@ int grouped_gemm_device_cus();
 // register-streaming kernel) and the tile class (0 small, 1 mid, 2 large128,
 // 3 large) of later launches; -1 restores the automatic choice.
 void set_dispatch_override(int decode_path, int tile_class);
+// Testing hook: 1 combines in the down projection's epilogue where its
+// tiles can; 0 or -1 (automatic) never (a combine launch of its own).
+void set_scatter_override(int mode);
 
 // Packed weights: W [G][K][N] as G x ceil(N/64) x ceil(K/64) blocks of
 // 64 x 64 (block (g, nb, kb) at element ((g*NB + nb)*KB + kb)*4096), each

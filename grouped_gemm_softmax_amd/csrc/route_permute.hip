@@ -154,6 +154,17 @@ __global__ __launch_bounds__(kRouteThreads) void hist_kernel(
 
 constexpr int kPermThreads = 256;
 
+// Zeroes clear[0, nclear) across the whole grid (one int per thread and
+// pass): the arrival counters of a down projection that combines in its
+// epilogue, cleared by the launch before it in the stream.
+__device__ __forceinline__ void clear_range(int32_t* clear, int64_t nclear) {
+  if (!clear) return;
+  const int64_t nthreads = static_cast<int64_t>(gridDim.x) * gridDim.y * blockDim.x;
+  const int64_t first =
+      (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+  for (int64_t i = first; i < nclear; i += nthreads) clear[i] = 0;
+}
+
 // One block per group of `cpb` (<= kPermChunks) routing chunks (and per column slice of
 // x). Steps:
 //  1. One coalesced pass over the [nchunks][E] histogram gives each expert's
@@ -168,7 +179,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     int H, int E, int k, int chunk_tokens, int nchunks, int cpb, int slice_cols,
     const int32_t* __restrict__ hist, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ row_token, int32_t* __restrict__ row_dest,
-    bf16_t* __restrict__ x_perm) {
+    bf16_t* __restrict__ x_perm, int32_t* __restrict__ clear, int64_t nclear) {
   __shared__ int s_total[kMaxExperts];
   __shared__ int s_base[kPermChunks][kMaxExperts];
   __shared__ int s_wave_total[kPermThreads / kWave];
@@ -179,6 +190,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   const int wave = tid / kWave;
   const int c0 = blockIdx.x * cpb;                       // first routing chunk
   const int nc = min(cpb, nchunks - c0);                 // routing chunks here
+  clear_range(clear, nclear);
 
   // 1a. totals and counts before this block (integer LDS atomics: exact and
   //     order-independent)
@@ -313,7 +325,8 @@ __global__ __launch_bounds__(kSmallThreads) void route_permute_small_kernel(
     const float* __restrict__ logits, const bf16_t* __restrict__ x, int T, int H, int E,
     int k, int slice_cols, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ row_token,
-    int32_t* __restrict__ row_dest, bf16_t* __restrict__ x_perm) {
+    int32_t* __restrict__ row_dest, bf16_t* __restrict__ x_perm, int32_t* __restrict__ clear,
+    int64_t nclear) {
   __shared__ int s_count[kMaxExperts];
   __shared__ int s_off[kMaxExperts];
   __shared__ int s_ids[kMaxChunkAssign];
@@ -326,6 +339,7 @@ __global__ __launch_bounds__(kSmallThreads) void route_permute_small_kernel(
   const int wave = tid / kWave;
   const bool lead = blockIdx.x == 0;
   const int n = T * k;
+  clear_range(clear, nclear);
   for (int e = tid; e < E; e += kSmallThreads) {
     s_count[e] = 0;
     s_first_wave[e] = 0;
@@ -432,7 +446,8 @@ bool route_permute_fits_one_launch(int T, int E, int k) {
 hipError_t launch_route_permute_small(const float* logits, const bf16_t* x, int T, int H,
                                       int E, int k, int32_t* topk_ids, float* topk_w,
                                       int32_t* expert_offsets, int32_t* row_token,
-                                      int32_t* row_dest, bf16_t* x_perm, hipStream_t stream) {
+                                      int32_t* row_dest, bf16_t* x_perm, hipStream_t stream,
+                                      int32_t* clear, int64_t nclear) {
   if (T <= 0) return hipSuccess;
   const int slice = kPermuteSliceCols;
   const int nslices = (H + slice - 1) / slice;
@@ -440,7 +455,7 @@ hipError_t launch_route_permute_small(const float* logits, const bf16_t* x, int 
                    "T=%d H=%d E=%d k=%d", T, H, E, k);
   hipLaunchKernelGGL(route_permute_small_kernel, dim3(nslices), dim3(kSmallThreads), 0, stream,
                      logits, x, T, H, E, k, slice, topk_ids, topk_w, expert_offsets, row_token,
-                     row_dest, x_perm);
+                     row_dest, x_perm, clear, nclear);
   return hipGetLastError();
 }
 
@@ -488,7 +503,7 @@ hipError_t launch_permute(const bf16_t* x, const int32_t* topk_ids, int T,
                           int H, int E, int k, const int32_t* hist,
                           int32_t* expert_offsets, int32_t* row_token,
                           int32_t* row_dest, bf16_t* x_perm,
-                          hipStream_t stream) {
+                          hipStream_t stream, int32_t* clear, int64_t nclear) {
   const int chunk = route_chunk_tokens(T, k);
   const int nchunks = route_num_chunks(T, k);
   const int slice = kPermuteSliceCols;
@@ -502,7 +517,7 @@ hipError_t launch_permute(const bf16_t* x, const int32_t* topk_ids, int T,
                    "T=%d H=%d E=%d k=%d chunk=%d copy=%d", T, H, E, k, chunk, x_perm ? 1 : 0);
   hipLaunchKernelGGL(permute_kernel, dim3(nblocks, nslices), dim3(kPermThreads),
                      0, stream, x, topk_ids, T, H, E, k, chunk, nchunks, cpb, slice,
-                     hist, expert_offsets, row_token, row_dest, x_perm);
+                     hist, expert_offsets, row_token, row_dest, x_perm, clear, nclear);
   return hipGetLastError();
 }
 

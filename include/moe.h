@@ -604,6 +604,18 @@ int moe_check_topk_ids(const int32_t* topk_ids, int T, int k, int E, void* strea
  * MOE_ERR_INVALID_ARG for values outside those ranges. */
 int moe_set_dispatch_override(int decode_path, int tile_class);
 
+/* Testing hook, like moe_set_dispatch_override: where the fused layer
+ * combines. mode 1: in the down projection's epilogue whenever its tiles are
+ * the decode-size ones (the scatter-add half of gather/scatter fusion: each
+ * workgroup counts its rows into per-(token, column tile) integer counters
+ * after storing its partial sums at device scope, and the one that completes
+ * a tile adds the token's rows in the combine's order, so the result is
+ * deterministic and bit-identical to the separate combine); 0 or -1
+ * (automatic): in a combine launch of its own after the down projection,
+ * which measured as fast or faster on MI355X. Returns MOE_OK, or
+ * MOE_ERR_INVALID_ARG outside -1..1. */
+int moe_set_combine_override(int mode);
+
 #ifdef __cplusplus
 }
 #endif

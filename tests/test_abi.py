@@ -42,6 +42,14 @@ def test_dispatch_override_hook(L):
     assert L.moe_set_dispatch_override(-1, -1) == OK
 
 
+def test_combine_override_hook(L):
+    assert L.moe_set_combine_override(2) == INVALID
+    assert L.moe_set_combine_override(-2) == INVALID
+    assert L.moe_set_combine_override(1) == OK
+    assert L.moe_set_combine_override(0) == OK
+    assert L.moe_set_combine_override(-1) == OK
+
+
 def test_diagnostics_hook(L):
     assert L.moe_set_diagnostics(2, 0) == INVALID
     assert L.moe_set_diagnostics(0, -2) == INVALID
@@ -389,7 +397,8 @@ def _layout_model(T, H, F, E, k, Fs):
     nch = (T + chunk - 1) // chunk
     S, S_sh = _down_ksplit(T, H, F, E, k, Fs)
     parts = [nch * E * 4, A * 4, A * 4, (E + 1) * 4, A * 4, A * 4, A * H * 2,
-             A * F * 2, T * Fs * 2, S * A * H * 4, S_sh * T * (H if Fs else 0) * 4]
+             A * F * 2, T * Fs * 2, S * A * H * 4, S_sh * T * (H if Fs else 0) * 4,
+             T * ((H + 63) // 64) * 4]   # arrival counters of the epilogue combine
     return sum(al(p) for p in parts)
 
 

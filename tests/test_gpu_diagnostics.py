@@ -103,7 +103,19 @@ def test_launch_trace(diag, capfd):
     names = [l.split()[2] for l in lines]
     # five launches: routing (+ permutation), gate/up, down, combine
     assert len(lines) in (4, 5), lines
-    assert names[-1] == "combine_kernel"
+    assert names[-1] == "combine_kernel" and " combine=0" in lines[-2], lines
     gemm = [l for l in lines if " grouped_gemm_kernel " in l or " rs_gateup_kernel " in l]
     assert len(gemm) == 2 and all(" tile=" in l and " grid=" in l for l in gemm), gemm
     assert out.shape == layer.x.shape
+    # the combine in the down projection's epilogue (testing hook)
+    B.moe_set_combine_override(1)
+    try:
+        B.moe_set_diagnostics(1, -1)
+        B.moe_forward(layer.x, layer.logits, cfg.k, layer.w_gate, layer.w_up, layer.w_down)
+        torch.cuda.synchronize()
+    finally:
+        B.moe_set_diagnostics(0, -1)
+        B.moe_set_combine_override(-1)
+    lines = [l for l in capfd.readouterr().err.splitlines() if l.startswith("moe: launch ")]
+    assert len(lines) in (3, 4) and lines[-1].split()[2] == "grouped_gemm_kernel", lines
+    assert " combine=1" in lines[-1], lines
