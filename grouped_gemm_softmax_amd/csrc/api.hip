@@ -1065,28 +1065,47 @@ static int backward_impl(const moe_bf16* x, const int32_t* topk_ids, const float
   }
   // dx: dG W_gate^T and dU W_up^T per row (fp32 slices), summed over the
   // token's k rows and the two slices by the combine with unit weights
-  // (plus the shared expert's two slices per token)
-  for (int slice = 0; slice < 2; ++slice) {
-    moe::GemmProblem g4{};
-    g4.seg[0] = segment(slice ? du : dg, offsets, slice ? w_up : w_gate, nullptr,
-                        dxp + static_cast<int64_t>(slice) * M * H, M, E, F, H,
-                        moe::kWeightsTransposed, nullptr, nullptr);
-    g4.nseg = 1;
-    g4.gated = false;
-    g4.out_f32 = true;
-    g4.rows_hint = M / E;
+  // (plus the shared expert's two slices per token). Both products run as
+  // the two segments of one launch (twice the items of either alone, which
+  // at a few row tiles per expert left half of the CUs idle), while their
+  // groups fit the item table.
+  auto dx_segment = [&](int slice) {
+    return segment(slice ? du : dg, offsets, slice ? w_up : w_gate, nullptr,
+                   dxp + static_cast<int64_t>(slice) * M * H, M, E, F, H,
+                   moe::kWeightsTransposed, nullptr, nullptr);
+  };
+  auto dx_shared_segment = [&](int slice) {
+    return segment(slice ? dush : dgsh, nullptr, slice ? sh->w_up : sh->w_gate, nullptr,
+                   dxsh + static_cast<int64_t>(slice) * T * H, T, 1, Fs, H,
+                   moe::kWeightsTransposed, nullptr, nullptr);
+  };
+  auto plain_f32 = [](int rows_hint) {
+    moe::GemmProblem q{};
+    q.nseg = 1;
+    q.gated = false;
+    q.out_f32 = true;
+    q.rows_hint = rows_hint;
+    return q;
+  };
+  if (2 * E <= moe::kMaxExperts + 1) {
+    moe::GemmProblem g4 = plain_f32(M / E);
+    g4.seg[0] = dx_segment(0);
+    g4.seg[1] = dx_segment(1);
+    g4.nseg = 2;
     MOE_TRY(hip_status(moe::launch_grouped_gemm(g4, s)));
-    if (sh) {
-      moe::GemmProblem g5{};
-      g5.seg[0] = segment(slice ? dush : dgsh, nullptr, slice ? sh->w_up : sh->w_gate, nullptr,
-                          dxsh + static_cast<int64_t>(slice) * T * H, T, 1, Fs, H,
-                          moe::kWeightsTransposed, nullptr, nullptr);
-      g5.nseg = 1;
-      g5.gated = false;
-      g5.out_f32 = true;
-      g5.rows_hint = T;
-      MOE_TRY(hip_status(moe::launch_grouped_gemm(g5, s)));
+  } else {
+    for (int slice = 0; slice < 2; ++slice) {
+      moe::GemmProblem g4 = plain_f32(M / E);
+      g4.seg[0] = dx_segment(slice);
+      MOE_TRY(hip_status(moe::launch_grouped_gemm(g4, s)));
     }
+  }
+  if (sh) {
+    moe::GemmProblem g5 = plain_f32(T);
+    g5.seg[0] = dx_shared_segment(0);
+    g5.seg[1] = dx_shared_segment(1);
+    g5.nseg = 2;
+    MOE_TRY(hip_status(moe::launch_grouped_gemm(g5, s)));
   }
   MOE_TRY(hip_status(moe::launch_combine(dxp, true, 2, static_cast<int64_t>(M) * H, row_dest,
                                          nullptr, T, H, k, sh ? dxsh : nullptr, 2,
