@@ -576,8 +576,8 @@ int moe_backward_shared(const moe_bf16* x, const int32_t* topk_ids, const float*
                         void* ws, size_t ws_bytes, void* stream);
 
 /* ---- Diagnostics ----
- * Not part of the layer's arithmetic; for debugging and tuning (the survey of
- * the method's tooling: a launch log and an id check on demand).
+ * Not part of the layer's arithmetic; for debugging and tuning: a launch log
+ * and an id check on demand.
  *
  * moe_set_diagnostics: trace = 1 logs every later kernel launch to stderr
  * (MOE_TRACE), check_ids = 1 turns on the id check of the calls that take
