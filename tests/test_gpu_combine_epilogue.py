@@ -91,3 +91,20 @@ def test_epilogue_combine_matches_oracle(name, orc):
     out = _fwd(layer, (layer.w_gate, layer.w_up, layer.w_down), layer.shared)
     torch.cuda.synchronize()
     assert_close(gpu_bf16_f64(out), ref["out"], f"out[{name}]")
+
+
+def test_epilogue_combine_from_given_routing():
+    """moe_forward_routed (the caller's ids and weights; the permutation
+    launch without routing clears the counters) against the default."""
+    cfg, T = CASES["shared_gated_k_slices"]
+    layer = synth.make_layer(cfg.name, T, seed=6, device="cuda", cfg=cfg)
+    ids, w = B.moe_route(layer.logits, cfg.k)
+    say("epilogue combine, given routing", T)
+    sep = B.moe_forward_routed(layer.x, ids, w, layer.w_gate, layer.w_up, layer.w_down,
+                               shared=layer.shared).clone()
+    torch.cuda.synchronize()
+    B.moe_set_combine_override(1)
+    epi = B.moe_forward_routed(layer.x, ids, w, layer.w_gate, layer.w_up, layer.w_down,
+                               shared=layer.shared)
+    torch.cuda.synchronize()
+    assert torch.equal(epi.view(torch.int16), sep.view(torch.int16))
