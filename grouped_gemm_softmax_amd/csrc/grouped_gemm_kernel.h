@@ -1051,30 +1051,43 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
         s0 = *reinterpret_cast<const float4*>(static_cast<const float*>(cur.sc0) + fc);
         if (C::GATED) s1 = *reinterpret_cast<const float4*>(static_cast<const float*>(cur.sc1) + fc);
       }
-      const float sc0[4] = {s0.x, s0.y, s0.z, s0.w};
-      const float sc1[4] = {s1.x, s1.y, s1.z, s1.w};
+      // (only in the transposed-weight bf16 kernels, which the backward's dh
+      // product runs: the forward's kernels carry no code for it)
+      if constexpr (TRANSW && !C::GATED && sizeof(OutT) == 2) {
+        if (prob.epi == kSwigluBwd) {
+          // acc = g = dout W_down^T for the row; with its routing weight w
+          // and the forward's G, U, h: dh = w g, dG = dh U silu'(G),
+          // dU = dh silu(G), silu'(z) = s (1 + z (1 - s)), s = 1/(1+e^-z);
+          // and the fragment's partial sum of h g (the routing-weight
+          // gradient <dout, y> = <h, g>), summed over its 16 columns across
+          // the four lanes of the token. The column's loads for all of the
+          // wave's token blocks are issued first, with no store between
+          // them, so that they are in flight together (issued block by
+          // block between the stores, each block waited for its own).
+          const int f = cur.n0 + wf * C::TF + fi * 16 + 4 * g16;
+          uint2 gq[C::FT], uq[C::FT], hq[C::FT];
+          float wv[C::FT];
 #pragma unroll
-      for (int ti = 0; ti < C::FT; ++ti) {
-        const int tok = wt * C::TT + ti * 16 + i16;
-        const int f = cur.n0 + wf * C::TF + fi * 16 + 4 * g16;
-        // (only in the transposed-weight bf16 kernels, which the backward's
-        // dh product runs: the forward's kernels carry no code for it)
-        if constexpr (TRANSW && !C::GATED && sizeof(OutT) == 2) {
-          if (prob.epi == kSwigluBwd) {
-            // acc = g = dout W_down^T for the row; with its routing weight w
-            // and the forward's G, U, h: dh = w g, dG = dh U silu'(G),
-            // dU = dh silu(G), silu'(z) = s (1 + z (1 - s)), s = 1/(1+e^-z);
-            // and the fragment's partial sum of h g (the routing-weight
-            // gradient <dout, y> = <h, g>), summed over its 16 columns
-            // across the four lanes of the token
+          for (int ti = 0; ti < C::FT; ++ti) {
+            const int tok = wt * C::TT + ti * 16 + i16;
+            gq[ti] = uq[ti] = hq[ti] = uint2{0u, 0u};
+            wv[ti] = 0.f;
+            if (tok < cur.rows_valid && f < cur.N) {
+              const int64_t o = static_cast<int64_t>(cur.row_base + tok) * cur.N + f;
+              gq[ti] = *reinterpret_cast<const uint2*>(cur.aux0 + o);
+              uq[ti] = *reinterpret_cast<const uint2*>(cur.aux1 + o);
+              hq[ti] = *reinterpret_cast<const uint2*>(cur.aux2 + o);
+              wv[ti] = cur.wrow[cur.row_base + tok];
+            }
+          }
+#pragma unroll
+          for (int ti = 0; ti < C::FT; ++ti) {
+            const int tok = wt * C::TT + ti * 16 + i16;
             float part = 0.f;
             if (tok < cur.rows_valid && f < cur.N) {
               const int64_t o = static_cast<int64_t>(cur.row_base + tok) * cur.N + f;
-              const uint2 gq = *reinterpret_cast<const uint2*>(cur.aux0 + o);
-              const uint2 uq = *reinterpret_cast<const uint2*>(cur.aux1 + o);
-              const uint2 hq = *reinterpret_cast<const uint2*>(cur.aux2 + o);
-              const float w = cur.wrow[cur.row_base + tok];
-              const uint32_t gw[2] = {gq.x, gq.y}, uw[2] = {uq.x, uq.y}, hw[2] = {hq.x, hq.y};
+              const uint32_t gw[2] = {gq[ti].x, gq[ti].y}, uw[2] = {uq[ti].x, uq[ti].y},
+                             hw[2] = {hq[ti].x, hq[ti].y};
               float dg[4], du[4];
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
@@ -1083,7 +1096,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
                 const float hv = bf16_to_f32(static_cast<bf16_t>(hw[r / 2] >> (16 * (r % 2))));
                 const float sg = 1.0f / (1.0f + __expf(-g));
                 const float gr = acc[0][fi][ti][r];
-                const float dh = w * gr;
+                const float dh = wv[ti] * gr;
                 dg[r] = dh * u * sg * (1.0f + g * (1.0f - sg));
                 du[r] = dh * g * sg;
                 part += hv * gr;
@@ -1097,9 +1110,16 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
             if (g16 == 0 && tok < cur.rows_valid && fc < cur.N)
               cur.part[static_cast<int64_t>(cur.row_base + tok) * ((cur.N + 15) / 16) + fc / 16] =
                   part;
-            continue;
           }
+          continue;
         }
+      }
+      const float sc0[4] = {s0.x, s0.y, s0.z, s0.w};
+      const float sc1[4] = {s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int ti = 0; ti < C::FT; ++ti) {
+        const int tok = wt * C::TT + ti * 16 + i16;
+        const int f = cur.n0 + wf * C::TF + fi * 16 + 4 * g16;
         if (tok < cur.rows_valid && f < cur.N) {
           const int64_t o = static_cast<int64_t>(cur.row_base + tok) * cur.N + f;
           float vals[4];
