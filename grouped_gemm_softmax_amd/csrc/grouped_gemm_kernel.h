@@ -1618,6 +1618,13 @@ using DownSmall8 = TileCfg<32, 64, 64, 1, 4, 4, false, true, 1, 8>;
 // class (a 256-row tile with 64-deep stages spills even so; the down
 // projection's K-split plan is valid for any tile, only tuned for another).
 using GateUpSmall4 = TileCfg<16, 64, 64, 1, 2, 4, true, true, 4, 4>;
+// At up to 4 rows per group (the stream is almost all weight codes), a
+// 32 x 128 gate/up tile on 4 waves, twice the codes per stage: same box,
+// A/B, Mixtral-shaped T = 1 0.090 -> 0.084 ms (gate/up 52 -> 47 us),
+// DeepSeek-V3-shaped T = 128 1.02 -> 1.00 ms, Qwen2-shaped T = 16 0.083 ->
+// 0.081 ms; at 8 rows per group (Mixtral-shaped T = 32) it was slower
+// (0.210 -> 0.219 ms), which keeps the 16 x 64 tile.
+using GateUpSmall4W = TileCfg<32, 128, 64, 1, 4, 4, true, true, 4, 4>;
 using GateUpMid4 = TileCfg<32, 64, 64, 1, 2, 4, true, true, 4, 4>;
 using DownSmall4 = TileCfg<16, 64, 64, 1, 2, 4, false, true, 4, 4>;
 using GateUpLarge128_4 = TileCfg<128, 128, 64, 4, 2, 4, true, false, 2, 4>;

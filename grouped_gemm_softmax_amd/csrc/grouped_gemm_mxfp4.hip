@@ -15,8 +15,9 @@ hipError_t launch_mxfp4(const GemmProblem& p, int tc, hipStream_t stream) {
   if (p.gated)
     return wide  ? launch_cfg<GateUpLarge_4W, bf16_t>(p, stream)
            : big ? launch_cfg<GateUpLarge128_4, bf16_t>(p, stream)
-           : tc == kMid ? launch_cfg<GateUpMid4, bf16_t>(p, stream)
-                        : launch_cfg<GateUpSmall4, bf16_t>(p, stream);
+           : tc == kMid          ? launch_cfg<GateUpMid4, bf16_t>(p, stream)
+           : p.rows_hint <= 4    ? launch_cfg<GateUpSmall4W, bf16_t>(p, stream)
+                                 : launch_cfg<GateUpSmall4, bf16_t>(p, stream);
   if (p.out_f32)
     return wide  ? launch_cfg<DownLarge_4W, float>(p, stream)
            : big ? launch_cfg<DownLarge128_4, float>(p, stream)
