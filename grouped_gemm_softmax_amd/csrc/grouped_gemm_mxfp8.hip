@@ -15,6 +15,7 @@ hipError_t launch_mxfp8(const GemmProblem& p, int tc, hipStream_t stream) {
     return tcm == kLarge      ? launch_cfg<GateUpLargeM8, bf16_t>(p, stream)
            : tcm == kLarge128 ? launch_cfg<GateUpLarge128_M8, bf16_t>(p, stream)
            : tcm == kMid      ? launch_cfg<GateUpMidM8, bf16_t>(p, stream)
+           : p.rows_hint <= 4 ? launch_cfg<GateUpSmallM8W, bf16_t>(p, stream)
                               : launch_cfg<GateUpSmallM8, bf16_t>(p, stream);
   if (p.out_f32)
     return tcm == kLarge      ? launch_cfg<DownLargeM8, float>(p, stream)
