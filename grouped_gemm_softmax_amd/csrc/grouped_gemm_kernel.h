@@ -1627,6 +1627,11 @@ using GateUpSmall4 = TileCfg<16, 64, 64, 1, 2, 4, true, true, 4, 4>;
 using GateUpSmall4W = TileCfg<32, 128, 64, 1, 4, 4, true, true, 4, 4>;
 using GateUpMid4 = TileCfg<32, 64, 64, 1, 2, 4, true, true, 4, 4>;
 using DownSmall4 = TileCfg<16, 64, 64, 1, 2, 4, false, true, 4, 4>;
+// ... and the fused layer's down projection (fp32 K-slices) likewise:
+// Qwen2-shaped T = 16 0.081 -> 0.079 ms, DeepSeek-V3-shaped T = 128 1.028 ->
+// 1.013 ms (same box, A/B; the K-split plan, made for 64 columns, holds for
+// any width)
+using DownSmall4W = TileCfg<32, 128, 64, 1, 4, 4, false, true, 4, 4>;
 using GateUpLarge128_4 = TileCfg<128, 128, 64, 4, 2, 4, true, false, 2, 4>;
 using DownLarge128_4 = TileCfg<128, 256, 64, 4, 2, 4, false, false, 2, 4>;
 // ... and, for the 128- and 256-row classes, FP8's widen-once ping-pong
@@ -1651,6 +1656,9 @@ using GateUpSmallM8 = TileCfg<16, 64, 64, 1, 2, 4, true, true, 1, 8, false, true
 using GateUpSmallM8W = TileCfg<32, 128, 64, 1, 4, 3, true, true, 1, 8, false, true>;
 using GateUpMidM8 = TileCfg<32, 64, 64, 1, 2, 4, true, true, 1, 8, false, true>;
 using DownSmallM8 = TileCfg<32, 64, 64, 1, 4, 4, false, true, 1, 8, false, true>;
+// ... and its fp32-output down tile likewise (DeepSeek-V3-shaped T = 128
+// layer 1.485 -> 1.440 ms, Qwen2-shaped T = 16 0.111 -> 0.107 ms)
+using DownSmallM8W = TileCfg<32, 128, 64, 1, 4, 4, false, true, 1, 8, false, true>;
 using GateUpLargeM8 = TileCfg<256, 128, 32, 4, 2, 5, true, false, 1, 8, true, true>;
 using GateUpLarge128_M8 = TileCfg<128, 128, 32, 4, 2, 5, true, false, 1, 8, true, true>;
 using DownLarge128_M8 = TileCfg<128, 256, 32, 4, 2, 5, false, false, 1, 8, true, true>;

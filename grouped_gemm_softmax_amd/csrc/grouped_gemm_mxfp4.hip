@@ -21,7 +21,8 @@ hipError_t launch_mxfp4(const GemmProblem& p, int tc, hipStream_t stream) {
   if (p.out_f32)
     return wide  ? launch_cfg<DownLarge_4W, float>(p, stream)
            : big ? launch_cfg<DownLarge128_4, float>(p, stream)
-                 : launch_cfg<DownSmall4, float>(p, stream);
+           : p.rows_hint <= 4 ? launch_cfg<DownSmall4W, float>(p, stream)
+                              : launch_cfg<DownSmall4, float>(p, stream);
   return wide  ? launch_cfg<DownLarge_4W, bf16_t>(p, stream)
          : big ? launch_cfg<DownLarge128_4, bf16_t>(p, stream)
                : launch_cfg<DownSmall4, bf16_t>(p, stream);

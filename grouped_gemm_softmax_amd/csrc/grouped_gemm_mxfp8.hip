@@ -20,6 +20,7 @@ hipError_t launch_mxfp8(const GemmProblem& p, int tc, hipStream_t stream) {
   if (p.out_f32)
     return tcm == kLarge      ? launch_cfg<DownLargeM8, float>(p, stream)
            : tcm == kLarge128 ? launch_cfg<DownLarge128_M8, float>(p, stream)
+           : p.rows_hint <= 4 ? launch_cfg<DownSmallM8W, float>(p, stream)
                               : launch_cfg<DownSmallM8, float>(p, stream);
   return tcm == kLarge      ? launch_cfg<DownLargeM8, bf16_t>(p, stream)
          : tcm == kLarge128 ? launch_cfg<DownLarge128_M8, bf16_t>(p, stream)
