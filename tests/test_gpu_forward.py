@@ -24,6 +24,9 @@ SHARED_CASES = {
     # ... and into 4 with the large tile
     "shared_long_k_large_batch": (synth.small_config("slkl", H=128, F=256, E=4, k=2, Fs=1024,
                                                      shared_gated=True), 200),
+    # 1024 routed experts and the shared one: every group table at its limit
+    "max_groups_shared": (synth.small_config("mgs", H=64, F=64, E=1024, k=8, Fs=128,
+                                             shared_gated=True), 50),
 }
 
 

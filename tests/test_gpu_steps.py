@@ -53,6 +53,11 @@ CASES = {
     "rowmajor_wide256": (synth.small_config("rw256", H=200, F=1480, E=64, k=2), 200, None),
     # ... few tokens: the 128-column gate/up tile (about 7 touched experts)
     "rowmajor_wide128": (synth.small_config("rw128", H=328, F=2344, E=8, k=2), 8, None),
+    # the ABI's limits: 1024 experts (16 logits per lane of the routing
+    # kernel, the permutation's and the GEMMs' group tables at full size) and
+    # k = 16
+    "max_experts_k16": (synth.small_config("mek", H=64, F=64, E=1024, k=16, logits="zipf"),
+                        100, None),
 }
 
 
