@@ -42,6 +42,9 @@ CASES = {
     "zipf_empty_experts": (synth.small_config("zm", H=256, F=128, E=64, k=8, logits="zipf"), 60),
     "single_token": (synth.small_config("st", H=136, F=72, E=8, k=2), 1),
     "k_equals_E": (synth.small_config("ke", H=64, F=48, E=5, k=5), 23),
+    # the ABI's limits: 1024 experts, k = 16 (the two dx products then take
+    # one launch each: their 2048 groups exceed one launch's group table)
+    "max_experts_k16": (synth.small_config("mek", H=64, F=64, E=1024, k=16, logits="zipf"), 100),
 }
 
 
