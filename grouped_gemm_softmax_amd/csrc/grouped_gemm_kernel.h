@@ -275,6 +275,15 @@ __device__ __forceinline__ void store4(float* p, const float v[4]) {
 // write through to, and read from, the memory all eight XCDs share, instead
 // of an XCD's own L2, so partial sums handed to another workgroup need no
 // write-back or invalidation of the whole L2 (which agent-scope fences do).
+// The logistic sigmoid 1/(1 + e^-z) with the reciprocal taken by v_rcp_f32
+// (1 ulp) instead of an IEEE division (about ten VALU instructions, which the
+// SwiGLU epilogues pay once per output element): h is rounded to bf16 right
+// after, 2^15 times coarser. 1 + e^-z >= 1, so no denormal reaches the
+// reciprocal; e^-z = inf gives 0, as the division would.
+__device__ __forceinline__ float sigmoid_rcp(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
 __device__ __forceinline__ void store4_device(float* p, const float v[4]) {
   typedef __attribute__((address_space(1))) float gfloat_t;
 #pragma unroll
@@ -1094,7 +1103,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
                 const float g = bf16_to_f32(static_cast<bf16_t>(gw[r / 2] >> (16 * (r % 2))));
                 const float u = bf16_to_f32(static_cast<bf16_t>(uw[r / 2] >> (16 * (r % 2))));
                 const float hv = bf16_to_f32(static_cast<bf16_t>(hw[r / 2] >> (16 * (r % 2))));
-                const float sg = 1.0f / (1.0f + __expf(-g));
+                const float sg = sigmoid_rcp(g);
                 const float gr = acc[0][fi][ti][r];
                 const float dh = wv[ti] * gr;
                 dg[r] = dh * u * sg * (1.0f + g * (1.0f - sg));
@@ -1129,7 +1138,7 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
               const float gt = FP8 ? acc[0][fi][ti][r] * sc0[r] : acc[0][fi][ti][r];
               const float up = FP8 ? acc[C::NMAT - 1][fi][ti][r] * sc1[r]
                                    : acc[C::NMAT - 1][fi][ti][r];
-              vals[r] = gt / (1.0f + __expf(-gt)) * up;
+              vals[r] = gt * sigmoid_rcp(gt) * up;
             } else {
               vals[r] = FP8 ? acc[0][fi][ti][r] * sc0[r] : acc[0][fi][ti][r];
             }
@@ -1452,7 +1461,7 @@ __global__ __launch_bounds__(kRsThreads) void rs_gateup_kernel(GemmProblem prob)
         for (int r = 0; r < 4; ++r) {
           const float gt = FP8 ? acc[0][r] * csc0[r] : acc[0][r];
           const float up = FP8 ? acc[1][r] * csc1[r] : acc[1][r];
-          v[r] = gt / (1.0f + __expf(-gt)) * up;
+          v[r] = gt * sigmoid_rcp(gt) * up;
         }
         store4(cc.out + static_cast<int64_t>(cc.row_base + i16) * cc.N + f, v);
       }
