@@ -68,51 +68,33 @@ namespace {
 
 constexpr int kMaxGroups = kMaxExperts + 1;  // routed experts + one shared
 
-// Eight E4M3 codes (the bytes of u, in order) widened to bf16. gfx950's
-// v_cvt_pk_f32_fp8 decodes two OCP E4M3 codes (the low or the high pair of
-// a dword) to fp32 exactly; every E4M3 value is a bf16 value, so the upper
-// half of each fp32 is its exact bf16. (Compiler builtins, so that the
-// compiler keeps its hazard waits against MFMAs still reading registers.)
-__device__ __forceinline__ uint32_t hi16_pair(float a, float b) {
-  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
-}
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 u) {
-  const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, false);
-  const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(u.x, true);
-  const auto f45 = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, false);
-  const auto f67 = __builtin_amdgcn_cvt_pk_f32_fp8(u.y, true);
-  const uint4 v = uint4{hi16_pair(f01[0], f01[1]), hi16_pair(f23[0], f23[1]),
-                        hi16_pair(f45[0], f45[1]), hi16_pair(f67[0], f67[1])};
-  return __builtin_bit_cast(bf16x8, v);
+// gfx950's v_cvt_scalef32_pk_bf16_fp8 / _fp4 decode two OCP E4M3 codes (the
+// low or the high word of a dword) or two E2M1 codes (one byte) straight to
+// bf16, times a power-of-two scale. Every such product of a weight is a bf16
+// value, so the conversion is exact. (Compiler builtins, so that the compiler
+// keeps its hazard waits against MFMAs still reading registers.)
+__device__ __forceinline__ bf16x8 cat4(bf16x2_t a, bf16x2_t b, bf16x2_t c, bf16x2_t d) {
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// Eight E4M3 codes (the bytes of u, in order) times a power-of-two scale,
-// widened to bf16: gfx950's v_cvt_scalef32_pk_f32_fp8 decodes two codes of
-// the low or the high word of a dword to fp32 and applies the scale; every
-// such product of an MXFP8 weight is a bf16 value, so the upper half of each
-// fp32 is exact.
+// Eight E4M3 codes (the bytes of u, in order) times a power-of-two scale.
 __device__ __forceinline__ bf16x8 fp8x8_scaled_to_bf16(uint2 u, float scale) {
-  const auto f01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u.x, scale, false);
-  const auto f23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u.x, scale, true);
-  const auto f45 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u.y, scale, false);
-  const auto f67 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u.y, scale, true);
-  const uint4 v = uint4{hi16_pair(f01[0], f01[1]), hi16_pair(f23[0], f23[1]),
-                        hi16_pair(f45[0], f45[1]), hi16_pair(f67[0], f67[1])};
-  return __builtin_bit_cast(bf16x8, v);
+  return cat4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.x, scale, false),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.x, scale, true),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.y, scale, false),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(u.y, scale, true));
 }
+
+// Eight E4M3 codes (the bytes of u, in order), unscaled.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 u) { return fp8x8_scaled_to_bf16(u, 1.0f); }
 
 // Eight E2M1 codes (the nibbles of u, low nibble first) times a power-of-two
-// scale, widened to bf16: gfx950's v_cvt_scalef32_pk_f32_fp4 decodes the two
-// codes of one byte to fp32 and applies the scale; every such product is a
-// bf16 value, so the upper half of each fp32 is exact.
+// scale.
 __device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t u, float scale) {
-  const auto f01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, scale, 0);
-  const auto f23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, scale, 1);
-  const auto f45 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, scale, 2);
-  const auto f67 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, scale, 3);
-  const uint4 v = uint4{hi16_pair(f01[0], f01[1]), hi16_pair(f23[0], f23[1]),
-                        hi16_pair(f45[0], f45[1]), hi16_pair(f67[0], f67[1])};
-  return __builtin_bit_cast(bf16x8, v);
+  return cat4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, scale, 0),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, scale, 1),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, scale, 2),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, scale, 3));
 }
 
 // MXFP4 scale bytes per 64-column block: K-blocks of 32, rounded up to a
