@@ -557,23 +557,19 @@ __global__ __launch_bounds__(C::kThreads, C::MIN_WAVES) void grouped_gemm_kernel
           // copies 8 consecutive rows (1 KB) of one block. Sub-blocks past N
           // re-load the last block (their outputs are masked).
           const int nb = min(it.n0 / 64 + jj / IPS, it.nblk - 1);
-          if constexpr (C::WBITS == 8) {
-            // 4 KB blocks of codes: [32-row half][64 columns][32 bytes]; a
-            // 32-deep step reads one half, a 64-deep step both (element
-            // offsets below are in bf16 units, 2 codes each)
-            const int64_t blk = static_cast<int64_t>(nb) * it.kblk + k0 / 64;
-            base = w + blk * 2048 + ((k0 % 64) / 32) * 1024 + (jj % IPS) * 512;
-          } else if constexpr (C::WBITS == 4) {
-            // 2 KB blocks of E2M1 codes: [32-row half][64 columns][16 bytes]
-            // (bf16-unit offsets: 4 codes each)
-            const int64_t blk = static_cast<int64_t>(nb) * it.kblk + k0 / 64;
-            base = w + blk * 1024 + ((k0 % 64) / 32) * 512 + (jj % IPS) * 512;
-          } else {
-            // 8 KB blocks: [32-row half][64 columns][32 K-values]; a 32-deep
-            // step reads one half, a 64-deep step the whole block
-            const int64_t blk = static_cast<int64_t>(nb) * it.kblk + k0 / 64;
-            base = w + blk * 4096 + ((k0 % 64) / 32) * 2048 + (jj % IPS) * 512;
-          }
+          // blocks of BLK bf16-unit elements, two 32-row halves each:
+          // 8 KB blocks [32-row half][64 columns][32 K-values] (bf16); 4 KB
+          // of codes [32-row half][64 columns][32 bytes] (8-bit, 2 codes per
+          // bf16 unit); 2 KB of E2M1 codes [32-row half][64 columns][16
+          // bytes] (4 codes per unit). A 32-deep step reads one half, a
+          // 64-deep step the whole block. The instruction's block row at
+          // K-block 0 is the same for every step of the item, so it is
+          // formed apart from the step's K offset.
+          constexpr int BLK = C::WBITS == 8 ? 2048 : C::WBITS == 4 ? 1024 : 4096;
+          const bf16_t* const wrow =
+              w + static_cast<int64_t>(nb) * it.kblk * BLK + (jj % IPS) * 512;
+          const uint32_t kb = static_cast<uint32_t>(k0);  // >= 0, below K
+          base = wrow + static_cast<int64_t>(kb >> 6) * BLK + ((kb >> 5) & 1u) * (BLK / 2);
         } else if constexpr (TRANSW) {
           base = w + k0;
           if constexpr (KTAIL) {

@@ -6,7 +6,6 @@
 namespace moe {
 
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Transposing LDS read: within each 16-lane group, lane i receives element
 // i%4 of the 8-byte chunks read by lanes 4r + i/4, r = 0..3.
@@ -44,10 +43,13 @@ __device__ __forceinline__ T* uniform(T* p) {
 // lds + 16*l; M0 holds the wave's LDS destination. Written as inline
 // assembly: the compiler's own LDS-DMA tracking cannot tell the ring buffers
 // apart for every LDS read and would drain all loads in flight before it,
-// while the kernel waits for exactly the stage it needs (vmcnt).
+// while the kernel waits for exactly the stage it needs (vmcnt). An LDS
+// byte's generic address is the LDS aperture's base in the upper 32 bits and
+// the LDS address in the lower 32, so the lower half is M0's value: a
+// generic-to-LDS cast would give the same for the (never null) ring
+// buffers, plus a null test and a 64-bit readfirstlane per instruction.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, char* lds) {
-  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (lds_void_t*)(lds)));
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   asm volatile("global_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(uniform(base)), "{m0}"(__builtin_amdgcn_readfirstlane(m0))
