@@ -267,8 +267,18 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   for (int i = tid; i < n; i += kPermThreads) {
     const int e = s_ids[i];
     const int r = i / per_chunk;
+    // the earlier assignments of the chunk with the same expert, eight LDS
+    // reads in flight at a time (a read-compare loop waits for each read)
     int rank = 0;
-    for (int i2 = r * per_chunk; i2 < i; ++i2) rank += (s_ids[i2] == e);
+    int i2 = r * per_chunk;
+    for (; i2 + 8 <= i; i2 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = s_ids[i2 + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) rank += (v[u] == e);
+    }
+    for (; i2 < i; ++i2) rank += (s_ids[i2] == e);
     int p = s_base[r][e] + rank;
     p = p < T * k ? p : T * k - 1;  // in bounds even for out-of-contract ids
     s_dest[i] = p;
